@@ -1,0 +1,173 @@
+/*
+ * vqkv.h — C ABI of libvqkv.so: single-query decode attention computed
+ * directly over a vector-quantised low-bit KV cache on AMD MI355X (gfx950).
+ *
+ * The method is VecInfer's ("VecInfer: Efficient LLM Inference With Low-Bit
+ * KV Cache via Outlier-Suppressed Vector Quantization", notes page):
+ *   - keys are smoothed per channel and Walsh–Hadamard transformed,
+ *       K~ = K diag(lambda)^-1 H_D            (Method details)
+ *     then stored as vector-quantisation codes: every d = 4 consecutive
+ *     channels (a sub-vector) is replaced by the index of its nearest
+ *     codebook centroid                      (Background, VQ principle);
+ *   - values are quantised the same way without any transform;
+ *   - the query is transformed as q~ = q diag(lambda) H_D, so that
+ *     q~ K~^T = q K^T                        (Method details, score rewrite);
+ *   - attention is s = q~ VQ^-1(K~_q)^T / sqrt(D), p = softmax(s),
+ *     o = p VQ^-1(V_q)                       (Method details, VQ KV cache in
+ *                                             attention)
+ *     and the codes are never dequantised to memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers allocated and owned by the
+ *    caller.  The library allocates no device memory; split partials live in
+ *    a caller-provided workspace.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on that stream and returns without
+ *    synchronising.  Faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued; the
+ *    validation never dereferences a pointer.  On failure the call returns a
+ *    non-zero vq_status, enqueues nothing and leaves a message for
+ *    vq_last_error().  No C++ exception crosses this interface.
+ *  - Only D = 128 and d = 4 are supported (VQ_ERR_UNSUPPORTED otherwise).
+ *  - Layouts (row-major, innermost last; B batch, Hq query heads, Hkv KV
+ *    heads, G = Hq / Hkv, P = D / d = 32 sub-vectors, cap = capacity):
+ *      q        [B][Hq][128]            fp16 or fp32 (q_dtype)
+ *      lambda   [Hkv][128]              fp32, finite and > 0 (caller contract)
+ *      cb_k     [Hkv][2^k_code_bits][4] fp16 (bit patterns as uint16)
+ *      cb_v     [Hkv][2^v_code_bits][4] fp16
+ *      codes_k  [B][Hkv][cap][P*k_code_bits/8] uint8 — token-major code rows:
+ *               8-bit codes are one byte per sub-vector; 12-bit codes are a
+ *               little-endian bit stream, code i in bits [12i, 12i+12) of
+ *               the 48-byte row.
+ *      codes_v  [B][Hkv][cap][P*v_code_bits/8] uint8
+ *      out      [B][Hq][128]            fp32
+ *    Query head h reads KV head h / G.  One codebook and one lambda per KV
+ *    head, shared by every sub-vector position and every sequence.
+ *  - Base pointers of codes, codebooks, q, lambda and out must be 16-byte
+ *    aligned (VQ_ERR_INVALID_ARG otherwise).
+ */
+#ifndef VQKV_H
+#define VQKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VQ_OK = 0,
+    VQ_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad alignment, Hq % Hkv != 0 */
+    VQ_ERR_UNSUPPORTED = 2,   /* geometry the kernels do not implement */
+    VQ_ERR_CAPACITY = 3,      /* tokens beyond the cache capacity */
+    VQ_ERR_WORKSPACE = 4,     /* workspace missing or too small */
+    VQ_ERR_HIP = 5            /* a HIP runtime or launch error */
+} vq_status;
+
+typedef enum { VQ_F16 = 0, VQ_F32 = 1 } vq_dtype;
+
+/* Cache geometry, plain data, passed by pointer. */
+typedef struct {
+    int32_t head_dim;      /* D: must be 128                          */
+    int32_t sub_dim;       /* d: must be 4                            */
+    int32_t k_code_bits;   /* log2 |C_k|: 8 or 12                     */
+    int32_t v_code_bits;   /* log2 |C_v|: 8                           */
+    int32_t num_kv_heads;  /* Hkv >= 1                                */
+    int32_t capacity;      /* token slots per (sequence, KV head) >= 1 */
+} vq_layout;
+
+/*
+ * q~ = q diag(lambda) H_128 for every (sequence, query head).
+ * VecInfer page, Method details: smooth factors and the Walsh–Hadamard
+ * recursion H_{2^k} = (1/sqrt 2)[[H, H], [H, -H]]; the query side of the
+ * attention-score rewrite.  H is the orthonormal Sylvester matrix in natural
+ * order.
+ *   q        [B][Hq][128] in q_dtype;   lambda [Hkv][128] fp32
+ *   q_tilde  [B][Hq][128] fp32 output
+ */
+int vq_transform_query(const vq_layout* layout, const void* q, int q_dtype,
+                       const float* lambda, int32_t batch, int32_t num_q_heads,
+                       float* q_tilde, void* stream);
+
+/*
+ * Quantise `num_new` new tokens per (sequence, KV head) and store their codes
+ * at token slots [cur_len, cur_len + num_new) of the cache.
+ * VecInfer page, Method details (VQ KV cache in attention): each new key gets
+ * the online dual transform k~ = k diag(lambda)^-1 H_D and is quantised with
+ * C_k; the value is quantised as is with C_v; codes are concatenated to the
+ * cache.  Background (VQ principle): j* = argmin_j ||x_i - C_j||^2.
+ * The transform and the distances are evaluated in fp64; exact distance ties
+ * go to the lowest centroid index.
+ *   k_new, v_new [B][Hkv][num_new][128] in kv_dtype (fp16 or fp32)
+ *   codes_k / codes_v: written at the slots above, nothing else is touched.
+ * Errors: VQ_ERR_CAPACITY if cur_len + num_new > capacity; VQ_ERR_INVALID_ARG
+ * if cur_len < 0 or num_new < 0.  num_new = 0 is a no-op that returns VQ_OK.
+ * The caller tracks the cache length; the call mutates no length.
+ */
+int vq_encode_append(const vq_layout* layout, const void* k_new, const void* v_new,
+                     int kv_dtype, const float* lambda, const uint16_t* cb_k,
+                     const uint16_t* cb_v, uint8_t* codes_k, uint8_t* codes_v,
+                     int32_t batch, int32_t cur_len, int32_t num_new, void* stream);
+
+/*
+ * Split count vq_decode_attention uses for this shape when num_splits = 0,
+ * and the workspace it needs for a given split count (0 = the default).
+ */
+int32_t vq_decode_attention_default_splits(const vq_layout* layout, int32_t batch,
+                                           int32_t num_q_heads, int32_t context_len);
+size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batch,
+                                           int32_t num_q_heads, int32_t context_len,
+                                           int32_t num_splits);
+
+/*
+ * Decode attention of one query per (sequence, query head) over the first
+ * `context_len` tokens of the VQ cache, without dequantising it to memory.
+ * VecInfer page, Method details (VQ KV cache in attention) for what is
+ * computed; Appendix (FlashAttention block recurrence and Algorithm 1) for
+ * the blockwise online softmax.  The context is split into `num_splits`
+ * contiguous ranges processed in parallel, and their partial results are
+ * merged by log-sum-exp (0 = library default; larger requests are clamped
+ * so that no split is empty).
+ *   q [B][Hq][128] in q_dtype (raw query: the transform happens inside)
+ *   out [B][Hq][128] fp32
+ *   workspace: device memory of at least
+ *              vq_decode_attention_workspace_bytes(...) bytes.
+ * Errors: VQ_ERR_CAPACITY if context_len > capacity; VQ_ERR_INVALID_ARG if
+ * context_len < 1 (softmax over an empty set) or Hq % Hkv != 0;
+ * VQ_ERR_UNSUPPORTED if G > 8; VQ_ERR_WORKSPACE if the workspace is too small.
+ * Results are bitwise reproducible for a fixed split count.
+ */
+int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype,
+                        const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                        const uint8_t* codes_k, const uint8_t* codes_v, int32_t batch,
+                        int32_t num_q_heads, int32_t context_len, int32_t num_splits,
+                        float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Uncompressed comparator: the same decode attention over an fp16 cache,
+ * o = softmax(q K^T / sqrt(128)) V with fp32 accumulation (VecInfer page,
+ * Background, KV cache and attention).  No transform, no quantisation.
+ *   q [B][Hq][128] fp16; k, v [B][Hkv][capacity][128] fp16; out fp32.
+ */
+size_t vq_fp16_attention_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t context_len,
+                                         int32_t num_splits);
+int vq_fp16_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t capacity, int32_t context_len, int32_t num_splits,
+                             float* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Static description of a vq_status value. */
+const char* vq_status_string(int status);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* vq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQKV_H */

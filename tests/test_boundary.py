@@ -1,0 +1,157 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any device
+work (every call below fails validation, so nothing is ever launched and the
+fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import vector_quantized_bit_amd as vq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "vqkv.h")
+
+OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE, HIP = range(6)
+A = 0x100000          # a fake, 16-byte aligned device address (never touched)
+MIS = 0x100004        # a fake misaligned address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vq.LIB_PATH):
+        pytest.fail("libvqkv.so is not built (run python -m vector_quantized_bit_amd.build)")
+    return vq.library()
+
+
+def lay(k_bits=8, v_bits=8, hkv=2, cap=1000, head_dim=128, sub_dim=4):
+    return vq.Layout(head_dim, sub_dim, k_bits, v_bits, hkv, cap)
+
+
+def test_header_functions_are_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    raw = ctypes.CDLL(vq.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(lib):
+    for st in range(6):
+        assert vq.status_string(st)
+    assert vq.status_string(OK) == "ok"
+    assert "unknown" in vq.status_string(99)
+
+
+def attn(lib, layout, q=A, q_dtype=0, lam=A, cbk=A, cbv=A, ck=A, cv=A, batch=1, hq=4, n=100,
+         splits=0, out=A, ws=A, ws_bytes=1 << 30):
+    return lib.vq_decode_attention(ctypes.byref(layout) if layout is not None else None, q,
+                                   q_dtype, lam, cbk, cbv, ck, cv, batch, hq, n, splits, out, ws,
+                                   ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,layout_kw,status,needle", [
+    (dict(), dict(head_dim=64), UNSUPPORTED, "head_dim"),
+    (dict(), dict(sub_dim=8), UNSUPPORTED, "sub_dim"),
+    (dict(), dict(k_bits=10), UNSUPPORTED, "k_code_bits"),
+    (dict(), dict(v_bits=12), UNSUPPORTED, "v_code_bits"),
+    (dict(), dict(hkv=0), INVALID, "num_kv_heads"),
+    (dict(), dict(cap=0), INVALID, "capacity"),
+    (dict(hq=3), dict(), INVALID, "multiple"),
+    (dict(hq=18), dict(), UNSUPPORTED, "group"),
+    (dict(batch=0), dict(), INVALID, "batch"),
+    (dict(n=0), dict(), INVALID, "context_len"),
+    (dict(n=1001), dict(), CAPACITY, "capacity"),
+    (dict(q_dtype=7), dict(), INVALID, "q_dtype"),
+    (dict(splits=-1), dict(), INVALID, "num_splits"),
+    (dict(q=None), dict(), INVALID, "q is NULL"),
+    (dict(lam=MIS), dict(), INVALID, "lambda"),
+    (dict(ck=None), dict(), INVALID, "codes_k"),
+    (dict(cv=MIS), dict(), INVALID, "codes_v"),
+    (dict(cbk=None), dict(), INVALID, "cb_k"),
+    (dict(out=MIS), dict(), INVALID, "out"),
+    (dict(ws=None), dict(), WORKSPACE, "workspace"),
+    (dict(ws_bytes=16), dict(), WORKSPACE, "workspace"),
+    (dict(ws=MIS), dict(), INVALID, "workspace"),
+])
+def test_decode_attention_validation(lib, kw, layout_kw, status, needle):
+    st = attn(lib, lay(**layout_kw), **kw)
+    assert st == status, vq._last_error()
+    assert needle in vq._last_error()
+
+
+def test_decode_attention_null_layout(lib):
+    assert attn(lib, None) == INVALID
+
+
+def test_workspace_query_matches_partials_layout(lib):
+    layout = lay(hkv=8, cap=196608)
+    s = lib.vq_decode_attention_default_splits(ctypes.byref(layout), 1, 32, 196608)
+    assert s >= 1
+    need = lib.vq_decode_attention_workspace_bytes(ctypes.byref(layout), 1, 32, 196608, 0)
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    n = 1 * 32 * s
+    assert need == 2 * a256(4 * n) + a256(4 * 128 * n)
+    # explicit split requests are clamped so that no split is empty
+    one = lib.vq_decode_attention_workspace_bytes(ctypes.byref(layout), 1, 32, 300, 10 ** 6)
+    n = 32 * 2                                       # 300 tokens -> at most 2 tiles of 256
+    assert one == 2 * a256(4 * n) + a256(4 * 128 * n)
+    assert lib.vq_decode_attention_workspace_bytes(None, 1, 32, 100, 0) == 0
+
+
+def encode(lib, layout, k=A, v=A, dtype=0, lam=A, cbk=A, cbv=A, ck=A, cv=A, batch=1, cur=0, new=1):
+    return lib.vq_encode_append(ctypes.byref(layout), k, v, dtype, lam, cbk, cbv, ck, cv, batch,
+                                cur, new, None)
+
+
+@pytest.mark.parametrize("kw,layout_kw,status", [
+    (dict(cur=1000, new=1), dict(), CAPACITY),
+    (dict(cur=990, new=11), dict(), CAPACITY),
+    (dict(cur=-1), dict(), INVALID),
+    (dict(new=-1), dict(), INVALID),
+    (dict(batch=0), dict(), INVALID),
+    (dict(dtype=3), dict(), INVALID),
+    (dict(k=None), dict(), INVALID),
+    (dict(cbv=MIS), dict(), INVALID),
+    (dict(), dict(k_bits=4), UNSUPPORTED),
+])
+def test_encode_append_validation(lib, kw, layout_kw, status):
+    assert encode(lib, lay(**layout_kw), **kw) == status, vq._last_error()
+
+
+def test_encode_append_zero_tokens_is_a_no_op(lib):
+    # validated, then returns before any device work
+    assert encode(lib, lay(), new=0) == OK
+    assert vq._last_error() == ""
+
+
+def test_transform_query_validation(lib):
+    layout = lay(hkv=2)
+    f = lib.vq_transform_query
+    assert f(ctypes.byref(layout), None, 0, A, 1, 4, A, None) == INVALID
+    assert f(ctypes.byref(layout), A, 0, A, 1, 5, A, None) == INVALID
+    assert f(ctypes.byref(layout), A, 2, A, 1, 4, A, None) == INVALID
+    assert f(ctypes.byref(layout), A, 0, A, 1, 4, MIS, None) == INVALID
+
+
+def test_fp16_attention_validation(lib):
+    f = lib.vq_fp16_decode_attention
+    big = 1 << 30
+    assert f(A, A, A, 1, 4, 0, 10, 5, 0, A, A, big, None) == INVALID       # num_kv_heads
+    assert f(A, A, A, 1, 4, 1, 10, 11, 0, A, A, big, None) == CAPACITY
+    assert f(A, A, A, 1, 4, 1, 10, 0, 0, A, A, big, None) == INVALID
+    assert f(A, A, A, 1, 36, 4, 10, 5, 0, A, A, big, None) == UNSUPPORTED  # G = 9
+    assert f(None, A, A, 1, 4, 1, 10, 5, 0, A, A, big, None) == INVALID
+    assert f(A, A, A, 1, 4, 1, 10, 5, 0, A, A, 8, None) == WORKSPACE
+    need = lib.vq_fp16_attention_workspace_bytes(1, 4, 1, 10, 0)
+    assert need > 0

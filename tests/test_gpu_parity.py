@@ -1,0 +1,227 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances on attention outputs are relative L2 <= 1e-3 over the whole
+output and max-abs <= 2e-3; encoder codes must be bit-identical wherever the
+fp64 reference has a strict winner (distance gap above 1e-9 (1 + d)); at a
+gap below that both indices are nearest to within fp64 rounding and the
+GPU's pick must be one of the tied minima.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vector_quantized_bit_amd as vq
+import workloads as W
+from fixtures import attention_errors, chain_cache, expected_all, expected_head, random_cache
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-3
+ABS_TOL = 2e-3
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def upload(c):
+    return dict(q=dev(c.q), lam=dev(c.lam), cb_k=dev(c.cb_k), cb_v=dev(c.cb_v),
+                codes_k=dev(c.codes_k), codes_v=dev(c.codes_v))
+
+
+def run_attention(d, n, splits=0):
+    out = vq.decode_attention(d["q"], d["lam"], d["cb_k"], d["cb_v"], d["codes_k"], d["codes_v"],
+                              n, num_splits=splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def assert_close(got, ref, what):
+    rel, mab = attention_errors(got, ref)
+    print(f"{what}: rel_l2={rel:.3e} max_abs={mab:.3e}", flush=True)
+    assert rel <= REL_TOL and mab <= ABS_TOL, (what, rel, mab)
+
+
+# --- query transform --------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_transform_query_matches_oracle(dtype):
+    rng = np.random.default_rng(100)
+    q = W.as_storage(rng.standard_normal((3, 8, 128)) * 2, dtype)
+    lam = (0.5 + rng.random((2, 128)) * 4).astype(np.float32)
+    got = vq.transform_query(dev(q), dev(lam)).cpu().numpy().astype(np.float64)
+    ref = np.stack([oracle.transform_query(q[b, h], lam[h // 4]) for b in range(3)
+                    for h in range(8)]).reshape(3, 8, 128)
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    print(f"transform_query {dtype}: max rel {err:.2e}", flush=True)
+    assert err < 2e-6
+
+
+# --- decode attention: the tiny recipe case, in full ----------------------------------
+
+@pytest.fixture(scope="module")
+def tiny():
+    c = chain_cache(W.WORKLOADS[1])
+    return c, upload(c), expected_all(c)
+
+
+def test_tiny_recipe_case_matches_oracle(tiny):
+    c, d, ref = tiny
+    assert_close(run_attention(d, c.context_len), ref, "config1 chain")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 64])
+def test_split_count_does_not_change_the_result(tiny, splits):
+    c, d, ref = tiny
+    assert_close(run_attention(d, c.context_len, splits), ref, f"config1 splits={splits}")
+
+
+def test_bitwise_reproducible(tiny):
+    c, d, _ = tiny
+    a = run_attention(d, c.context_len)
+    b = run_attention(d, c.context_len)
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 255, 256, 257, 511, 700, 1024])
+def test_ragged_context_lengths(tiny, n):
+    c, d, _ = tiny
+    assert_close(run_attention(d, n), expected_all(c, n), f"config1 n={n}")
+
+
+@pytest.mark.parametrize("group,k_bits,n", [(1, 8, 300), (2, 8, 1000), (3, 12, 777),
+                                            (5, 12, 1500), (6, 8, 513), (8, 8, 2049),
+                                            (8, 12, 600)])
+def test_group_sizes_and_code_widths(group, k_bits, n):
+    wl = W.Workload(90 + group, "adhoc", batch=2, num_q_heads=2 * group, num_kv_heads=2,
+                    context_len=n, k_bits=k_bits, qkv_dtype="f16")
+    c = random_cache(wl)
+    d = upload(c)
+    assert_close(run_attention(d, n), expected_all(c), f"G={group} kbits={k_bits} n={n}")
+
+
+# --- decode attention at the full workload sizes (sampled outputs) --------------------
+
+FULL = [(2, [(0, 0), (0, 5)]), (3, [(0, 1), (9, 7), (15, 3)]), (4, [(0, 2), (0, 7)]),
+        (5, [(0, 0), (6, 4)])]
+
+
+@pytest.mark.parametrize("config,samples", FULL)
+def test_full_size_sampled_heads(config, samples):
+    wl = W.WORKLOADS[config]
+    c = random_cache(wl)
+    d = upload(c)
+    splits = vq.decode_attention_default_splits(d["codes_k"], d["codes_v"], d["cb_k"], d["cb_v"],
+                                                wl.batch, wl.num_q_heads, wl.context_len)
+    print(f"config{config}: default splits {splits}", flush=True)
+    got = run_attention(d, wl.context_len)
+    assert np.isfinite(got).all()
+    g = wl.group
+    for b, h in samples:
+        ref = expected_head(c, b, h)
+        assert_close(got[b, h * g:(h + 1) * g], ref, f"config{config} b={b} kv={h}")
+
+
+# --- encoder ------------------------------------------------------------------------
+
+def check_codes(got_rows, ref_rows, gaps, bits, x=None, cb=None, what=""):
+    got = oracle.unpack_codes(got_rows, bits, 32)
+    ref = oracle.unpack_codes(ref_rows, bits, 32)
+    gaps = np.asarray(gaps)
+    mism = got != ref
+    n_mis = int(mism.sum())
+    print(f"{what}: {got.size} codes, {n_mis} differ, min gap {gaps.min():.3e}", flush=True)
+    if n_mis:
+        # every difference must sit at an fp64 near-tie: both picks are nearest
+        # centroids to within rounding
+        sub = np.asarray(x, np.float64).reshape(-1, 32, 4)[mism]
+        cbd = np.asarray(cb, np.float64)
+        dg = ((sub - cbd[got[mism]]) ** 2).sum(-1)
+        dr = ((sub - cbd[ref[mism]]) ** 2).sum(-1)
+        assert np.all(gaps[mism] <= 1e-9 * (1 + dr)), what
+        assert np.all(np.abs(dg - dr) <= 1e-9 * (1 + dr)), what
+
+
+def test_encoder_tiny_recipe_case_bit_exact(tiny):
+    c, d, _ = tiny
+    wl = c.wl
+    n = wl.context_len
+    k = W.kv_rows(1, 0, 0, "k", n).astype(np.float32)[None, None]
+    v = W.kv_rows(1, 0, 0, "v", n).astype(np.float32)[None, None]
+    ck = torch.zeros_like(d["codes_k"])
+    cv = torch.zeros_like(d["codes_v"])
+    vq.encode_append(dev(k), dev(v), d["lam"], d["cb_k"], d["cb_v"], ck, cv, 0)
+    torch.cuda.synchronize()
+    _, _, gk, gv = oracle.encode_append(k[0, 0], v[0, 0], c.lam[0], c.cb_k[0], c.cb_v[0])
+    kt = oracle.transform_keys(k[0, 0], c.lam[0])
+    check_codes(ck.cpu().numpy()[0, 0, :n], c.codes_k[0, 0, :n], gk, 8, kt, c.cb_k[0], "enc K c1")
+    check_codes(cv.cpu().numpy()[0, 0, :n], c.codes_v[0, 0, :n], gv, 8, v[0, 0], c.cb_v[0],
+                "enc V c1")
+    # the GPU-encoded cache then decodes to the oracle's attention
+    d2 = dict(d, codes_k=ck, codes_v=cv)
+    assert_close(run_attention(d2, n), expected_all(c), "config1 encode->attend")
+
+
+def test_encoder_append_mixed_bits_full_size():
+    wl = W.WORKLOADS[5]
+    bsz, hkv, t_new, cur = wl.batch, wl.num_kv_heads, wl.append_tokens, wl.context_len
+    lam = np.stack([W.random_lambda(5, g) for g in range(hkv)])
+    cb_k = np.stack([W.random_codebook(5, g, "k", 4096, 0.6) for g in range(hkv)])
+    cb_v = np.stack([W.random_codebook(5, g, "v", 256, 1.0, 1 / 32) for g in range(hkv)])
+    k = np.stack([np.stack([W.kv_rows(5, b, g, "k", t_new, append=True) for g in range(hkv)])
+                  for b in range(bsz)]).astype(np.float16)
+    v = np.stack([np.stack([W.kv_rows(5, b, g, "v", t_new, append=True) for g in range(hkv)])
+                  for b in range(bsz)]).astype(np.float16)
+    cap = wl.capacity
+    ck = torch.full((bsz, hkv, cap, 48), 0xA5, dtype=torch.uint8, device=DEV)
+    cv = torch.full((bsz, hkv, cap, 32), 0x5A, dtype=torch.uint8, device=DEV)
+    vq.encode_append(dev(k), dev(v), dev(lam), dev(cb_k), dev(cb_v), ck, cv, cur)
+    torch.cuda.synchronize()
+    ckh = ck.cpu().numpy()
+    cvh = cv.cpu().numpy()
+    # nothing outside the appended slots changed
+    assert np.all(ckh[:, :, :cur] == 0xA5) and np.all(cvh[:, :, :cur] == 0x5A)
+    for b in range(bsz):
+        for g in range(hkv):
+            pk, pv, gk, gv = oracle.encode_append(k[b, g], v[b, g], lam[g], cb_k[g], cb_v[g], 12, 8)
+            kt = oracle.transform_keys(k[b, g], lam[g])
+            check_codes(ckh[b, g, cur:cur + t_new], pk, gk, 12, kt, cb_k[g], f"enc K c5 b{b} g{g}")
+            check_codes(cvh[b, g, cur:cur + t_new], pv, gv, 8, v[b, g], cb_v[g], f"enc V c5 b{b} g{g}")
+
+
+def test_encoder_exact_ties_go_to_lowest_index():
+    rng = np.random.default_rng(200)
+    base = rng.standard_normal((128, 4)).astype(np.float16)
+    cb_v = np.concatenate([base, base])[None]              # entry j and j+128 identical
+    cb_k = cb_v.copy()
+    # values equal to centroid entries: both copies tie at distance 0
+    codes = rng.integers(0, 128, size=(5, 32))
+    v = base.astype(np.float64)[codes].reshape(5, 128).astype(np.float32)[None, None]
+    lam = np.ones((1, 128), np.float32)
+    ck = torch.zeros((1, 1, 8, 32), dtype=torch.uint8, device=DEV)
+    cv = torch.zeros((1, 1, 8, 32), dtype=torch.uint8, device=DEV)
+    vq.encode_append(dev(v), dev(v), dev(lam), dev(cb_k), dev(cb_v), ck, cv, 2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cv.cpu().numpy()[0, 0, 2:7], codes)
+    assert cv.cpu().numpy()[0, 0, 2:7].max() < 128
+
+
+# --- fp16 comparator -----------------------------------------------------------------
+
+@pytest.mark.parametrize("bsz,hq,hkv,n", [(1, 4, 1, 1), (1, 4, 1, 1000), (2, 10, 2, 3001),
+                                          (1, 32, 8, 32768)])
+def test_fp16_attention_matches_oracle(bsz, hq, hkv, n):
+    rng = np.random.default_rng(300 + n)
+    q = rng.standard_normal((bsz, hq, 128)).astype(np.float16)
+    k = (rng.standard_normal((bsz, hkv, n + 5, 128)) * 1.5).astype(np.float16)
+    v = rng.standard_normal((bsz, hkv, n + 5, 128)).astype(np.float16)
+    out = vq.fp16_decode_attention(dev(q), dev(k), dev(v), n)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    g = hq // hkv
+    ref = np.stack([np.stack([oracle.softmax_attention(q[b, h].astype(np.float64),
+                                                       k[b, h // g, :n], v[b, h // g, :n])
+                              for h in range(hq)]) for b in range(bsz)])
+    assert_close(got, ref, f"fp16 b={bsz} hq={hq} hkv={hkv} n={n}")

@@ -1,0 +1,228 @@
+"""Thin Python binding of libvqkv.so (VQ-KV decode attention for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/vqkv.h``.  PyTorch supplies
+device memory and the current stream; nothing here computes on tensors.
+The functions keep the C entry points' names without the ``vq_`` prefix.
+
+The library must have been built (``python -m vector_quantized_bit_amd.build``);
+importing works without it, but the first call raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "VqError", "Layout", "library", "make_layout", "transform_query",
+    "encode_append", "decode_attention", "decode_attention_workspace_bytes",
+    "decode_attention_default_splits", "fp16_decode_attention",
+    "fp16_attention_workspace_bytes", "status_string",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqkv.so")
+
+VQ_F16, VQ_F32 = 0, 1
+_c_int = ctypes.c_int
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_size = ctypes.c_size_t
+
+
+class Layout(ctypes.Structure):
+    """The C ``vq_layout`` struct."""
+
+    _fields_ = [("head_dim", _i32), ("sub_dim", _i32), ("k_code_bits", _i32),
+                ("v_code_bits", _i32), ("num_kv_heads", _i32), ("capacity", _i32)]
+
+
+class VqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status}): {_last_error()}")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libvqkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m vector_quantized_bit_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lp = ctypes.POINTER(Layout)
+    sig = {
+        "vq_transform_query": (_c_int, [lp, _vp, _c_int, _vp, _i32, _i32, _vp, _vp]),
+        "vq_encode_append": (_c_int, [lp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _i32,
+                                      _i32, _i32, _vp]),
+        "vq_decode_attention_default_splits": (_i32, [lp, _i32, _i32, _i32]),
+        "vq_decode_attention_workspace_bytes": (_size, [lp, _i32, _i32, _i32, _i32]),
+        "vq_decode_attention": (_c_int, [lp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                         _i32, _i32, _vp, _vp, _size, _vp]),
+        "vq_fp16_attention_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32]),
+        "vq_fp16_decode_attention": (_c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              _vp, _vp, _size, _vp]),
+        "vq_status_string": (ctypes.c_char_p, [_c_int]),
+        "vq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().vq_status_string(status).decode()
+
+
+def _last_error() -> str:
+    return library().vq_last_error().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise VqError(status, what)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return VQ_F16
+    if t.dtype == torch.float32:
+        return VQ_F32
+    raise TypeError(f"expected float16 or float32, got {t.dtype}")
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def make_layout(codes_k: torch.Tensor, codes_v: torch.Tensor, cb_k: torch.Tensor,
+                cb_v: torch.Tensor) -> Layout:
+    """Cache geometry from the tensors: codes_* [B][Hkv][cap][row] uint8,
+    cb_* [Hkv][2^bits][4] float16."""
+    _need(codes_k.dim() == 4 and codes_v.dim() == 4, "codes must be [B][Hkv][cap][row]")
+    _need(cb_k.dim() == 3 and cb_v.dim() == 3, "codebooks must be [Hkv][entries][4]")
+    k_bits = cb_k.shape[1].bit_length() - 1
+    v_bits = cb_v.shape[1].bit_length() - 1
+    return Layout(head_dim=128, sub_dim=int(cb_k.shape[2]), k_code_bits=k_bits,
+                  v_code_bits=v_bits, num_kv_heads=int(codes_k.shape[1]),
+                  capacity=int(codes_k.shape[2]))
+
+
+def _check_cache(codes_k, codes_v, cb_k, cb_v, lam):
+    for name, t, dt in (("codes_k", codes_k, torch.uint8), ("codes_v", codes_v, torch.uint8),
+                        ("cb_k", cb_k, torch.float16), ("cb_v", cb_v, torch.float16),
+                        ("lambda", lam, torch.float32)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+        _need(t.dtype == dt, f"{name} must be {dt}, got {t.dtype}")
+    _need(codes_k.shape[:3] == codes_v.shape[:3], "codes_k and codes_v disagree in [B][Hkv][cap]")
+
+
+def transform_query(q: torch.Tensor, lam: torch.Tensor, out: torch.Tensor | None = None):
+    """q~ = q diag(lambda) H_128 -> float32 [B][Hq][128]."""
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
+    _need(lam.is_cuda and lam.is_contiguous() and lam.dtype == torch.float32 and lam.dim() == 2,
+          "lambda must be contiguous float32 [Hkv][128]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lay = Layout(128, 4, 8, 8, int(lam.shape[0]), 1)
+    _check(library().vq_transform_query(ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam),
+                                        q.shape[0], q.shape[1], _ptr(out), _stream(q)),
+           "vq_transform_query")
+    return out
+
+
+def encode_append(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int) -> None:
+    """Encode k_new / v_new [B][Hkv][T][128] into slots [cur_len, cur_len+T)."""
+    _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
+    _need(k_new.shape == v_new.shape and k_new.dim() == 4, "k_new/v_new must be [B][Hkv][T][128]")
+    _need(k_new.dtype == v_new.dtype, "k_new and v_new must share a dtype")
+    _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new/v_new must be contiguous")
+    _need(k_new.shape[0] == codes_k.shape[0] and k_new.shape[1] == codes_k.shape[1],
+          "k_new [B][Hkv] disagrees with the cache")
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    _check(library().vq_encode_append(ctypes.byref(lay), _ptr(k_new), _ptr(v_new),
+                                      _dtype_code(k_new), _ptr(lam), _ptr(cb_k), _ptr(cb_v),
+                                      _ptr(codes_k), _ptr(codes_v), k_new.shape[0], cur_len,
+                                      k_new.shape[2], _stream(k_new)),
+           "vq_encode_append")
+
+
+def decode_attention_default_splits(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads,
+                                    context_len) -> int:
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    return int(library().vq_decode_attention_default_splits(ctypes.byref(lay), batch,
+                                                            num_q_heads, context_len))
+
+
+def decode_attention_workspace_bytes(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads,
+                                     context_len, num_splits: int = 0) -> int:
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    return int(library().vq_decode_attention_workspace_bytes(ctypes.byref(lay), batch,
+                                                             num_q_heads, context_len,
+                                                             num_splits))
+
+
+def decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
+                     num_splits: int = 0, out=None, workspace=None):
+    """Decode attention over the VQ cache -> float32 [B][Hq][128]."""
+    _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
+    batch, hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = decode_attention_workspace_bytes(codes_k, codes_v, cb_k, cb_v, batch, hq,
+                                                  context_len, num_splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    _check(library().vq_decode_attention(ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam),
+                                         _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
+                                         batch, hq, context_len, num_splits, _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream(q)),
+           "vq_decode_attention")
+    return out
+
+
+def fp16_attention_workspace_bytes(batch, num_q_heads, num_kv_heads, context_len,
+                                   num_splits: int = 0) -> int:
+    return int(library().vq_fp16_attention_workspace_bytes(batch, num_q_heads, num_kv_heads,
+                                                           context_len, num_splits))
+
+
+def fp16_decode_attention(q, k, v, context_len: int, num_splits: int = 0, out=None,
+                          workspace=None):
+    """Uncompressed comparator: q [B][Hq][128], k/v [B][Hkv][cap][128], all fp16."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float16,
+              f"{name} must be a contiguous float16 device tensor")
+    _need(k.shape == v.shape and k.dim() == 4, "k/v must be [B][Hkv][cap][128]")
+    batch, hq = q.shape[0], q.shape[1]
+    hkv, cap = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = fp16_attention_workspace_bytes(batch, hq, hkv, context_len, num_splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(library().vq_fp16_decode_attention(_ptr(q), _ptr(k), _ptr(v), batch, hq, hkv, cap,
+                                              context_len, num_splits, _ptr(out),
+                                              _ptr(workspace), workspace.numel(), _stream(q)),
+           "vq_fp16_decode_attention")
+    return out

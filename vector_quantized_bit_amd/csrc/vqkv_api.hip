@@ -1,0 +1,273 @@
+// C ABI of libvqkv (declared in include/vqkv.h): host-side validation, split
+// planning, workspace layout and kernel dispatch.  Validation never touches
+// the device or dereferences a caller pointer.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/vqkv.h"
+#include "launchers.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return VQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define VQ_REQUIRE_PTR(p)                                                             \
+    do {                                                                              \
+        if ((p) == nullptr) return fail(VQ_ERR_INVALID_ARG, "%s is NULL", #p);        \
+        if (!aligned16(p)) return fail(VQ_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+// Device-independent plan: the same shape always gets the same split count,
+// so results are reproducible across devices and runs.
+constexpr int kTargetWorkgroups = 512;   // two per CU of a 256-CU MI355X
+constexpr int kMaxGroup = 8;
+
+int check_layout(const vq_layout* L) {
+    if (L == nullptr) return fail(VQ_ERR_INVALID_ARG, "layout is NULL");
+    if (L->head_dim != vqkv::kHeadDim)
+        return fail(VQ_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", L->head_dim);
+    if (L->sub_dim != vqkv::kSubDim)
+        return fail(VQ_ERR_UNSUPPORTED, "sub_dim %d unsupported (only 4)", L->sub_dim);
+    if (L->k_code_bits != 8 && L->k_code_bits != 12)
+        return fail(VQ_ERR_UNSUPPORTED, "k_code_bits %d unsupported (8 or 12)", L->k_code_bits);
+    if (L->v_code_bits != 8)
+        return fail(VQ_ERR_UNSUPPORTED, "v_code_bits %d unsupported (only 8)", L->v_code_bits);
+    if (L->num_kv_heads < 1 || L->num_kv_heads > 65535)
+        return fail(VQ_ERR_INVALID_ARG, "num_kv_heads %d out of range [1, 65535]", L->num_kv_heads);
+    if (L->capacity < 1) return fail(VQ_ERR_INVALID_ARG, "capacity %d < 1", L->capacity);
+    return VQ_OK;
+}
+
+int check_heads(int batch, int num_q_heads, int num_kv_heads) {
+    if (batch < 1 || batch > 65535)
+        return fail(VQ_ERR_INVALID_ARG, "batch %d out of range [1, 65535]", batch);
+    if (num_q_heads < 1) return fail(VQ_ERR_INVALID_ARG, "num_q_heads %d < 1", num_q_heads);
+    if (num_q_heads % num_kv_heads != 0)
+        return fail(VQ_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    if (num_q_heads / num_kv_heads > kMaxGroup)
+        return fail(VQ_ERR_UNSUPPORTED, "GQA group %d > %d", num_q_heads / num_kv_heads, kMaxGroup);
+    return VQ_OK;
+}
+
+struct SplitPlan {
+    int num_splits;
+    int tokens_per_split;
+};
+
+SplitPlan plan_splits(int streams, int context_len, int requested, int tile) {
+    const int max_splits = (context_len + tile - 1) / tile;
+    int s = requested > 0 ? requested : (kTargetWorkgroups + streams - 1) / streams;
+    if (s < 1) s = 1;
+    if (s > max_splits) s = max_splits;
+    const int per = (context_len + s - 1) / s;
+    const int tps = ((per + tile - 1) / tile) * tile;
+    return {(context_len + tps - 1) / tps, tps};
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t partials_bytes(int batch, int num_q_heads, int num_splits) {
+    const size_t n = static_cast<size_t>(batch) * num_q_heads * num_splits;
+    return 2 * align256(n * sizeof(float)) + align256(n * vqkv::kHeadDim * sizeof(float));
+}
+
+vqkv::Partials carve_partials(void* ws, int batch, int num_q_heads, int num_splits) {
+    const size_t n = static_cast<size_t>(batch) * num_q_heads * num_splits;
+    char* p = static_cast<char*>(ws);
+    vqkv::Partials part;
+    part.m = reinterpret_cast<float*>(p);
+    part.l = reinterpret_cast<float*>(p + align256(n * sizeof(float)));
+    part.o = reinterpret_cast<float*>(p + 2 * align256(n * sizeof(float)));
+    return part;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(VQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vq_status_string(int status) {
+    switch (status) {
+        case VQ_OK: return "ok";
+        case VQ_ERR_INVALID_ARG: return "invalid argument";
+        case VQ_ERR_UNSUPPORTED: return "unsupported geometry";
+        case VQ_ERR_CAPACITY: return "cache capacity exceeded";
+        case VQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case VQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* vq_last_error(void) { return g_last_error; }
+
+int vq_transform_query(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
+                       int32_t batch, int32_t num_q_heads, float* q_tilde, void* stream) {
+    int st = check_layout(layout);
+    if (st) return st;
+    if ((st = check_heads(batch, num_q_heads, layout->num_kv_heads))) return st;
+    if (q_dtype != VQ_F16 && q_dtype != VQ_F32)
+        return fail(VQ_ERR_INVALID_ARG, "q_dtype %d is not VQ_F16 or VQ_F32", q_dtype);
+    VQ_REQUIRE_PTR(q);
+    VQ_REQUIRE_PTR(lambda);
+    VQ_REQUIRE_PTR(q_tilde);
+    return hip_status(vqkv::launch_transform_query(q, q_dtype == VQ_F32, lambda, batch, num_q_heads,
+                                                   layout->num_kv_heads, q_tilde,
+                                                   static_cast<hipStream_t>(stream)),
+                      "transform_query launch");
+}
+
+int vq_encode_append(const vq_layout* layout, const void* k_new, const void* v_new, int kv_dtype,
+                     const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                     uint8_t* codes_k, uint8_t* codes_v, int32_t batch, int32_t cur_len,
+                     int32_t num_new, void* stream) {
+    int st = check_layout(layout);
+    if (st) return st;
+    if (batch < 1 || batch > 65535)
+        return fail(VQ_ERR_INVALID_ARG, "batch %d out of range [1, 65535]", batch);
+    if (kv_dtype != VQ_F16 && kv_dtype != VQ_F32)
+        return fail(VQ_ERR_INVALID_ARG, "kv_dtype %d is not VQ_F16 or VQ_F32", kv_dtype);
+    if (num_new < 0) return fail(VQ_ERR_INVALID_ARG, "num_new %d < 0", num_new);
+    if (cur_len < 0) return fail(VQ_ERR_INVALID_ARG, "cur_len %d < 0", cur_len);
+    if (static_cast<int64_t>(cur_len) + num_new > layout->capacity)
+        return fail(VQ_ERR_CAPACITY, "cur_len %d + num_new %d exceeds capacity %d", cur_len,
+                    num_new, layout->capacity);
+    VQ_REQUIRE_PTR(k_new);
+    VQ_REQUIRE_PTR(v_new);
+    VQ_REQUIRE_PTR(lambda);
+    VQ_REQUIRE_PTR(cb_k);
+    VQ_REQUIRE_PTR(cb_v);
+    VQ_REQUIRE_PTR(codes_k);
+    VQ_REQUIRE_PTR(codes_v);
+    if (num_new == 0) return ok();
+    return hip_status(vqkv::launch_encode_append(layout->k_code_bits, k_new, v_new,
+                                                 kv_dtype == VQ_F32, lambda, cb_k, cb_v, codes_k,
+                                                 codes_v, batch, layout->num_kv_heads,
+                                                 layout->capacity, cur_len, num_new,
+                                                 static_cast<hipStream_t>(stream)),
+                      "encode_append launch");
+}
+
+int32_t vq_decode_attention_default_splits(const vq_layout* layout, int32_t batch,
+                                           int32_t num_q_heads, int32_t context_len) {
+    (void)num_q_heads;
+    if (layout == nullptr || batch < 1 || context_len < 1 || layout->num_kv_heads < 1) return 0;
+    return plan_splits(batch * layout->num_kv_heads, context_len, 0, vqkv::kVqTile).num_splits;
+}
+
+size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batch,
+                                           int32_t num_q_heads, int32_t context_len,
+                                           int32_t num_splits) {
+    if (layout == nullptr || batch < 1 || num_q_heads < 1 || context_len < 1 ||
+        layout->num_kv_heads < 1)
+        return 0;
+    const SplitPlan p =
+        plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
+    return partials_bytes(batch, num_q_heads, p.num_splits);
+}
+
+int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
+                        const uint16_t* cb_k, const uint16_t* cb_v, const uint8_t* codes_k,
+                        const uint8_t* codes_v, int32_t batch, int32_t num_q_heads,
+                        int32_t context_len, int32_t num_splits, float* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    int st = check_layout(layout);
+    if (st) return st;
+    if ((st = check_heads(batch, num_q_heads, layout->num_kv_heads))) return st;
+    if (q_dtype != VQ_F16 && q_dtype != VQ_F32)
+        return fail(VQ_ERR_INVALID_ARG, "q_dtype %d is not VQ_F16 or VQ_F32", q_dtype);
+    if (context_len < 1)
+        return fail(VQ_ERR_INVALID_ARG, "context_len %d < 1 (softmax over no tokens)", context_len);
+    if (context_len > layout->capacity)
+        return fail(VQ_ERR_CAPACITY, "context_len %d exceeds capacity %d", context_len,
+                    layout->capacity);
+    if (num_splits < 0) return fail(VQ_ERR_INVALID_ARG, "num_splits %d < 0", num_splits);
+    VQ_REQUIRE_PTR(q);
+    VQ_REQUIRE_PTR(lambda);
+    VQ_REQUIRE_PTR(cb_k);
+    VQ_REQUIRE_PTR(cb_v);
+    VQ_REQUIRE_PTR(codes_k);
+    VQ_REQUIRE_PTR(codes_v);
+    VQ_REQUIRE_PTR(out);
+    const SplitPlan p =
+        plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
+    const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, p.num_splits);
+    const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
+                                context_len, p.num_splits, p.tokens_per_split};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(vqkv::launch_vq_attention_splits(shape, layout->k_code_bits, q,
+                                                     q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                                                     codes_k, codes_v, part, s),
+                    "decode_attention split launch");
+    if (st) return st;
+    return hip_status(vqkv::launch_merge_splits(batch, num_q_heads, p.num_splits, part, out, s),
+                      "decode_attention merge launch");
+}
+
+size_t vq_fp16_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t context_len, int32_t num_splits) {
+    if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || context_len < 1) return 0;
+    const SplitPlan p = plan_splits(batch * num_kv_heads, context_len, num_splits, vqkv::kFp16Tile);
+    return partials_bytes(batch, num_q_heads, p.num_splits);
+}
+
+int vq_fp16_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t capacity, int32_t context_len, int32_t num_splits,
+                             float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_kv_heads < 1 || num_kv_heads > 65535)
+        return fail(VQ_ERR_INVALID_ARG, "num_kv_heads %d out of range [1, 65535]", num_kv_heads);
+    int st = check_heads(batch, num_q_heads, num_kv_heads);
+    if (st) return st;
+    if (capacity < 1) return fail(VQ_ERR_INVALID_ARG, "capacity %d < 1", capacity);
+    if (context_len < 1)
+        return fail(VQ_ERR_INVALID_ARG, "context_len %d < 1 (softmax over no tokens)", context_len);
+    if (context_len > capacity)
+        return fail(VQ_ERR_CAPACITY, "context_len %d exceeds capacity %d", context_len, capacity);
+    if (num_splits < 0) return fail(VQ_ERR_INVALID_ARG, "num_splits %d < 0", num_splits);
+    VQ_REQUIRE_PTR(q);
+    VQ_REQUIRE_PTR(k);
+    VQ_REQUIRE_PTR(v);
+    VQ_REQUIRE_PTR(out);
+    const SplitPlan p = plan_splits(batch * num_kv_heads, context_len, num_splits, vqkv::kFp16Tile);
+    const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, p.num_splits);
+    const vqkv::AttnShape shape{batch, num_q_heads, num_kv_heads, capacity, context_len,
+                                p.num_splits, p.tokens_per_split};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(vqkv::launch_fp16_attention_splits(shape, q, k, v, part, s),
+                    "fp16 attention split launch");
+    if (st) return st;
+    return hip_status(vqkv::launch_merge_splits(batch, num_q_heads, p.num_splits, part, out, s),
+                      "fp16 attention merge launch");
+}
+
+}  // extern "C"
