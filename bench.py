@@ -1,0 +1,237 @@
+"""Benchmark: one decode step over a VQ-KV cache layer on one MI355X.
+
+A step is the whole hot path over one batch: append one new token per
+(sequence, KV head) with the HIP encoder (into the last slot of the cache),
+then decode attention of every query head over the full context.  The
+default workload is the Llama-3.1-8B-shaped layer at 196608 tokens (batch 1,
+32 query heads over 8 KV heads, D = 128, 2-bit K and V: 8-bit codes over
+4-dim sub-vectors, 256-entry fp16 codebooks).
+
+Inputs are seeded synthetic tensors (see ``workloads``); the cache is drawn
+directly as uniform codes.  Timing keeps every input resident in HBM and
+rotates over enough independent copies of the cache (>= 1 GiB in total) that
+the 256 MB Infinity Cache cannot hold the codes between steps.
+
+Prints one JSON line (rank 0).  Only N = 1 GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "VQ-KV decode attn: KV tokens/s per layer + achieved HBM GB/s (% of peak)"
+HBM_PEAK_GBPS = 8000.0
+COLD_BYTES = 1 << 30
+
+
+def algorithmic_bytes(wl: W.Workload, context_len: int) -> dict:
+    """Bytes one decode-attention launch must move at minimum.
+
+    Per KV token per KV head: (D/d) (bk + bv) / 8 bytes of codes (VecInfer
+    page, Background: (d_h/d)(b/8) index bytes per vector), i.e. 64 B for 8-bit
+    K and V codes; plus once per launch the fp16 codebooks (2^b x d x 2 bytes
+    each), q, lambda and the fp32 output."""
+    units = wl.batch * wl.num_kv_heads * context_len
+    per_unit = wl.num_sub * (wl.k_bits + wl.v_bits) // 8
+    fixed = (wl.num_kv_heads * ((1 << wl.k_bits) + (1 << wl.v_bits)) * wl.sub_dim * 2
+             + wl.batch * wl.num_q_heads * wl.head_dim * 2
+             + wl.num_kv_heads * wl.head_dim * 4
+             + wl.batch * wl.num_q_heads * wl.head_dim * 4)
+    return {"per_unit": per_unit, "units": units, "total": per_unit * units + fixed}
+
+
+def fp16_bytes(wl: W.Workload, context_len: int) -> int:
+    """K and V in fp16: 2 x D x 2 bytes per KV token per KV head (VecInfer page,
+    Background: an uncompressed d_h-vector takes d_h x 2 bytes), plus q/out."""
+    return (wl.batch * wl.num_kv_heads * context_len * 2 * wl.head_dim * 2
+            + wl.batch * wl.num_q_heads * wl.head_dim * (2 + 4))
+
+
+def cpu_baseline(wl: W.Workload, heads: int) -> dict:
+    """The fp64 oracle, as is, on `heads` KV heads of sequence 0 at the full
+    context, scaled to KV tokens/s per layer."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    n = wl.context_len
+    q = W.queries(wl.config_id, 0, wl.num_q_heads).astype(np.float16)
+    g = wl.group
+    t0 = time.perf_counter()
+    for h in range(heads):
+        lam = W.random_lambda(wl.config_id, h)
+        cbk = W.random_codebook(wl.config_id, h, "k", 1 << wl.k_bits, 0.6)
+        cbv = W.random_codebook(wl.config_id, h, "v", 1 << wl.v_bits, 1.0, 1 / 32)
+        ck = W.random_code_rows(wl.config_id, 0, h, "k", n, wl.k_row_bytes)
+        cv = W.random_code_rows(wl.config_id, 0, h, "v", n, wl.v_row_bytes)
+        oracle.decode_attention_head(q[h * g:(h + 1) * g], lam, cbk, cbv, ck, cv,
+                                     wl.k_bits, wl.v_bits)
+    dt = time.perf_counter() - t0
+    per_layer = dt / heads * wl.num_kv_heads
+    threads = max([1] + [p.get("num_threads", 1) for p in threadpool_info()])
+    return {"value": wl.batch * n / (per_layer * wl.batch), "unit": "KV tokens/s per layer",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {wl.num_kv_heads} KV heads of sequence 0 at N={n} "
+                      f"({dt:.1f} s), scaled to the layer"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4, help="workload id (see workloads)")
+    ap.add_argument("--splits", type=int, default=0, help="split count (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 comparator")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a measured configuration",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import vector_quantized_bit_amd as vq
+
+    wl = W.WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n, cap, bsz, hkv, hq = wl.context_len, wl.context_len, wl.batch, wl.num_kv_heads, wl.num_q_heads
+    st = np.float16 if wl.qkv_dtype == "f16" else np.float32
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- inputs (resident in HBM before timing) ---------------------------
+    q = t(np.stack([W.queries(wl.config_id, b, hq) for b in range(bsz)]).astype(st))
+    lam = t(np.stack([W.random_lambda(wl.config_id, g) for g in range(hkv)]))
+    cb_k = t(np.stack([W.random_codebook(wl.config_id, g, "k", 1 << wl.k_bits, 0.6)
+                       for g in range(hkv)]))
+    cb_v = t(np.stack([W.random_codebook(wl.config_id, g, "v", 1 << wl.v_bits, 1.0, 1 / 32)
+                       for g in range(hkv)]))
+    ck0 = torch.empty((bsz, hkv, cap, wl.k_row_bytes), dtype=torch.uint8, device=dev)
+    cv0 = torch.empty((bsz, hkv, cap, wl.v_row_bytes), dtype=torch.uint8, device=dev)
+    for b in range(bsz):
+        for g in range(hkv):
+            ck0[b, g] = t(W.random_code_rows(wl.config_id, b, g, "k", cap, wl.k_row_bytes))
+            cv0[b, g] = t(W.random_code_rows(wl.config_id, b, g, "v", cap, wl.v_row_bytes))
+    k_new = t(np.stack([np.stack([W.kv_rows(wl.config_id, b, g, "k", 1, append=True)
+                                  for g in range(hkv)]) for b in range(bsz)]).astype(st))
+    v_new = t(np.stack([np.stack([W.kv_rows(wl.config_id, b, g, "v", 1, append=True)
+                                  for g in range(hkv)]) for b in range(bsz)]).astype(st))
+    cache_bytes = ck0.numel() + cv0.numel()
+    copies = max(1, -(-COLD_BYTES // cache_bytes))
+    caches = [(ck0, cv0)] + [(ck0.clone(), cv0.clone()) for _ in range(copies - 1)]
+    out = torch.empty((bsz, hq, 128), dtype=torch.float32, device=dev)
+    splits = args.splits or vq.decode_attention_default_splits(ck0, cv0, cb_k, cb_v, bsz, hq, n)
+    ws = torch.zeros(vq.decode_attention_workspace_bytes(ck0, cv0, cb_k, cb_v, bsz, hq, n, splits),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        ck, cv = caches[i % copies]
+        vq.encode_append(k_new, v_new, lam, cb_k, cb_v, ck, cv, n - 1)
+        ev_a[i].record()
+        vq.decode_attention(q, lam, cb_k, cb_v, ck, cv, n, splits, out, ws)
+        ev_b[i].record()
+
+    steps, warm = args.steps, args.warmup
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(max(steps, warm))]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(max(steps, warm))]
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / steps
+    attn_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(steps)]
+    attn_us = float(np.mean(attn_ms) * 1e3)
+    attn_med_us = float(np.median(attn_ms) * 1e3)
+    assert torch.isfinite(out).all().item()
+
+    ab = algorithmic_bytes(wl, n)
+    achieved = ab["total"] / (attn_us * 1e-6) / 1e9
+    tokens = bsz * n
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "KV tokens/s per layer",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": bsz, "context_len": n, "q_heads": hq,
+                   "kv_heads": hkv, "head_dim": 128, "k_code_bits": wl.k_bits,
+                   "v_code_bits": wl.v_bits, "sub_dim": 4, "append_tokens_per_step": 1,
+                   "num_splits": splits, "cold_cache_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "vq_attention_mfma_kernel (one launch: splits + merge)",
+                     "bytes_per_launch": ab["total"], "bytes_per_unit": ab["per_unit"],
+                     "units_per_launch": ab["units"], "avg_launch_us": attn_us,
+                     "median_launch_us": attn_med_us},
+        "step_hbm_gbps": ab["total"] / (ms_step * 1e-3) / 1e9,
+    }
+
+    if not args.no_fp16:
+        fk = torch.empty((bsz, hkv, cap, 128), dtype=torch.float16, device=dev)
+        fv = torch.empty_like(fk)
+        g16 = torch.Generator(device=dev)
+        g16.manual_seed(wl.config_id)
+        fk.normal_(generator=g16)
+        fv.normal_(generator=g16)
+        fcopies = max(1, -(-COLD_BYTES // (2 * fk.numel() * 2)))
+        fcaches = [(fk, fv)] + [(fk.clone(), fv.clone()) for _ in range(fcopies - 1)]
+        q16 = q.to(torch.float16)
+        fws = torch.empty(vq.fp16_attention_workspace_bytes(bsz, hq, hkv, n), dtype=torch.uint8,
+                          device=dev)
+        fout = torch.empty_like(out)
+        reps = max(10, steps // 2)
+        fa = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        fb = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(3):
+            vq.fp16_decode_attention(q16, *fcaches[i % fcopies], n, out=fout, workspace=fws)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            fa[i].record()
+            vq.fp16_decode_attention(q16, *fcaches[i % fcopies], n, out=fout, workspace=fws)
+            fb[i].record()
+        torch.cuda.synchronize()
+        f_us = float(np.mean([fa[i].elapsed_time(fb[i]) for i in range(reps)]) * 1e3)
+        result["fp16_comparator"] = {
+            "avg_launch_us": f_us, "gbps": fp16_bytes(wl, n) / (f_us * 1e-6) / 1e9,
+            "vq_speedup": f_us / attn_us, "cold_cache_copies": fcopies}
+        del fcaches, fk, fv
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_heads, wl.num_kv_heads))
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

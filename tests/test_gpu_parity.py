@@ -85,6 +85,24 @@ def test_bitwise_reproducible(tiny):
     np.testing.assert_array_equal(a, b)
 
 
+def test_workspace_is_reusable_and_left_zeroed(tiny):
+    c, d, ref = tiny
+    n = c.context_len
+    args = (d["codes_k"], d["codes_v"], d["cb_k"], d["cb_v"], 1, 4, n)
+    ws = torch.zeros(vq.decode_attention_workspace_bytes(*args), dtype=torch.uint8, device=DEV)
+    outs = []
+    for splits in (0, 3, 0):
+        o = vq.decode_attention(d["q"], d["lam"], d["cb_k"], d["cb_v"], d["codes_k"],
+                                d["codes_v"], n, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        # the split-completion tickets at the head of the workspace are zero again
+        assert int(ws[:256].count_nonzero()) == 0
+        outs.append(o.cpu().numpy().astype(np.float64))
+    np.testing.assert_array_equal(outs[0], outs[2])
+    for o in outs:
+        assert_close(o, ref, "config1 reused workspace")
+
+
 @pytest.mark.parametrize("n", [1, 2, 7, 255, 256, 257, 511, 700, 1024])
 def test_ragged_context_lengths(tiny, n):
     c, d, _ = tiny

@@ -82,6 +82,10 @@ SplitPlan plan_splits(int streams, int context_len, int requested, int tile) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+size_t tickets_bytes(int batch, int num_kv_heads) {
+    return align256(static_cast<size_t>(batch) * num_kv_heads * sizeof(uint32_t));
+}
+
 size_t partials_bytes(int batch, int num_q_heads, int num_splits) {
     const size_t n = static_cast<size_t>(batch) * num_q_heads * num_splits;
     return 2 * align256(n * sizeof(float)) + align256(n * vqkv::kHeadDim * sizeof(float));
@@ -182,7 +186,7 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
         return 0;
     const SplitPlan p =
         plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
-    return partials_bytes(batch, num_q_heads, p.num_splits);
+    return tickets_bytes(batch, layout->num_kv_heads) + partials_bytes(batch, num_q_heads, p.num_splits);
 }
 
 int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
@@ -210,22 +214,22 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
     VQ_REQUIRE_PTR(out);
     const SplitPlan p =
         plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
-    const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
+    const size_t tk = tickets_bytes(batch, layout->num_kv_heads);
+    const size_t need = tk + partials_bytes(batch, num_q_heads, p.num_splits);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
     if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, p.num_splits);
+    uint32_t* tickets = static_cast<uint32_t*>(workspace);
+    const vqkv::Partials part =
+        carve_partials(static_cast<char*>(workspace) + tk, batch, num_q_heads, p.num_splits);
     const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
                                 context_len, p.num_splits, p.tokens_per_split};
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    st = hip_status(vqkv::launch_vq_attention_splits(shape, layout->k_code_bits, q,
-                                                     q_dtype == VQ_F32, lambda, cb_k, cb_v,
-                                                     codes_k, codes_v, part, s),
-                    "decode_attention split launch");
-    if (st) return st;
-    return hip_status(vqkv::launch_merge_splits(batch, num_q_heads, p.num_splits, part, out, s),
-                      "decode_attention merge launch");
+    return hip_status(vqkv::launch_vq_attention_fused(shape, layout->k_code_bits, q,
+                                                      q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                                                      codes_k, codes_v, part, tickets, out,
+                                                      static_cast<hipStream_t>(stream)),
+                      "decode_attention launch");
 }
 
 size_t vq_fp16_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
