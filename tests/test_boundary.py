@@ -104,8 +104,9 @@ def test_workspace_query_matches_partials_layout(lib):
     tickets = a256(4 * 1 * 8)
     assert need == tickets + 2 * a256(4 * n) + a256(4 * 128 * n)
     # explicit split requests are clamped so that no split is empty
-    one = lib.vq_decode_attention_workspace_bytes(ctypes.byref(layout), 1, 32, 300, 10 ** 6)
-    n = 32 * 2                                       # 300 tokens -> at most 2 tiles of 256
+    # (splits are whole sweeps of 512 tokens: 1100 tokens allow at most 3)
+    one = lib.vq_decode_attention_workspace_bytes(ctypes.byref(layout), 1, 32, 1100, 10 ** 6)
+    n = 32 * 3
     assert one == a256(4 * 8) + 2 * a256(4 * n) + a256(4 * 128 * n)
     assert lib.vq_decode_attention_workspace_bytes(None, 1, 32, 100, 0) == 0
 

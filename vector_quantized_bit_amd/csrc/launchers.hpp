@@ -19,11 +19,6 @@ hipError_t launch_transform_query(const void* q, bool q_f32, const float* lambda
                                   int num_q_heads, int num_kv_heads, float* q_tilde,
                                   hipStream_t stream);
 
-hipError_t launch_vq_attention_splits(const AttnShape& s, int k_bits, const void* q, bool q_f32,
-                                      const float* lambda, const uint16_t* cb_k,
-                                      const uint16_t* cb_v, const uint8_t* codes_k,
-                                      const uint8_t* codes_v, Partials part, hipStream_t stream);
-
 // Fused split-K attention + cross-split merge on the matrix cores.  `tickets`
 // holds batch * num_kv_heads zero-initialised counters; the kernel leaves them
 // zero again.
@@ -46,7 +41,7 @@ hipError_t launch_fp16_attention_splits(const AttnShape& s, const uint16_t* q, c
 
 // Tokens one workgroup of the VQ split kernel processes per tile; split
 // lengths are multiples of it.
-constexpr int kVqTile = 256;       // = waves per workgroup x tokens per wave tile
+constexpr int kVqTile = 512;       // = waves per workgroup x tokens per wave tile
 constexpr int kFp16Tile = 128;
 
 }  // namespace vqkv

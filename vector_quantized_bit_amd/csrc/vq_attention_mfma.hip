@@ -6,27 +6,32 @@
 // Appendix (FlashAttention block recurrence, Algorithm 1): running max m,
 // running sum l, rescaled output accumulator, final o / l.
 //
-// How it maps to gfx950 (one workgroup = 8 waves = one contiguous token range
-// of one (sequence, KV head); one wave = 32-token tiles):
+// How it maps to gfx950.  One workgroup (16 waves, one per CU) streams one
+// contiguous token range of one (sequence, KV head); each wave takes 32-token
+// tiles in turn.
 //  * Both products are dense contractions once a centroid is looked up, so
 //    both run on v_mfma_f32_16x16x32_f16.  The 16 MFMA rows are (head, part):
-//    every fp32 operand that is not exact in fp16 (q~ and p) is split into
-//    hi = fp16(x) and lo = fp16(x - hi) and the two rows are summed after the
-//    product; codebook entries are fp16 already.  Accuracy is that of fp32.
-//  * Scores: B operand = the 8 fp16 values of two key centroids per lane,
-//    read from LDS with one 8-byte gather each.
+//    q~ and p, the operands that are not exact in fp16, are split into
+//    hi = fp16(x) and lo = fp16(x - hi) on separate rows that are summed
+//    after the product; codebook entries are fp16 already.  Row 4j + i holds
+//    (head 2j, hi), (head 2j+1, hi), (head 2j, lo), (head 2j+1, lo) for
+//    i = 0..3, so G <= 8 heads fit; rows of heads >= G are zero.
+//  * Scores: the B operand is two key centroids (8 fp16) per lane, each one
+//    8-byte LDS gather.
 //  * Values: the MFMA wants 8 tokens x 1 channel per lane, a gather gives
 //    1 token x 4 channels.  ds_read_b64_tr_b16 does both at once: every lane
-//    supplies the address of one centroid and the hardware returns, to lane
-//    16G+4a+e, channel e of the centroids fetched by lanes 16G+4k+a, k=0..3.
-//  * The codebooks live in a 64 KiB LDS table with one 256-byte row per code:
-//    16 copies of the key centroid then 16 copies of the value centroid, so
-//    lane n of every 16-lane group reads its own copy (slot n): the gathers
-//    are bank-conflict free for any codes, and the address
-//    (code << 8) | slot is one v_perm_b32 of the loaded code bytes.  (12-bit
-//    key codebooks, 4096 x 8 B, fill the 16 key slots of all 256 rows.)
-//  * Code rows stay token-major in HBM; every load is 8 contiguous bytes per
-//    lane and the scores and values each read a wave's tile once.
+//    supplies the address of one centroid and lane 16G+4a+e receives channel
+//    e of the centroids fetched by lanes 16G+4k+a, k = 0..3.
+//  * Codebooks live in LDS as two 64 KiB tables, keys then values, with one
+//    256-byte row per code holding 32 copies of the centroid: lane l reads
+//    copy l mod 32, so the 32 lanes one LDS cycle serves always hit 64
+//    distinct banks — no bank conflicts for any codes — and the address
+//    (code << 8) | slot is a single v_perm_b32 of the loaded code bytes.
+//    (A 12-bit key codebook, 4096 x 8 B, is stored once, unreplicated.)
+//  * Code rows stay token-major in HBM.  Loads are raw buffer loads of 8
+//    (or 12) contiguous bytes per lane: the split's rows form the buffer
+//    range, so rows past the split's end read as zero without any clamp.
+//    Two register sets alternate so one tile of loads is always in flight.
 //  * The cross-split log-sum-exp merge runs in the same kernel: the last
 //    workgroup of each (sequence, KV head) to finish (device-scope atomic
 //    ticket) merges all split partials for its G heads.
@@ -39,20 +44,18 @@ namespace {
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 8;
-constexpr int kTok = 32;                  // tokens per wave tile
-constexpr float kTau = 8.0f;              // lazy-rescale slack (log2 units)
-constexpr int kRow = 256;                 // bytes per code row of the LDS table
-constexpr int kVOff = 128;                // value slots start here in a row
-
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-// ds_read_b64_tr_b16 at an LDS byte address
-__device__ __forceinline__ half4_t read_tr16(const uint8_t* p) {
-    return __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p));
-}
+constexpr int kWaves = 16;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTok = 32;                  // tokens per wave tile
+constexpr int kStride = kWaves * kTok;    // tokens per workgroup sweep
+constexpr float kTau = 8.0f;              // lazy-rescale slack (log2 units)
+constexpr int kTable = 65536;             // bytes of one codebook table
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9
+
+static_assert(kStride == kVqTile, "split lengths are multiples of one sweep");
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -76,44 +79,54 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
-// LDS address (code << 8) | slot, code = byte k of w: one v_perm_b32
+// LDS address bytes [slot.b2 : code : slot.b0], code = byte K of w
 template <int K>
 __device__ __forceinline__ uint32_t row_addr(uint32_t w, uint32_t slot) {
-    return __builtin_amdgcn_perm(w, slot, 0x0C0C0000u | ((4u + K) << 8));
+    return __builtin_amdgcn_perm(w, slot, 0x0C020000u | ((4u + K) << 8));
 }
 
 __device__ __forceinline__ half8_t cat(uint2 a, uint2 b) {
     return __builtin_bit_cast(half8_t, make_uint4(a.x, a.y, b.x, b.y));
 }
+__device__ __forceinline__ half8_t cat(half4_t a, half4_t b) {
+    return half8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
-// 2^x with the hardware exponential (results below 2^-126 flush to 0, which
-// only drops weights that are negligible next to the running sum >= 1)
+__device__ __forceinline__ half4_t read_tr16(const uint8_t* p) {
+    return __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p));
+}
+
+// 2^x on the hardware exponential (results below 2^-126 flush to 0, which
+// only drops weights negligible next to the running sum, itself >= 1)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float rescale_factor(float m_old, float m_new) {
-    return (m_new == -INFINITY) ? 1.f : fast_exp2(m_old - m_new);
+    return (m_old == m_new) ? 1.f : fast_exp2(m_old - m_new);
 }
 
-// hi/lo fp16 pair of x (two halves packed: lo half = hi part, high half = lo part)
-__device__ __forceinline__ uint32_t split_hi_lo(float x) {
-    const _Float16 hi = static_cast<_Float16>(x);
-    const _Float16 lo = static_cast<_Float16>(x - static_cast<float>(hi));
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) << 16);
+__device__ __forceinline__ uint32_t pack_rtz(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
-// the 8 key codes of positions 8*grp .. 8*grp+7 of one token
+__device__ __forceinline__ float lo_half_to_float(uint32_t w) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float hi_half_to_float(uint32_t w) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// The 8 key codes of positions 8 grp .. 8 grp + 7 of one token, and the LDS
+// address of the key centroid of position 8 grp + I.
 template <int KBITS>
 struct KChunk;
 
 template <>
 struct KChunk<8> {
     uint2 w;
-    __device__ void load(const uint8_t* row, int grp) {
-        w = *reinterpret_cast<const uint2*>(row + 8 * grp);
+    __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        w = make_uint2(v[0], v[1]);
     }
-    __device__ void clear() { w = make_uint2(0, 0); }
-    // LDS address of the key centroid for position 8*grp + i
     template <int I>
     __device__ uint32_t addr(uint32_t slot) const {
         return row_addr<I & 3>(I < 4 ? w.x : w.y, slot);
@@ -123,15 +136,14 @@ struct KChunk<8> {
 template <>
 struct KChunk<12> {
     uint32_t w0, w1, w2;   // 96 bits: 8 codes of 12 bits, little-endian
-    __device__ void load(const uint8_t* row, int grp) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(row + 12 * grp);
-        w0 = p[0];
-        w1 = p[1];
-        w2 = p[2];
+    __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+        w0 = v[0];
+        w1 = v[1];
+        w2 = v[2];
     }
-    __device__ void clear() { w0 = w1 = w2 = 0; }
     template <int I>
-    __device__ uint32_t addr(uint32_t slot) const {
+    __device__ uint32_t addr(uint32_t) const {
         constexpr int bit = 12 * I, lo = bit >> 5, sh = bit & 31;
         const uint32_t a = lo == 0 ? w0 : (lo == 1 ? w1 : w2);
         uint32_t code;
@@ -141,16 +153,106 @@ struct KChunk<12> {
             const uint32_t b = lo == 0 ? w1 : w2;
             code = __builtin_amdgcn_alignbit(b, a, sh) & 0xfffu;
         }
-        // entry e of a 4096-entry table sits at row e >> 4, key slot e & 15
-        (void)slot;
-        return ((code & 0xff0u) << 4) | ((code & 0xfu) << 3);
+        return code << 3;   // unreplicated 4096 x 8 B table at the start of LDS
     }
 };
+
+// Log-sum-exp merge of the S split partials of G query heads by one
+// workgroup: out[h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s.  Loads are issued eight splits at a time per thread so their
+// latencies overlap.  scratch: LDS floats for [G][S] weights and the slice sums.
+constexpr int kMaxMergeSplits = 512;   // the split planner never exceeds this
+
+template <int G>
+__device__ void merge_splits_block(const Partials& part, size_t hbase, int num_splits,
+                                   float* __restrict__ out, float* scratch, float* red) {
+    constexpr int COLS = G * 32;                 // (head, 4-channel column) pairs
+    constexpr int J = kThreads / COLS;           // split slices
+    float* msh = scratch;                        // [G][S] split maxima
+    float* wsh = scratch + G * kMaxMergeSplits;  // [G][S] weights 2^(m_s - M)
+    float* osum = wsh + G * kMaxMergeSplits;     // [J][G][128] slice sums
+    float* lsum = osum + J * G * kHeadDim;       // [J][G]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    float mloc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
+    for (int s = tid; s < num_splits; s += kThreads) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float v = part.m[hbase + static_cast<size_t>(h) * num_splits + s];
+            msh[h * kMaxMergeSplits + s] = v;
+            mloc[h] = fmaxf(mloc[h], v);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float w = wave_max(mloc[h]);
+        if (lane == 0) red[wave * G + h] = w;
+    }
+    __syncthreads();
+    for (int i = tid; i < G * num_splits; i += kThreads) {
+        const int h = i / num_splits, s = i % num_splits;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w * G + h]);
+        const float ms = msh[h * kMaxMergeSplits + s];
+        wsh[h * kMaxMergeSplits + s] = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+    }
+    __syncthreads();
+
+    const int j = tid / COLS;
+    if (j < J) {
+        const int cg = tid % COLS, h = cg / 32, c4 = cg % 32;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        float lacc = 0.f;
+        const float* wrow = wsh + h * kMaxMergeSplits;
+        const size_t prow = hbase + static_cast<size_t>(h) * num_splits;
+        for (int s0 = j; s0 < num_splits; s0 += 8 * J) {
+            float4 o[8];
+            float l[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = s0 + u * J;
+                if (s < num_splits) {
+                    o[u] = reinterpret_cast<const float4*>(part.o + (prow + s) * kHeadDim)[c4];
+                    l[u] = part.l[prow + s];
+                } else {
+                    o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    l[u] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = s0 + u * J;
+                const float w = (s < num_splits) ? wrow[s] : 0.f;
+                acc.x += w * o[u].x;
+                acc.y += w * o[u].y;
+                acc.z += w * o[u].z;
+                acc.w += w * o[u].w;
+                lacc += w * l[u];
+            }
+        }
+        *reinterpret_cast<float4*>(osum + (j * G + h) * kHeadDim + 4 * c4) = acc;
+        if (c4 == 0) lsum[j * G + h] = lacc;
+    }
+    __syncthreads();
+    for (int i = tid; i < G * kHeadDim; i += kThreads) {
+        const int h = i / kHeadDim, d = i % kHeadDim;
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < J; ++jj) {
+            num += osum[(jj * G + h) * kHeadDim + d];
+            den += lsum[jj * G + h];
+        }
+        out[h * kHeadDim + d] = num / den;
+    }
+}
 
 }  // namespace
 
 template <int G, int KBITS>
-__global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
+__global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const void* __restrict__ q, int q_f32, const float* __restrict__ lambda,
     const uint16_t* __restrict__ cb_k, const uint16_t* __restrict__ cb_v,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v, int num_q_heads,
@@ -159,36 +261,70 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
     static_assert(G >= 1 && G <= 8, "2G MFMA rows");
     constexpr int KROW = kNumSub * KBITS / 8;
 
-    __shared__ __attribute__((aligned(16))) uint8_t tab[256 * kRow];
-    __shared__ __attribute__((aligned(16))) uint2 pbuf[kWaves][kTok * 4];   // [token][16 rows] fp16
+    __shared__ __attribute__((aligned(16))) uint8_t tab[2 * kTable];       // keys | values
+    __shared__ __attribute__((aligned(16))) uint2 pbuf[kWaves][kTok * 4];  // [token][16 rows] fp16
     __shared__ half8_t qa[4][64];
-    // q~ (fp32) lives in the p buffers during the prologue
-    static_assert(sizeof(float) * G * kHeadDim <= sizeof(uint2) * kWaves * kTok * 4, "qsh fits");
-    float (*qsh)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&pbuf[0][0]);
     __shared__ float wm[kWaves][G], wl[kWaves][G];
     __shared__ uint32_t last_flag;
+    // q~ (fp32) lives in the p buffers during the prologue
+    static_assert(sizeof(float) * G * kHeadDim <= sizeof(pbuf), "q~ fits in the p buffers");
+    float (*qsh)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&pbuf[0][0]);
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 4, n = lane & 15;
+    const int kq = n >> 2, aq4 = n & 3;   // fetch-lane split of n for the transposed reads
 
-    // ---- prologue: codebook table, q~ --------------------------------------
+    const int t_begin = split * tokens_per_split;
+    const int t_len = min(context_len, t_begin + tokens_per_split) - t_begin;
+    const size_t row0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + t_begin;
+    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(codes_k + row0 * KROW), 0, t_len * KROW, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(codes_v + row0 * kNumSub), 0, t_len * kNumSub, kBufferWord3);
+    // per-lane byte offsets of the chunks inside a tile
+    const uint32_t koff0 = static_cast<uint32_t>(n * KROW + (KBITS == 8 ? 8 : 12) * grp);
+    const uint32_t koff1 = koff0 + 16 * KROW;
+    const uint32_t voff0 = static_cast<uint32_t>((8 * grp + kq) * kNumSub + 8 * aq4);
+    const uint32_t voff1 = voff0 + 4 * kNumSub;
+
+    // the first tile's code loads go out before the prologue
+    KChunk<KBITS> kA[2], kB[2];
+    uint2 vA[2], vB[2];
+    // (the whole offset goes in the VGPR operand: the buffer range check
+    // covers the VGPR offset, not the scalar one)
+    auto load_tile = [&](int rel, KChunk<KBITS>* kk_, uint2* vv_) {
+        const uint32_t ks = static_cast<uint32_t>(rel * KROW);
+        const uint32_t vs = static_cast<uint32_t>(rel * kNumSub);
+        kk_[0].load(krsrc, koff0 + ks, 0);
+        kk_[1].load(krsrc, koff1 + ks, 0);
+        const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff0 + vs, 0, 0);
+        const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff1 + vs, 0, 0);
+        vv_[0] = make_uint2(v0[0], v0[1]);
+        vv_[1] = make_uint2(v1[0], v1[1]);
+    };
+    int rel = wave * kTok;
+    if (rel < t_len) load_tile(rel, kA, vA);
+
+    // ---- prologue: codebook tables, q~ -------------------------------------
     {
         const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
         const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
         if constexpr (KBITS == 8) {
-            const int code = tid >> 1;
-            const uint2 c = (tid & 1) ? vsrc[code] : ksrc[code];
-            uint4* dst = reinterpret_cast<uint4*>(tab + code * kRow + (tid & 1) * kVOff);
+            // thread: code = tid / 4, table = (tid / 2) % 2, slots 16 (tid % 2) .. + 15
+            const int code = tid >> 2, which = (tid >> 1) & 1, half = tid & 1;
+            const uint2 c = which ? vsrc[code] : ksrc[code];
+            uint4* dst = reinterpret_cast<uint4*>(tab + which * kTable + code * 256 + half * 128);
             const uint4 cc = make_uint4(c.x, c.y, c.x, c.y);
 #pragma unroll
             for (int s = 0; s < 8; ++s) dst[s] = cc;
         } else {
-            for (int e = tid; e < 4096; e += kWaves * 64)
-                *reinterpret_cast<uint2*>(tab + (e >> 4) * kRow + (e & 15) * 8) = ksrc[e];
-            if (tid < 256) {
-                const uint2 c = vsrc[tid];
-                uint4* dst = reinterpret_cast<uint4*>(tab + tid * kRow + kVOff);
+            for (int e = tid; e < 4096; e += kThreads)
+                *reinterpret_cast<uint2*>(tab + e * 8) = ksrc[e];
+            if (tid < 512) {
+                const int code = tid >> 1, half = tid & 1;
+                const uint2 c = vsrc[code];
+                uint4* dst = reinterpret_cast<uint4*>(tab + kTable + code * 256 + half * 128);
                 const uint4 cc = make_uint4(c.x, c.y, c.x, c.y);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) dst[s] = cc;
@@ -204,8 +340,8 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
             x1 = v.y;
         } else {
             const uint32_t w = reinterpret_cast<const uint32_t*>(q)[vec * (kHeadDim / 2) + lane];
-            x0 = half_bits_to_float(static_cast<uint16_t>(w & 0xffffu));
-            x1 = half_bits_to_float(static_cast<uint16_t>(w >> 16));
+            x0 = lo_half_to_float(w);
+            x1 = hi_half_to_float(w);
         }
         const float2 l = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
         x0 *= l.x;
@@ -215,71 +351,42 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
         qsh[wave][2 * lane + 1] = x1 * kScoreScaleLog2;
     }
     __syncthreads();
-
-    // score A operand, shared by all waves through LDS: lane (16 grp + r)
-    // holds row r = 2h + part of q~ for dims 32 grp + 8 kk + e (K-step kk,
-    // element e); part 0 = hi, 1 = lo; rows of heads >= G are zero
+    // score A operand, shared by every wave: lane (16 grp + r) holds row r of
+    // q~ for dims 32 grp + 8 kk + e (K-step kk, element e)
     if (wave == 0) {
         const int r = n;
-        const int h = r >> 1;
+        const int h = 2 * (r >> 2) + (r & 1);
+        const bool lo_part = (r & 2) != 0;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             half8_t a;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float x = 0.f;
-                if (h < G) x = qsh[h][32 * grp + 8 * kk + e];
+                const float x = (h < G) ? qsh[h][32 * grp + 8 * kk + e] : 0.f;
                 const _Float16 hi = static_cast<_Float16>(x);
-                a[e] = (r & 1) ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
+                a[e] = lo_part ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
             }
             qa[kk][lane] = a;
         }
     }
     __syncthreads();
 
-    const int t_begin = split * tokens_per_split;
-    const int t_end = min(context_len, t_begin + tokens_per_split);
-    const size_t row0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity;
-    const uint8_t* kbase = codes_k + row0 * KROW;
-    const uint8_t* vbase = codes_v + row0 * kNumSub;
-    const uint32_t kslot = static_cast<uint32_t>(n) * 8;
-    const uint32_t vslot = kVOff + static_cast<uint32_t>(n) * 8;
-    const int kq = n >> 2, aq4 = n & 3;   // fetch-lane split of n for the transposed reads
-
-    // heads of this lane's MFMA output rows: rows 4 grp .. 4 grp + 3 = (hA hi,
-    // hA lo, hB hi, hB lo)
+    // lane state: rows 4 grp .. 4 grp + 3 = (hA hi, hB hi, hA lo, hB lo)
     const int hA = 2 * grp, hB = 2 * grp + 1;
-    const bool validA = hA < G, validB = hB < G;
-
-    float mA = -INFINITY, mB = -INFINITY, lA = 0.f, lB = 0.f;
+    // heads >= G start at m = +inf, so their p = 2^(s - m) is 0 with no mask
+    float mA = hA < G ? -INFINITY : INFINITY;
+    float mB = hB < G ? -INFINITY : INFINITY;
+    float lA = 0.f, lB = 0.f;
     float4_t oacc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
     uint2* pw = pbuf[wave];
     const uint8_t* pw_bytes = reinterpret_cast<const uint8_t*>(pw);
+    const uint32_t kslot = static_cast<uint32_t>(lane & 31) * 8;               // key table
+    const uint32_t vslot = 0x10000u | (static_cast<uint32_t>(lane & 31) * 8);  // value table
 
-    // Code loads: 8 bytes per lane per chunk, rows clamped into the split so
-    // every load is unconditional (masked tokens are discarded by the scores).
-    // (uniform 64-bit base of the split + 32-bit per-lane offsets)
-    const uint8_t* ksplit = kbase + static_cast<size_t>(t_begin) * KROW;
-    const uint8_t* vsplit = vbase + static_cast<size_t>(t_begin) * kNumSub;
-    const int t_last = t_end - 1 - t_begin;
-    auto load_tile = [&](int tile, KChunk<KBITS>* kk_, uint2* vv_) {
-        const int rel = tile - t_begin;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const uint32_t t = static_cast<uint32_t>(min(rel + 16 * sb + n, t_last));
-            kk_[sb].load(ksplit + t * KROW, grp);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t t = static_cast<uint32_t>(min(rel + 8 * grp + 4 * j + kq, t_last));
-            vv_[j] = *reinterpret_cast<const uint2*>(vsplit + t * kNumSub + 8 * aq4);
-        }
-    };
-
-    auto compute_tile = [&](int tile, const KChunk<KBITS>* kc, const uint2* vc) {
+    auto compute_tile = [&](int rel_, const KChunk<KBITS>* kc, const uint2* vc) {
         // ---- scores: 2 blocks of 16 tokens, 4 K-steps of 32 dims ------------
         float4_t sacc[2];
 #pragma unroll
@@ -310,9 +417,16 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
         float sA[2], sB[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-            const bool live = tile + 16 * sb + n < t_end;
-            sA[sb] = (validA && live) ? sacc[sb][0] + sacc[sb][1] : -INFINITY;
-            sB[sb] = (validB && live) ? sacc[sb][2] + sacc[sb][3] : -INFINITY;
+            sA[sb] = sacc[sb][0] + sacc[sb][2];
+            sB[sb] = sacc[sb][1] + sacc[sb][3];
+        }
+        if (rel_ + kTok > t_len) {               // the split's last, partial tile
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const bool live = rel_ + 16 * sb + n < t_len;
+                sA[sb] = live ? sA[sb] : -INFINITY;
+                sB[sb] = live ? sB[sb] : -INFINITY;
+            }
         }
         const float tA = row_max16(fmaxf(sA[0], sA[1]));
         const float tB = row_max16(fmaxf(sB[0], sB[1]));
@@ -326,34 +440,32 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 oacc[c][0] *= fA;
-                oacc[c][1] *= fA;
-                oacc[c][2] *= fB;
+                oacc[c][1] *= fB;
+                oacc[c][2] *= fA;
                 oacc[c][3] *= fB;
             }
         }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-            // 0 for masked tokens; padded rows (head >= G) stay 0 too
-            const float pA = validA ? fast_exp2(sA[sb] - mA) : 0.f;
-            const float pB = validB ? fast_exp2(sB[sb] - mB) : 0.f;
+            const float pA = fast_exp2(sA[sb] - mA);
+            const float pB = fast_exp2(sB[sb] - mB);
             lA += pA;
             lB += pB;
-            // token 16 sb + n, rows 4 grp .. 4 grp + 3
-            pw[(16 * sb + n) * 4 + grp] = make_uint2(split_hi_lo(pA), split_hi_lo(pB));
+            // hi parts round toward zero; the remainders are exact in fp32
+            const uint32_t hi = pack_rtz(pA, pB);
+            const uint32_t lo = pack_rtz(pA - lo_half_to_float(hi), pB - hi_half_to_float(hi));
+            pw[(16 * sb + n) * 4 + grp] = make_uint2(hi, lo);   // token 16 sb + n, rows 4 grp + i
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // V A operand: lane (16 grp + r) gets p rows r of tokens 8 grp .. 8 grp + 7
-        half8_t ap;
-        {
-            const half4_t x0 = read_tr16(pw_bytes + (8 * grp + kq) * 32 + aq4 * 8);
-            const half4_t x1 = read_tr16(pw_bytes + (8 * grp + 4 + kq) * 32 + aq4 * 8);
-            ap = half8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        }
+        // V A operand: lane (16 grp + r) gets p row r of tokens 8 grp .. 8 grp + 7
+        const half8_t ap = cat(read_tr16(pw_bytes + (8 * grp + kq) * 32 + aq4 * 8),
+                               read_tr16(pw_bytes + (8 * grp + 4 + kq) * 32 + aq4 * 8));
 
         // ---- values: 8 N-tiles of 16 channels, gathered 2 tiles at a time ------
+        // N-tile c, column 4a + e is channel 4 (8a + c) + e = 32 a + 4 c + e
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const uint32_t w0 = (q4 < 2) ? vc[0].x : vc[0].y;
@@ -371,57 +483,47 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
                 x[1][1] = read_tr16(tab + row_addr<3>(w1, vslot));
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const half8_t bv = half8_t{x[i][0][0], x[i][0][1], x[i][0][2], x[i][0][3],
-                                           x[i][1][0], x[i][1][1], x[i][1][2], x[i][1][3]};
-                oacc[2 * q4 + i] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, bv, oacc[2 * q4 + i], 0, 0, 0);
-            }
+            for (int i = 0; i < 2; ++i)
+                oacc[2 * q4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    ap, cat(x[i][0], x[i][1]), oacc[2 * q4 + i], 0, 0, 0);
         }
     };
 
-    // two register sets, alternating: load the next tile, then compute the
-    // current one, so one tile of code loads is always in flight
-    const int stride = kWaves * kTok;
-    int tile = t_begin + wave * kTok;
-    if (tile < t_end) {
-        KChunk<KBITS> kA[2], kB[2];
-        uint2 vA[2], vB[2];
-        load_tile(tile, kA, vA);
+    // two register sets, alternating: load the next tile, compute the current
+    if (rel < t_len) {
         for (;;) {
-            load_tile(tile + stride, kB, vB);
-            compute_tile(tile, kA, vA);
-            tile += stride;
-            if (tile >= t_end) break;
-            load_tile(tile + stride, kA, vA);
-            compute_tile(tile, kB, vB);
-            tile += stride;
-            if (tile >= t_end) break;
+            load_tile(rel + kStride, kB, vB);
+            compute_tile(rel, kA, vA);
+            rel += kStride;
+            if (rel >= t_len) break;
+            load_tile(rel + kStride, kA, vA);
+            compute_tile(rel, kB, vB);
+            rel += kStride;
+            if (rel >= t_len) break;
         }
     }
 
-    // ---- merge the 8 waves of the workgroup ----------------------------------
+    // ---- merge the waves of the workgroup ------------------------------------
     lA = row_sum16(lA);
     lB = row_sum16(lB);
     __syncthreads();                                      // everyone is done with tab
     float* obuf = reinterpret_cast<float*>(tab);          // [kWaves][G][128]
     if (n == 0) {
-        if (validA) { wm[wave][hA] = mA; wl[wave][hA] = lA; }
-        if (validB) { wm[wave][hB] = mB; wl[wave][hB] = lB; }
+        if (hA < G) { wm[wave][hA] = mA; wl[wave][hA] = lA; }
+        if (hB < G) { wm[wave][hB] = mB; wl[wave][hB] = lB; }
     }
-    // lane (16 grp + 4 a + e), tile c: channel 32 a + 4 c + e; rows (hA, hB) hi + lo
     {
         const int a = n >> 2, e = n & 3;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const int d = 32 * a + 4 * c + e;
-            if (validA) obuf[(wave * G + hA) * kHeadDim + d] = oacc[c][0] + oacc[c][1];
-            if (validB) obuf[(wave * G + hB) * kHeadDim + d] = oacc[c][2] + oacc[c][3];
+            if (hA < G) obuf[(wave * G + hA) * kHeadDim + d] = oacc[c][0] + oacc[c][2];
+            if (hB < G) obuf[(wave * G + hB) * kHeadDim + d] = oacc[c][1] + oacc[c][3];
         }
     }
     __syncthreads();
     const size_t pbase = (static_cast<size_t>(b) * num_q_heads + g * G) * num_splits + split;
-    for (int i = tid; i < G * kHeadDim; i += kWaves * 64) {
+    for (int i = tid; i < G * kHeadDim; i += kThreads) {
         const int h = i / kHeadDim, d = i % kHeadDim;
         float mx = -INFINITY;
 #pragma unroll
@@ -429,6 +531,7 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
         float ls = 0.f, os = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
+            // a wave that got no tile has m = -inf and weighs 0
             const float f = (wm[w][h] == -INFINITY) ? 0.f : exp2f(wm[w][h] - mx);
             ls += f * wl[w][h];
             os += f * obuf[(w * G + h) * kHeadDim + d];
@@ -441,7 +544,7 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
         }
     }
 
-    // ---- last workgroup of this (sequence, KV head) merges all splits -------
+    // ---- the last workgroup of this (sequence, KV head) merges all splits ---
     __syncthreads();
     if (tid == 0) {
         __threadfence();
@@ -451,23 +554,11 @@ __global__ __launch_bounds__(kWaves * 64, 4) void vq_attention_mfma_kernel(
     __syncthreads();
     if (last_flag == 0u) return;
     __threadfence();
-    const size_t hbase = (static_cast<size_t>(b) * num_q_heads + g * G) * num_splits;
-    for (int i = tid; i < G * kHeadDim; i += kWaves * 64) {
-        const int h = i / kHeadDim, d = i % kHeadDim;
-        const float* m = part.m + hbase + static_cast<size_t>(h) * num_splits;
-        const float* l = part.l + hbase + static_cast<size_t>(h) * num_splits;
-        const float* o = part.o + (hbase + static_cast<size_t>(h) * num_splits) * kHeadDim + d;
-        float mx = -INFINITY;
-        for (int s = 0; s < num_splits; ++s) mx = fmaxf(mx, m[s]);
-        float den = 0.f, num = 0.f;
-        for (int s = 0; s < num_splits; ++s) {
-            const float ms = m[s];
-            const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
-            den += f * l[s];
-            num += f * o[static_cast<size_t>(s) * kHeadDim];
-        }
-        out[(static_cast<size_t>(b) * num_q_heads + g * G + h) * kHeadDim + d] = num / den;
-    }
+    static_assert(sizeof(float) * (2 * G * kMaxMergeSplits + (kThreads / (G * 32)) * G * (kHeadDim + 1)) <=
+                      sizeof(tab), "merge scratch fits in the tables");
+    merge_splits_block<G>(part, (static_cast<size_t>(b) * num_q_heads + g * G) * num_splits,
+                          num_splits, out + (static_cast<size_t>(b) * num_q_heads + g * G) * kHeadDim,
+                          reinterpret_cast<float*>(tab), &wm[0][0]);
     if (tid == 0) tickets[static_cast<size_t>(b) * num_kv_heads + g] = 0u;   // ready for the next call
 }
 
@@ -478,12 +569,12 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
                          const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                          const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
                          uint32_t* tickets, float* out, hipStream_t stream) {
-#define VQKV_LAUNCH(GG)                                                                        \
-    case GG:                                                                                   \
-        hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS>), grid, dim3(kWaves * 64), 0,  \
-                           stream, q, q_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,    \
-                           s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,           \
-                           s.num_splits, s.tokens_per_split, part, tickets, out);              \
+#define VQKV_LAUNCH(GG)                                                                       \
+    case GG:                                                                                  \
+        hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS>), grid, dim3(kThreads), 0,    \
+                           stream, q, q_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,   \
+                           s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
+                           s.num_splits, s.tokens_per_split, part, tickets, out);             \
         break;
     switch (group) {
         VQKV_LAUNCH(1)

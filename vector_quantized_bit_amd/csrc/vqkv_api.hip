@@ -34,7 +34,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Device-independent plan: the same shape always gets the same split count,
 // so results are reproducible across devices and runs.
-constexpr int kTargetWorkgroups = 512;   // two per CU of a 256-CU MI355X
+constexpr int kTargetWorkgroups = 256;   // one 16-wave workgroup per CU of a 256-CU MI355X
 constexpr int kMaxGroup = 8;
 
 int check_layout(const vq_layout* L) {
@@ -70,8 +70,11 @@ struct SplitPlan {
     int tokens_per_split;
 };
 
+constexpr int kMaxSplits = 512;          // bound of the in-kernel merge
+
 SplitPlan plan_splits(int streams, int context_len, int requested, int tile) {
-    const int max_splits = (context_len + tile - 1) / tile;
+    int max_splits = (context_len + tile - 1) / tile;
+    if (max_splits > kMaxSplits) max_splits = kMaxSplits;
     int s = requested > 0 ? requested : (kTargetWorkgroups + streams - 1) / streams;
     if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;
