@@ -138,7 +138,7 @@ def main(argv=None) -> int:
     caches = [(ck0, cv0)] + [(ck0.clone(), cv0.clone()) for _ in range(copies - 1)]
     out = torch.empty((bsz, hq, 128), dtype=torch.float32, device=dev)
     splits = args.splits or vq.decode_attention_default_splits(ck0, cv0, cb_k, cb_v, bsz, hq, n)
-    ws = torch.zeros(vq.decode_attention_workspace_bytes(ck0, cv0, cb_k, cb_v, bsz, hq, n, splits),
+    ws = torch.empty(vq.decode_attention_workspace_bytes(ck0, cv0, cb_k, cb_v, bsz, hq, n, splits),
                      dtype=torch.uint8, device=dev)
 
     def step(i):
@@ -189,7 +189,7 @@ def main(argv=None) -> int:
                    "num_splits": splits, "cold_cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "vq_attention_mfma_kernel (one launch: splits + merge)",
+                     "kernel": "vq_decode_attention: vq_attention_mfma_kernel + merge_partials_kernel",
                      "bytes_per_launch": ab["total"], "bytes_per_unit": ab["per_unit"],
                      "units_per_launch": ab["units"], "avg_launch_us": attn_us,
                      "median_launch_us": attn_med_us},

@@ -20,8 +20,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All array pointers are DEVICE pointers allocated and owned by the
- *    caller.  The library allocates no device memory; split partials and
- *    the split-completion counters live in a caller-provided workspace.
+ *    caller.  The library allocates no device memory; split partials live in
+ *    a caller-provided workspace.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call only enqueues work on that stream and returns without
  *    synchronising.  Faults inside kernels surface at the caller's next
@@ -134,10 +134,9 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
  *   q [B][Hq][128] in q_dtype (raw query: the transform happens inside)
  *   out [B][Hq][128] fp32
  *   workspace: device memory of at least
- *              vq_decode_attention_workspace_bytes(...) bytes, ZERO-FILLED
- *              before its first use; every call returns it to that state, so
- *              one allocation serves any number of calls.  Calls that run
- *              concurrently must not share a workspace.
+ *              vq_decode_attention_workspace_bytes(...) bytes, any contents;
+ *              it holds the split partials until the merge has read them, so
+ *              calls that run concurrently must not share a workspace.
  * Errors: VQ_ERR_CAPACITY if context_len > capacity; VQ_ERR_INVALID_ARG if
  * context_len < 1 (softmax over an empty set) or Hq % Hkv != 0;
  * VQ_ERR_UNSUPPORTED if G > 8; VQ_ERR_WORKSPACE if the workspace is too small.

@@ -101,13 +101,12 @@ def test_workspace_query_matches_partials_layout(lib):
         return (x + 255) // 256 * 256
 
     n = 1 * 32 * s
-    tickets = a256(4 * 1 * 8)
-    assert need == tickets + 2 * a256(4 * n) + a256(4 * 128 * n)
+    assert need == 2 * a256(4 * n) + a256(4 * 128 * n)
     # explicit split requests are clamped so that no split is empty
     # (splits are whole sweeps of 512 tokens: 1100 tokens allow at most 3)
     one = lib.vq_decode_attention_workspace_bytes(ctypes.byref(layout), 1, 32, 1100, 10 ** 6)
     n = 32 * 3
-    assert one == a256(4 * 8) + 2 * a256(4 * n) + a256(4 * 128 * n)
+    assert one == 2 * a256(4 * n) + a256(4 * 128 * n)
     assert lib.vq_decode_attention_workspace_bytes(None, 1, 32, 100, 0) == 0
 
 

@@ -85,18 +85,17 @@ def test_bitwise_reproducible(tiny):
     np.testing.assert_array_equal(a, b)
 
 
-def test_workspace_is_reusable_and_left_zeroed(tiny):
+def test_workspace_contents_do_not_matter(tiny):
     c, d, ref = tiny
     n = c.context_len
     args = (d["codes_k"], d["codes_v"], d["cb_k"], d["cb_v"], 1, 4, n)
-    ws = torch.zeros(vq.decode_attention_workspace_bytes(*args), dtype=torch.uint8, device=DEV)
+    ws = torch.full((vq.decode_attention_workspace_bytes(*args, 4),), 0xFF, dtype=torch.uint8,
+                    device=DEV)
     outs = []
-    for splits in (0, 3, 0):
+    for splits in (2, 1, 2):
         o = vq.decode_attention(d["q"], d["lam"], d["cb_k"], d["cb_v"], d["codes_k"],
                                 d["codes_v"], n, num_splits=splits, workspace=ws)
         torch.cuda.synchronize()
-        # the split-completion tickets at the head of the workspace are zero again
-        assert int(ws[:256].count_nonzero()) == 0
         outs.append(o.cpu().numpy().astype(np.float64))
     np.testing.assert_array_equal(outs[0], outs[2])
     for o in outs:

@@ -185,8 +185,8 @@ def decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
     """Decode attention over the VQ cache -> float32 [B][Hq][128].
 
     ``workspace`` (optional, reusable): a uint8 device tensor of at least
-    ``decode_attention_workspace_bytes(...)`` bytes, zero-filled before its
-    first use (``torch.zeros``); the kernel leaves it zeroed."""
+    ``decode_attention_workspace_bytes(...)`` bytes; its contents do not
+    matter."""
     _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
     _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
     batch, hq = q.shape[0], q.shape[1]
@@ -195,7 +195,7 @@ def decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
     if workspace is None:
         nbytes = decode_attention_workspace_bytes(codes_k, codes_v, cb_k, cb_v, batch, hq,
                                                   context_len, num_splits)
-        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
     _check(library().vq_decode_attention(ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam),
                                          _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),

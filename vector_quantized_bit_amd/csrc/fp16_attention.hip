@@ -202,31 +202,4 @@ hipError_t launch_fp16_attention_splits(const AttnShape& s, const uint16_t* q, c
     return hipGetLastError();
 }
 
-// ---- cross-split log-sum-exp merge (one workgroup per (sequence, q head)) ----
-__global__ __launch_bounds__(128) void merge_splits_kernel(int num_splits, Partials part,
-                                                           float* __restrict__ out) {
-    const size_t bh = blockIdx.x;
-    const int d = threadIdx.x;
-    const float* m = part.m + bh * num_splits;
-    const float* l = part.l + bh * num_splits;
-    const float* o = part.o + bh * num_splits * kHeadDim;
-    float mx = -INFINITY;
-    for (int s = 0; s < num_splits; ++s) mx = fmaxf(mx, m[s]);
-    float den = 0.f, num = 0.f;
-    for (int s = 0; s < num_splits; ++s) {
-        const float ms = m[s];
-        const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
-        den += w * l[s];
-        num += w * o[static_cast<size_t>(s) * kHeadDim + d];
-    }
-    out[bh * kHeadDim + d] = num / den;
-}
-
-hipError_t launch_merge_splits(int batch, int num_q_heads, int num_splits, Partials part,
-                               float* out, hipStream_t stream) {
-    hipLaunchKernelGGL(merge_splits_kernel, dim3(batch * num_q_heads), dim3(kHeadDim), 0, stream,
-                       num_splits, part, out);
-    return hipGetLastError();
-}
-
 }  // namespace vqkv

@@ -19,17 +19,16 @@ hipError_t launch_transform_query(const void* q, bool q_f32, const float* lambda
                                   int num_q_heads, int num_kv_heads, float* q_tilde,
                                   hipStream_t stream);
 
-// Fused split-K attention + cross-split merge on the matrix cores.  `tickets`
-// holds batch * num_kv_heads zero-initialised counters; the kernel leaves them
-// zero again.
-hipError_t launch_vq_attention_fused(const AttnShape& s, int k_bits, const void* q, bool q_f32,
-                                     const float* lambda, const uint16_t* cb_k,
-                                     const uint16_t* cb_v, const uint8_t* codes_k,
-                                     const uint8_t* codes_v, Partials part, uint32_t* tickets,
-                                     float* out, hipStream_t stream);
-
-hipError_t launch_merge_splits(int batch, int num_q_heads, int num_splits, Partials part,
+// Split-K decode attention over the VQ cache on the matrix cores, followed by
+// the cross-split merge when there is more than one split.
+hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bool q_f32,
+                               const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                               const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
                                float* out, hipStream_t stream);
+
+// out[bh][:] from the num_splits partials of every (sequence, query head) bh.
+hipError_t launch_merge_partials(int batch, int num_q_heads, int num_splits, Partials part,
+                                 float* out, hipStream_t stream);
 
 hipError_t launch_encode_append(int k_bits, const void* k_new, const void* v_new, bool kv_f32,
                                 const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
@@ -43,5 +42,6 @@ hipError_t launch_fp16_attention_splits(const AttnShape& s, const uint16_t* q, c
 // lengths are multiples of it.
 constexpr int kVqTile = 512;       // = waves per workgroup x tokens per wave tile
 constexpr int kFp16Tile = 128;
+constexpr int kMaxSplits = 512;    // bound of the split planner and the merge's LDS
 
 }  // namespace vqkv

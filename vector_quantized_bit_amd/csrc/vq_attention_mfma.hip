@@ -32,9 +32,11 @@
 //    (or 12) contiguous bytes per lane: the split's rows form the buffer
 //    range, so rows past the split's end read as zero without any clamp.
 //    Two register sets alternate so one tile of loads is always in flight.
-//  * The cross-split log-sum-exp merge runs in the same kernel: the last
-//    workgroup of each (sequence, KV head) to finish (device-scope atomic
-//    ticket) merges all split partials for its G heads.
+//  * Each workgroup leaves base-2 partials (m, l, o) of its token range; a
+//    second, small kernel merges the splits by log-sum-exp (a single split
+//    writes the output directly).  Merging inside this kernel would need a
+//    device-scope release per workgroup, which writes back the XCD's L2 and
+//    costs more than the extra launch.
 #include "launchers.hpp"
 
 namespace vqkv {
@@ -157,98 +159,6 @@ struct KChunk<12> {
     }
 };
 
-// Log-sum-exp merge of the S split partials of G query heads by one
-// workgroup: out[h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s with
-// M = max_s m_s.  Loads are issued eight splits at a time per thread so their
-// latencies overlap.  scratch: LDS floats for [G][S] weights and the slice sums.
-constexpr int kMaxMergeSplits = 512;   // the split planner never exceeds this
-
-template <int G>
-__device__ void merge_splits_block(const Partials& part, size_t hbase, int num_splits,
-                                   float* __restrict__ out, float* scratch, float* red) {
-    constexpr int COLS = G * 32;                 // (head, 4-channel column) pairs
-    constexpr int J = kThreads / COLS;           // split slices
-    float* msh = scratch;                        // [G][S] split maxima
-    float* wsh = scratch + G * kMaxMergeSplits;  // [G][S] weights 2^(m_s - M)
-    float* osum = wsh + G * kMaxMergeSplits;     // [J][G][128] slice sums
-    float* lsum = osum + J * G * kHeadDim;       // [J][G]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    float mloc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
-    for (int s = tid; s < num_splits; s += kThreads) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float v = part.m[hbase + static_cast<size_t>(h) * num_splits + s];
-            msh[h * kMaxMergeSplits + s] = v;
-            mloc[h] = fmaxf(mloc[h], v);
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float w = wave_max(mloc[h]);
-        if (lane == 0) red[wave * G + h] = w;
-    }
-    __syncthreads();
-    for (int i = tid; i < G * num_splits; i += kThreads) {
-        const int h = i / num_splits, s = i % num_splits;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w * G + h]);
-        const float ms = msh[h * kMaxMergeSplits + s];
-        wsh[h * kMaxMergeSplits + s] = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
-    }
-    __syncthreads();
-
-    const int j = tid / COLS;
-    if (j < J) {
-        const int cg = tid % COLS, h = cg / 32, c4 = cg % 32;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        float lacc = 0.f;
-        const float* wrow = wsh + h * kMaxMergeSplits;
-        const size_t prow = hbase + static_cast<size_t>(h) * num_splits;
-        for (int s0 = j; s0 < num_splits; s0 += 8 * J) {
-            float4 o[8];
-            float l[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int s = s0 + u * J;
-                if (s < num_splits) {
-                    o[u] = reinterpret_cast<const float4*>(part.o + (prow + s) * kHeadDim)[c4];
-                    l[u] = part.l[prow + s];
-                } else {
-                    o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    l[u] = 0.f;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int s = s0 + u * J;
-                const float w = (s < num_splits) ? wrow[s] : 0.f;
-                acc.x += w * o[u].x;
-                acc.y += w * o[u].y;
-                acc.z += w * o[u].z;
-                acc.w += w * o[u].w;
-                lacc += w * l[u];
-            }
-        }
-        *reinterpret_cast<float4*>(osum + (j * G + h) * kHeadDim + 4 * c4) = acc;
-        if (c4 == 0) lsum[j * G + h] = lacc;
-    }
-    __syncthreads();
-    for (int i = tid; i < G * kHeadDim; i += kThreads) {
-        const int h = i / kHeadDim, d = i % kHeadDim;
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < J; ++jj) {
-            num += osum[(jj * G + h) * kHeadDim + d];
-            den += lsum[jj * G + h];
-        }
-        out[h * kHeadDim + d] = num / den;
-    }
-}
-
 }  // namespace
 
 template <int G, int KBITS>
@@ -257,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint16_t* __restrict__ cb_k, const uint16_t* __restrict__ cb_v,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v, int num_q_heads,
     int num_kv_heads, int capacity, int context_len, int num_splits, int tokens_per_split,
-    Partials part, uint32_t* __restrict__ tickets, float* __restrict__ out) {
+    Partials part, float* __restrict__ out) {
     static_assert(G >= 1 && G <= 8, "2G MFMA rows");
     constexpr int KROW = kNumSub * KBITS / 8;
 
@@ -265,7 +175,6 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     __shared__ __attribute__((aligned(16))) uint2 pbuf[kWaves][kTok * 4];  // [token][16 rows] fp16
     __shared__ half8_t qa[4][64];
     __shared__ float wm[kWaves][G], wl[kWaves][G];
-    __shared__ uint32_t last_flag;
     // q~ (fp32) lives in the p buffers during the prologue
     static_assert(sizeof(float) * G * kHeadDim <= sizeof(pbuf), "q~ fits in the p buffers");
     float (*qsh)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&pbuf[0][0]);
@@ -532,34 +441,22 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             // a wave that got no tile has m = -inf and weighs 0
-            const float f = (wm[w][h] == -INFINITY) ? 0.f : exp2f(wm[w][h] - mx);
+            const float f = (wm[w][h] == -INFINITY) ? 0.f : fast_exp2(wm[w][h] - mx);
             ls += f * wl[w][h];
             os += f * obuf[(w * G + h) * kHeadDim + d];
         }
-        const size_t pi = pbase + static_cast<size_t>(h) * num_splits;
-        part.o[pi * kHeadDim + d] = os;
-        if (d == 0) {
-            part.m[pi] = mx;
-            part.l[pi] = ls;
+        if (num_splits == 1) {
+            // one split: this is the whole softmax
+            out[(static_cast<size_t>(b) * num_q_heads + g * G + h) * kHeadDim + d] = os / ls;
+        } else {
+            const size_t pi = pbase + static_cast<size_t>(h) * num_splits;
+            part.o[pi * kHeadDim + d] = os;
+            if (d == 0) {
+                part.m[pi] = mx;
+                part.l[pi] = ls;
+            }
         }
     }
-
-    // ---- the last workgroup of this (sequence, KV head) merges all splits ---
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const uint32_t prev = atomicAdd(&tickets[static_cast<size_t>(b) * num_kv_heads + g], 1u);
-        last_flag = (prev == static_cast<uint32_t>(num_splits - 1)) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (last_flag == 0u) return;
-    __threadfence();
-    static_assert(sizeof(float) * (2 * G * kMaxMergeSplits + (kThreads / (G * 32)) * G * (kHeadDim + 1)) <=
-                      sizeof(tab), "merge scratch fits in the tables");
-    merge_splits_block<G>(part, (static_cast<size_t>(b) * num_q_heads + g * G) * num_splits,
-                          num_splits, out + (static_cast<size_t>(b) * num_q_heads + g * G) * kHeadDim,
-                          reinterpret_cast<float*>(tab), &wm[0][0]);
-    if (tid == 0) tickets[static_cast<size_t>(b) * num_kv_heads + g] = 0u;   // ready for the next call
 }
 
 namespace {
@@ -568,13 +465,13 @@ template <int KBITS>
 hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q, bool q_f32,
                          const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                          const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                         uint32_t* tickets, float* out, hipStream_t stream) {
+                         float* out, hipStream_t stream) {
 #define VQKV_LAUNCH(GG)                                                                       \
     case GG:                                                                                  \
         hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS>), grid, dim3(kThreads), 0,    \
                            stream, q, q_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,   \
                            s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
-                           s.num_splits, s.tokens_per_split, part, tickets, out);             \
+                           s.num_splits, s.tokens_per_split, part, out);             \
         break;
     switch (group) {
         VQKV_LAUNCH(1)
@@ -594,18 +491,19 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
 
 }  // namespace
 
-hipError_t launch_vq_attention_fused(const AttnShape& s, int k_bits, const void* q, bool q_f32,
-                                     const float* lambda, const uint16_t* cb_k,
-                                     const uint16_t* cb_v, const uint8_t* codes_k,
-                                     const uint8_t* codes_v, Partials part, uint32_t* tickets,
-                                     float* out, hipStream_t stream) {
+hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bool q_f32,
+                               const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                               const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
+                               float* out, hipStream_t stream) {
     const dim3 grid(s.num_splits, s.num_kv_heads, s.batch);
     const int group = s.num_q_heads / s.num_kv_heads;
-    if (k_bits == 8)
-        return launch_mfma_g<8>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k, codes_v,
-                                part, tickets, out, stream);
-    return launch_mfma_g<12>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k, codes_v,
-                             part, tickets, out, stream);
+    const hipError_t e =
+        (k_bits == 8) ? launch_mfma_g<8>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
+                                         codes_v, part, out, stream)
+                      : launch_mfma_g<12>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
+                                          codes_v, part, out, stream);
+    if (e != hipSuccess || s.num_splits == 1) return e;
+    return launch_merge_partials(s.batch, s.num_q_heads, s.num_splits, part, out, stream);
 }
 
 }  // namespace vqkv

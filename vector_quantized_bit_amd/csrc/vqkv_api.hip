@@ -34,7 +34,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Device-independent plan: the same shape always gets the same split count,
 // so results are reproducible across devices and runs.
-constexpr int kTargetWorkgroups = 256;   // one 16-wave workgroup per CU of a 256-CU MI355X
+constexpr int kTargetWorkgroups = 256;       // VQ kernel: one 16-wave workgroup per CU (256 CUs)
+constexpr int kTargetWorkgroupsFp16 = 1024;  // fp16 comparator: 4-wave workgroups, 4 per CU
 constexpr int kMaxGroup = 8;
 
 int check_layout(const vq_layout* L) {
@@ -70,12 +71,11 @@ struct SplitPlan {
     int tokens_per_split;
 };
 
-constexpr int kMaxSplits = 512;          // bound of the in-kernel merge
-
-SplitPlan plan_splits(int streams, int context_len, int requested, int tile) {
+SplitPlan plan_splits(int streams, int context_len, int requested, int tile,
+                      int target = kTargetWorkgroups) {
     int max_splits = (context_len + tile - 1) / tile;
-    if (max_splits > kMaxSplits) max_splits = kMaxSplits;
-    int s = requested > 0 ? requested : (kTargetWorkgroups + streams - 1) / streams;
+    if (max_splits > vqkv::kMaxSplits) max_splits = vqkv::kMaxSplits;
+    int s = requested > 0 ? requested : (target + streams - 1) / streams;
     if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;
     const int per = (context_len + s - 1) / s;
@@ -84,10 +84,6 @@ SplitPlan plan_splits(int streams, int context_len, int requested, int tile) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-size_t tickets_bytes(int batch, int num_kv_heads) {
-    return align256(static_cast<size_t>(batch) * num_kv_heads * sizeof(uint32_t));
-}
 
 size_t partials_bytes(int batch, int num_q_heads, int num_splits) {
     const size_t n = static_cast<size_t>(batch) * num_q_heads * num_splits;
@@ -189,7 +185,7 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
         return 0;
     const SplitPlan p =
         plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
-    return tickets_bytes(batch, layout->num_kv_heads) + partials_bytes(batch, num_q_heads, p.num_splits);
+    return partials_bytes(batch, num_q_heads, p.num_splits);
 }
 
 int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
@@ -217,28 +213,25 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
     VQ_REQUIRE_PTR(out);
     const SplitPlan p =
         plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
-    const size_t tk = tickets_bytes(batch, layout->num_kv_heads);
-    const size_t need = tk + partials_bytes(batch, num_q_heads, p.num_splits);
+    const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
     if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    uint32_t* tickets = static_cast<uint32_t*>(workspace);
-    const vqkv::Partials part =
-        carve_partials(static_cast<char*>(workspace) + tk, batch, num_q_heads, p.num_splits);
+    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, p.num_splits);
     const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
                                 context_len, p.num_splits, p.tokens_per_split};
-    return hip_status(vqkv::launch_vq_attention_fused(shape, layout->k_code_bits, q,
-                                                      q_dtype == VQ_F32, lambda, cb_k, cb_v,
-                                                      codes_k, codes_v, part, tickets, out,
-                                                      static_cast<hipStream_t>(stream)),
+    return hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
+                                                lambda, cb_k, cb_v, codes_k, codes_v, part, out,
+                                                static_cast<hipStream_t>(stream)),
                       "decode_attention launch");
 }
 
 size_t vq_fp16_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t context_len, int32_t num_splits) {
     if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || context_len < 1) return 0;
-    const SplitPlan p = plan_splits(batch * num_kv_heads, context_len, num_splits, vqkv::kFp16Tile);
+    const SplitPlan p = plan_splits(batch * num_kv_heads, context_len, num_splits, vqkv::kFp16Tile,
+                                      kTargetWorkgroupsFp16);
     return partials_bytes(batch, num_q_heads, p.num_splits);
 }
 
@@ -260,7 +253,8 @@ int vq_fp16_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_
     VQ_REQUIRE_PTR(k);
     VQ_REQUIRE_PTR(v);
     VQ_REQUIRE_PTR(out);
-    const SplitPlan p = plan_splits(batch * num_kv_heads, context_len, num_splits, vqkv::kFp16Tile);
+    const SplitPlan p = plan_splits(batch * num_kv_heads, context_len, num_splits, vqkv::kFp16Tile,
+                                      kTargetWorkgroupsFp16);
     const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -273,7 +267,7 @@ int vq_fp16_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_
     st = hip_status(vqkv::launch_fp16_attention_splits(shape, q, k, v, part, s),
                     "fp16 attention split launch");
     if (st) return st;
-    return hip_status(vqkv::launch_merge_splits(batch, num_q_heads, p.num_splits, part, out, s),
+    return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, p.num_splits, part, out, s),
                       "fp16 attention merge launch");
 }
 
