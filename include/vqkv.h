@@ -140,7 +140,8 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
  * Errors: VQ_ERR_CAPACITY if context_len > capacity; VQ_ERR_INVALID_ARG if
  * context_len < 1 (softmax over an empty set) or Hq % Hkv != 0;
  * VQ_ERR_UNSUPPORTED if G > 8; VQ_ERR_WORKSPACE if the workspace is too small.
- * Results are bitwise reproducible for a fixed split count.
+ * Tiles are scheduled dynamically inside a split, so repeated calls agree to
+ * fp32 rounding (not bit for bit).
  */
 int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype,
                         const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,

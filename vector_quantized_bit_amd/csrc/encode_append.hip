@@ -8,133 +8,141 @@
 //
 // The transform and the squared distances are evaluated in fp64 (products
 // and sums rounded separately, summed over the 4 channels in order), so the
-// argmin is decided in the same precision as the fp64 reference; exact ties
-// go to the lowest index because the scan is ascending with a strict '<'.
+// argmin is decided in the same precision as the fp64 reference.  Exact ties
+// go to the lowest index: every thread scans its centroids in ascending order
+// with a strict '<', and the per-thread winners are combined by the
+// lexicographic minimum of (distance, index).
 //
-// One workgroup encodes 8 tokens of one (sequence, KV head); thread
-// (token, position) owns one key and one value sub-vector.
+// One 256-thread workgroup encodes one token of one (sequence, KV head):
+// thread (slice s, position p) scans centroids s, s + 8, s + 16, ... of
+// sub-vector p, so a single decode-step append (one token per head) is 8x
+// shorter than a scan per sub-vector.  Codebooks are staged in LDS (2 KiB,
+// or 32 KiB for 12-bit keys); the 8 threads that share a centroid index sit
+// in different waves, the 32 threads of a wave read one broadcast address.
 #include "launchers.hpp"
 
 namespace vqkv {
 
 namespace {
 
-constexpr int kEncTok = 8;
-constexpr int kEncChunk = 1024;   // codebook entries staged in LDS at a time
+constexpr int kEncThreads = 256;
+constexpr int kEncSlices = kEncThreads / kNumSub;   // 8
 
 __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
     if (f32) return static_cast<double>(reinterpret_cast<const float*>(p)[i]);
     return static_cast<double>(half_bits_to_float(reinterpret_cast<const uint16_t*>(p)[i]));
 }
 
-__device__ __forceinline__ double sqdist4(const double x[4], const float4 c) {
-    double d = 0.0;
-    const double e0 = __dadd_rn(x[0], -static_cast<double>(c.x));
-    const double e1 = __dadd_rn(x[1], -static_cast<double>(c.y));
-    const double e2 = __dadd_rn(x[2], -static_cast<double>(c.z));
-    const double e3 = __dadd_rn(x[3], -static_cast<double>(c.w));
-    d = __dadd_rn(d, __dmul_rn(e0, e0));
+__device__ __forceinline__ double sqdist4(const double x[4], const uint2 c) {
+    const double c0 = half_bits_to_float(c.x & 0xffffu), c1 = half_bits_to_float(c.x >> 16);
+    const double c2 = half_bits_to_float(c.y & 0xffffu), c3 = half_bits_to_float(c.y >> 16);
+    const double e0 = __dadd_rn(x[0], -c0), e1 = __dadd_rn(x[1], -c1);
+    const double e2 = __dadd_rn(x[2], -c2), e3 = __dadd_rn(x[3], -c3);
+    double d = __dmul_rn(e0, e0);
     d = __dadd_rn(d, __dmul_rn(e1, e1));
     d = __dadd_rn(d, __dmul_rn(e2, e2));
     d = __dadd_rn(d, __dmul_rn(e3, e3));
     return d;
 }
 
-// Scan `entries` fp16 centroids for the nearest one to x; all threads of the
-// block call this together (it stages the codebook through LDS).
-__device__ __forceinline__ uint32_t nearest(const double x[4], const uint16_t* __restrict__ cb,
-                                            int entries, float4* cbuf) {
+// Nearest of `entries` LDS centroids to x among indices slice, slice + 8, ...,
+// combined across the 8 slices; returns the code for this thread's position.
+__device__ __forceinline__ uint32_t nearest(const double x[4], const uint2* cb, int entries,
+                                            int slice, int pos, double* bd, uint32_t* bi) {
     double best = INFINITY;
     uint32_t arg = 0;
-    const uint2* src = reinterpret_cast<const uint2*>(cb);
-    for (int base = 0; base < entries; base += kEncChunk) {
-        const int n = min(kEncChunk, entries - base);
-        __syncthreads();
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const uint2 raw = src[base + i];
-            cbuf[i] = make_float4(half_bits_to_float(raw.x & 0xffffu), half_bits_to_float(raw.x >> 16),
-                                  half_bits_to_float(raw.y & 0xffffu), half_bits_to_float(raw.y >> 16));
-        }
-        __syncthreads();
-        for (int j = 0; j < n; ++j) {
-            const double d = sqdist4(x, cbuf[j]);
-            if (d < best) {
-                best = d;
-                arg = static_cast<uint32_t>(base + j);
-            }
+#pragma unroll 4
+    for (int c = slice; c < entries; c += kEncSlices) {
+        const double d = sqdist4(x, cb[c]);
+        if (d < best) {
+            best = d;
+            arg = static_cast<uint32_t>(c);
         }
     }
-    return arg;
+    bd[slice * kNumSub + pos] = best;
+    bi[slice * kNumSub + pos] = arg;
+    __syncthreads();
+    double b0 = bd[pos];
+    uint32_t a0 = bi[pos];
+#pragma unroll
+    for (int s = 1; s < kEncSlices; ++s) {
+        const double d = bd[s * kNumSub + pos];
+        const uint32_t a = bi[s * kNumSub + pos];
+        if (d < b0 || (d == b0 && a < a0)) {
+            b0 = d;
+            a0 = a;
+        }
+    }
+    __syncthreads();   // bd / bi are reused by the next call
+    return a0;
 }
 
 }  // namespace
 
 template <int KBITS>
-__global__ __launch_bounds__(256) void encode_append_kernel(
+__global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
     const float* __restrict__ lambda, const uint16_t* __restrict__ cb_k,
     const uint16_t* __restrict__ cb_v, uint8_t* __restrict__ codes_k,
     uint8_t* __restrict__ codes_v, int num_kv_heads, int capacity, int cur_len, int num_new) {
+    constexpr int KENT = 1 << KBITS;
     constexpr int KROW = kNumSub * KBITS / 8;
-    __shared__ double xk[kEncTok][kHeadDim];
-    __shared__ float4 cbuf[kEncChunk];
-    __shared__ uint16_t kcode[kEncTok][kNumSub];
+    __shared__ uint2 kcb[KENT];
+    __shared__ uint2 vcb[256];
+    __shared__ double xk[kHeadDim];
+    __shared__ double bd[kEncSlices * kNumSub];
+    __shared__ uint32_t bi[kEncSlices * kNumSub];
+    __shared__ uint32_t kcode[kNumSub];
 
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
-    const int tok0 = blockIdx.x * kEncTok;
-    const int ntok = min(kEncTok, num_new - tok0);
-    const int tid = threadIdx.x;
+    const int tok = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const bool f32 = kv_f32 != 0;
-    const size_t in_row0 = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + tok0;
-    const float* lam = lambda + g * kHeadDim;
+    const size_t in_row = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + tok;
 
-    // k / lambda in fp64, then the +-1 Walsh–Hadamard butterflies in LDS
-    for (int e = tid; e < kEncTok * kHeadDim; e += 256) {
-        const int t = e / kHeadDim, c = e % kHeadDim;
-        xk[t][c] = (t < ntok) ? load_elem(k_new, f32, (in_row0 + t) * kHeadDim + c) /
-                                    static_cast<double>(lam[c])
-                              : 0.0;
+    // this thread's value sub-vector is loaded first so its latency hides
+    // behind the codebook staging and the key scan
+    const int pos = tid % kNumSub, slice = tid / kNumSub;
+    double xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = load_elem(v_new, f32, in_row * kHeadDim + 4 * pos + i);
+
+    const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
+    for (int i = tid; i < KENT; i += kEncThreads) kcb[i] = ksrc[i];
+    vcb[tid] = reinterpret_cast<const uint2*>(cb_v)[static_cast<size_t>(g) * 256 + tid];
+
+    // k / lambda in fp64, +-1 Walsh–Hadamard butterflies in one wave, then 1/sqrt(128)
+    if (tid < kWave) {
+        const float* lam = lambda + g * kHeadDim;
+        double x0 = load_elem(k_new, f32, in_row * kHeadDim + 2 * lane) /
+                    static_cast<double>(lam[2 * lane]);
+        double x1 = load_elem(k_new, f32, in_row * kHeadDim + 2 * lane + 1) /
+                    static_cast<double>(lam[2 * lane + 1]);
+        wave_fwht128(x0, x1);
+        xk[2 * lane] = x0 * kInvSqrtD64;
+        xk[2 * lane + 1] = x1 * kInvSqrtD64;
     }
     __syncthreads();
-    for (int h = 1; h < kHeadDim; h <<= 1) {
-        for (int e = tid; e < kEncTok * (kHeadDim / 2); e += 256) {
-            const int t = e / (kHeadDim / 2), i = e % (kHeadDim / 2);
-            const int lo = (i / h) * 2 * h + (i % h);
-            const double a = xk[t][lo], c = xk[t][lo + h];
-            xk[t][lo] = a + c;
-            xk[t][lo + h] = a - c;
-        }
-        __syncthreads();
-    }
 
-    const int t = tid / kNumSub;
-    const int p = tid % kNumSub;
     double x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = xk[t][4 * p + i] * kInvSqrtD64;
-    const uint32_t ck = nearest(x, cb_k + static_cast<size_t>(g) * (4u << KBITS), 1 << KBITS, cbuf);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        x[i] = (t < ntok) ? load_elem(v_new, f32, (in_row0 + t) * kHeadDim + 4 * p + i) : 0.0;
-    const uint32_t cvc = nearest(x, cb_v + static_cast<size_t>(g) * 1024, 256, cbuf);
+    for (int i = 0; i < 4; ++i) x[i] = xk[4 * pos + i];
+    const uint32_t ck = nearest(x, kcb, KENT, slice, pos, bd, bi);
+    const uint32_t cv = nearest(xv, vcb, 256, slice, pos, bd, bi);
 
-    const size_t out_row0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + cur_len + tok0;
-    if (t < ntok) codes_v[(out_row0 + t) * kNumSub + p] = static_cast<uint8_t>(cvc);
+    const size_t out_row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + cur_len + tok;
+    if (tid < kNumSub) codes_v[out_row * kNumSub + pos] = static_cast<uint8_t>(cv);
     if constexpr (KBITS == 8) {
-        if (t < ntok) codes_k[(out_row0 + t) * kNumSub + p] = static_cast<uint8_t>(ck);
+        if (tid < kNumSub) codes_k[out_row * KROW + pos] = static_cast<uint8_t>(ck);
     } else {
-        kcode[t][p] = static_cast<uint16_t>(ck);
+        if (tid < kNumSub) kcode[pos] = ck;
         __syncthreads();
-        // byte j of a row holds bits [8j, 8j+8) of the little-endian 12-bit stream
-        for (int e = tid; e < kEncTok * KROW; e += 256) {
-            const int tt = e / KROW, j = e % KROW;
-            if (tt >= ntok) continue;
-            const int bit = 8 * j;
+        // byte j of the row holds bits [8j, 8j+8) of the little-endian 12-bit stream
+        if (tid < KROW) {
+            const int bit = 8 * tid;
             const int i0 = bit / 12, sh = bit % 12;
-            uint32_t v = static_cast<uint32_t>(kcode[tt][i0]) >> sh;
-            if (sh > 4) v |= static_cast<uint32_t>(kcode[tt][i0 + 1]) << (12 - sh);
-            codes_k[(out_row0 + tt) * KROW + j] = static_cast<uint8_t>(v & 0xffu);
+            uint32_t v = kcode[i0] >> sh;
+            if (sh > 4) v |= kcode[i0 + 1] << (12 - sh);
+            codes_k[out_row * KROW + tid] = static_cast<uint8_t>(v & 0xffu);
         }
     }
 }
@@ -143,15 +151,15 @@ hipError_t launch_encode_append(int k_bits, const void* k_new, const void* v_new
                                 const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                                 uint8_t* codes_k, uint8_t* codes_v, int batch, int num_kv_heads,
                                 int capacity, int cur_len, int num_new, hipStream_t stream) {
-    const dim3 grid((num_new + kEncTok - 1) / kEncTok, num_kv_heads, batch);
+    const dim3 grid(num_new, num_kv_heads, batch);
     if (k_bits == 8)
-        hipLaunchKernelGGL(encode_append_kernel<8>, grid, dim3(256), 0, stream, k_new, v_new,
-                           kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v, num_kv_heads,
-                           capacity, cur_len, num_new);
+        hipLaunchKernelGGL(encode_append_kernel<8>, grid, dim3(kEncThreads), 0, stream, k_new,
+                           v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
+                           num_kv_heads, capacity, cur_len, num_new);
     else
-        hipLaunchKernelGGL(encode_append_kernel<12>, grid, dim3(256), 0, stream, k_new, v_new,
-                           kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v, num_kv_heads,
-                           capacity, cur_len, num_new);
+        hipLaunchKernelGGL(encode_append_kernel<12>, grid, dim3(kEncThreads), 0, stream, k_new,
+                           v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
+                           num_kv_heads, capacity, cur_len, num_new);
     return hipGetLastError();
 }
 

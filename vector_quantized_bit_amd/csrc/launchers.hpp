@@ -26,8 +26,8 @@ hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bo
                                const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
                                float* out, hipStream_t stream);
 
-// out[bh][:] from the num_splits partials of every (sequence, query head) bh.
-hipError_t launch_merge_partials(int batch, int num_q_heads, int num_splits, Partials part,
+// out[bh][:] from the num_partials partials of every (sequence, query head) bh.
+hipError_t launch_merge_partials(int batch, int num_q_heads, int num_partials, Partials part,
                                  float* out, hipStream_t stream);
 
 hipError_t launch_encode_append(int k_bits, const void* k_new, const void* v_new, bool kv_f32,
@@ -40,8 +40,9 @@ hipError_t launch_fp16_attention_splits(const AttnShape& s, const uint16_t* q, c
 
 // Tokens one workgroup of the VQ split kernel processes per tile; split
 // lengths are multiples of it.
+constexpr int kVqWaves = 16;       // waves per workgroup of the VQ kernel; each leaves a partial
 constexpr int kVqTile = 512;       // = waves per workgroup x tokens per wave tile
 constexpr int kFp16Tile = 128;
-constexpr int kMaxSplits = 512;    // bound of the split planner and the merge's LDS
+constexpr int kMaxSplits = 512;    // bound of the split planner
 
 }  // namespace vqkv

@@ -32,9 +32,12 @@
 //    (or 12) contiguous bytes per lane: the split's rows form the buffer
 //    range, so rows past the split's end read as zero without any clamp.
 //    Two register sets alternate so one tile of loads is always in flight.
-//  * Each workgroup leaves base-2 partials (m, l, o) of its token range; a
-//    second, small kernel merges the splits by log-sum-exp (a single split
-//    writes the output directly).  Merging inside this kernel would need a
+//  * Tiles are handed to waves dynamically (LDS counter), so the tokens a
+//    wave folds into its online softmax depend on timing: results agree run
+//    to run to fp32 rounding, not bit for bit.
+//  * The workgroup folds its 16 wave states in LDS and leaves one base-2
+//    partial (m, l, o); a second, small kernel merges the splits by
+//    log-sum-exp.  Merging the splits inside this kernel would need a
 //    device-scope release per workgroup, which writes back the XCD's L2 and
 //    costs more than the extra launch.
 #include "launchers.hpp"
@@ -49,7 +52,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-constexpr int kWaves = 16;
+constexpr int kWaves = kVqWaves;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTok = 32;                  // tokens per wave tile
 constexpr int kStride = kWaves * kTok;    // tokens per workgroup sweep
@@ -175,6 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     __shared__ __attribute__((aligned(16))) uint2 pbuf[kWaves][kTok * 4];  // [token][16 rows] fp16
     __shared__ half8_t qa[4][64];
     __shared__ float wm[kWaves][G], wl[kWaves][G];
+    __shared__ uint32_t tile_ctr;   // next 32-token tile of the split to hand out
     // q~ (fp32) lives in the p buffers during the prologue
     static_assert(sizeof(float) * G * kHeadDim <= sizeof(pbuf), "q~ fits in the p buffers");
     float (*qsh)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&pbuf[0][0]);
@@ -197,7 +201,35 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint32_t voff0 = static_cast<uint32_t>((8 * grp + kq) * kNumSub + 8 * aq4);
     const uint32_t voff1 = voff0 + 4 * kNumSub;
 
-    // the first tile's code loads go out before the prologue
+    // ---- prologue ----------------------------------------------------------
+    if (tid == 0) tile_ctr = kWaves;   // tiles 0 .. kWaves-1 go to waves 0 .. kWaves-1
+    // codebook entries and q go out first (they gate the table and q~), then
+    // the first tile of codes; both are in flight while the tables are built.
+    const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
+    const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
+    uint2 centroid = make_uint2(0, 0);
+    if constexpr (KBITS == 8) {
+        // thread: code = tid / 4, table = (tid / 2) % 2, slots 16 (tid % 2) .. + 15
+        centroid = ((tid >> 1) & 1) ? vsrc[tid >> 2] : ksrc[tid >> 2];
+    } else {
+        if (tid < 512) centroid = vsrc[tid >> 1];
+    }
+    float x0 = 0.f, x1 = 0.f;
+    float2 lam2 = make_float2(0.f, 0.f);
+    if (wave < G) {
+        const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + wave;
+        if (q_f32) {
+            const float2 v = reinterpret_cast<const float2*>(q)[vec * (kHeadDim / 2) + lane];
+            x0 = v.x;
+            x1 = v.y;
+        } else {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(q)[vec * (kHeadDim / 2) + lane];
+            x0 = lo_half_to_float(w);
+            x1 = hi_half_to_float(w);
+        }
+        lam2 = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
+    }
+
     KChunk<KBITS> kA[2], kB[2];
     uint2 vA[2], vB[2];
     // (the whole offset goes in the VGPR operand: the buffer range check
@@ -212,71 +244,49 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         vv_[0] = make_uint2(v0[0], v0[1]);
         vv_[1] = make_uint2(v1[0], v1[1]);
     };
-    int rel = wave * kTok;
-    if (rel < t_len) load_tile(rel, kA, vA);
+    if (wave * kTok < t_len) load_tile(wave * kTok, kA, vA);
 
-    // ---- prologue: codebook tables, q~ -------------------------------------
     {
-        const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
-        const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
+        const uint4 cc = make_uint4(centroid.x, centroid.y, centroid.x, centroid.y);
         if constexpr (KBITS == 8) {
-            // thread: code = tid / 4, table = (tid / 2) % 2, slots 16 (tid % 2) .. + 15
-            const int code = tid >> 2, which = (tid >> 1) & 1, half = tid & 1;
-            const uint2 c = which ? vsrc[code] : ksrc[code];
-            uint4* dst = reinterpret_cast<uint4*>(tab + which * kTable + code * 256 + half * 128);
-            const uint4 cc = make_uint4(c.x, c.y, c.x, c.y);
+            uint4* dst = reinterpret_cast<uint4*>(tab + ((tid >> 1) & 1) * kTable +
+                                                  (tid >> 2) * 256 + (tid & 1) * 128);
 #pragma unroll
             for (int s = 0; s < 8; ++s) dst[s] = cc;
         } else {
             for (int e = tid; e < 4096; e += kThreads)
                 *reinterpret_cast<uint2*>(tab + e * 8) = ksrc[e];
             if (tid < 512) {
-                const int code = tid >> 1, half = tid & 1;
-                const uint2 c = vsrc[code];
-                uint4* dst = reinterpret_cast<uint4*>(tab + kTable + code * 256 + half * 128);
-                const uint4 cc = make_uint4(c.x, c.y, c.x, c.y);
+                uint4* dst = reinterpret_cast<uint4*>(tab + kTable + (tid >> 1) * 256 + (tid & 1) * 128);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) dst[s] = cc;
             }
         }
     }
     if (wave < G) {
-        const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + wave;
-        float x0, x1;
-        if (q_f32) {
-            const float2 v = reinterpret_cast<const float2*>(q)[vec * (kHeadDim / 2) + lane];
-            x0 = v.x;
-            x1 = v.y;
-        } else {
-            const uint32_t w = reinterpret_cast<const uint32_t*>(q)[vec * (kHeadDim / 2) + lane];
-            x0 = lo_half_to_float(w);
-            x1 = hi_half_to_float(w);
-        }
-        const float2 l = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
-        x0 *= l.x;
-        x1 *= l.y;
+        x0 *= lam2.x;
+        x1 *= lam2.y;
         wave_fwht128(x0, x1);
         qsh[wave][2 * lane] = x0 * kScoreScaleLog2;
         qsh[wave][2 * lane + 1] = x1 * kScoreScaleLog2;
     }
     __syncthreads();
-    // score A operand, shared by every wave: lane (16 grp + r) holds row r of
-    // q~ for dims 32 grp + 8 kk + e (K-step kk, element e)
-    if (wave == 0) {
-        const int r = n;
+    // score A operand, shared by every wave: lane (16 grp' + r) holds row r of
+    // q~ for dims 32 grp' + 8 kk + e (K-step kk, element e); thread tid < 256
+    // builds entry (kk = tid / 64, lane = tid % 64)
+    if (tid < 256) {
+        const int kk = tid >> 6, ql = tid & 63;
+        const int r = ql & 15, qg = ql >> 4;
         const int h = 2 * (r >> 2) + (r & 1);
         const bool lo_part = (r & 2) != 0;
+        half8_t a;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            half8_t a;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = (h < G) ? qsh[h][32 * grp + 8 * kk + e] : 0.f;
-                const _Float16 hi = static_cast<_Float16>(x);
-                a[e] = lo_part ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
-            }
-            qa[kk][lane] = a;
+        for (int e = 0; e < 8; ++e) {
+            const float x = (h < G) ? qsh[h][32 * qg + 8 * kk + e] : 0.f;
+            const _Float16 hi = static_cast<_Float16>(x);
+            a[e] = lo_part ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
         }
+        qa[kk][ql] = a;
     }
     __syncthreads();
 
@@ -398,21 +408,35 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         }
     };
 
-    // two register sets, alternating: load the next tile, compute the current
-    if (rel < t_len) {
+    // Tiles are handed out from an LDS counter as waves become free: the SIMD
+    // issue arbiter favours older waves, so a fixed interleave leaves the
+    // youngest waves with a long tail.  Two register sets alternate: the next
+    // tile's loads are in flight while the current one is computed.
+    auto grab = [&]() -> int {
+        uint32_t v = 0;
+        if (lane == 0) v = atomicAdd(&tile_ctr, 1u);
+        return static_cast<int>(__builtin_amdgcn_readfirstlane(v));
+    };
+    int cur = wave;
+    if (cur * kTok < t_len) {
+        int nxt = grab();
         for (;;) {
-            load_tile(rel + kStride, kB, vB);
-            compute_tile(rel, kA, vA);
-            rel += kStride;
-            if (rel >= t_len) break;
-            load_tile(rel + kStride, kA, vA);
-            compute_tile(rel, kB, vB);
-            rel += kStride;
-            if (rel >= t_len) break;
+            load_tile(nxt * kTok, kB, vB);
+            compute_tile(cur * kTok, kA, vA);
+            cur = nxt;
+            if (cur * kTok >= t_len) break;
+            nxt = grab();
+            load_tile(nxt * kTok, kA, vA);
+            compute_tile(cur * kTok, kB, vB);
+            cur = nxt;
+            if (cur * kTok >= t_len) break;
+            nxt = grab();
         }
     }
 
-    // ---- merge the waves of the workgroup ------------------------------------
+    // ---- fold the waves' states, leave one partial per split ----------------
+    // lane (16 grp + 4 a + e), N-tile c holds channel 32 a + 4 c + e of rows
+    // (hA hi, hB hi, hA lo, hB lo); a wave that got no tile has m = -inf.
     lA = row_sum16(lA);
     lB = row_sum16(lB);
     __syncthreads();                                      // everyone is done with tab
@@ -440,21 +464,15 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         float ls = 0.f, os = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            // a wave that got no tile has m = -inf and weighs 0
             const float f = (wm[w][h] == -INFINITY) ? 0.f : fast_exp2(wm[w][h] - mx);
             ls += f * wl[w][h];
             os += f * obuf[(w * G + h) * kHeadDim + d];
         }
-        if (num_splits == 1) {
-            // one split: this is the whole softmax
-            out[(static_cast<size_t>(b) * num_q_heads + g * G + h) * kHeadDim + d] = os / ls;
-        } else {
-            const size_t pi = pbase + static_cast<size_t>(h) * num_splits;
-            part.o[pi * kHeadDim + d] = os;
-            if (d == 0) {
-                part.m[pi] = mx;
-                part.l[pi] = ls;
-            }
+        const size_t pi = pbase + static_cast<size_t>(h) * num_splits;
+        part.o[pi * kHeadDim + d] = os;
+        if (d == 0) {
+            part.m[pi] = mx;
+            part.l[pi] = ls;
         }
     }
 }
@@ -502,7 +520,7 @@ hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bo
                                          codes_v, part, out, stream)
                       : launch_mfma_g<12>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
                                           codes_v, part, out, stream);
-    if (e != hipSuccess || s.num_splits == 1) return e;
+    if (e != hipSuccess) return e;
     return launch_merge_partials(s.batch, s.num_q_heads, s.num_splits, part, out, stream);
 }
 

@@ -213,12 +213,13 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
     VQ_REQUIRE_PTR(out);
     const SplitPlan p =
         plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
-    const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
+    const int nparts = p.num_splits;
+    const size_t need = partials_bytes(batch, num_q_heads, nparts);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
     if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, p.num_splits);
+    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, nparts);
     const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
                                 context_len, p.num_splits, p.tokens_per_split};
     return hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
