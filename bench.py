@@ -58,31 +58,82 @@ def fp16_bytes(wl: W.Workload, context_len: int) -> int:
             + wl.batch * wl.num_q_heads * wl.head_dim * (2 + 4))
 
 
-def cpu_baseline(wl: W.Workload, heads: int) -> dict:
-    """The fp64 oracle, as is, on `heads` KV heads of sequence 0 at the full
-    context, scaled to KV tokens/s per layer."""
+def cpu_baseline(wl: W.Workload, seconds: float) -> dict:
+    """The fp64 oracle, as is, timed on the host: whole KV heads of sequence 0
+    at the full context, cycling over the layer's KV heads until `seconds`
+    have passed, scaled to KV tokens/s per layer.  Inputs are drawn before
+    the clock starts."""
     import oracle
     from threadpoolctl import threadpool_info
 
-    n = wl.context_len
+    n, g = wl.context_len, wl.group
     q = W.queries(wl.config_id, 0, wl.num_q_heads).astype(np.float16)
-    g = wl.group
+    heads = []
+    for h in range(wl.num_kv_heads):
+        heads.append((q[h * g:(h + 1) * g], W.random_lambda(wl.config_id, h),
+                      W.random_codebook(wl.config_id, h, "k", 1 << wl.k_bits, 0.6),
+                      W.random_codebook(wl.config_id, h, "v", 1 << wl.v_bits, 1.0, 1 / 32),
+                      W.random_code_rows(wl.config_id, 0, h, "k", n, wl.k_row_bytes),
+                      W.random_code_rows(wl.config_id, 0, h, "v", n, wl.v_row_bytes)))
+    done = 0
     t0 = time.perf_counter()
-    for h in range(heads):
-        lam = W.random_lambda(wl.config_id, h)
-        cbk = W.random_codebook(wl.config_id, h, "k", 1 << wl.k_bits, 0.6)
-        cbv = W.random_codebook(wl.config_id, h, "v", 1 << wl.v_bits, 1.0, 1 / 32)
-        ck = W.random_code_rows(wl.config_id, 0, h, "k", n, wl.k_row_bytes)
-        cv = W.random_code_rows(wl.config_id, 0, h, "v", n, wl.v_row_bytes)
-        oracle.decode_attention_head(q[h * g:(h + 1) * g], lam, cbk, cbv, ck, cv,
-                                     wl.k_bits, wl.v_bits)
-    dt = time.perf_counter() - t0
-    per_layer = dt / heads * wl.num_kv_heads
+    while True:
+        oracle.decode_attention_head(*heads[done % len(heads)], wl.k_bits, wl.v_bits)
+        done += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    per_layer = dt / done * wl.num_kv_heads
     threads = max([1] + [p.get("num_threads", 1) for p in threadpool_info()])
-    return {"value": wl.batch * n / (per_layer * wl.batch), "unit": "KV tokens/s per layer",
+    return {"value": n / per_layer, "unit": "KV tokens/s per layer",
             "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} of {wl.num_kv_heads} KV heads of sequence 0 at N={n} "
-                      f"({dt:.1f} s), scaled to the layer"}
+            "sample": f"{done} KV-head passes (of {wl.num_kv_heads} per layer) of sequence 0 at "
+                      f"N={n} in {dt:.1f} s, scaled to one layer of one sequence"}
+
+
+# Sources that determine the attention kernel's code: a counter record taken
+# from other sources no longer describes it.
+KERNEL_SOURCES = ["vector_quantized_bit_amd/csrc/vq_attention_mfma.hip",
+                  "vector_quantized_bit_amd/csrc/launchers.hpp",
+                  "vector_quantized_bit_amd/csrc/device_common.hpp",
+                  "vector_quantized_bit_amd/build.py"]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str) -> dict | None:
+    """HBM bytes per attention launch from the committed counter record of
+    this workload (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what
+    the same counter read for a plain copy of known size), or None when there
+    is no record or the kernel sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    fetch = rec["fetch_kib_per_dispatch"] * 1024 * rec["fetch_scale"]
+    write = rec["write_kib_per_dispatch"] * 1024 * rec["write_scale"]
+    return {"bytes": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+            "source": os.path.relpath(path, ROOT)}
+
+
+def copy_calibration(torch, dev, mib: int = 256, reps: int = 3) -> None:
+    """Plain device copies of known size (`mib` MiB read, `mib` MiB written)
+    for scaling the HBM byte counters; each copy is its own dispatch."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
 
 
 def main(argv=None) -> int:
@@ -93,7 +144,10 @@ def main(argv=None) -> int:
     ap.add_argument("--config", type=int, default=4, help="workload id (see workloads)")
     ap.add_argument("--splits", type=int, default=0, help="split count (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="host time spent timing the oracle")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain copies of known size (for byte-counter runs)")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 comparator")
     args = ap.parse_args(argv)
 
@@ -141,11 +195,17 @@ def main(argv=None) -> int:
     ws = torch.empty(vq.decode_attention_workspace_bytes(ck0, cv0, cb_k, cb_v, bsz, hq, n, splits),
                      dtype=torch.uint8, device=dev)
 
+    # arguments marshalled once per cache copy, so the host stays ahead of the GPU
+    appends = [vq.prepare_encode_append(k_new, v_new, lam, cb_k, cb_v, ck, cv, n - 1)
+               for ck, cv in caches]
+    attends = [vq.prepare_decode_attention(q, lam, cb_k, cb_v, ck, cv, n, splits, out, ws)
+               for ck, cv in caches]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
     def step(i):
-        ck, cv = caches[i % copies]
-        vq.encode_append(k_new, v_new, lam, cb_k, cb_v, ck, cv, n - 1)
+        appends[i % copies](stream)
         ev_a[i].record()
-        vq.decode_attention(q, lam, cb_k, cb_v, ck, cv, n, splits, out, ws)
+        attends[i % copies](stream)
         ev_b[i].record()
 
     steps, warm = args.steps, args.warmup
@@ -167,8 +227,12 @@ def main(argv=None) -> int:
     attn_med_us = float(np.median(attn_ms) * 1e3)
     assert torch.isfinite(out).all().item()
 
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+
     ab = algorithmic_bytes(wl, n)
     achieved = ab["total"] / (attn_us * 1e-6) / 1e9
+    traffic = measured_traffic(wl.name)
     tokens = bsz * n
     result = {
         "metric": METRIC,
@@ -188,11 +252,13 @@ def main(argv=None) -> int:
                    "v_code_bits": wl.v_bits, "sub_dim": 4, "append_tokens_per_step": 1,
                    "num_splits": splits, "cold_cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None if traffic is None else traffic["bytes"],
                      "kernel": "vq_decode_attention: vq_attention_mfma_kernel + merge_partials_kernel",
                      "bytes_per_launch": ab["total"], "bytes_per_unit": ab["per_unit"],
                      "units_per_launch": ab["units"], "avg_launch_us": attn_us,
-                     "median_launch_us": attn_med_us},
+                     "median_launch_us": attn_med_us,
+                     "traffic_record": None if traffic is None else traffic["source"]},
         "step_hbm_gbps": ab["total"] / (ms_step * 1e-3) / 1e9,
     }
 
@@ -227,7 +293,7 @@ def main(argv=None) -> int:
         del fcaches, fk, fv
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_heads, wl.num_kv_heads))
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
     return 0

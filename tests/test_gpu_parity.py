@@ -243,3 +243,57 @@ def test_fp16_attention_matches_oracle(bsz, hq, hkv, n):
                                                        k[b, h // g, :n], v[b, h // g, :n])
                               for h in range(hq)]) for b in range(bsz)])
     assert_close(got, ref, f"fp16 b={bsz} hq={hq} hkv={hkv} n={n}")
+
+
+# --- prepared calls (arguments marshalled once) ----------------------------------------
+
+def test_prepared_calls_match_direct_calls(tiny):
+    c, d, ref = tiny
+    wl = c.wl
+    n = wl.context_len
+    k = W.kv_rows(1, 0, 0, "k", n).astype(np.float32)[None, None]
+    v = W.kv_rows(1, 0, 0, "v", n).astype(np.float32)[None, None]
+    ck, cv = torch.zeros_like(d["codes_k"]), torch.zeros_like(d["codes_v"])
+    ck2, cv2 = torch.zeros_like(ck), torch.zeros_like(cv)
+    vq.encode_append(dev(k), dev(v), d["lam"], d["cb_k"], d["cb_v"], ck, cv, 0)
+    enc = vq.prepare_encode_append(dev(k), dev(v), d["lam"], d["cb_k"], d["cb_v"], ck2, cv2, 0)
+    enc()
+    torch.cuda.synchronize()
+    assert torch.equal(ck, ck2) and torch.equal(cv, cv2)
+    att = vq.prepare_decode_attention(d["q"], d["lam"], d["cb_k"], d["cb_v"], ck2, cv2, n)
+    for _ in range(2):
+        att()
+        torch.cuda.synchronize()
+        assert_close(att.out.cpu().numpy().astype(np.float64), expected_all(c), "prepared")
+
+
+def test_prepared_step_replays_in_a_graph(tiny):
+    # append + attention captured once; every replay, with eager work and
+    # synchronisations in between, must give the eager result
+    c, d, _ = tiny
+    wl = c.wl
+    n = wl.context_len
+    k = dev(W.kv_rows(1, 0, 0, "k", 1, append=True).astype(np.float32)[None, None])
+    v = dev(W.kv_rows(1, 0, 0, "v", 1, append=True).astype(np.float32)[None, None])
+    ck, cv = d["codes_k"].clone(), d["codes_v"].clone()
+    enc = vq.prepare_encode_append(k, v, d["lam"], d["cb_k"], d["cb_v"], ck, cv, n - 1)
+    att = vq.prepare_decode_attention(d["q"], d["lam"], d["cb_k"], d["cb_v"], ck, cv, n)
+    enc()
+    att()
+    torch.cuda.synchronize()
+    eager = att.out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            enc()
+            att()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        att.out.fill_(float("nan"))
+        run_attention(d, n)                      # eager work between the replays
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(att.out.cpu().numpy(), eager.cpu().numpy(), rtol=1e-5,
+                                   atol=1e-6, err_msg=f"replay {rep}")

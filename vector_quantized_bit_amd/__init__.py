@@ -19,7 +19,8 @@ __all__ = [
     "LIB_PATH", "VqError", "Layout", "library", "make_layout", "transform_query",
     "encode_append", "decode_attention", "decode_attention_workspace_bytes",
     "decode_attention_default_splits", "fp16_decode_attention",
-    "fp16_attention_workspace_bytes", "status_string",
+    "fp16_attention_workspace_bytes", "status_string", "PreparedCall",
+    "prepare_encode_append", "prepare_decode_attention",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqkv.so")
@@ -149,8 +150,24 @@ def transform_query(q: torch.Tensor, lam: torch.Tensor, out: torch.Tensor | None
     return out
 
 
-def encode_append(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int) -> None:
-    """Encode k_new / v_new [B][Hkv][T][128] into slots [cur_len, cur_len+T)."""
+class PreparedCall:
+    """A C entry point with its arguments marshalled once.
+
+    Calling it passes the same pointers and sizes again, with the stream that
+    is current at call time (or ``stream``, a raw HIP stream handle), and
+    raises on a non-zero status.  The tensors named at preparation are kept
+    alive by the object; the caller must not resize or reallocate them."""
+
+    def __init__(self, name: str, fn, args: tuple, keep: tuple, device: torch.device):
+        self._name, self._fn, self._args, self._keep, self._device = name, fn, args, keep, device
+
+    def __call__(self, stream: int | None = None) -> None:
+        if stream is None:
+            stream = torch.cuda.current_stream(self._device).cuda_stream
+        _check(self._fn(*self._args, stream), self._name)
+
+
+def _encode_append_args(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int):
     _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
     _need(k_new.shape == v_new.shape and k_new.dim() == 4, "k_new/v_new must be [B][Hkv][T][128]")
     _need(k_new.dtype == v_new.dtype, "k_new and v_new must share a dtype")
@@ -158,11 +175,23 @@ def encode_append(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int)
     _need(k_new.shape[0] == codes_k.shape[0] and k_new.shape[1] == codes_k.shape[1],
           "k_new [B][Hkv] disagrees with the cache")
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
-    _check(library().vq_encode_append(ctypes.byref(lay), _ptr(k_new), _ptr(v_new),
-                                      _dtype_code(k_new), _ptr(lam), _ptr(cb_k), _ptr(cb_v),
-                                      _ptr(codes_k), _ptr(codes_v), k_new.shape[0], cur_len,
-                                      k_new.shape[2], _stream(k_new)),
-           "vq_encode_append")
+    return (ctypes.byref(lay), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(lam),
+            _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v), k_new.shape[0], cur_len,
+            k_new.shape[2]), lay
+
+
+def encode_append(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int) -> None:
+    """Encode k_new / v_new [B][Hkv][T][128] into slots [cur_len, cur_len+T)."""
+    args, _ = _encode_append_args(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len)
+    _check(library().vq_encode_append(*args, _stream(k_new)), "vq_encode_append")
+
+
+def prepare_encode_append(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v,
+                          cur_len: int) -> PreparedCall:
+    """``encode_append`` with its arguments validated and marshalled once."""
+    args, lay = _encode_append_args(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len)
+    return PreparedCall("vq_encode_append", library().vq_encode_append, args,
+                        (lay, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v), k_new.device)
 
 
 def decode_attention_default_splits(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads,
@@ -180,13 +209,8 @@ def decode_attention_workspace_bytes(codes_k, codes_v, cb_k, cb_v, batch, num_q_
                                                              num_splits))
 
 
-def decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
-                     num_splits: int = 0, out=None, workspace=None):
-    """Decode attention over the VQ cache -> float32 [B][Hq][128].
-
-    ``workspace`` (optional, reusable): a uint8 device tensor of at least
-    ``decode_attention_workspace_bytes(...)`` bytes; its contents do not
-    matter."""
+def _decode_attention_args(q, lam, cb_k, cb_v, codes_k, codes_v, context_len, num_splits, out,
+                           workspace):
     _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
     _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
     batch, hq = q.shape[0], q.shape[1]
@@ -197,12 +221,35 @@ def decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
                                                   context_len, num_splits)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
-    _check(library().vq_decode_attention(ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam),
-                                         _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
-                                         batch, hq, context_len, num_splits, _ptr(out),
-                                         _ptr(workspace), workspace.numel(), _stream(q)),
-           "vq_decode_attention")
+    args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam), _ptr(cb_k), _ptr(cb_v),
+            _ptr(codes_k), _ptr(codes_v), batch, hq, context_len, num_splits, _ptr(out),
+            _ptr(workspace), workspace.numel())
+    return args, lay, out, workspace
+
+
+def decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
+                     num_splits: int = 0, out=None, workspace=None):
+    """Decode attention over the VQ cache -> float32 [B][Hq][128].
+
+    ``workspace`` (optional, reusable): a uint8 device tensor of at least
+    ``decode_attention_workspace_bytes(...)`` bytes; its contents do not
+    matter."""
+    args, _, out, _ = _decode_attention_args(q, lam, cb_k, cb_v, codes_k, codes_v, context_len,
+                                             num_splits, out, workspace)
+    _check(library().vq_decode_attention(*args, _stream(q)), "vq_decode_attention")
     return out
+
+
+def prepare_decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
+                             num_splits: int = 0, out=None, workspace=None) -> PreparedCall:
+    """``decode_attention`` with its arguments validated and marshalled once;
+    the output tensor is the prepared call's ``out`` attribute."""
+    args, lay, out, workspace = _decode_attention_args(q, lam, cb_k, cb_v, codes_k, codes_v,
+                                                       context_len, num_splits, out, workspace)
+    call = PreparedCall("vq_decode_attention", library().vq_decode_attention, args,
+                        (lay, q, lam, cb_k, cb_v, codes_k, codes_v, out, workspace), q.device)
+    call.out = out
+    return call
 
 
 def fp16_attention_workspace_bytes(batch, num_q_heads, num_kv_heads, context_len,

@@ -1,103 +1,91 @@
 // Cross-split log-sum-exp merge of decode-attention partials.
 //
-// Every partial s of a (sequence, query head) — a split, or a wave within a
-// split — leaves, in base-2 units, the running max m_s, the running sum l_s = sum_t 2^(s_t - m_s) and the
-// unnormalised output o_s = sum_t 2^(s_t - m_s) v_t.  The softmax over the
-// union of the partials is
-//     out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s,
-// computed by folding partials pairwise with the FlashAttention rescaling step
-// of the VecInfer page's Appendix (block recurrence of m, l and O).  A
-// partial with no tokens has m = -inf and weighs 0.  The folds run in a fixed
-// order, so the result is reproducible bit for bit.
+// Every split s of a (sequence, query head) leaves, in base-2 units, its
+// running max m_s, its running sum l_s = sum_t 2^(x_t - m_s) and its
+// unnormalised output o_s = sum_t 2^(x_t - m_s) v_t.  The softmax over the
+// union of the splits is
+//     out = sum_s w_s o_s / sum_s w_s l_s,   w_s = 2^(m_s - M),  M = max_s m_s,
+// the block-merge step of the FlashAttention recurrence (VecInfer page,
+// Appendix: m, l and O rescaled by exp(m_old - m_new) across blocks), taken
+// here for all splits at once.  A split with no tokens has m = -inf and
+// weighs 0.
 //
-// Four 256-thread workgroups per (sequence, query head), one per 32
-// channels; 32 slices of 8 threads each take every 32nd partial.  A thread
-// issues the loads of 16 partials (m, l and 16 bytes of o) before using any,
-// folds them with the same rescaling step in registers, and the 32 slice
-// results are folded once more through LDS: one round trip to memory when
-// there are at most 512 partials.
+// One 128-thread workgroup per (sequence, query head).  The first 32 o_s
+// rows are requested before anything else; meanwhile the threads share the
+// m_s, l_s (split s on thread s mod 128), reduce M and the denominator, and
+// leave the weights in LDS.  Thread d then accumulates channel d over the
+// splits in split order, 32 loads in flight: the result is reproducible.
 #include "launchers.hpp"
 
 namespace vqkv {
 
 namespace {
-constexpr int kMergeThreads = 256;
-constexpr int kQuarter = 32;                       // channels per workgroup
-constexpr int kCols = kQuarter / 4;                // float4 columns per workgroup
-constexpr int kSlices = kMergeThreads / kCols;     // 32
-constexpr int kInFlight = 16;
-
-// fold (m2, l2, o2) into the running (m, l, o)
-__device__ __forceinline__ void fold(float& m, float& l, float4& o, float m2, float l2,
-                                     const float4& o2) {
-    if (m2 == -INFINITY) return;   // an empty partial
-    const float mn = fmaxf(m, m2);
-    const float a = (m == -INFINITY) ? 0.f : exp2f(m - mn);
-    const float b = exp2f(m2 - mn);
-    l = a * l + b * l2;
-    o.x = a * o.x + b * o2.x;
-    o.y = a * o.y + b * o2.y;
-    o.z = a * o.z + b * o2.z;
-    o.w = a * o.w + b * o2.w;
-    m = mn;
-}
+constexpr int kChunk = 32;
+constexpr int kPer = kMaxSplits / kHeadDim;   // splits per thread in the weight pass
+static_assert(kMaxSplits % kHeadDim == 0 && kMaxSplits % kChunk == 0, "split tiling");
 }  // namespace
 
-__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(int num_partials,
-                                                                       Partials part,
-                                                                       float* __restrict__ out) {
-    __shared__ float msl[kSlices], lsl[kSlices];
-    __shared__ float4 osl[kSlices][kCols];
+__global__ __launch_bounds__(kHeadDim) void merge_partials_kernel(int num_partials,
+                                                                  Partials part,
+                                                                  float* __restrict__ out) {
+    __shared__ float wsh[kMaxSplits];   // w_s, zero beyond num_partials
+    __shared__ float red[2][2];
 
     const size_t bh = blockIdx.x;
-    const int quarter = blockIdx.y;
-    const size_t base = bh * num_partials;
-    const int tid = threadIdx.x;
-    const int j = tid / kCols, c4 = tid % kCols;
-    const int col = quarter * kCols + c4;
+    const int d = threadIdx.x, lane = d & (kWave - 1), wave = d / kWave;
+    const int last = num_partials - 1;
+    const float* pm = part.m + bh * num_partials;
+    const float* pl = part.l + bh * num_partials;
+    const float* po = part.o + bh * num_partials * kHeadDim + d;
 
-    float m = -INFINITY, l = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = j; s0 < num_partials; s0 += kInFlight * kSlices) {
-        float mv[kInFlight], lv[kInFlight];
-        float4 ov[kInFlight];
+    float ov[kChunk];
 #pragma unroll
-        for (int u = 0; u < kInFlight; ++u) {
-            const int s = s0 + u * kSlices;
-            if (s < num_partials) {
-                mv[u] = part.m[base + s];
-                lv[u] = part.l[base + s];
-                ov[u] = reinterpret_cast<const float4*>(part.o + (base + s) * kHeadDim)[col];
-            } else {
-                mv[u] = -INFINITY;
-                lv[u] = 0.f;
-                ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
+    for (int u = 0; u < kChunk; ++u) ov[u] = po[static_cast<size_t>(min(u, last)) * kHeadDim];
+
+    float mv[kPer], lv[kPer];
 #pragma unroll
-        for (int u = 0; u < kInFlight; ++u) fold(m, l, o, mv[u], lv[u], ov[u]);
+    for (int i = 0; i < kPer; ++i) {
+        const int s = d + i * kHeadDim;
+        mv[i] = (s < num_partials) ? pm[s] : -INFINITY;
+        lv[i] = (s < num_partials) ? pl[s] : 0.f;
     }
-    osl[j][c4] = o;
-    if (c4 == 0) {
-        msl[j] = m;
-        lsl[j] = l;
-    }
+    float mx = mv[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) mx = fmaxf(mx, mv[i]);
+    mx = wave_max(mx);
+    if (lane == 0) red[0][wave] = mx;
     __syncthreads();
-    if (tid < kQuarter) {
-        float mm = -INFINITY, ll = 0.f;
-        float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
+    mx = fmaxf(red[0][0], red[0][1]);
+    float den = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < kSlices; ++jj) fold(mm, ll, oo, msl[jj], lsl[jj], osl[jj][tid >> 2]);
-        const int e = tid & 3;
-        const float num = e == 0 ? oo.x : (e == 1 ? oo.y : (e == 2 ? oo.z : oo.w));
-        out[bh * kHeadDim + quarter * kQuarter + tid] = num / ll;
+    for (int i = 0; i < kPer; ++i) {
+        const float w = (mv[i] == -INFINITY) ? 0.f : exp2f(mv[i] - mx);
+        wsh[d + i * kHeadDim] = w;
+        den += w * lv[i];
     }
+    den = wave_sum(den);
+    if (lane == 0) red[1][wave] = den;
+    __syncthreads();
+    den = red[1][0] + red[1][1];
+
+    float num = 0.f;
+    for (int s0 = 0;;) {
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) num += wsh[s0 + u] * ov[u];
+        s0 += kChunk;
+        if (s0 >= num_partials) break;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u)
+            ov[u] = po[static_cast<size_t>(min(s0 + u, last)) * kHeadDim];
+    }
+    out[bh * kHeadDim + d] = num / den;
 }
 
 hipError_t launch_merge_partials(int batch, int num_q_heads, int num_partials, Partials part,
                                  float* out, hipStream_t stream) {
-    hipLaunchKernelGGL(merge_partials_kernel, dim3(batch * num_q_heads, kHeadDim / kQuarter),
-                       dim3(kMergeThreads), 0, stream, num_partials, part, out);
+    if (num_partials < 1 || num_partials > kMaxSplits) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(merge_partials_kernel, dim3(batch * num_q_heads), dim3(kHeadDim), 0,
+                       stream, num_partials, part, out);
     return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ namespace {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -66,6 +67,54 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
                                                                  CTRL, 0xF, 0xF, false));
+}
+
+// One butterfly stage of the Walsh–Hadamard transform across lanes at
+// distance M: the lane with bit M clear keeps a + b, the one with it set
+// b - a (its own value being b).  The partner's value comes from DPP (M = 1, 2, 4, 8) or a permlane swap (16, 32)
+// instead of an LDS permute.
+template <int M>
+__device__ __forceinline__ float partner(float x, int lane) {
+    if constexpr (M == 1) return dpp<0xB1>(x);                  // quad_perm 1,0,3,2
+    if constexpr (M == 2) return dpp<0x4E>(x);                  // quad_perm 2,3,0,1
+    if constexpr (M == 4) {
+        // both rotations in every lane: a DPP read from a lane that is off
+        // in exec yields the fallback, so this must not become a branch
+        const float down = dpp<0x124>(x);   // row_ror 4: lane i - 4
+        const float up = dpp<0x12C>(x);     // row_ror 12: lane i + 4
+        return (lane & 4) ? down : up;
+    }
+    if constexpr (M == 8) return dpp<0x128>(x);                 // row_ror 8
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if constexpr (M == 16) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __builtin_bit_cast(float, (lane & 16) ? sw[0] : sw[1]);
+    } else {
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __builtin_bit_cast(float, (lane & 32) ? sw[0] : sw[1]);
+    }
+}
+
+template <int M>
+__device__ __forceinline__ void butterfly(float& x0, float& x1, int lane) {
+    const float p0 = partner<M>(x0, lane), p1 = partner<M>(x1, lane);
+    const bool upper = (lane & M) != 0;
+    x0 = upper ? p0 - x0 : x0 + p0;
+    x1 = upper ? p1 - x1 : x1 + p1;
+}
+
+// Unnormalised (+-1) Walsh–Hadamard transform of a 128-vector held by one
+// wave, lane l holding elements 2l and 2l + 1; natural order in and out.
+__device__ __forceinline__ void fwht128(float& x0, float& x1, int lane) {
+    const float a = x0 + x1, b = x0 - x1;
+    x0 = a;
+    x1 = b;
+    butterfly<1>(x0, x1, lane);
+    butterfly<2>(x0, x1, lane);
+    butterfly<4>(x0, x1, lane);
+    butterfly<8>(x0, x1, lane);
+    butterfly<16>(x0, x1, lane);
+    butterfly<32>(x0, x1, lane);
 }
 
 // max / sum over the 16 lanes of a DPP row, result in every lane of the row
@@ -179,9 +228,6 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     __shared__ half8_t qa[4][64];
     __shared__ float wm[kWaves][G], wl[kWaves][G];
     __shared__ uint32_t tile_ctr;   // next 32-token tile of the split to hand out
-    // q~ (fp32) lives in the p buffers during the prologue
-    static_assert(sizeof(float) * G * kHeadDim <= sizeof(pbuf), "q~ fits in the p buffers");
-    float (*qsh)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&pbuf[0][0]);
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -203,32 +249,31 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 
     // ---- prologue ----------------------------------------------------------
     if (tid == 0) tile_ctr = kWaves;   // tiles 0 .. kWaves-1 go to waves 0 .. kWaves-1
-    // codebook entries and q go out first (they gate the table and q~), then
-    // the first tile of codes; both are in flight while the tables are built.
+    // Every prologue load is unconditional (indices clamped into range, code
+    // loads range-checked), so the waits that follow can count outstanding
+    // loads instead of draining them: codebook entries, q and lambda go out
+    // first (they gate the tables and q~), then the first tile of codes, which
+    // stays in flight while the tables are built.
     const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
     const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
-    uint2 centroid = make_uint2(0, 0);
+    uint2 centroid;
+    uint2 kcent[KBITS == 8 ? 1 : 4];
     if constexpr (KBITS == 8) {
         // thread: code = tid / 4, table = (tid / 2) % 2, slots 16 (tid % 2) .. + 15
         centroid = ((tid >> 1) & 1) ? vsrc[tid >> 2] : ksrc[tid >> 2];
     } else {
-        if (tid < 512) centroid = vsrc[tid >> 1];
+        centroid = vsrc[(tid >> 1) & 255];                  // used by tid < 512
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kcent[i] = ksrc[tid + i * kThreads];
     }
-    float x0 = 0.f, x1 = 0.f;
-    float2 lam2 = make_float2(0.f, 0.f);
-    if (wave < G) {
-        const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + wave;
-        if (q_f32) {
-            const float2 v = reinterpret_cast<const float2*>(q)[vec * (kHeadDim / 2) + lane];
-            x0 = v.x;
-            x1 = v.y;
-        } else {
-            const uint32_t w = reinterpret_cast<const uint32_t*>(q)[vec * (kHeadDim / 2) + lane];
-            x0 = lo_half_to_float(w);
-            x1 = hi_half_to_float(w);
-        }
-        lam2 = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
-    }
+    // q row of head min(wave, G - 1), two consecutive elements per lane: as
+    // fp32, words 2 lane and 2 lane + 1; as fp16, both halves of word lane
+    const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + min(wave, G - 1);
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(q) +
+                         (q_f32 ? vec * kHeadDim + 2 * lane : vec * (kHeadDim / 2) + lane);
+    const uint32_t qw0 = qw[0];
+    const uint32_t qw1 = qw[q_f32 ? 1 : 0];
+    const float2 lam2 = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
 
     KChunk<KBITS> kA[2], kB[2];
     uint2 vA[2], vB[2];
@@ -244,7 +289,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         vv_[0] = make_uint2(v0[0], v0[1]);
         vv_[1] = make_uint2(v1[0], v1[1]);
     };
-    if (wave * kTok < t_len) load_tile(wave * kTok, kA, vA);
+    load_tile(wave * kTok, kA, vA);   // past the split's end: range-checked, reads zeros
+    __builtin_amdgcn_sched_barrier(0);   // keep the table writes (and their wait) below
 
     {
         const uint4 cc = make_uint4(centroid.x, centroid.y, centroid.x, centroid.y);
@@ -254,8 +300,9 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 #pragma unroll
             for (int s = 0; s < 8; ++s) dst[s] = cc;
         } else {
-            for (int e = tid; e < 4096; e += kThreads)
-                *reinterpret_cast<uint2*>(tab + e * 8) = ksrc[e];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint2*>(tab + (tid + i * kThreads) * 8) = kcent[i];
             if (tid < 512) {
                 uint4* dst = reinterpret_cast<uint4*>(tab + kTable + (tid >> 1) * 256 + (tid & 1) * 128);
 #pragma unroll
@@ -263,30 +310,31 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             }
         }
     }
-    if (wave < G) {
-        x0 *= lam2.x;
-        x1 *= lam2.y;
-        wave_fwht128(x0, x1);
-        qsh[wave][2 * lane] = x0 * kScoreScaleLog2;
-        qsh[wave][2 * lane + 1] = x1 * kScoreScaleLog2;
-    }
-    __syncthreads();
-    // score A operand, shared by every wave: lane (16 grp' + r) holds row r of
-    // q~ for dims 32 grp' + 8 kk + e (K-step kk, element e); thread tid < 256
-    // builds entry (kk = tid / 64, lane = tid % 64)
-    if (tid < 256) {
-        const int kk = tid >> 6, ql = tid & 63;
-        const int r = ql & 15, qg = ql >> 4;
-        const int h = 2 * (r >> 2) + (r & 1);
-        const bool lo_part = (r & 2) != 0;
-        half8_t a;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = (h < G) ? qsh[h][32 * qg + 8 * kk + e] : 0.f;
-            const _Float16 hi = static_cast<_Float16>(x);
-            a[e] = lo_part ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
-        }
-        qa[kk][ql] = a;
+    float x0 = q_f32 ? __builtin_bit_cast(float, qw0) : lo_half_to_float(qw0);
+    float x1 = q_f32 ? __builtin_bit_cast(float, qw1) : hi_half_to_float(qw0);
+    // Every wave transforms (waves >= G a copy of head G - 1, discarded), so
+    // the q loads are not sunk behind the tile loads into a branch.  Waves
+    // 0 .. 7 then write head `wave` (zeros for wave >= G) straight into the
+    // score A operand, shared by every wave: lane (16 qg + r) of K-step kk
+    // holds row r for dims 32 qg + 8 kk + e, e = 0 .. 7, where row r is head
+    // 2 (r / 4) + r % 2, its fp16 high part for r % 4 < 2, else the low part
+    // (x - hi rounded to fp16).  This lane's dims 2 lane, 2 lane + 1 are
+    // elements e = 2 (lane % 4), + 1 of entry qg = lane / 16, kk = lane % 16 / 4.
+    x0 *= lam2.x;
+    x1 *= lam2.y;
+    fwht128(x0, x1, lane);
+    if (wave < 8) {
+        const bool real = wave < G;
+        x0 = real ? x0 * kScoreScaleLog2 : 0.f;
+        x1 = real ? x1 * kScoreScaleLog2 : 0.f;
+        const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+        const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
+        const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
+        const int r = 4 * (wave >> 1) + (wave & 1);
+        const int kk = (lane & 15) >> 2, qg = lane >> 4;
+        uint32_t* row = reinterpret_cast<uint32_t*>(&qa[kk][16 * qg + r]) + (lane & 3);
+        row[0] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
+        row[8] = __builtin_bit_cast(uint32_t, half2_t{l0, l1});   // row r + 2
     }
     __syncthreads();
 
