@@ -192,39 +192,70 @@ def main(argv=None) -> int:
     caches = [(ck0, cv0)] + [(ck0.clone(), cv0.clone()) for _ in range(copies - 1)]
     out = torch.empty((bsz, hq, 128), dtype=torch.float32, device=dev)
     splits = args.splits or vq.decode_attention_default_splits(ck0, cv0, cb_k, cb_v, bsz, hq, n)
-    ws = torch.empty(vq.decode_attention_workspace_bytes(ck0, cv0, cb_k, cb_v, bsz, hq, n, splits),
-                     dtype=torch.uint8, device=dev)
 
-    # arguments marshalled once per cache copy, so the host stays ahead of the GPU
+    # Arguments are marshalled once per cache copy, so the host stays ahead
+    # of the GPU.  A step is the encoder's append followed by decode
+    # attention (the split pass, then the merge).
     appends = [vq.prepare_encode_append(k_new, v_new, lam, cb_k, cb_v, ck, cv, n - 1)
                for ck, cv in caches]
+    parts = vq.decode_attention_partials(q, lam, cb_k, cb_v, ck0, cv0, n, splits)
+    split_pass = [vq.prepare_decode_attention_partials(q, lam, cb_k, cb_v, ck, cv, n, splits,
+                                                       partials=parts) for ck, cv in caches]
+    merge = vq.prepare_merge_partials(parts, out)
+    ws = torch.empty(vq.decode_attention_workspace_bytes(ck0, cv0, cb_k, cb_v, bsz, hq, n, splits),
+                     dtype=torch.uint8, device=dev)
     attends = [vq.prepare_decode_attention(q, lam, cb_k, cb_v, ck, cv, n, splits, out, ws)
                for ck, cv in caches]
     stream = torch.cuda.current_stream(dev).cuda_stream
-
-    def step(i):
-        appends[i % copies](stream)
-        ev_a[i].record()
-        attends[i % copies](stream)
-        ev_b[i].record()
-
     steps, warm = args.steps, args.warmup
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(max(steps, warm))]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(max(steps, warm))]
+
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+
     for i in range(warm):
-        step(i)
+        appends[i % copies](stream)
+        split_pass[i % copies](stream)
+        merge(stream)
     torch.cuda.synchronize()
+
+    # 1. whole steps back to back: the throughput (no events inside, since
+    #    every event costs the stream a few microseconds)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        step(i)
+        appends[i % copies](stream)
+        split_pass[i % copies](stream)
+        merge(stream)
     stop.record()
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / steps
-    attn_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(steps)]
-    attn_us = float(np.mean(attn_ms) * 1e3)
-    attn_med_us = float(np.median(attn_ms) * 1e3)
+    ms_step = start.elapsed_time(stop) / steps
+
+    # 2. the same steps with an event pair around the split kernel alone
+    ev_a, ev_b = new_events(), new_events()
+    for i in range(steps):
+        appends[i % copies](stream)
+        ev_a[i].record()
+        split_pass[i % copies](stream)
+        ev_b[i].record()
+        merge(stream)
+    torch.cuda.synchronize()
+    split_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(steps)]
+
+    # 3. the same steps with an event pair around one vq_decode_attention
+    #    call (split pass and merge)
+    ev_a, ev_c = new_events(), new_events()
+    for i in range(steps):
+        appends[i % copies](stream)
+        ev_a[i].record()
+        attends[i % copies](stream)
+        ev_c[i].record()
+    torch.cuda.synchronize()
+    call_ms = [ev_a[i].elapsed_time(ev_c[i]) for i in range(steps)]
+
+    attn_us = float(np.mean(split_ms) * 1e3)
+    attn_med_us = float(np.median(split_ms) * 1e3)
+    call_us = float(np.mean(call_ms) * 1e3)
+    call_med_us = float(np.median(call_ms) * 1e3)
     assert torch.isfinite(out).all().item()
 
     if args.copy_calibration:
@@ -254,12 +285,15 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic["bytes"],
-                     "kernel": "vq_decode_attention: vq_attention_mfma_kernel + merge_partials_kernel",
+                     "kernel": "vq_attention_mfma_kernel (vq_decode_attention_partials)",
                      "bytes_per_launch": ab["total"], "bytes_per_unit": ab["per_unit"],
                      "units_per_launch": ab["units"], "avg_launch_us": attn_us,
                      "median_launch_us": attn_med_us,
                      "traffic_record": None if traffic is None else traffic["source"]},
         "step_hbm_gbps": ab["total"] / (ms_step * 1e-3) / 1e9,
+        "decode_attention": {"avg_us": call_us, "median_us": call_med_us,
+                             "gbps": ab["total"] / (call_us * 1e-6) / 1e9,
+                             "kernels": "vq_attention_mfma_kernel + merge_partials_kernel"},
     }
 
     if not args.no_fp16:

@@ -21,7 +21,7 @@
  * ---------------------------------------
  *  - All array pointers are DEVICE pointers allocated and owned by the
  *    caller.  The library allocates no device memory; split partials live in
- *    a caller-provided workspace.
+ *    a caller-provided workspace or caller-provided arrays.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call only enqueues work on that stream and returns without
  *    synchronising.  Faults inside kernels surface at the caller's next
@@ -148,6 +148,46 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype,
                         const uint8_t* codes_k, const uint8_t* codes_v, int32_t batch,
                         int32_t num_q_heads, int32_t context_len, int32_t num_splits,
                         float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of vq_decode_attention, for callers that place the split
+ * partials themselves, e.g. to merge partials of context shards held by
+ * different devices.
+ *
+ * vq_decode_attention_plan_splits: the split count the library uses for
+ * `requested` splits (0 = its default; larger requests are clamped so that
+ * no split is empty).  Returns 0 for invalid arguments.
+ *
+ * vq_decode_attention_partials: the split pass alone.  Split s of
+ * (sequence b, query head h) covers tokens [s T, min((s + 1) T, context_len))
+ * for a T fixed by the plan, and leaves, in base-2 units with
+ * x_t = log2(e) (q~ . k^_t) / sqrt(128):
+ *     part_m[b][h][s]     a reference value m (>= -inf)
+ *     part_l[b][h][s]     l = sum_t 2^(x_t - m)
+ *     part_o[b][h][s][:]  o = sum_t 2^(x_t - m) v^_t          (all fp32)
+ * i.e. one block of the FlashAttention recurrence (VecInfer page,
+ * Appendix).  num_splits must be a value vq_decode_attention_plan_splits
+ * returns for this shape (VQ_ERR_INVALID_ARG otherwise).  part_m and
+ * part_l hold B * Hq * num_splits floats, part_o 128 times as many.
+ * Other arguments and errors as for vq_decode_attention.
+ *
+ * vq_merge_partials: out[b][h][:] = sum_s w_s o_s / sum_s w_s l_s with
+ * w_s = 2^(m_s - max_s m_s), over the num_partials (1 .. 512) partials of
+ * each (sequence, query head) laid out as above; a partial with m = -inf
+ * weighs 0.  Partials of disjoint token sets may come from different calls
+ * or devices: the merge is the softmax over their union.
+ */
+int32_t vq_decode_attention_plan_splits(const vq_layout* layout, int32_t batch,
+                                        int32_t num_q_heads, int32_t context_len,
+                                        int32_t requested);
+int vq_decode_attention_partials(const vq_layout* layout, const void* q, int q_dtype,
+                                 const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                                 const uint8_t* codes_k, const uint8_t* codes_v, int32_t batch,
+                                 int32_t num_q_heads, int32_t context_len, int32_t num_splits,
+                                 float* part_m, float* part_l, float* part_o, void* stream);
+int vq_merge_partials(int32_t batch, int32_t num_q_heads, int32_t num_partials,
+                      const float* part_m, const float* part_l, const float* part_o, float* out,
+                      void* stream);
 
 /*
  * Uncompressed comparator: the same decode attention over an fp16 cache,

@@ -156,3 +156,56 @@ def test_fp16_attention_validation(lib):
     assert f(A, A, A, 1, 4, 1, 10, 5, 0, A, A, 8, None) == WORKSPACE
     need = lib.vq_fp16_attention_workspace_bytes(1, 4, 1, 10, 0)
     assert need > 0
+
+
+def test_plan_splits_is_a_fixed_point(lib):
+    layout = lay(hkv=8, cap=196608)
+    plan = lib.vq_decode_attention_plan_splits
+    default = plan(ctypes.byref(layout), 1, 32, 196608, 0)
+    assert default == lib.vq_decode_attention_default_splits(ctypes.byref(layout), 1, 32, 196608)
+    for req in (0, 1, 3, 7, 32, 100, 10 ** 6):
+        s = plan(ctypes.byref(layout), 1, 32, 196608, req)
+        assert 1 <= s <= 384          # 196608 tokens hold 384 sweeps of 512
+        assert plan(ctypes.byref(layout), 1, 32, 196608, s) == s
+    assert plan(ctypes.byref(layout), 1, 32, 1100, 10 ** 6) == 3
+    assert plan(None, 1, 32, 100, 0) == 0
+    assert plan(ctypes.byref(layout), 1, 32, 0, 0) == 0
+    assert plan(ctypes.byref(layout), 1, 32, 100, -1) == 0
+
+
+def partials(lib, layout, splits=1, n=100, pm=A, pl=A, po=A, **kw):
+    args = dict(q=A, q_dtype=0, lam=A, cbk=A, cbv=A, ck=A, cv=A, batch=1, hq=4)
+    args.update(kw)
+    return lib.vq_decode_attention_partials(
+        ctypes.byref(layout), args["q"], args["q_dtype"], args["lam"], args["cbk"], args["cbv"],
+        args["ck"], args["cv"], args["batch"], args["hq"], n, splits, pm, pl, po, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(splits=2), INVALID, "planned"),        # 100 tokens allow one split only
+    (dict(splits=-1), INVALID, "num_splits"),
+    (dict(pm=None), INVALID, "part_m"),
+    (dict(pl=MIS), INVALID, "part_l"),
+    (dict(po=None), INVALID, "part_o"),
+    (dict(n=0), INVALID, "context_len"),
+    (dict(n=1001), CAPACITY, "capacity"),
+    (dict(hq=3), INVALID, "multiple"),
+    (dict(ck=None), INVALID, "codes_k"),
+])
+def test_partials_validation(lib, kw, status, needle):
+    assert partials(lib, lay(hkv=2), **kw) == status, vq._last_error()
+    assert needle in vq._last_error()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((0, 4, 2, A, A, A, A), INVALID, "batch"),
+    ((1, 0, 2, A, A, A, A), INVALID, "num_q_heads"),
+    ((1, 4, 0, A, A, A, A), INVALID, "num_partials"),
+    ((1, 4, 513, A, A, A, A), INVALID, "num_partials"),
+    ((1, 4, 2, None, A, A, A), INVALID, "part_m"),
+    ((1, 4, 2, A, A, MIS, A), INVALID, "part_o"),
+    ((1, 4, 2, A, A, A, None), INVALID, "out"),
+])
+def test_merge_validation(lib, args, status, needle):
+    assert lib.vq_merge_partials(*args, None) == status, vq._last_error()
+    assert needle in vq._last_error()

@@ -297,3 +297,36 @@ def test_prepared_step_replays_in_a_graph(tiny):
         torch.cuda.synchronize()
         np.testing.assert_allclose(att.out.cpu().numpy(), eager.cpu().numpy(), rtol=1e-5,
                                    atol=1e-6, err_msg=f"replay {rep}")
+
+
+# --- split pass and merge as separate calls -------------------------------------------
+
+def test_partials_then_merge_equals_decode_attention(tiny):
+    c, d, ref = tiny
+    n = c.context_len
+    args = (d["q"], d["lam"], d["cb_k"], d["cb_v"], d["codes_k"], d["codes_v"], n)
+    for splits in (1, 2):
+        parts = vq.decode_attention_partials(*args, num_splits=splits)
+        assert parts[0].shape[2] == splits
+        out = vq.merge_partials(parts)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy().astype(np.float64), ref, f"partials+merge S={splits}")
+
+
+def test_merging_partials_of_context_shards(tiny):
+    # two caches holding disjoint token ranges (as two devices would): their
+    # partials, concatenated over the split axis, merge to the full attention
+    c, d, ref = tiny
+    n = c.context_len
+    cut = 700
+    shards = [(d["codes_k"][:, :, :cut].contiguous(), d["codes_v"][:, :, :cut].contiguous(), cut),
+              (d["codes_k"][:, :, cut:n].contiguous(), d["codes_v"][:, :, cut:n].contiguous(),
+               n - cut)]
+    parts = [vq.decode_attention_partials(d["q"], d["lam"], d["cb_k"], d["cb_v"], ck, cv, m)
+             for ck, cv, m in shards]
+    m = torch.cat([p[0] for p in parts], dim=2).contiguous()
+    l = torch.cat([p[1] for p in parts], dim=2).contiguous()
+    o = torch.cat([p[2] for p in parts], dim=2).contiguous()
+    out = vq.merge_partials((m, l, o))
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy().astype(np.float64), ref, "merged shards")

@@ -20,7 +20,9 @@ __all__ = [
     "encode_append", "decode_attention", "decode_attention_workspace_bytes",
     "decode_attention_default_splits", "fp16_decode_attention",
     "fp16_attention_workspace_bytes", "status_string", "PreparedCall",
-    "prepare_encode_append", "prepare_decode_attention",
+    "prepare_encode_append", "prepare_decode_attention", "decode_attention_plan_splits",
+    "decode_attention_partials", "merge_partials", "prepare_decode_attention_partials",
+    "prepare_merge_partials",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqkv.so")
@@ -66,6 +68,10 @@ def library() -> ctypes.CDLL:
         "vq_decode_attention_workspace_bytes": (_size, [lp, _i32, _i32, _i32, _i32]),
         "vq_decode_attention": (_c_int, [lp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                          _i32, _i32, _vp, _vp, _size, _vp]),
+        "vq_decode_attention_plan_splits": (_i32, [lp, _i32, _i32, _i32, _i32]),
+        "vq_decode_attention_partials": (_c_int, [lp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                  _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+        "vq_merge_partials": (_c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
         "vq_fp16_attention_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32]),
         "vq_fp16_decode_attention": (_c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _vp, _vp, _size, _vp]),
@@ -248,6 +254,92 @@ def prepare_decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: 
                                                        context_len, num_splits, out, workspace)
     call = PreparedCall("vq_decode_attention", library().vq_decode_attention, args,
                         (lay, q, lam, cb_k, cb_v, codes_k, codes_v, out, workspace), q.device)
+    call.out = out
+    return call
+
+
+def decode_attention_plan_splits(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads,
+                                 context_len, requested: int = 0) -> int:
+    """Split count the library uses for ``requested`` splits (0 = default)."""
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    return int(library().vq_decode_attention_plan_splits(ctypes.byref(lay), batch, num_q_heads,
+                                                         context_len, requested))
+
+
+def _partials_args(q, lam, cb_k, cb_v, codes_k, codes_v, context_len, num_splits, partials):
+    _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
+    batch, hq = q.shape[0], q.shape[1]
+    splits = decode_attention_plan_splits(codes_k, codes_v, cb_k, cb_v, batch, hq, context_len,
+                                          num_splits)
+    if partials is None:
+        m = torch.empty((batch, hq, splits), dtype=torch.float32, device=q.device)
+        partials = (m, torch.empty_like(m),
+                    torch.empty((batch, hq, splits, 128), dtype=torch.float32, device=q.device))
+    m, l, o = partials
+    for name, t, shape in (("m", m, (batch, hq, splits)), ("l", l, (batch, hq, splits)),
+                           ("o", o, (batch, hq, splits, 128))):
+        _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float32
+              and tuple(t.shape) == shape, f"partials {name} must be contiguous float32 {shape}")
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam), _ptr(cb_k), _ptr(cb_v),
+            _ptr(codes_k), _ptr(codes_v), batch, hq, context_len, splits, _ptr(m), _ptr(l),
+            _ptr(o))
+    return args, lay, partials
+
+
+def decode_attention_partials(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
+                              num_splits: int = 0, partials=None):
+    """The split pass alone -> (m [B][Hq][S], l [B][Hq][S], o [B][Hq][S][128]),
+    S = decode_attention_plan_splits(..., num_splits)."""
+    args, _, partials = _partials_args(q, lam, cb_k, cb_v, codes_k, codes_v, context_len,
+                                       num_splits, partials)
+    _check(library().vq_decode_attention_partials(*args, _stream(q)),
+           "vq_decode_attention_partials")
+    return partials
+
+
+def prepare_decode_attention_partials(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
+                                      num_splits: int = 0, partials=None) -> PreparedCall:
+    """``decode_attention_partials`` marshalled once; the partials are the
+    prepared call's ``partials`` attribute."""
+    args, lay, partials = _partials_args(q, lam, cb_k, cb_v, codes_k, codes_v, context_len,
+                                         num_splits, partials)
+    call = PreparedCall("vq_decode_attention_partials", library().vq_decode_attention_partials,
+                        args, (lay, q, lam, cb_k, cb_v, codes_k, codes_v) + tuple(partials),
+                        q.device)
+    call.partials = partials
+    return call
+
+
+def _merge_args(partials, out):
+    m, l, o = partials
+    _need(m.dim() == 3 and l.shape == m.shape and o.dim() == 4 and o.shape[:3] == m.shape
+          and o.shape[3] == 128, "partials must be m, l [B][Hq][S] and o [B][Hq][S][128]")
+    for name, t in (("m", m), ("l", l), ("o", o)):
+        _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float32,
+              f"partials {name} must be a contiguous float32 device tensor")
+    batch, hq, splits = m.shape
+    if out is None:
+        out = torch.empty((batch, hq, 128), dtype=torch.float32, device=m.device)
+    _need(out.is_cuda and out.is_contiguous() and out.dtype == torch.float32
+          and tuple(out.shape) == (batch, hq, 128), "out must be contiguous float32 [B][Hq][128]")
+    return (batch, hq, splits, _ptr(m), _ptr(l), _ptr(o), _ptr(out)), out
+
+
+def merge_partials(partials, out=None):
+    """Log-sum-exp merge of (m, l, o) partials over their split axis."""
+    args, out = _merge_args(partials, out)
+    _check(library().vq_merge_partials(*args, _stream(out)), "vq_merge_partials")
+    return out
+
+
+def prepare_merge_partials(partials, out=None) -> PreparedCall:
+    """``merge_partials`` marshalled once; the output is the prepared call's
+    ``out`` attribute."""
+    args, out = _merge_args(partials, out)
+    call = PreparedCall("vq_merge_partials", library().vq_merge_partials, args,
+                        tuple(partials) + (out,), out.device)
     call.out = out
     return call
 

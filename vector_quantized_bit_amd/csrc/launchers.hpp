@@ -19,12 +19,12 @@ hipError_t launch_transform_query(const void* q, bool q_f32, const float* lambda
                                   int num_q_heads, int num_kv_heads, float* q_tilde,
                                   hipStream_t stream);
 
-// Split-K decode attention over the VQ cache on the matrix cores, followed by
-// the cross-split merge when there is more than one split.
+// Split-K decode attention over the VQ cache on the matrix cores: one
+// partial (m, l, o) per (sequence, query head, split).
 hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bool q_f32,
                                const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                                const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                               float* out, hipStream_t stream);
+                               hipStream_t stream);
 
 // out[bh][:] from the num_partials partials of every (sequence, query head) bh.
 hipError_t launch_merge_partials(int batch, int num_q_heads, int num_partials, Partials part,

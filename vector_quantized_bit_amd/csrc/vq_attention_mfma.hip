@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint16_t* __restrict__ cb_k, const uint16_t* __restrict__ cb_v,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v, int num_q_heads,
     int num_kv_heads, int capacity, int context_len, int num_splits, int tokens_per_split,
-    Partials part, float* __restrict__ out) {
+    Partials part) {
     static_assert(G >= 1 && G <= 8, "2G MFMA rows");
     constexpr int KROW = kNumSub * KBITS / 8;
 
@@ -531,13 +531,13 @@ template <int KBITS>
 hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q, bool q_f32,
                          const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                          const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                         float* out, hipStream_t stream) {
+                         hipStream_t stream) {
 #define VQKV_LAUNCH(GG)                                                                       \
     case GG:                                                                                  \
         hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS>), grid, dim3(kThreads), 0,    \
                            stream, q, q_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,   \
                            s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
-                           s.num_splits, s.tokens_per_split, part, out);             \
+                           s.num_splits, s.tokens_per_split, part);                   \
         break;
     switch (group) {
         VQKV_LAUNCH(1)
@@ -560,16 +560,13 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
 hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bool q_f32,
                                const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                                const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                               float* out, hipStream_t stream) {
+                               hipStream_t stream) {
     const dim3 grid(s.num_splits, s.num_kv_heads, s.batch);
     const int group = s.num_q_heads / s.num_kv_heads;
-    const hipError_t e =
-        (k_bits == 8) ? launch_mfma_g<8>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
-                                         codes_v, part, out, stream)
-                      : launch_mfma_g<12>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
-                                          codes_v, part, out, stream);
-    if (e != hipSuccess) return e;
-    return launch_merge_partials(s.batch, s.num_q_heads, s.num_splits, part, out, stream);
+    return (k_bits == 8) ? launch_mfma_g<8>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
+                                            codes_k, codes_v, part, stream)
+                         : launch_mfma_g<12>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
+                                             codes_k, codes_v, part, stream);
 }
 
 }  // namespace vqkv

@@ -188,11 +188,24 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
     return partials_bytes(batch, num_q_heads, p.num_splits);
 }
 
-int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
-                        const uint16_t* cb_k, const uint16_t* cb_v, const uint8_t* codes_k,
-                        const uint8_t* codes_v, int32_t batch, int32_t num_q_heads,
-                        int32_t context_len, int32_t num_splits, float* out, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+int32_t vq_decode_attention_plan_splits(const vq_layout* layout, int32_t batch,
+                                        int32_t num_q_heads, int32_t context_len,
+                                        int32_t requested) {
+    (void)num_q_heads;
+    if (layout == nullptr || batch < 1 || context_len < 1 || layout->num_kv_heads < 1 ||
+        requested < 0)
+        return 0;
+    return plan_splits(batch * layout->num_kv_heads, context_len, requested, vqkv::kVqTile)
+        .num_splits;
+}
+
+namespace {
+
+// Everything the split pass checks, shared by the partials and the fused entry.
+int check_attention_args(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
+                         const uint16_t* cb_k, const uint16_t* cb_v, const uint8_t* codes_k,
+                         const uint8_t* codes_v, int32_t batch, int32_t num_q_heads,
+                         int32_t context_len, int32_t num_splits) {
     int st = check_layout(layout);
     if (st) return st;
     if ((st = check_heads(batch, num_q_heads, layout->num_kv_heads))) return st;
@@ -210,22 +223,90 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
     VQ_REQUIRE_PTR(cb_v);
     VQ_REQUIRE_PTR(codes_k);
     VQ_REQUIRE_PTR(codes_v);
+    return VQ_OK;
+}
+
+int check_partials_ptrs(const float* part_m, const float* part_l, const float* part_o) {
+    VQ_REQUIRE_PTR(part_m);
+    VQ_REQUIRE_PTR(part_l);
+    VQ_REQUIRE_PTR(part_o);
+    return VQ_OK;
+}
+
+}  // namespace
+
+int vq_decode_attention_partials(const vq_layout* layout, const void* q, int q_dtype,
+                                 const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                                 const uint8_t* codes_k, const uint8_t* codes_v, int32_t batch,
+                                 int32_t num_q_heads, int32_t context_len, int32_t num_splits,
+                                 float* part_m, float* part_l, float* part_o, void* stream) {
+    int st = check_attention_args(layout, q, q_dtype, lambda, cb_k, cb_v, codes_k, codes_v, batch,
+                                  num_q_heads, context_len, num_splits);
+    if (st) return st;
+    if ((st = check_partials_ptrs(part_m, part_l, part_o))) return st;
+    const SplitPlan p =
+        plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
+    if (num_splits != p.num_splits)
+        return fail(VQ_ERR_INVALID_ARG,
+                    "num_splits %d is not a planned split count for this shape "
+                    "(vq_decode_attention_plan_splits gives %d)",
+                    num_splits, p.num_splits);
+    const vqkv::Partials part{part_m, part_l, part_o};
+    const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
+                                context_len, p.num_splits, p.tokens_per_split};
+    return hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
+                                                lambda, cb_k, cb_v, codes_k, codes_v, part,
+                                                static_cast<hipStream_t>(stream)),
+                      "decode_attention_partials launch");
+}
+
+int vq_merge_partials(int32_t batch, int32_t num_q_heads, int32_t num_partials,
+                      const float* part_m, const float* part_l, const float* part_o, float* out,
+                      void* stream) {
+    if (batch < 1 || batch > 65535)
+        return fail(VQ_ERR_INVALID_ARG, "batch %d out of range [1, 65535]", batch);
+    if (num_q_heads < 1) return fail(VQ_ERR_INVALID_ARG, "num_q_heads %d < 1", num_q_heads);
+    if (static_cast<int64_t>(batch) * num_q_heads > 0x7fffffff)
+        return fail(VQ_ERR_INVALID_ARG, "batch * num_q_heads too large");
+    if (num_partials < 1 || num_partials > vqkv::kMaxSplits)
+        return fail(VQ_ERR_INVALID_ARG, "num_partials %d out of range [1, %d]", num_partials,
+                    vqkv::kMaxSplits);
+    int st = check_partials_ptrs(part_m, part_l, part_o);
+    if (st) return st;
+    VQ_REQUIRE_PTR(out);
+    const vqkv::Partials part{const_cast<float*>(part_m), const_cast<float*>(part_l),
+                              const_cast<float*>(part_o)};
+    return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, num_partials, part, out,
+                                                  static_cast<hipStream_t>(stream)),
+                      "merge_partials launch");
+}
+
+int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
+                        const uint16_t* cb_k, const uint16_t* cb_v, const uint8_t* codes_k,
+                        const uint8_t* codes_v, int32_t batch, int32_t num_q_heads,
+                        int32_t context_len, int32_t num_splits, float* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    int st = check_attention_args(layout, q, q_dtype, lambda, cb_k, cb_v, codes_k, codes_v, batch,
+                                  num_q_heads, context_len, num_splits);
+    if (st) return st;
     VQ_REQUIRE_PTR(out);
     const SplitPlan p =
         plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
-    const int nparts = p.num_splits;
-    const size_t need = partials_bytes(batch, num_q_heads, nparts);
+    const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
     if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, nparts);
+    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, p.num_splits);
     const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
                                 context_len, p.num_splits, p.tokens_per_split};
-    return hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
-                                                lambda, cb_k, cb_v, codes_k, codes_v, part, out,
-                                                static_cast<hipStream_t>(stream)),
-                      "decode_attention launch");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
+                                              lambda, cb_k, cb_v, codes_k, codes_v, part, s),
+                    "decode_attention launch");
+    if (st) return st;
+    return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, p.num_splits, part, out, s),
+                      "decode_attention merge launch");
 }
 
 size_t vq_fp16_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
