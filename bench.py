@@ -1,11 +1,12 @@
 """Benchmark: one decode step over a VQ-KV cache layer on one MI355X.
 
 A step is the whole hot path over one batch: append one new token per
-(sequence, KV head) with the HIP encoder (into the last slot of the cache),
-then decode attention of every query head over the full context.  The
-default workload is the Llama-3.1-8B-shaped layer at 196608 tokens (batch 1,
-32 query heads over 8 KV heads, D = 128, 2-bit K and V: 8-bit codes over
-4-dim sub-vectors, 256-entry fp16 codebooks).
+(sequence, KV head) into the last slot of the cache and run decode attention
+of every query head over the full context — one vq_decode_step call, whose
+split kernel encodes the token before attending.  The default workload is the
+Llama-3.1-8B-shaped layer at 196608 tokens (batch 1, 32 query heads over 8 KV
+heads, D = 128, 2-bit K and V: 8-bit codes over 4-dim sub-vectors, 256-entry
+fp16 codebooks).
 
 Inputs are seeded synthetic tensors (see ``workloads``); the cache is drawn
 directly as uniform codes.  Timing keeps every input resident in HBM and
@@ -35,19 +36,23 @@ HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30
 
 
-def algorithmic_bytes(wl: W.Workload, context_len: int) -> dict:
+def algorithmic_bytes(wl: W.Workload, context_len: int, append: bool = False) -> dict:
     """Bytes one decode-attention launch must move at minimum.
 
     Per KV token per KV head: (D/d) (bk + bv) / 8 bytes of codes (VecInfer
     page, Background: (d_h/d)(b/8) index bytes per vector), i.e. 64 B for 8-bit
     K and V codes; plus once per launch the fp16 codebooks (2^b x d x 2 bytes
-    each), q, lambda and the fp32 output."""
+    each), q, lambda and the fp32 output.  With `append`, the launch also reads
+    the new token's k and v rows (fp16) and writes its codes (its read of the
+    codes is already counted in the context)."""
     units = wl.batch * wl.num_kv_heads * context_len
     per_unit = wl.num_sub * (wl.k_bits + wl.v_bits) // 8
     fixed = (wl.num_kv_heads * ((1 << wl.k_bits) + (1 << wl.v_bits)) * wl.sub_dim * 2
              + wl.batch * wl.num_q_heads * wl.head_dim * 2
              + wl.num_kv_heads * wl.head_dim * 4
              + wl.batch * wl.num_q_heads * wl.head_dim * 4)
+    if append:
+        fixed += wl.batch * wl.num_kv_heads * (2 * wl.head_dim * 2 + per_unit)
     return {"per_unit": per_unit, "units": units, "total": per_unit * units + fixed}
 
 
@@ -194,13 +199,21 @@ def main(argv=None) -> int:
     splits = args.splits or vq.decode_attention_default_splits(ck0, cv0, cb_k, cb_v, bsz, hq, n)
 
     # Arguments are marshalled once per cache copy, so the host stays ahead
-    # of the GPU.  A step is the encoder's append followed by decode
-    # attention (the split pass, then the merge).
-    appends = [vq.prepare_encode_append(k_new, v_new, lam, cb_k, cb_v, ck, cv, n - 1)
-               for ck, cv in caches]
-    parts = vq.decode_attention_partials(q, lam, cb_k, cb_v, ck0, cv0, n, splits)
-    split_pass = [vq.prepare_decode_attention_partials(q, lam, cb_k, cb_v, ck, cv, n, splits,
-                                                       partials=parts) for ck, cv in caches]
+    # of the GPU.  A step appends one token per (sequence, KV head) at slot
+    # n - 1 and attends over all n tokens: vq_decode_step, i.e. one launch of
+    # the split kernel (which encodes the token) and the merge.
+    k_new2, v_new2 = k_new[:, :, 0].contiguous(), v_new[:, :, 0].contiguous()
+    step_parts = vq.decode_step_num_partials(ck0, cv0, cb_k, cb_v, bsz, hq, n - 1, args.splits)
+    ws_step = torch.empty(vq.decode_step_workspace_bytes(ck0, cv0, cb_k, cb_v, bsz, hq, n - 1,
+                                                         args.splits),
+                          dtype=torch.uint8, device=dev)
+    steps_fused = [vq.prepare_decode_step(q, k_new2, v_new2, lam, cb_k, cb_v, ck, cv, n - 1,
+                                          args.splits, out, ws_step) for ck, cv in caches]
+    parts = vq.decode_step_partials(q, k_new2, v_new2, lam, cb_k, cb_v, ck0, cv0, n - 1,
+                                    args.splits)
+    split_pass = [vq.prepare_decode_step_partials(q, k_new2, v_new2, lam, cb_k, cb_v, ck, cv,
+                                                  n - 1, args.splits, partials=parts)
+                  for ck, cv in caches]
     merge = vq.prepare_merge_partials(parts, out)
     ws = torch.empty(vq.decode_attention_workspace_bytes(ck0, cv0, cb_k, cb_v, bsz, hq, n, splits),
                      dtype=torch.uint8, device=dev)
@@ -209,13 +222,8 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev).cuda_stream
     steps, warm = args.steps, args.warmup
 
-    def new_events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-
     for i in range(warm):
-        appends[i % copies](stream)
-        split_pass[i % copies](stream)
-        merge(stream)
+        steps_fused[i % copies](stream)
     torch.cuda.synchronize()
 
     # 1. whole steps back to back: the throughput (no events inside, since
@@ -223,45 +231,40 @@ def main(argv=None) -> int:
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        appends[i % copies](stream)
-        split_pass[i % copies](stream)
-        merge(stream)
+        steps_fused[i % copies](stream)
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / steps
 
-    # 2. the same steps with an event pair around the split kernel alone
-    ev_a, ev_b = new_events(), new_events()
+    # 2. the split kernel alone: the steps' split passes back to back between
+    #    one event pair (per-launch event pairs would let the host fall behind
+    #    the GPU and time its gaps), averaged over the launches
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
     for i in range(steps):
-        appends[i % copies](stream)
-        ev_a[i].record()
         split_pass[i % copies](stream)
-        ev_b[i].record()
-        merge(stream)
+    ev1.record()
     torch.cuda.synchronize()
-    split_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(steps)]
+    split_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    merge(stream)
 
-    # 3. the same steps with an event pair around one vq_decode_attention
-    #    call (split pass and merge)
-    ev_a, ev_c = new_events(), new_events()
+    # 3. decode attention alone (no append): vq_decode_attention calls (split
+    #    pass and merge) back to back between one event pair
+    ev0.record()
     for i in range(steps):
-        appends[i % copies](stream)
-        ev_a[i].record()
         attends[i % copies](stream)
-        ev_c[i].record()
+    ev1.record()
     torch.cuda.synchronize()
-    call_ms = [ev_a[i].elapsed_time(ev_c[i]) for i in range(steps)]
+    call_us = ev0.elapsed_time(ev1) * 1e3 / steps
 
-    attn_us = float(np.mean(split_ms) * 1e3)
-    attn_med_us = float(np.median(split_ms) * 1e3)
-    call_us = float(np.mean(call_ms) * 1e3)
-    call_med_us = float(np.median(call_ms) * 1e3)
+    attn_us = float(split_us)
     assert torch.isfinite(out).all().item()
 
     if args.copy_calibration:
         copy_calibration(torch, dev)
 
-    ab = algorithmic_bytes(wl, n)
+    ab = algorithmic_bytes(wl, n, append=True)
+    ab_attn = algorithmic_bytes(wl, n)
     achieved = ab["total"] / (attn_us * 1e-6) / 1e9
     traffic = measured_traffic(wl.name)
     tokens = bsz * n
@@ -281,18 +284,18 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "batch": bsz, "context_len": n, "q_heads": hq,
                    "kv_heads": hkv, "head_dim": 128, "k_code_bits": wl.k_bits,
                    "v_code_bits": wl.v_bits, "sub_dim": 4, "append_tokens_per_step": 1,
-                   "num_splits": splits, "cold_cache_copies": copies},
+                   "step_partials": step_parts, "attention_splits": splits,
+                   "cold_cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic["bytes"],
-                     "kernel": "vq_attention_mfma_kernel (vq_decode_attention_partials)",
+                     "kernel": "vq_attention_mfma_kernel (vq_decode_step_partials: append + split pass)",
                      "bytes_per_launch": ab["total"], "bytes_per_unit": ab["per_unit"],
                      "units_per_launch": ab["units"], "avg_launch_us": attn_us,
-                     "median_launch_us": attn_med_us,
                      "traffic_record": None if traffic is None else traffic["source"]},
         "step_hbm_gbps": ab["total"] / (ms_step * 1e-3) / 1e9,
-        "decode_attention": {"avg_us": call_us, "median_us": call_med_us,
-                             "gbps": ab["total"] / (call_us * 1e-6) / 1e9,
+        "decode_attention": {"avg_us": call_us,
+                             "gbps": ab_attn["total"] / (call_us * 1e-6) / 1e9,
                              "kernels": "vq_attention_mfma_kernel + merge_partials_kernel"},
     }
 
@@ -323,7 +326,7 @@ def main(argv=None) -> int:
         f_us = float(np.mean([fa[i].elapsed_time(fb[i]) for i in range(reps)]) * 1e3)
         result["fp16_comparator"] = {
             "avg_launch_us": f_us, "gbps": fp16_bytes(wl, n) / (f_us * 1e-6) / 1e9,
-            "vq_speedup": f_us / attn_us, "cold_cache_copies": fcopies}
+            "vq_decode_attention_speedup": f_us / call_us, "cold_cache_copies": fcopies}
         del fcaches, fk, fv
 
     if not args.no_cpu_baseline:

@@ -190,6 +190,53 @@ int vq_merge_partials(int32_t batch, int32_t num_q_heads, int32_t num_partials,
                       void* stream);
 
 /*
+ * One decode step: encode the new token of every (sequence, KV head) into
+ * slot cur_len of the cache, then decode attention over the first
+ * cur_len + 1 tokens — one launch of the split kernel plus the merge.
+ * The results equal vq_encode_append(..., cur_len, num_new = 1, ...)
+ * followed by vq_decode_attention(..., context_len = cur_len + 1, ...):
+ * identical codes, outputs equal to fp32 rounding.
+ * VecInfer page, Method details (VQ KV cache in attention): each newly
+ * arrived key takes the online dual transform and is quantised with C_k,
+ * the value with C_v, both are concatenated to the cache, and the query
+ * attends over the updated cache.
+ * Inside the launch, one extra workgroup per (sequence, KV head) encodes the
+ * new token (fp64 decisions, ties to the lowest index, as vq_encode_append)
+ * and leaves that token's own partial; the other workgroups attend over the
+ * cur_len cached tokens in num_splits splits (0 = library default, which
+ * leaves room on the GPU for the extra workgroups).
+ *   k_new, v_new [B][Hkv][128] in kv_dtype (fp16 or fp32)
+ *   codes_k / codes_v: read over [0, cur_len), written at slot cur_len only.
+ *   workspace: at least vq_decode_step_workspace_bytes(...) bytes, any
+ *   contents; not shared by calls that run concurrently.
+ * Errors: VQ_ERR_CAPACITY if cur_len + 1 > capacity; VQ_ERR_INVALID_ARG if
+ * cur_len < 0; otherwise as for vq_encode_append and vq_decode_attention.
+ *
+ * vq_decode_step_num_partials: the partial count of a step (attention
+ * splits + 1) for `requested` splits (0 = default); 0 for invalid arguments.
+ * vq_decode_step_partials: the split pass alone, leaving num_partials
+ * partials per (sequence, query head) as vq_decode_attention_partials does
+ * (the last one is the new token's); num_partials must be a value
+ * vq_decode_step_num_partials returns for this shape.  vq_merge_partials
+ * completes it.
+ */
+int32_t vq_decode_step_num_partials(const vq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                    int32_t cur_len, int32_t requested);
+size_t vq_decode_step_workspace_bytes(const vq_layout* layout, int32_t batch,
+                                      int32_t num_q_heads, int32_t cur_len, int32_t requested);
+int vq_decode_step(const vq_layout* layout, const void* q, int q_dtype, const void* k_new,
+                   const void* v_new, int kv_dtype, const float* lambda, const uint16_t* cb_k,
+                   const uint16_t* cb_v, uint8_t* codes_k, uint8_t* codes_v, int32_t batch,
+                   int32_t num_q_heads, int32_t cur_len, int32_t num_splits, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
+                            const void* k_new, const void* v_new, int kv_dtype,
+                            const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                            uint8_t* codes_k, uint8_t* codes_v, int32_t batch,
+                            int32_t num_q_heads, int32_t cur_len, int32_t num_partials,
+                            float* part_m, float* part_l, float* part_o, void* stream);
+
+/*
  * Uncompressed comparator: the same decode attention over an fp16 cache,
  * o = softmax(q K^T / sqrt(128)) V with fp32 accumulation (VecInfer page,
  * Background, KV cache and attention).  No transform, no quantisation.

@@ -209,3 +209,53 @@ def test_partials_validation(lib, kw, status, needle):
 def test_merge_validation(lib, args, status, needle):
     assert lib.vq_merge_partials(*args, None) == status, vq._last_error()
     assert needle in vq._last_error()
+
+
+def step(lib, layout, cur=10, splits=0, kv_dtype=0, kn=A, vn=A, ws=A, ws_bytes=1 << 30, out=A,
+         hq=4):
+    return lib.vq_decode_step(ctypes.byref(layout), A, 0, kn, vn, kv_dtype, A, A, A, A, A, 1, hq,
+                              cur, splits, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cur=1000), CAPACITY, "capacity"),        # slot 1000 of a 1000-slot cache
+    (dict(cur=-1), INVALID, "cur_len"),
+    (dict(kv_dtype=5), INVALID, "kv_dtype"),
+    (dict(kn=None), INVALID, "k_new"),
+    (dict(vn=MIS), INVALID, "v_new"),
+    (dict(out=None), INVALID, "out"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(ws_bytes=8), WORKSPACE, "workspace"),
+    (dict(hq=3), INVALID, "multiple"),
+])
+def test_decode_step_validation(lib, kw, status, needle):
+    assert step(lib, lay(hkv=2), **kw) == status, vq._last_error()
+    assert needle in vq._last_error()
+
+
+def test_decode_step_partials_validation(lib):
+    f = lib.vq_decode_step_partials
+    layout = lay(hkv=2)
+    # 10 cached tokens allow one split: 2 partials, nothing else
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 4, 10, 0) == 2
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 4, 10, 5) == 2
+    assert f(ctypes.byref(layout), A, 0, A, A, 0, A, A, A, A, A, 1, 4, 10, 3, A, A, A,
+             None) == INVALID
+    assert "planned" in vq._last_error()
+    assert f(ctypes.byref(layout), A, 0, A, A, 0, A, A, A, A, A, 1, 4, 999, 2, A, None, A,
+             None) == INVALID
+    assert "part_l" in vq._last_error()
+
+
+def test_decode_step_plan_leaves_room_for_the_new_token_workgroups(lib):
+    layout = lay(hkv=8, cap=196609)
+    n = lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 196608, 0)
+    assert n == 32                                   # 31 splits x 8 heads + 8 = 256 workgroups
+    need = lib.vq_decode_step_workspace_bytes(ctypes.byref(layout), 1, 32, 196608, 0)
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    assert need == 2 * a256(4 * 32 * n) + a256(4 * 128 * 32 * n)
+    # the first token of a sequence: no cached tokens, one empty split
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 0, 0) == 2

@@ -6,6 +6,8 @@ fp64 reference has a strict winner (distance gap above 1e-9 (1 + d)); at a
 gap below that both indices are nearest to within fp64 rounding and the
 GPU's pick must be one of the tied minima.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -330,3 +332,133 @@ def test_merging_partials_of_context_shards(tiny):
     out = vq.merge_partials((m, l, o))
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy().astype(np.float64), ref, "merged shards")
+
+
+# --- decode step: append one token, then attend (one split-kernel launch) -------------
+
+def new_rows(wl, bsz, hkv, dtype):
+    k = np.stack([np.stack([W.kv_rows(wl.config_id, b, g, "k", 1, append=True)[0]
+                            for g in range(hkv)]) for b in range(bsz)]).astype(dtype)
+    v = np.stack([np.stack([W.kv_rows(wl.config_id, b, g, "v", 1, append=True)[0]
+                            for g in range(hkv)]) for b in range(bsz)]).astype(dtype)
+    return k, v
+
+
+def check_step(c, cur, splits=0, heads=None, what=""):
+    """decode_step at slot `cur` of cache `c`: codes at that slot bit-exact to
+    the oracle encoder (near-tie rule), nothing else written, output equal to
+    the oracle's attention over the cache read back from the device."""
+    wl = c.wl
+    bsz, hkv = c.codes_k.shape[:2]
+    dtype = np.float32 if wl.qkv_dtype == "f32" else np.float16
+    k, v = new_rows(wl, bsz, hkv, dtype)
+    d = upload(c)
+    out = vq.decode_step(d["q"], dev(k), dev(v), d["lam"], d["cb_k"], d["cb_v"], d["codes_k"],
+                         d["codes_v"], cur, num_splits=splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ck, cv = d["codes_k"].cpu().numpy(), d["codes_v"].cpu().numpy()
+    others = np.ones(ck.shape[2], bool)
+    others[cur] = False
+    assert np.array_equal(ck[:, :, others], c.codes_k[:, :, others]), what
+    assert np.array_equal(cv[:, :, others], c.codes_v[:, :, others]), what
+    kb = wl.k_bits
+    for b in range(bsz):
+        for g in range(hkv):
+            pk, pv, gk, gv = oracle.encode_append(k[b, g][None], v[b, g][None], c.lam[g],
+                                                  c.cb_k[g], c.cb_v[g], kb, 8)
+            kt = oracle.transform_keys(k[b, g][None], c.lam[g])
+            check_codes(ck[b, g, cur:cur + 1], pk, gk, kb, kt, c.cb_k[g], f"{what} K b{b} g{g}")
+            check_codes(cv[b, g, cur:cur + 1], pv, gv, 8, v[b, g][None], c.cb_v[g],
+                        f"{what} V b{b} g{g}")
+    after = dataclasses.replace(c, codes_k=ck, codes_v=cv, context_len=cur + 1)
+    if heads is None:
+        assert_close(got, expected_all(after), what)
+    else:
+        grp = wl.group
+        for b, g in heads:
+            assert_close(got[b, g * grp:(g + 1) * grp], expected_head(after, b, g),
+                         f"{what} b={b} kv={g}")
+    return got, ck, cv
+
+
+@pytest.mark.parametrize("cur,splits", [(0, 0), (1, 0), (31, 0), (32, 0), (33, 2), (511, 0),
+                                        (512, 2), (700, 0), (1023, 0), (1023, 2)])
+def test_decode_step_slot_positions(cur, splits):
+    wl = W.Workload(80, "adhoc", batch=2, num_q_heads=8, num_kv_heads=2, context_len=1024)
+    check_step(random_cache(wl), cur, splits, what=f"step cur={cur} S={splits}")
+
+
+@pytest.mark.parametrize("group,k_bits,cur,splits", [(5, 12, 1499, 0), (5, 12, 700, 2),
+                                                     (1, 8, 300, 0), (8, 12, 64, 0)])
+def test_decode_step_groups_and_widths(group, k_bits, cur, splits):
+    wl = W.Workload(85 + group, "adhoc", batch=2, num_q_heads=2 * group, num_kv_heads=2,
+                    context_len=1500, k_bits=k_bits)
+    check_step(random_cache(wl), cur, splits, what=f"step G={group} kbits={k_bits} cur={cur}")
+
+
+def test_decode_step_tiny_recipe_case(tiny):
+    # the chain's last token appended by the step: the oracle's own codes and
+    # attention over the whole chain (fp32 rows)
+    c, d, ref = tiny
+    n = c.context_len
+    k = W.kv_rows(1, 0, 0, "k", n).astype(np.float32)[n - 1][None, None]
+    v = W.kv_rows(1, 0, 0, "v", n).astype(np.float32)[n - 1][None, None]
+    ck, cv = d["codes_k"].clone(), d["codes_v"].clone()
+    ck[:, :, n - 1] = 0
+    cv[:, :, n - 1] = 0
+    out = vq.decode_step(d["q"], dev(k), dev(v), d["lam"], d["cb_k"], d["cb_v"], ck, cv, n - 1)
+    torch.cuda.synchronize()
+    k1, v1 = k[0, 0][None], v[0, 0][None]
+    _, _, gk, gv = oracle.encode_append(k1, v1, c.lam[0], c.cb_k[0], c.cb_v[0])
+    check_codes(ck.cpu().numpy()[0, 0, n - 1:n], c.codes_k[0, 0, n - 1:n], gk, 8,
+                oracle.transform_keys(k1, c.lam[0]), c.cb_k[0], "step chain K")
+    check_codes(cv.cpu().numpy()[0, 0, n - 1:n], c.codes_v[0, 0, n - 1:n], gv, 8, v1,
+                c.cb_v[0], "step chain V")
+    assert_close(out.cpu().numpy().astype(np.float64), ref, "step chain")
+
+
+def test_decode_step_equals_append_then_attend():
+    wl = W.Workload(81, "adhoc", batch=2, num_q_heads=8, num_kv_heads=2, context_len=3000)
+    c = random_cache(wl)
+    cur = 2999
+    k, v = new_rows(wl, 2, 2, np.float16)
+    d1, d2 = upload(c), upload(c)
+    out1 = vq.decode_step(d1["q"], dev(k), dev(v), d1["lam"], d1["cb_k"], d1["cb_v"],
+                          d1["codes_k"], d1["codes_v"], cur)
+    vq.encode_append(dev(k[:, :, None]), dev(v[:, :, None]), d2["lam"], d2["cb_k"], d2["cb_v"],
+                     d2["codes_k"], d2["codes_v"], cur)
+    out2 = vq.decode_attention(d2["q"], d2["lam"], d2["cb_k"], d2["cb_v"], d2["codes_k"],
+                               d2["codes_v"], cur + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(d1["codes_k"], d2["codes_k"]) and torch.equal(d1["codes_v"], d2["codes_v"])
+    np.testing.assert_allclose(out1.cpu().numpy(), out2.cpu().numpy(), rtol=1e-5, atol=1e-6)
+
+
+def test_decode_step_partials_then_merge():
+    wl = W.Workload(82, "adhoc", batch=1, num_q_heads=4, num_kv_heads=1, context_len=3000)
+    c = random_cache(wl)
+    k, v = new_rows(wl, 1, 1, np.float16)
+    d1, d2 = upload(c), upload(c)
+    parts = vq.decode_step_partials(d1["q"], dev(k), dev(v), d1["lam"], d1["cb_k"], d1["cb_v"],
+                                    d1["codes_k"], d1["codes_v"], 2999, num_splits=3)
+    assert parts[0].shape[2] == 4                  # 3 splits of the cached tokens + the new one
+    out1 = vq.merge_partials(parts)
+    out2 = vq.decode_step(d2["q"], dev(k), dev(v), d2["lam"], d2["cb_k"], d2["cb_v"],
+                          d2["codes_k"], d2["codes_v"], 2999, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(d1["codes_k"], d2["codes_k"]) and torch.equal(d1["codes_v"], d2["codes_v"])
+    np.testing.assert_allclose(out1.cpu().numpy(), out2.cpu().numpy(), rtol=1e-5, atol=1e-6)
+
+
+# full workload sizes, in the configuration bench.py times: the token goes to
+# the last slot of the context (or the first free slot with append room)
+STEP_FULL = [(4, None, [(0, 2), (0, 7)]), (5, 65536, [(0, 0), (7, 5)])]
+
+
+@pytest.mark.parametrize("config,cur,samples", STEP_FULL)
+def test_decode_step_full_size(config, cur, samples):
+    wl = W.WORKLOADS[config]
+    c = random_cache(wl)
+    cur = wl.context_len - 1 if cur is None else cur
+    check_step(c, cur, heads=samples, what=f"step config{config}")

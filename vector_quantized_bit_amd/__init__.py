@@ -22,7 +22,8 @@ __all__ = [
     "fp16_attention_workspace_bytes", "status_string", "PreparedCall",
     "prepare_encode_append", "prepare_decode_attention", "decode_attention_plan_splits",
     "decode_attention_partials", "merge_partials", "prepare_decode_attention_partials",
-    "prepare_merge_partials",
+    "prepare_merge_partials", "decode_step", "prepare_decode_step", "decode_step_partials",
+    "prepare_decode_step_partials", "decode_step_num_partials", "decode_step_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqkv.so")
@@ -72,6 +73,13 @@ def library() -> ctypes.CDLL:
         "vq_decode_attention_partials": (_c_int, [lp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _i32,
                                                   _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
         "vq_merge_partials": (_c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+        "vq_decode_step_num_partials": (_i32, [lp, _i32, _i32, _i32, _i32]),
+        "vq_decode_step_workspace_bytes": (_size, [lp, _i32, _i32, _i32, _i32]),
+        "vq_decode_step": (_c_int, [lp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
+                                    _i32, _i32, _i32, _i32, _vp, _vp, _size, _vp]),
+        "vq_decode_step_partials": (_c_int, [lp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp,
+                                             _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                             _vp]),
         "vq_fp16_attention_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32]),
         "vq_fp16_decode_attention": (_c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _vp, _vp, _size, _vp]),
@@ -341,6 +349,118 @@ def prepare_merge_partials(partials, out=None) -> PreparedCall:
     call = PreparedCall("vq_merge_partials", library().vq_merge_partials, args,
                         tuple(partials) + (out,), out.device)
     call.out = out
+    return call
+
+
+def _step_common(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v):
+    _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
+    batch, hkv = codes_k.shape[0], codes_k.shape[1]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t.is_cuda and t.is_contiguous() and t.numel() == batch * hkv * 128
+              and t.shape[0] == batch and t.shape[1] == hkv,
+              f"{name} must be contiguous [B][Hkv][128] (or [B][Hkv][1][128])")
+    _need(k_new.dtype == v_new.dtype, "k_new and v_new must share a dtype")
+    return batch, q.shape[1]
+
+
+def _step_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len, num_splits, out,
+               workspace):
+    batch, hq = _step_common(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v)
+    if out is None:
+        out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    if workspace is None:
+        nbytes = library().vq_decode_step_workspace_bytes(ctypes.byref(lay), batch, hq, cur_len,
+                                                         num_splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(k_new), _ptr(v_new),
+            _dtype_code(k_new), _ptr(lam), _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
+            batch, hq, cur_len, num_splits, _ptr(out), _ptr(workspace), workspace.numel())
+    return args, lay, out, workspace
+
+
+def decode_step(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int,
+                num_splits: int = 0, out=None, workspace=None):
+    """Encode k_new / v_new [B][Hkv][128] into slot ``cur_len``, then decode
+    attention over ``cur_len + 1`` tokens -> float32 [B][Hq][128]."""
+    args, _, out, _ = _step_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len,
+                                 num_splits, out, workspace)
+    _check(library().vq_decode_step(*args, _stream(q)), "vq_decode_step")
+    return out
+
+
+def prepare_decode_step(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int,
+                        num_splits: int = 0, out=None, workspace=None) -> PreparedCall:
+    """``decode_step`` marshalled once; the output is the call's ``out``."""
+    args, lay, out, workspace = _step_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v,
+                                           cur_len, num_splits, out, workspace)
+    call = PreparedCall("vq_decode_step", library().vq_decode_step, args,
+                        (lay, q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, out,
+                         workspace), q.device)
+    call.out = out
+    return call
+
+
+def decode_step_num_partials(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads, cur_len,
+                             requested: int = 0) -> int:
+    """Partials of a decode step: attention splits (``requested``, 0 =
+    default) + 1 for the new token."""
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    return int(library().vq_decode_step_num_partials(ctypes.byref(lay), batch, num_q_heads,
+                                                     cur_len, requested))
+
+
+def decode_step_workspace_bytes(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads, cur_len,
+                                requested: int = 0) -> int:
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    return int(library().vq_decode_step_workspace_bytes(ctypes.byref(lay), batch, num_q_heads,
+                                                        cur_len, requested))
+
+
+def _step_partials_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len,
+                        num_splits, partials):
+    batch, hq = _step_common(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v)
+    splits = decode_step_num_partials(codes_k, codes_v, cb_k, cb_v, batch, hq, cur_len,
+                                      num_splits)
+    if partials is None:
+        m = torch.empty((batch, hq, splits), dtype=torch.float32, device=q.device)
+        partials = (m, torch.empty_like(m),
+                    torch.empty((batch, hq, splits, 128), dtype=torch.float32, device=q.device))
+    m, l, o = partials
+    for name, t, shape in (("m", m, (batch, hq, splits)), ("l", l, (batch, hq, splits)),
+                           ("o", o, (batch, hq, splits, 128))):
+        _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float32
+              and tuple(t.shape) == shape, f"partials {name} must be contiguous float32 {shape}")
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(k_new), _ptr(v_new),
+            _dtype_code(k_new), _ptr(lam), _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
+            batch, hq, cur_len, splits, _ptr(m), _ptr(l), _ptr(o))
+    return args, lay, partials
+
+
+def decode_step_partials(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int,
+                         num_splits: int = 0, partials=None):
+    """``decode_step``'s split pass alone -> (m, l, o) partials over
+    ``decode_step_num_partials(..., num_splits)`` partials (the last is the new
+    token's)."""
+    args, _, partials = _step_partials_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v,
+                                            cur_len, num_splits, partials)
+    _check(library().vq_decode_step_partials(*args, _stream(q)), "vq_decode_step_partials")
+    return partials
+
+
+def prepare_decode_step_partials(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v,
+                                 cur_len: int, num_splits: int = 0,
+                                 partials=None) -> PreparedCall:
+    """``decode_step_partials`` marshalled once; the partials are the call's
+    ``partials`` attribute."""
+    args, lay, partials = _step_partials_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k,
+                                              codes_v, cur_len, num_splits, partials)
+    call = PreparedCall("vq_decode_step_partials", library().vq_decode_step_partials, args,
+                        (lay, q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v)
+                        + tuple(partials), q.device)
+    call.partials = partials
     return call
 
 

@@ -40,25 +40,100 @@ __device__ __forceinline__ T wave_sum(T v) {
     return v;
 }
 
+// The value held by the lane at distance M (lane ^ M) of the wave, for one
+// 32-bit word: DPP for M = 1, 2, 4, 8, a gfx950 permlane swap for 16 and 32,
+// so no LDS round trip.  Every lane must be active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int M>
+__device__ __forceinline__ uint32_t lane_partner(uint32_t x, int lane) {
+    if constexpr (M == 1) {
+        return dpp_u32<0xB1>(x);                   // quad_perm 1,0,3,2
+    } else if constexpr (M == 2) {
+        return dpp_u32<0x4E>(x);                   // quad_perm 2,3,0,1
+    } else if constexpr (M == 4) {
+        // both rotations in every lane: a DPP read from a lane that is off
+        // in exec yields the fallback, so this must not become a branch
+        const uint32_t down = dpp_u32<0x124>(x);   // row_ror 4: lane i - 4
+        const uint32_t up = dpp_u32<0x12C>(x);     // row_ror 12: lane i + 4
+        return (lane & 4) ? down : up;
+    } else if constexpr (M == 8) {
+        return dpp_u32<0x128>(x);                  // row_ror 8
+    } else if constexpr (M == 16) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? sw[0] : sw[1];
+    } else {
+        static_assert(M == 32, "distance within a wave");
+        const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? sw[0] : sw[1];
+    }
+}
+
+template <int M>
+__device__ __forceinline__ float lane_partner(float x, int lane) {
+    return __builtin_bit_cast(float, lane_partner<M>(__builtin_bit_cast(uint32_t, x), lane));
+}
+
+template <int M>
+__device__ __forceinline__ double lane_partner(double x, int lane) {
+    uint2 u = __builtin_bit_cast(uint2, x);
+    u.x = lane_partner<M>(u.x, lane);
+    u.y = lane_partner<M>(u.y, lane);
+    return __builtin_bit_cast(double, u);
+}
+
+// One butterfly stage at lane distance M: the lane with bit M clear keeps
+// a + b, the one with it set b - a (its own value being b).
+template <int M, typename T>
+__device__ __forceinline__ void butterfly(T& x0, T& x1, int lane) {
+    const T p0 = lane_partner<M>(x0, lane), p1 = lane_partner<M>(x1, lane);
+    const bool upper = (lane & M) != 0;
+    x0 = upper ? p0 - x0 : x0 + p0;
+    x1 = upper ? p1 - x1 : x1 + p1;
+}
+
 // Unnormalised Walsh–Hadamard transform (the +-1 Sylvester matrix H') of a
-// 128-vector held by one wave, two consecutive elements per lane
-// (lane l holds x[2l], x[2l+1]).  Butterfly (a, b) -> (a + b, a - b) on
-// element pairs at distance 1, 2, ..., 64; the result is in natural order.
+// 128-vector held by one wave, two consecutive elements per lane (lane l
+// holds x[2l], x[2l+1]).  Butterfly (a, b) -> (a + b, a - b) on element
+// pairs at distance 1, 2, ..., 64, each add rounded once; the result is in
+// natural order.  All 64 lanes must be active.
 template <typename T>
-__device__ __forceinline__ void wave_fwht128(T& x0, T& x1) {
+__device__ __forceinline__ void fwht128(T& x0, T& x1) {
     const int lane = threadIdx.x & (kWave - 1);
-    T a = x0 + x1;
-    T b = x0 - x1;
+    const T a = x0 + x1, b = x0 - x1;
     x0 = a;
     x1 = b;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const T p0 = __shfl_xor(x0, m, kWave);
-        const T p1 = __shfl_xor(x1, m, kWave);
-        const bool upper = (lane & m) != 0;
-        x0 = upper ? p0 - x0 : x0 + p0;
-        x1 = upper ? p1 - x1 : x1 + p1;
-    }
+    butterfly<1>(x0, x1, lane);
+    butterfly<2>(x0, x1, lane);
+    butterfly<4>(x0, x1, lane);
+    butterfly<8>(x0, x1, lane);
+    butterfly<16>(x0, x1, lane);
+    butterfly<32>(x0, x1, lane);
+}
+
+// Squared distance ||x - c||^2 of a 4-dim sub-vector to an fp16 centroid
+// (4 halves in c), in fp64 with every difference, product and sum rounded
+// separately and the 4 terms summed in order, as the fp64 reference does.
+__device__ __forceinline__ double sqdist4_f64(const double x[4], const uint2 c) {
+    const double c0 = half_bits_to_float(c.x & 0xffffu), c1 = half_bits_to_float(c.x >> 16);
+    const double c2 = half_bits_to_float(c.y & 0xffffu), c3 = half_bits_to_float(c.y >> 16);
+    const double e0 = __dadd_rn(x[0], -c0), e1 = __dadd_rn(x[1], -c1);
+    const double e2 = __dadd_rn(x[2], -c2), e3 = __dadd_rn(x[3], -c3);
+    double d = __dmul_rn(e0, e0);
+    d = __dadd_rn(d, __dmul_rn(e1, e1));
+    d = __dadd_rn(d, __dmul_rn(e2, e2));
+    d = __dadd_rn(d, __dmul_rn(e3, e3));
+    return d;
+}
+
+// Lexicographic (distance, index) order: the nearest centroid, exact ties
+// to the lowest index, whatever order candidates are combined in.
+__device__ __forceinline__ bool nearer(double d, uint32_t i, double d0, uint32_t i0) {
+    return d < d0 || (d == d0 && i < i0);
 }
 
 // Split partials of one (sequence, query head, split): running max m and

@@ -33,18 +33,6 @@ __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
     return static_cast<double>(half_bits_to_float(reinterpret_cast<const uint16_t*>(p)[i]));
 }
 
-__device__ __forceinline__ double sqdist4(const double x[4], const uint2 c) {
-    const double c0 = half_bits_to_float(c.x & 0xffffu), c1 = half_bits_to_float(c.x >> 16);
-    const double c2 = half_bits_to_float(c.y & 0xffffu), c3 = half_bits_to_float(c.y >> 16);
-    const double e0 = __dadd_rn(x[0], -c0), e1 = __dadd_rn(x[1], -c1);
-    const double e2 = __dadd_rn(x[2], -c2), e3 = __dadd_rn(x[3], -c3);
-    double d = __dmul_rn(e0, e0);
-    d = __dadd_rn(d, __dmul_rn(e1, e1));
-    d = __dadd_rn(d, __dmul_rn(e2, e2));
-    d = __dadd_rn(d, __dmul_rn(e3, e3));
-    return d;
-}
-
 // Nearest of `entries` LDS centroids to x among indices slice, slice + 8, ...,
 // combined across the 8 slices; returns the code for this thread's position.
 __device__ __forceinline__ uint32_t nearest(const double x[4], const uint2* cb, int entries,
@@ -53,7 +41,7 @@ __device__ __forceinline__ uint32_t nearest(const double x[4], const uint2* cb, 
     uint32_t arg = 0;
 #pragma unroll 4
     for (int c = slice; c < entries; c += kEncSlices) {
-        const double d = sqdist4(x, cb[c]);
+        const double d = sqdist4_f64(x, cb[c]);
         if (d < best) {
             best = d;
             arg = static_cast<uint32_t>(c);
@@ -68,7 +56,7 @@ __device__ __forceinline__ uint32_t nearest(const double x[4], const uint2* cb, 
     for (int s = 1; s < kEncSlices; ++s) {
         const double d = bd[s * kNumSub + pos];
         const uint32_t a = bi[s * kNumSub + pos];
-        if (d < b0 || (d == b0 && a < a0)) {
+        if (nearer(d, a, b0, a0)) {
             b0 = d;
             a0 = a;
         }
@@ -117,7 +105,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
                     static_cast<double>(lam[2 * lane]);
         double x1 = load_elem(k_new, f32, in_row * kHeadDim + 2 * lane + 1) /
                     static_cast<double>(lam[2 * lane + 1]);
-        wave_fwht128(x0, x1);
+        fwht128(x0, x1);
         xk[2 * lane] = x0 * kInvSqrtD64;
         xk[2 * lane + 1] = x1 * kInvSqrtD64;
     }

@@ -19,12 +19,26 @@ hipError_t launch_transform_query(const void* q, bool q_f32, const float* lambda
                                   int num_q_heads, int num_kv_heads, float* q_tilde,
                                   hipStream_t stream);
 
+// One new token per (sequence, KV head) to encode into slot append_pos
+// (k_new == nullptr: none).  k_new, v_new [B][Hkv][128].  The split pass
+// then leaves num_splits + 1 partials per (sequence, query head), the last
+// one for the new token; AttnShape covers the cached tokens only.
+struct AppendArgs {
+    const void* k_new = nullptr;
+    const void* v_new = nullptr;
+    bool kv_f32 = false;
+    int append_pos = -1;
+    uint8_t* codes_k = nullptr;   // the cache, written at that slot
+    uint8_t* codes_v = nullptr;
+};
+
 // Split-K decode attention over the VQ cache on the matrix cores: one
-// partial (m, l, o) per (sequence, query head, split).
+// partial (m, l, o) per (sequence, query head, split), plus the new token's
+// when appending.
 hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bool q_f32,
                                const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                                const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                               hipStream_t stream);
+                               const AppendArgs& append, hipStream_t stream);
 
 // out[bh][:] from the num_partials partials of every (sequence, query head) bh.
 hipError_t launch_merge_partials(int batch, int num_q_heads, int num_partials, Partials part,
@@ -41,7 +55,8 @@ hipError_t launch_fp16_attention_splits(const AttnShape& s, const uint16_t* q, c
 // Tokens one workgroup of the VQ split kernel processes per tile; split
 // lengths are multiples of it.
 constexpr int kVqWaves = 16;       // waves per workgroup of the VQ kernel; each leaves a partial
-constexpr int kVqTile = 512;       // = waves per workgroup x tokens per wave tile
+constexpr int kVqTile = 512;       // shortest split: waves per workgroup x tokens per wave tile
+constexpr int kVqTileGrain = 32;   // split lengths are multiples of one wave tile
 constexpr int kFp16Tile = 128;
 constexpr int kMaxSplits = 512;    // bound of the split planner
 

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void transform_query_kernel(
     const float2 l = reinterpret_cast<const float2*>(lam)[lane];
     x0 *= l.x;
     x1 *= l.y;
-    wave_fwht128(x0, x1);
+    fwht128(x0, x1);
     reinterpret_cast<float2*>(q_tilde)[vec * (kHeadDim / 2) + lane] =
         make_float2(x0 * kInvSqrtD, x1 * kInvSqrtD);
 }

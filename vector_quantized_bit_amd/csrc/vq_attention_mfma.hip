@@ -61,7 +61,7 @@ constexpr float kTau = 8.0f;              // lazy-rescale slack (log2 units)
 constexpr int kTable = 65536;             // bytes of one codebook table
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9
 
-static_assert(kStride == kVqTile, "split lengths are multiples of one sweep");
+static_assert(kStride == kVqTile && kTok == kVqTileGrain, "split planning matches the tiles");
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -69,52 +69,24 @@ __device__ __forceinline__ float dpp(float x) {
                                                                  CTRL, 0xF, 0xF, false));
 }
 
-// One butterfly stage of the Walsh–Hadamard transform across lanes at
-// distance M: the lane with bit M clear keeps a + b, the one with it set
-// b - a (its own value being b).  The partner's value comes from DPP (M = 1, 2, 4, 8) or a permlane swap (16, 32)
-// instead of an LDS permute.
-template <int M>
-__device__ __forceinline__ float partner(float x, int lane) {
-    if constexpr (M == 1) return dpp<0xB1>(x);                  // quad_perm 1,0,3,2
-    if constexpr (M == 2) return dpp<0x4E>(x);                  // quad_perm 2,3,0,1
-    if constexpr (M == 4) {
-        // both rotations in every lane: a DPP read from a lane that is off
-        // in exec yields the fallback, so this must not become a branch
-        const float down = dpp<0x124>(x);   // row_ror 4: lane i - 4
-        const float up = dpp<0x12C>(x);     // row_ror 12: lane i + 4
-        return (lane & 4) ? down : up;
-    }
-    if constexpr (M == 8) return dpp<0x128>(x);                 // row_ror 8
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    if constexpr (M == 16) {
-        const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        return __builtin_bit_cast(float, (lane & 16) ? sw[0] : sw[1]);
-    } else {
-        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        return __builtin_bit_cast(float, (lane & 32) ? sw[0] : sw[1]);
-    }
-}
-
-template <int M>
-__device__ __forceinline__ void butterfly(float& x0, float& x1, int lane) {
-    const float p0 = partner<M>(x0, lane), p1 = partner<M>(x1, lane);
-    const bool upper = (lane & M) != 0;
-    x0 = upper ? p0 - x0 : x0 + p0;
-    x1 = upper ? p1 - x1 : x1 + p1;
-}
-
-// Unnormalised (+-1) Walsh–Hadamard transform of a 128-vector held by one
-// wave, lane l holding elements 2l and 2l + 1; natural order in and out.
-__device__ __forceinline__ void fwht128(float& x0, float& x1, int lane) {
-    const float a = x0 + x1, b = x0 - x1;
-    x0 = a;
-    x1 = b;
-    butterfly<1>(x0, x1, lane);
-    butterfly<2>(x0, x1, lane);
-    butterfly<4>(x0, x1, lane);
-    butterfly<8>(x0, x1, lane);
-    butterfly<16>(x0, x1, lane);
-    butterfly<32>(x0, x1, lane);
+// fp32 squared distance of a 4-dim sub-vector (x rounded to fp32, squared
+// norm xx) to an fp16 centroid, and a bound err on its distance from the
+// exact value ||x - c||^2 of the unrounded x.  With u = 2^-24, rounding x
+// and each difference, square and sum once gives
+//     |d32 - d| <= 9 u (d + ||x||^2 + ||c||^2)
+// (each difference carries u (2|x_i| + |x_i - c_i|), its square twice that
+// times |x_i - c_i| plus u of itself, and 2|a||b| <= a^2 + b^2); fused
+// multiply-adds only remove roundings.  The bound used is 2^-18 (> 9 u) of
+// the same sum, plus 1e-30 for underflow.
+__device__ __forceinline__ float sqdist4_f32(const float x[4], float xx, const uint2 c,
+                                             float& err) {
+    const float c0 = half_bits_to_float(c.x & 0xffffu), c1 = half_bits_to_float(c.x >> 16);
+    const float c2 = half_bits_to_float(c.y & 0xffffu), c3 = half_bits_to_float(c.y >> 16);
+    const float e0 = x[0] - c0, e1 = x[1] - c1, e2 = x[2] - c2, e3 = x[3] - c3;
+    const float d = e0 * e0 + e1 * e1 + e2 * e2 + e3 * e3;
+    const float cc = c0 * c0 + c1 * c1 + c2 * c2 + c3 * c3;
+    err = 0x1p-18f * (d + xx + cc) + 1e-30f;
+    return d;
 }
 
 // max / sum over the 16 lanes of a DPP row, result in every lane of the row
@@ -181,6 +153,7 @@ struct KChunk<8> {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
         w = make_uint2(v[0], v[1]);
     }
+    __device__ void set(const uint8_t* p) { w = *reinterpret_cast<const uint2*>(p); }
     template <int I>
     __device__ uint32_t addr(uint32_t slot) const {
         return row_addr<I & 3>(I < 4 ? w.x : w.y, slot);
@@ -195,6 +168,12 @@ struct KChunk<12> {
         w0 = v[0];
         w1 = v[1];
         w2 = v[2];
+    }
+    __device__ void set(const uint8_t* p) {
+        const uint32_t* u = reinterpret_cast<const uint32_t*>(p);
+        w0 = u[0];
+        w1 = u[1];
+        w2 = u[2];
     }
     template <int I>
     __device__ uint32_t addr(uint32_t) const {
@@ -213,13 +192,182 @@ struct KChunk<12> {
 
 }  // namespace
 
+// The appended token of one (sequence, KV head), handled by one extra
+// workgroup of the split kernel while the others attend over the cached
+// tokens (VecInfer page, Method details, "VQ KV cache in attention": each
+// newly arrived key takes the online dual transform k~ = k diag(lambda)^-1
+// H_D and is quantised with C_k, its value with C_v, and both are
+// concatenated to the cache before the query attends).
+//  1. Codes: the nearest centroid of each 4-dim sub-vector (Background, VQ
+//     principle), distances in fp64 with every operation rounded separately,
+//     ties to the lowest index: the decisions of vq_encode_append.  Thread
+//     (slice, pos) scans centroids slice, slice + 32, ... of sub-vector pos;
+//     the 32 slices are combined by the lexicographic (distance, index)
+//     minimum.  The codes are written to the cache slot append_pos.
+//  2. Its attention partial, as one more split of one token: m = x (its
+//     base-2 score), l = 1, o = its dequantised value, at split index `slot`.
+// LDS: the codebooks unreplicated in `tab` (keys at 0, values at 32 KiB),
+// the scratch of the combination in `scratch` (the p buffers).
+template <int G, int KBITS>
+__device__ __forceinline__ void new_token_workgroup(
+    const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+    const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads,
+    int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v, Partials part,
+    int part_stride, int slot, uint8_t* tab, uint8_t* scratch, double (*xnew)[kHeadDim],
+    uint32_t (*newc)[kNumSub]) {
+    constexpr int KENT = 1 << KBITS;
+    constexpr int kVtab = 32768;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
+    const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
+    for (int i = tid; i < KENT; i += kThreads) reinterpret_cast<uint2*>(tab)[i] = ksrc[i];
+    if (tid < 256) reinterpret_cast<uint2*>(tab + kVtab)[tid] = vsrc[tid];
+
+    // q~ of head `wave` (fp32, base-2 score scale), two elements per lane
+    float x0 = 0.f, x1 = 0.f;
+    if (wave < G) {
+        const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + wave;
+        const uint32_t* qw = reinterpret_cast<const uint32_t*>(q) +
+                             (q_f32 ? vec * kHeadDim + 2 * lane : vec * (kHeadDim / 2) + lane);
+        const float2 lam2 = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
+        x0 = (q_f32 ? __builtin_bit_cast(float, qw[0]) : half_bits_to_float(qw[0] & 0xffffu)) *
+             lam2.x;
+        x1 = (q_f32 ? __builtin_bit_cast(float, qw[1]) : half_bits_to_float(qw[0] >> 16)) *
+             lam2.y;
+        fwht128(x0, x1);
+        x0 *= kScoreScaleLog2;
+        x1 *= kScoreScaleLog2;
+    } else if (wave == 8 || wave == 9) {
+        // k / lambda in fp64 with the +-1 transform and 1/sqrt(128) (wave 8);
+        // the value as is (wave 9)
+        const size_t row = static_cast<size_t>(b) * num_kv_heads + g;
+        const void* src = wave == 8 ? k_new : v_new;
+        double y0, y1;
+        if (kv_f32) {
+            const float2 v = reinterpret_cast<const float2*>(src)[row * (kHeadDim / 2) + lane];
+            y0 = v.x;
+            y1 = v.y;
+        } else {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(src)[row * (kHeadDim / 2) + lane];
+            y0 = half_bits_to_float(w & 0xffffu);
+            y1 = half_bits_to_float(w >> 16);
+        }
+        if (wave == 8) {
+            const float* lam = lambda + g * kHeadDim;
+            y0 = y0 / static_cast<double>(lam[2 * lane]);
+            y1 = y1 / static_cast<double>(lam[2 * lane + 1]);
+            fwht128(y0, y1);
+            y0 *= kInvSqrtD64;
+            y1 *= kInvSqrtD64;
+        }
+        xnew[wave - 8][2 * lane] = y0;
+        xnew[wave - 8][2 * lane + 1] = y1;
+    }
+    __syncthreads();
+
+    // 1. codes
+    const int pos = tid & 31, slice = tid >> 5;
+    double xk[4], xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        xk[i] = xnew[0][4 * pos + i];
+        xv[i] = xnew[1][4 * pos + i];
+    }
+    double dk = INFINITY, dv = INFINITY;
+    uint32_t ik = 0, iv = 0;
+    for (int c = slice; c < KENT; c += 32) {
+        const double d = sqdist4_f64(xk, reinterpret_cast<const uint2*>(tab)[c]);
+        if (d < dk) {
+            dk = d;
+            ik = static_cast<uint32_t>(c);
+        }
+    }
+#pragma unroll 2
+    for (int c = slice; c < 256; c += 32) {
+        const double d = sqdist4_f64(xv, reinterpret_cast<const uint2*>(tab + kVtab)[c]);
+        if (d < dv) {
+            dv = d;
+            iv = static_cast<uint32_t>(c);
+        }
+    }
+    {
+        const double dk2 = __shfl_xor(dk, 32, kWave), dv2 = __shfl_xor(dv, 32, kWave);
+        const uint32_t ik2 = __shfl_xor(ik, 32, kWave), iv2 = __shfl_xor(iv, 32, kWave);
+        if (nearer(dk2, ik2, dk, ik)) {
+            dk = dk2;
+            ik = ik2;
+        }
+        if (nearer(dv2, iv2, dv, iv)) {
+            dv = dv2;
+            iv = iv2;
+        }
+    }
+    // [tensor][wave][pos]: lanes 0..31 report keys, 32..63 values
+    double* sd = reinterpret_cast<double*>(scratch);
+    uint32_t* si = reinterpret_cast<uint32_t*>(sd + 2 * kWaves * 32);
+    const int tsel = lane >> 5;
+    sd[(tsel * kWaves + wave) * 32 + pos] = tsel ? dv : dk;
+    si[(tsel * kWaves + wave) * 32 + pos] = tsel ? iv : ik;
+    __syncthreads();
+    const size_t row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + append_pos;
+    if (tid < 64) {
+        double d0 = sd[tsel * kWaves * 32 + pos];
+        uint32_t i0 = si[tsel * kWaves * 32 + pos];
+        for (int w = 1; w < kWaves; ++w) {
+            const double d = sd[(tsel * kWaves + w) * 32 + pos];
+            const uint32_t i = si[(tsel * kWaves + w) * 32 + pos];
+            if (nearer(d, i, d0, i0)) {
+                d0 = d;
+                i0 = i;
+            }
+        }
+        newc[tsel][pos] = i0;
+        if (tsel) {
+            new_codes_v[row * kNumSub + pos] = static_cast<uint8_t>(i0);
+        } else if constexpr (KBITS == 8) {
+            new_codes_k[row * kNumSub + pos] = static_cast<uint8_t>(i0);
+        }
+    }
+    __syncthreads();
+    if constexpr (KBITS == 12) {
+        // byte j of the row holds bits [8j, 8j + 8) of the 12-bit stream
+        if (tid < 48) {
+            const int bit = 8 * tid, i0 = bit / 12, sh = bit % 12;
+            uint32_t v = newc[0][i0] >> sh;
+            if (sh > 4) v |= newc[0][i0 + 1] << (12 - sh);
+            new_codes_k[row * 48 + tid] = static_cast<uint8_t>(v & 0xffu);
+        }
+    }
+
+    // 2. the one-token partial of each query head: lane l holds dims 2l, 2l + 1,
+    //    components 2 (l % 2), + 1 of sub-vector l / 2
+    if (wave < G) {
+        const int j = lane >> 1, comp = 2 * (lane & 1);
+        const uint2 kc = reinterpret_cast<const uint2*>(tab)[newc[0][j]];
+        const uint2 vc = reinterpret_cast<const uint2*>(tab + kVtab)[newc[1][j]];
+        const uint32_t kw = comp ? kc.y : kc.x, vw = comp ? vc.y : vc.x;
+        const float x = wave_sum(x0 * half_bits_to_float(kw & 0xffffu) +
+                                 x1 * half_bits_to_float(kw >> 16));
+        const size_t pi = (static_cast<size_t>(b) * num_q_heads + g * G + wave) * part_stride + slot;
+        part.o[pi * kHeadDim + 2 * lane] = half_bits_to_float(vw & 0xffffu);
+        part.o[pi * kHeadDim + 2 * lane + 1] = half_bits_to_float(vw >> 16);
+        if (lane == 0) {
+            part.m[pi] = x;
+            part.l[pi] = 1.f;
+        }
+    }
+}
+
 template <int G, int KBITS>
 __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const void* __restrict__ q, int q_f32, const float* __restrict__ lambda,
     const uint16_t* __restrict__ cb_k, const uint16_t* __restrict__ cb_v,
     const uint8_t* __restrict__ codes_k, const uint8_t* __restrict__ codes_v, int num_q_heads,
     int num_kv_heads, int capacity, int context_len, int num_splits, int tokens_per_split,
-    Partials part) {
+    Partials part, const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
+    int append_pos, uint8_t* __restrict__ new_codes_k, uint8_t* __restrict__ new_codes_v,
+    int part_stride) {
     static_assert(G >= 1 && G <= 8, "2G MFMA rows");
     constexpr int KROW = kNumSub * KBITS / 8;
 
@@ -228,9 +376,19 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     __shared__ half8_t qa[4][64];
     __shared__ float wm[kWaves][G], wl[kWaves][G];
     __shared__ uint32_t tile_ctr;   // next 32-token tile of the split to hand out
+    // appended token (new-token workgroup): transformed key and value (fp64)
+    __shared__ double xnew[2][kHeadDim];
+    __shared__ uint32_t newc[2][kNumSub];   // its key and value codes
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (append_pos >= 0 && split == num_splits) {   // the extra, new-token workgroup
+        new_token_workgroup<G, KBITS>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
+                                      num_q_heads, num_kv_heads, capacity, append_pos,
+                                      new_codes_k, new_codes_v, part, part_stride, num_splits,
+                                      tab, reinterpret_cast<uint8_t*>(&pbuf[0][0]), xnew, newc);
+        return;
+    }
     const int grp = lane >> 4, n = lane & 15;
     const int kq = n >> 2, aq4 = n & 3;   // fetch-lane split of n for the transposed reads
 
@@ -274,7 +432,6 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint32_t qw0 = qw[0];
     const uint32_t qw1 = qw[q_f32 ? 1 : 0];
     const float2 lam2 = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
-
     KChunk<KBITS> kA[2], kB[2];
     uint2 vA[2], vB[2];
     // (the whole offset goes in the VGPR operand: the buffer range check
@@ -322,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // elements e = 2 (lane % 4), + 1 of entry qg = lane / 16, kk = lane % 16 / 4.
     x0 *= lam2.x;
     x1 *= lam2.y;
-    fwht128(x0, x1, lane);
+    fwht128(x0, x1);
     if (wave < 8) {
         const bool real = wave < G;
         x0 = real ? x0 * kScoreScaleLog2 : 0.f;
@@ -503,7 +660,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         }
     }
     __syncthreads();
-    const size_t pbase = (static_cast<size_t>(b) * num_q_heads + g * G) * num_splits + split;
+    const size_t pbase = (static_cast<size_t>(b) * num_q_heads + g * G) * part_stride + split;
     for (int i = tid; i < G * kHeadDim; i += kThreads) {
         const int h = i / kHeadDim, d = i % kHeadDim;
         float mx = -INFINITY;
@@ -516,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             ls += f * wl[w][h];
             os += f * obuf[(w * G + h) * kHeadDim + d];
         }
-        const size_t pi = pbase + static_cast<size_t>(h) * num_splits;
+        const size_t pi = pbase + static_cast<size_t>(h) * part_stride;
         part.o[pi * kHeadDim + d] = os;
         if (d == 0) {
             part.m[pi] = mx;
@@ -531,13 +688,20 @@ template <int KBITS>
 hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q, bool q_f32,
                          const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                          const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                         hipStream_t stream) {
+                         const AppendArgs& ap, hipStream_t stream) {
+    // with an append, one more workgroup per (sequence, KV head) encodes the
+    // new token (split index num_splits) and leaves its one-token partial
+    const bool app = ap.k_new != nullptr;
+    const int pos = app ? ap.append_pos : -1;
+    const int stride = s.num_splits + (app ? 1 : 0);
+    const dim3 full(grid.x + (app ? 1 : 0), grid.y, grid.z);
 #define VQKV_LAUNCH(GG)                                                                       \
     case GG:                                                                                  \
-        hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS>), grid, dim3(kThreads), 0,    \
+        hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS>), full, dim3(kThreads), 0,    \
                            stream, q, q_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,   \
                            s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
-                           s.num_splits, s.tokens_per_split, part);                   \
+                           s.num_splits, s.tokens_per_split, part, ap.k_new, ap.v_new,        \
+                           ap.kv_f32 ? 1 : 0, pos, ap.codes_k, ap.codes_v, stride);          \
         break;
     switch (group) {
         VQKV_LAUNCH(1)
@@ -560,13 +724,13 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
 hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bool q_f32,
                                const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                                const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                               hipStream_t stream) {
+                               const AppendArgs& append, hipStream_t stream) {
     const dim3 grid(s.num_splits, s.num_kv_heads, s.batch);
     const int group = s.num_q_heads / s.num_kv_heads;
     return (k_bits == 8) ? launch_mfma_g<8>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
-                                            codes_k, codes_v, part, stream)
+                                            codes_k, codes_v, part, append, stream)
                          : launch_mfma_g<12>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
-                                             codes_k, codes_v, part, stream);
+                                             codes_k, codes_v, part, append, stream);
 }
 
 }  // namespace vqkv

@@ -35,7 +35,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Device-independent plan: the same shape always gets the same split count,
 // so results are reproducible across devices and runs.
 constexpr int kTargetWorkgroups = 256;       // VQ kernel: one 16-wave workgroup per CU (256 CUs)
-constexpr int kTargetWorkgroupsFp16 = 1024;  // fp16 comparator: 4-wave workgroups, 4 per CU
+constexpr int kTargetWorkgroupsFp16 = 512;   // fp16 comparator: 4-wave workgroups, 2 per CU
 constexpr int kMaxGroup = 8;
 
 int check_layout(const vq_layout* L) {
@@ -71,16 +71,25 @@ struct SplitPlan {
     int tokens_per_split;
 };
 
-SplitPlan plan_splits(int streams, int context_len, int requested, int tile,
-                      int target = kTargetWorkgroups) {
-    int max_splits = (context_len + tile - 1) / tile;
+// Splits hold at least `min_len` tokens (one sweep of the workgroup) and a
+// multiple of `gran` tokens (one wave tile); the last split takes the rest.
+SplitPlan plan_splits(int streams, int context_len, int requested, int min_len,
+                      int target = kTargetWorkgroups, int gran = 0) {
+    if (gran <= 0) gran = min_len;
+    int max_splits = (context_len + min_len - 1) / min_len;
     if (max_splits > vqkv::kMaxSplits) max_splits = vqkv::kMaxSplits;
     int s = requested > 0 ? requested : (target + streams - 1) / streams;
     if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;
     const int per = (context_len + s - 1) / s;
-    const int tps = ((per + tile - 1) / tile) * tile;
+    const int tps = ((per + gran - 1) / gran) * gran;
     return {(context_len + tps - 1) / tps, tps};
+}
+
+// The VQ kernel's plan for `streams` (sequence, KV head) streams.
+SplitPlan plan_vq(int streams, int context_len, int requested) {
+    return plan_splits(streams, context_len, requested, vqkv::kVqTile, kTargetWorkgroups,
+                       vqkv::kVqTileGrain);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -174,7 +183,7 @@ int32_t vq_decode_attention_default_splits(const vq_layout* layout, int32_t batc
                                            int32_t num_q_heads, int32_t context_len) {
     (void)num_q_heads;
     if (layout == nullptr || batch < 1 || context_len < 1 || layout->num_kv_heads < 1) return 0;
-    return plan_splits(batch * layout->num_kv_heads, context_len, 0, vqkv::kVqTile).num_splits;
+    return plan_vq(batch * layout->num_kv_heads, context_len, 0).num_splits;
 }
 
 size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batch,
@@ -184,7 +193,7 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
         layout->num_kv_heads < 1)
         return 0;
     const SplitPlan p =
-        plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
+        plan_vq(batch * layout->num_kv_heads, context_len, num_splits);
     return partials_bytes(batch, num_q_heads, p.num_splits);
 }
 
@@ -195,7 +204,7 @@ int32_t vq_decode_attention_plan_splits(const vq_layout* layout, int32_t batch,
     if (layout == nullptr || batch < 1 || context_len < 1 || layout->num_kv_heads < 1 ||
         requested < 0)
         return 0;
-    return plan_splits(batch * layout->num_kv_heads, context_len, requested, vqkv::kVqTile)
+    return plan_vq(batch * layout->num_kv_heads, context_len, requested)
         .num_splits;
 }
 
@@ -245,7 +254,7 @@ int vq_decode_attention_partials(const vq_layout* layout, const void* q, int q_d
     if (st) return st;
     if ((st = check_partials_ptrs(part_m, part_l, part_o))) return st;
     const SplitPlan p =
-        plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
+        plan_vq(batch * layout->num_kv_heads, context_len, num_splits);
     if (num_splits != p.num_splits)
         return fail(VQ_ERR_INVALID_ARG,
                     "num_splits %d is not a planned split count for this shape "
@@ -256,6 +265,7 @@ int vq_decode_attention_partials(const vq_layout* layout, const void* q, int q_d
                                 context_len, p.num_splits, p.tokens_per_split};
     return hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
                                                 lambda, cb_k, cb_v, codes_k, codes_v, part,
+                                                vqkv::AppendArgs{},
                                                 static_cast<hipStream_t>(stream)),
                       "decode_attention_partials launch");
 }
@@ -281,6 +291,124 @@ int vq_merge_partials(int32_t batch, int32_t num_q_heads, int32_t num_partials,
                       "merge_partials launch");
 }
 
+namespace {
+
+// Shared by the decode-step entry points: validate the appended rows, then
+// the attention over cur_len + 1 tokens.
+int check_step_args(const vq_layout* layout, const void* q, int q_dtype, const void* k_new,
+                    const void* v_new, int kv_dtype, const float* lambda, const uint16_t* cb_k,
+                    const uint16_t* cb_v, const uint8_t* codes_k, const uint8_t* codes_v,
+                    int32_t batch, int32_t num_q_heads, int32_t cur_len, int32_t num_splits) {
+    int st = check_layout(layout);
+    if (st) return st;
+    if (cur_len < 0) return fail(VQ_ERR_INVALID_ARG, "cur_len %d < 0", cur_len);
+    if (static_cast<int64_t>(cur_len) + 1 > layout->capacity)
+        return fail(VQ_ERR_CAPACITY, "cur_len %d + 1 exceeds capacity %d", cur_len,
+                    layout->capacity);
+    if (kv_dtype != VQ_F16 && kv_dtype != VQ_F32)
+        return fail(VQ_ERR_INVALID_ARG, "kv_dtype %d is not VQ_F16 or VQ_F32", kv_dtype);
+    VQ_REQUIRE_PTR(k_new);
+    VQ_REQUIRE_PTR(v_new);
+    return check_attention_args(layout, q, q_dtype, lambda, cb_k, cb_v, codes_k, codes_v, batch,
+                                num_q_heads, cur_len + 1, num_splits);
+}
+
+// A decode step splits the cur_len cached tokens over the workgroups that one
+// per (sequence, KV head) new-token workgroup leaves free.
+SplitPlan plan_step(int streams, int cur_len, int requested) {
+    const int target = kTargetWorkgroups > 2 * streams ? kTargetWorkgroups - streams : streams;
+    return plan_splits(streams, cur_len > 0 ? cur_len : 1, requested, vqkv::kVqTile, target,
+                       vqkv::kVqTileGrain);
+}
+
+vqkv::AppendArgs append_args(const void* k_new, const void* v_new, int kv_dtype, int cur_len,
+                             uint8_t* codes_k, uint8_t* codes_v) {
+    vqkv::AppendArgs app;
+    app.k_new = k_new;
+    app.v_new = v_new;
+    app.kv_f32 = kv_dtype == VQ_F32;
+    app.append_pos = cur_len;
+    app.codes_k = codes_k;
+    app.codes_v = codes_v;
+    return app;
+}
+
+}  // namespace
+
+int32_t vq_decode_step_num_partials(const vq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                    int32_t cur_len, int32_t requested) {
+    (void)num_q_heads;
+    if (layout == nullptr || batch < 1 || cur_len < 0 || layout->num_kv_heads < 1 ||
+        requested < 0)
+        return 0;
+    return plan_step(batch * layout->num_kv_heads, cur_len, requested).num_splits + 1;
+}
+
+size_t vq_decode_step_workspace_bytes(const vq_layout* layout, int32_t batch,
+                                      int32_t num_q_heads, int32_t cur_len, int32_t requested) {
+    const int32_t n = vq_decode_step_num_partials(layout, batch, num_q_heads, cur_len, requested);
+    if (n < 1 || num_q_heads < 1) return 0;
+    return partials_bytes(batch, num_q_heads, n);
+}
+
+int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
+                            const void* k_new, const void* v_new, int kv_dtype,
+                            const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                            uint8_t* codes_k, uint8_t* codes_v, int32_t batch,
+                            int32_t num_q_heads, int32_t cur_len, int32_t num_partials,
+                            float* part_m, float* part_l, float* part_o, void* stream) {
+    int st = check_step_args(layout, q, q_dtype, k_new, v_new, kv_dtype, lambda, cb_k, cb_v,
+                             codes_k, codes_v, batch, num_q_heads, cur_len, 0);
+    if (st) return st;
+    if ((st = check_partials_ptrs(part_m, part_l, part_o))) return st;
+    const SplitPlan p = plan_step(batch * layout->num_kv_heads, cur_len,
+                                  num_partials > 1 ? num_partials - 1 : 1);
+    if (num_partials != p.num_splits + 1)
+        return fail(VQ_ERR_INVALID_ARG,
+                    "num_partials %d is not a planned count for this shape "
+                    "(vq_decode_step_num_partials gives %d)",
+                    num_partials, p.num_splits + 1);
+    const vqkv::Partials part{part_m, part_l, part_o};
+    const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity, cur_len,
+                                p.num_splits, p.tokens_per_split};
+    return hip_status(vqkv::launch_vq_attention(
+                          shape, layout->k_code_bits, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                          codes_k, codes_v, part,
+                          append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v),
+                          static_cast<hipStream_t>(stream)),
+                      "decode_step_partials launch");
+}
+
+int vq_decode_step(const vq_layout* layout, const void* q, int q_dtype, const void* k_new,
+                   const void* v_new, int kv_dtype, const float* lambda, const uint16_t* cb_k,
+                   const uint16_t* cb_v, uint8_t* codes_k, uint8_t* codes_v, int32_t batch,
+                   int32_t num_q_heads, int32_t cur_len, int32_t num_splits, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_step_args(layout, q, q_dtype, k_new, v_new, kv_dtype, lambda, cb_k, cb_v,
+                             codes_k, codes_v, batch, num_q_heads, cur_len, num_splits);
+    if (st) return st;
+    VQ_REQUIRE_PTR(out);
+    const SplitPlan p = plan_step(batch * layout->num_kv_heads, cur_len, num_splits);
+    const int nparts = p.num_splits + 1;
+    const size_t need = partials_bytes(batch, num_q_heads, nparts);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, nparts);
+    const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity, cur_len,
+                                p.num_splits, p.tokens_per_split};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(vqkv::launch_vq_attention(
+                        shape, layout->k_code_bits, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                        codes_k, codes_v, part,
+                        append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v), s),
+                    "decode_step launch");
+    if (st) return st;
+    return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, nparts, part, out, s),
+                      "decode_step merge launch");
+}
+
 int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
                         const uint16_t* cb_k, const uint16_t* cb_v, const uint8_t* codes_k,
                         const uint8_t* codes_v, int32_t batch, int32_t num_q_heads,
@@ -291,7 +419,7 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
     if (st) return st;
     VQ_REQUIRE_PTR(out);
     const SplitPlan p =
-        plan_splits(batch * layout->num_kv_heads, context_len, num_splits, vqkv::kVqTile);
+        plan_vq(batch * layout->num_kv_heads, context_len, num_splits);
     const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -302,7 +430,8 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
                                 context_len, p.num_splits, p.tokens_per_split};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     st = hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
-                                              lambda, cb_k, cb_v, codes_k, codes_v, part, s),
+                                              lambda, cb_k, cb_v, codes_k, codes_v, part,
+                                              vqkv::AppendArgs{}, s),
                     "decode_attention launch");
     if (st) return st;
     return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, p.num_splits, part, out, s),
