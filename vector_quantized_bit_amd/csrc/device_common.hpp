@@ -115,6 +115,27 @@ __device__ __forceinline__ void fwht128(T& x0, T& x1) {
     butterfly<32>(x0, x1, lane);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, x)));
+}
+
+// max / sum over the 16 lanes of a DPP row, result in every lane of the row
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<0x128>(x));   // row_ror:8
+    x = fmaxf(x, dpp<0x124>(x));   // row_ror:4
+    x = fmaxf(x, dpp<0x122>(x));   // row_ror:2
+    x = fmaxf(x, dpp<0x121>(x));   // row_ror:1
+    return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp<0x128>(x);
+    x += dpp<0x124>(x);
+    x += dpp<0x122>(x);
+    x += dpp<0x121>(x);
+    return x;
+}
+
 // Squared distance ||x - c||^2 of a 4-dim sub-vector to an fp16 centroid
 // (4 halves in c), in fp64 with every difference, product and sum rounded
 // separately and the 4 terms summed in order, as the fp64 reference does.

@@ -3,27 +3,28 @@
 // Background: KV cache and attention).  Same split partials and merge as the
 // VQ kernels.
 //
-// Each wave owns 32-token chunks of the workgroup's range; 16 lanes share one
-// token (8 channels per lane), so one 16-byte load per lane moves 4 whole
-// 256-byte key (or value) rows per wave instruction.  Each 16-lane group keeps
-// its own online-softmax state; groups and waves are merged at the end.
+// A 16-lane DPP row owns one token at a time (8 channels per lane, one
+// 16-byte load per lane per row of K or V), so a wave instruction moves 4
+// whole 256-byte rows.  Each wave takes 16-token chunks (4 tokens per row);
+// both K and V of a chunk are requested before any is used.  Scores are
+// fp16 x fp16 dot products accumulated in fp32 (v_dot2_f32_f16) and summed
+// over the row by DPP; every row keeps its own online-softmax state, merged
+// across rows and waves at the end.  Registers stay near 100 per lane, so
+// 4 waves per SIMD keep loads in flight.
 #include "launchers.hpp"
 
 namespace vqkv {
 
 namespace {
 
-__device__ __forceinline__ void unpack8(const uint4 u, float f[8]) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = half_bits_to_float(static_cast<uint16_t>(w[i] & 0xffffu));
-        f[2 * i + 1] = half_bits_to_float(static_cast<uint16_t>(w[i] >> 16));
-    }
+typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2v_t as_half2(uint32_t w) {
+    return __builtin_bit_cast(half2v_t, w);
 }
 
 __device__ __forceinline__ float scale_of(float m_old, float m_new) {
-    return (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
+    return (m_old == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_old - m_new);
 }
 
 }  // namespace
@@ -33,23 +34,21 @@ __global__ __launch_bounds__(256) void fp16_attention_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int num_q_heads, int num_kv_heads, int capacity,
     int context_len, int num_splits, int tokens_per_split, Partials part) {
-    constexpr int CH = 32;   // tokens per wave chunk (8 per 16-lane group)
+    constexpr int CH = 16;   // tokens per wave chunk: 4 per 16-lane row
     __shared__ float wm[4][G], wl[4][G];
     __shared__ float wo[4][G][kHeadDim];
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int grp = lane >> 4;      // which of the 4 tokens of a row quad
-    const int sl = lane & 15;       // channels 8*sl .. 8*sl+7
-    constexpr float kScale = 1.4426950408889634f * kInvSqrtD;
+    const int grp = lane >> 4;      // row of the wave: token 4 i + grp of a chunk
+    const int sl = lane & 15;       // channels 8 sl .. 8 sl + 7
+    constexpr float kScale = 1.4426950408889634f * kInvSqrtD;   // base-2 scores
 
-    float qf[G][8];
+    uint4 qh[G];                    // q as stored (fp16), this lane's 8 channels
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + h;
-        unpack8(reinterpret_cast<const uint4*>(q + vec * kHeadDim)[sl], qf[h]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[h][e] *= kScale;
+        qh[h] = reinterpret_cast<const uint4*>(q + vec * kHeadDim)[sl];
     }
 
     float m[G], l[G], o[G][8];
@@ -68,63 +67,58 @@ __global__ __launch_bounds__(256) void fp16_attention_split_kernel(
     const uint4* v4 = reinterpret_cast<const uint4*>(v);
 
     for (int base = t_begin + wave * CH; base < t_end; base += 4 * CH) {
-        float s[8][G];
-        uint4 kr[8];
+        uint4 kr[4], vr[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int t = base + 4 * i + grp;
-            kr[i] = (t < t_end) ? k4[(row0 + t) * (kHeadDim / 8) + sl] : make_uint4(0, 0, 0, 0);
+            const size_t r = (row0 + min(t, t_end - 1)) * (kHeadDim / 8) + sl;
+            kr[i] = k4[r];
+            vr[i] = v4[r];
         }
+        float s[4][G];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float kf[8];
-            unpack8(kr[i], kf);
+        for (int i = 0; i < 4; ++i) {
             const bool ok = base + 4 * i + grp < t_end;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) d += qf[h][e] * kf[e];
-                d += __shfl_xor(d, 1, kWave);
-                d += __shfl_xor(d, 2, kWave);
-                d += __shfl_xor(d, 4, kWave);
-                d += __shfl_xor(d, 8, kWave);
+                float d = __builtin_amdgcn_fdot2(as_half2(qh[h].x), as_half2(kr[i].x), 0.f, false);
+                d = __builtin_amdgcn_fdot2(as_half2(qh[h].y), as_half2(kr[i].y), d, false);
+                d = __builtin_amdgcn_fdot2(as_half2(qh[h].z), as_half2(kr[i].z), d, false);
+                d = __builtin_amdgcn_fdot2(as_half2(qh[h].w), as_half2(kr[i].w), d, false);
+                d = row_sum16(d) * kScale;
                 s[i][h] = ok ? d : -INFINITY;
             }
         }
-        uint4 vr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = base + 4 * i + grp;
-            vr[i] = (t < t_end) ? v4[(row0 + t) * (kHeadDim / 8) + sl] : make_uint4(0, 0, 0, 0);
-        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float cmax = s[0][h];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, s[i][h]);
+            const float cmax = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
             const float m_new = fmaxf(m[h], cmax);
-            const float a = scale_of(m[h], m_new);
-            l[h] *= a;
+            if (m_new != m[h]) {
+                const float a = scale_of(m[h], m_new);
+                l[h] *= a;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] *= a;
-            m[h] = m_new;
+                for (int e = 0; e < 8; ++e) o[h][e] *= a;
+                m[h] = m_new;
+            }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float vf[8];
-            unpack8(vr[i], vf);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float p = (s[i][h] == -INFINITY) ? 0.f : exp2f(s[i][h] - m[h]);
+                const float p = (s[i][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i][h] - m[h]);
                 l[h] += p;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[h][e] += p * vf[e];
+                for (int e = 0; e < 4; ++e) {
+                    o[h][2 * e] += p * half_bits_to_float(static_cast<uint16_t>(vw[e] & 0xffffu));
+                    o[h][2 * e + 1] += p * half_bits_to_float(static_cast<uint16_t>(vw[e] >> 16));
+                }
             }
         }
     }
 
-    // merge the 4 row groups of the wave (lanes differing in bits 4 and 5)
+    // merge the 4 rows of the wave (lanes differing in bits 4 and 5); l is
+    // the same in every lane of a row
 #pragma unroll
     for (int step = 16; step <= 32; step <<= 1) {
 #pragma unroll

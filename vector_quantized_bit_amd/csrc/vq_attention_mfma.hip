@@ -63,48 +63,6 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9
 
 static_assert(kStride == kVqTile && kTok == kVqTileGrain, "split planning matches the tiles");
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                 CTRL, 0xF, 0xF, false));
-}
-
-// fp32 squared distance of a 4-dim sub-vector (x rounded to fp32, squared
-// norm xx) to an fp16 centroid, and a bound err on its distance from the
-// exact value ||x - c||^2 of the unrounded x.  With u = 2^-24, rounding x
-// and each difference, square and sum once gives
-//     |d32 - d| <= 9 u (d + ||x||^2 + ||c||^2)
-// (each difference carries u (2|x_i| + |x_i - c_i|), its square twice that
-// times |x_i - c_i| plus u of itself, and 2|a||b| <= a^2 + b^2); fused
-// multiply-adds only remove roundings.  The bound used is 2^-18 (> 9 u) of
-// the same sum, plus 1e-30 for underflow.
-__device__ __forceinline__ float sqdist4_f32(const float x[4], float xx, const uint2 c,
-                                             float& err) {
-    const float c0 = half_bits_to_float(c.x & 0xffffu), c1 = half_bits_to_float(c.x >> 16);
-    const float c2 = half_bits_to_float(c.y & 0xffffu), c3 = half_bits_to_float(c.y >> 16);
-    const float e0 = x[0] - c0, e1 = x[1] - c1, e2 = x[2] - c2, e3 = x[3] - c3;
-    const float d = e0 * e0 + e1 * e1 + e2 * e2 + e3 * e3;
-    const float cc = c0 * c0 + c1 * c1 + c2 * c2 + c3 * c3;
-    err = 0x1p-18f * (d + xx + cc) + 1e-30f;
-    return d;
-}
-
-// max / sum over the 16 lanes of a DPP row, result in every lane of the row
-__device__ __forceinline__ float row_max16(float x) {
-    x = fmaxf(x, dpp<0x128>(x));   // row_ror:8
-    x = fmaxf(x, dpp<0x124>(x));   // row_ror:4
-    x = fmaxf(x, dpp<0x122>(x));   // row_ror:2
-    x = fmaxf(x, dpp<0x121>(x));   // row_ror:1
-    return x;
-}
-__device__ __forceinline__ float row_sum16(float x) {
-    x += dpp<0x128>(x);
-    x += dpp<0x124>(x);
-    x += dpp<0x122>(x);
-    x += dpp<0x121>(x);
-    return x;
-}
-
 // LDS address bytes [slot.b2 : code : slot.b0], code = byte K of w
 template <int K>
 __device__ __forceinline__ uint32_t row_addr(uint32_t w, uint32_t slot) {

@@ -35,7 +35,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Device-independent plan: the same shape always gets the same split count,
 // so results are reproducible across devices and runs.
 constexpr int kTargetWorkgroups = 256;       // VQ kernel: one 16-wave workgroup per CU (256 CUs)
-constexpr int kTargetWorkgroupsFp16 = 512;   // fp16 comparator: 4-wave workgroups, 2 per CU
+constexpr int kTargetWorkgroupsFp16 = 1024;  // fp16 comparator: 4-wave workgroups, 4 per CU
 constexpr int kMaxGroup = 8;
 
 int check_layout(const vq_layout* L) {
