@@ -128,6 +128,13 @@ __device__ __forceinline__ float row_max16(float x) {
     x = fmaxf(x, dpp<0x121>(x));   // row_ror:1
     return x;
 }
+__device__ __forceinline__ float row_min16(float x) {
+    x = fminf(x, dpp<0x128>(x));
+    x = fminf(x, dpp<0x124>(x));
+    x = fminf(x, dpp<0x122>(x));
+    x = fminf(x, dpp<0x121>(x));
+    return x;
+}
 __device__ __forceinline__ float row_sum16(float x) {
     x += dpp<0x128>(x);
     x += dpp<0x124>(x);

@@ -4,65 +4,152 @@
 // the online dual transform k~ = k diag(lambda)^-1 H_D and is quantised with
 // C_k; its value is quantised untransformed with C_v; the codes are
 // concatenated to the cache.  Background (VQ principle): every 4-channel
-// sub-vector gets j* = argmin_j ||x_i - C_j||^2.
+// sub-vector x gets j* = argmin_j ||x - C_j||^2.
 //
-// The transform and the squared distances are evaluated in fp64 (products
-// and sums rounded separately, summed over the 4 channels in order), so the
-// argmin is decided in the same precision as the fp64 reference.  Exact ties
-// go to the lowest index: every thread scans its centroids in ascending order
-// with a strict '<', and the per-thread winners are combined by the
-// lexicographic minimum of (distance, index).
+// The decision is the one the fp64 reference takes: squared distances in
+// fp64 with every difference, product and sum rounded separately, exact ties
+// to the lowest index.  Computing all of them in fp64 is slow (fp64 vector
+// rate), so the search runs in two passes over each row of sub-vectors:
+//  1. On the matrix cores (v_mfma_f32_16x16x4_f32: 16 sub-vectors x 16
+//     centroids per instruction, the 4 channels as the contraction) the fp32
+//     scores s(c) = ||c||^2 - 2 x.c, whose row minimum picks the nearest
+//     centroid (||x||^2 is common to the row).  With u = 2^-24 the fp32
+//     score is within about 10 u (||x||^2 + ||c||^2) of the exact one; the
+//     bound used, E = 2^-16 (||x||^2 + max_c ||c||^2), has a margin of 25x.
+//     A row's threshold is min_c s(c) + 2E: every centroid that can be the
+//     exact (or fp64) nearest one scores below it.
+//  2. The same scores again; centroids under the threshold (normally one)
+//     get their fp64 distance, and the lexicographic (distance, index)
+//     minimum over them is the code.
 //
-// One 256-thread workgroup encodes one token of one (sequence, KV head):
-// thread (slice s, position p) scans centroids s, s + 8, s + 16, ... of
-// sub-vector p, so a single decode-step append (one token per head) is 8x
-// shorter than a scan per sub-vector.  Codebooks are staged in LDS (2 KiB,
-// or 32 KiB for 12-bit keys); the 8 threads that share a centroid index sit
-// in different waves, the 32 threads of a wave read one broadcast address.
+// One 512-thread workgroup encodes up to 8 tokens of one (sequence, KV
+// head): 256 key and 256 value sub-vectors, 16 row blocks each, spread over
+// the 8 waves.  Codebooks (-2c by channel, fp32) and their squared norms are
+// staged in LDS.
 #include "launchers.hpp"
 
 namespace vqkv {
 
 namespace {
 
-constexpr int kEncThreads = 256;
-constexpr int kEncSlices = kEncThreads / kNumSub;   // 8
+constexpr int kEncThreads = 512;
+constexpr int kEncWaves = kEncThreads / kWave;     // 8
+constexpr int kEncTok = 8;                          // tokens per workgroup
+constexpr int kEncBlocks = kEncTok * kNumSub / 16;  // row blocks per tensor
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
     if (f32) return static_cast<double>(reinterpret_cast<const float*>(p)[i]);
     return static_cast<double>(half_bits_to_float(reinterpret_cast<const uint16_t*>(p)[i]));
 }
 
-// Nearest of `entries` LDS centroids to x among indices slice, slice + 8, ...,
-// combined across the 8 slices; returns the code for this thread's position.
-__device__ __forceinline__ uint32_t nearest(const double x[4], const uint2* cb, int entries,
-                                            int slice, int pos, double* bd, uint32_t* bi) {
-    double best = INFINITY;
-    uint32_t arg = 0;
-#pragma unroll 4
-    for (int c = slice; c < entries; c += kEncSlices) {
-        const double d = sqdist4_f64(x, cb[c]);
-        if (d < best) {
-            best = d;
-            arg = static_cast<uint32_t>(c);
-        }
-    }
-    bd[slice * kNumSub + pos] = best;
-    bi[slice * kNumSub + pos] = arg;
-    __syncthreads();
-    double b0 = bd[pos];
-    uint32_t a0 = bi[pos];
+// ||c||^2 of an fp16 centroid: the squares are exact in fp32, the sums rounded
+__device__ __forceinline__ float norm2(const uint2 c) {
+    const float c0 = half_bits_to_float(c.x & 0xffffu), c1 = half_bits_to_float(c.x >> 16);
+    const float c2 = half_bits_to_float(c.y & 0xffffu), c3 = half_bits_to_float(c.y >> 16);
+    return (c0 * c0 + c1 * c1) + (c2 * c2 + c3 * c3);
+}
+
+// Row stride of the -2c tables: 16 floats of padding put the 4 channel rows
+// on different banks for the 64 lanes of one B-operand read.
+template <int NENT>
+constexpr int kM2Stride = NENT + 16;
+
+// The nearest of NENT centroids for the 16 sub-vectors of row block rb of
+// `xs` ([8 tokens][128] fp64 = [256 sub-vectors][4]): on return lane l has
+// the lexicographic (fp64 distance, index) minimum over its 16-column slice
+// of the candidates of rows rb*16 + 4 (l / 16) + i in bd[i], bi[i].
+// m2 holds -2c by channel (rows kM2Stride apart), cc the squared norms.  The
+// MFMA accumulates -2 x.c onto a multiple of ||c||^2, which folds the
+// per-centroid part of the error bound E(c) = 2^-16 (||x||^2 + ||c||^2)
+// into the product: pass 1 takes s + 2^-16 ||c||^2, pass 2 s - 2^-16 ||c||^2.
+template <int NENT>
+__device__ __forceinline__ void search_rows(const float* m2, const float* cc,
+                                            const double (*xs)[kHeadDim], int rb, int lane,
+                                            double bd[4], uint32_t bi[4]) {
+    constexpr int kUnroll = 8;
+    constexpr float kUp = 1.0f + 0x1p-16f, kDown = 1.0f - 0x1p-16f;
+    static_assert(NENT % (16 * kUnroll) == 0, "whole unrolled groups");
+    const double* xrow = &xs[0][0];
+    // A operand: sub-vector rb*16 + lane%16, channel lane/16
+    const float a = static_cast<float>(xrow[(rb * 16 + (lane & 15)) * 4 + (lane >> 4)]);
+    const int r0 = rb * 16 + 4 * (lane >> 4);   // this lane's D rows r0 .. r0 + 3
+    const float* bcol = m2 + (lane >> 4) * kM2Stride<NENT> + (lane & 15);
+    const float* ccol = cc + (lane & 15);
+    float ex[4];
 #pragma unroll
-    for (int s = 1; s < kEncSlices; ++s) {
-        const double d = bd[s * kNumSub + pos];
-        const uint32_t a = bi[s * kNumSub + pos];
-        if (nearer(d, a, b0, a0)) {
-            b0 = d;
-            a0 = a;
+    for (int i = 0; i < 4; ++i) {
+        float xx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v = static_cast<float>(xrow[(r0 + i) * 4 + j]);
+            xx += v * v;
+        }
+        ex[i] = 2.f * (0x1p-16f * xx) + 1e-30f;   // the ||x||^2 parts of both bounds
+    }
+
+    // pass 1: min over c of s(c) + E(c), up to the ||x||^2 part
+    float smin[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
+    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
+        f32x4_t d[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const float c0 = ccol[(blk + u) * 16] * kUp;
+            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bcol[(blk + u) * 16],
+                                                        f32x4_t{c0, c0, c0, c0}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) smin[i] = fminf(smin[i], d[u][i]);
+    }
+    float thr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) thr[i] = row_min16(smin[i]) + ex[i];
+
+    // pass 2: candidates are the c with s(c) - E(c) <= that minimum; they get
+    // fp64 distances.  Groups of 8 x 16 centroids without one are skipped.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bd[i] = INFINITY;
+        bi[i] = 0xffffffffu;
+    }
+    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
+        f32x4_t d[kUnroll];
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const float c0 = ccol[(blk + u) * 16] * kDown;
+            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bcol[(blk + u) * 16],
+                                                        f32x4_t{c0, c0, c0, c0}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) any |= d[u][i] <= thr[i];
+        }
+        if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (d[u][i] <= thr[i]) {
+                    const int nc = (blk + u) * 16 + (lane & 15);
+                    // the fp16 centroid, recovered exactly from -2c; the
+                    // distance rounded as the fp64 reference rounds it
+                    double dd = 0.0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const double c = -0.5 * static_cast<double>(m2[j * kM2Stride<NENT> + nc]);
+                        const double e = __dadd_rn(xrow[(r0 + i) * 4 + j], -c);
+                        dd = j == 0 ? __dmul_rn(e, e) : __dadd_rn(dd, __dmul_rn(e, e));
+                    }
+                    if (nearer(dd, static_cast<uint32_t>(nc), bd[i], bi[i])) {
+                        bd[i] = dd;
+                        bi[i] = static_cast<uint32_t>(nc);
+                    }
+                }
+            }
         }
     }
-    __syncthreads();   // bd / bi are reused by the next call
-    return a0;
 }
 
 }  // namespace
@@ -75,62 +162,120 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     uint8_t* __restrict__ codes_v, int num_kv_heads, int capacity, int cur_len, int num_new) {
     constexpr int KENT = 1 << KBITS;
     constexpr int KROW = kNumSub * KBITS / 8;
-    __shared__ uint2 kcb[KENT];
-    __shared__ uint2 vcb[256];
-    __shared__ double xk[kHeadDim];
-    __shared__ double bd[kEncSlices * kNumSub];
-    __shared__ uint32_t bi[kEncSlices * kNumSub];
-    __shared__ uint32_t kcode[kNumSub];
+    // -2c by channel ([4][E], exact in fp32) and ||c||^2, per tensor
+    __shared__ float km2[4 * kM2Stride<KENT>];
+    __shared__ float vm2[4 * kM2Stride<256>];
+    __shared__ float kcc[KENT];
+    __shared__ float vcc[256];
+    __shared__ double xs[2][kEncTok][kHeadDim];       // transformed keys, values (fp64)
+    __shared__ uint16_t code[2][kEncTok][kNumSub];
 
-    const int tok = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int t0 = blockIdx.x * kEncTok, g = blockIdx.y, b = blockIdx.z;
+    const int ntok = min(kEncTok, num_new - t0);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const bool f32 = kv_f32 != 0;
-    const size_t in_row = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + tok;
 
-    // this thread's value sub-vector is loaded first so its latency hides
-    // behind the codebook staging and the key scan
-    const int pos = tid % kNumSub, slice = tid / kNumSub;
-    double xv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xv[i] = load_elem(v_new, f32, in_row * kHeadDim + 4 * pos + i);
-
+    // codebooks (-2c by channel) and squared norms
     const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
-    for (int i = tid; i < KENT; i += kEncThreads) kcb[i] = ksrc[i];
-    vcb[tid] = reinterpret_cast<const uint2*>(cb_v)[static_cast<size_t>(g) * 256 + tid];
+    const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
+    // every load is issued before any is used (one latency, not one per entry)
+    constexpr int KPER = (KENT + kEncThreads - 1) / kEncThreads;
+    uint2 kc[KPER];
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) kc[j] = ksrc[min(tid + j * kEncThreads, KENT - 1)];
+    const uint2 vc = vsrc[tid & 255];
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) {
+        const int i = tid + j * kEncThreads;
+        if (i < KENT) {
+            km2[0 * kM2Stride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x & 0xffffu);
+            km2[1 * kM2Stride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x >> 16);
+            km2[2 * kM2Stride<KENT> + i] = -2.f * half_bits_to_float(kc[j].y & 0xffffu);
+            km2[3 * kM2Stride<KENT> + i] = -2.f * half_bits_to_float(kc[j].y >> 16);
+            kcc[i] = norm2(kc[j]);
+        }
+    }
+    if (tid < 256) {
+        vm2[0 * kM2Stride<256> + tid] = -2.f * half_bits_to_float(vc.x & 0xffffu);
+        vm2[1 * kM2Stride<256> + tid] = -2.f * half_bits_to_float(vc.x >> 16);
+        vm2[2 * kM2Stride<256> + tid] = -2.f * half_bits_to_float(vc.y & 0xffffu);
+        vm2[3 * kM2Stride<256> + tid] = -2.f * half_bits_to_float(vc.y >> 16);
+        vcc[tid] = norm2(vc);
+    }
 
-    // k / lambda in fp64, +-1 Walsh–Hadamard butterflies in one wave, then 1/sqrt(128)
-    if (tid < kWave) {
-        const float* lam = lambda + g * kHeadDim;
+    // k / lambda in fp64, the +-1 Walsh–Hadamard transform, then 1/sqrt(128);
+    // values as they are.  Rows of tokens past num_new are zero.
+    const float* lam = lambda + g * kHeadDim;
+    for (int t = wave; t < kEncTok; t += kEncWaves) {
+        const bool live = t < ntok;
+        const size_t in_row = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + t0 +
+                              (live ? t : 0);
         double x0 = load_elem(k_new, f32, in_row * kHeadDim + 2 * lane) /
                     static_cast<double>(lam[2 * lane]);
         double x1 = load_elem(k_new, f32, in_row * kHeadDim + 2 * lane + 1) /
                     static_cast<double>(lam[2 * lane + 1]);
         fwht128(x0, x1);
-        xk[2 * lane] = x0 * kInvSqrtD64;
-        xk[2 * lane + 1] = x1 * kInvSqrtD64;
+        xs[0][t][2 * lane] = live ? x0 * kInvSqrtD64 : 0.0;
+        xs[0][t][2 * lane + 1] = live ? x1 * kInvSqrtD64 : 0.0;
+        xs[1][t][2 * lane] = live ? load_elem(v_new, f32, in_row * kHeadDim + 2 * lane) : 0.0;
+        xs[1][t][2 * lane + 1] =
+            live ? load_elem(v_new, f32, in_row * kHeadDim + 2 * lane + 1) : 0.0;
     }
     __syncthreads();
 
-    double x[4];
+    // row block jobs: keys then values; sub-vector r = 32 token + position
+    for (int job = wave; job < 2 * kEncBlocks; job += kEncWaves) {
+        const int tt = job / kEncBlocks, rb = job % kEncBlocks;
+        if (rb * 16 >= ntok * kNumSub) continue;   // whole block past the last token
+        double bd[4];
+        uint32_t bi[4];
+        if (tt == 0)
+            search_rows<KENT>(km2, kcc, xs[0], rb, lane, bd, bi);
+        else
+            search_rows<256>(vm2, vcc, xs[1], rb, lane, bd, bi);
+        const int r0 = rb * 16 + 4 * (lane >> 4);
+        // lexicographic minimum over the 16 lanes that share the rows
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = xk[4 * pos + i];
-    const uint32_t ck = nearest(x, kcb, KENT, slice, pos, bd, bi);
-    const uint32_t cv = nearest(xv, vcb, 256, slice, pos, bd, bi);
+        for (int i = 0; i < 4; ++i) {
+            double d0 = bd[i];
+            uint32_t i0 = bi[i];
+#define VQKV_TAKE(M)                                                                       \
+    {                                                                                      \
+        const double d2 = lane_partner<M>(d0, lane);                                       \
+        const uint32_t i2 = lane_partner<M>(i0, lane);                                     \
+        if (nearer(d2, i2, d0, i0)) {                                                      \
+            d0 = d2;                                                                       \
+            i0 = i2;                                                                       \
+        }                                                                                  \
+    }
+            VQKV_TAKE(1)
+            VQKV_TAKE(2)
+            VQKV_TAKE(4)
+            VQKV_TAKE(8)
+#undef VQKV_TAKE
+            const int r = r0 + i;
+            if ((lane & 15) == 0) code[tt][r >> 5][r & 31] = static_cast<uint16_t>(i0);
+        }
+    }
+    __syncthreads();
 
-    const size_t out_row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + cur_len + tok;
-    if (tid < kNumSub) codes_v[out_row * kNumSub + pos] = static_cast<uint8_t>(cv);
-    if constexpr (KBITS == 8) {
-        if (tid < kNumSub) codes_k[out_row * KROW + pos] = static_cast<uint8_t>(ck);
-    } else {
-        if (tid < kNumSub) kcode[pos] = ck;
-        __syncthreads();
-        // byte j of the row holds bits [8j, 8j+8) of the little-endian 12-bit stream
-        if (tid < KROW) {
-            const int bit = 8 * tid;
-            const int i0 = bit / 12, sh = bit % 12;
-            uint32_t v = kcode[i0] >> sh;
-            if (sh > 4) v |= kcode[i0 + 1] << (12 - sh);
-            codes_k[out_row * KROW + tid] = static_cast<uint8_t>(v & 0xffu);
+    // codes of the live tokens to their slots
+    const size_t out0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + cur_len + t0;
+    {
+        const int t = tid / kNumSub, pos = tid % kNumSub;   // 8 tokens x 32 positions (tid < 256)
+        if (t < ntok) codes_v[(out0 + t) * kNumSub + pos] = static_cast<uint8_t>(code[1][t][pos]);
+        if constexpr (KBITS == 8) {
+            if (t < ntok) codes_k[(out0 + t) * KROW + pos] = static_cast<uint8_t>(code[0][t][pos]);
+        }
+    }
+    if constexpr (KBITS == 12) {
+        // byte j of a row holds bits [8j, 8j + 8) of the little-endian 12-bit stream
+        for (int e = tid; e < ntok * KROW; e += kEncThreads) {
+            const int t = e / KROW, j = e % KROW;
+            const int bit = 8 * j, i0 = bit / 12, sh = bit % 12;
+            uint32_t v = static_cast<uint32_t>(code[0][t][i0]) >> sh;
+            if (sh > 4) v |= static_cast<uint32_t>(code[0][t][i0 + 1]) << (12 - sh);
+            codes_k[(out0 + t) * KROW + j] = static_cast<uint8_t>(v & 0xffu);
         }
     }
 }
@@ -139,7 +284,7 @@ hipError_t launch_encode_append(int k_bits, const void* k_new, const void* v_new
                                 const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                                 uint8_t* codes_k, uint8_t* codes_v, int batch, int num_kv_heads,
                                 int capacity, int cur_len, int num_new, hipStream_t stream) {
-    const dim3 grid(num_new, num_kv_heads, batch);
+    const dim3 grid((num_new + kEncTok - 1) / kEncTok, num_kv_heads, batch);
     if (k_bits == 8)
         hipLaunchKernelGGL(encode_append_kernel<8>, grid, dim3(kEncThreads), 0, stream, k_new,
                            v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
