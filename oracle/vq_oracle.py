@@ -15,7 +15,7 @@ over the dequantised cache.  So this oracle is that definition written
 out — dequantise by table lookup, transform the query, textbook softmax
 attention in float64 — with no blocking, splitting or fusion.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * H_D is the orthonormal Sylvester matrix (1/sqrt(2) per recursion
     level), natural order, no random signs.
   * One lambda in R^128 and one codebook per KV head per tensor, shared by
