@@ -332,14 +332,15 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t tab[2 * kTable];       // keys | values
     __shared__ __attribute__((aligned(16))) uint2 pbuf[kWaves][kTok * 4];  // [token][16 rows] fp16
     __shared__ half8_t qa[4][64];
-    __shared__ float wm[kWaves][G], wl[kWaves][G];
+    __shared__ float wmT[G][kWaves], wlT[G][kWaves];   // per head and wave: m, rescaled l
     __shared__ uint32_t tile_ctr;   // next 32-token tile of the split to hand out
     // appended token (new-token workgroup): transformed key and value (fp64)
     __shared__ double xnew[2][kHeadDim];
     __shared__ uint32_t newc[2][kNumSub];   // its key and value codes
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: tile indices stay in SGPRs
     if (append_pos >= 0 && split == num_splits) {   // the extra, new-token workgroup
         new_token_workgroup<G, KBITS>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
                                       num_q_heads, num_kv_heads, capacity, append_pos,
@@ -409,11 +410,17 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 
     {
         const uint4 cc = make_uint4(centroid.x, centroid.y, centroid.x, centroid.y);
+        // A thread fills half a row (8 x 16 B).  Its 16-B slots are taken in
+        // an order rotated by tid / 2, so any 16 consecutive lanes store to
+        // 16 distinct 16-B bank groups: without the rotation every lane of a
+        // half row hits the same four banks, and the table build took longer
+        // than the rest of the prologue.
+        const int rot = tid >> 1;
         if constexpr (KBITS == 8) {
             uint4* dst = reinterpret_cast<uint4*>(tab + ((tid >> 1) & 1) * kTable +
                                                   (tid >> 2) * 256 + (tid & 1) * 128);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) dst[s] = cc;
+            for (int s = 0; s < 8; ++s) dst[(s + rot) & 7] = cc;
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             if (tid < 512) {
                 uint4* dst = reinterpret_cast<uint4*>(tab + kTable + (tid >> 1) * 256 + (tid & 1) * 128);
 #pragma unroll
-                for (int s = 0; s < 8; ++s) dst[s] = cc;
+                for (int s = 0; s < 8; ++s) dst[(s + rot) & 7] = cc;
             }
         }
     }
@@ -459,12 +466,24 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     float mA = hA < G ? -INFINITY : INFINITY;
     float mB = hB < G ? -INFINITY : INFINITY;
     float lA = 0.f, lB = 0.f;
+    float thA = mA + kTau, thB = mB + kTau;   // rescale thresholds
     float4_t oacc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+    // p tile of a wave: the 8-byte chunk (token t, rows 4 rb .. 4 rb + 3) sits
+    // in slot 4 t' + (rb ^ 2 o), with o = bit 3 of t and t' = t ^ 4 o.  With
+    // the plain [token][row] order the chunk writes of a 16-lane group hit
+    // every bank pair twice and the transposed reads of lanes 0-15 and 16-31
+    // shared banks (measured: 32 and 4 LDS cycles per instruction); with the
+    // swizzle every 16- or 32-lane write group and every 32-lane read group
+    // covers distinct banks (8 and 2 cycles).
     uint2* pw = pbuf[wave];
     const uint8_t* pw_bytes = reinterpret_cast<const uint8_t*>(pw);
+    const int ow = (n >> 3) & 1, orr = grp & 1;
+    const int pslot_w = 4 * (n ^ (ow << 2)) + (grp ^ (2 * ow));        // token n (+ 64 for 16 + n)
+    const uint32_t pread0 = 8u * (4 * (8 * grp + 4 * orr + kq) + (aq4 ^ (2 * orr)));        // tokens 8 grp + kq
+    const uint32_t pread1 = 8u * (4 * (8 * grp + 4 * (orr ^ 1) + kq) + (aq4 ^ (2 * orr)));  // tokens 8 grp + 4 + kq
     const uint32_t kslot = static_cast<uint32_t>(lane & 31) * 8;               // key table
     const uint32_t vslot = 0x10000u | (static_cast<uint32_t>(lane & 31) * 8);  // value table
 
@@ -510,13 +529,18 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
                 sB[sb] = live ? sB[sb] : -INFINITY;
             }
         }
-        const float tA = row_max16(fmaxf(sA[0], sA[1]));
-        const float tB = row_max16(fmaxf(sB[0], sB[1]));
-        if (__builtin_amdgcn_ballot_w64(tA > mA + kTau || tB > mB + kTau) != 0) {
-            const float nA = fmaxf(mA, tA), nB = fmaxf(mB, tB);
+        // A row's maximum exceeds m + tau exactly when one of its scores
+        // does, so the rescale test needs no row reduction; the row maxima
+        // are formed only on the (rare) rescale.
+        if (__builtin_amdgcn_ballot_w64(sA[0] > thA || sA[1] > thA || sB[0] > thB ||
+                                        sB[1] > thB) != 0) {
+            const float nA = fmaxf(mA, row_max16(fmaxf(sA[0], sA[1])));
+            const float nB = fmaxf(mB, row_max16(fmaxf(sB[0], sB[1])));
             const float fA = rescale_factor(mA, nA), fB = rescale_factor(mB, nB);
             mA = nA;
             mB = nB;
+            thA = nA + kTau;
+            thB = nB + kTau;
             lA *= fA;
             lB *= fB;
 #pragma unroll
@@ -536,15 +560,14 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             // hi parts round toward zero; the remainders are exact in fp32
             const uint32_t hi = pack_rtz(pA, pB);
             const uint32_t lo = pack_rtz(pA - lo_half_to_float(hi), pB - hi_half_to_float(hi));
-            pw[(16 * sb + n) * 4 + grp] = make_uint2(hi, lo);   // token 16 sb + n, rows 4 grp + i
+            pw[pslot_w + 64 * sb] = make_uint2(hi, lo);   // token 16 sb + n, rows 4 grp + i
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // V A operand: lane (16 grp + r) gets p row r of tokens 8 grp .. 8 grp + 7
-        const half8_t ap = cat(read_tr16(pw_bytes + (8 * grp + kq) * 32 + aq4 * 8),
-                               read_tr16(pw_bytes + (8 * grp + 4 + kq) * 32 + aq4 * 8));
+        const half8_t ap = cat(read_tr16(pw_bytes + pread0), read_tr16(pw_bytes + pread1));
 
         // ---- values: 8 N-tiles of 16 channels, gathered 2 tiles at a time ------
         // N-tile c, column 4a + e is channel 4 (8a + c) + e = 32 a + 4 c + e
@@ -600,43 +623,72 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // ---- fold the waves' states, leave one partial per split ----------------
     // lane (16 grp + 4 a + e), N-tile c holds channel 32 a + 4 c + e of rows
     // (hA hi, hB hi, hA lo, hB lo); a wave that got no tile has m = -inf.
+    //  1. every wave publishes its m per head;
+    //  2. every wave reads the maxima M over the waves, rescales its l and o by
+    //     2^(m - M) in registers and stores them lane by lane (no bank
+    //     conflicts: a channel-major store had four-way conflicts and took
+    //     longer than the rest of the fold);
+    //  3. the partial is then a plain sum over the waves.
     lA = row_sum16(lA);
     lB = row_sum16(lB);
-    __syncthreads();                                      // everyone is done with tab
-    float* obuf = reinterpret_cast<float*>(tab);          // [kWaves][G][128]
     if (n == 0) {
-        if (hA < G) { wm[wave][hA] = mA; wl[wave][hA] = lA; }
-        if (hB < G) { wm[wave][hB] = mB; wl[wave][hB] = lB; }
+        if (hA < G) wmT[hA][wave] = mA;
+        if (hB < G) wmT[hB][wave] = mB;
     }
+    __syncthreads();   // the m are complete, and every wave is done with tab
+    float MA = -INFINITY, MB = -INFINITY;
     {
-        const int a = n >> 2, e = n & 3;
+        // lane row r reduces heads r and r + 4 over the 16 waves
+        const float mr0 = row_max16(wmT[min(grp, G - 1)][n]);
+        const float mr1 = row_max16(wmT[min(grp + 4, G - 1)][n]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int d = 32 * a + 4 * c + e;
-            if (hA < G) obuf[(wave * G + hA) * kHeadDim + d] = oacc[c][0] + oacc[c][2];
-            if (hB < G) obuf[(wave * G + hB) * kHeadDim + d] = oacc[c][1] + oacc[c][3];
+        for (int h = 0; h < G; ++h) {
+            const float mh = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, h < 4 ? mr0 : mr1), 16 * (h & 3)));
+            MA = (hA == h) ? mh : MA;
+            MB = (hB == h) ? mh : MB;
         }
+    }
+    const float fA = (hA < G && mA != -INFINITY) ? fast_exp2(mA - MA) : 0.f;
+    const float fB = (hB < G && mB != -INFINITY) ? fast_exp2(mB - MB) : 0.f;
+    constexpr int kLanes = 16 * ((G + 1) / 2);   // lanes holding rows of real heads
+    float2* obuf = reinterpret_cast<float2*>(tab);   // [kWaves][8][kLanes] (head hA, head hB)
+    if (lane < kLanes) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            obuf[(wave * 8 + c) * kLanes + lane] =
+                make_float2(fA * (oacc[c][0] + oacc[c][2]), fB * (oacc[c][1] + oacc[c][3]));
+    }
+    if (n == 0) {
+        if (hA < G) wlT[hA][wave] = fA * lA;
+        if (hB < G) wlT[hB][wave] = fB * lB;
     }
     __syncthreads();
     const size_t pbase = (static_cast<size_t>(b) * num_q_heads + g * G) * part_stride + split;
-    for (int i = tid; i < G * kHeadDim; i += kThreads) {
-        const int h = i / kHeadDim, d = i % kHeadDim;
-        float mx = -INFINITY;
+    constexpr int kItems = 8 * kLanes * 2;   // (N-tile, lane, head of the lane's pair)
+    static_assert(kItems <= kThreads, "one fold item per thread");
+    if (tid < kItems) {
+        const int comp = tid & 1, ln = (tid >> 1) % kLanes, c = (tid >> 1) / kLanes;
+        const float* src = reinterpret_cast<const float*>(obuf) + (c * kLanes + ln) * 2 + comp;
+        float os = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, wm[w][h]);
-        float ls = 0.f, os = 0.f;
+        for (int w = 0; w < kWaves; ++w) os += src[w * 8 * kLanes * 2];
+        const int h = 2 * (ln >> 4) + comp;
+        if (h < G) {
+            const int d = 32 * ((ln & 15) >> 2) + 4 * c + (ln & 3);
+            part.o[(pbase + static_cast<size_t>(h) * part_stride) * kHeadDim + d] = os;
+        }
+    }
+    if (tid < G) {
+        float mx = -INFINITY, ls = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = (wm[w][h] == -INFINITY) ? 0.f : fast_exp2(wm[w][h] - mx);
-            ls += f * wl[w][h];
-            os += f * obuf[(w * G + h) * kHeadDim + d];
+            mx = fmaxf(mx, wmT[tid][w]);
+            ls += wlT[tid][w];
         }
-        const size_t pi = pbase + static_cast<size_t>(h) * part_stride;
-        part.o[pi * kHeadDim + d] = os;
-        if (d == 0) {
-            part.m[pi] = mx;
-            part.l[pi] = ls;
-        }
+        const size_t pi = pbase + static_cast<size_t>(tid) * part_stride;
+        part.m[pi] = mx;
+        part.l[pi] = ls;
     }
 }
 

@@ -291,6 +291,7 @@ int vq_merge_partials(int32_t batch, int32_t num_q_heads, int32_t num_partials,
                       "merge_partials launch");
 }
 
+extern "C++" {  // helpers with C++ return types: not part of the C ABI
 namespace {
 
 // Shared by the decode-step entry points: validate the appended rows, then
@@ -334,6 +335,7 @@ vqkv::AppendArgs append_args(const void* k_new, const void* v_new, int kv_dtype,
 }
 
 }  // namespace
+}  // extern "C++"
 
 int32_t vq_decode_step_num_partials(const vq_layout* layout, int32_t batch, int32_t num_q_heads,
                                     int32_t cur_len, int32_t requested) {
