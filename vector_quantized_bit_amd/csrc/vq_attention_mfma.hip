@@ -31,7 +31,10 @@
 //  * Code rows stay token-major in HBM.  Loads are raw buffer loads of 8
 //    (or 12) contiguous bytes per lane: the split's rows form the buffer
 //    range, so rows past the split's end read as zero without any clamp.
-//    Two register sets alternate so one tile of loads is always in flight.
+//    One register set: once a tile's key gathers are issued its key-code
+//    registers take the next tile's key codes, and likewise the value codes
+//    after the value gathers, so the next tile's loads are in flight while
+//    the rest of the tile is computed.
 //  * Tiles are handed to waves dynamically (LDS counter), so the tokens a
 //    wave folds into its online softmax depend on timing: results agree run
 //    to run to fp32 rounding, not bit for bit.
@@ -86,6 +89,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float rescale_factor(float m_old, float m_new) {
     return (m_old == m_new) ? 1.f : fast_exp2(m_old - m_new);
+}
+
+// Lanes 0-31 of a, then lanes 0-31 of b (in lanes 32-63): one permlane swap.
+__device__ __forceinline__ float lo_halves(float a, float b) {
+    return __builtin_bit_cast(float, static_cast<uint32_t>(__builtin_amdgcn_permlane32_swap(
+        __builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), false, false)[0]));
 }
 
 __device__ __forceinline__ uint32_t pack_rtz(float a, float b) {
@@ -327,6 +336,10 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     int append_pos, uint8_t* __restrict__ new_codes_k, uint8_t* __restrict__ new_codes_v,
     int part_stride) {
     static_assert(G >= 1 && G <= 8, "2G MFMA rows");
+    // G <= 4: the rows of every head are in lanes 0-31 of an MFMA result, so
+    // the softmax packs a tile's two 16-token blocks into one set of lanes
+    constexpr bool kPack = G <= 4;
+    constexpr int kSb = kPack ? 1 : 2;   // 16-token score blocks per lane and tile
     constexpr int KROW = kNumSub * KBITS / 8;
 
     __shared__ __attribute__((aligned(16))) uint8_t tab[2 * kTable];       // keys | values
@@ -391,8 +404,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint32_t qw0 = qw[0];
     const uint32_t qw1 = qw[q_f32 ? 1 : 0];
     const float2 lam2 = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
-    KChunk<KBITS> kA[2], kB[2];
-    uint2 vA[2], vB[2];
+    KChunk<KBITS> kA[2];
+    uint2 vA[2];
     // (the whole offset goes in the VGPR operand: the buffer range check
     // covers the VGPR offset, not the scalar one)
     auto load_tile = [&](int rel, KChunk<KBITS>* kk_, uint2* vv_) {
@@ -432,6 +445,10 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             }
         }
     }
+    if constexpr (kPack) {   // p rows 8-15 (heads 4-7) are never written: keep them zero
+        reinterpret_cast<uint4*>(&pbuf[0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);
+        static_assert(sizeof(pbuf) == kThreads * sizeof(uint4), "one 16-byte store per thread");
+    }
     float x0 = q_f32 ? __builtin_bit_cast(float, qw0) : lo_half_to_float(qw0);
     float x1 = q_f32 ? __builtin_bit_cast(float, qw1) : hi_half_to_float(qw0);
     // Every wave transforms (waves >= G a copy of head G - 1, discarded), so
@@ -460,11 +477,15 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     }
     __syncthreads();
 
-    // lane state: rows 4 grp .. 4 grp + 3 = (hA hi, hB hi, hA lo, hB lo)
+    // MFMA rows of lane 16 grp + n: 4 grp .. 4 grp + 3 = (hA hi, hB hi, hA lo, hB lo)
     const int hA = 2 * grp, hB = 2 * grp + 1;
+    // softmax state of the lane: heads sh, sh + 1 for token tok0 + n of each
+    // 16-token block it holds (see the online softmax below)
+    const int sh = kPack ? 2 * (grp & 1) : hA;
+    const int tok0 = kPack ? 16 * (grp >> 1) : 0;
     // heads >= G start at m = +inf, so their p = 2^(s - m) is 0 with no mask
-    float mA = hA < G ? -INFINITY : INFINITY;
-    float mB = hB < G ? -INFINITY : INFINITY;
+    float mA = sh < G ? -INFINITY : INFINITY;
+    float mB = sh + 1 < G ? -INFINITY : INFINITY;
     float lA = 0.f, lB = 0.f;
     float thA = mA + kTau, thB = mB + kTau;   // rescale thresholds
     float4_t oacc[8];
@@ -479,15 +500,18 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // swizzle every 16- or 32-lane write group and every 32-lane read group
     // covers distinct banks (8 and 2 cycles).
     uint2* pw = pbuf[wave];
+    // the score A operand stays in registers for the whole loop
+    const half8_t qr[4] = {qa[0][lane], qa[1][lane], qa[2][lane], qa[3][lane]};
     const uint8_t* pw_bytes = reinterpret_cast<const uint8_t*>(pw);
     const int ow = (n >> 3) & 1, orr = grp & 1;
-    const int pslot_w = 4 * (n ^ (ow << 2)) + (grp ^ (2 * ow));        // token n (+ 64 for 16 + n)
+    const int rbw = kPack ? (grp & 1) : grp;   // row block (head pair) this lane writes
+    const int pslot_w = 4 * tok0 + 4 * (n ^ (ow << 2)) + (rbw ^ (2 * ow));   // token tok0 + n (+ 64: + 16)
     const uint32_t pread0 = 8u * (4 * (8 * grp + 4 * orr + kq) + (aq4 ^ (2 * orr)));        // tokens 8 grp + kq
     const uint32_t pread1 = 8u * (4 * (8 * grp + 4 * (orr ^ 1) + kq) + (aq4 ^ (2 * orr)));  // tokens 8 grp + 4 + kq
     const uint32_t kslot = static_cast<uint32_t>(lane & 31) * 8;               // key table
     const uint32_t vslot = 0x10000u | (static_cast<uint32_t>(lane & 31) * 8);  // value table
 
-    auto compute_tile = [&](int rel_, const KChunk<KBITS>* kc, const uint2* vc) {
+    auto compute_tile = [&](int rel_, KChunk<KBITS>* kc, uint2* vc, int nrel) {
         // ---- scores: 2 blocks of 16 tokens, 4 K-steps of 32 dims ------------
         float4_t sacc[2];
 #pragma unroll
@@ -507,24 +531,40 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
                     kg[2] = *reinterpret_cast<const uint2*>(tab + kc[sb].template addr<6>(kslot));
                     kg[3] = *reinterpret_cast<const uint2*>(tab + kc[sb].template addr<7>(kslot));
                 }
-                sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk][lane], cat(kg[0], kg[1]),
+                sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qr[kk], cat(kg[0], kg[1]),
                                                                   sacc[sb], 0, 0, 0);
-                sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk + 1][lane], cat(kg[2], kg[3]),
+                sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qr[kk + 1], cat(kg[2], kg[3]),
                                                                   sacc[sb], 0, 0, 0);
             }
         }
 
-        // ---- online softmax (base 2) -----------------------------------------
-        float sA[2], sB[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            sA[sb] = sacc[sb][0] + sacc[sb][2];
-            sB[sb] = sacc[sb][1] + sacc[sb][3];
+        __builtin_amdgcn_sched_barrier(0);
+        {   // this tile's key codes are consumed: the next tile's go into the same registers
+            const uint32_t ks = static_cast<uint32_t>(nrel * KROW);
+            kc[0].load(krsrc, koff0 + ks, 0);
+            kc[1].load(krsrc, koff1 + ks, 0);
         }
-        if (rel_ + kTok > t_len) {               // the split's last, partial tile
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- online softmax (base 2) -----------------------------------------
+        // With G <= 4 every head's rows sit in lanes 0-31, so the scores of
+        // tokens 16-31 move to lanes 32-63 (one permlane swap) and the
+        // softmax runs once per tile: lane 16 grp + n then holds token
+        // 16 (grp / 2) + n of heads 2 (grp % 2) and 2 (grp % 2) + 1.
+        float sA[kSb], sB[kSb];
+        if constexpr (kPack) {
+            sA[0] = lo_halves(sacc[0][0] + sacc[0][2], sacc[1][0] + sacc[1][2]);
+            sB[0] = lo_halves(sacc[0][1] + sacc[0][3], sacc[1][1] + sacc[1][3]);
+        } else {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
-                const bool live = rel_ + 16 * sb + n < t_len;
+                sA[sb] = sacc[sb][0] + sacc[sb][2];
+                sB[sb] = sacc[sb][1] + sacc[sb][3];
+            }
+        }
+        if (__builtin_expect(rel_ + kTok > t_len, 0)) {   // the split's last, partial tile
+#pragma unroll
+            for (int sb = 0; sb < kSb; ++sb) {
+                const bool live = rel_ + tok0 + 16 * sb + n < t_len;
                 sA[sb] = live ? sA[sb] : -INFINITY;
                 sB[sb] = live ? sB[sb] : -INFINITY;
             }
@@ -532,10 +572,22 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         // A row's maximum exceeds m + tau exactly when one of its scores
         // does, so the rescale test needs no row reduction; the row maxima
         // are formed only on the (rare) rescale.
-        if (__builtin_amdgcn_ballot_w64(sA[0] > thA || sA[1] > thA || sB[0] > thB ||
-                                        sB[1] > thB) != 0) {
-            const float nA = fmaxf(mA, row_max16(fmaxf(sA[0], sA[1])));
-            const float nB = fmaxf(mB, row_max16(fmaxf(sB[0], sB[1])));
+        bool over = false;
+#pragma unroll
+        for (int sb = 0; sb < kSb; ++sb) over = over || sA[sb] > thA || sB[sb] > thB;
+        if (__builtin_amdgcn_ballot_w64(over) != 0) {
+            float cA = sA[0], cB = sB[0];
+            if constexpr (!kPack) {
+                cA = fmaxf(sA[0], sA[1]);
+                cB = fmaxf(sB[0], sB[1]);
+            }
+            cA = row_max16(cA);
+            cB = row_max16(cB);
+            if constexpr (kPack) {   // the same heads' other 16 tokens
+                cA = fmaxf(cA, lane_partner<32>(cA, lane));
+                cB = fmaxf(cB, lane_partner<32>(cB, lane));
+            }
+            const float nA = fmaxf(mA, cA), nB = fmaxf(mB, cB);
             const float fA = rescale_factor(mA, nA), fB = rescale_factor(mB, nB);
             mA = nA;
             mB = nB;
@@ -552,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             }
         }
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+        for (int sb = 0; sb < kSb; ++sb) {
             const float pA = fast_exp2(sA[sb] - mA);
             const float pB = fast_exp2(sB[sb] - mB);
             lA += pA;
@@ -560,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             // hi parts round toward zero; the remainders are exact in fp32
             const uint32_t hi = pack_rtz(pA, pB);
             const uint32_t lo = pack_rtz(pA - lo_half_to_float(hi), pB - hi_half_to_float(hi));
-            pw[pslot_w + 64 * sb] = make_uint2(hi, lo);   // token 16 sb + n, rows 4 grp + i
+            pw[pslot_w + 64 * sb] = make_uint2(hi, lo);   // this lane's token, rows of its heads
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -592,32 +644,32 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
                 oacc[2 * q4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     ap, cat(x[i][0], x[i][1]), oacc[2 * q4 + i], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        {   // and the value codes
+            const uint32_t vs = static_cast<uint32_t>(nrel * kNumSub);
+            const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff0 + vs, 0, 0);
+            const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff1 + vs, 0, 0);
+            vc[0] = make_uint2(v0[0], v0[1]);
+            vc[1] = make_uint2(v1[0], v1[1]);
+        }
     };
 
     // Tiles are handed out from an LDS counter as waves become free: the SIMD
     // issue arbiter favours older waves, so a fixed interleave leaves the
-    // youngest waves with a long tail.  Two register sets alternate: the next
-    // tile's loads are in flight while the current one is computed.
+    // youngest waves with a long tail.  A single register set holds a tile's
+    // codes and is refilled during the tile (a second set, alternated by
+    // unrolling, made the compiler copy the 32 output accumulators on every
+    // other tile).
     auto grab = [&]() -> int {
         uint32_t v = 0;
         if (lane == 0) v = atomicAdd(&tile_ctr, 1u);
         return static_cast<int>(__builtin_amdgcn_readfirstlane(v));
     };
     int cur = wave;
-    if (cur * kTok < t_len) {
-        int nxt = grab();
-        for (;;) {
-            load_tile(nxt * kTok, kB, vB);
-            compute_tile(cur * kTok, kA, vA);
-            cur = nxt;
-            if (cur * kTok >= t_len) break;
-            nxt = grab();
-            load_tile(nxt * kTok, kA, vA);
-            compute_tile(cur * kTok, kB, vB);
-            cur = nxt;
-            if (cur * kTok >= t_len) break;
-            nxt = grab();
-        }
+    while (cur * kTok < t_len) {
+        const int nxt = grab();
+        compute_tile(cur * kTok, kA, vA, nxt * kTok);
+        cur = nxt;
     }
 
     // ---- fold the waves' states, leave one partial per split ----------------
@@ -631,6 +683,10 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     //  3. the partial is then a plain sum over the waves.
     lA = row_sum16(lA);
     lB = row_sum16(lB);
+    if constexpr (kPack) {   // the same heads' sums over the other 16-token blocks
+        lA += lane_partner<32>(lA, lane);
+        lB += lane_partner<32>(lB, lane);
+    }
     if (n == 0) {
         if (hA < G) wmT[hA][wave] = mA;
         if (hB < G) wmT[hB][wave] = mB;
