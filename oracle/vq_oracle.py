@@ -39,7 +39,8 @@ __all__ = [
     "sylvester_hadamard", "smooth_factors", "transform_keys", "transform_query",
     "vq_assign", "vq_encode", "vq_decode", "pack_codes", "unpack_codes",
     "softmax_attention", "decode_attention", "decode_attention_head",
-    "encode_append", "lloyd_kmeans", "codebook_bytes", "index_bytes",
+    "encode_append", "decode_attention_window_head", "decode_attention_window",
+    "lloyd_kmeans", "codebook_bytes", "index_bytes",
     "commvq_reduction_ratio",
 ]
 
@@ -226,6 +227,49 @@ def decode_attention(q, lam, cb_k, cb_v, codes_k, codes_v, context_len: int,
             out[b, heads] = decode_attention_head(
                 q[b, heads], lam[g], cb_k[g], cb_v[g],
                 codes_k[b, g, :context_len], codes_v[b, g, :context_len], k_bits, v_bits)
+    return out
+
+
+def decode_attention_window_head(q_heads, lam, cb_k, cb_v, codes_k, codes_v, win_k, win_v,
+                                 k_bits: int = 8, v_bits: int = 8) -> np.ndarray:
+    """Attention of the G query heads of one KV head over its coded tokens and
+    a full-precision residual window, in one softmax.
+
+    [VecInfer] Experiments: every method keeps the most recent tokens (the
+    residual, length 128) in full precision; the HACK notes page keeps its
+    last, not yet full block in fp16 beside the quantised cache in the same
+    attention.  win_k / win_v [n_win, D] are raw (untransformed) rows.  A raw
+    key k scores q . k, which equals q~ . k~ with k~ = k diag(lambda)^-1 H_D
+    (H_D orthonormal): the window keys are transformed like the cache's,
+    appended to the dequantised keys, and one textbook softmax runs over the
+    union.  Returns float64 [G, D].
+    """
+    dim = np.asarray(q_heads).shape[-1]
+    sub = np.asarray(cb_k).shape[1]
+    k_hat = vq_decode(unpack_codes(codes_k, k_bits, dim // sub), cb_k)
+    v_hat = vq_decode(unpack_codes(codes_v, v_bits, dim // sub), cb_v)
+    keys = np.concatenate([k_hat, transform_keys(np.asarray(win_k, dtype=np.float64), lam)])
+    values = np.concatenate([v_hat, np.asarray(win_v, dtype=np.float64)])
+    return softmax_attention(transform_query(q_heads, lam), keys, values)
+
+
+def decode_attention_window(q, lam, cb_k, cb_v, codes_k, codes_v, num_codes: int, win_k, win_v,
+                            win_len: int, k_bits: int = 8, v_bits: int = 8) -> np.ndarray:
+    """Full layer with a residual window: q [B, Hq, D]; codes_* [B, Hkv, >=num_codes,
+    bytes]; win_* [B, Hkv, >=win_len, D].  Query head h reads KV head h // G.
+    Returns float64 [B, Hq, D]."""
+    q = np.asarray(q)
+    batch, hq, dim = q.shape
+    hkv = np.asarray(lam).shape[0]
+    group = hq // hkv
+    out = np.empty((batch, hq, dim), dtype=np.float64)
+    for b in range(batch):
+        for g in range(hkv):
+            heads = slice(g * group, (g + 1) * group)
+            out[b, heads] = decode_attention_window_head(
+                q[b, heads], lam[g], cb_k[g], cb_v[g], codes_k[b, g, :num_codes],
+                codes_v[b, g, :num_codes], win_k[b, g, :win_len], win_v[b, g, :win_len],
+                k_bits, v_bits)
     return out
 
 

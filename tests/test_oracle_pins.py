@@ -259,6 +259,50 @@ def test_identical_keys_give_uniform_weights():
     np.testing.assert_allclose(out[0, 1], vhat.mean(0), rtol=1e-12, atol=1e-13)
 
 
+# --- residual window ------------------------------------------------------------
+
+def test_window_empty_equals_codes_only():
+    rng = np.random.default_rng(40)
+    q, lam, cb_k, cb_v, codes_k, codes_v, _, _ = _lossless_layer(rng, 2, 4, 77, 8)
+    win = np.zeros((1, 2, 5, 128))
+    a = oracle.decode_attention_window(q[None], lam, cb_k, cb_v, codes_k, codes_v, 77, win, win, 0)
+    b = oracle.decode_attention(q[None], lam, cb_k, cb_v, codes_k, codes_v, 77)
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("hkv,group", [(1, 4), (2, 3)])
+def test_window_only_is_raw_domain_attention(hkv, group):
+    # no codes: the window keys are used untransformed against the raw query
+    rng = np.random.default_rng(41 + hkv)
+    n = 9
+    q = rng.standard_normal((1, hkv * group, 128)).astype(np.float16)
+    lam = (1 + 3 * rng.random((hkv, 128))).astype(np.float32)
+    cb_k = rng.standard_normal((hkv, 256, 4)).astype(np.float16)
+    cb_v = rng.standard_normal((hkv, 256, 4)).astype(np.float16)
+    codes = np.zeros((1, hkv, 4, 32), np.uint8)
+    wk = rng.standard_normal((1, hkv, n, 128)).astype(np.float16)
+    wv = rng.standard_normal((1, hkv, n, 128)).astype(np.float16)
+    out = oracle.decode_attention_window(q, lam, cb_k, cb_v, codes, codes, 0, wk, wv, n)
+    for h in range(hkv * group):
+        ref = oracle.softmax_attention(q[0, h].astype(np.float64), wk[0, h // group], wv[0, h // group])
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("hkv,group,k_bits,moved", [(1, 4, 8, 1), (2, 5, 8, 17), (2, 4, 12, 60)])
+def test_window_token_equals_its_coded_twin(hkv, group, k_bits, moved):
+    # a coded token and its raw-domain key/value placed in the window instead
+    # contribute the same term: moving the last tokens changes nothing
+    rng = np.random.default_rng(50 + moved)
+    n = 140
+    q, lam, cb_k, cb_v, codes_k, codes_v, keys, vals = _lossless_layer(rng, hkv, group, n, k_bits)
+    full = oracle.decode_attention(q[None], lam, cb_k, cb_v, codes_k, codes_v, n, k_bits, 8)
+    wk = np.stack([keys[g][n - moved:] for g in range(hkv)])[None]
+    wv = np.stack([vals[g][n - moved:] for g in range(hkv)])[None]
+    split = oracle.decode_attention_window(q[None], lam, cb_k, cb_v, codes_k, codes_v, n - moved,
+                                           wk, wv, moved, k_bits, 8)
+    np.testing.assert_allclose(split, full, rtol=1e-10, atol=1e-11)
+
+
 def test_encode_append_lossless_keys():
     rng = np.random.default_rng(22)
     q, lam, cb_k, cb_v, codes_k, codes_v, keys, vals = _lossless_layer(rng, 1, 1, 40, 8)
