@@ -237,6 +237,55 @@ int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
                             float* part_m, float* part_l, float* part_o, void* stream);
 
 /*
+ * Decode step with a full-precision residual window: the most recent tokens
+ * of every (sequence, KV head) stay in fp16 beside the VQ cache and enter
+ * the same softmax.  VecInfer page, Experiments (every method keeps a
+ * residual of 128 full-precision tokens); HACK page (the last, not yet full
+ * block stays in fp16 and is multiplied in fp16 within the attention, and
+ * is quantised when it fills).
+ * The new token of every (sequence, KV head), rounded to fp16 (round to
+ * nearest even), is written to window slot win_len; then decode attention
+ * runs over the coded tokens [0, num_codes) and the window slots
+ * [0, win_len] in one softmax.  Window keys are raw (untransformed): a raw
+ * key k scores q . k / sqrt(D), which is q~ . k~ / sqrt(D).  One launch of
+ * the split kernel (the extra workgroup per (sequence, KV head) attends over
+ * the window) plus the merge.
+ *   win_k, win_v [B][Hkv][win_cap][128] fp16, caller-owned; slots
+ *   [0, win_len) are read, slot win_len is written.
+ *   codes_k / codes_v: read over [0, num_codes) only (num_codes may be 0).
+ *   workspace: at least vq_decode_step_window_workspace_bytes(...) bytes.
+ * The caller keeps win_len (it grows by one per step).  When the window is
+ * full (win_len == win_cap) the next step returns VQ_ERR_CAPACITY: call
+ * vq_flush_window first.
+ * Errors: VQ_ERR_CAPACITY if num_codes > capacity or win_len >= win_cap;
+ * VQ_ERR_INVALID_ARG for negative lengths, win_cap < 1, null or misaligned
+ * window pointers; otherwise as for vq_decode_step.
+ *
+ * vq_flush_window: encode the win_cap window tokens into code slots
+ * [num_codes, num_codes + win_cap) — exactly vq_encode_append over the
+ * window as fp16 rows (same codes, ties to the lowest index).  Afterwards
+ * the caller's num_codes grows by win_cap and win_len restarts at 0.
+ * Errors as for vq_encode_append (VQ_ERR_CAPACITY if the codes overflow).
+ */
+int32_t vq_decode_step_window_num_partials(const vq_layout* layout, int32_t batch,
+                                           int32_t num_q_heads, int32_t num_codes,
+                                           int32_t requested);
+size_t vq_decode_step_window_workspace_bytes(const vq_layout* layout, int32_t batch,
+                                             int32_t num_q_heads, int32_t num_codes,
+                                             int32_t requested);
+int vq_decode_step_window(const vq_layout* layout, const void* q, int q_dtype, const void* k_new,
+                          const void* v_new, int kv_dtype, const float* lambda,
+                          const uint16_t* cb_k, const uint16_t* cb_v, const uint8_t* codes_k,
+                          const uint8_t* codes_v, uint16_t* win_k, uint16_t* win_v,
+                          int32_t win_cap, int32_t batch, int32_t num_q_heads, int32_t num_codes,
+                          int32_t win_len, int32_t num_splits, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+int vq_flush_window(const vq_layout* layout, const uint16_t* win_k, const uint16_t* win_v,
+                    const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                    uint8_t* codes_k, uint8_t* codes_v, int32_t win_cap, int32_t batch,
+                    int32_t num_codes, void* stream);
+
+/*
  * Uncompressed comparator: the same decode attention over an fp16 cache,
  * o = softmax(q K^T / sqrt(128)) V with fp32 accumulation (VecInfer page,
  * Background, KV cache and attention).  No transform, no quantisation.

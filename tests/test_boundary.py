@@ -259,3 +259,56 @@ def test_decode_step_plan_leaves_room_for_the_new_token_workgroups(lib):
     assert need == 2 * a256(4 * 32 * n) + a256(4 * 128 * 32 * n)
     # the first token of a sequence: no cached tokens, one empty split
     assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 0, 0) == 2
+
+
+def wstep(lib, layout, codes=10, wlen=0, wcap=128, splits=0, kv_dtype=0, kn=A, vn=A, wk=A, wv=A,
+          ws=A, ws_bytes=1 << 30, out=A, hq=4):
+    return lib.vq_decode_step_window(ctypes.byref(layout), A, 0, kn, vn, kv_dtype, A, A, A, A, A,
+                                     wk, wv, wcap, 1, hq, codes, wlen, splits, out, ws, ws_bytes,
+                                     None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(wlen=128), CAPACITY, "window full"),     # no free slot: flush first
+    (dict(wlen=-1), INVALID, "win_len"),
+    (dict(wcap=0), INVALID, "window capacity"),
+    (dict(codes=1001), CAPACITY, "num_codes"),
+    (dict(codes=-1), INVALID, "num_codes"),
+    (dict(wk=None), INVALID, "win_k"),
+    (dict(wv=MIS), INVALID, "win_v"),
+    (dict(kn=None), INVALID, "k_new"),
+    (dict(kv_dtype=7), INVALID, "kv_dtype"),
+    (dict(out=None), INVALID, "out"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(ws_bytes=8), WORKSPACE, "workspace"),
+    (dict(hq=3), INVALID, "multiple"),
+])
+def test_decode_step_window_validation(lib, kw, status, needle):
+    assert wstep(lib, lay(hkv=2), **kw) == status, vq._last_error()
+    assert needle in vq._last_error()
+
+
+def test_decode_step_window_plan(lib):
+    layout = lay(hkv=8, cap=196608)
+    np_ = lib.vq_decode_step_window_num_partials
+    # coded tokens split as in a decode step, plus the window's partial
+    assert np_(ctypes.byref(layout), 1, 32, 196608, 0) == \
+        lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 196608, 0) == 32
+    # no coded tokens: the window workgroup alone, one partial
+    assert np_(ctypes.byref(layout), 1, 32, 0, 0) == 1
+    assert np_(ctypes.byref(layout), 1, 32, -1, 0) == 0
+    need = lib.vq_decode_step_window_workspace_bytes(ctypes.byref(layout), 1, 32, 0, 0)
+    assert need == 2 * 256 + 4 * 128 * 32          # m, l (256-byte aligned) and o of 32 heads
+    # a window-only step with too small a workspace is refused before any launch
+    small = lib.vq_decode_step_window_workspace_bytes(ctypes.byref(lay(hkv=2)), 1, 4, 0, 0)
+    assert wstep(lib, lay(hkv=2), codes=0, ws_bytes=small - 1) == WORKSPACE
+
+
+def test_flush_window_validation(lib):
+    layout = lay(hkv=2, cap=1000)
+    f = lib.vq_flush_window
+    assert f(ctypes.byref(layout), A, A, A, A, A, A, A, 0, 1, 0, None) == INVALID
+    assert "window capacity" in vq._last_error()
+    assert f(ctypes.byref(layout), A, A, A, A, A, A, A, 128, 1, 900, None) == CAPACITY
+    assert f(ctypes.byref(layout), None, A, A, A, A, A, A, 128, 1, 0, None) == INVALID
+    assert f(ctypes.byref(layout), A, A, A, A, A, A, A, 128, 1, -1, None) == INVALID

@@ -462,3 +462,124 @@ def test_decode_step_full_size(config, cur, samples):
     c = random_cache(wl)
     cur = wl.context_len - 1 if cur is None else cur
     check_step(c, cur, heads=samples, what=f"step config{config}")
+
+
+# --- decode step with a full-precision residual window ------------------------------
+
+def window_rows(wl, bsz, hkv, win_cap):
+    """Raw fp16 window rows [B][Hkv][win_cap][128] (the same generator as the
+    model's keys and values, a stream apart from the step's new token)."""
+    wk = np.stack([np.stack([W.kv_rows(wl.config_id, b, g, "k", win_cap + 1, append=True)[1:]
+                             for g in range(hkv)]) for b in range(bsz)]).astype(np.float16)
+    wv = np.stack([np.stack([W.kv_rows(wl.config_id, b, g, "v", win_cap + 1, append=True)[1:]
+                             for g in range(hkv)]) for b in range(bsz)]).astype(np.float16)
+    return wk, wv
+
+
+def check_window_step(c, num_codes, win_len, win_cap=128, splits=0, heads=None, what=""):
+    """decode_step_window: window slot win_len holds the new token in fp16
+    (bit-exact), nothing else is written, and the output equals the oracle's
+    attention over the coded tokens and window slots 0 .. win_len."""
+    wl = c.wl
+    bsz, hkv = c.codes_k.shape[:2]
+    dtype = np.float32 if wl.qkv_dtype == "f32" else np.float16
+    k, v = new_rows(wl, bsz, hkv, dtype)
+    wk, wv = window_rows(wl, bsz, hkv, win_cap)
+    d = upload(c)
+    dwk, dwv = dev(wk), dev(wv)
+    print(f"{what}: num_codes={num_codes} win_len={win_len} win_cap={win_cap}", flush=True)
+    out = vq.decode_step_window(d["q"], dev(k), dev(v), d["lam"], d["cb_k"], d["cb_v"],
+                                d["codes_k"], d["codes_v"], dwk, dwv, num_codes, win_len,
+                                num_splits=splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    exp_wk, exp_wv = wk.copy(), wv.copy()
+    exp_wk[:, :, win_len] = k.astype(np.float16)          # round to nearest even, as stored
+    exp_wv[:, :, win_len] = v.astype(np.float16)
+    assert np.array_equal(dwk.cpu().numpy().view(np.uint16), exp_wk.view(np.uint16)), what
+    assert np.array_equal(dwv.cpu().numpy().view(np.uint16), exp_wv.view(np.uint16)), what
+    assert np.array_equal(d["codes_k"].cpu().numpy(), c.codes_k), what
+    assert np.array_equal(d["codes_v"].cpu().numpy(), c.codes_v), what
+    kb, vb = wl.k_bits, wl.v_bits
+    if heads is None:
+        ref = oracle.decode_attention_window(c.q, c.lam, c.cb_k, c.cb_v, c.codes_k, c.codes_v,
+                                             num_codes, exp_wk, exp_wv, win_len + 1, kb, vb)
+        assert_close(got, ref, what)
+    else:
+        grp = wl.group
+        for b, g in heads:
+            ref = oracle.decode_attention_window_head(
+                c.q[b, g * grp:(g + 1) * grp], c.lam[g], c.cb_k[g], c.cb_v[g],
+                c.codes_k[b, g, :num_codes], c.codes_v[b, g, :num_codes],
+                exp_wk[b, g, :win_len + 1], exp_wv[b, g, :win_len + 1], kb, vb)
+            assert_close(got[b, g * grp:(g + 1) * grp], ref, f"{what} b={b} kv={g}")
+    return got
+
+
+@pytest.mark.parametrize("num_codes,win_len,splits", [
+    (700, 0, 0), (700, 1, 0), (700, 63, 0), (3000, 127, 0), (3000, 64, 3), (512, 50, 0),
+    (1, 17, 0), (0, 0, 0), (0, 5, 0), (0, 127, 0)])
+def test_decode_step_window_positions(num_codes, win_len, splits):
+    wl = W.Workload(90, "adhoc", batch=2, num_q_heads=8, num_kv_heads=2, context_len=3000)
+    check_window_step(random_cache(wl), num_codes, win_len, splits=splits,
+                      what=f"window codes={num_codes} win={win_len} S={splits}")
+
+
+@pytest.mark.parametrize("group,k_bits,dtype,num_codes,win_len", [
+    (5, 12, "f16", 1499, 100), (1, 8, "f16", 300, 7), (8, 12, "f16", 64, 127),
+    (4, 8, "f32", 1024, 31), (3, 8, "f16", 999, 0)])
+def test_decode_step_window_groups_widths_dtypes(group, k_bits, dtype, num_codes, win_len):
+    wl = W.Workload(95 + group, "adhoc", batch=2, num_q_heads=2 * group, num_kv_heads=2,
+                    context_len=1500, k_bits=k_bits, qkv_dtype=dtype)
+    check_window_step(random_cache(wl), num_codes, win_len,
+                      what=f"window G={group} kbits={k_bits} {dtype}")
+
+
+def test_decode_step_window_full_size():
+    # the long-context layer: 196608 coded tokens and a nearly full window
+    wl = W.WORKLOADS[4]
+    check_window_step(random_cache(wl), wl.context_len, 127, heads=[(0, 1), (0, 6)],
+                      what="window config4")
+
+
+def test_window_chain_and_flush():
+    # a window of 4 fills over four steps, is flushed into codes, and the next
+    # step attends over the longer code prefix and a fresh window
+    wl = W.Workload(99, "adhoc", batch=2, num_q_heads=8, num_kv_heads=2, context_len=900)
+    c = random_cache(wl)
+    bsz, hkv, cap4 = 2, 2, 4
+    d = upload(c)
+    wk = torch.zeros((bsz, hkv, cap4, 128), dtype=torch.float16, device=DEV)
+    wv = torch.zeros_like(wk)
+    host_k = np.zeros((bsz, hkv, cap4, 128), np.float16)
+    host_v = np.zeros_like(host_k)
+    num_codes = 700
+    for step in range(cap4 + 1):
+        win_len = step % cap4
+        if step == cap4:   # full: flush into codes [700, 704)
+            vq.flush_window(wk, wv, d["lam"], d["cb_k"], d["cb_v"], d["codes_k"], d["codes_v"],
+                            num_codes)
+            torch.cuda.synchronize()
+            ck, cv = d["codes_k"].cpu().numpy(), d["codes_v"].cpu().numpy()
+            for b in range(bsz):
+                for g in range(hkv):
+                    pk, pv, gk, gv = oracle.encode_append(host_k[b, g], host_v[b, g], c.lam[g],
+                                                          c.cb_k[g], c.cb_v[g], 8, 8)
+                    kt = oracle.transform_keys(host_k[b, g], c.lam[g])
+                    check_codes(ck[b, g, num_codes:num_codes + cap4], pk, gk, 8, kt, c.cb_k[g],
+                                f"flush K b{b} g{g}")
+                    check_codes(cv[b, g, num_codes:num_codes + cap4], pv, gv, 8, host_v[b, g],
+                                c.cb_v[g], f"flush V b{b} g{g}")
+            c = dataclasses.replace(c, codes_k=ck, codes_v=cv)
+            num_codes += cap4
+        k = np.stack([np.stack([W.kv_rows(wl.config_id + step, b, g, "k", 1, append=True)[0]
+                                for g in range(hkv)]) for b in range(bsz)]).astype(np.float16)
+        v = np.stack([np.stack([W.kv_rows(wl.config_id + step, b, g, "v", 1, append=True)[0]
+                                for g in range(hkv)]) for b in range(bsz)]).astype(np.float16)
+        out = vq.decode_step_window(d["q"], dev(k), dev(v), d["lam"], d["cb_k"], d["cb_v"],
+                                    d["codes_k"], d["codes_v"], wk, wv, num_codes, win_len)
+        torch.cuda.synchronize()
+        host_k[:, :, win_len], host_v[:, :, win_len] = k, v
+        ref = oracle.decode_attention_window(c.q, c.lam, c.cb_k, c.cb_v, c.codes_k, c.codes_v,
+                                             num_codes, host_k, host_v, win_len + 1)
+        assert_close(out.cpu().numpy().astype(np.float64), ref, f"chain step {step}")

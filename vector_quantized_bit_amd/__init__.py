@@ -24,6 +24,8 @@ __all__ = [
     "decode_attention_partials", "merge_partials", "prepare_decode_attention_partials",
     "prepare_merge_partials", "decode_step", "prepare_decode_step", "decode_step_partials",
     "prepare_decode_step_partials", "decode_step_num_partials", "decode_step_workspace_bytes",
+    "decode_step_window", "prepare_decode_step_window", "decode_step_window_num_partials",
+    "decode_step_window_workspace_bytes", "flush_window",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqkv.so")
@@ -80,6 +82,13 @@ def library() -> ctypes.CDLL:
         "vq_decode_step_partials": (_c_int, [lp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp,
                                              _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                              _vp]),
+        "vq_decode_step_window_num_partials": (_i32, [lp, _i32, _i32, _i32, _i32]),
+        "vq_decode_step_window_workspace_bytes": (_size, [lp, _i32, _i32, _i32, _i32]),
+        "vq_decode_step_window": (_c_int, [lp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                           _vp, _vp, _size, _vp]),
+        "vq_flush_window": (_c_int, [lp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                     _vp]),
         "vq_fp16_attention_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32]),
         "vq_fp16_decode_attention": (_c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _vp, _vp, _size, _vp]),
@@ -400,6 +409,87 @@ def prepare_decode_step(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_
                          workspace), q.device)
     call.out = out
     return call
+
+
+def _check_window(win_k, win_v, codes_k):
+    batch, hkv = codes_k.shape[0], codes_k.shape[1]
+    for name, t in (("win_k", win_k), ("win_v", win_v)):
+        _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float16 and t.dim() == 4
+              and t.shape[0] == batch and t.shape[1] == hkv and t.shape[3] == 128,
+              f"{name} must be contiguous float16 [B][Hkv][win_cap][128]")
+    _need(win_k.shape == win_v.shape, "win_k and win_v must have the same shape")
+    return int(win_k.shape[2])
+
+
+def decode_step_window_workspace_bytes(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads,
+                                       num_codes, requested: int = 0) -> int:
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    return int(library().vq_decode_step_window_workspace_bytes(ctypes.byref(lay), batch,
+                                                               num_q_heads, num_codes, requested))
+
+
+def decode_step_window_num_partials(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads, num_codes,
+                                    requested: int = 0) -> int:
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    return int(library().vq_decode_step_window_num_partials(ctypes.byref(lay), batch,
+                                                            num_q_heads, num_codes, requested))
+
+
+def _window_step_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, win_k, win_v,
+                      num_codes, win_len, num_splits, out, workspace):
+    batch, hq = _step_common(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v)
+    win_cap = _check_window(win_k, win_v, codes_k)
+    if out is None:
+        out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    if workspace is None:
+        nbytes = library().vq_decode_step_window_workspace_bytes(ctypes.byref(lay), batch, hq,
+                                                                 num_codes, num_splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(k_new), _ptr(v_new),
+            _dtype_code(k_new), _ptr(lam), _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
+            _ptr(win_k), _ptr(win_v), win_cap, batch, hq, num_codes, win_len, num_splits,
+            _ptr(out), _ptr(workspace), workspace.numel())
+    return args, lay, out, workspace
+
+
+def decode_step_window(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, win_k, win_v,
+                       num_codes: int, win_len: int, num_splits: int = 0, out=None,
+                       workspace=None):
+    """Store k_new / v_new [B][Hkv][128] (as fp16) in window slot ``win_len``
+    of win_k / win_v [B][Hkv][win_cap][128], then decode attention over the
+    ``num_codes`` coded tokens and window slots 0 .. win_len in one softmax
+    -> float32 [B][Hq][128]."""
+    args, _, out, _ = _window_step_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v,
+                                        win_k, win_v, num_codes, win_len, num_splits, out,
+                                        workspace)
+    _check(library().vq_decode_step_window(*args, _stream(q)), "vq_decode_step_window")
+    return out
+
+
+def prepare_decode_step_window(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, win_k,
+                               win_v, num_codes: int, win_len: int, num_splits: int = 0,
+                               out=None, workspace=None) -> PreparedCall:
+    """``decode_step_window`` marshalled once; the output is the call's ``out``."""
+    args, lay, out, workspace = _window_step_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k,
+                                                  codes_v, win_k, win_v, num_codes, win_len,
+                                                  num_splits, out, workspace)
+    call = PreparedCall("vq_decode_step_window", library().vq_decode_step_window, args,
+                        (lay, q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, win_k, win_v,
+                         out, workspace), q.device)
+    call.out = out
+    return call
+
+
+def flush_window(win_k, win_v, lam, cb_k, cb_v, codes_k, codes_v, num_codes: int) -> None:
+    """Encode the full window into code slots [num_codes, num_codes + win_cap)."""
+    _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
+    win_cap = _check_window(win_k, win_v, codes_k)
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    _check(library().vq_flush_window(ctypes.byref(lay), _ptr(win_k), _ptr(win_v), _ptr(lam),
+                                     _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
+                                     win_cap, codes_k.shape[0], num_codes, _stream(win_k)),
+           "vq_flush_window")
 
 
 def decode_step_num_partials(codes_k, codes_v, cb_k, cb_v, batch, num_q_heads, cur_len,

@@ -30,6 +30,13 @@ struct AppendArgs {
     int append_pos = -1;
     uint8_t* codes_k = nullptr;   // the cache, written at that slot
     uint8_t* codes_v = nullptr;
+    // Residual window (win_k != nullptr): the new token goes, as fp16, to slot
+    // win_len of win_k / win_v [B][Hkv][win_cap][128] instead of being
+    // encoded, and the extra partial covers window slots 0 .. win_len.
+    uint16_t* win_k = nullptr;
+    uint16_t* win_v = nullptr;
+    int win_len = 0;
+    int win_cap = 0;
 };
 
 // Split-K decode attention over the VQ cache on the matrix cores: one

@@ -326,6 +326,123 @@ __device__ __forceinline__ void new_token_workgroup(
     }
 }
 
+// The residual-window workgroup of one (sequence, KV head), for a decode
+// step that keeps the most recent tokens in full precision (VecInfer page,
+// Experiments: a residual of 128 full-precision tokens beside the VQ cache;
+// HACK page: the last, not yet full block stays in fp16 and is multiplied in
+// fp16 within the same attention).  It replaces the new-token workgroup.
+//  1. The new token's k and v, rounded to fp16, go to window slot win_len.
+//  2. The G query heads attend over window tokens 0 .. win_len with raw
+//     keys: q . k / sqrt(D), which equals q~ . k~ (H_D orthonormal), so the
+//     window needs no transform.  Wave w takes tokens w, w + 16, ...; lane l
+//     holds dims 2l, 2l + 1; every wave keeps an online softmax per head.
+//  3. The 16 wave states fold in LDS into one partial (m, l, o) at split
+//     index `slot`, in the base-2 units of the code splits.
+template <int G>
+__device__ __forceinline__ void window_workgroup(
+    const void* q, int q_f32, const void* k_new, const void* v_new, int kv_f32, int num_q_heads,
+    int num_kv_heads, uint16_t* win_k, uint16_t* win_v, int win_len, int win_cap, Partials part,
+    int part_stride, int slot, float* lds) {
+    constexpr float kScale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
+    constexpr int kWords = kHeadDim / 2;                                  // fp16 pairs per row
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const size_t stream = static_cast<size_t>(b) * num_kv_heads + g;
+    uint32_t* wk = reinterpret_cast<uint32_t*>(win_k) + stream * win_cap * kWords;
+    uint32_t* wv = reinterpret_cast<uint32_t*>(win_v) + stream * win_cap * kWords;
+
+    float qx[G], qy[G];   // the raw query of every head, scaled to base-2 scores
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + h;
+        if (q_f32) {
+            const float2 f = reinterpret_cast<const float2*>(q)[vec * kWords + lane];
+            qx[h] = f.x * kScale;
+            qy[h] = f.y * kScale;
+        } else {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(q)[vec * kWords + lane];
+            qx[h] = half_bits_to_float(w & 0xffffu) * kScale;
+            qy[h] = half_bits_to_float(w >> 16) * kScale;
+        }
+    }
+    // the new token as the window stores it (fp16, round to nearest even)
+    uint32_t kn, vn;
+    if (kv_f32) {
+        const float2 a = reinterpret_cast<const float2*>(k_new)[stream * kWords + lane];
+        const float2 c = reinterpret_cast<const float2*>(v_new)[stream * kWords + lane];
+        kn = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(a.x), static_cast<_Float16>(a.y)});
+        vn = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(c.x), static_cast<_Float16>(c.y)});
+    } else {
+        kn = reinterpret_cast<const uint32_t*>(k_new)[stream * kWords + lane];
+        vn = reinterpret_cast<const uint32_t*>(v_new)[stream * kWords + lane];
+    }
+    if (wave == 0) {
+        wk[static_cast<size_t>(win_len) * kWords + lane] = kn;
+        wv[static_cast<size_t>(win_len) * kWords + lane] = vn;
+    }
+
+    float m[G], l[G], ox[G], oy[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = ox[h] = oy[h] = 0.f;
+    }
+    for (int t = wave; t <= win_len; t += kWaves) {
+        uint32_t kw = kn, vw = vn;   // slot win_len: the new token, from registers
+        if (t < win_len) {
+            kw = wk[static_cast<size_t>(t) * kWords + lane];
+            vw = wv[static_cast<size_t>(t) * kWords + lane];
+        }
+        const float kx = half_bits_to_float(kw & 0xffffu), ky = half_bits_to_float(kw >> 16);
+        const float vx = half_bits_to_float(vw & 0xffffu), vy = half_bits_to_float(vw >> 16);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float sc = wave_sum(qx[h] * kx + qy[h] * ky);
+            const float mn = fmaxf(m[h], sc);
+            const float f = (m[h] == -INFINITY) ? 0.f : fast_exp2(m[h] - mn);
+            const float p = fast_exp2(sc - mn);
+            l[h] = l[h] * f + p;
+            ox[h] = ox[h] * f + p * vx;
+            oy[h] = oy[h] * f + p * vy;
+            m[h] = mn;
+        }
+    }
+
+    // fold: LDS m, l [kWaves][G] and o [kWaves][G][128]
+    float* fm = lds;
+    float* fl = fm + kWaves * G;
+    float* fo = fl + kWaves * G;
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            fm[wave * G + h] = m[h];
+            fl[wave * G + h] = l[h];
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+        reinterpret_cast<float2*>(fo + (wave * G + h) * kHeadDim)[lane] = make_float2(ox[h], oy[h]);
+    __syncthreads();
+    for (int i = tid; i < G * kHeadDim; i += kThreads) {
+        const int h = i / kHeadDim, d = i % kHeadDim;
+        float mx = -INFINITY;
+        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, fm[w * G + h]);
+        float ls = 0.f, os = 0.f;
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = (fm[w * G + h] == -INFINITY) ? 0.f : fast_exp2(fm[w * G + h] - mx);
+            ls += f * fl[w * G + h];
+            os += f * fo[(w * G + h) * kHeadDim + d];
+        }
+        const size_t pi = (static_cast<size_t>(b) * num_q_heads + g * G + h) * part_stride + slot;
+        part.o[pi * kHeadDim + d] = os;
+        if (d == 0) {
+            part.m[pi] = mx;
+            part.l[pi] = ls;
+        }
+    }
+}
+
 template <int G, int KBITS>
 __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const void* __restrict__ q, int q_f32, const float* __restrict__ lambda,
@@ -334,7 +451,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     int num_kv_heads, int capacity, int context_len, int num_splits, int tokens_per_split,
     Partials part, const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
     int append_pos, uint8_t* __restrict__ new_codes_k, uint8_t* __restrict__ new_codes_v,
-    int part_stride) {
+    int part_stride, uint16_t* __restrict__ win_k, uint16_t* __restrict__ win_v, int win_len,
+    int win_cap) {
     static_assert(G >= 1 && G <= 8, "2G MFMA rows");
     // G <= 4: the rows of every head are in lanes 0-31 of an MFMA result, so
     // the softmax packs a tile's two 16-token blocks into one set of lanes
@@ -354,6 +472,12 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: tile indices stay in SGPRs
+    if (append_pos >= 0 && split == num_splits && win_k != nullptr) {   // the residual window
+        window_workgroup<G>(q, q_f32, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, win_k, win_v,
+                            win_len, win_cap, part, part_stride, num_splits,
+                            reinterpret_cast<float*>(tab));
+        return;
+    }
     if (append_pos >= 0 && split == num_splits) {   // the extra, new-token workgroup
         new_token_workgroup<G, KBITS>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
                                       num_q_heads, num_kv_heads, capacity, append_pos,
@@ -767,7 +891,8 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
                            stream, q, q_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,   \
                            s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
                            s.num_splits, s.tokens_per_split, part, ap.k_new, ap.v_new,        \
-                           ap.kv_f32 ? 1 : 0, pos, ap.codes_k, ap.codes_v, stride);          \
+                           ap.kv_f32 ? 1 : 0, pos, ap.codes_k, ap.codes_v, stride,           \
+                           ap.win_k, ap.win_v, ap.win_len, ap.win_cap);                      \
         break;
     switch (group) {
         VQKV_LAUNCH(1)

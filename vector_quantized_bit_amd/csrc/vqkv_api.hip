@@ -334,6 +334,57 @@ vqkv::AppendArgs append_args(const void* k_new, const void* v_new, int kv_dtype,
     return app;
 }
 
+// A window step splits the num_codes coded tokens like a decode step; with
+// no coded tokens there is no code split, only the window workgroup.
+SplitPlan plan_window_step(int streams, int num_codes, int requested) {
+    if (num_codes == 0) return SplitPlan{0, 0};
+    return plan_step(streams, num_codes, requested);
+}
+
+int check_window_step_args(const vq_layout* layout, const void* q, int q_dtype,
+                           const void* k_new, const void* v_new, int kv_dtype,
+                           const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                           const uint8_t* codes_k, const uint8_t* codes_v, const uint16_t* win_k,
+                           const uint16_t* win_v, int32_t win_cap, int32_t batch,
+                           int32_t num_q_heads, int32_t num_codes, int32_t win_len,
+                           int32_t num_splits) {
+    int st = check_layout(layout);
+    if (st) return st;
+    if (num_codes < 0) return fail(VQ_ERR_INVALID_ARG, "num_codes %d < 0", num_codes);
+    if (num_codes > layout->capacity)
+        return fail(VQ_ERR_CAPACITY, "num_codes %d exceeds capacity %d", num_codes,
+                    layout->capacity);
+    if (win_cap < 1) return fail(VQ_ERR_INVALID_ARG, "window capacity %d < 1", win_cap);
+    if (win_len < 0) return fail(VQ_ERR_INVALID_ARG, "win_len %d < 0", win_len);
+    if (win_len >= win_cap)
+        return fail(VQ_ERR_CAPACITY,
+                    "window full: win_len %d, capacity %d (flush it with vq_flush_window)",
+                    win_len, win_cap);
+    if (kv_dtype != VQ_F16 && kv_dtype != VQ_F32)
+        return fail(VQ_ERR_INVALID_ARG, "kv_dtype %d is not VQ_F16 or VQ_F32", kv_dtype);
+    VQ_REQUIRE_PTR(k_new);
+    VQ_REQUIRE_PTR(v_new);
+    VQ_REQUIRE_PTR(win_k);
+    VQ_REQUIRE_PTR(win_v);
+    // the code-side arguments, for at least one token (none is read when num_codes is 0)
+    return check_attention_args(layout, q, q_dtype, lambda, cb_k, cb_v, codes_k, codes_v, batch,
+                                num_q_heads, num_codes > 0 ? num_codes : 1, num_splits);
+}
+
+vqkv::AppendArgs window_args(const void* k_new, const void* v_new, int kv_dtype, int num_codes,
+                             uint16_t* win_k, uint16_t* win_v, int win_len, int win_cap) {
+    vqkv::AppendArgs app;
+    app.k_new = k_new;
+    app.v_new = v_new;
+    app.kv_f32 = kv_dtype == VQ_F32;
+    app.append_pos = num_codes;   // marks the extra workgroup; no code is written
+    app.win_k = win_k;
+    app.win_v = win_v;
+    app.win_len = win_len;
+    app.win_cap = win_cap;
+    return app;
+}
+
 }  // namespace
 }  // extern "C++"
 
@@ -409,6 +460,69 @@ int vq_decode_step(const vq_layout* layout, const void* q, int q_dtype, const vo
     if (st) return st;
     return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, nparts, part, out, s),
                       "decode_step merge launch");
+}
+
+int32_t vq_decode_step_window_num_partials(const vq_layout* layout, int32_t batch,
+                                           int32_t num_q_heads, int32_t num_codes,
+                                           int32_t requested) {
+    (void)num_q_heads;
+    if (layout == nullptr || batch < 1 || num_codes < 0 || layout->num_kv_heads < 1 ||
+        requested < 0)
+        return 0;
+    return plan_window_step(batch * layout->num_kv_heads, num_codes, requested).num_splits + 1;
+}
+
+size_t vq_decode_step_window_workspace_bytes(const vq_layout* layout, int32_t batch,
+                                             int32_t num_q_heads, int32_t num_codes,
+                                             int32_t requested) {
+    const int32_t n =
+        vq_decode_step_window_num_partials(layout, batch, num_q_heads, num_codes, requested);
+    if (n < 1 || num_q_heads < 1) return 0;
+    return partials_bytes(batch, num_q_heads, n);
+}
+
+int vq_decode_step_window(const vq_layout* layout, const void* q, int q_dtype, const void* k_new,
+                          const void* v_new, int kv_dtype, const float* lambda,
+                          const uint16_t* cb_k, const uint16_t* cb_v, const uint8_t* codes_k,
+                          const uint8_t* codes_v, uint16_t* win_k, uint16_t* win_v,
+                          int32_t win_cap, int32_t batch, int32_t num_q_heads, int32_t num_codes,
+                          int32_t win_len, int32_t num_splits, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    int st = check_window_step_args(layout, q, q_dtype, k_new, v_new, kv_dtype, lambda, cb_k, cb_v,
+                                    codes_k, codes_v, win_k, win_v, win_cap, batch, num_q_heads,
+                                    num_codes, win_len, num_splits);
+    if (st) return st;
+    VQ_REQUIRE_PTR(out);
+    const SplitPlan p = plan_window_step(batch * layout->num_kv_heads, num_codes, num_splits);
+    const int nparts = p.num_splits + 1;
+    const size_t need = partials_bytes(batch, num_q_heads, nparts);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    const vqkv::Partials part = carve_partials(workspace, batch, num_q_heads, nparts);
+    const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
+                                num_codes, p.num_splits, p.tokens_per_split};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(vqkv::launch_vq_attention(
+                        shape, layout->k_code_bits, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                        codes_k, codes_v, part,
+                        window_args(k_new, v_new, kv_dtype, num_codes, win_k, win_v, win_len,
+                                    win_cap),
+                        s),
+                    "decode_step_window launch");
+    if (st) return st;
+    return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, nparts, part, out, s),
+                      "decode_step_window merge launch");
+}
+
+int vq_flush_window(const vq_layout* layout, const uint16_t* win_k, const uint16_t* win_v,
+                    const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                    uint8_t* codes_k, uint8_t* codes_v, int32_t win_cap, int32_t batch,
+                    int32_t num_codes, void* stream) {
+    if (win_cap < 1) return fail(VQ_ERR_INVALID_ARG, "window capacity %d < 1", win_cap);
+    return vq_encode_append(layout, win_k, win_v, VQ_F16, lambda, cb_k, cb_v, codes_k, codes_v,
+                            batch, num_codes, win_cap, stream);
 }
 
 int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
