@@ -264,6 +264,38 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     call_us = ev0.elapsed_time(ev1) * 1e3 / steps
 
+    # 4. decode steps with a full-precision residual window of 128 tokens at
+    #    the same total length: n - 128 coded tokens, window slots 0..127
+    #    (slot 127 takes the new token), and the flush that encodes a full
+    #    window into codes
+    win = 128
+    win_k = torch.empty((bsz, hkv, win, 128), dtype=torch.float16, device=dev)
+    win_v = torch.empty_like(win_k)
+    win_k.normal_()
+    win_v.normal_()
+    steps_win = [vq.prepare_decode_step_window(q, k_new2, v_new2, lam, cb_k, cb_v, ck, cv, win_k,
+                                               win_v, n - win, win - 1, args.splits)
+                 for ck, cv in caches]
+    for i in range(3):
+        steps_win[i % copies](stream)
+    torch.cuda.synchronize()
+    head_start()
+    ev0.record()
+    for i in range(steps):
+        steps_win[i % copies](stream)
+    ev1.record()
+    torch.cuda.synchronize()
+    win_step_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    flushes = max(10, steps // 5)
+    head_start()
+    ev0.record()
+    for i in range(flushes):
+        ck, cv = caches[i % copies]
+        vq.flush_window(win_k, win_v, lam, cb_k, cb_v, ck, cv, n - win)
+    ev1.record()
+    torch.cuda.synchronize()
+    flush_us = ev0.elapsed_time(ev1) * 1e3 / flushes
+
     attn_us = float(split_us)
     assert torch.isfinite(out).all().item()
 
@@ -302,6 +334,10 @@ def main(argv=None) -> int:
                      "timing": "one HIP event pair around the back-to-back split passes, per launch",
                      "traffic_record": None if traffic is None else traffic["source"]},
         "step_hbm_gbps": ab["total"] / (ms_step * 1e-3) / 1e9,
+        "decode_step_window": {"avg_us": win_step_us, "coded_tokens": n - win,
+                               "window_tokens": win,
+                               "tokens_per_s": tokens / (win_step_us * 1e-6),
+                               "flush_us": flush_us, "flush_tokens_per_stream": win},
         "decode_attention": {"avg_us": call_us,
                              "gbps": ab_attn["total"] / (call_us * 1e-6) / 1e9,
                              "kernels": "vq_attention_mfma_kernel + merge_partials_kernel"},
