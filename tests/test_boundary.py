@@ -312,3 +312,71 @@ def test_flush_window_validation(lib):
     assert f(ctypes.byref(layout), A, A, A, A, A, A, A, 128, 1, 900, None) == CAPACITY
     assert f(ctypes.byref(layout), None, A, A, A, A, A, A, 128, 1, 0, None) == INVALID
     assert f(ctypes.byref(layout), A, A, A, A, A, A, A, 128, 1, -1, None) == INVALID
+
+
+# --- offline calibration -----------------------------------------------------------
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((A, 2, 8, 100, A), INVALID, "kv_dtype"),
+    ((A, 0, 0, 100, A), INVALID, "num_kv_heads"),
+    ((A, 0, 65536, 100, A), INVALID, "num_kv_heads"),
+    ((A, 1, 8, 0, A), INVALID, "num_tokens"),
+    ((None, 0, 8, 100, A), INVALID, "keys is NULL"),
+    ((MIS, 0, 8, 100, A), INVALID, "keys"),
+    ((A, 0, 8, 100, None), INVALID, "lambda"),
+    ((A, 0, 8, 100, MIS), INVALID, "lambda"),
+])
+def test_calibrate_lambda_validation(lib, args, status, needle):
+    assert lib.vq_calibrate_lambda(*args, None) == status, vq._last_error()
+    assert needle in vq._last_error()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((A, 0, None, 8, 100, A), INVALID, "lambda"),
+    ((A, 0, A, 8, 100, MIS), INVALID, "keys_tilde"),
+    ((A, 0, A, 8, -5, A), INVALID, "num_tokens"),
+    ((A, 5, A, 8, 100, A), INVALID, "kv_dtype"),
+])
+def test_transform_keys_validation(lib, args, status, needle):
+    assert lib.vq_transform_keys(*args, None) == status, vq._last_error()
+    assert needle in vq._last_error()
+
+
+def kmeans_call(lib, samples=A, sets=2, n=1000, bits=8, init=A, iters=3, cent=A, cb=A, asg=A,
+                ws=A, ws_bytes=1 << 30):
+    return lib.vq_kmeans(samples, sets, n, bits, init, iters, cent, cb, asg, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(sets=0), INVALID, "num_sets"),
+    (dict(sets=65536), INVALID, "num_sets"),
+    (dict(n=0), INVALID, "num_samples"),
+    (dict(n=(1 << 28) + 1), INVALID, "num_samples"),
+    (dict(bits=10), UNSUPPORTED, "code_bits"),
+    (dict(iters=-1), INVALID, "iters"),
+    (dict(iters=10001), INVALID, "iters"),
+    (dict(samples=None), INVALID, "samples"),
+    (dict(init=MIS), INVALID, "init"),
+    (dict(cent=None), INVALID, "centroids"),
+    (dict(cb=MIS), INVALID, "codebook"),
+    (dict(asg=MIS), INVALID, "assign"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(ws_bytes=4096), WORKSPACE, "workspace"),
+    (dict(ws=MIS), INVALID, "workspace"),
+])
+def test_kmeans_validation(lib, kw, status, needle):
+    assert kmeans_call(lib, **kw) == status, vq._last_error()
+    assert needle in vq._last_error()
+
+
+def test_kmeans_workspace_layout(lib):
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    for sets, n, bits in ((1, 1, 8), (8, 4194304, 8), (3, 8193, 12)):
+        ent, chunks = 1 << bits, -(-n // 8192)
+        want = (a256(sets * n * 4) + a256(sets * chunks * ent * 4) + 2 * a256(sets * ent * 4) +
+                a256(sets * n * 16))
+        assert lib.vq_kmeans_workspace_bytes(sets, n, bits) == want
+    for bad in ((0, 10, 8), (1, 0, 8), (1, 10, 9), (1, (1 << 28) + 1, 8)):
+        assert lib.vq_kmeans_workspace_bytes(*bad) == 0

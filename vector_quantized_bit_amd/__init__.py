@@ -25,7 +25,8 @@ __all__ = [
     "prepare_merge_partials", "decode_step", "prepare_decode_step", "decode_step_partials",
     "prepare_decode_step_partials", "decode_step_num_partials", "decode_step_workspace_bytes",
     "decode_step_window", "prepare_decode_step_window", "decode_step_window_num_partials",
-    "decode_step_window_workspace_bytes", "flush_window",
+    "decode_step_window_workspace_bytes", "flush_window", "calibrate_lambda", "transform_keys",
+    "kmeans_workspace_bytes", "kmeans",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqkv.so")
@@ -89,6 +90,11 @@ def library() -> ctypes.CDLL:
                                            _vp, _vp, _size, _vp]),
         "vq_flush_window": (_c_int, [lp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                      _vp]),
+        "vq_calibrate_lambda": (_c_int, [_vp, _c_int, _i32, _i32, _vp, _vp]),
+        "vq_transform_keys": (_c_int, [_vp, _c_int, _vp, _i32, _i32, _vp, _vp]),
+        "vq_kmeans_workspace_bytes": (_size, [_i32, _i32, _i32]),
+        "vq_kmeans": (_c_int, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _size,
+                               _vp]),
         "vq_fp16_attention_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32]),
         "vq_fp16_decode_attention": (_c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _vp, _vp, _size, _vp]),
@@ -579,3 +585,80 @@ def fp16_decode_attention(q, k, v, context_len: int, num_splits: int = 0, out=No
                                               _ptr(workspace), workspace.numel(), _stream(q)),
            "vq_fp16_decode_attention")
     return out
+
+
+# --- offline calibration --------------------------------------------------------
+
+def _check_calib_keys(keys):
+    _need(keys.is_cuda and keys.is_contiguous() and keys.dim() == 3 and keys.shape[2] == 128,
+          "keys must be contiguous [Hkv][T][128]")
+
+
+def calibrate_lambda(keys: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """lambda = sqrt(max_t |K|) per (KV head, channel) from calibration keys
+    [Hkv][T][128] (float16/float32) -> float32 [Hkv][128]."""
+    _check_calib_keys(keys)
+    if out is None:
+        out = torch.empty((keys.shape[0], 128), dtype=torch.float32, device=keys.device)
+    _need(out.is_contiguous() and out.dtype == torch.float32 and
+          tuple(out.shape) == (keys.shape[0], 128), "out must be contiguous float32 [Hkv][128]")
+    _check(library().vq_calibrate_lambda(_ptr(keys), _dtype_code(keys), keys.shape[0],
+                                         keys.shape[1], _ptr(out), _stream(keys)),
+           "vq_calibrate_lambda")
+    return out
+
+
+def transform_keys(keys: torch.Tensor, lam: torch.Tensor,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """K~ = K diag(lambda)^-1 H_128 of calibration keys [Hkv][T][128] -> float32
+    [Hkv][T][128] (view it as [Hkv][T*32][4] for K-Means)."""
+    _check_calib_keys(keys)
+    _need(lam.is_cuda and lam.is_contiguous() and lam.dtype == torch.float32 and
+          tuple(lam.shape) == (keys.shape[0], 128), "lambda must be contiguous float32 [Hkv][128]")
+    if out is None:
+        out = torch.empty(keys.shape, dtype=torch.float32, device=keys.device)
+    _need(out.is_contiguous() and out.dtype == torch.float32 and out.shape == keys.shape,
+          "out must be contiguous float32 like keys")
+    _check(library().vq_transform_keys(_ptr(keys), _dtype_code(keys), _ptr(lam), keys.shape[0],
+                                       keys.shape[1], _ptr(out), _stream(keys)),
+           "vq_transform_keys")
+    return out
+
+
+def kmeans_workspace_bytes(num_sets: int, num_samples: int, code_bits: int) -> int:
+    return int(library().vq_kmeans_workspace_bytes(num_sets, num_samples, code_bits))
+
+
+def kmeans(samples: torch.Tensor, init: torch.Tensor, iters: int, *, codebook: bool = True,
+           assign: bool = False, centroids: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None):
+    """Lloyd K-Means of fp32 samples [S][n][4] from fp64 init [S][2^bits][4].
+
+    Returns (centroids float64 [S][2^bits][4], codebook float16 or None,
+    assign int32 [S][n] or None).  ``centroids`` may be ``init`` (updated in
+    place); ``workspace`` is an optional reusable uint8 device tensor of at
+    least ``kmeans_workspace_bytes(...)`` bytes."""
+    _need(samples.is_cuda and samples.is_contiguous() and samples.dtype == torch.float32 and
+          samples.dim() == 3 and samples.shape[2] == 4, "samples must be contiguous float32 [S][n][4]")
+    _need(init.is_cuda and init.is_contiguous() and init.dtype == torch.float64 and
+          init.dim() == 3 and init.shape[0] == samples.shape[0] and init.shape[2] == 4,
+          "init must be contiguous float64 [S][entries][4]")
+    entries = int(init.shape[1])
+    bits = entries.bit_length() - 1
+    _need(entries == 1 << bits, "the number of centroids must be a power of two")
+    sets, n = int(samples.shape[0]), int(samples.shape[1])
+    dev = samples.device
+    if centroids is None:
+        centroids = torch.empty_like(init)
+    _need(centroids.is_contiguous() and centroids.dtype == torch.float64 and
+          centroids.shape == init.shape, "centroids must be contiguous float64 like init")
+    cb = torch.empty(init.shape, dtype=torch.float16, device=dev) if codebook else None
+    asg = torch.empty((sets, n), dtype=torch.int32, device=dev) if assign else None
+    need = kmeans_workspace_bytes(sets, n, bits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(library().vq_kmeans(_ptr(samples), sets, n, bits, _ptr(init), int(iters),
+                               _ptr(centroids), _ptr(cb), _ptr(asg), _ptr(workspace),
+                               workspace.numel(), _stream(samples)),
+           "vq_kmeans")
+    return centroids, cb, asg

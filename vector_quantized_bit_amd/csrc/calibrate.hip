@@ -1,0 +1,647 @@
+// Offline calibration on the GPU: smoothing factors, transformed calibration
+// keys and Lloyd K-Means codebooks.
+//
+// VecInfer page, Method details: the smoothing factors lambda_i =
+// sqrt(max_t |K[t, i]|) per channel are precomputed offline from calibration
+// keys, and the codebooks are pretrained offline by K-Means, on the
+// transformed keys K~ = K diag(lambda)^-1 H_D for C_k and on the values as they
+// are for C_v; Experimental setup: at most 30 K-Means iterations.
+//
+// K-Means is Lloyd's algorithm: every sample goes to its nearest centroid
+// (fp64 squared distance with every difference, product and sum rounded
+// separately, channels in order, exact ties to the lowest index), then every
+// centroid with samples moves to their mean, the samples of a cluster summed
+// in sample order from zero and divided once by their count; a centroid
+// without samples stays where it is.  Each iteration reproduces that
+// definition bit for bit, whatever the launch shape:
+//  - assignment: the encoder's certified filter (fp32 scores on the matrix
+//    cores, an error bound, fp64 distances for the few centroids under it),
+//    here with fp64 centroids whose fp32 roundings feed the matrix cores;
+//  - update: a stable counting sort of the samples by cluster, then one
+//    sequential fp64 chain per (cluster, channel).
+#include "launchers.hpp"
+
+namespace vqkv {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// smoothing factors
+// ---------------------------------------------------------------------------
+
+constexpr int kLamThreads = 256;
+constexpr int kLamRows = 256;   // token rows per workgroup
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v,
+                                                       int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// Channel maxima of |K| over rows [r0, r0 + kLamRows) of KV head blockIdx.y,
+// merged into lam_bits[g][c] as fp32 bit patterns (for non-negative floats the
+// patterns order like the values, NaN above infinity).
+template <bool F32>
+__global__ __launch_bounds__(kLamThreads) void channel_absmax_kernel(
+    const void* __restrict__ keys, int num_tokens, uint32_t* __restrict__ lam_bits) {
+    constexpr int kPerVec = F32 ? 4 : 8;                  // channels per 16-byte load
+    constexpr int kVecPerRow = kHeadDim / kPerVec;        // 32 or 16
+    constexpr int kRowStep = kLamThreads / kVecPerRow;    // 8 or 16 rows per sweep
+    __shared__ uint32_t red[kRowStep][kHeadDim];
+    const int g = blockIdx.y, tid = threadIdx.x;
+    const int cv = tid % kVecPerRow, rsub = tid / kVecPerRow;
+    const int r0 = blockIdx.x * kLamRows, r1 = min(num_tokens, r0 + kLamRows);
+    const uint4* src =
+        reinterpret_cast<const uint4*>(keys) + static_cast<size_t>(g) * num_tokens * kVecPerRow;
+    // fp16: maxima of the 15-bit magnitude patterns; fp32: of the 31-bit ones
+    uint32_t mx[kPerVec];
+#pragma unroll
+    for (int j = 0; j < kPerVec; ++j) mx[j] = 0;
+#pragma unroll 4
+    for (int r = r0 + rsub; r < r1; r += kRowStep) {
+        const uint4 v = src[static_cast<size_t>(r) * kVecPerRow + cv];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (F32) {
+                mx[q] = max(mx[q], w[q] & 0x7fffffffu);
+            } else {
+                mx[2 * q] = max(mx[2 * q], w[q] & 0x7fffu);
+                mx[2 * q + 1] = max(mx[2 * q + 1], (w[q] >> 16) & 0x7fffu);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kPerVec; ++j) {
+        uint32_t bits = mx[j];
+        if constexpr (!F32)
+            bits = __builtin_bit_cast(uint32_t, half_bits_to_float(static_cast<uint16_t>(bits)));
+        red[rsub][cv * kPerVec + j] = bits;
+    }
+    __syncthreads();
+    if (tid < kHeadDim) {
+        uint32_t m = red[0][tid];
+#pragma unroll
+        for (int s = 1; s < kRowStep; ++s) m = max(m, red[s][tid]);
+        atomicMax(&lam_bits[g * kHeadDim + tid], m);
+    }
+}
+
+// lambda = sqrt(max |K|): the square root in fp64, rounded once to fp32 (the
+// same value as a correctly rounded fp32 square root).
+__global__ __launch_bounds__(256) void sqrt_lambda_kernel(uint32_t* __restrict__ lam_bits,
+                                                          int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const double m = static_cast<double>(__builtin_bit_cast(float, lam_bits[i]));
+        lam_bits[i] = __builtin_bit_cast(uint32_t, static_cast<float>(__dsqrt_rn(m)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// transformed calibration keys
+// ---------------------------------------------------------------------------
+
+// K~ = K diag(lambda)^-1 H_128 for one token row per wave: k / lambda in fp64,
+// the +-1 Walsh–Hadamard transform, 1/sqrt(128), rounded once to fp32 (the
+// arithmetic of the encoder's key transform).
+__global__ __launch_bounds__(256) void transform_keys_kernel(const void* __restrict__ keys,
+                                                             int kv_f32,
+                                                             const float* __restrict__ lambda,
+                                                             int num_tokens,
+                                                             float* __restrict__ out) {
+    const int g = blockIdx.y, lane = threadIdx.x & (kWave - 1);
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= num_tokens) return;   // the whole wave: the transform needs every lane
+    const size_t row = static_cast<size_t>(g) * num_tokens + t;
+    const float* lam = lambda + g * kHeadDim;
+    double k0, k1;
+    if (kv_f32) {
+        const float2 v = reinterpret_cast<const float2*>(keys)[row * (kHeadDim / 2) + lane];
+        k0 = v.x;
+        k1 = v.y;
+    } else {
+        const uint32_t v = reinterpret_cast<const uint32_t*>(keys)[row * (kHeadDim / 2) + lane];
+        k0 = half_bits_to_float(static_cast<uint16_t>(v & 0xffffu));
+        k1 = half_bits_to_float(static_cast<uint16_t>(v >> 16));
+    }
+    const float2 l = reinterpret_cast<const float2*>(lam)[lane];
+    double x0 = k0 / static_cast<double>(l.x);
+    double x1 = k1 / static_cast<double>(l.y);
+    fwht128(x0, x1);
+    reinterpret_cast<float2*>(out)[row * (kHeadDim / 2) + lane] =
+        make_float2(static_cast<float>(x0 * kInvSqrtD64), static_cast<float>(x1 * kInvSqrtD64));
+}
+
+// ---------------------------------------------------------------------------
+// K-Means
+// ---------------------------------------------------------------------------
+
+constexpr int kKmThreads = 512;
+constexpr int kKmWaves = kKmThreads / kWave;   // 8
+constexpr int kKmChunk = 8192;                 // samples per assignment workgroup = sort chunk
+constexpr int kSortWaves = 4;                  // chunks per scatter workgroup (one per wave)
+
+template <int NENT>
+constexpr int kKmStride = NENT + 16;           // -2c rows on different banks
+
+// fp64 centroids staged in LDS when they fit beside the fp32 tables (8 KiB);
+// the 4096-entry case reads its few candidates from global memory (L2).
+template <int NENT>
+constexpr bool kKmLdsC64 = NENT <= 256;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// fp64 squared distance of fp32 sample x to fp64 centroid c, rounded as the
+// definition rounds it (difference, square and running sum separately, in
+// channel order, from zero).
+__device__ __forceinline__ double sqdist4_c64(const float4 x, const double c[4]) {
+    const double e0 = __dadd_rn(static_cast<double>(x.x), -c[0]);
+    const double e1 = __dadd_rn(static_cast<double>(x.y), -c[1]);
+    const double e2 = __dadd_rn(static_cast<double>(x.z), -c[2]);
+    const double e3 = __dadd_rn(static_cast<double>(x.w), -c[3]);
+    double d = __dmul_rn(e0, e0);
+    d = __dadd_rn(d, __dmul_rn(e1, e1));
+    d = __dadd_rn(d, __dmul_rn(e2, e2));
+    d = __dadd_rn(d, __dmul_rn(e3, e3));
+    return d;
+}
+
+// Nearest centroid of every sample of one sort chunk (kKmChunk samples of set
+// blockIdx.y): assign[set][i], and, when hist is given, the chunk's cluster
+// histogram hist[set][chunk][NENT].
+//
+// The filter: with u = 2^-24, the matrix-core score s(c) = fl(||c||^2) -
+// 2 x.fl32(c) (fp32 products and sums) is within about 12 u (||x||^2 +
+// ||c||^2) of ||x - c||^2 - ||x||^2 (fp32 rounding of c and of ||c||^2, four
+// accumulations), and the fp64 distance within 2^-50 of the same scale.  The
+// bound used, E(c) = 2^-16 (||x||^2 + ||c||^2) plus 1e-30 for underflow, has a
+// margin of about 20x: every centroid whose s(c) - E(c) is not above min over
+// c' of s(c') + E(c') gets its fp64 distance, and the true nearest one is
+// among them.  Samples and centroids must be finite with magnitudes below
+// about 2^60 so that no fp32 score overflows.
+template <int NENT>
+__global__ __launch_bounds__(kKmThreads) void kmeans_assign_kernel(
+    const float* __restrict__ samples, int num_samples, const double* __restrict__ centroids,
+    int32_t* __restrict__ assign, int32_t* __restrict__ hist) {
+    __shared__ float m2[4 * kKmStride<NENT>];   // -2 fl32(c) by channel
+    __shared__ float cc[NENT];                  // fl32(||c||^2)
+    __shared__ double c64s[kKmLdsC64<NENT> ? NENT * 4 : 1];
+    __shared__ int32_t cnt[NENT];
+    constexpr int kUnroll = 8;
+    constexpr float kUp = 1.0f + 0x1p-16f, kDown = 1.0f - 0x1p-16f;
+    static_assert(NENT % (16 * kUnroll) == 0, "whole unrolled groups");
+
+    const int set = blockIdx.y, chunk = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const double* cset = centroids + static_cast<size_t>(set) * NENT * 4;
+    const float4* xset = reinterpret_cast<const float4*>(samples) +
+                         static_cast<size_t>(set) * num_samples;
+    for (int i = tid; i < NENT; i += kKmThreads) {
+        const double2 lo = reinterpret_cast<const double2*>(cset)[2 * i];
+        const double2 hi = reinterpret_cast<const double2*>(cset)[2 * i + 1];
+        const double c[4] = {lo.x, lo.y, hi.x, hi.y};
+        double nn = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m2[j * kKmStride<NENT> + i] = -2.f * static_cast<float>(c[j]);
+            nn += c[j] * c[j];
+            if constexpr (kKmLdsC64<NENT>) c64s[i * 4 + j] = c[j];
+        }
+        cc[i] = static_cast<float>(nn);
+        cnt[i] = 0;
+    }
+    __syncthreads();
+
+    const int s0 = chunk * kKmChunk, s1 = min(num_samples, s0 + kKmChunk);
+    const float* bcol = m2 + (lane >> 4) * kKmStride<NENT> + (lane & 15);
+    const float* ccol = cc + (lane & 15);
+    int32_t* aset = assign + static_cast<size_t>(set) * num_samples;
+    for (int base = s0 + wave * 16; base < s1; base += kKmWaves * 16) {
+        // A operand: sample base + lane % 16, channel lane / 16
+        const int ra = base + (lane & 15);
+        const float a = ra < s1 ? samples[(static_cast<size_t>(set) * num_samples + ra) * 4 +
+                                          (lane >> 4)]
+                                : 0.f;
+        const int r0 = base + 4 * (lane >> 4);   // this lane's D rows r0 .. r0 + 3
+        float4 xr[4];
+        float ex[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xr[i] = r0 + i < s1 ? xset[r0 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float xx = (xr[i].x * xr[i].x + xr[i].y * xr[i].y) +
+                             (xr[i].z * xr[i].z + xr[i].w * xr[i].w);
+            ex[i] = 2.f * (0x1p-16f * xx) + 1e-30f;   // the ||x||^2 parts of both bounds
+        }
+
+        // pass 1: min over c of s(c) + E(c), up to the ||x||^2 part
+        float smin[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
+#pragma nounroll
+        for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
+            f32x4_t d[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float c0 = ccol[(blk + u) * 16] * kUp;
+                d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bcol[(blk + u) * 16],
+                                                            f32x4_t{c0, c0, c0, c0}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) smin[i] = fminf(smin[i], d[u][i]);
+        }
+        float thr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) thr[i] = row_min16(smin[i]) + ex[i];
+
+        // pass 2: the candidates get fp64 distances; groups of 8 x 16
+        // centroids without one are skipped
+        double bd[4];
+        uint32_t bi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bd[i] = INFINITY;
+            bi[i] = 0xffffffffu;
+        }
+#pragma nounroll
+        for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
+            f32x4_t d[kUnroll];
+            bool any = false;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float c0 = ccol[(blk + u) * 16] * kDown;
+                d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bcol[(blk + u) * 16],
+                                                            f32x4_t{c0, c0, c0, c0}, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) any |= d[u][i] <= thr[i];
+            }
+            if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (d[u][i] <= thr[i]) {
+                        const int nc = (blk + u) * 16 + (lane & 15);
+                        double c[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            if constexpr (kKmLdsC64<NENT>)
+                                c[j] = c64s[nc * 4 + j];
+                            else
+                                c[j] = cset[nc * 4 + j];
+                        }
+                        const double dd = sqdist4_c64(xr[i], c);
+                        if (nearer(dd, static_cast<uint32_t>(nc), bd[i], bi[i])) {
+                            bd[i] = dd;
+                            bi[i] = static_cast<uint32_t>(nc);
+                        }
+                    }
+                }
+            }
+        }
+        // lexicographic minimum over the 16 lanes that share the rows
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            double d0 = bd[i];
+            uint32_t i0 = bi[i];
+#define VQKV_TAKE(M)                                                                       \
+    {                                                                                      \
+        const double d2 = lane_partner<M>(d0, lane);                                       \
+        const uint32_t i2 = lane_partner<M>(i0, lane);                                     \
+        if (nearer(d2, i2, d0, i0)) {                                                      \
+            d0 = d2;                                                                       \
+            i0 = i2;                                                                       \
+        }                                                                                  \
+    }
+            VQKV_TAKE(1)
+            VQKV_TAKE(2)
+            VQKV_TAKE(4)
+            VQKV_TAKE(8)
+#undef VQKV_TAKE
+            const int r = r0 + i;
+            if ((lane & 15) == 0 && r < s1) {
+                aset[r] = static_cast<int32_t>(i0);
+                if (hist != nullptr) atomicAdd(&cnt[i0 & (NENT - 1)], 1);
+            }
+        }
+    }
+    if (hist != nullptr) {
+        __syncthreads();
+        int32_t* h = hist + (static_cast<size_t>(set) * gridDim.x + chunk) * NENT;
+        for (int i = tid; i < NENT; i += kKmThreads) h[i] = cnt[i];
+    }
+}
+
+// Per (set, cluster): the chunk histograms become exclusive prefix sums over
+// the chunks (in place), and counts[set][c] the cluster sizes.
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(int32_t* __restrict__ hist,
+                                                            int nchunks, int nent,
+                                                            int32_t* __restrict__ counts) {
+    const int set = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= nent) return;
+    int32_t* h = hist + static_cast<size_t>(set) * nchunks * nent + c;
+    int32_t run = 0;
+    int k = 0;
+    for (; k + 8 <= nchunks; k += 8) {   // 8 independent loads in flight
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = h[static_cast<size_t>(k + u) * nent];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            h[static_cast<size_t>(k + u) * nent] = run;
+            run += v[u];
+        }
+    }
+    for (; k < nchunks; ++k) {
+        const int32_t v = h[static_cast<size_t>(k) * nent];
+        h[static_cast<size_t>(k) * nent] = run;
+        run += v;
+    }
+    counts[static_cast<size_t>(set) * nent + c] = run;
+}
+
+// base[set][c] = exclusive prefix sum of counts[set][.] over the clusters:
+// where cluster c starts in the sorted samples.  One 1024-thread workgroup
+// per set; nent <= 4096.
+__global__ __launch_bounds__(1024) void cluster_base_kernel(const int32_t* __restrict__ counts,
+                                                            int nent,
+                                                            int32_t* __restrict__ base) {
+    __shared__ int32_t wsum[1024 / kWave];
+    const int set = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int per = (nent + 1023) / 1024;   // 1 .. 4 consecutive clusters per thread
+    const int32_t* cs = counts + static_cast<size_t>(set) * nent;
+    int32_t* bs = base + static_cast<size_t>(set) * nent;
+    int32_t v[4] = {0, 0, 0, 0};
+    int32_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = tid * per + j;
+        if (j < per && c < nent) v[j] = cs[c];
+        tot += v[j];
+    }
+    int32_t incl = tot;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t y = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int32_t run = incl - tot;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = tid * per + j;
+        if (j < per && c < nent) bs[c] = run;
+        run += v[j];
+    }
+}
+
+// Stable counting sort of the samples by cluster: sample i of chunk k goes to
+// base[c] + (samples of c in chunks before k) + (samples of c before i in
+// chunk k).  One wave per chunk walks it in order, 64 samples a step; lanes
+// with the same cluster are found with one ballot per code bit.  No barrier:
+// every wave works alone on its own chunk and its own LDS counters.
+template <int BITS>
+__global__ __launch_bounds__(kSortWaves * kWave) void kmeans_scatter_kernel(
+    const float* __restrict__ samples, int num_samples, const int32_t* __restrict__ assign,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ base, int nchunks,
+    float* __restrict__ sorted) {
+    constexpr int NENT = 1 << BITS;
+    __shared__ int32_t cnt[kSortWaves][NENT];
+    const int set = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int chunk = blockIdx.x * kSortWaves + wave;
+    if (chunk >= nchunks) return;
+    const int32_t* off = offs + (static_cast<size_t>(set) * nchunks + chunk) * NENT;
+    const int32_t* bs = base + static_cast<size_t>(set) * NENT;
+    int32_t* my = cnt[wave];
+    for (int c = lane; c < NENT; c += kWave) my[c] = bs[c] + off[c];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const int s0 = chunk * kKmChunk, s1 = min(num_samples, s0 + kKmChunk);
+    const int32_t* aset = assign + static_cast<size_t>(set) * num_samples;
+    const float4* xs = reinterpret_cast<const float4*>(samples) +
+                       static_cast<size_t>(set) * num_samples;
+    float4* out = reinterpret_cast<float4*>(sorted) + static_cast<size_t>(set) * num_samples;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int i0 = s0; i0 < s1; i0 += kWave) {
+        const int i = i0 + lane;
+        const bool valid = i < s1;
+        const uint32_t c = valid ? static_cast<uint32_t>(aset[i]) & (NENT - 1) : 0u;
+        const float4 x = valid ? xs[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        uint64_t same = __builtin_amdgcn_ballot_w64(valid);
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) {
+            const bool bit = (c >> b) & 1u;
+            const uint64_t set_bits = __builtin_amdgcn_ballot_w64(bit);
+            same &= bit ? set_bits : ~set_bits;
+        }
+        const int rank = __popcll(same & below);
+        const int total = __popcll(same);
+        int32_t start = 0;
+        if (valid) start = my[c];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (valid) my[c] = start + total;   // every lane of the group writes the same value
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int32_t pos = start + rank;
+        if (valid && static_cast<uint32_t>(pos) < static_cast<uint32_t>(num_samples))
+            out[pos] = x;
+    }
+}
+
+// New centroids: one thread per (set, cluster, channel) sums the cluster's
+// sorted samples in order in fp64 from zero and divides once by the count;
+// a cluster without samples keeps its centroid.
+__global__ __launch_bounds__(256) void kmeans_update_kernel(const float* __restrict__ sorted,
+                                                            int num_samples,
+                                                            const int32_t* __restrict__ base,
+                                                            const int32_t* __restrict__ counts,
+                                                            int nent,
+                                                            double* __restrict__ centroids) {
+    const int set = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= nent * 4) return;
+    const int c = t >> 2, j = t & 3;
+    const int32_t n = counts[static_cast<size_t>(set) * nent + c];
+    if (n == 0) return;
+    const float* col =
+        sorted + (static_cast<size_t>(set) * num_samples + base[static_cast<size_t>(set) * nent + c]) * 4 + j;
+    double s = 0.0;
+    int k = 0;
+    for (; k + 16 <= n; k += 16) {   // 16 loads in flight, then 16 chained adds
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = col[static_cast<size_t>(k + u) * 4];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s = __dadd_rn(s, static_cast<double>(v[u]));
+    }
+    for (; k < n; ++k) s = __dadd_rn(s, static_cast<double>(col[static_cast<size_t>(k) * 4]));
+    centroids[(static_cast<size_t>(set) * nent + c) * 4 + j] = __ddiv_rn(s, static_cast<double>(n));
+}
+
+// fp64 -> fp16 bit pattern, rounded once to nearest even (subnormal halves,
+// overflow to infinity, NaN kept), not through fp32.
+__device__ __forceinline__ uint16_t double_to_half_bits(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t sign = static_cast<uint32_t>(u >> 48) & 0x8000u;
+    const uint64_t a = u & 0x7fffffffffffffffull;
+    if (a >= 0x7ff0000000000000ull)
+        return static_cast<uint16_t>(sign | (a > 0x7ff0000000000000ull ? 0x7e00u : 0x7c00u));
+    const int e = static_cast<int>(a >> 52) - 1023;
+    if (e >= 16) return static_cast<uint16_t>(sign | 0x7c00u);
+    const uint64_t m = (a & 0x000fffffffffffffull) | (1ull << 52);
+    // normal halves keep 11 significant bits (shift 42); subnormal ones count
+    // units of 2^-24 (shift 28 - e)
+    const int shift = e >= -14 ? 42 : 28 - e;
+    if (shift > 53) return static_cast<uint16_t>(sign);   // below half the smallest subnormal
+    const uint64_t q = m >> shift, rem = m & ((1ull << shift) - 1ull), half = 1ull << (shift - 1);
+    const uint32_t up = (rem > half || (rem == half && (q & 1ull))) ? 1u : 0u;
+    const uint32_t mag = e >= -14 ? (static_cast<uint32_t>(e + 15) << 10) +
+                                        static_cast<uint32_t>(q - 1024) + up
+                                  : static_cast<uint32_t>(q) + up;
+    return static_cast<uint16_t>(sign | mag);
+}
+
+__global__ __launch_bounds__(256) void centroids_to_half_kernel(const double* __restrict__ c,
+                                                                size_t n,
+                                                                uint16_t* __restrict__ out) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = double_to_half_bits(c[i]);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int kmeans_chunks(int num_samples) { return (num_samples + kKmChunk - 1) / kKmChunk; }
+
+struct KmWorkspace {
+    int32_t* assign;   // [sets][n]
+    int32_t* hist;     // [sets][chunks][E]
+    int32_t* counts;   // [sets][E]
+    int32_t* base;     // [sets][E]
+    float* sorted;     // [sets][n][4]
+};
+
+size_t kmeans_ws_layout(int num_sets, int num_samples, int code_bits, char* p, KmWorkspace* w) {
+    const size_t sets = static_cast<size_t>(num_sets), n = static_cast<size_t>(num_samples);
+    const size_t ent = static_cast<size_t>(1) << code_bits;
+    const size_t chunks = static_cast<size_t>(kmeans_chunks(num_samples));
+    size_t off = 0;
+    const auto take = [&](size_t bytes) {
+        char* q = p ? p + off : nullptr;
+        off += align256(bytes);
+        return q;
+    };
+    char* a = take(sets * n * 4);
+    char* h = take(sets * chunks * ent * 4);
+    char* c = take(sets * ent * 4);
+    char* b = take(sets * ent * 4);
+    char* s = take(sets * n * 16);
+    if (w) {
+        w->assign = reinterpret_cast<int32_t*>(a);
+        w->hist = reinterpret_cast<int32_t*>(h);
+        w->counts = reinterpret_cast<int32_t*>(c);
+        w->base = reinterpret_cast<int32_t*>(b);
+        w->sorted = reinterpret_cast<float*>(s);
+    }
+    return off;
+}
+
+template <int BITS>
+hipError_t kmeans_assign(const float* samples, int num_sets, int num_samples,
+                         const double* centroids, int32_t* assign, int32_t* hist,
+                         hipStream_t stream) {
+    const dim3 grid(kmeans_chunks(num_samples), num_sets);
+    hipLaunchKernelGGL(kmeans_assign_kernel<1 << BITS>, grid, dim3(kKmThreads), 0, stream,
+                       samples, num_samples, centroids, assign, hist);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t kmeans_run(const float* samples, int num_sets, int num_samples, const double* init,
+                      int iters, double* centroids, uint16_t* codebook, int32_t* assign_out,
+                      void* workspace, hipStream_t stream) {
+    constexpr int NENT = 1 << BITS;
+    KmWorkspace w;
+    kmeans_ws_layout(num_sets, num_samples, BITS, static_cast<char*>(workspace), &w);
+    const int nchunks = kmeans_chunks(num_samples);
+    const size_t cbytes = static_cast<size_t>(num_sets) * NENT * 4 * sizeof(double);
+    hipError_t e = hipSuccess;
+    if (init != centroids) {
+        e = hipMemcpyAsync(centroids, init, cbytes, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return e;
+    }
+    for (int it = 0; it < iters; ++it) {
+        if ((e = kmeans_assign<BITS>(samples, num_sets, num_samples, centroids, w.assign, w.hist,
+                                     stream)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3((NENT + 255) / 256, num_sets), dim3(256), 0,
+                           stream, w.hist, nchunks, NENT, w.counts);
+        hipLaunchKernelGGL(cluster_base_kernel, dim3(num_sets), dim3(1024), 0, stream, w.counts,
+                           NENT, w.base);
+        hipLaunchKernelGGL(kmeans_scatter_kernel<BITS>,
+                           dim3((nchunks + kSortWaves - 1) / kSortWaves, num_sets),
+                           dim3(kSortWaves * kWave), 0, stream, samples, num_samples, w.assign,
+                           w.hist, w.base, nchunks, w.sorted);
+        hipLaunchKernelGGL(kmeans_update_kernel, dim3((NENT * 4 + 255) / 256, num_sets), dim3(256),
+                           0, stream, w.sorted, num_samples, w.base, w.counts, NENT, centroids);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (assign_out != nullptr &&
+        (e = kmeans_assign<BITS>(samples, num_sets, num_samples, centroids, assign_out, nullptr,
+                                 stream)) != hipSuccess)
+        return e;
+    if (codebook != nullptr) {
+        const size_t n = static_cast<size_t>(num_sets) * NENT * 4;
+        hipLaunchKernelGGL(centroids_to_half_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                           dim3(256), 0, stream, centroids, n, codebook);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_calibrate_lambda(const void* keys, bool kv_f32, int num_kv_heads,
+                                   int num_tokens, float* lambda, hipStream_t stream) {
+    const int n = num_kv_heads * kHeadDim;
+    uint32_t* bits = reinterpret_cast<uint32_t*>(lambda);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, bits, 0u, n);
+    const dim3 grid((num_tokens + kLamRows - 1) / kLamRows, num_kv_heads);
+    if (kv_f32)
+        hipLaunchKernelGGL(channel_absmax_kernel<true>, grid, dim3(kLamThreads), 0, stream, keys,
+                           num_tokens, bits);
+    else
+        hipLaunchKernelGGL(channel_absmax_kernel<false>, grid, dim3(kLamThreads), 0, stream, keys,
+                           num_tokens, bits);
+    hipLaunchKernelGGL(sqrt_lambda_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, bits, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_transform_keys(const void* keys, bool kv_f32, const float* lambda,
+                                 int num_kv_heads, int num_tokens, float* out,
+                                 hipStream_t stream) {
+    const dim3 grid((num_tokens + 3) / 4, num_kv_heads);
+    hipLaunchKernelGGL(transform_keys_kernel, grid, dim3(256), 0, stream, keys, kv_f32 ? 1 : 0,
+                       lambda, num_tokens, out);
+    return hipGetLastError();
+}
+
+size_t kmeans_workspace_bytes(int num_sets, int num_samples, int code_bits) {
+    return kmeans_ws_layout(num_sets, num_samples, code_bits, nullptr, nullptr);
+}
+
+hipError_t launch_kmeans(const float* samples, int num_sets, int num_samples, int code_bits,
+                         const double* init, int iters, double* centroids, uint16_t* codebook,
+                         int32_t* assign, void* workspace, hipStream_t stream) {
+    if (code_bits == 8)
+        return kmeans_run<8>(samples, num_sets, num_samples, init, iters, centroids, codebook,
+                             assign, workspace, stream);
+    return kmeans_run<12>(samples, num_sets, num_samples, init, iters, centroids, codebook,
+                          assign, workspace, stream);
+}
+
+}  // namespace vqkv

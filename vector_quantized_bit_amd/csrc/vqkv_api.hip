@@ -598,4 +598,93 @@ int vq_fp16_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_
                       "fp16 attention merge launch");
 }
 
+// ---------------------------------------------------------------------------
+// offline calibration
+// ---------------------------------------------------------------------------
+
+extern "C++" {  // validation helpers: not part of the C ABI
+namespace {
+
+int check_calib_keys(const void* keys, int kv_dtype, int32_t num_kv_heads, int32_t num_tokens) {
+    if (kv_dtype != VQ_F16 && kv_dtype != VQ_F32)
+        return fail(VQ_ERR_INVALID_ARG, "kv_dtype %d is not VQ_F16 or VQ_F32", kv_dtype);
+    if (num_kv_heads < 1 || num_kv_heads > 65535)
+        return fail(VQ_ERR_INVALID_ARG, "num_kv_heads %d out of range [1, 65535]", num_kv_heads);
+    if (num_tokens < 1) return fail(VQ_ERR_INVALID_ARG, "num_tokens %d < 1", num_tokens);
+    VQ_REQUIRE_PTR(keys);
+    return VQ_OK;
+}
+
+constexpr int32_t kMaxKmeansSamples = 1 << 28;
+constexpr int32_t kMaxKmeansIters = 10000;
+
+int check_kmeans_shape(int32_t num_sets, int32_t num_samples, int32_t code_bits) {
+    if (num_sets < 1 || num_sets > 65535)
+        return fail(VQ_ERR_INVALID_ARG, "num_sets %d out of range [1, 65535]", num_sets);
+    if (num_samples < 1 || num_samples > kMaxKmeansSamples)
+        return fail(VQ_ERR_INVALID_ARG, "num_samples %d out of range [1, %d]", num_samples,
+                    kMaxKmeansSamples);
+    if (code_bits != 8 && code_bits != 12)
+        return fail(VQ_ERR_UNSUPPORTED, "code_bits %d unsupported (8 or 12)", code_bits);
+    return VQ_OK;
+}
+
+}  // namespace
+}  // extern "C++"
+
+int vq_calibrate_lambda(const void* keys, int kv_dtype, int32_t num_kv_heads, int32_t num_tokens,
+                        float* lambda, void* stream) {
+    int st = check_calib_keys(keys, kv_dtype, num_kv_heads, num_tokens);
+    if (st) return st;
+    VQ_REQUIRE_PTR(lambda);
+    return hip_status(vqkv::launch_calibrate_lambda(keys, kv_dtype == VQ_F32, num_kv_heads,
+                                                    num_tokens, lambda,
+                                                    static_cast<hipStream_t>(stream)),
+                      "calibrate_lambda launch");
+}
+
+int vq_transform_keys(const void* keys, int kv_dtype, const float* lambda, int32_t num_kv_heads,
+                      int32_t num_tokens, float* keys_tilde, void* stream) {
+    int st = check_calib_keys(keys, kv_dtype, num_kv_heads, num_tokens);
+    if (st) return st;
+    VQ_REQUIRE_PTR(lambda);
+    VQ_REQUIRE_PTR(keys_tilde);
+    return hip_status(vqkv::launch_transform_keys(keys, kv_dtype == VQ_F32, lambda, num_kv_heads,
+                                                  num_tokens, keys_tilde,
+                                                  static_cast<hipStream_t>(stream)),
+                      "transform_keys launch");
+}
+
+size_t vq_kmeans_workspace_bytes(int32_t num_sets, int32_t num_samples, int32_t code_bits) {
+    if (num_sets < 1 || num_sets > 65535 || num_samples < 1 || num_samples > kMaxKmeansSamples ||
+        (code_bits != 8 && code_bits != 12))
+        return 0;
+    return vqkv::kmeans_workspace_bytes(num_sets, num_samples, code_bits);
+}
+
+int vq_kmeans(const float* samples, int32_t num_sets, int32_t num_samples, int32_t code_bits,
+              const double* init, int32_t iters, double* centroids, uint16_t* codebook,
+              int32_t* assign, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_kmeans_shape(num_sets, num_samples, code_bits);
+    if (st) return st;
+    if (iters < 0 || iters > kMaxKmeansIters)
+        return fail(VQ_ERR_INVALID_ARG, "iters %d out of range [0, %d]", iters, kMaxKmeansIters);
+    VQ_REQUIRE_PTR(samples);
+    VQ_REQUIRE_PTR(init);
+    VQ_REQUIRE_PTR(centroids);
+    if (codebook != nullptr && !aligned16(codebook))
+        return fail(VQ_ERR_INVALID_ARG, "codebook is not 16-byte aligned");
+    if (assign != nullptr && !aligned16(assign))
+        return fail(VQ_ERR_INVALID_ARG, "assign is not 16-byte aligned");
+    const size_t need = vqkv::kmeans_workspace_bytes(num_sets, num_samples, code_bits);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    return hip_status(vqkv::launch_kmeans(samples, num_sets, num_samples, code_bits, init, iters,
+                                          centroids, codebook, assign, workspace,
+                                          static_cast<hipStream_t>(stream)),
+                      "kmeans launch");
+}
+
 }  // extern "C"

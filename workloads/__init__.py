@@ -36,6 +36,15 @@ STREAM_CODES_V = 8
 STREAM_CODEBOOK_K = 9
 STREAM_CODEBOOK_V = 10
 STREAM_LAMBDA = 11
+STREAM_CALIB_K = 12
+STREAM_CALIB_V = 13
+STREAM_CALIB_PICK = 14
+
+# Calibration set size on the VecInfer page (Experimental setup): 256
+# sequences of 512 tokens.
+CALIB_SEQS = 256
+CALIB_SEQ_LEN = 512
+CALIB_TOKENS = CALIB_SEQS * CALIB_SEQ_LEN
 
 OUTLIER_CHANNELS = 4
 OUTLIER_SCALE = 15.0
@@ -132,6 +141,28 @@ def kv_rows(config_id: int, b: int, kv_head: int, tensor: str, n: int,
 def queries(config_id: int, b: int, num_q_heads: int) -> np.ndarray:
     """q ~ N(0, 1): float64 [num_q_heads, 128] for one sequence."""
     return rng(config_id, b, 0, STREAM_Q).standard_normal((num_q_heads, HEAD_DIM))
+
+
+def calibration_rows(config_id: int, kv_head: int, tensor: str, n: int) -> np.ndarray:
+    """n calibration token rows of K or V for one KV head: float64 [n, 128].
+
+    The same distribution as ``kv_rows`` (N(0, 1) with the head's x15 outlier
+    channels) from streams of their own, standing in for the page's
+    calibration text.
+    """
+    stream = STREAM_CALIB_K if tensor == "k" else STREAM_CALIB_V
+    x = rng(config_id, 0, kv_head, stream).standard_normal((n, HEAD_DIM))
+    x[:, outlier_channels(config_id, kv_head, tensor)] *= OUTLIER_SCALE
+    return x
+
+
+def calibration_init_rows(config_id: int, kv_head: int, tensor: str, total: int,
+                          count: int) -> np.ndarray:
+    """Indices of the ``count`` samples (of ``total``) that seed Lloyd: a
+    uniform draw without replacement."""
+    t = {"k": 0, "v": 1}[tensor]
+    g = rng(config_id, t, kv_head, STREAM_CALIB_PICK)
+    return np.sort(g.choice(total, size=min(count, total), replace=False))
 
 
 def kmeans_sample_rows(config_id: int, kv_head: int, tensor: str, total: int,
