@@ -141,6 +141,102 @@ def copy_calibration(torch, dev, mib: int = 256, reps: int = 3) -> None:
     torch.cuda.synchronize()
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3
+PREFILL_TOKENS = 32768
+
+
+def synthetic_rows(torch, wl, dev, shape, tensor, seed):
+    """N(0, 1) rows [..., Hkv, T, 128] in fp16 with each head's x15 outlier
+    channels (the distribution of the test inputs), drawn on the GPU."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    x = torch.empty(shape, dtype=torch.float32, device=dev).normal_(generator=g)
+    for h in range(shape[-3]):
+        ch = torch.from_numpy(W.outlier_channels(wl.config_id, h, tensor)).to(dev)
+        x[..., h, :, ch] *= W.OUTLIER_SCALE
+    return x.to(torch.float16)
+
+
+def time_calls(torch, fn, reps, head_start, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    head_start()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def distance_flops(pairs: int) -> int:
+    """One dense pass of the nearest-centroid search as a contraction:
+    ||c||^2 - 2 x.c for every (sub-vector, centroid) pair, 4 multiply-adds."""
+    return 8 * pairs
+
+
+def prefill_encode(torch, vq, wl, dev, lam, cb_k, cb_v, head_start) -> dict:
+    """A prompt of PREFILL_TOKENS tokens per sequence encoded by one
+    vq_encode_append call (every KV head of the layer)."""
+    bsz, hkv = wl.batch, wl.num_kv_heads
+    p = min(PREFILL_TOKENS, wl.context_len)
+    kp = synthetic_rows(torch, wl, dev, (bsz, hkv, p, 128), "k", 1000 + wl.config_id)
+    vp = synthetic_rows(torch, wl, dev, (bsz, hkv, p, 128), "v", 2000 + wl.config_id)
+    ck = torch.empty((bsz, hkv, p, wl.k_row_bytes), dtype=torch.uint8, device=dev)
+    cv = torch.empty((bsz, hkv, p, wl.v_row_bytes), dtype=torch.uint8, device=dev)
+    enc = vq.prepare_encode_append(kp, vp, lam, cb_k, cb_v, ck, cv, 0)
+    us = time_calls(torch, enc, 5, head_start)
+    pairs = bsz * hkv * p * 32 * ((1 << wl.k_bits) + (1 << wl.v_bits))
+    tflops = distance_flops(pairs) / (us * 1e-6) / 1e12
+    hbm = bsz * hkv * p * (2 * 128 * 2 + wl.k_row_bytes + wl.v_row_bytes)
+    return {"workload": f"{wl.name}-prompt-{p}", "tokens": bsz * p, "avg_launch_us": us,
+            "tokens_per_s": bsz * p / (us * 1e-6), "hbm_gbps": hbm / (us * 1e-6) / 1e9,
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / MFMA_F32_PEAK_TFLOPS,
+                         "kernel": "encode_append_kernel",
+                         "flops_per_launch": distance_flops(pairs)}}
+
+
+def calibration(torch, vq, wl, dev, head_start, iters: int) -> dict:
+    """The offline calibration path at the page's calibration-set size (256
+    sequences x 512 tokens per KV head): lambda, K~, and Lloyd K-Means for
+    C_k and C_v (and a 4096-entry C_k)."""
+    hkv, t = wl.num_kv_heads, W.CALIB_TOKENS
+    keys = synthetic_rows(torch, wl, dev, (hkv, t, 128), "k", 3000)
+    vals = synthetic_rows(torch, wl, dev, (hkv, t, 128), "v", 4000)
+    lam = torch.empty((hkv, 128), dtype=torch.float32, device=dev)
+    kt = torch.empty((hkv, t, 128), dtype=torch.float32, device=dev)
+    lam_us = time_calls(torch, lambda: vq.calibrate_lambda(keys, out=lam), 10, head_start)
+    tk_us = time_calls(torch, lambda: vq.transform_keys(keys, lam, out=kt), 10, head_start)
+    out = {"workload": f"{hkv} KV heads x {W.CALIB_SEQS} x {W.CALIB_SEQ_LEN} calibration tokens",
+           "lambda_us": lam_us, "lambda_gbps": keys.numel() * 2 / (lam_us * 1e-6) / 1e9,
+           "transform_keys_us": tk_us,
+           "transform_keys_gbps": keys.numel() * 6 / (tk_us * 1e-6) / 1e9}
+    n = t * 32
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(5)
+    km = {}
+    for name, samples, bits, its in (("k8", kt.view(hkv, n, 4), 8, iters),
+                                     ("v8", vals.float().view(hkv, n, 4), 8, iters),
+                                     ("k12", kt.view(hkv, n, 4), 12, max(1, iters // 2))):
+        ent = 1 << bits
+        idx = torch.randperm(n, generator=gen)[:ent].to(dev)
+        init = samples[:, idx].double().contiguous()
+        cent = torch.empty_like(init)
+        ws = torch.empty(vq.kmeans_workspace_bytes(hkv, n, bits), dtype=torch.uint8, device=dev)
+        us = time_calls(torch, lambda: vq.kmeans(samples, init, its, centroids=cent, workspace=ws),
+                        1, head_start, warm=1)
+        per_it = us / its
+        tflops = distance_flops(hkv * n * ent) / (per_it * 1e-6) / 1e12
+        km[name] = {"sets": hkv, "samples_per_set": n, "entries": ent, "iters": its,
+                    "us_per_iter": per_it, "dense_pass_tflops": tflops,
+                    "frac_of_mfma_f32_peak": tflops / MFMA_F32_PEAK_TFLOPS}
+    out["kmeans"] = km
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +250,11 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain copies of known size (for byte-counter runs)")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 comparator")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill encode timing")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the calibration timings (lambda, K~, K-Means)")
+    ap.add_argument("--kmeans-iters", type=int, default=3,
+                    help="Lloyd iterations per timed K-Means call")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -373,6 +474,11 @@ def main(argv=None) -> int:
             "avg_launch_us": f_us, "gbps": fp16_bytes(wl, n) / (f_us * 1e-6) / 1e9,
             "vq_decode_attention_speedup": f_us / call_us, "cold_cache_copies": fcopies}
         del fcaches, fk, fv
+
+    if not args.no_prefill:
+        result["prefill_encode"] = prefill_encode(torch, vq, wl, dev, lam, cb_k, cb_v, head_start)
+    if not args.no_calibration:
+        result["calibration"] = calibration(torch, vq, wl, dev, head_start, args.kmeans_iters)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -20,6 +20,7 @@
 //  - update: a stable counting sort of the samples by cluster, then one
 //    sequential fp64 chain per (cluster, channel).
 #include "launchers.hpp"
+#include "nearest_search.hpp"
 
 namespace vqkv {
 
@@ -142,15 +143,10 @@ constexpr int kKmWaves = kKmThreads / kWave;   // 8
 constexpr int kKmChunk = 8192;                 // samples per assignment workgroup = sort chunk
 constexpr int kSortWaves = 4;                  // chunks per scatter workgroup (one per wave)
 
-template <int NENT>
-constexpr int kKmStride = NENT + 16;           // -2c rows on different banks
-
 // fp64 centroids staged in LDS when they fit beside the fp32 tables (8 KiB);
 // the 4096-entry case reads its few candidates from global memory (L2).
 template <int NENT>
 constexpr bool kKmLdsC64 = NENT <= 256;
-
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // fp64 squared distance of fp32 sample x to fp64 centroid c, rounded as the
 // definition rounds it (difference, square and running sum separately, in
@@ -169,28 +165,20 @@ __device__ __forceinline__ double sqdist4_c64(const float4 x, const double c[4])
 
 // Nearest centroid of every sample of one sort chunk (kKmChunk samples of set
 // blockIdx.y): assign[set][i], and, when hist is given, the chunk's cluster
-// histogram hist[set][chunk][NENT].
-//
-// The filter: with u = 2^-24, the matrix-core score s(c) = fl(||c||^2) -
-// 2 x.fl32(c) (fp32 products and sums) is within about 12 u (||x||^2 +
-// ||c||^2) of ||x - c||^2 - ||x||^2 (fp32 rounding of c and of ||c||^2, four
-// accumulations), and the fp64 distance within 2^-50 of the same scale.  The
-// bound used, E(c) = 2^-16 (||x||^2 + ||c||^2) plus 1e-30 for underflow, has a
-// margin of about 20x: every centroid whose s(c) - E(c) is not above min over
-// c' of s(c') + E(c') gets its fp64 distance, and the true nearest one is
-// among them.  Samples and centroids must be finite with magnitudes below
-// about 2^60 so that no fp32 score overflows.
+// histogram hist[set][chunk][NENT].  The search is nearest_search.hpp's with
+// the fp64 centroids rounded to fp32 for the scores: that rounding adds u
+// (||x||^2 + ||c||^2) to the score error, well inside the bound.  Samples
+// and centroids must be finite with magnitudes below about 2^60 so that no
+// fp32 score overflows.
 template <int NENT>
 __global__ __launch_bounds__(kKmThreads) void kmeans_assign_kernel(
     const float* __restrict__ samples, int num_samples, const double* __restrict__ centroids,
     int32_t* __restrict__ assign, int32_t* __restrict__ hist) {
-    __shared__ float m2[4 * kKmStride<NENT>];   // -2 fl32(c) by channel
-    __shared__ float cc[NENT];                  // fl32(||c||^2)
+    __shared__ float m2[4 * kSearchStride<NENT>];   // -2 fl32(c) by channel
+    __shared__ __align__(16) float ccu[NENT];       // fl32(||c||^2) (1 + 2^-16)
+    __shared__ __align__(16) float ccd[NENT];       // fl32(||c||^2) (1 - 2^-16)
     __shared__ double c64s[kKmLdsC64<NENT> ? NENT * 4 : 1];
     __shared__ int32_t cnt[NENT];
-    constexpr int kUnroll = 8;
-    constexpr float kUp = 1.0f + 0x1p-16f, kDown = 1.0f - 0x1p-16f;
-    static_assert(NENT % (16 * kUnroll) == 0, "whole unrolled groups");
 
     const int set = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -204,125 +192,41 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_assign_kernel(
         double nn = 0.0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            m2[j * kKmStride<NENT> + i] = -2.f * static_cast<float>(c[j]);
+            m2[j * kSearchStride<NENT> + i] = -2.f * static_cast<float>(c[j]);
             nn += c[j] * c[j];
             if constexpr (kKmLdsC64<NENT>) c64s[i * 4 + j] = c[j];
         }
-        cc[i] = static_cast<float>(nn);
+        const float nf = static_cast<float>(nn);
+        ccu[i] = nf * kBoundUp;
+        ccd[i] = nf * kBoundDown;
         cnt[i] = 0;
     }
     __syncthreads();
 
     const int s0 = chunk * kKmChunk, s1 = min(num_samples, s0 + kKmChunk);
-    const float* bcol = m2 + (lane >> 4) * kKmStride<NENT> + (lane & 15);
-    const float* ccol = cc + (lane & 15);
     int32_t* aset = assign + static_cast<size_t>(set) * num_samples;
     for (int base = s0 + wave * 16; base < s1; base += kKmWaves * 16) {
-        // A operand: sample base + lane % 16, channel lane / 16
-        const int ra = base + (lane & 15);
-        const float a = ra < s1 ? samples[(static_cast<size_t>(set) * num_samples + ra) * 4 +
-                                          (lane >> 4)]
-                                : 0.f;
-        const int r0 = base + 4 * (lane >> 4);   // this lane's D rows r0 .. r0 + 3
-        float4 xr[4];
-        float ex[4];
+        // this lane's sample base + lane % 16 (zero past the chunk)
+        const int r = base + (lane & 15);
+        const float4 x = r < s1 ? xset[r] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float xc[4] = {x.x, x.y, x.z, x.w};
+        const float bop = xc[lane >> 4];   // B operand: channel lane / 16
+        const float ex = row_bound((x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w));
+        const auto exact = [&](uint32_t nc) {
+            double c[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xr[i] = r0 + i < s1 ? xset[r0 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float xx = (xr[i].x * xr[i].x + xr[i].y * xr[i].y) +
-                             (xr[i].z * xr[i].z + xr[i].w * xr[i].w);
-            ex[i] = 2.f * (0x1p-16f * xx) + 1e-30f;   // the ||x||^2 parts of both bounds
-        }
-
-        // pass 1: min over c of s(c) + E(c), up to the ||x||^2 part
-        float smin[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
-#pragma nounroll
-        for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
-            f32x4_t d[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const float c0 = ccol[(blk + u) * 16] * kUp;
-                d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bcol[(blk + u) * 16],
-                                                            f32x4_t{c0, c0, c0, c0}, 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (kKmLdsC64<NENT>)
+                    c[j] = c64s[nc * 4 + j];
+                else
+                    c[j] = cset[nc * 4 + j];
             }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) smin[i] = fminf(smin[i], d[u][i]);
-        }
-        float thr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) thr[i] = row_min16(smin[i]) + ex[i];
-
-        // pass 2: the candidates get fp64 distances; groups of 8 x 16
-        // centroids without one are skipped
-        double bd[4];
-        uint32_t bi[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bd[i] = INFINITY;
-            bi[i] = 0xffffffffu;
-        }
-#pragma nounroll
-        for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
-            f32x4_t d[kUnroll];
-            bool any = false;
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const float c0 = ccol[(blk + u) * 16] * kDown;
-                d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bcol[(blk + u) * 16],
-                                                            f32x4_t{c0, c0, c0, c0}, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) any |= d[u][i] <= thr[i];
-            }
-            if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (d[u][i] <= thr[i]) {
-                        const int nc = (blk + u) * 16 + (lane & 15);
-                        double c[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            if constexpr (kKmLdsC64<NENT>)
-                                c[j] = c64s[nc * 4 + j];
-                            else
-                                c[j] = cset[nc * 4 + j];
-                        }
-                        const double dd = sqdist4_c64(xr[i], c);
-                        if (nearer(dd, static_cast<uint32_t>(nc), bd[i], bi[i])) {
-                            bd[i] = dd;
-                            bi[i] = static_cast<uint32_t>(nc);
-                        }
-                    }
-                }
-            }
-        }
-        // lexicographic minimum over the 16 lanes that share the rows
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            double d0 = bd[i];
-            uint32_t i0 = bi[i];
-#define VQKV_TAKE(M)                                                                       \
-    {                                                                                      \
-        const double d2 = lane_partner<M>(d0, lane);                                       \
-        const uint32_t i2 = lane_partner<M>(i0, lane);                                     \
-        if (nearer(d2, i2, d0, i0)) {                                                      \
-            d0 = d2;                                                                       \
-            i0 = i2;                                                                       \
-        }                                                                                  \
-    }
-            VQKV_TAKE(1)
-            VQKV_TAKE(2)
-            VQKV_TAKE(4)
-            VQKV_TAKE(8)
-#undef VQKV_TAKE
-            const int r = r0 + i;
-            if ((lane & 15) == 0 && r < s1) {
-                aset[r] = static_cast<int32_t>(i0);
-                if (hist != nullptr) atomicAdd(&cnt[i0 & (NENT - 1)], 1);
-            }
+            return sqdist4_c64(x, c);
+        };
+        const uint32_t code = nearest16<NENT>(m2, ccu, ccd, bop, ex, lane, exact);
+        if (lane < 16 && r < s1) {
+            aset[r] = static_cast<int32_t>(code);
+            if (hist != nullptr) atomicAdd(&cnt[code & (NENT - 1)], 1);
         }
     }
     if (hist != nullptr) {
@@ -455,33 +359,72 @@ __global__ __launch_bounds__(kSortWaves * kWave) void kmeans_scatter_kernel(
     }
 }
 
-// New centroids: one thread per (set, cluster, channel) sums the cluster's
-// sorted samples in order in fp64 from zero and divides once by the count;
-// a cluster without samples keeps its centroid.
-__global__ __launch_bounds__(256) void kmeans_update_kernel(const float* __restrict__ sorted,
-                                                            int num_samples,
-                                                            const int32_t* __restrict__ base,
-                                                            const int32_t* __restrict__ counts,
-                                                            int nent,
-                                                            double* __restrict__ centroids) {
-    const int set = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
-    if (t >= nent * 4) return;
-    const int c = t >> 2, j = t & 3;
+// New centroids: one wave per (set, cluster).  The 64 lanes stream the
+// cluster's sorted samples in tiles of 64 (coalesced 16-byte loads, kPre
+// tiles in flight), stage each tile channel-major in LDS, and lanes 0..3 add
+// channel `lane` of the tile's samples in order onto one fp64 sum each: the
+// sum of the cluster's samples in sample order from zero, then one division
+// by the count.  A cluster without samples keeps its centroid.
+constexpr int kUpdWaves = 4;
+constexpr int kPre = 8;   // tiles of 64 samples in flight per wave
+
+__global__ __launch_bounds__(kUpdWaves * kWave) void kmeans_update_kernel(
+    const float* __restrict__ sorted, int num_samples, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ counts, int nent, double* __restrict__ centroids) {
+    __shared__ __align__(16) float stage[kUpdWaves][4][kWave];
+    const int set = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int c = blockIdx.x * kUpdWaves + wave;
+    if (c >= nent) return;   // the whole wave; no barrier below
     const int32_t n = counts[static_cast<size_t>(set) * nent + c];
     if (n == 0) return;
-    const float* col =
-        sorted + (static_cast<size_t>(set) * num_samples + base[static_cast<size_t>(set) * nent + c]) * 4 + j;
+    const float4* src = reinterpret_cast<const float4*>(sorted) + static_cast<size_t>(set) * num_samples +
+                        base[static_cast<size_t>(set) * nent + c];
+    float* st = &stage[wave][0][0];
+    const int tiles = (n + kWave - 1) / kWave;
+    // loads past the cluster read its last sample (never added): unconditional
+    // loads keep the memory counters exact, so the prefetches stay in flight
+    float4 pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) pre[k] = src[min(k * kWave + lane, n - 1)];
     double s = 0.0;
-    int k = 0;
-    for (; k + 16 <= n; k += 16) {   // 16 loads in flight, then 16 chained adds
-        float v[16];
+    for (int t0 = 0; t0 < tiles; t0 += kPre) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = col[static_cast<size_t>(k + u) * 4];
+        for (int k = 0; k < kPre; ++k) {
+            const int t = t0 + k;   // t >= tiles: a padding tile, loaded and skipped
+            const float4 x = pre[k];
+            pre[k] = src[min((t + kPre) * kWave + lane, n - 1)];
+            st[0 * kWave + lane] = x.x;
+            st[1 * kWave + lane] = x.y;
+            st[2 * kWave + lane] = x.z;
+            st[3 * kWave + lane] = x.w;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < 4 && t < tiles) {
+                const int m = min(kWave, n - t * kWave);   // samples in this tile
+                if (m == kWave) {
+                    const float4* row = reinterpret_cast<const float4*>(st + lane * kWave);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) s = __dadd_rn(s, static_cast<double>(v[u]));
+                    for (int q = 0; q < kWave / 4; ++q) {
+                        const float4 v = row[q];
+                        s = __dadd_rn(s, static_cast<double>(v.x));
+                        s = __dadd_rn(s, static_cast<double>(v.y));
+                        s = __dadd_rn(s, static_cast<double>(v.z));
+                        s = __dadd_rn(s, static_cast<double>(v.w));
+                    }
+                } else {
+                    for (int q = 0; q < m; ++q)
+                        s = __dadd_rn(s, static_cast<double>(st[lane * kWave + q]));
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
     }
-    for (; k < n; ++k) s = __dadd_rn(s, static_cast<double>(col[static_cast<size_t>(k) * 4]));
-    centroids[(static_cast<size_t>(set) * nent + c) * 4 + j] = __ddiv_rn(s, static_cast<double>(n));
+    if (lane < 4)
+        centroids[(static_cast<size_t>(set) * nent + c) * 4 + lane] =
+            __ddiv_rn(s, static_cast<double>(n));
 }
 
 // fp64 -> fp16 bit pattern, rounded once to nearest even (subnormal halves,
@@ -587,8 +530,9 @@ hipError_t kmeans_run(const float* samples, int num_sets, int num_samples, const
                            dim3((nchunks + kSortWaves - 1) / kSortWaves, num_sets),
                            dim3(kSortWaves * kWave), 0, stream, samples, num_samples, w.assign,
                            w.hist, w.base, nchunks, w.sorted);
-        hipLaunchKernelGGL(kmeans_update_kernel, dim3((NENT * 4 + 255) / 256, num_sets), dim3(256),
-                           0, stream, w.sorted, num_samples, w.base, w.counts, NENT, centroids);
+        hipLaunchKernelGGL(kmeans_update_kernel, dim3((NENT + kUpdWaves - 1) / kUpdWaves, num_sets),
+                           dim3(kUpdWaves * kWave), 0, stream, w.sorted, num_samples, w.base,
+                           w.counts, NENT, centroids);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (assign_out != nullptr &&

@@ -6,27 +6,18 @@
 // concatenated to the cache.  Background (VQ principle): every 4-channel
 // sub-vector x gets j* = argmin_j ||x - C_j||^2.
 //
-// The decision is the one the fp64 reference takes: squared distances in
+// The decision is the one the fp64 reference takes (squared distances in
 // fp64 with every difference, product and sum rounded separately, exact ties
-// to the lowest index.  Computing all of them in fp64 is slow (fp64 vector
-// rate), so the search runs in two passes over each row of sub-vectors:
-//  1. On the matrix cores (v_mfma_f32_16x16x4_f32: 16 sub-vectors x 16
-//     centroids per instruction, the 4 channels as the contraction) the fp32
-//     scores s(c) = ||c||^2 - 2 x.c, whose row minimum picks the nearest
-//     centroid (||x||^2 is common to the row).  With u = 2^-24 the fp32
-//     score is within about 10 u (||x||^2 + ||c||^2) of the exact one; the
-//     bound used, E = 2^-16 (||x||^2 + max_c ||c||^2), has a margin of 25x.
-//     A row's threshold is min_c s(c) + 2E: every centroid that can be the
-//     exact (or fp64) nearest one scores below it.
-//  2. The same scores again; centroids under the threshold (normally one)
-//     get their fp64 distance, and the lexicographic (distance, index)
-//     minimum over them is the code.
+// to the lowest index), found by the certified matrix-core search of
+// nearest_search.hpp with the transformed keys and the values rounded to fp32
+// for the scores and kept in fp64 for the few exact distances.
 //
 // One 512-thread workgroup encodes up to 8 tokens of one (sequence, KV
 // head): 256 key and 256 value sub-vectors, 16 row blocks each, spread over
-// the 8 waves.  Codebooks (-2c by channel, fp32) and their squared norms are
-// staged in LDS.
+// the 8 waves.  Codebooks (-2c by channel, fp32) and their bound-scaled
+// squared norms are staged in LDS.
 #include "launchers.hpp"
+#include "nearest_search.hpp"
 
 namespace vqkv {
 
@@ -37,7 +28,6 @@ constexpr int kEncWaves = kEncThreads / kWave;     // 8
 constexpr int kEncTok = 8;                          // tokens per workgroup
 constexpr int kEncBlocks = kEncTok * kNumSub / 16;  // row blocks per tensor
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
     if (f32) return static_cast<double>(reinterpret_cast<const float*>(p)[i]);
@@ -51,105 +41,34 @@ __device__ __forceinline__ float norm2(const uint2 c) {
     return (c0 * c0 + c1 * c1) + (c2 * c2 + c3 * c3);
 }
 
-// Row stride of the -2c tables: 16 floats of padding put the 4 channel rows
-// on different banks for the 64 lanes of one B-operand read.
+// The nearest centroid of sub-vector rb*16 + lane % 16 of `xs` ([8 tokens]
+// [128] fp64 = [256 sub-vectors][4]) among NENT fp16 centroids staged as -2c
+// by channel (m2) and bound-scaled squared norms (cu, cd).
 template <int NENT>
-constexpr int kM2Stride = NENT + 16;
-
-// The nearest of NENT centroids for the 16 sub-vectors of row block rb of
-// `xs` ([8 tokens][128] fp64 = [256 sub-vectors][4]): on return lane l has
-// the lexicographic (fp64 distance, index) minimum over its 16-column slice
-// of the candidates of rows rb*16 + 4 (l / 16) + i in bd[i], bi[i].
-// m2 holds -2c by channel (rows kM2Stride apart), cc the squared norms.  The
-// MFMA accumulates -2 x.c onto a multiple of ||c||^2, which folds the
-// per-centroid part of the error bound E(c) = 2^-16 (||x||^2 + ||c||^2)
-// into the product: pass 1 takes s + 2^-16 ||c||^2, pass 2 s - 2^-16 ||c||^2.
-template <int NENT>
-__device__ __forceinline__ void search_rows(const float* m2, const float* cc,
-                                            const double (*xs)[kHeadDim], int rb, int lane,
-                                            double bd[4], uint32_t bi[4]) {
-    constexpr int kUnroll = 8;
-    constexpr float kUp = 1.0f + 0x1p-16f, kDown = 1.0f - 0x1p-16f;
-    static_assert(NENT % (16 * kUnroll) == 0, "whole unrolled groups");
-    const double* xrow = &xs[0][0];
-    // A operand: sub-vector rb*16 + lane%16, channel lane/16
-    const float a = static_cast<float>(xrow[(rb * 16 + (lane & 15)) * 4 + (lane >> 4)]);
-    const int r0 = rb * 16 + 4 * (lane >> 4);   // this lane's D rows r0 .. r0 + 3
-    const float* bcol = m2 + (lane >> 4) * kM2Stride<NENT> + (lane & 15);
-    const float* ccol = cc + (lane & 15);
-    float ex[4];
+__device__ __forceinline__ uint32_t search_rows(const float* m2, const float* cu,
+                                                const float* cd, const double (*xs)[kHeadDim],
+                                                int rb, int lane) {
+    const double* x = &xs[0][0] + (rb * 16 + (lane & 15)) * 4;
+    const float b = static_cast<float>(x[lane >> 4]);   // B operand: channel lane / 16
+    float xx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float xx = 0.f;
+    for (int j = 0; j < 4; ++j) {
+        const float v = static_cast<float>(x[j]);
+        xx += v * v;
+    }
+    // the fp16 centroid, recovered exactly from -2c; the distance rounded as
+    // the fp64 reference rounds it
+    const auto exact = [&](uint32_t nc) {
+        double dd = 0.0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float v = static_cast<float>(xrow[(r0 + i) * 4 + j]);
-            xx += v * v;
+            const double c = -0.5 * static_cast<double>(m2[j * kSearchStride<NENT> + nc]);
+            const double e = __dadd_rn(x[j], -c);
+            dd = j == 0 ? __dmul_rn(e, e) : __dadd_rn(dd, __dmul_rn(e, e));
         }
-        ex[i] = 2.f * (0x1p-16f * xx) + 1e-30f;   // the ||x||^2 parts of both bounds
-    }
-
-    // pass 1: min over c of s(c) + E(c), up to the ||x||^2 part
-    float smin[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
-    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
-        f32x4_t d[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const float c0 = ccol[(blk + u) * 16] * kUp;
-            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bcol[(blk + u) * 16],
-                                                        f32x4_t{c0, c0, c0, c0}, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) smin[i] = fminf(smin[i], d[u][i]);
-    }
-    float thr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) thr[i] = row_min16(smin[i]) + ex[i];
-
-    // pass 2: candidates are the c with s(c) - E(c) <= that minimum; they get
-    // fp64 distances.  Groups of 8 x 16 centroids without one are skipped.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bd[i] = INFINITY;
-        bi[i] = 0xffffffffu;
-    }
-    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
-        f32x4_t d[kUnroll];
-        bool any = false;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const float c0 = ccol[(blk + u) * 16] * kDown;
-            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bcol[(blk + u) * 16],
-                                                        f32x4_t{c0, c0, c0, c0}, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) any |= d[u][i] <= thr[i];
-        }
-        if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (d[u][i] <= thr[i]) {
-                    const int nc = (blk + u) * 16 + (lane & 15);
-                    // the fp16 centroid, recovered exactly from -2c; the
-                    // distance rounded as the fp64 reference rounds it
-                    double dd = 0.0;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const double c = -0.5 * static_cast<double>(m2[j * kM2Stride<NENT> + nc]);
-                        const double e = __dadd_rn(xrow[(r0 + i) * 4 + j], -c);
-                        dd = j == 0 ? __dmul_rn(e, e) : __dadd_rn(dd, __dmul_rn(e, e));
-                    }
-                    if (nearer(dd, static_cast<uint32_t>(nc), bd[i], bi[i])) {
-                        bd[i] = dd;
-                        bi[i] = static_cast<uint32_t>(nc);
-                    }
-                }
-            }
-        }
-    }
+        return dd;
+    };
+    return nearest16<NENT>(m2, cu, cd, b, row_bound(xx), lane, exact);
 }
 
 }  // namespace
@@ -163,10 +82,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     constexpr int KENT = 1 << KBITS;
     constexpr int KROW = kNumSub * KBITS / 8;
     // -2c by channel ([4][E], exact in fp32) and ||c||^2, per tensor
-    __shared__ float km2[4 * kM2Stride<KENT>];
-    __shared__ float vm2[4 * kM2Stride<256>];
-    __shared__ float kcc[KENT];
-    __shared__ float vcc[256];
+    __shared__ float km2[4 * kSearchStride<KENT>];
+    __shared__ float vm2[4 * kSearchStride<256>];
+    // ||c||^2 (1 + 2^-16), ||c||^2 (1 - 2^-16), read as float4
+    __shared__ __align__(16) float kcu[KENT];
+    __shared__ __align__(16) float kcd[KENT];
+    __shared__ __align__(16) float vcu[256];
+    __shared__ __align__(16) float vcd[256];
     __shared__ double xs[2][kEncTok][kHeadDim];       // transformed keys, values (fp64)
     __shared__ uint16_t code[2][kEncTok][kNumSub];
 
@@ -188,19 +110,23 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     for (int j = 0; j < KPER; ++j) {
         const int i = tid + j * kEncThreads;
         if (i < KENT) {
-            km2[0 * kM2Stride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x & 0xffffu);
-            km2[1 * kM2Stride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x >> 16);
-            km2[2 * kM2Stride<KENT> + i] = -2.f * half_bits_to_float(kc[j].y & 0xffffu);
-            km2[3 * kM2Stride<KENT> + i] = -2.f * half_bits_to_float(kc[j].y >> 16);
-            kcc[i] = norm2(kc[j]);
+            km2[0 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x & 0xffffu);
+            km2[1 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x >> 16);
+            km2[2 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].y & 0xffffu);
+            km2[3 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].y >> 16);
+            const float nn = norm2(kc[j]);
+            kcu[i] = nn * kBoundUp;
+            kcd[i] = nn * kBoundDown;
         }
     }
     if (tid < 256) {
-        vm2[0 * kM2Stride<256> + tid] = -2.f * half_bits_to_float(vc.x & 0xffffu);
-        vm2[1 * kM2Stride<256> + tid] = -2.f * half_bits_to_float(vc.x >> 16);
-        vm2[2 * kM2Stride<256> + tid] = -2.f * half_bits_to_float(vc.y & 0xffffu);
-        vm2[3 * kM2Stride<256> + tid] = -2.f * half_bits_to_float(vc.y >> 16);
-        vcc[tid] = norm2(vc);
+        vm2[0 * kSearchStride<256> + tid] = -2.f * half_bits_to_float(vc.x & 0xffffu);
+        vm2[1 * kSearchStride<256> + tid] = -2.f * half_bits_to_float(vc.x >> 16);
+        vm2[2 * kSearchStride<256> + tid] = -2.f * half_bits_to_float(vc.y & 0xffffu);
+        vm2[3 * kSearchStride<256> + tid] = -2.f * half_bits_to_float(vc.y >> 16);
+        const float nn = norm2(vc);
+        vcu[tid] = nn * kBoundUp;
+        vcd[tid] = nn * kBoundDown;
     }
 
     // k / lambda in fp64, the +-1 Walsh–Hadamard transform, then 1/sqrt(128);
@@ -227,35 +153,10 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     for (int job = wave; job < 2 * kEncBlocks; job += kEncWaves) {
         const int tt = job / kEncBlocks, rb = job % kEncBlocks;
         if (rb * 16 >= ntok * kNumSub) continue;   // whole block past the last token
-        double bd[4];
-        uint32_t bi[4];
-        if (tt == 0)
-            search_rows<KENT>(km2, kcc, xs[0], rb, lane, bd, bi);
-        else
-            search_rows<256>(vm2, vcc, xs[1], rb, lane, bd, bi);
-        const int r0 = rb * 16 + 4 * (lane >> 4);
-        // lexicographic minimum over the 16 lanes that share the rows
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            double d0 = bd[i];
-            uint32_t i0 = bi[i];
-#define VQKV_TAKE(M)                                                                       \
-    {                                                                                      \
-        const double d2 = lane_partner<M>(d0, lane);                                       \
-        const uint32_t i2 = lane_partner<M>(i0, lane);                                     \
-        if (nearer(d2, i2, d0, i0)) {                                                      \
-            d0 = d2;                                                                       \
-            i0 = i2;                                                                       \
-        }                                                                                  \
-    }
-            VQKV_TAKE(1)
-            VQKV_TAKE(2)
-            VQKV_TAKE(4)
-            VQKV_TAKE(8)
-#undef VQKV_TAKE
-            const int r = r0 + i;
-            if ((lane & 15) == 0) code[tt][r >> 5][r & 31] = static_cast<uint16_t>(i0);
-        }
+        const uint32_t cd = tt == 0 ? search_rows<KENT>(km2, kcu, kcd, xs[0], rb, lane)
+                                    : search_rows<256>(vm2, vcu, vcd, xs[1], rb, lane);
+        const int r = rb * 16 + lane;
+        if (lane < 16) code[tt][r >> 5][r & 31] = static_cast<uint16_t>(cd);
     }
     __syncthreads();
 

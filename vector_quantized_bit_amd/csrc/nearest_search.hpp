@@ -1,0 +1,166 @@
+// Certified nearest-centroid search for 16 sub-vectors of dimension 4 on the
+// matrix cores, shared by the encoder and by K-Means.
+//
+// VecInfer page, Background (VQ principle): each sub-vector x gets
+// j* = argmin_j ||x - C_j||^2.  The decision taken is the fp64 one: squared
+// distance with every difference, product and sum rounded separately, in
+// channel order; exact ties to the lowest index.
+//
+// Scores s(c) = ||c||^2 - 2 x.c come from v_mfma_f32_16x16x4_f32 with the
+// centroids as the 16 rows (A: -2c), the sub-vectors as the 16 columns (B)
+// and the 4 channels as the contraction; the accumulator input is the
+// centroids' squared norms, read from LDS straight into the C registers.
+// ||x||^2 is common to a column and left out.  With u = 2^-24, s(c) is within
+// about 12 u (||x||^2 + ||c||^2) of the exact ||x - c||^2 - ||x||^2 when x
+// and c enter the matrix cores rounded to fp32; the bound used, E(c) =
+// 2^-16 (||x||^2 + ||c||^2) + 1e-30, has a margin of about 20x.
+//   pass 1: thr = min_c (s(c) + E(c))          (per sub-vector)
+//   pass 2: candidates are the c with s(c) - E(c) <= thr; the exact nearest
+//           centroid is always one of them.
+// A sub-vector with exactly one candidate has its answer without any fp64
+// work.  Only a wave in which some sub-vector has two or more candidates
+// evaluates the fp64 distances of the candidates and takes the
+// lexicographic (distance, index) minimum.
+//
+// Lane l holds sub-vector l % 16 and, of every 16 centroids, the 4 rows
+// 4 (l / 16) .. 4 (l / 16) + 3: the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 share a
+// sub-vector and together see all centroids.  The ||c||^2 (1 + 2^-16) and
+// ||c||^2 (1 - 2^-16) terms (the per-centroid part of E folded into the
+// accumulator input) come precomputed from LDS; the per-sub-vector part
+// 2 * 2^-16 ||x||^2 + 1e-30 is the caller's ex.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace vqkv {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Row stride of the -2c tables: 16 floats of padding put the 4 channel rows
+// on different banks for the 64 lanes of one B-operand read.
+template <int NENT>
+constexpr int kSearchStride = NENT + 16;
+
+constexpr float kBoundUp = 1.0f + 0x1p-16f;
+constexpr float kBoundDown = 1.0f - 0x1p-16f;
+
+// ex[i] of a row from its fp32 squared norm
+__device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * xx) + 1e-30f; }
+
+// The nearest of NENT centroids for 16 sub-vectors (one MFMA column block).
+//   m2   [4][kSearchStride<NENT>] fp32: -2 fl32(c) by channel
+//   ccu, ccd [NENT] fp32, 16-byte aligned: fl32(||c||^2) (1 + 2^-16), (1 - 2^-16)
+//   b    this lane's B operand: channel lane / 16 of sub-vector lane % 16
+//   ex   the bound term of sub-vector lane % 16
+//   exact(c) -> double: the fp64 distance of sub-vector lane % 16 to centroid c
+// Returns the nearest centroid of sub-vector lane % 16 (in all 4 of its
+// lanes; 0xffffffff only for a sub-vector with no candidate, which finite
+// inputs never produce).  Every lane of the wave must be active; all
+// branches below are uniform.
+template <int NENT, typename Exact>
+__device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
+                                              const float* __restrict__ ccu,
+                                              const float* __restrict__ ccd, float b, float ex,
+                                              int lane, Exact exact) {
+    constexpr int kUnroll = 8;
+    static_assert(NENT % (16 * kUnroll) == 0, "whole unrolled groups");
+    const float* acol = m2 + (lane >> 4) * kSearchStride<NENT> + (lane & 15);
+    const int q4 = 4 * (lane >> 4);   // this lane's first centroid row in a block
+    const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(ccu + q4);
+    const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(ccd + q4);
+
+    // pass 1: thr = min over c of s(c) + E(c)
+    float smin = INFINITY;
+#pragma nounroll
+    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
+        f32x4_t d[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(acol[(blk + u) * 16], b,
+                                                        ucol[(blk + u) * 4], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            smin = fminf(smin, fminf(fminf(d[u][0], d[u][1]), fminf(d[u][2], d[u][3])));
+    }
+    smin = fminf(smin, lane_partner<16>(smin, lane));
+    smin = fminf(smin, lane_partner<32>(smin, lane));
+    const float thr = smin + ex;
+
+    // pass 2: each lane counts its candidates and keeps one
+    int cand = -1, cnt = 0;
+#pragma nounroll
+    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
+        f32x4_t d[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(acol[(blk + u) * 16], b,
+                                                        dcol[(blk + u) * 4], 0, 0, 0);
+        // the group's last hit as u * 4 + r (an inline constant, 0 .. 31),
+        // turned into a centroid row once per group
+        const int before = cnt;
+        int loc = 0;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool hit = d[u][r] <= thr;
+                loc = hit ? u * 4 + r : loc;
+                cnt += hit ? 1 : 0;
+            }
+        }
+        cand = cnt != before ? blk * 16 + (loc >> 2) * 16 + (loc & 3) : cand;
+    }
+    cnt += static_cast<int>(lane_partner<16>(static_cast<uint32_t>(cnt), lane));
+    cnt += static_cast<int>(lane_partner<32>(static_cast<uint32_t>(cnt), lane));
+    int best = cand < 0 ? -1 : cand + q4;
+    best = max(best, static_cast<int>(lane_partner<16>(static_cast<uint32_t>(best), lane)));
+    best = max(best, static_cast<int>(lane_partner<32>(static_cast<uint32_t>(best), lane)));
+
+    // every sub-vector has exactly one candidate: it is the nearest centroid
+    if (__builtin_amdgcn_ballot_w64(cnt != 1) == 0) return static_cast<uint32_t>(best);
+
+    // some sub-vector has several candidates: fp64 distances for all
+    // candidates of this block (pass 2 again), lexicographic minimum over
+    // the 4 lanes of each sub-vector
+    double bd = INFINITY;
+    uint32_t bi = 0xffffffffu;
+#pragma nounroll
+    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
+        f32x4_t d[kUnroll];
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(acol[(blk + u) * 16], b,
+                                                        dcol[(blk + u) * 4], 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) any |= d[u][r] <= thr;
+        }
+        if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (d[u][r] <= thr) {
+                    const uint32_t nc = static_cast<uint32_t>((blk + u) * 16 + q4 + r);
+                    const double dd = exact(nc);
+                    if (nearer(dd, nc, bd, bi)) {
+                        bd = dd;
+                        bi = nc;
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        const double d2 = step == 0 ? lane_partner<16>(bd, lane) : lane_partner<32>(bd, lane);
+        const uint32_t i2 = step == 0 ? lane_partner<16>(bi, lane) : lane_partner<32>(bi, lane);
+        if (nearer(d2, i2, bd, bi)) {
+            bd = d2;
+            bi = i2;
+        }
+    }
+    return bi;
+}
+
+}  // namespace vqkv
