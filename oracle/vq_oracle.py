@@ -288,9 +288,11 @@ def encode_append(k_new, v_new, lam, cb_k, cb_v, k_bits: int = 8, v_bits: int = 
 
 
 # ---------------------------------------------------------------------------
-# codebook training (fixtures only) — [VecInfer] Method details: codebooks
-# are pretrained offline by K-Means on transformed keys (raw values for V);
-# Experimental setup: at most 30 iterations.
+# codebook training (the fixtures' codebooks and the K-Means parity reference)
+# — [VecInfer] Method details: codebooks are pretrained offline by K-Means on
+# transformed keys (raw values for V); Experimental setup: at most 30
+# iterations.  The mean is the in-order fp64 sum (np.add.at adds the samples
+# of a cluster one by one, in sample order) divided once by the count.
 # ---------------------------------------------------------------------------
 
 def lloyd_kmeans(samples: np.ndarray, init: np.ndarray, iters: int) -> np.ndarray:

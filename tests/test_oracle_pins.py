@@ -340,6 +340,37 @@ def test_lloyd_objective_never_increases():
         c = oracle.lloyd_kmeans(x, c, 1)
 
 
+def test_lloyd_mean_is_the_in_order_sum():
+    """One Lloyd step written as plain Python loops (nearest centroid by the
+    channel-ordered squared distance, first minimum; each cluster's samples
+    added one by one in sample order from 0.0, then one division) equals the
+    oracle bit for bit, including an empty cluster that keeps its place."""
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((300, 4)) * [1.0, 3.0, 0.5, 2.0]).astype(np.float32).astype(np.float64)
+    init = x[:6].copy()
+    init[5] = [50.0, 50.0, 50.0, 50.0]          # far away: receives no sample
+    sums = [[0.0] * 4 for _ in range(6)]
+    counts = [0] * 6
+    for row in x.tolist():
+        best, arg = None, None
+        for j, cen in enumerate(init.tolist()):
+            d = 0.0
+            for a, b in zip(row, cen):
+                d = d + (a - b) * (a - b)
+            if best is None or d < best:
+                best, arg = d, j
+        counts[arg] += 1
+        for i in range(4):
+            sums[arg][i] = sums[arg][i] + row[i]
+    want = init.copy()
+    for j in range(6):
+        if counts[j]:
+            want[j] = [v / counts[j] for v in sums[j]]
+    got = oracle.lloyd_kmeans(x, init, 1)
+    assert counts[5] == 0
+    assert np.array_equal(got.view(np.uint64), want.view(np.uint64))
+
+
 # --- byte counts the pages print ------------------------------------------------
 
 def test_byte_counts_match_the_pages():
