@@ -76,8 +76,10 @@ def cpu_baseline(wl: W.Workload, seconds: float) -> dict:
     heads = []
     for h in range(wl.num_kv_heads):
         heads.append((q[h * g:(h + 1) * g], W.random_lambda(wl.config_id, h),
-                      W.random_codebook(wl.config_id, h, "k", 1 << wl.k_bits, 0.6),
-                      W.random_codebook(wl.config_id, h, "v", 1 << wl.v_bits, 1.0, 1 / 32),
+                      W.random_codebook(wl.config_id, h, "k", 1 << wl.k_bits, 0.6,
+                                        sub_dim=wl.sub_dim),
+                      W.random_codebook(wl.config_id, h, "v", 1 << wl.v_bits, 1.0, 1 / 32,
+                                        sub_dim=wl.sub_dim),
                       W.random_code_rows(wl.config_id, 0, h, "k", n, wl.k_row_bytes),
                       W.random_code_rows(wl.config_id, 0, h, "v", n, wl.v_row_bytes)))
     done = 0
@@ -171,10 +173,10 @@ def time_calls(torch, fn, reps, head_start, warm=2):
     return a.elapsed_time(b) * 1e3 / reps
 
 
-def distance_flops(pairs: int) -> int:
+def distance_flops(pairs: int, sub_dim: int = 4) -> int:
     """One dense pass of the nearest-centroid search as a contraction:
-    ||c||^2 - 2 x.c for every (sub-vector, centroid) pair, 4 multiply-adds."""
-    return 8 * pairs
+    ||c||^2 - 2 x.c for every (sub-vector, centroid) pair, d multiply-adds."""
+    return 2 * sub_dim * pairs
 
 
 def prefill_encode(torch, vq, wl, dev, lam, cb_k, cb_v, head_start) -> dict:
@@ -188,15 +190,17 @@ def prefill_encode(torch, vq, wl, dev, lam, cb_k, cb_v, head_start) -> dict:
     cv = torch.empty((bsz, hkv, p, wl.v_row_bytes), dtype=torch.uint8, device=dev)
     enc = vq.prepare_encode_append(kp, vp, lam, cb_k, cb_v, ck, cv, 0)
     us = time_calls(torch, enc, 5, head_start)
-    pairs = bsz * hkv * p * 32 * ((1 << wl.k_bits) + (1 << wl.v_bits))
-    tflops = distance_flops(pairs) / (us * 1e-6) / 1e12
+    pairs = bsz * hkv * p * wl.num_sub * ((1 << wl.k_bits) + (1 << wl.v_bits))
+    flops = distance_flops(pairs, wl.sub_dim)
+    tflops = flops / (us * 1e-6) / 1e12
     hbm = bsz * hkv * p * (2 * 128 * 2 + wl.k_row_bytes + wl.v_row_bytes)
     return {"workload": f"{wl.name}-prompt-{p}", "tokens": bsz * p, "avg_launch_us": us,
             "tokens_per_s": bsz * p / (us * 1e-6), "hbm_gbps": hbm / (us * 1e-6) / 1e9,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / MFMA_F32_PEAK_TFLOPS,
-                         "kernel": "encode_append_kernel",
-                         "flops_per_launch": distance_flops(pairs)}}
+                         "kernel": "encode_append8_kernel" if wl.sub_dim == 8
+                         else "encode_append_kernel",
+                         "flops_per_launch": flops}}
 
 
 def calibration(torch, vq, wl, dev, head_start, iters: int) -> dict:
@@ -279,10 +283,10 @@ def main(argv=None) -> int:
     # ---- inputs (resident in HBM before timing) ---------------------------
     q = t(np.stack([W.queries(wl.config_id, b, hq) for b in range(bsz)]).astype(st))
     lam = t(np.stack([W.random_lambda(wl.config_id, g) for g in range(hkv)]))
-    cb_k = t(np.stack([W.random_codebook(wl.config_id, g, "k", 1 << wl.k_bits, 0.6)
-                       for g in range(hkv)]))
-    cb_v = t(np.stack([W.random_codebook(wl.config_id, g, "v", 1 << wl.v_bits, 1.0, 1 / 32)
-                       for g in range(hkv)]))
+    cb_k = t(np.stack([W.random_codebook(wl.config_id, g, "k", 1 << wl.k_bits, 0.6,
+                                         sub_dim=wl.sub_dim) for g in range(hkv)]))
+    cb_v = t(np.stack([W.random_codebook(wl.config_id, g, "v", 1 << wl.v_bits, 1.0, 1 / 32,
+                                         sub_dim=wl.sub_dim) for g in range(hkv)]))
     ck0 = torch.empty((bsz, hkv, cap, wl.k_row_bytes), dtype=torch.uint8, device=dev)
     cv0 = torch.empty((bsz, hkv, cap, wl.v_row_bytes), dtype=torch.uint8, device=dev)
     for b in range(bsz):
@@ -423,7 +427,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": bsz, "context_len": n, "q_heads": hq,
                    "kv_heads": hkv, "head_dim": 128, "k_code_bits": wl.k_bits,
-                   "v_code_bits": wl.v_bits, "sub_dim": 4, "append_tokens_per_step": 1,
+                   "v_code_bits": wl.v_bits, "sub_dim": wl.sub_dim, "append_tokens_per_step": 1,
                    "step_partials": step_parts, "attention_splits": splits,
                    "cold_cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,

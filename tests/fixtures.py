@@ -54,8 +54,10 @@ def chain_cache(wl: W.Workload, seqs=None, heads=None) -> Cache:
     for g in range(wl.num_kv_heads):
         if g not in heads:
             lam[g] = W.random_lambda(wl.config_id, g)
-            cb_k[g] = W.random_codebook(wl.config_id, g, "k", 1 << wl.k_bits, 0.6)
-            cb_v[g] = W.random_codebook(wl.config_id, g, "v", 1 << wl.v_bits, 1.0, 1 / 32)
+            cb_k[g] = W.random_codebook(wl.config_id, g, "k", 1 << wl.k_bits, 0.6,
+                                        sub_dim=wl.sub_dim)
+            cb_v[g] = W.random_codebook(wl.config_id, g, "v", 1 << wl.v_bits, 1.0, 1 / 32,
+                                        sub_dim=wl.sub_dim)
             for b in range(wl.batch):
                 codes_k[b, g, :n] = W.random_code_rows(wl.config_id, b, g, "k", n, wl.k_row_bytes)
                 codes_v[b, g, :n] = W.random_code_rows(wl.config_id, b, g, "v", n, wl.v_row_bytes)
@@ -97,10 +99,10 @@ def random_cache(wl: W.Workload, context_len: int | None = None, batch: int | No
     st = _storage(wl.qkv_dtype)
     q = np.stack([W.queries(wl.config_id, b, hq) for b in range(bsz)]).astype(st)
     lam = np.stack([W.random_lambda(wl.config_id, g) for g in range(hkv)])
-    cb_k = np.stack([W.random_codebook(wl.config_id, g, "k", 1 << wl.k_bits, 0.6)
-                     for g in range(hkv)])
-    cb_v = np.stack([W.random_codebook(wl.config_id, g, "v", 1 << wl.v_bits, 1.0, 1 / 32)
-                     for g in range(hkv)])
+    cb_k = np.stack([W.random_codebook(wl.config_id, g, "k", 1 << wl.k_bits, 0.6,
+                                       sub_dim=wl.sub_dim) for g in range(hkv)])
+    cb_v = np.stack([W.random_codebook(wl.config_id, g, "v", 1 << wl.v_bits, 1.0, 1 / 32,
+                                       sub_dim=wl.sub_dim) for g in range(hkv)])
     codes_k = np.zeros((bsz, hkv, cap, wl.k_row_bytes), np.uint8)
     codes_v = np.zeros((bsz, hkv, cap, wl.v_row_bytes), np.uint8)
     for b in range(bsz):

@@ -60,6 +60,9 @@ def attn(lib, layout, q=A, q_dtype=0, lam=A, cbk=A, cbv=A, ck=A, cv=A, batch=1, 
 @pytest.mark.parametrize("kw,layout_kw,status,needle", [
     (dict(), dict(head_dim=64), UNSUPPORTED, "head_dim"),
     (dict(), dict(sub_dim=8), UNSUPPORTED, "sub_dim"),
+    (dict(), dict(sub_dim=8, k_bits=12, v_bits=8), UNSUPPORTED, "sub_dim"),
+    (dict(), dict(sub_dim=6), UNSUPPORTED, "sub_dim"),
+    (dict(q=None), dict(sub_dim=8, k_bits=12, v_bits=12), INVALID, "q is NULL"),
     (dict(), dict(k_bits=10), UNSUPPORTED, "k_code_bits"),
     (dict(), dict(v_bits=12), UNSUPPORTED, "v_code_bits"),
     (dict(), dict(hkv=0), INVALID, "num_kv_heads"),

@@ -146,9 +146,10 @@ def test_full_size_sampled_heads(config, samples):
 
 # --- encoder ------------------------------------------------------------------------
 
-def check_codes(got_rows, ref_rows, gaps, bits, x=None, cb=None, what=""):
-    got = oracle.unpack_codes(got_rows, bits, 32)
-    ref = oracle.unpack_codes(ref_rows, bits, 32)
+def check_codes(got_rows, ref_rows, gaps, bits, x=None, cb=None, what="", sub=4):
+    num_sub = 128 // sub
+    got = oracle.unpack_codes(got_rows, bits, num_sub)
+    ref = oracle.unpack_codes(ref_rows, bits, num_sub)
     gaps = np.asarray(gaps)
     mism = got != ref
     n_mis = int(mism.sum())
@@ -156,10 +157,10 @@ def check_codes(got_rows, ref_rows, gaps, bits, x=None, cb=None, what=""):
     if n_mis:
         # every difference must sit at an fp64 near-tie: both picks are nearest
         # centroids to within rounding
-        sub = np.asarray(x, np.float64).reshape(-1, 32, 4)[mism]
+        xs = np.asarray(x, np.float64).reshape(-1, num_sub, sub)[mism]
         cbd = np.asarray(cb, np.float64)
-        dg = ((sub - cbd[got[mism]]) ** 2).sum(-1)
-        dr = ((sub - cbd[ref[mism]]) ** 2).sum(-1)
+        dg = ((xs - cbd[got[mism]]) ** 2).sum(-1)
+        dr = ((xs - cbd[ref[mism]]) ** 2).sum(-1)
         assert np.all(gaps[mism] <= 1e-9 * (1 + dr)), what
         assert np.all(np.abs(dg - dr) <= 1e-9 * (1 + dr)), what
 
@@ -362,15 +363,16 @@ def check_step(c, cur, splits=0, heads=None, what=""):
     others[cur] = False
     assert np.array_equal(ck[:, :, others], c.codes_k[:, :, others]), what
     assert np.array_equal(cv[:, :, others], c.codes_v[:, :, others]), what
-    kb = wl.k_bits
+    kb, vb, sd = wl.k_bits, wl.v_bits, wl.sub_dim
     for b in range(bsz):
         for g in range(hkv):
             pk, pv, gk, gv = oracle.encode_append(k[b, g][None], v[b, g][None], c.lam[g],
-                                                  c.cb_k[g], c.cb_v[g], kb, 8)
+                                                  c.cb_k[g], c.cb_v[g], kb, vb)
             kt = oracle.transform_keys(k[b, g][None], c.lam[g])
-            check_codes(ck[b, g, cur:cur + 1], pk, gk, kb, kt, c.cb_k[g], f"{what} K b{b} g{g}")
-            check_codes(cv[b, g, cur:cur + 1], pv, gv, 8, v[b, g][None], c.cb_v[g],
-                        f"{what} V b{b} g{g}")
+            check_codes(ck[b, g, cur:cur + 1], pk, gk, kb, kt, c.cb_k[g], f"{what} K b{b} g{g}",
+                        sd)
+            check_codes(cv[b, g, cur:cur + 1], pv, gv, vb, v[b, g][None], c.cb_v[g],
+                        f"{what} V b{b} g{g}", sd)
     after = dataclasses.replace(c, codes_k=ck, codes_v=cv, context_len=cur + 1)
     if heads is None:
         assert_close(got, expected_all(after), what)
@@ -583,3 +585,132 @@ def test_window_chain_and_flush():
         ref = oracle.decode_attention_window(c.q, c.lam, c.cb_k, c.cb_v, c.codes_k, c.codes_v,
                                              num_codes, host_k, host_v, win_len + 1)
         assert_close(out.cpu().numpy().astype(np.float64), ref, f"chain step {step}")
+
+
+# --- the 1.5-bit layout: 8-dim sub-vectors, 4096-entry C_k and C_v, 12-bit codes ----
+
+def d8_workload(config_id, batch, group, hkv, n, dtype="f16"):
+    return W.Workload(config_id, "adhoc-1.5bit", batch=batch, num_q_heads=group * hkv,
+                      num_kv_heads=hkv, context_len=n, k_bits=12, v_bits=12, sub_dim=8,
+                      qkv_dtype=dtype)
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 511, 512, 513, 1024])
+def test_d8_attention_ragged_lengths(n):
+    c = random_cache(W.WORKLOADS[7], context_len=n)
+    d = upload(c)
+    assert_close(run_attention(d, n), expected_all(c), f"1.5bit tiny n={n}")
+
+
+@pytest.mark.parametrize("group,batch,hkv,n,dtype,splits", [
+    (1, 2, 2, 300, "f16", 0), (4, 1, 2, 2049, "f16", 3), (5, 2, 2, 1500, "f16", 0),
+    (8, 1, 2, 777, "f32", 0), (3, 3, 1, 4096, "f16", 64)])
+def test_d8_attention_groups_and_splits(group, batch, hkv, n, dtype, splits):
+    c = random_cache(d8_workload(110 + group, batch, group, hkv, n, dtype))
+    d = upload(c)
+    assert_close(run_attention(d, n, splits), expected_all(c),
+                 f"1.5bit G={group} B={batch} n={n} {dtype} S={splits}")
+
+
+def test_d8_attention_full_size_sampled_heads():
+    wl = W.WORKLOADS[6]
+    c = random_cache(wl)
+    d = upload(c)
+    got = run_attention(d, wl.context_len)
+    assert np.isfinite(got).all()
+    g = wl.group
+    for b, h in [(0, 0), (0, 5)]:
+        assert_close(got[b, h * g:(h + 1) * g], expected_head(c, b, h), f"config6 kv={h}")
+
+
+def test_d8_attention_lossless_codebooks():
+    """Keys and values built from codebook entries: the 1.5-bit kernel must
+    then equal textbook attention on the raw (q, K, V)."""
+    rng = np.random.default_rng(120)
+    n, group = 700, 4
+    h = oracle.sylvester_hadamard(128)
+    cb_k = (rng.standard_normal((1, 4096, 8)) * 0.7).astype(np.float16)
+    cb_v = (rng.standard_normal((1, 4096, 8)) * 2).astype(np.float16)
+    ck = rng.integers(0, 4096, size=(n, 16))
+    cv = rng.integers(0, 4096, size=(n, 16))
+    lam = (1.0 + rng.random((1, 128)) * 3).astype(np.float32)
+    keys = (cb_k[0].astype(np.float64)[ck].reshape(n, 128) @ h.T) * lam[0].astype(np.float64)
+    vals = cb_v[0].astype(np.float64)[cv].reshape(n, 128)
+    q = rng.standard_normal((1, group, 128)).astype(np.float16)
+    codes_k = oracle.pack_codes(ck, 12)[None, None]
+    codes_v = oracle.pack_codes(cv, 12)[None, None]
+    d = dict(q=dev(q), lam=dev(lam), cb_k=dev(cb_k), cb_v=dev(cb_v), codes_k=dev(codes_k),
+             codes_v=dev(codes_v))
+    got = run_attention(d, n)
+    ref = np.stack([oracle.softmax_attention(q[0, i].astype(np.float64), keys, vals)
+                    for i in range(group)])[None]
+    assert_close(got, ref, "1.5bit lossless")
+
+
+@pytest.mark.parametrize("cur,splits,group", [(0, 0, 4), (31, 0, 4), (511, 2, 4), (1023, 0, 4),
+                                              (700, 0, 5), (300, 0, 1)])
+def test_d8_decode_step(cur, splits, group):
+    wl = d8_workload(130 + group, 2, group, 2, 1024)
+    check_step(random_cache(wl), cur, splits, what=f"1.5bit step cur={cur} G={group}")
+
+
+def test_d8_decode_step_full_size():
+    wl = W.WORKLOADS[6]
+    check_step(random_cache(wl), wl.context_len - 1, heads=[(0, 2), (0, 7)],
+               what="1.5bit step config6")
+
+
+@pytest.mark.parametrize("t_new,cur,dtype", [(1, 0, "f16"), (13, 5, "f16"), (64, 100, "f32"),
+                                             (200, 0, "f16")])
+def test_d8_encode_append(t_new, cur, dtype):
+    bsz, hkv = 2, 2
+    lam = np.stack([W.random_lambda(140, g) for g in range(hkv)])
+    cb_k = np.stack([W.random_codebook(140, g, "k", 4096, 0.6, sub_dim=8) for g in range(hkv)])
+    cb_v = np.stack([W.random_codebook(140, g, "v", 4096, 1.0, 1 / 32, sub_dim=8)
+                     for g in range(hkv)])
+    st = np.float16 if dtype == "f16" else np.float32
+    k = np.stack([np.stack([W.kv_rows(140, b, g, "k", t_new, append=True) for g in range(hkv)])
+                  for b in range(bsz)]).astype(st)
+    v = np.stack([np.stack([W.kv_rows(140, b, g, "v", t_new, append=True) for g in range(hkv)])
+                  for b in range(bsz)]).astype(st)
+    cap = cur + t_new + 3
+    ck = torch.full((bsz, hkv, cap, 24), 0xA5, dtype=torch.uint8, device=DEV)
+    cv = torch.full((bsz, hkv, cap, 24), 0x5A, dtype=torch.uint8, device=DEV)
+    vq.encode_append(dev(k), dev(v), dev(lam), dev(cb_k), dev(cb_v), ck, cv, cur)
+    torch.cuda.synchronize()
+    ckh, cvh = ck.cpu().numpy(), cv.cpu().numpy()
+    outside = np.ones(cap, bool)
+    outside[cur:cur + t_new] = False
+    assert np.all(ckh[:, :, outside] == 0xA5) and np.all(cvh[:, :, outside] == 0x5A)
+    for b in range(bsz):
+        for g in range(hkv):
+            pk, pv, gk, gv = oracle.encode_append(k[b, g], v[b, g], lam[g], cb_k[g], cb_v[g],
+                                                  12, 12)
+            kt = oracle.transform_keys(k[b, g], lam[g])
+            check_codes(ckh[b, g, cur:cur + t_new], pk, gk, 12, kt, cb_k[g],
+                        f"1.5bit enc K b{b} g{g}", 8)
+            check_codes(cvh[b, g, cur:cur + t_new], pv, gv, 12, v[b, g], cb_v[g],
+                        f"1.5bit enc V b{b} g{g}", 8)
+
+
+def test_d8_encoder_exact_ties_go_to_lowest_index():
+    rng = np.random.default_rng(150)
+    base = rng.standard_normal((2048, 8)).astype(np.float16)
+    cb = np.concatenate([base, base])[None]             # entry j and j + 2048 identical
+    codes = rng.integers(0, 2048, size=(5, 16))
+    v = base.astype(np.float64)[codes].reshape(5, 128).astype(np.float32)[None, None]
+    lam = np.ones((1, 128), np.float32)
+    ck = torch.zeros((1, 1, 8, 24), dtype=torch.uint8, device=DEV)
+    cv = torch.zeros((1, 1, 8, 24), dtype=torch.uint8, device=DEV)
+    vq.encode_append(dev(v), dev(v), dev(lam), dev(cb), dev(cb), ck, cv, 2)
+    torch.cuda.synchronize()
+    got = oracle.unpack_codes(cv.cpu().numpy()[0, 0, 2:7], 12, 16)
+    np.testing.assert_array_equal(got, codes)
+
+
+@pytest.mark.parametrize("num_codes,win_len,group", [(700, 0, 4), (1000, 127, 4), (0, 9, 4),
+                                                     (513, 64, 5)])
+def test_d8_decode_step_window(num_codes, win_len, group):
+    wl = d8_workload(160 + group, 2, group, 2, 1024)
+    check_window_step(random_cache(wl), num_codes, win_len,
+                      what=f"1.5bit window codes={num_codes} win={win_len} G={group}")

@@ -190,7 +190,7 @@ def test_pack_roundtrip_random():
 
 # --- the dequantise + attention chain -------------------------------------------
 
-def _lossless_layer(rng, hkv, group, n, k_bits):
+def _lossless_layer(rng, hkv, group, n, k_bits, sub=4, v_bits=8):
     """A layer whose keys/values are exactly representable by their codebooks.
 
     Transformed keys are built from codebook entries, then mapped back to
@@ -200,17 +200,17 @@ def _lossless_layer(rng, hkv, group, n, k_bits):
     h = scipy.linalg.hadamard(dim) / math.sqrt(dim)
     q = rng.standard_normal((hkv * group, dim)).astype(np.float16)
     lam = (1.0 + rng.random((hkv, dim)) * 3).astype(np.float32)
-    cb_k = (rng.standard_normal((hkv, 1 << k_bits, 4)) * 0.7).astype(np.float16)
-    cb_v = (rng.standard_normal((hkv, 256, 4)) * 2).astype(np.float16)
-    ck = rng.integers(0, 1 << k_bits, size=(hkv, n, 32))
-    cv = rng.integers(0, 256, size=(hkv, n, 32))
+    cb_k = (rng.standard_normal((hkv, 1 << k_bits, sub)) * 0.7).astype(np.float16)
+    cb_v = (rng.standard_normal((hkv, 1 << v_bits, sub)) * 2).astype(np.float16)
+    ck = rng.integers(0, 1 << k_bits, size=(hkv, n, dim // sub))
+    cv = rng.integers(0, 1 << v_bits, size=(hkv, n, dim // sub))
     keys, vals = [], []
     for g in range(hkv):
         kt = cb_k[g].astype(np.float64)[ck[g]].reshape(n, dim)
         keys.append((kt @ h.T) * lam[g].astype(np.float64))
         vals.append(cb_v[g].astype(np.float64)[cv[g]].reshape(n, dim))
     codes_k = np.stack([oracle.pack_codes(ck[g], k_bits) for g in range(hkv)])[None]
-    codes_v = np.stack([oracle.pack_codes(cv[g], 8) for g in range(hkv)])[None]
+    codes_v = np.stack([oracle.pack_codes(cv[g], v_bits) for g in range(hkv)])[None]
     return q, lam, cb_k, cb_v, codes_k, codes_v, keys, vals
 
 
@@ -228,6 +228,38 @@ def test_lossless_codebook_reduces_to_textbook_attention(hkv, group, k_bits):
     kt = oracle.transform_keys(keys[0], lam[0])
     codes, _ = oracle.vq_encode(kt, cb_k[0])
     np.testing.assert_array_equal(oracle.pack_codes(codes, k_bits), codes_k[0, 0])
+
+
+@pytest.mark.parametrize("hkv,group", [(1, 4), (2, 5)])
+def test_lossless_codebook_1p5bit_layout(hkv, group):
+    """The VecInfer page's 1.5-bit choice (codebook-size ablation: 2^12 x 8 x 2
+    bytes): 8-dim sub-vectors, 4096-entry C_k and C_v, 16 codes of 12 bits per
+    vector.  With lossless codebooks it reduces to textbook attention, and the
+    transformed keys and the values re-encode to their codes."""
+    rng = np.random.default_rng(40 + hkv * group)
+    n = 257
+    q, lam, cb_k, cb_v, codes_k, codes_v, keys, vals = _lossless_layer(rng, hkv, group, n, 12,
+                                                                       sub=8, v_bits=12)
+    assert codes_k.shape[-1] == 24 and codes_v.shape[-1] == 24
+    out = oracle.decode_attention(q[None], lam, cb_k, cb_v, codes_k, codes_v, n, 12, 12)[0]
+    for hq in range(hkv * group):
+        g = hq // group
+        ref = oracle.softmax_attention(q[hq].astype(np.float64), keys[g], vals[g])
+        np.testing.assert_allclose(out[hq], ref, rtol=1e-10, atol=1e-11)
+    pk, pv, _, _ = oracle.encode_append(keys[0], vals[0], lam[0], cb_k[0], cb_v[0], 12, 12)
+    np.testing.assert_array_equal(pk, codes_k[0, 0])
+    np.testing.assert_array_equal(pv, codes_v[0, 0])
+
+
+def test_pack12_sixteen_codes_per_row():
+    """16 codes of 12 bits fill 24 bytes; code i occupies bits [12 i, 12 i + 12)
+    (hand-checked on the first three codes)."""
+    codes = np.array([[0xABC, 0x123, 0xFFF] + [0] * 13])
+    packed = oracle.pack_codes(codes, 12)
+    assert packed.shape == (1, 24)
+    # bits 0-11: ABC, 12-23: 123, 24-35: FFF -> bytes BC, 3A, 12, FF, 0F
+    assert list(packed[0, :5]) == [0xBC, 0x3A, 0x12, 0xFF, 0x0F]
+    np.testing.assert_array_equal(oracle.unpack_codes(packed, 12, 16), codes)
 
 
 def test_single_token_returns_its_value_row():

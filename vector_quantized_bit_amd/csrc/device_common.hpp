@@ -158,6 +158,19 @@ __device__ __forceinline__ double sqdist4_f64(const double x[4], const uint2 c) 
     return d;
 }
 
+// The same for an 8-dim sub-vector and an fp16 centroid of 8 halves.
+__device__ __forceinline__ double sqdist8_f64(const double x[8], const uint4 c) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    double d = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t bits = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
+        const double e = __dadd_rn(x[j], -static_cast<double>(half_bits_to_float(bits)));
+        d = j == 0 ? __dmul_rn(e, e) : __dadd_rn(d, __dmul_rn(e, e));
+    }
+    return d;
+}
+
 // Lexicographic (distance, index) order: the nearest centroid, exact ties
 // to the lowest index, whatever order candidates are combined in.
 __device__ __forceinline__ bool nearer(double d, uint32_t i, double d0, uint32_t i0) {

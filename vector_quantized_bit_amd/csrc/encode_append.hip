@@ -181,12 +181,120 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     }
 }
 
-hipError_t launch_encode_append(int k_bits, const void* k_new, const void* v_new, bool kv_f32,
-                                const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
-                                uint8_t* codes_k, uint8_t* codes_v, int batch, int num_kv_heads,
-                                int capacity, int cur_len, int num_new, hipStream_t stream) {
+// The d = 8 layout (16 sub-vectors of 8 channels, C_k and C_v of 4096
+// entries, 24-byte rows of 12-bit codes): 8 tokens per workgroup, as above,
+// searched with nearest16_d8 against the fp16 codebook in LDS.  A 4096 x 8
+// table with its two norm tables takes 96 KiB, so keys and values are
+// searched one after the other with the same LDS.
+constexpr int kEnc8Ent = 4096;
+constexpr int kEnc8Pos = kHeadDim / 8;           // 16 sub-vectors per vector
+constexpr int kEnc8Row = kEnc8Pos * 12 / 8;      // 24 bytes per code row
+
+__global__ __launch_bounds__(kEncThreads) void encode_append8_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
+    const float* __restrict__ lambda, const uint16_t* __restrict__ cb_k,
+    const uint16_t* __restrict__ cb_v, uint8_t* __restrict__ codes_k,
+    uint8_t* __restrict__ codes_v, int num_kv_heads, int capacity, int cur_len, int num_new) {
+    __shared__ __align__(16) uint16_t ctab[kEnc8Ent * 8];   // one codebook, fp16 as stored
+    __shared__ __align__(16) float cu[kEnc8Ent];            // ||c||^2 (1 + 2^-16)
+    __shared__ __align__(16) float cd[kEnc8Ent];            // ||c||^2 (1 - 2^-16)
+    __shared__ double xs[2][kEncTok][kHeadDim];             // transformed keys, values (fp64)
+    __shared__ uint16_t code[2][kEncTok][kEnc8Pos];
+
+    const int t0 = blockIdx.x * kEncTok, g = blockIdx.y, b = blockIdx.z;
+    const int ntok = min(kEncTok, num_new - t0);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const bool f32 = kv_f32 != 0;
+
+    // k / lambda in fp64, the +-1 Walsh–Hadamard transform, then 1/sqrt(128);
+    // values as they are.  Rows of tokens past num_new are zero.
+    const float* lam = lambda + g * kHeadDim;
+    for (int t = wave; t < kEncTok; t += kEncWaves) {
+        const bool live = t < ntok;
+        const size_t in_row = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + t0 +
+                              (live ? t : 0);
+        double x0 = load_elem(k_new, f32, in_row * kHeadDim + 2 * lane) /
+                    static_cast<double>(lam[2 * lane]);
+        double x1 = load_elem(k_new, f32, in_row * kHeadDim + 2 * lane + 1) /
+                    static_cast<double>(lam[2 * lane + 1]);
+        fwht128(x0, x1);
+        xs[0][t][2 * lane] = live ? x0 * kInvSqrtD64 : 0.0;
+        xs[0][t][2 * lane + 1] = live ? x1 * kInvSqrtD64 : 0.0;
+        xs[1][t][2 * lane] = live ? load_elem(v_new, f32, in_row * kHeadDim + 2 * lane) : 0.0;
+        xs[1][t][2 * lane + 1] =
+            live ? load_elem(v_new, f32, in_row * kHeadDim + 2 * lane + 1) : 0.0;
+    }
+
+    for (int tt = 0; tt < 2; ++tt) {
+        if (tt == 1) __syncthreads();   // every search of the key table is done
+        const uint4* src = reinterpret_cast<const uint4*>(tt == 0 ? cb_k : cb_v) +
+                           static_cast<size_t>(g) * kEnc8Ent;
+        for (int i = tid; i < kEnc8Ent; i += kEncThreads) {
+            const uint4 c = src[i];
+            reinterpret_cast<uint4*>(ctab)[i] = c;
+            const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+            float nn = 0.f;   // the squares of fp16 values are exact in fp32
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = half_bits_to_float(static_cast<uint16_t>(w[j] & 0xffffu));
+                const float hi = half_bits_to_float(static_cast<uint16_t>(w[j] >> 16));
+                nn += lo * lo;
+                nn += hi * hi;
+            }
+            cu[i] = nn * kBoundUp;
+            cd[i] = nn * kBoundDown;
+        }
+        __syncthreads();
+        // wave w: the 16 sub-vectors of token w (position lane % 16)
+        const int tok = wave, pos = lane & 15;
+        static_assert(kEncWaves == kEncTok && kEnc8Pos == 16, "one token per wave");
+        if (tok < ntok) {   // uniform
+            const double* x = &xs[tt][tok][8 * pos];
+            const int gq = lane >> 4;
+            const float b0 = -2.f * static_cast<float>(x[2 * gq]);
+            const float b1 = -2.f * static_cast<float>(x[2 * gq + 1]);
+            float xx = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = static_cast<float>(x[j]);
+                xx += v * v;
+            }
+            double xd[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xd[j] = x[j];
+            const auto exact = [&](uint32_t nc) {
+                return sqdist8_f64(xd, reinterpret_cast<const uint4*>(ctab)[nc]);
+            };
+            const uint32_t c = nearest16_d8<kEnc8Ent>(ctab, cu, cd, b0, b1, row_bound(xx), lane,
+                                                      exact);
+            if (lane < 16) code[tt][tok][pos] = static_cast<uint16_t>(c);
+        }
+    }
+    __syncthreads();
+
+    // the live tokens' rows: byte j holds bits [8j, 8j + 8) of the 12-bit stream
+    const size_t out0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + cur_len + t0;
+    for (int e = tid; e < 2 * ntok * kEnc8Row; e += kEncThreads) {
+        const int tt = e / (ntok * kEnc8Row), rem = e % (ntok * kEnc8Row);
+        const int t = rem / kEnc8Row, j = rem % kEnc8Row;
+        const int bit = 8 * j, i0 = bit / 12, sh = bit % 12;
+        uint32_t v = static_cast<uint32_t>(code[tt][t][i0]) >> sh;
+        if (sh > 4) v |= static_cast<uint32_t>(code[tt][t][i0 + 1]) << (12 - sh);
+        (tt == 0 ? codes_k : codes_v)[(out0 + t) * kEnc8Row + j] = static_cast<uint8_t>(v & 0xffu);
+    }
+}
+
+hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, const void* v_new,
+                                bool kv_f32, const float* lambda, const uint16_t* cb_k,
+                                const uint16_t* cb_v, uint8_t* codes_k, uint8_t* codes_v,
+                                int batch, int num_kv_heads, int capacity, int cur_len,
+                                int num_new, hipStream_t stream) {
     const dim3 grid((num_new + kEncTok - 1) / kEncTok, num_kv_heads, batch);
-    if (k_bits == 8)
+    if (sub_dim == 8)
+        hipLaunchKernelGGL(encode_append8_kernel, grid, dim3(kEncThreads), 0, stream, k_new, v_new,
+                           kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v, num_kv_heads,
+                           capacity, cur_len, num_new);
+    else if (k_bits == 8)
         hipLaunchKernelGGL(encode_append_kernel<8>, grid, dim3(kEncThreads), 0, stream, k_new,
                            v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
                            num_kv_heads, capacity, cur_len, num_new);

@@ -42,19 +42,22 @@ struct AppendArgs {
 // Split-K decode attention over the VQ cache on the matrix cores: one
 // partial (m, l, o) per (sequence, query head, split), plus the new token's
 // when appending.
-hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bool q_f32,
-                               const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
-                               const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                               const AppendArgs& append, hipStream_t stream);
+// sub_dim 4 (k_bits 8 or 12, 8-bit values) or 8 (12-bit keys and values).
+hipError_t launch_vq_attention(const AttnShape& s, int k_bits, int sub_dim, const void* q,
+                               bool q_f32, const float* lambda, const uint16_t* cb_k,
+                               const uint16_t* cb_v, const uint8_t* codes_k,
+                               const uint8_t* codes_v, Partials part, const AppendArgs& append,
+                               hipStream_t stream);
 
 // out[bh][:] from the num_partials partials of every (sequence, query head) bh.
 hipError_t launch_merge_partials(int batch, int num_q_heads, int num_partials, Partials part,
                                  float* out, hipStream_t stream);
 
-hipError_t launch_encode_append(int k_bits, const void* k_new, const void* v_new, bool kv_f32,
-                                const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
-                                uint8_t* codes_k, uint8_t* codes_v, int batch, int num_kv_heads,
-                                int capacity, int cur_len, int num_new, hipStream_t stream);
+hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, const void* v_new,
+                                bool kv_f32, const float* lambda, const uint16_t* cb_k,
+                                const uint16_t* cb_v, uint8_t* codes_k, uint8_t* codes_v,
+                                int batch, int num_kv_heads, int capacity, int cur_len,
+                                int num_new, hipStream_t stream);
 
 hipError_t launch_fp16_attention_splits(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                                         const uint16_t* v, Partials part, hipStream_t stream);

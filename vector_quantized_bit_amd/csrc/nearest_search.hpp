@@ -57,14 +57,20 @@ __device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * 
 // lanes; 0xffffffff only for a sub-vector with no candidate, which finite
 // inputs never produce).  Every lane of the wave must be active; all
 // branches below are uniform.
-template <int NENT, typename Exact>
-__device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
-                                              const float* __restrict__ ccu,
-                                              const float* __restrict__ ccd, float b, float ex,
-                                              int lane, Exact exact) {
+//
+// SUB = 8 (nearest16_d8 below): the centroids stay fp16 in LDS as the
+// codebook stores them, c [NENT][8], and are widened to fp32 for the A
+// operand; the sub-vector enters as -2x (exact scaling).  Two K = 4 steps
+// per 16 centroids, channels 2 g and 2 g + 1 of lane group g = lane / 16 (one
+// 32-bit LDS read per lane gives both), accumulate ||c||^2 (1 +- 2^-16) -
+// 2 x.c.  With 8 products the score error is within about 16 u (||x||^2 +
+// ||c||^2), so the same bound keeps a 16x margin.
+template <int NENT, int SUB, typename Block, typename Exact>
+__device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu,
+                                                   const float* __restrict__ ccd, Block block,
+                                                   float ex, int lane, Exact exact) {
     constexpr int kUnroll = 8;
     static_assert(NENT % (16 * kUnroll) == 0, "whole unrolled groups");
-    const float* acol = m2 + (lane >> 4) * kSearchStride<NENT> + (lane & 15);
     const int q4 = 4 * (lane >> 4);   // this lane's first centroid row in a block
     const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(ccu + q4);
     const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(ccd + q4);
@@ -76,8 +82,7 @@ __device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
         f32x4_t d[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(acol[(blk + u) * 16], b,
-                                                        ucol[(blk + u) * 4], 0, 0, 0);
+            d[u] = block(blk + u, ucol[(blk + u) * 4]);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
             smin = fminf(smin, fminf(fminf(d[u][0], d[u][1]), fminf(d[u][2], d[u][3])));
@@ -93,8 +98,7 @@ __device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
         f32x4_t d[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(acol[(blk + u) * 16], b,
-                                                        dcol[(blk + u) * 4], 0, 0, 0);
+            d[u] = block(blk + u, dcol[(blk + u) * 4]);
         // the group's last hit as u * 4 + r (an inline constant, 0 .. 31),
         // turned into a centroid row once per group
         const int before = cnt;
@@ -130,8 +134,7 @@ __device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
         bool any = false;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            d[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(acol[(blk + u) * 16], b,
-                                                        dcol[(blk + u) * 4], 0, 0, 0);
+            d[u] = block(blk + u, dcol[(blk + u) * 4]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) any |= d[u][r] <= thr;
         }
@@ -161,6 +164,39 @@ __device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
         }
     }
     return bi;
+}
+
+// d = 4: m2 [4][kSearchStride<NENT>] fp32 -2 fl32(c) by channel; b is this
+// lane's B operand, channel lane / 16 of sub-vector lane % 16.
+template <int NENT, typename Exact>
+__device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
+                                              const float* __restrict__ ccu,
+                                              const float* __restrict__ ccd, float b, float ex,
+                                              int lane, Exact exact) {
+    const float* acol = m2 + (lane >> 4) * kSearchStride<NENT> + (lane & 15);
+    const auto block = [&](int blk, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(acol[blk * 16], b, c, 0, 0, 0);
+    };
+    return nearest16_core<NENT, 4>(ccu, ccd, block, ex, lane, exact);
+}
+
+// d = 8: ctab [NENT][8] fp16 centroids (16 B each, 4-byte aligned); b0, b1
+// are -2x of channels 2 (lane / 16) and 2 (lane / 16) + 1 of sub-vector
+// lane % 16.
+template <int NENT, typename Exact>
+__device__ __forceinline__ uint32_t nearest16_d8(const uint16_t* __restrict__ ctab,
+                                                 const float* __restrict__ ccu,
+                                                 const float* __restrict__ ccd, float b0, float b1,
+                                                 float ex, int lane, Exact exact) {
+    const uint32_t* acol = reinterpret_cast<const uint32_t*>(ctab) + (lane & 15) * 4 + (lane >> 4);
+    const auto block = [&](int blk, f32x4_t c) {
+        const uint32_t w = acol[blk * 64];   // channels 2 g, 2 g + 1 of centroid 16 blk + lane % 16
+        const float a0 = half_bits_to_float(static_cast<uint16_t>(w & 0xffffu));
+        const float a1 = half_bits_to_float(static_cast<uint16_t>(w >> 16));
+        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, d, 0, 0, 0);
+    };
+    return nearest16_core<NENT, 8>(ccu, ccd, block, ex, lane, exact);
 }
 
 }  // namespace vqkv

@@ -43,6 +43,8 @@
 //    log-sum-exp.  Merging the splits inside this kernel would need a
 //    device-scope release per workgroup, which writes back the XCD's L2 and
 //    costs more than the extra launch.
+#include <type_traits>
+
 #include "launchers.hpp"
 
 namespace vqkv {
@@ -157,42 +159,42 @@ struct KChunk<12> {
     }
 };
 
+// Four 12-bit codes, positions 4 j .. 4 j + 3, of one 24-byte row of the
+// d = 8 layout (16 codes of 12 bits): bytes [6 j, 6 j + 6).  They are read as
+// the dword-aligned 8 bytes at 12 (j / 2) + 4 (j % 2) and shifted down by
+// 16 (j % 2) bits when used (a shift at load time would wait for the load).
+struct Chunk8 {
+    uint32_t x, y;
+    __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+        x = v[0];
+        y = v[1];
+    }
+    // the 4 codes, given the lane's shift (0 or 16)
+    __device__ void codes(uint32_t sh, uint32_t c[4]) const {
+        const uint32_t lo = __builtin_amdgcn_alignbit(y, x, sh), hi = y >> sh;
+        c[0] = lo & 0xfffu;
+        c[1] = (lo >> 12) & 0xfffu;
+        c[2] = __builtin_amdgcn_alignbit(hi, lo, 24) & 0xfffu;
+        c[3] = (hi >> 4) & 0xfffu;
+    }
+};
+
 }  // namespace
 
-// The appended token of one (sequence, KV head), handled by one extra
-// workgroup of the split kernel while the others attend over the cached
-// tokens (VecInfer page, Method details, "VQ KV cache in attention": each
-// newly arrived key takes the online dual transform k~ = k diag(lambda)^-1
-// H_D and is quantised with C_k, its value with C_v, and both are
-// concatenated to the cache before the query attends).
-//  1. Codes: the nearest centroid of each 4-dim sub-vector (Background, VQ
-//     principle), distances in fp64 with every operation rounded separately,
-//     ties to the lowest index: the decisions of vq_encode_append.  Thread
-//     (slice, pos) scans centroids slice, slice + 32, ... of sub-vector pos;
-//     the 32 slices are combined by the lexicographic (distance, index)
-//     minimum.  The codes are written to the cache slot append_pos.
-//  2. Its attention partial, as one more split of one token: m = x (its
-//     base-2 score), l = 1, o = its dequantised value, at split index `slot`.
-// LDS: the codebooks unreplicated in `tab` (keys at 0, values at 32 KiB),
-// the scratch of the combination in `scratch` (the p buffers).
-template <int G, int KBITS>
-__device__ __forceinline__ void new_token_workgroup(
-    const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
-    const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads,
-    int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v, Partials part,
-    int part_stride, int slot, uint8_t* tab, uint8_t* scratch, double (*xnew)[kHeadDim],
-    uint32_t (*newc)[kNumSub]) {
-    constexpr int KENT = 1 << KBITS;
-    constexpr int kVtab = 32768;
+// Inputs of the new-token workgroups: q~ of head `wave` (fp32, base-2 score
+// scale, two elements per lane) for waves < G; the new key transformed,
+// k diag(lambda)^-1 H_D in fp64 (wave 8), and the new value as is (wave 9),
+// into xnew.
+template <int G>
+__device__ __forceinline__ void new_token_inputs(const void* q, int q_f32, const float* lambda,
+                                                 const void* k_new, const void* v_new, int kv_f32,
+                                                 int num_q_heads, int num_kv_heads, int wave,
+                                                 int lane, float& x0, float& x1,
+                                                 double (*xnew)[kHeadDim]) {
     const int g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
-    const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
-    for (int i = tid; i < KENT; i += kThreads) reinterpret_cast<uint2*>(tab)[i] = ksrc[i];
-    if (tid < 256) reinterpret_cast<uint2*>(tab + kVtab)[tid] = vsrc[tid];
-
-    // q~ of head `wave` (fp32, base-2 score scale), two elements per lane
-    float x0 = 0.f, x1 = 0.f;
+    x0 = 0.f;
+    x1 = 0.f;
     if (wave < G) {
         const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + wave;
         const uint32_t* qw = reinterpret_cast<const uint32_t*>(q) +
@@ -231,6 +233,43 @@ __device__ __forceinline__ void new_token_workgroup(
         xnew[wave - 8][2 * lane] = y0;
         xnew[wave - 8][2 * lane + 1] = y1;
     }
+}
+
+// The appended token of one (sequence, KV head), handled by one extra
+// workgroup of the split kernel while the others attend over the cached
+// tokens (VecInfer page, Method details, "VQ KV cache in attention": each
+// newly arrived key takes the online dual transform k~ = k diag(lambda)^-1
+// H_D and is quantised with C_k, its value with C_v, and both are
+// concatenated to the cache before the query attends).
+//  1. Codes: the nearest centroid of each 4-dim sub-vector (Background, VQ
+//     principle), distances in fp64 with every operation rounded separately,
+//     ties to the lowest index: the decisions of vq_encode_append.  Thread
+//     (slice, pos) scans centroids slice, slice + 32, ... of sub-vector pos;
+//     the 32 slices are combined by the lexicographic (distance, index)
+//     minimum.  The codes are written to the cache slot append_pos.
+//  2. Its attention partial, as one more split of one token: m = x (its
+//     base-2 score), l = 1, o = its dequantised value, at split index `slot`.
+// LDS: the codebooks unreplicated in `tab` (keys at 0, values at 32 KiB),
+// the scratch of the combination in `scratch` (the p buffers).
+template <int G, int KBITS>
+__device__ __forceinline__ void new_token_workgroup(
+    const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+    const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads,
+    int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v, Partials part,
+    int part_stride, int slot, uint8_t* tab, uint8_t* scratch, double (*xnew)[kHeadDim],
+    uint32_t (*newc)[kNumSub]) {
+    constexpr int KENT = 1 << KBITS;
+    constexpr int kVtab = 32768;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
+    const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
+    for (int i = tid; i < KENT; i += kThreads) reinterpret_cast<uint2*>(tab)[i] = ksrc[i];
+    if (tid < 256) reinterpret_cast<uint2*>(tab + kVtab)[tid] = vsrc[tid];
+
+    float x0, x1;
+    new_token_inputs<G>(q, q_f32, lambda, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, wave,
+                        lane, x0, x1, xnew);
     __syncthreads();
 
     // 1. codes
@@ -314,6 +353,123 @@ __device__ __forceinline__ void new_token_workgroup(
         const uint2 kc = reinterpret_cast<const uint2*>(tab)[newc[0][j]];
         const uint2 vc = reinterpret_cast<const uint2*>(tab + kVtab)[newc[1][j]];
         const uint32_t kw = comp ? kc.y : kc.x, vw = comp ? vc.y : vc.x;
+        const float x = wave_sum(x0 * half_bits_to_float(kw & 0xffffu) +
+                                 x1 * half_bits_to_float(kw >> 16));
+        const size_t pi = (static_cast<size_t>(b) * num_q_heads + g * G + wave) * part_stride + slot;
+        part.o[pi * kHeadDim + 2 * lane] = half_bits_to_float(vw & 0xffffu);
+        part.o[pi * kHeadDim + 2 * lane + 1] = half_bits_to_float(vw >> 16);
+        if (lane == 0) {
+            part.m[pi] = x;
+            part.l[pi] = 1.f;
+        }
+    }
+}
+
+// The appended token in the d = 8 layout (16 sub-vectors of 8 channels; C_k
+// and C_v of 4096 entries; 24-byte rows of 12-bit codes), with the steps and
+// decisions of new_token_workgroup.  Thread (slice, pos) scans centroids
+// slice, slice + 64, ... of sub-vector pos = tid % 16 (64 slices); lanes l,
+// l ^ 16, l ^ 32, l ^ 48 of a wave hold 4 slices of one position and are
+// combined first, then the 16 waves.  LDS: C_k in `tab`, C_v 64 KiB above.
+template <int G>
+__device__ __forceinline__ void new_token_workgroup8(
+    const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+    const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads,
+    int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v, Partials part,
+    int part_stride, int slot, uint8_t* tab, uint8_t* scratch, double (*xnew)[kHeadDim],
+    uint32_t (*newc)[kNumSub]) {
+    constexpr int kEnt = 4096, kPos = kHeadDim / 8, kRow = kPos * 12 / 8;   // 16 codes, 24 B
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint4* ksrc = reinterpret_cast<const uint4*>(cb_k) + static_cast<size_t>(g) * kEnt;
+    const uint4* vsrc = reinterpret_cast<const uint4*>(cb_v) + static_cast<size_t>(g) * kEnt;
+    const uint4* kt = reinterpret_cast<const uint4*>(tab);
+    const uint4* vt = reinterpret_cast<const uint4*>(tab + kTable);
+    for (int i = tid; i < kEnt; i += kThreads) {
+        reinterpret_cast<uint4*>(tab)[i] = ksrc[i];
+        reinterpret_cast<uint4*>(tab + kTable)[i] = vsrc[i];
+    }
+    float x0, x1;
+    new_token_inputs<G>(q, q_f32, lambda, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, wave,
+                        lane, x0, x1, xnew);
+    __syncthreads();
+
+    // 1. codes
+    const int pos = tid & (kPos - 1), slice = tid / kPos;
+    double xk[8], xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        xk[i] = xnew[0][8 * pos + i];
+        xv[i] = xnew[1][8 * pos + i];
+    }
+    double dk = INFINITY, dv = INFINITY;
+    uint32_t ik = 0, iv = 0;
+    for (int c = slice; c < kEnt; c += kThreads / kPos) {
+        const double d1 = sqdist8_f64(xk, kt[c]);
+        if (d1 < dk) {
+            dk = d1;
+            ik = static_cast<uint32_t>(c);
+        }
+        const double d2 = sqdist8_f64(xv, vt[c]);
+        if (d2 < dv) {
+            dv = d2;
+            iv = static_cast<uint32_t>(c);
+        }
+    }
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        const int m = step == 0 ? 16 : 32;
+        const double dk2 = __shfl_xor(dk, m, kWave), dv2 = __shfl_xor(dv, m, kWave);
+        const uint32_t ik2 = __shfl_xor(ik, m, kWave), iv2 = __shfl_xor(iv, m, kWave);
+        if (nearer(dk2, ik2, dk, ik)) {
+            dk = dk2;
+            ik = ik2;
+        }
+        if (nearer(dv2, iv2, dv, iv)) {
+            dv = dv2;
+            iv = iv2;
+        }
+    }
+    // [tensor][wave][pos]: lanes 0..15 report keys, 16..31 values
+    double* sd = reinterpret_cast<double*>(scratch);
+    uint32_t* si = reinterpret_cast<uint32_t*>(sd + 2 * kWaves * kPos);
+    if (lane < 2 * kPos) {
+        const int tsel = lane / kPos;
+        sd[(tsel * kWaves + wave) * kPos + pos] = tsel ? dv : dk;
+        si[(tsel * kWaves + wave) * kPos + pos] = tsel ? iv : ik;
+    }
+    __syncthreads();
+    if (tid < 2 * kPos) {
+        const int tsel = tid / kPos;
+        double d0 = sd[tsel * kWaves * kPos + pos];
+        uint32_t i0 = si[tsel * kWaves * kPos + pos];
+        for (int w = 1; w < kWaves; ++w) {
+            const double d = sd[(tsel * kWaves + w) * kPos + pos];
+            const uint32_t i = si[(tsel * kWaves + w) * kPos + pos];
+            if (nearer(d, i, d0, i0)) {
+                d0 = d;
+                i0 = i;
+            }
+        }
+        newc[tsel][pos] = i0;
+    }
+    __syncthreads();
+    const size_t row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + append_pos;
+    if (tid < 2 * kRow) {   // byte j of a row holds bits [8j, 8j + 8) of the 12-bit stream
+        const int tsel = tid / kRow, j = tid % kRow;
+        const int bit = 8 * j, i0 = bit / 12, sh = bit % 12;
+        uint32_t v = newc[tsel][i0] >> sh;
+        if (sh > 4) v |= newc[tsel][i0 + 1] << (12 - sh);
+        (tsel ? new_codes_v : new_codes_k)[row * kRow + j] = static_cast<uint8_t>(v & 0xffu);
+    }
+
+    // 2. the one-token partial of each query head: lane l holds dims 2l, 2l + 1,
+    //    halves 2 (l % 4), + 1 of sub-vector l / 4
+    if (wave < G) {
+        const int j = lane >> 2, word = lane & 3;
+        const uint4 kc = kt[newc[0][j]], vc = vt[newc[1][j]];
+        const uint32_t kw = word == 0 ? kc.x : (word == 1 ? kc.y : (word == 2 ? kc.z : kc.w));
+        const uint32_t vw = word == 0 ? vc.x : (word == 1 ? vc.y : (word == 2 ? vc.z : vc.w));
         const float x = wave_sum(x0 * half_bits_to_float(kw & 0xffffu) +
                                  x1 * half_bits_to_float(kw >> 16));
         const size_t pi = (static_cast<size_t>(b) * num_q_heads + g * G + wave) * part_stride + slot;
@@ -443,7 +599,7 @@ __device__ __forceinline__ void window_workgroup(
     }
 }
 
-template <int G, int KBITS>
+template <int G, int KBITS, int SUB>
 __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const void* __restrict__ q, int q_f32, const float* __restrict__ lambda,
     const uint16_t* __restrict__ cb_k, const uint16_t* __restrict__ cb_v,
@@ -458,7 +614,13 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // the softmax packs a tile's two 16-token blocks into one set of lanes
     constexpr bool kPack = G <= 4;
     constexpr int kSb = kPack ? 1 : 2;   // 16-token score blocks per lane and tile
-    constexpr int KROW = kNumSub * KBITS / 8;
+    // SUB = 8: the 1.5-bit layout, 16 sub-vectors of 8 channels per vector,
+    // 4096-entry C_k and C_v (64 KiB each, unreplicated), 24-byte rows of
+    // 12-bit codes for K and V
+    constexpr bool kD8 = SUB == 8;
+    static_assert(SUB == 4 || (SUB == 8 && KBITS == 12), "d = 4, or d = 8 with 12-bit codes");
+    constexpr int KROW = kD8 ? 24 : kNumSub * KBITS / 8;
+    constexpr int VROW = kD8 ? 24 : kNumSub;
 
     __shared__ __attribute__((aligned(16))) uint8_t tab[2 * kTable];       // keys | values
     __shared__ __attribute__((aligned(16))) uint2 pbuf[kWaves][kTok * 4];  // [token][16 rows] fp16
@@ -479,10 +641,17 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         return;
     }
     if (append_pos >= 0 && split == num_splits) {   // the extra, new-token workgroup
-        new_token_workgroup<G, KBITS>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
-                                      num_q_heads, num_kv_heads, capacity, append_pos,
-                                      new_codes_k, new_codes_v, part, part_stride, num_splits,
-                                      tab, reinterpret_cast<uint8_t*>(&pbuf[0][0]), xnew, newc);
+        if constexpr (kD8)
+            new_token_workgroup8<G>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
+                                    num_q_heads, num_kv_heads, capacity, append_pos, new_codes_k,
+                                    new_codes_v, part, part_stride, num_splits, tab,
+                                    reinterpret_cast<uint8_t*>(&pbuf[0][0]), xnew, newc);
+        else
+            new_token_workgroup<G, KBITS>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
+                                          num_q_heads, num_kv_heads, capacity, append_pos,
+                                          new_codes_k, new_codes_v, part, part_stride,
+                                          num_splits, tab,
+                                          reinterpret_cast<uint8_t*>(&pbuf[0][0]), xnew, newc);
         return;
     }
     const int grp = lane >> 4, n = lane & 15;
@@ -494,12 +663,17 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(codes_k + row0 * KROW), 0, t_len * KROW, kBufferWord3);
     const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(codes_v + row0 * kNumSub), 0, t_len * kNumSub, kBufferWord3);
-    // per-lane byte offsets of the chunks inside a tile
-    const uint32_t koff0 = static_cast<uint32_t>(n * KROW + (KBITS == 8 ? 8 : 12) * grp);
+        const_cast<uint8_t*>(codes_v + row0 * VROW), 0, t_len * VROW, kBufferWord3);
+    // per-lane byte offsets of the chunks inside a tile (d = 8: the dword-
+    // aligned 8 bytes that hold codes 4 j .. 4 j + 3, and the shift to them)
+    const uint32_t koff0 = static_cast<uint32_t>(
+        n * KROW + (kD8 ? 12 * (grp >> 1) + 4 * (grp & 1) : (KBITS == 8 ? 8 : 12) * grp));
     const uint32_t koff1 = koff0 + 16 * KROW;
-    const uint32_t voff0 = static_cast<uint32_t>((8 * grp + kq) * kNumSub + 8 * aq4);
-    const uint32_t voff1 = voff0 + 4 * kNumSub;
+    const uint32_t voff0 = static_cast<uint32_t>(
+        (8 * grp + kq) * VROW + (kD8 ? 12 * (aq4 >> 1) + 4 * (aq4 & 1) : 8 * aq4));
+    const uint32_t voff1 = voff0 + 4 * VROW;
+    const uint32_t ksh = 16u * static_cast<uint32_t>(grp & 1);   // d = 8 only
+    const uint32_t vsh = 16u * static_cast<uint32_t>(aq4 & 1);
 
     // ---- prologue ----------------------------------------------------------
     if (tid == 0) tile_ctr = kWaves;   // tiles 0 .. kWaves-1 go to waves 0 .. kWaves-1
@@ -512,7 +686,16 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
     uint2 centroid;
     uint2 kcent[KBITS == 8 ? 1 : 4];
-    if constexpr (KBITS == 8) {
+    uint4 cent8[kD8 ? 8 : 1];   // d = 8: entries tid + 1024 i of C_k (i < 4), C_v (i >= 4)
+    if constexpr (kD8) {
+        const uint4* k8 = reinterpret_cast<const uint4*>(cb_k) + static_cast<size_t>(g) * 4096;
+        const uint4* v8 = reinterpret_cast<const uint4*>(cb_v) + static_cast<size_t>(g) * 4096;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cent8[i] = k8[tid + i * kThreads];
+            cent8[4 + i] = v8[tid + i * kThreads];
+        }
+    } else if constexpr (KBITS == 8) {
         // thread: code = tid / 4, table = (tid / 2) % 2, slots 16 (tid % 2) .. + 15
         centroid = ((tid >> 1) & 1) ? vsrc[tid >> 2] : ksrc[tid >> 2];
     } else {
@@ -528,19 +711,37 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint32_t qw0 = qw[0];
     const uint32_t qw1 = qw[q_f32 ? 1 : 0];
     const float2 lam2 = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
-    KChunk<KBITS> kA[2];
-    uint2 vA[2];
+    using KC = std::conditional_t<kD8, Chunk8, KChunk<KBITS>>;
+    using VC = std::conditional_t<kD8, Chunk8, uint2>;
+    KC kA[2];
+    VC vA[2];
     // (the whole offset goes in the VGPR operand: the buffer range check
     // covers the VGPR offset, not the scalar one)
-    auto load_tile = [&](int rel, KChunk<KBITS>* kk_, uint2* vv_) {
+    auto load_k = [&](int rel, KC* kk_) {
         const uint32_t ks = static_cast<uint32_t>(rel * KROW);
-        const uint32_t vs = static_cast<uint32_t>(rel * kNumSub);
-        kk_[0].load(krsrc, koff0 + ks, 0);
-        kk_[1].load(krsrc, koff1 + ks, 0);
-        const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff0 + vs, 0, 0);
-        const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff1 + vs, 0, 0);
-        vv_[0] = make_uint2(v0[0], v0[1]);
-        vv_[1] = make_uint2(v1[0], v1[1]);
+        if constexpr (kD8) {
+            kk_[0].load(krsrc, koff0 + ks);
+            kk_[1].load(krsrc, koff1 + ks);
+        } else {
+            kk_[0].load(krsrc, koff0 + ks, 0);
+            kk_[1].load(krsrc, koff1 + ks, 0);
+        }
+    };
+    auto load_v = [&](int rel, VC* vv_) {
+        const uint32_t vs = static_cast<uint32_t>(rel * VROW);
+        if constexpr (kD8) {
+            vv_[0].load(vrsrc, voff0 + vs);
+            vv_[1].load(vrsrc, voff1 + vs);
+        } else {
+            const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff0 + vs, 0, 0);
+            const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff1 + vs, 0, 0);
+            vv_[0] = make_uint2(v0[0], v0[1]);
+            vv_[1] = make_uint2(v1[0], v1[1]);
+        }
+    };
+    auto load_tile = [&](int rel, KC* kk_, VC* vv_) {
+        load_k(rel, kk_);
+        load_v(rel, vv_);
     };
     load_tile(wave * kTok, kA, vA);   // past the split's end: range-checked, reads zeros
     __builtin_amdgcn_sched_barrier(0);   // keep the table writes (and their wait) below
@@ -553,7 +754,13 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         // half row hits the same four banks, and the table build took longer
         // than the rest of the prologue.
         const int rot = tid >> 1;
-        if constexpr (KBITS == 8) {
+        if constexpr (kD8) {   // C_k then C_v, 16-byte entries, stored once
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                reinterpret_cast<uint4*>(tab)[tid + i * kThreads] = cent8[i];
+                reinterpret_cast<uint4*>(tab + kTable)[tid + i * kThreads] = cent8[4 + i];
+            }
+        } else if constexpr (KBITS == 8) {
             uint4* dst = reinterpret_cast<uint4*>(tab + ((tid >> 1) & 1) * kTable +
                                                   (tid >> 2) * 256 + (tid & 1) * 128);
 #pragma unroll
@@ -635,9 +842,27 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint32_t kslot = static_cast<uint32_t>(lane & 31) * 8;               // key table
     const uint32_t vslot = 0x10000u | (static_cast<uint32_t>(lane & 31) * 8);  // value table
 
-    auto compute_tile = [&](int rel_, KChunk<KBITS>* kc, uint2* vc, int nrel) {
+    auto compute_tile = [&](int rel_, KC* kc, VC* vc, int nrel) {
         // ---- scores: 2 blocks of 16 tokens, 4 K-steps of 32 dims ------------
         float4_t sacc[2];
+        if constexpr (kD8) {
+            // K-step kk of lane (16 grp + n): dims 32 grp + 8 kk .. + 7 of its
+            // token = the centroid of code kk of its chunk, one 16-byte gather
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                uint32_t c[4];
+                kc[sb].codes(ksh, c);
+                half8_t kg[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    kg[kk] = *reinterpret_cast<const half8_t*>(tab + (c[kk] << 4));
+                sacc[sb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qr[kk], kg[kk], sacc[sb],
+                                                                      0, 0, 0);
+            }
+        } else
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             sacc[sb] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -663,11 +888,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         }
 
         __builtin_amdgcn_sched_barrier(0);
-        {   // this tile's key codes are consumed: the next tile's go into the same registers
-            const uint32_t ks = static_cast<uint32_t>(nrel * KROW);
-            kc[0].load(krsrc, koff0 + ks, 0);
-            kc[1].load(krsrc, koff1 + ks, 0);
-        }
+        // this tile's key codes are consumed: the next tile's go into the same registers
+        load_k(nrel, kc);
         __builtin_amdgcn_sched_barrier(0);
         // ---- online softmax (base 2) -----------------------------------------
         // With G <= 4 every head's rows sit in lanes 0-31, so the scores of
@@ -747,6 +969,28 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 
         // ---- values: 8 N-tiles of 16 channels, gathered 2 tiles at a time ------
         // N-tile c, column 4a + e is channel 4 (8a + c) + e = 32 a + 4 c + e
+        if constexpr (kD8) {
+            // channel 32 a + 4 c + e is element 4 (c % 2) + e of the centroid
+            // of code c / 2 of the chunk (positions 4 a ..): the fetching lane
+            // points the transposing read at that half of the 16-byte entry
+            uint32_t c0[4], c1[4];
+            vc[0].codes(vsh, c0);
+            vc[1].codes(vsh, c1);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const uint32_t a0 = kTable + (c0[q4] << 4), a1 = kTable + (c1[q4] << 4);
+                half4_t x[2][2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    x[i][0] = read_tr16(tab + a0 + 8 * i);
+                    x[i][1] = read_tr16(tab + a1 + 8 * i);
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    oacc[2 * q4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        ap, cat(x[i][0], x[i][1]), oacc[2 * q4 + i], 0, 0, 0);
+            }
+        } else
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const uint32_t w0 = (q4 < 2) ? vc[0].x : vc[0].y;
@@ -769,13 +1013,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
                     ap, cat(x[i][0], x[i][1]), oacc[2 * q4 + i], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        {   // and the value codes
-            const uint32_t vs = static_cast<uint32_t>(nrel * kNumSub);
-            const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff0 + vs, 0, 0);
-            const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff1 + vs, 0, 0);
-            vc[0] = make_uint2(v0[0], v0[1]);
-            vc[1] = make_uint2(v1[0], v1[1]);
-        }
+        load_v(nrel, vc);   // and the value codes
     };
 
     // Tiles are handed out from an LDS counter as waves become free: the SIMD
@@ -874,7 +1112,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 
 namespace {
 
-template <int KBITS>
+template <int KBITS, int SUB>
 hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q, bool q_f32,
                          const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                          const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
@@ -887,7 +1125,7 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
     const dim3 full(grid.x + (app ? 1 : 0), grid.y, grid.z);
 #define VQKV_LAUNCH(GG)                                                                       \
     case GG:                                                                                  \
-        hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS>), full, dim3(kThreads), 0,    \
+        hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS, SUB>), full, dim3(kThreads), 0, \
                            stream, q, q_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,   \
                            s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
                            s.num_splits, s.tokens_per_split, part, ap.k_new, ap.v_new,        \
@@ -912,16 +1150,20 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
 
 }  // namespace
 
-hipError_t launch_vq_attention(const AttnShape& s, int k_bits, const void* q, bool q_f32,
-                               const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
-                               const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
-                               const AppendArgs& append, hipStream_t stream) {
+hipError_t launch_vq_attention(const AttnShape& s, int k_bits, int sub_dim, const void* q,
+                               bool q_f32, const float* lambda, const uint16_t* cb_k,
+                               const uint16_t* cb_v, const uint8_t* codes_k,
+                               const uint8_t* codes_v, Partials part, const AppendArgs& append,
+                               hipStream_t stream) {
     const dim3 grid(s.num_splits, s.num_kv_heads, s.batch);
     const int group = s.num_q_heads / s.num_kv_heads;
-    return (k_bits == 8) ? launch_mfma_g<8>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
-                                            codes_k, codes_v, part, append, stream)
-                         : launch_mfma_g<12>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
-                                             codes_k, codes_v, part, append, stream);
+    if (sub_dim == 8)
+        return launch_mfma_g<12, 8>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
+                                    codes_v, part, append, stream);
+    return (k_bits == 8) ? launch_mfma_g<8, 4>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
+                                               codes_k, codes_v, part, append, stream)
+                         : launch_mfma_g<12, 4>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
+                                                codes_k, codes_v, part, append, stream);
 }
 
 }  // namespace vqkv

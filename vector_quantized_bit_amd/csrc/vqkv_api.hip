@@ -42,12 +42,21 @@ int check_layout(const vq_layout* L) {
     if (L == nullptr) return fail(VQ_ERR_INVALID_ARG, "layout is NULL");
     if (L->head_dim != vqkv::kHeadDim)
         return fail(VQ_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", L->head_dim);
-    if (L->sub_dim != vqkv::kSubDim)
-        return fail(VQ_ERR_UNSUPPORTED, "sub_dim %d unsupported (only 4)", L->sub_dim);
-    if (L->k_code_bits != 8 && L->k_code_bits != 12)
-        return fail(VQ_ERR_UNSUPPORTED, "k_code_bits %d unsupported (8 or 12)", L->k_code_bits);
-    if (L->v_code_bits != 8)
-        return fail(VQ_ERR_UNSUPPORTED, "v_code_bits %d unsupported (only 8)", L->v_code_bits);
+    if (L->sub_dim != 4 && L->sub_dim != 8)
+        return fail(VQ_ERR_UNSUPPORTED, "sub_dim %d unsupported (4 or 8)", L->sub_dim);
+    if (L->sub_dim == 8) {
+        if (L->k_code_bits != 12 || L->v_code_bits != 12)
+            return fail(VQ_ERR_UNSUPPORTED,
+                        "sub_dim 8 takes 12-bit K and V codes (got k_code_bits %d, v_code_bits %d)",
+                        L->k_code_bits, L->v_code_bits);
+    } else {
+        if (L->k_code_bits != 8 && L->k_code_bits != 12)
+            return fail(VQ_ERR_UNSUPPORTED, "k_code_bits %d unsupported (8 or 12)",
+                        L->k_code_bits);
+        if (L->v_code_bits != 8)
+            return fail(VQ_ERR_UNSUPPORTED, "v_code_bits %d unsupported with sub_dim 4 (only 8)",
+                        L->v_code_bits);
+    }
     if (L->num_kv_heads < 1 || L->num_kv_heads > 65535)
         return fail(VQ_ERR_INVALID_ARG, "num_kv_heads %d out of range [1, 65535]", L->num_kv_heads);
     if (L->capacity < 1) return fail(VQ_ERR_INVALID_ARG, "capacity %d < 1", L->capacity);
@@ -171,7 +180,7 @@ int vq_encode_append(const vq_layout* layout, const void* k_new, const void* v_n
     VQ_REQUIRE_PTR(codes_k);
     VQ_REQUIRE_PTR(codes_v);
     if (num_new == 0) return ok();
-    return hip_status(vqkv::launch_encode_append(layout->k_code_bits, k_new, v_new,
+    return hip_status(vqkv::launch_encode_append(layout->k_code_bits, layout->sub_dim, k_new, v_new,
                                                  kv_dtype == VQ_F32, lambda, cb_k, cb_v, codes_k,
                                                  codes_v, batch, layout->num_kv_heads,
                                                  layout->capacity, cur_len, num_new,
@@ -263,7 +272,7 @@ int vq_decode_attention_partials(const vq_layout* layout, const void* q, int q_d
     const vqkv::Partials part{part_m, part_l, part_o};
     const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
                                 context_len, p.num_splits, p.tokens_per_split};
-    return hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
+    return hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32,
                                                 lambda, cb_k, cb_v, codes_k, codes_v, part,
                                                 vqkv::AppendArgs{},
                                                 static_cast<hipStream_t>(stream)),
@@ -425,7 +434,7 @@ int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
     const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity, cur_len,
                                 p.num_splits, p.tokens_per_split};
     return hip_status(vqkv::launch_vq_attention(
-                          shape, layout->k_code_bits, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                          shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
                           codes_k, codes_v, part,
                           append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v),
                           static_cast<hipStream_t>(stream)),
@@ -453,7 +462,7 @@ int vq_decode_step(const vq_layout* layout, const void* q, int q_dtype, const vo
                                 p.num_splits, p.tokens_per_split};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     st = hip_status(vqkv::launch_vq_attention(
-                        shape, layout->k_code_bits, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                        shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
                         codes_k, codes_v, part,
                         append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v), s),
                     "decode_step launch");
@@ -505,7 +514,7 @@ int vq_decode_step_window(const vq_layout* layout, const void* q, int q_dtype, c
                                 num_codes, p.num_splits, p.tokens_per_split};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     st = hip_status(vqkv::launch_vq_attention(
-                        shape, layout->k_code_bits, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                        shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
                         codes_k, codes_v, part,
                         window_args(k_new, v_new, kv_dtype, num_codes, win_k, win_v, win_len,
                                     win_cap),
@@ -545,7 +554,7 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
     const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity,
                                 context_len, p.num_splits, p.tokens_per_split};
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    st = hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, q, q_dtype == VQ_F32,
+    st = hip_status(vqkv::launch_vq_attention(shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32,
                                               lambda, cb_k, cb_v, codes_k, codes_v, part,
                                               vqkv::AppendArgs{}, s),
                     "decode_attention launch");

@@ -102,6 +102,12 @@ WORKLOADS = {
     5: Workload(5, "qwen2.5-14b-layer-b8-n65536-k3bit", batch=8, num_q_heads=40,
                 num_kv_heads=8, context_len=65536, k_bits=12, v_bits=8,
                 append_tokens=64),
+    # the 1.5-bit layout of the VecInfer page (codebook-size ablation:
+    # 2^12 x 8 x 2 B): 8-dim sub-vectors, 4096-entry C_k and C_v, 12-bit codes
+    6: Workload(6, "llama3.1-8b-layer-b1-n196608-1.5bit", batch=1, num_q_heads=32,
+                num_kv_heads=8, context_len=196608, k_bits=12, v_bits=12, sub_dim=8),
+    7: Workload(7, "tiny-g4-n1024-1.5bit", batch=1, num_q_heads=4, num_kv_heads=1,
+                context_len=1024, k_bits=12, v_bits=12, sub_dim=8, qkv_dtype="f32"),
 }
 
 
@@ -201,8 +207,9 @@ def random_code_rows(config_id: int, b: int, kv_head: int, tensor: str, n: int,
 
 
 def random_codebook(config_id: int, kv_head: int, tensor: str, entries: int,
-                    scale: float, heavy_fraction: float = 0.0) -> np.ndarray:
-    """fp16-valued codebook [entries, SUB_DIM] (returned as float16).
+                    scale: float, heavy_fraction: float = 0.0,
+                    sub_dim: int = SUB_DIM) -> np.ndarray:
+    """fp16-valued codebook [entries, sub_dim] (returned as float16).
 
     Entries are N(0, scale^2); the last ``heavy_fraction`` of the entries
     are scaled by OUTLIER_SCALE, the way centroids of the sub-vectors that
@@ -210,7 +217,7 @@ def random_codebook(config_id: int, kv_head: int, tensor: str, entries: int,
     type of every codebook.
     """
     stream = STREAM_CODEBOOK_K if tensor == "k" else STREAM_CODEBOOK_V
-    c = rng(config_id, 0, kv_head, stream).standard_normal((entries, SUB_DIM)) * scale
+    c = rng(config_id, 0, kv_head, stream).standard_normal((entries, sub_dim)) * scale
     heavy = int(round(entries * heavy_fraction))
     if heavy:
         c[entries - heavy:] *= OUTLIER_SCALE
