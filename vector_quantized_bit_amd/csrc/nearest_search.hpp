@@ -65,46 +65,46 @@ __device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * 
 // 32-bit LDS read per lane gives both), accumulate ||c||^2 (1 +- 2^-16) -
 // 2 x.c.  With 8 products the score error is within about 16 u (||x||^2 +
 // ||c||^2), so the same bound keeps a 16x margin.
-template <int NENT, int SUB, typename Block, typename Exact>
-__device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu,
-                                                   const float* __restrict__ ccd, Block block,
-                                                   float ex, int lane, Exact exact) {
-    constexpr int kUnroll = 8;
-    static_assert(NENT % (16 * kUnroll) == 0, "whole unrolled groups");
-    const int q4 = 4 * (lane >> 4);   // this lane's first centroid row in a block
-    const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(ccu + q4);
-    const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(ccd + q4);
+// The passes over centroid blocks [b0, b1) (16 centroids each; b1 - b0 a
+// multiple of 8).  block(blk, c) is the MFMA score of block blk with
+// accumulator input c; cup(blk) / cdown(blk) give the lane's 4 norm terms
+// ||c||^2 (1 + 2^-16) / (1 - 2^-16).
+constexpr int kSearchUnroll = 8;
 
-    // pass 1: thr = min over c of s(c) + E(c)
+// pass 1: this lane's minimum of s(c) + E(c) (without the ||x||^2 part)
+template <typename Block, typename Cop>
+__device__ __forceinline__ float search_pass1(Block block, Cop cup, int b0, int b1) {
     float smin = INFINITY;
 #pragma nounroll
-    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
-        f32x4_t d[kUnroll];
+    for (int blk = b0; blk < b1; blk += kSearchUnroll) {
+        f32x4_t d[kSearchUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            d[u] = block(blk + u, ucol[(blk + u) * 4]);
+        for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cup(blk + u));
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kSearchUnroll; ++u)
             smin = fminf(smin, fminf(fminf(d[u][0], d[u][1]), fminf(d[u][2], d[u][3])));
     }
-    smin = fminf(smin, lane_partner<16>(smin, lane));
-    smin = fminf(smin, lane_partner<32>(smin, lane));
-    const float thr = smin + ex;
+    return smin;
+}
 
-    // pass 2: each lane counts its candidates and keeps one
-    int cand = -1, cnt = 0;
+// pass 2: how many of this lane's centroids have s(c) - E(c) <= thr, and the
+// row (16 blk + r, without the lane's 4 (lane / 16)) of the last of them
+template <typename Block, typename Cop>
+__device__ __forceinline__ void search_pass2(Block block, Cop cdown, int b0, int b1, float thr,
+                                             int& cnt, int& cand) {
+    cnt = 0;
+    cand = -1;
 #pragma nounroll
-    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
-        f32x4_t d[kUnroll];
+    for (int blk = b0; blk < b1; blk += kSearchUnroll) {
+        f32x4_t d[kSearchUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            d[u] = block(blk + u, dcol[(blk + u) * 4]);
+        for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cdown(blk + u));
         // the group's last hit as u * 4 + r (an inline constant, 0 .. 31),
         // turned into a centroid row once per group
         const int before = cnt;
         int loc = 0;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kSearchUnroll; ++u) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool hit = d[u][r] <= thr;
@@ -114,33 +114,28 @@ __device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu
         }
         cand = cnt != before ? blk * 16 + (loc >> 2) * 16 + (loc & 3) : cand;
     }
-    cnt += static_cast<int>(lane_partner<16>(static_cast<uint32_t>(cnt), lane));
-    cnt += static_cast<int>(lane_partner<32>(static_cast<uint32_t>(cnt), lane));
-    int best = cand < 0 ? -1 : cand + q4;
-    best = max(best, static_cast<int>(lane_partner<16>(static_cast<uint32_t>(best), lane)));
-    best = max(best, static_cast<int>(lane_partner<32>(static_cast<uint32_t>(best), lane)));
+}
 
-    // every sub-vector has exactly one candidate: it is the nearest centroid
-    if (__builtin_amdgcn_ballot_w64(cnt != 1) == 0) return static_cast<uint32_t>(best);
-
-    // some sub-vector has several candidates: fp64 distances for all
-    // candidates of this block (pass 2 again), lexicographic minimum over
-    // the 4 lanes of each sub-vector
-    double bd = INFINITY;
-    uint32_t bi = 0xffffffffu;
+// pass 3: the lexicographic (fp64 distance, index) minimum over this lane's
+// candidates (bd = inf, bi = 0xffffffff when it has none)
+template <typename Block, typename Cop, typename Exact>
+__device__ __forceinline__ void search_pass3(Block block, Cop cdown, int b0, int b1, float thr,
+                                             int q4, Exact exact, double& bd, uint32_t& bi) {
+    bd = INFINITY;
+    bi = 0xffffffffu;
 #pragma nounroll
-    for (int blk = 0; blk < NENT / 16; blk += kUnroll) {
-        f32x4_t d[kUnroll];
+    for (int blk = b0; blk < b1; blk += kSearchUnroll) {
+        f32x4_t d[kSearchUnroll];
         bool any = false;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            d[u] = block(blk + u, dcol[(blk + u) * 4]);
+        for (int u = 0; u < kSearchUnroll; ++u) {
+            d[u] = block(blk + u, cdown(blk + u));
 #pragma unroll
             for (int r = 0; r < 4; ++r) any |= d[u][r] <= thr;
         }
         if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kSearchUnroll; ++u) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if (d[u][r] <= thr) {
@@ -154,6 +149,10 @@ __device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu
             }
         }
     }
+}
+
+// The lexicographic minimum over the 4 lanes of a sub-vector.
+__device__ __forceinline__ void take_lanes16_32(double& bd, uint32_t& bi, int lane) {
 #pragma unroll
     for (int step = 0; step < 2; ++step) {
         const double d2 = step == 0 ? lane_partner<16>(bd, lane) : lane_partner<32>(bd, lane);
@@ -163,8 +162,71 @@ __device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu
             bi = i2;
         }
     }
+}
+
+// Sum and maximum over the 4 lanes of a sub-vector.
+__device__ __forceinline__ int sum_lanes16_32(int x, int lane) {
+    x += static_cast<int>(lane_partner<16>(static_cast<uint32_t>(x), lane));
+    return x + static_cast<int>(lane_partner<32>(static_cast<uint32_t>(x), lane));
+}
+__device__ __forceinline__ int max_lanes16_32(int x, int lane) {
+    x = max(x, static_cast<int>(lane_partner<16>(static_cast<uint32_t>(x), lane)));
+    return max(x, static_cast<int>(lane_partner<32>(static_cast<uint32_t>(x), lane)));
+}
+
+template <int NENT, int SUB, typename Block, typename Exact>
+__device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu,
+                                                   const float* __restrict__ ccd, Block block,
+                                                   float ex, int lane, Exact exact) {
+    static_assert(NENT % (16 * kSearchUnroll) == 0, "whole unrolled groups");
+    const int q4 = 4 * (lane >> 4);   // this lane's first centroid row in a block
+    const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(ccu + q4);
+    const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(ccd + q4);
+    const auto cup = [&](int blk) { return ucol[blk * 4]; };
+    const auto cdown = [&](int blk) { return dcol[blk * 4]; };
+
+    // pass 1: thr = min over c of s(c) + E(c)
+    float smin = search_pass1(block, cup, 0, NENT / 16);
+    smin = fminf(smin, lane_partner<16>(smin, lane));
+    smin = fminf(smin, lane_partner<32>(smin, lane));
+    const float thr = smin + ex;
+
+    // pass 2: each lane counts its candidates and keeps one
+    int cnt, cand;
+    search_pass2(block, cdown, 0, NENT / 16, thr, cnt, cand);
+    cnt = sum_lanes16_32(cnt, lane);
+    const int best = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
+
+    // every sub-vector has exactly one candidate: it is the nearest centroid
+    if (__builtin_amdgcn_ballot_w64(cnt != 1) == 0) return static_cast<uint32_t>(best);
+
+    // some sub-vector has several candidates: fp64 distances for all
+    // candidates of this block (pass 2 again), lexicographic minimum over
+    // the 4 lanes of each sub-vector
+    double bd;
+    uint32_t bi;
+    search_pass3(block, cdown, 0, NENT / 16, thr, q4, exact, bd, bi);
+    take_lanes16_32(bd, bi, lane);
     return bi;
 }
+
+// The MFMA score of one block of 16 centroids for the d = 8 layout: ctab
+// [.][8] fp16 centroids, b0, b1 = -2x of channels 2 (lane / 16) and
+// 2 (lane / 16) + 1 of sub-vector lane % 16.
+struct BlockD8 {
+    const uint32_t* acol;
+    float b0, b1;
+    __device__ BlockD8(const uint16_t* ctab, float b0_, float b1_, int lane)
+        : acol(reinterpret_cast<const uint32_t*>(ctab) + (lane & 15) * 4 + (lane >> 4)),
+          b0(b0_), b1(b1_) {}
+    __device__ f32x4_t operator()(int blk, f32x4_t c) const {
+        const uint32_t w = acol[blk * 64];   // channels 2 g, 2 g + 1 of centroid 16 blk + lane % 16
+        const float a0 = half_bits_to_float(static_cast<uint16_t>(w & 0xffffu));
+        const float a1 = half_bits_to_float(static_cast<uint16_t>(w >> 16));
+        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, d, 0, 0, 0);
+    }
+};
 
 // d = 4: m2 [4][kSearchStride<NENT>] fp32 -2 fl32(c) by channel; b is this
 // lane's B operand, channel lane / 16 of sub-vector lane % 16.
@@ -188,15 +250,7 @@ __device__ __forceinline__ uint32_t nearest16_d8(const uint16_t* __restrict__ ct
                                                  const float* __restrict__ ccu,
                                                  const float* __restrict__ ccd, float b0, float b1,
                                                  float ex, int lane, Exact exact) {
-    const uint32_t* acol = reinterpret_cast<const uint32_t*>(ctab) + (lane & 15) * 4 + (lane >> 4);
-    const auto block = [&](int blk, f32x4_t c) {
-        const uint32_t w = acol[blk * 64];   // channels 2 g, 2 g + 1 of centroid 16 blk + lane % 16
-        const float a0 = half_bits_to_float(static_cast<uint16_t>(w & 0xffffu));
-        const float a1 = half_bits_to_float(static_cast<uint16_t>(w >> 16));
-        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c, 0, 0, 0);
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, d, 0, 0, 0);
-    };
-    return nearest16_core<NENT, 8>(ccu, ccd, block, ex, lane, exact);
+    return nearest16_core<NENT, 8>(ccu, ccd, BlockD8(ctab, b0, b1, lane), ex, lane, exact);
 }
 
 }  // namespace vqkv

@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "launchers.hpp"
+#include "nearest_search.hpp"
 
 namespace vqkv {
 
@@ -366,18 +367,23 @@ __device__ __forceinline__ void new_token_workgroup(
 }
 
 // The appended token in the d = 8 layout (16 sub-vectors of 8 channels; C_k
-// and C_v of 4096 entries; 24-byte rows of 12-bit codes), with the steps and
-// decisions of new_token_workgroup.  Thread (slice, pos) scans centroids
-// slice, slice + 64, ... of sub-vector pos = tid % 16 (64 slices); lanes l,
-// l ^ 16, l ^ 32, l ^ 48 of a wave hold 4 slices of one position and are
-// combined first, then the 16 waves.  LDS: C_k in `tab`, C_v 64 KiB above.
+// and C_v of 4096 entries; 24-byte rows of 12-bit codes), with the decisions
+// of new_token_workgroup, found by the certified matrix-core search of
+// nearest_search.hpp spread over the workgroup: the 16 sub-vectors of a
+// tensor are one MFMA column block, and wave w scans centroids 256 w ..
+// 256 w + 255.  Per tensor: the waves' pass-1 minima meet in LDS (the
+// threshold), their candidate counts meet in LDS, and a sub-vector with
+// exactly one candidate takes it; only when some sub-vector has several do
+// the waves evaluate their candidates in fp64 and meet a third time.
+// LDS: C_k in `tab`, C_v 64 KiB above; ||c||^2 of the current tensor in
+// `scratch` (16 KiB); the exchanges in `xbuf` (4 KiB).
 template <int G>
 __device__ __forceinline__ void new_token_workgroup8(
     const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
     const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads,
     int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v, Partials part,
-    int part_stride, int slot, uint8_t* tab, uint8_t* scratch, double (*xnew)[kHeadDim],
-    uint32_t (*newc)[kNumSub]) {
+    int part_stride, int slot, uint8_t* tab, uint8_t* scratch, uint8_t* xbuf,
+    double (*xnew)[kHeadDim], uint32_t (*newc)[kNumSub]) {
     constexpr int kEnt = 4096, kPos = kHeadDim / 8, kRow = kPos * 12 / 8;   // 16 codes, 24 B
     const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -394,66 +400,104 @@ __device__ __forceinline__ void new_token_workgroup8(
                         lane, x0, x1, xnew);
     __syncthreads();
 
-    // 1. codes
-    const int pos = tid & (kPos - 1), slice = tid / kPos;
-    double xk[8], xv[8];
+    // 1. codes, one tensor after the other
+    static_assert(kThreads == 1024 && kEnt == kWaves * 256, "16 waves of 256 centroids");
+    float* nrm = reinterpret_cast<float*>(scratch);             // [4096] ||c||^2
+    float* wmin = reinterpret_cast<float*>(xbuf);               // [16 waves][16] pass-1 minima
+    int* wcnt = reinterpret_cast<int*>(xbuf + 1024);            // [16][16] candidate counts
+    int* wcand = reinterpret_cast<int*>(xbuf + 2048);           // [16][16] a candidate (or -1)
+    int* flag = reinterpret_cast<int*>(xbuf + 3072);            // [16] several candidates
+    double* wbd = reinterpret_cast<double*>(xbuf);              // [16][16] (reuses the above)
+    uint32_t* wbi = reinterpret_cast<uint32_t*>(xbuf + 2048);
+    const int pos = lane & (kPos - 1), q4 = 4 * (lane >> 4);
+    const int b0 = 16 * wave, b1 = b0 + 16;   // this wave's centroid blocks
+    for (int t = 0; t < 2; ++t) {
+        const uint16_t* table = reinterpret_cast<const uint16_t*>(tab + t * kTable);
+        for (int i = tid; i < kEnt; i += kThreads) {
+            const uint4 c = reinterpret_cast<const uint4*>(table)[i];
+            const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+            float nn = 0.f;   // the squares of fp16 values are exact in fp32
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        xk[i] = xnew[0][8 * pos + i];
-        xv[i] = xnew[1][8 * pos + i];
-    }
-    double dk = INFINITY, dv = INFINITY;
-    uint32_t ik = 0, iv = 0;
-    for (int c = slice; c < kEnt; c += kThreads / kPos) {
-        const double d1 = sqdist8_f64(xk, kt[c]);
-        if (d1 < dk) {
-            dk = d1;
-            ik = static_cast<uint32_t>(c);
+            for (int j = 0; j < 4; ++j) {
+                const float lo = half_bits_to_float(static_cast<uint16_t>(w[j] & 0xffffu));
+                const float hi = half_bits_to_float(static_cast<uint16_t>(w[j] >> 16));
+                nn += lo * lo;
+                nn += hi * hi;
+            }
+            nrm[i] = nn;
         }
-        const double d2 = sqdist8_f64(xv, vt[c]);
-        if (d2 < dv) {
-            dv = d2;
-            iv = static_cast<uint32_t>(c);
-        }
-    }
+        __syncthreads();
+        double xd[8];
 #pragma unroll
-    for (int step = 0; step < 2; ++step) {
-        const int m = step == 0 ? 16 : 32;
-        const double dk2 = __shfl_xor(dk, m, kWave), dv2 = __shfl_xor(dv, m, kWave);
-        const uint32_t ik2 = __shfl_xor(ik, m, kWave), iv2 = __shfl_xor(iv, m, kWave);
-        if (nearer(dk2, ik2, dk, ik)) {
-            dk = dk2;
-            ik = ik2;
+        for (int j = 0; j < 8; ++j) xd[j] = xnew[t][8 * pos + j];
+        float xx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float v = static_cast<float>(xd[j]);
+            xx += v * v;
         }
-        if (nearer(dv2, iv2, dv, iv)) {
-            dv = dv2;
-            iv = iv2;
+        const int gq = lane >> 4;
+        const BlockD8 block(table, -2.f * static_cast<float>(xd[2 * gq]),
+                            -2.f * static_cast<float>(xd[2 * gq + 1]), lane);
+        const f32x4_t* ncol = reinterpret_cast<const f32x4_t*>(nrm + q4);
+        const auto cup = [&](int blk) { return ncol[blk * 4] * kBoundUp; };
+        const auto cdown = [&](int blk) { return ncol[blk * 4] * kBoundDown; };
+        const auto exact = [&](uint32_t nc) {
+            return sqdist8_f64(xd, reinterpret_cast<const uint4*>(table)[nc]);
+        };
+        float smin = search_pass1(block, cup, b0, b1);
+        smin = fminf(smin, lane_partner<16>(smin, lane));
+        smin = fminf(smin, lane_partner<32>(smin, lane));
+        if (lane < kPos) wmin[wave * kPos + lane] = smin;
+        __syncthreads();
+        float gmin = wmin[pos];
+        for (int w = 1; w < kWaves; ++w) gmin = fminf(gmin, wmin[w * kPos + pos]);
+        const float thr = gmin + row_bound(xx);
+        int cnt, cand;
+        search_pass2(block, cdown, b0, b1, thr, cnt, cand);
+        cnt = sum_lanes16_32(cnt, lane);
+        cand = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
+        if (lane < kPos) {
+            wcnt[wave * kPos + lane] = cnt;
+            wcand[wave * kPos + lane] = cand;
         }
-    }
-    // [tensor][wave][pos]: lanes 0..15 report keys, 16..31 values
-    double* sd = reinterpret_cast<double*>(scratch);
-    uint32_t* si = reinterpret_cast<uint32_t*>(sd + 2 * kWaves * kPos);
-    if (lane < 2 * kPos) {
-        const int tsel = lane / kPos;
-        sd[(tsel * kWaves + wave) * kPos + pos] = tsel ? dv : dk;
-        si[(tsel * kWaves + wave) * kPos + pos] = tsel ? iv : ik;
-    }
-    __syncthreads();
-    if (tid < 2 * kPos) {
-        const int tsel = tid / kPos;
-        double d0 = sd[tsel * kWaves * kPos + pos];
-        uint32_t i0 = si[tsel * kWaves * kPos + pos];
-        for (int w = 1; w < kWaves; ++w) {
-            const double d = sd[(tsel * kWaves + w) * kPos + pos];
-            const uint32_t i = si[(tsel * kWaves + w) * kPos + pos];
-            if (nearer(d, i, d0, i0)) {
-                d0 = d;
-                i0 = i;
+        __syncthreads();
+        if (tid < kPos) {
+            int total = 0, one = -1;
+            for (int w = 0; w < kWaves; ++w) {
+                total += wcnt[w * kPos + tid];
+                one = max(one, wcnt[w * kPos + tid] > 0 ? wcand[w * kPos + tid] : -1);
+            }
+            newc[t][tid] = static_cast<uint32_t>(one) & (kEnt - 1);
+            flag[tid] = total != 1;
+        }
+        __syncthreads();
+        bool several = false;
+        for (int k = 0; k < kPos; ++k) several |= flag[k] != 0;
+        if (several) {   // uniform: fp64 resolution of every sub-vector's candidates
+            double bd;
+            uint32_t bi;
+            search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi);
+            take_lanes16_32(bd, bi, lane);
+            if (lane < kPos) {
+                wbd[wave * kPos + lane] = bd;
+                wbi[wave * kPos + lane] = bi;
+            }
+            __syncthreads();
+            if (tid < kPos) {
+                double d0 = wbd[tid];
+                uint32_t i0 = wbi[tid];
+                for (int w = 1; w < kWaves; ++w) {
+                    if (nearer(wbd[w * kPos + tid], wbi[w * kPos + tid], d0, i0)) {
+                        d0 = wbd[w * kPos + tid];
+                        i0 = wbi[w * kPos + tid];
+                    }
+                }
+                newc[t][tid] = i0 & (kEnt - 1);   // (a code always exists for finite inputs)
             }
         }
-        newc[tsel][pos] = i0;
+        __syncthreads();   // the exchange buffers and norms are free for the next tensor
     }
-    __syncthreads();
     const size_t row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + append_pos;
     if (tid < 2 * kRow) {   // byte j of a row holds bits [8j, 8j + 8) of the 12-bit stream
         const int tsel = tid / kRow, j = tid % kRow;
@@ -645,7 +689,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             new_token_workgroup8<G>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
                                     num_q_heads, num_kv_heads, capacity, append_pos, new_codes_k,
                                     new_codes_v, part, part_stride, num_splits, tab,
-                                    reinterpret_cast<uint8_t*>(&pbuf[0][0]), xnew, newc);
+                                    reinterpret_cast<uint8_t*>(&pbuf[0][0]),
+                                    reinterpret_cast<uint8_t*>(&qa[0][0]), xnew, newc);
         else
             new_token_workgroup<G, KBITS>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
                                           num_q_heads, num_kv_heads, capacity, append_pos,
