@@ -6,7 +6,7 @@
  * KV Cache via Outlier-Suppressed Vector Quantization", notes page):
  *   - keys are smoothed per channel and Walsh–Hadamard transformed,
  *       K~ = K diag(lambda)^-1 H_D            (Method details)
- *     then stored as vector-quantisation codes: every d = 4 consecutive
+ *     then stored as vector-quantisation codes: every d (4 or 8) consecutive
  *     channels (a sub-vector) is replaced by the index of its nearest
  *     codebook centroid                      (Background, VQ principle);
  *   - values are quantised the same way without any transform;
@@ -30,17 +30,22 @@
  *    validation never dereferences a pointer.  On failure the call returns a
  *    non-zero vq_status, enqueues nothing and leaves a message for
  *    vq_last_error().  No C++ exception crosses this interface.
- *  - Only D = 128 and d = 4 are supported (VQ_ERR_UNSUPPORTED otherwise).
+ *  - D = 128 only.  Two sub-vector layouts (VQ_ERR_UNSUPPORTED otherwise):
+ *      d = 4: 32 sub-vectors per vector, k_code_bits 8 or 12, v_code_bits 8
+ *             (the VecInfer page's 2-bit choice, 2^8 x 4 x 2 B codebooks);
+ *      d = 8: 16 sub-vectors per vector, k_code_bits = v_code_bits = 12 (the
+ *             page's 1.5-bit choice, 2^12 x 8 x 2 B codebooks; Results,
+ *             codebook-size ablation).
  *  - Layouts (row-major, innermost last; B batch, Hq query heads, Hkv KV
- *    heads, G = Hq / Hkv, P = D / d = 32 sub-vectors, cap = capacity):
+ *    heads, G = Hq / Hkv, P = D / d sub-vectors (32 or 16), cap = capacity):
  *      q        [B][Hq][128]            fp16 or fp32 (q_dtype)
  *      lambda   [Hkv][128]              fp32, finite and > 0 (caller contract)
- *      cb_k     [Hkv][2^k_code_bits][4] fp16 (bit patterns as uint16)
- *      cb_v     [Hkv][2^v_code_bits][4] fp16
- *      codes_k  [B][Hkv][cap][P*k_code_bits/8] uint8 — token-major code rows:
- *               8-bit codes are one byte per sub-vector; 12-bit codes are a
- *               little-endian bit stream, code i in bits [12i, 12i+12) of
- *               the 48-byte row.
+ *      cb_k     [Hkv][2^k_code_bits][d] fp16 (bit patterns as uint16)
+ *      cb_v     [Hkv][2^v_code_bits][d] fp16
+ *      codes_k  [B][Hkv][cap][P*k_code_bits/8] uint8 — token-major code rows
+ *               (P = 128 / d): 8-bit codes are one byte per sub-vector;
+ *               12-bit codes are a little-endian bit stream, code i in bits
+ *               [12i, 12i+12) of the row (48 bytes at d = 4, 24 at d = 8).
  *      codes_v  [B][Hkv][cap][P*v_code_bits/8] uint8
  *      out      [B][Hq][128]            fp32
  *    Query head h reads KV head h / G.  One codebook and one lambda per KV
@@ -72,9 +77,9 @@ typedef enum { VQ_F16 = 0, VQ_F32 = 1 } vq_dtype;
 /* Cache geometry, plain data, passed by pointer. */
 typedef struct {
     int32_t head_dim;      /* D: must be 128                          */
-    int32_t sub_dim;       /* d: must be 4                            */
-    int32_t k_code_bits;   /* log2 |C_k|: 8 or 12                     */
-    int32_t v_code_bits;   /* log2 |C_v|: 8                           */
+    int32_t sub_dim;       /* d: 4 or 8                               */
+    int32_t k_code_bits;   /* log2 |C_k|: 8 or 12 (d = 4), 12 (d = 8)  */
+    int32_t v_code_bits;   /* log2 |C_v|: 8 (d = 4), 12 (d = 8)        */
     int32_t num_kv_heads;  /* Hkv >= 1                                */
     int32_t capacity;      /* token slots per (sequence, KV head) >= 1 */
 } vq_layout;
