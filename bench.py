@@ -103,6 +103,7 @@ def cpu_baseline(wl: W.Workload, seconds: float) -> dict:
 KERNEL_SOURCES = ["vector_quantized_bit_amd/csrc/vq_attention_mfma.hip",
                   "vector_quantized_bit_amd/csrc/launchers.hpp",
                   "vector_quantized_bit_amd/csrc/device_common.hpp",
+                  "vector_quantized_bit_amd/csrc/nearest_search.hpp",
                   "vector_quantized_bit_amd/build.py"]
 
 
@@ -141,6 +142,24 @@ def copy_calibration(torch, dev, mib: int = 256, reps: int = 3) -> None:
     for _ in range(reps):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
+
+
+def copy_bandwidth(torch, dev, head_start, mib: int = 512, reps: int = 20) -> float:
+    """GB/s of a plain device copy (`mib` MiB read and written per copy, far
+    above the 256 MB Infinity Cache), back to back between one event pair:
+    the streaming rate this chip reaches in practice."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    head_start()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    return 2 * (mib << 20) * reps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
 MFMA_F32_PEAK_TFLOPS = 157.3
@@ -447,6 +466,9 @@ def main(argv=None) -> int:
                              "gbps": ab_attn["total"] / (call_us * 1e-6) / 1e9,
                              "kernels": "vq_attention_mfma_kernel + merge_partials_kernel"},
     }
+    copy_gbps = copy_bandwidth(torch, dev, head_start)
+    result["roofline"]["copy_gbps"] = copy_gbps
+    result["roofline"]["frac_of_copy"] = achieved / copy_gbps
 
     if not args.no_fp16:
         fk = torch.empty((bsz, hkv, cap, 128), dtype=torch.float16, device=dev)
