@@ -243,17 +243,22 @@ def calibration(torch, vq, wl, dev, head_start, iters: int) -> dict:
     km = {}
     for name, samples, bits, its in (("k8", kt.view(hkv, n, 4), 8, iters),
                                      ("v8", vals.float().view(hkv, n, 4), 8, iters),
-                                     ("k12", kt.view(hkv, n, 4), 12, max(1, iters // 2))):
+                                     ("k12", kt.view(hkv, n, 4), 12, max(1, iters // 2)),
+                                     ("k12_d8", kt.view(hkv, n // 2, 8), 12, max(1, iters // 2))):
         ent = 1 << bits
-        idx = torch.randperm(n, generator=gen)[:ent].to(dev)
+        rows = samples.shape[1]
+        idx = torch.randperm(rows, generator=gen)[:ent].to(dev)
         init = samples[:, idx].double().contiguous()
         cent = torch.empty_like(init)
-        ws = torch.empty(vq.kmeans_workspace_bytes(hkv, n, bits), dtype=torch.uint8, device=dev)
+        sub = samples.shape[2]
+        ws = torch.empty(vq.kmeans_workspace_bytes(hkv, rows, bits, sub), dtype=torch.uint8,
+                         device=dev)
         us = time_calls(torch, lambda: vq.kmeans(samples, init, its, centroids=cent, workspace=ws),
                         1, head_start, warm=1)
         per_it = us / its
-        tflops = distance_flops(hkv * n * ent) / (per_it * 1e-6) / 1e12
-        km[name] = {"sets": hkv, "samples_per_set": n, "entries": ent, "iters": its,
+        tflops = distance_flops(hkv * rows * ent, sub) / (per_it * 1e-6) / 1e12
+        km[name] = {"sets": hkv, "samples_per_set": rows, "sub_dim": sub, "entries": ent,
+                    "iters": its,
                     "us_per_iter": per_it, "dense_pass_tflops": tflops,
                     "frac_of_mfma_f32_peak": tflops / MFMA_F32_PEAK_TFLOPS}
     out["kmeans"] = km

@@ -297,7 +297,7 @@ int vq_flush_window(const vq_layout* layout, const uint16_t* win_k, const uint16
  * offline from calibration keys, lambda_i = sqrt(max_t |K[t, i]|), and the
  * codebooks are pretrained offline with K-Means, C_k on the transformed keys
  * K~ = K diag(lambda)^-1 H_D and C_v on the values as they are, split into
- * d = 4 sub-vectors; Experimental setup: at most 30 K-Means iterations.
+ * d-channel sub-vectors; Experimental setup: at most 30 K-Means iterations.
  * Calibration keys are [Hkv][T][128] in kv_dtype (one stream of T tokens per
  * KV head; several calibration sequences are concatenated by the caller).
  */
@@ -326,30 +326,33 @@ int vq_transform_keys(const void* keys, int kv_dtype, const float* lambda,
 
 /*
  * Lloyd K-Means for num_sets independent codebooks of 2^code_bits centroids
- * of dimension 4, `iters` iterations from `init`.  One iteration assigns
- * every sample to its nearest centroid, by the fp64 squared distance summed
- * channel by channel (every difference, square and sum rounded once), exact
- * ties to the lowest index; then moves every centroid that received samples
- * to their mean (the samples summed in fp64 in sample order, divided once by
- * their count); a centroid with no samples keeps its place.  The result is
- * identical, bit for bit, to that definition evaluated sequentially.
- *   samples   [num_sets][num_samples][4] fp32, finite, |x| < 2^60
- *   init      [num_sets][2^code_bits][4] fp64, finite, |c| < 2^60
- *   centroids [num_sets][2^code_bits][4] fp64 output (may be init itself)
- *   codebook  [num_sets][2^code_bits][4] fp16 output, or NULL: the
+ * of dimension d = sub_dim (4 or 8), `iters` iterations from `init`.  One
+ * iteration assigns every sample to its nearest centroid, by the fp64 squared
+ * distance summed channel by channel (every difference, square and sum
+ * rounded once), exact ties to the lowest index; then moves every centroid
+ * that received samples to their mean (the samples summed in fp64 in sample
+ * order, divided once by their count); a centroid with no samples keeps its
+ * place.  The result is identical, bit for bit, to that definition evaluated
+ * sequentially.
+ *   samples   [num_sets][num_samples][d] fp32, finite, |x| < 2^60
+ *   init      [num_sets][2^code_bits][d] fp64, finite, |c| < 2^60
+ *   centroids [num_sets][2^code_bits][d] fp64 output (may be init itself)
+ *   codebook  [num_sets][2^code_bits][d] fp16 output, or NULL: the
  *             centroids rounded once to nearest even
  *   assign    [num_sets][num_samples] int32 output, or NULL: each sample's
  *             nearest centroid among the returned ones (its code)
  *   workspace vq_kmeans_workspace_bytes(...) bytes, 16-byte aligned; its
  *             contents do not matter.
- * code_bits: 8 or 12 (VQ_ERR_UNSUPPORTED otherwise); num_samples in
- * [1, 2^28]; iters in [0, 10000] (0 copies init and only fills the outputs).
- * vq_kmeans_workspace_bytes returns 0 for an invalid shape.
+ * sub_dim 4 or 8 and code_bits 8 or 12 (VQ_ERR_UNSUPPORTED otherwise);
+ * num_samples in [1, 2^28]; iters in [0, 10000] (0 copies init and only fills
+ * the outputs).  vq_kmeans_workspace_bytes returns 0 for an invalid shape.
  */
-size_t vq_kmeans_workspace_bytes(int32_t num_sets, int32_t num_samples, int32_t code_bits);
-int vq_kmeans(const float* samples, int32_t num_sets, int32_t num_samples, int32_t code_bits,
-              const double* init, int32_t iters, double* centroids, uint16_t* codebook,
-              int32_t* assign, void* workspace, size_t workspace_bytes, void* stream);
+size_t vq_kmeans_workspace_bytes(int32_t num_sets, int32_t num_samples, int32_t sub_dim,
+                                 int32_t code_bits);
+int vq_kmeans(const float* samples, int32_t num_sets, int32_t num_samples, int32_t sub_dim,
+              int32_t code_bits, const double* init, int32_t iters, double* centroids,
+              uint16_t* codebook, int32_t* assign, void* workspace, size_t workspace_bytes,
+              void* stream);
 
 /*
  * Uncompressed comparator: the same decode attention over an fp16 cache,

@@ -346,8 +346,9 @@ def test_transform_keys_validation(lib, args, status, needle):
 
 
 def kmeans_call(lib, samples=A, sets=2, n=1000, bits=8, init=A, iters=3, cent=A, cb=A, asg=A,
-                ws=A, ws_bytes=1 << 30):
-    return lib.vq_kmeans(samples, sets, n, bits, init, iters, cent, cb, asg, ws, ws_bytes, None)
+                ws=A, ws_bytes=1 << 30, sub=4):
+    return lib.vq_kmeans(samples, sets, n, sub, bits, init, iters, cent, cb, asg, ws, ws_bytes,
+                         None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -356,6 +357,7 @@ def kmeans_call(lib, samples=A, sets=2, n=1000, bits=8, init=A, iters=3, cent=A,
     (dict(n=0), INVALID, "num_samples"),
     (dict(n=(1 << 28) + 1), INVALID, "num_samples"),
     (dict(bits=10), UNSUPPORTED, "code_bits"),
+    (dict(sub=6), UNSUPPORTED, "sub_dim"),
     (dict(iters=-1), INVALID, "iters"),
     (dict(iters=10001), INVALID, "iters"),
     (dict(samples=None), INVALID, "samples"),
@@ -376,10 +378,12 @@ def test_kmeans_workspace_layout(lib):
     def a256(x):
         return (x + 255) // 256 * 256
 
-    for sets, n, bits in ((1, 1, 8), (8, 4194304, 8), (3, 8193, 12)):
+    for sets, n, sub, bits in ((1, 1, 4, 8), (8, 4194304, 4, 8), (3, 8193, 4, 12),
+                               (8, 2097152, 8, 12), (2, 100, 8, 8)):
         ent, chunks = 1 << bits, -(-n // 8192)
         want = (a256(sets * n * 4) + a256(sets * chunks * ent * 4) + 2 * a256(sets * ent * 4) +
-                a256(sets * n * 16))
-        assert lib.vq_kmeans_workspace_bytes(sets, n, bits) == want
-    for bad in ((0, 10, 8), (1, 0, 8), (1, 10, 9), (1, (1 << 28) + 1, 8)):
+                a256(sets * n * 4 * sub))
+        assert lib.vq_kmeans_workspace_bytes(sets, n, sub, bits) == want
+    for bad in ((0, 10, 4, 8), (1, 0, 4, 8), (1, 10, 4, 9), (1, (1 << 28) + 1, 4, 8),
+                (1, 10, 5, 8)):
         assert lib.vq_kmeans_workspace_bytes(*bad) == 0

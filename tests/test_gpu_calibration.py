@@ -93,15 +93,15 @@ def test_transform_keys_matches_oracle(dtype, hkv, n):
 
 # --- K-Means ---------------------------------------------------------------------------
 
-def key_samples(config_id, g, n_tok):
+def key_samples(config_id, g, n_tok, sub=4):
     k = W.as_storage(W.calibration_rows(config_id, g, "k", n_tok), "f16")
     lam = oracle.smooth_factors(k).astype(np.float32)
-    return oracle.transform_keys(k, lam).astype(np.float32).reshape(-1, 4)
+    return oracle.transform_keys(k, lam).astype(np.float32).reshape(-1, sub)
 
 
-def value_samples(config_id, g, n_tok):
+def value_samples(config_id, g, n_tok, sub=4):
     v = W.as_storage(W.calibration_rows(config_id, g, "v", n_tok), "f16")
-    return v.astype(np.float32).reshape(-1, 4)
+    return v.astype(np.float32).reshape(-1, sub)
 
 
 def initial_centroids(samples, bits, config_id, g, tensor):
@@ -149,6 +149,40 @@ def test_kmeans_bit_exact(tensor, bits, sets, n_tok, iters):
     cent, cb, asg = run_kmeans(samples, init, iters)
     for g in range(sets):
         check_set(samples[g], init[g], iters, cent[g], cb[g], asg[g], f"set {g}")
+
+
+@pytest.mark.parametrize("tensor,bits,sets,n_tok,iters", [
+    ("k", 12, 2, 600, 1),    # the 1.5-bit C_k: 4096 centroids of 8 dims, 9600 samples
+    ("k", 12, 1, 300, 0),
+    ("v", 12, 1, 300, 2),
+    ("v", 8, 2, 1100, 3),    # 17600 samples: three sort chunks
+    ("k", 8, 1, 2, 2),       # 32 samples, 256 centroids: duplicates, empty clusters
+])
+def test_kmeans_bit_exact_8dim(tensor, bits, sets, n_tok, iters):
+    print(f"kmeans d=8 {tensor} bits={bits} sets={sets} tokens={n_tok} iters={iters}", flush=True)
+    make = key_samples if tensor == "k" else value_samples
+    samples = np.stack([make(2, g, n_tok, 8) for g in range(sets)])
+    init = np.stack([initial_centroids(samples[g], bits, 2, g, tensor) for g in range(sets)])
+    cent, cb, asg = run_kmeans(samples, init, iters)
+    assert cent.shape[-1] == 8 and cb.shape[-1] == 8
+    for g in range(sets):
+        check_set(samples[g], init[g], iters, cent[g], cb[g], asg[g], f"d8 set {g}")
+
+
+def test_kmeans_8dim_full_calibration_set_sampled():
+    """The 1.5-bit C_k at the calibration-set size: 131072 tokens per KV head
+    as 2,097,152 8-dim sub-vectors, 4096 centroids, one Lloyd iteration (two
+    heads).  Checked on sampled rows: each code is the nearest returned
+    centroid by the fp64 distance (ties to the lowest index)."""
+    n_tok, sets = W.CALIB_TOKENS, 2
+    samples = np.stack([key_samples(2, g, n_tok, 8) for g in range(sets)])
+    init = np.stack([initial_centroids(samples[g], 12, 2, g, "k") for g in range(sets)])
+    cent, cb, asg = run_kmeans(samples, init, 1)
+    rows = np.random.default_rng(42).choice(samples.shape[1], 2048, replace=False)
+    for g in range(sets):
+        codes, _, _ = oracle.vq_assign(samples[g, rows].astype(np.float64), cent[g])
+        np.testing.assert_array_equal(asg[g, rows], codes)
+        np.testing.assert_array_equal(cb[g].view(np.uint16), cent[g].astype(np.float16).view(np.uint16))
 
 
 def test_kmeans_exact_ties_and_degenerate_sets():

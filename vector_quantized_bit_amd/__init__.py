@@ -92,9 +92,9 @@ def library() -> ctypes.CDLL:
                                      _vp]),
         "vq_calibrate_lambda": (_c_int, [_vp, _c_int, _i32, _i32, _vp, _vp]),
         "vq_transform_keys": (_c_int, [_vp, _c_int, _vp, _i32, _i32, _vp, _vp]),
-        "vq_kmeans_workspace_bytes": (_size, [_i32, _i32, _i32]),
-        "vq_kmeans": (_c_int, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _size,
-                               _vp]),
+        "vq_kmeans_workspace_bytes": (_size, [_i32, _i32, _i32, _i32]),
+        "vq_kmeans": (_c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
+                               _size, _vp]),
         "vq_fp16_attention_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32]),
         "vq_fp16_decode_attention": (_c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _vp, _vp, _size, _vp]),
@@ -625,24 +625,27 @@ def transform_keys(keys: torch.Tensor, lam: torch.Tensor,
     return out
 
 
-def kmeans_workspace_bytes(num_sets: int, num_samples: int, code_bits: int) -> int:
-    return int(library().vq_kmeans_workspace_bytes(num_sets, num_samples, code_bits))
+def kmeans_workspace_bytes(num_sets: int, num_samples: int, code_bits: int,
+                           sub_dim: int = 4) -> int:
+    return int(library().vq_kmeans_workspace_bytes(num_sets, num_samples, sub_dim, code_bits))
 
 
 def kmeans(samples: torch.Tensor, init: torch.Tensor, iters: int, *, codebook: bool = True,
            assign: bool = False, centroids: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None):
-    """Lloyd K-Means of fp32 samples [S][n][4] from fp64 init [S][2^bits][4].
+    """Lloyd K-Means of fp32 samples [S][n][d] from fp64 init [S][2^bits][d]
+    (d = 4 or 8).
 
-    Returns (centroids float64 [S][2^bits][4], codebook float16 or None,
+    Returns (centroids float64 [S][2^bits][d], codebook float16 or None,
     assign int32 [S][n] or None).  ``centroids`` may be ``init`` (updated in
     place); ``workspace`` is an optional reusable uint8 device tensor of at
     least ``kmeans_workspace_bytes(...)`` bytes."""
     _need(samples.is_cuda and samples.is_contiguous() and samples.dtype == torch.float32 and
-          samples.dim() == 3 and samples.shape[2] == 4, "samples must be contiguous float32 [S][n][4]")
+          samples.dim() == 3, "samples must be contiguous float32 [S][n][d]")
+    sub = int(samples.shape[2])
     _need(init.is_cuda and init.is_contiguous() and init.dtype == torch.float64 and
-          init.dim() == 3 and init.shape[0] == samples.shape[0] and init.shape[2] == 4,
-          "init must be contiguous float64 [S][entries][4]")
+          init.dim() == 3 and init.shape[0] == samples.shape[0] and init.shape[2] == sub,
+          "init must be contiguous float64 [S][entries][d] with the samples' d")
     entries = int(init.shape[1])
     bits = entries.bit_length() - 1
     _need(entries == 1 << bits, "the number of centroids must be a power of two")
@@ -654,10 +657,10 @@ def kmeans(samples: torch.Tensor, init: torch.Tensor, iters: int, *, codebook: b
           centroids.shape == init.shape, "centroids must be contiguous float64 like init")
     cb = torch.empty(init.shape, dtype=torch.float16, device=dev) if codebook else None
     asg = torch.empty((sets, n), dtype=torch.int32, device=dev) if assign else None
-    need = kmeans_workspace_bytes(sets, n, bits)
+    need = kmeans_workspace_bytes(sets, n, bits, sub)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _check(library().vq_kmeans(_ptr(samples), sets, n, bits, _ptr(init), int(iters),
+    _check(library().vq_kmeans(_ptr(samples), sets, n, sub, bits, _ptr(init), int(iters),
                                _ptr(centroids), _ptr(cb), _ptr(asg), _ptr(workspace),
                                workspace.numel(), _stream(samples)),
            "vq_kmeans")

@@ -236,6 +236,103 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_assign_kernel(
     }
 }
 
+// The same for 8-dim samples and centroids.
+__device__ __forceinline__ double sqdist8_c64(const float x[8], const double c[8]) {
+    double d = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double e = __dadd_rn(static_cast<double>(x[j]), -c[j]);
+        d = j == 0 ? __dmul_rn(e, e) : __dadd_rn(d, __dmul_rn(e, e));
+    }
+    return d;
+}
+
+// kmeans_assign_kernel for 8-dim samples [S][n][8] and centroids [S][NENT][8]:
+// the fp64 centroids rounded to fp32 in a channel-pair-major table (A
+// operand), the sample as -2x (B operand), one norm table scaled by
+// (1 +- 2^-16) as it is read.  LDS: table 32 NENT bytes, norms and histogram
+// 4 NENT bytes each (160 KiB at NENT = 4096), plus the fp64 centroids when
+// they fit (NENT <= 256); the 4096-entry case reads its candidates from L2.
+template <int NENT>
+constexpr int kAssign8Lds = NENT * 40 + (kKmLdsC64<NENT> ? NENT * 64 : 0);
+
+template <int NENT>
+__global__ __launch_bounds__(kKmThreads) void kmeans_assign8_kernel(
+    const float* __restrict__ samples, int num_samples, const double* __restrict__ centroids,
+    int32_t* __restrict__ assign, int32_t* __restrict__ hist) {
+    __shared__ __align__(16) uint8_t lds[kAssign8Lds<NENT>];
+    float* tab = reinterpret_cast<float*>(lds);                   // [4][NENT][2]
+    float* nrm = reinterpret_cast<float*>(lds + NENT * 32);       // [NENT]
+    int32_t* cnt = reinterpret_cast<int32_t*>(lds + NENT * 36);   // [NENT]
+    double* c64s = reinterpret_cast<double*>(lds + NENT * 40);    // [NENT][8] (small NENT)
+
+    const int set = blockIdx.y, chunk = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const double* cset = centroids + static_cast<size_t>(set) * NENT * 8;
+    const float4* xset = reinterpret_cast<const float4*>(samples) +
+                         static_cast<size_t>(set) * num_samples * 2;
+    for (int i = tid; i < NENT; i += kKmThreads) {
+        double c[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double2 v = reinterpret_cast<const double2*>(cset)[4 * i + j];
+            c[2 * j] = v.x;
+            c[2 * j + 1] = v.y;
+        }
+        double nn = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            nn += c[j] * c[j];
+            if constexpr (kKmLdsC64<NENT>) c64s[i * 8 + j] = c[j];
+        }
+#pragma unroll
+        for (int g2 = 0; g2 < 4; ++g2)
+            reinterpret_cast<float2*>(tab)[g2 * NENT + i] =
+                make_float2(static_cast<float>(c[2 * g2]), static_cast<float>(c[2 * g2 + 1]));
+        nrm[i] = static_cast<float>(nn);
+        cnt[i] = 0;
+    }
+    __syncthreads();
+
+    const int s0 = chunk * kKmChunk, s1 = min(num_samples, s0 + kKmChunk);
+    int32_t* aset = assign + static_cast<size_t>(set) * num_samples;
+    const int q4 = 4 * (lane >> 4), gq = lane >> 4;
+    const ScaledNorms cup{reinterpret_cast<const f32x4_t*>(nrm + q4), kBoundUp};
+    const ScaledNorms cdown{reinterpret_cast<const f32x4_t*>(nrm + q4), kBoundDown};
+    for (int base = s0 + wave * 16; base < s1; base += kKmWaves * 16) {
+        // this lane's sample base + lane % 16 (zero past the chunk)
+        const int r = base + (lane & 15);
+        const float4 lo = r < s1 ? xset[2 * r] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 hi = r < s1 ? xset[2 * r + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        float xx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xx += x[j] * x[j];
+        const auto exact = [&](uint32_t nc) {
+            double c[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (kKmLdsC64<NENT>)
+                    c[j] = c64s[nc * 8 + j];
+                else
+                    c[j] = cset[nc * 8 + j];
+            }
+            return sqdist8_c64(x, c);
+        };
+        const BlockF32D8<NENT> block(tab, -2.f * x[2 * gq], -2.f * x[2 * gq + 1], lane);
+        const uint32_t code = nearest16_search<NENT>(block, cup, cdown, row_bound(xx), lane, exact);
+        if (lane < 16 && r < s1) {
+            aset[r] = static_cast<int32_t>(code);
+            if (hist != nullptr) atomicAdd(&cnt[code & (NENT - 1)], 1);
+        }
+    }
+    if (hist != nullptr) {
+        __syncthreads();
+        int32_t* h = hist + (static_cast<size_t>(set) * gridDim.x + chunk) * NENT;
+        for (int i = tid; i < NENT; i += kKmThreads) h[i] = cnt[i];
+    }
+}
+
 // Per (set, cluster): the chunk histograms become exclusive prefix sums over
 // the chunks (in place), and counts[set][c] the cluster sizes.
 __global__ __launch_bounds__(256) void chunk_offsets_kernel(int32_t* __restrict__ hist,
@@ -306,7 +403,7 @@ __global__ __launch_bounds__(1024) void cluster_base_kernel(const int32_t* __res
 // chunk k).  One wave per chunk walks it in order, 64 samples a step; lanes
 // with the same cluster are found with one ballot per code bit.  No barrier:
 // every wave works alone on its own chunk and its own LDS counters.
-template <int BITS>
+template <int BITS, int SUB>
 __global__ __launch_bounds__(kSortWaves * kWave) void kmeans_scatter_kernel(
     const float* __restrict__ samples, int num_samples, const int32_t* __restrict__ assign,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ base, int nchunks,
@@ -326,15 +423,18 @@ __global__ __launch_bounds__(kSortWaves * kWave) void kmeans_scatter_kernel(
 
     const int s0 = chunk * kKmChunk, s1 = min(num_samples, s0 + kKmChunk);
     const int32_t* aset = assign + static_cast<size_t>(set) * num_samples;
+    constexpr int kV = SUB / 4;   // float4 per sample
     const float4* xs = reinterpret_cast<const float4*>(samples) +
-                       static_cast<size_t>(set) * num_samples;
-    float4* out = reinterpret_cast<float4*>(sorted) + static_cast<size_t>(set) * num_samples;
+                       static_cast<size_t>(set) * num_samples * kV;
+    float4* out = reinterpret_cast<float4*>(sorted) + static_cast<size_t>(set) * num_samples * kV;
     const uint64_t below = (1ull << lane) - 1ull;
     for (int i0 = s0; i0 < s1; i0 += kWave) {
         const int i = i0 + lane;
         const bool valid = i < s1;
         const uint32_t c = valid ? static_cast<uint32_t>(aset[i]) & (NENT - 1) : 0u;
-        const float4 x = valid ? xs[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 x[kV];
+#pragma unroll
+        for (int v = 0; v < kV; ++v) x[v] = valid ? xs[i * kV + v] : make_float4(0.f, 0.f, 0.f, 0.f);
         uint64_t same = __builtin_amdgcn_ballot_w64(valid);
 #pragma unroll
         for (int b = 0; b < BITS; ++b) {
@@ -354,53 +454,63 @@ __global__ __launch_bounds__(kSortWaves * kWave) void kmeans_scatter_kernel(
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int32_t pos = start + rank;
-        if (valid && static_cast<uint32_t>(pos) < static_cast<uint32_t>(num_samples))
-            out[pos] = x;
+        if (valid && static_cast<uint32_t>(pos) < static_cast<uint32_t>(num_samples)) {
+#pragma unroll
+            for (int v = 0; v < kV; ++v) out[static_cast<size_t>(pos) * kV + v] = x[v];
+        }
     }
 }
 
 // New centroids: one wave per (set, cluster).  The 64 lanes stream the
 // cluster's sorted samples in tiles of 64 (coalesced 16-byte loads, kPre
-// tiles in flight), stage each tile channel-major in LDS, and lanes 0..3 add
-// channel `lane` of the tile's samples in order onto one fp64 sum each: the
+// tiles in flight), stage each tile channel-major in LDS, and lanes 0 .. SUB-1
+// add channel `lane` of the tile's samples in order onto one fp64 sum each: the
 // sum of the cluster's samples in sample order from zero, then one division
 // by the count.  A cluster without samples keeps its centroid.
 constexpr int kUpdWaves = 4;
 constexpr int kPre = 8;   // tiles of 64 samples in flight per wave
 
+template <int SUB>
 __global__ __launch_bounds__(kUpdWaves * kWave) void kmeans_update_kernel(
     const float* __restrict__ sorted, int num_samples, const int32_t* __restrict__ base,
     const int32_t* __restrict__ counts, int nent, double* __restrict__ centroids) {
-    __shared__ __align__(16) float stage[kUpdWaves][4][kWave];
+    constexpr int kV = SUB / 4;   // float4 per sample
+    __shared__ __align__(16) float stage[kUpdWaves][SUB][kWave];
     const int set = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int c = blockIdx.x * kUpdWaves + wave;
     if (c >= nent) return;   // the whole wave; no barrier below
     const int32_t n = counts[static_cast<size_t>(set) * nent + c];
     if (n == 0) return;
-    const float4* src = reinterpret_cast<const float4*>(sorted) + static_cast<size_t>(set) * num_samples +
-                        base[static_cast<size_t>(set) * nent + c];
+    const float4* src = reinterpret_cast<const float4*>(sorted) +
+                        (static_cast<size_t>(set) * num_samples +
+                         base[static_cast<size_t>(set) * nent + c]) * kV;
     float* st = &stage[wave][0][0];
     const int tiles = (n + kWave - 1) / kWave;
     // loads past the cluster read its last sample (never added): unconditional
     // loads keep the memory counters exact, so the prefetches stay in flight
-    float4 pre[kPre];
+    float4 pre[kPre][kV];
 #pragma unroll
-    for (int k = 0; k < kPre; ++k) pre[k] = src[min(k * kWave + lane, n - 1)];
+    for (int k = 0; k < kPre; ++k)
+#pragma unroll
+        for (int v = 0; v < kV; ++v) pre[k][v] = src[min(k * kWave + lane, n - 1) * kV + v];
     double s = 0.0;
     for (int t0 = 0; t0 < tiles; t0 += kPre) {
 #pragma unroll
         for (int k = 0; k < kPre; ++k) {
             const int t = t0 + k;   // t >= tiles: a padding tile, loaded and skipped
-            const float4 x = pre[k];
-            pre[k] = src[min((t + kPre) * kWave + lane, n - 1)];
-            st[0 * kWave + lane] = x.x;
-            st[1 * kWave + lane] = x.y;
-            st[2 * kWave + lane] = x.z;
-            st[3 * kWave + lane] = x.w;
+#pragma unroll
+            for (int v = 0; v < kV; ++v) {
+                const float4 x = pre[k][v];
+                pre[k][v] = src[min((t + kPre) * kWave + lane, n - 1) * kV + v];
+                st[(4 * v + 0) * kWave + lane] = x.x;
+                st[(4 * v + 1) * kWave + lane] = x.y;
+                st[(4 * v + 2) * kWave + lane] = x.z;
+                st[(4 * v + 3) * kWave + lane] = x.w;
+            }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < 4 && t < tiles) {
+            if (lane < SUB && t < tiles) {
                 const int m = min(kWave, n - t * kWave);   // samples in this tile
                 if (m == kWave) {
                     const float4* row = reinterpret_cast<const float4*>(st + lane * kWave);
@@ -422,8 +532,8 @@ __global__ __launch_bounds__(kUpdWaves * kWave) void kmeans_update_kernel(
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
-    if (lane < 4)
-        centroids[(static_cast<size_t>(set) * nent + c) * 4 + lane] =
+    if (lane < SUB)
+        centroids[(static_cast<size_t>(set) * nent + c) * SUB + lane] =
             __ddiv_rn(s, static_cast<double>(n));
 }
 
@@ -466,10 +576,11 @@ struct KmWorkspace {
     int32_t* hist;     // [sets][chunks][E]
     int32_t* counts;   // [sets][E]
     int32_t* base;     // [sets][E]
-    float* sorted;     // [sets][n][4]
+    float* sorted;     // [sets][n][d]
 };
 
-size_t kmeans_ws_layout(int num_sets, int num_samples, int code_bits, char* p, KmWorkspace* w) {
+size_t kmeans_ws_layout(int num_sets, int num_samples, int sub_dim, int code_bits, char* p,
+                        KmWorkspace* w) {
     const size_t sets = static_cast<size_t>(num_sets), n = static_cast<size_t>(num_samples);
     const size_t ent = static_cast<size_t>(1) << code_bits;
     const size_t chunks = static_cast<size_t>(kmeans_chunks(num_samples));
@@ -483,7 +594,7 @@ size_t kmeans_ws_layout(int num_sets, int num_samples, int code_bits, char* p, K
     char* h = take(sets * chunks * ent * 4);
     char* c = take(sets * ent * 4);
     char* b = take(sets * ent * 4);
-    char* s = take(sets * n * 16);
+    char* s = take(sets * n * 4 * static_cast<size_t>(sub_dim));
     if (w) {
         w->assign = reinterpret_cast<int32_t*>(a);
         w->hist = reinterpret_cast<int32_t*>(h);
@@ -494,53 +605,58 @@ size_t kmeans_ws_layout(int num_sets, int num_samples, int code_bits, char* p, K
     return off;
 }
 
-template <int BITS>
+template <int BITS, int SUB>
 hipError_t kmeans_assign(const float* samples, int num_sets, int num_samples,
                          const double* centroids, int32_t* assign, int32_t* hist,
                          hipStream_t stream) {
     const dim3 grid(kmeans_chunks(num_samples), num_sets);
-    hipLaunchKernelGGL(kmeans_assign_kernel<1 << BITS>, grid, dim3(kKmThreads), 0, stream,
-                       samples, num_samples, centroids, assign, hist);
+    if constexpr (SUB == 8)
+        hipLaunchKernelGGL(kmeans_assign8_kernel<1 << BITS>, grid, dim3(kKmThreads), 0, stream,
+                           samples, num_samples, centroids, assign, hist);
+    else
+        hipLaunchKernelGGL(kmeans_assign_kernel<1 << BITS>, grid, dim3(kKmThreads), 0, stream,
+                           samples, num_samples, centroids, assign, hist);
     return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, int SUB>
 hipError_t kmeans_run(const float* samples, int num_sets, int num_samples, const double* init,
                       int iters, double* centroids, uint16_t* codebook, int32_t* assign_out,
                       void* workspace, hipStream_t stream) {
     constexpr int NENT = 1 << BITS;
     KmWorkspace w;
-    kmeans_ws_layout(num_sets, num_samples, BITS, static_cast<char*>(workspace), &w);
+    kmeans_ws_layout(num_sets, num_samples, SUB, BITS, static_cast<char*>(workspace), &w);
     const int nchunks = kmeans_chunks(num_samples);
-    const size_t cbytes = static_cast<size_t>(num_sets) * NENT * 4 * sizeof(double);
+    const size_t cbytes = static_cast<size_t>(num_sets) * NENT * SUB * sizeof(double);
     hipError_t e = hipSuccess;
     if (init != centroids) {
         e = hipMemcpyAsync(centroids, init, cbytes, hipMemcpyDeviceToDevice, stream);
         if (e != hipSuccess) return e;
     }
     for (int it = 0; it < iters; ++it) {
-        if ((e = kmeans_assign<BITS>(samples, num_sets, num_samples, centroids, w.assign, w.hist,
-                                     stream)) != hipSuccess)
+        if ((e = kmeans_assign<BITS, SUB>(samples, num_sets, num_samples, centroids, w.assign,
+                                          w.hist, stream)) != hipSuccess)
             return e;
         hipLaunchKernelGGL(chunk_offsets_kernel, dim3((NENT + 255) / 256, num_sets), dim3(256), 0,
                            stream, w.hist, nchunks, NENT, w.counts);
         hipLaunchKernelGGL(cluster_base_kernel, dim3(num_sets), dim3(1024), 0, stream, w.counts,
                            NENT, w.base);
-        hipLaunchKernelGGL(kmeans_scatter_kernel<BITS>,
+        hipLaunchKernelGGL((kmeans_scatter_kernel<BITS, SUB>),
                            dim3((nchunks + kSortWaves - 1) / kSortWaves, num_sets),
                            dim3(kSortWaves * kWave), 0, stream, samples, num_samples, w.assign,
                            w.hist, w.base, nchunks, w.sorted);
-        hipLaunchKernelGGL(kmeans_update_kernel, dim3((NENT + kUpdWaves - 1) / kUpdWaves, num_sets),
+        hipLaunchKernelGGL(kmeans_update_kernel<SUB>,
+                           dim3((NENT + kUpdWaves - 1) / kUpdWaves, num_sets),
                            dim3(kUpdWaves * kWave), 0, stream, w.sorted, num_samples, w.base,
                            w.counts, NENT, centroids);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (assign_out != nullptr &&
-        (e = kmeans_assign<BITS>(samples, num_sets, num_samples, centroids, assign_out, nullptr,
-                                 stream)) != hipSuccess)
+        (e = kmeans_assign<BITS, SUB>(samples, num_sets, num_samples, centroids, assign_out,
+                                      nullptr, stream)) != hipSuccess)
         return e;
     if (codebook != nullptr) {
-        const size_t n = static_cast<size_t>(num_sets) * NENT * 4;
+        const size_t n = static_cast<size_t>(num_sets) * NENT * SUB;
         hipLaunchKernelGGL(centroids_to_half_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
                            dim3(256), 0, stream, centroids, n, codebook);
     }
@@ -574,18 +690,24 @@ hipError_t launch_transform_keys(const void* keys, bool kv_f32, const float* lam
     return hipGetLastError();
 }
 
-size_t kmeans_workspace_bytes(int num_sets, int num_samples, int code_bits) {
-    return kmeans_ws_layout(num_sets, num_samples, code_bits, nullptr, nullptr);
+size_t kmeans_workspace_bytes(int num_sets, int num_samples, int sub_dim, int code_bits) {
+    return kmeans_ws_layout(num_sets, num_samples, sub_dim, code_bits, nullptr, nullptr);
 }
 
-hipError_t launch_kmeans(const float* samples, int num_sets, int num_samples, int code_bits,
-                         const double* init, int iters, double* centroids, uint16_t* codebook,
-                         int32_t* assign, void* workspace, hipStream_t stream) {
-    if (code_bits == 8)
-        return kmeans_run<8>(samples, num_sets, num_samples, init, iters, centroids, codebook,
-                             assign, workspace, stream);
-    return kmeans_run<12>(samples, num_sets, num_samples, init, iters, centroids, codebook,
-                          assign, workspace, stream);
+hipError_t launch_kmeans(const float* samples, int num_sets, int num_samples, int sub_dim,
+                         int code_bits, const double* init, int iters, double* centroids,
+                         uint16_t* codebook, int32_t* assign, void* workspace,
+                         hipStream_t stream) {
+#define VQKV_KM(BITS, SUB)                                                                     \
+    return kmeans_run<BITS, SUB>(samples, num_sets, num_samples, init, iters, centroids,        \
+                                 codebook, assign, workspace, stream)
+    if (sub_dim == 8) {
+        if (code_bits == 8) VQKV_KM(8, 8);
+        VQKV_KM(12, 8);
+    }
+    if (code_bits == 8) VQKV_KM(8, 4);
+    VQKV_KM(12, 4);
+#undef VQKV_KM
 }
 
 }  // namespace vqkv

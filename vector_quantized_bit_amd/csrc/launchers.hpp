@@ -64,18 +64,19 @@ hipError_t launch_fp16_attention_splits(const AttnShape& s, const uint16_t* q, c
 
 // Offline calibration: lambda = sqrt(max |K|) per (KV head, channel) over
 // keys [Hkv][T][128]; K~ = K diag(lambda)^-1 H_128 as fp32 [Hkv][T][128];
-// Lloyd K-Means over fp32 samples [sets][n][4] with fp64 centroids
-// [sets][2^code_bits][4] (init may equal centroids), optional fp16 codebook
+// Lloyd K-Means over fp32 samples [sets][n][d] with fp64 centroids
+// [sets][2^code_bits][d], d = 4 or 8 (init may equal centroids), optional fp16 codebook
 // and final assignment outputs, workspace of kmeans_workspace_bytes.
 hipError_t launch_calibrate_lambda(const void* keys, bool kv_f32, int num_kv_heads,
                                    int num_tokens, float* lambda, hipStream_t stream);
 hipError_t launch_transform_keys(const void* keys, bool kv_f32, const float* lambda,
                                  int num_kv_heads, int num_tokens, float* out,
                                  hipStream_t stream);
-size_t kmeans_workspace_bytes(int num_sets, int num_samples, int code_bits);
-hipError_t launch_kmeans(const float* samples, int num_sets, int num_samples, int code_bits,
-                         const double* init, int iters, double* centroids, uint16_t* codebook,
-                         int32_t* assign, void* workspace, hipStream_t stream);
+size_t kmeans_workspace_bytes(int num_sets, int num_samples, int sub_dim, int code_bits);
+hipError_t launch_kmeans(const float* samples, int num_sets, int num_samples, int sub_dim,
+                         int code_bits, const double* init, int iters, double* centroids,
+                         uint16_t* codebook, int32_t* assign, void* workspace,
+                         hipStream_t stream);
 
 // Tokens one workgroup of the VQ split kernel processes per tile; split
 // lengths are multiples of it.

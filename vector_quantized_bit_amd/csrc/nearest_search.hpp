@@ -174,16 +174,12 @@ __device__ __forceinline__ int max_lanes16_32(int x, int lane) {
     return max(x, static_cast<int>(lane_partner<32>(static_cast<uint32_t>(x), lane)));
 }
 
-template <int NENT, int SUB, typename Block, typename Exact>
-__device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu,
-                                                   const float* __restrict__ ccd, Block block,
-                                                   float ex, int lane, Exact exact) {
+// The whole search over NENT centroids, the norm terms given by cup / cdown.
+template <int NENT, typename Block, typename Cop, typename Exact>
+__device__ __forceinline__ uint32_t nearest16_search(Block block, Cop cup, Cop cdown, float ex,
+                                                     int lane, Exact exact) {
     static_assert(NENT % (16 * kSearchUnroll) == 0, "whole unrolled groups");
     const int q4 = 4 * (lane >> 4);   // this lane's first centroid row in a block
-    const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(ccu + q4);
-    const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(ccd + q4);
-    const auto cup = [&](int blk) { return ucol[blk * 4]; };
-    const auto cdown = [&](int blk) { return dcol[blk * 4]; };
 
     // pass 1: thr = min over c of s(c) + E(c)
     float smin = search_pass1(block, cup, 0, NENT / 16);
@@ -209,6 +205,47 @@ __device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu
     take_lanes16_32(bd, bi, lane);
     return bi;
 }
+
+// Norm terms precomputed in LDS: ccu, ccd [NENT] fp32, 16-byte aligned.
+template <int NENT, int SUB, typename Block, typename Exact>
+__device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu,
+                                                   const float* __restrict__ ccd, Block block,
+                                                   float ex, int lane, Exact exact) {
+    const int q4 = 4 * (lane >> 4);
+    const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(ccu + q4);
+    const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(ccd + q4);
+    struct Col {
+        const f32x4_t* p;
+        __device__ f32x4_t operator()(int blk) const { return p[blk * 4]; }
+    };
+    return nearest16_search<NENT>(block, Col{ucol}, Col{dcol}, ex, lane, exact);
+}
+
+// One norm table [NENT] (fp32 ||c||^2, 16-byte aligned), scaled by
+// (1 +- 2^-16) as it is read.
+struct ScaledNorms {
+    const f32x4_t* p;
+    float scale;
+    __device__ f32x4_t operator()(int blk) const { return p[blk * 4] * scale; }
+};
+
+// The MFMA score of one block of 16 centroids, d = 8, fp32 centroids laid
+// out channel-pair-major: tab [4 pairs][NENT][2] (the 16 lanes of a group
+// read 16 consecutive 8-byte pairs: no bank conflicts); b0, b1 = -2x of
+// channels 2 (lane / 16) and 2 (lane / 16) + 1 of sub-vector lane % 16.
+template <int NENT>
+struct BlockF32D8 {
+    const float2* acol;
+    float b0, b1;
+    __device__ BlockF32D8(const float* tab, float b0_, float b1_, int lane)
+        : acol(reinterpret_cast<const float2*>(tab) + (lane >> 4) * NENT + (lane & 15)),
+          b0(b0_), b1(b1_) {}
+    __device__ f32x4_t operator()(int blk, f32x4_t c) const {
+        const float2 a = acol[blk * 16];
+        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b0, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b1, d, 0, 0, 0);
+    }
+};
 
 // The MFMA score of one block of 16 centroids for the d = 8 layout: ctab
 // [.][8] fp16 centroids, b0, b1 = -2x of channels 2 (lane / 16) and

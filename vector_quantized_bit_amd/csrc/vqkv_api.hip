@@ -627,12 +627,14 @@ int check_calib_keys(const void* keys, int kv_dtype, int32_t num_kv_heads, int32
 constexpr int32_t kMaxKmeansSamples = 1 << 28;
 constexpr int32_t kMaxKmeansIters = 10000;
 
-int check_kmeans_shape(int32_t num_sets, int32_t num_samples, int32_t code_bits) {
+int check_kmeans_shape(int32_t num_sets, int32_t num_samples, int32_t sub_dim, int32_t code_bits) {
     if (num_sets < 1 || num_sets > 65535)
         return fail(VQ_ERR_INVALID_ARG, "num_sets %d out of range [1, 65535]", num_sets);
     if (num_samples < 1 || num_samples > kMaxKmeansSamples)
         return fail(VQ_ERR_INVALID_ARG, "num_samples %d out of range [1, %d]", num_samples,
                     kMaxKmeansSamples);
+    if (sub_dim != 4 && sub_dim != 8)
+        return fail(VQ_ERR_UNSUPPORTED, "sub_dim %d unsupported (4 or 8)", sub_dim);
     if (code_bits != 8 && code_bits != 12)
         return fail(VQ_ERR_UNSUPPORTED, "code_bits %d unsupported (8 or 12)", code_bits);
     return VQ_OK;
@@ -664,17 +666,19 @@ int vq_transform_keys(const void* keys, int kv_dtype, const float* lambda, int32
                       "transform_keys launch");
 }
 
-size_t vq_kmeans_workspace_bytes(int32_t num_sets, int32_t num_samples, int32_t code_bits) {
+size_t vq_kmeans_workspace_bytes(int32_t num_sets, int32_t num_samples, int32_t sub_dim,
+                                 int32_t code_bits) {
     if (num_sets < 1 || num_sets > 65535 || num_samples < 1 || num_samples > kMaxKmeansSamples ||
-        (code_bits != 8 && code_bits != 12))
+        (sub_dim != 4 && sub_dim != 8) || (code_bits != 8 && code_bits != 12))
         return 0;
-    return vqkv::kmeans_workspace_bytes(num_sets, num_samples, code_bits);
+    return vqkv::kmeans_workspace_bytes(num_sets, num_samples, sub_dim, code_bits);
 }
 
-int vq_kmeans(const float* samples, int32_t num_sets, int32_t num_samples, int32_t code_bits,
-              const double* init, int32_t iters, double* centroids, uint16_t* codebook,
-              int32_t* assign, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_kmeans_shape(num_sets, num_samples, code_bits);
+int vq_kmeans(const float* samples, int32_t num_sets, int32_t num_samples, int32_t sub_dim,
+              int32_t code_bits, const double* init, int32_t iters, double* centroids,
+              uint16_t* codebook, int32_t* assign, void* workspace, size_t workspace_bytes,
+              void* stream) {
+    int st = check_kmeans_shape(num_sets, num_samples, sub_dim, code_bits);
     if (st) return st;
     if (iters < 0 || iters > kMaxKmeansIters)
         return fail(VQ_ERR_INVALID_ARG, "iters %d out of range [0, %d]", iters, kMaxKmeansIters);
@@ -685,12 +689,12 @@ int vq_kmeans(const float* samples, int32_t num_sets, int32_t num_samples, int32
         return fail(VQ_ERR_INVALID_ARG, "codebook is not 16-byte aligned");
     if (assign != nullptr && !aligned16(assign))
         return fail(VQ_ERR_INVALID_ARG, "assign is not 16-byte aligned");
-    const size_t need = vqkv::kmeans_workspace_bytes(num_sets, num_samples, code_bits);
+    const size_t need = vqkv::kmeans_workspace_bytes(num_sets, num_samples, sub_dim, code_bits);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
     if (!aligned16(workspace)) return fail(VQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    return hip_status(vqkv::launch_kmeans(samples, num_sets, num_samples, code_bits, init, iters,
+    return hip_status(vqkv::launch_kmeans(samples, num_sets, num_samples, sub_dim, code_bits, init, iters,
                                           centroids, codebook, assign, workspace,
                                           static_cast<hipStream_t>(stream)),
                       "kmeans launch");
