@@ -262,6 +262,11 @@ def test_decode_step_plan_leaves_room_for_the_new_token_workgroups(lib):
     assert need == 2 * a256(4 * 32 * n) + a256(4 * 128 * 32 * n)
     # the first token of a sequence: no cached tokens, one empty split
     assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 0, 0) == 2
+    # 128 streams (16 sequences x 8 heads): two splits each fill the 256 CUs,
+    # the 128 new-token workgroups run after them
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 16, 32, 32767, 0) == 3
+    # 64 streams: 192 split workgroups beside the 64 new-token ones
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 8, 32, 65535, 0) == 4
 
 
 def wstep(lib, layout, codes=10, wlen=0, wcap=128, splits=0, kv_dtype=0, kn=A, vn=A, wk=A, wv=A,

@@ -190,10 +190,9 @@ struct Chunk8 {
 template <int G>
 __device__ __forceinline__ void new_token_inputs(const void* q, int q_f32, const float* lambda,
                                                  const void* k_new, const void* v_new, int kv_f32,
-                                                 int num_q_heads, int num_kv_heads, int wave,
-                                                 int lane, float& x0, float& x1,
+                                                 int num_q_heads, int num_kv_heads, int g, int b,
+                                                 int wave, int lane, float& x0, float& x1,
                                                  double (*xnew)[kHeadDim]) {
-    const int g = blockIdx.y, b = blockIdx.z;
     x0 = 0.f;
     x1 = 0.f;
     if (wave < G) {
@@ -255,13 +254,12 @@ __device__ __forceinline__ void new_token_inputs(const void* q, int q_f32, const
 template <int G, int KBITS>
 __device__ __forceinline__ void new_token_workgroup(
     const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
-    const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads,
-    int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v, Partials part,
-    int part_stride, int slot, uint8_t* tab, uint8_t* scratch, double (*xnew)[kHeadDim],
-    uint32_t (*newc)[kNumSub]) {
+    const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads, int g,
+    int b, int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v,
+    Partials part, int part_stride, int slot, uint8_t* tab, uint8_t* scratch,
+    double (*xnew)[kHeadDim], uint32_t (*newc)[kNumSub]) {
     constexpr int KENT = 1 << KBITS;
     constexpr int kVtab = 32768;
-    const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
     const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
@@ -269,8 +267,8 @@ __device__ __forceinline__ void new_token_workgroup(
     if (tid < 256) reinterpret_cast<uint2*>(tab + kVtab)[tid] = vsrc[tid];
 
     float x0, x1;
-    new_token_inputs<G>(q, q_f32, lambda, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, wave,
-                        lane, x0, x1, xnew);
+    new_token_inputs<G>(q, q_f32, lambda, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, g, b,
+                        wave, lane, x0, x1, xnew);
     __syncthreads();
 
     // 1. codes
@@ -380,12 +378,11 @@ __device__ __forceinline__ void new_token_workgroup(
 template <int G>
 __device__ __forceinline__ void new_token_workgroup8(
     const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
-    const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads,
-    int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v, Partials part,
-    int part_stride, int slot, uint8_t* tab, uint8_t* scratch, uint8_t* xbuf,
+    const void* k_new, const void* v_new, int kv_f32, int num_q_heads, int num_kv_heads, int g,
+    int b, int capacity, int append_pos, uint8_t* new_codes_k, uint8_t* new_codes_v,
+    Partials part, int part_stride, int slot, uint8_t* tab, uint8_t* scratch, uint8_t* xbuf,
     double (*xnew)[kHeadDim], uint32_t (*newc)[kNumSub]) {
     constexpr int kEnt = 4096, kPos = kHeadDim / 8, kRow = kPos * 12 / 8;   // 16 codes, 24 B
-    const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint4* ksrc = reinterpret_cast<const uint4*>(cb_k) + static_cast<size_t>(g) * kEnt;
     const uint4* vsrc = reinterpret_cast<const uint4*>(cb_v) + static_cast<size_t>(g) * kEnt;
@@ -396,8 +393,8 @@ __device__ __forceinline__ void new_token_workgroup8(
         reinterpret_cast<uint4*>(tab + kTable)[i] = vsrc[i];
     }
     float x0, x1;
-    new_token_inputs<G>(q, q_f32, lambda, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, wave,
-                        lane, x0, x1, xnew);
+    new_token_inputs<G>(q, q_f32, lambda, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, g, b,
+                        wave, lane, x0, x1, xnew);
     __syncthreads();
 
     // 1. codes, one tensor after the other
@@ -541,11 +538,10 @@ __device__ __forceinline__ void new_token_workgroup8(
 template <int G>
 __device__ __forceinline__ void window_workgroup(
     const void* q, int q_f32, const void* k_new, const void* v_new, int kv_f32, int num_q_heads,
-    int num_kv_heads, uint16_t* win_k, uint16_t* win_v, int win_len, int win_cap, Partials part,
-    int part_stride, int slot, float* lds) {
+    int num_kv_heads, int g, int b, uint16_t* win_k, uint16_t* win_v, int win_len, int win_cap,
+    Partials part, int part_stride, int slot, float* lds) {
     constexpr float kScale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
     constexpr int kWords = kHeadDim / 2;                                  // fp16 pairs per row
-    const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t stream = static_cast<size_t>(b) * num_kv_heads + g;
@@ -675,25 +671,32 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     __shared__ double xnew[2][kHeadDim];
     __shared__ uint32_t newc[2][kNumSub];   // its key and value codes
 
-    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // A 1-D grid, split-major: the workgroups of split s of every stream
+    // (sequence, KV head) follow those of split s - 1, and the extra
+    // workgroups (split == num_splits: the new token or the window) come
+    // last, so every split workgroup is dispatched before any of them.
+    const int streams = static_cast<int>(gridDim.x) / (num_splits + (append_pos >= 0 ? 1 : 0));
+    const int split = static_cast<int>(blockIdx.x) / streams;
+    const int stream_id = static_cast<int>(blockIdx.x) - split * streams;
+    const int g = stream_id % num_kv_heads, b = stream_id / num_kv_heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: tile indices stay in SGPRs
     if (append_pos >= 0 && split == num_splits && win_k != nullptr) {   // the residual window
-        window_workgroup<G>(q, q_f32, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, win_k, win_v,
-                            win_len, win_cap, part, part_stride, num_splits,
+        window_workgroup<G>(q, q_f32, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, g, b, win_k,
+                            win_v, win_len, win_cap, part, part_stride, num_splits,
                             reinterpret_cast<float*>(tab));
         return;
     }
     if (append_pos >= 0 && split == num_splits) {   // the extra, new-token workgroup
         if constexpr (kD8)
             new_token_workgroup8<G>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
-                                    num_q_heads, num_kv_heads, capacity, append_pos, new_codes_k,
+                                    num_q_heads, num_kv_heads, g, b, capacity, append_pos, new_codes_k,
                                     new_codes_v, part, part_stride, num_splits, tab,
                                     reinterpret_cast<uint8_t*>(&pbuf[0][0]),
                                     reinterpret_cast<uint8_t*>(&qa[0][0]), xnew, newc);
         else
             new_token_workgroup<G, KBITS>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
-                                          num_q_heads, num_kv_heads, capacity, append_pos,
+                                          num_q_heads, num_kv_heads, g, b, capacity, append_pos,
                                           new_codes_k, new_codes_v, part, part_stride,
                                           num_splits, tab,
                                           reinterpret_cast<uint8_t*>(&pbuf[0][0]), xnew, newc);
@@ -1167,7 +1170,7 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
     const bool app = ap.k_new != nullptr;
     const int pos = app ? ap.append_pos : -1;
     const int stride = s.num_splits + (app ? 1 : 0);
-    const dim3 full(grid.x + (app ? 1 : 0), grid.y, grid.z);
+    const dim3 full((grid.x + (app ? 1 : 0)) * grid.y * grid.z);   // split-major, see the kernel
 #define VQKV_LAUNCH(GG)                                                                       \
     case GG:                                                                                  \
         hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS, SUB>), full, dim3(kThreads), 0, \

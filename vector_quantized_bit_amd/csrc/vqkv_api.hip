@@ -325,8 +325,15 @@ int check_step_args(const vq_layout* layout, const void* q, int q_dtype, const v
 
 // A decode step splits the cur_len cached tokens over the workgroups that one
 // per (sequence, KV head) new-token workgroup leaves free.
+// The split kernel of a decode step launches the splits of every stream and
+// then one extra workgroup per stream (the new token, or the window), all
+// split workgroups first.  With few streams the extra workgroups get CUs of
+// their own next to the splits (256 - streams split workgroups); from 128
+// streams on that would give half the chip or more to short workgroups, so
+// the splits fill all 256 CUs and the extra workgroups run after them.
 SplitPlan plan_step(int streams, int cur_len, int requested) {
-    const int target = kTargetWorkgroups > 2 * streams ? kTargetWorkgroups - streams : streams;
+    const int target = kTargetWorkgroups > 2 * streams ? kTargetWorkgroups - streams
+                                                       : kTargetWorkgroups;
     return plan_splits(streams, cur_len > 0 ? cur_len : 1, requested, vqkv::kVqTile, target,
                        vqkv::kVqTileGrain);
 }
