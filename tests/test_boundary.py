@@ -250,7 +250,7 @@ def test_decode_step_partials_validation(lib):
     assert "part_l" in vq._last_error()
 
 
-def test_decode_step_plan_leaves_room_for_the_new_token_workgroups(lib):
+def test_decode_step_plan_folds_or_leaves_room_for_the_new_token(lib):
     layout = lay(hkv=8, cap=196609)
     n = lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 196608, 0)
     assert n == 32                                   # 31 splits x 8 heads + 8 = 256 workgroups
@@ -263,10 +263,20 @@ def test_decode_step_plan_leaves_room_for_the_new_token_workgroups(lib):
     # the first token of a sequence: no cached tokens, one empty split
     assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 0, 0) == 2
     # 128 streams (16 sequences x 8 heads): two splits each fill the 256 CUs,
-    # the 128 new-token workgroups run after them
+    # the new token folded into the last
     assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 16, 32, 32767, 0) == 3
-    # 64 streams: 192 split workgroups beside the 64 new-token ones
-    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 8, 32, 65535, 0) == 4
+    # 64 streams: four splits each, folded
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 8, 32, 65535, 0) == 5
+    big = lay(k_bits=12, hkv=8, cap=65600)
+    assert lib.vq_decode_step_num_partials(ctypes.byref(big), 8, 40, 65535, 0) == 5
+    # 32 streams of short contexts do not fold: 4096 tokens give 8 sweeps of
+    # 512 (beside 32 new-token workgroups)
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 4, 32, 4096, 0) == 8
+    # an explicit split count is a fixed point, folded or not
+    for bsz, cur, req in ((1, 196608, 7), (1, 196608, 32), (4, 4096, 3), (8, 65535, 4),
+                          (16, 32767, 1)):
+        m = lib.vq_decode_step_num_partials(ctypes.byref(layout), bsz, 32, cur, req)
+        assert lib.vq_decode_step_num_partials(ctypes.byref(layout), bsz, 32, cur, m - 1) == m
 
 
 def wstep(lib, layout, codes=10, wlen=0, wcap=128, splits=0, kv_dtype=0, kn=A, vn=A, wk=A, wv=A,
@@ -302,6 +312,10 @@ def test_decode_step_window_plan(lib):
     # coded tokens split as in a decode step, plus the window's partial
     assert np_(ctypes.byref(layout), 1, 32, 196608, 0) == \
         lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 196608, 0) == 32
+    # many streams: a decode step folds its new token, a window step keeps its
+    # extra workgroups beside 256 - 64 split workgroups (3 splits per stream)
+    assert np_(ctypes.byref(layout), 8, 32, 65535, 0) == 4
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 8, 32, 65535, 0) == 5
     # no coded tokens: the window workgroup alone, one partial
     assert np_(ctypes.byref(layout), 1, 32, 0, 0) == 1
     assert np_(ctypes.byref(layout), 1, 32, -1, 0) == 0

@@ -399,6 +399,53 @@ def test_decode_step_groups_and_widths(group, k_bits, cur, splits):
     check_step(random_cache(wl), cur, splits, what=f"step G={group} kbits={k_bits} cur={cur}")
 
 
+def test_decode_step_exact_ties_go_to_lowest_index():
+    # C_k's second half repeats its first (4096 entries, 12-bit keys) and C_v's
+    # does too (256 entries): every sub-vector of the new token has two
+    # nearest centroids at exactly the same distance, in different waves of
+    # the key search, and must take the lower index
+    wl = W.Workload(95, "adhoc", batch=2, num_q_heads=8, num_kv_heads=2, context_len=600,
+                    k_bits=12)
+    c = random_cache(wl)
+    hk, hv = c.cb_k[:, :2048], c.cb_v[:, :128]
+    c = dataclasses.replace(c, cb_k=np.ascontiguousarray(np.concatenate([hk, hk], axis=1)),
+                            cb_v=np.ascontiguousarray(np.concatenate([hv, hv], axis=1)))
+    _, ck, cv = check_step(c, 599, what="step exact ties")
+    assert oracle.unpack_codes(ck[:, :, 599].reshape(-1, 48), 12, 32).max() < 2048
+    assert cv[:, :, 599].max() < 128
+
+
+@pytest.mark.parametrize("k_bits,group,splits", [(8, 4, 2), (8, 4, 1), (12, 5, 2), (12, 1, 1)])
+def test_decode_step_folded(k_bits, group, splits):
+    # 32 streams with splits long against the new token's encode (20000 or
+    # 40000 cached tokens in one or two splits): the last split of each stream
+    # encodes the new token before attending over its own, shorter range
+    n = 20000 if k_bits == 8 else 40000
+    wl = W.Workload(96 + group, "adhoc", batch=8, num_q_heads=4 * group, num_kv_heads=4,
+                    context_len=n + 1, k_bits=k_bits)
+    c = random_cache(wl)
+    check_step(c, n, splits, heads=[(0, 0), (3, 1), (5, 2), (7, 3)],
+               what=f"folded step kbits={k_bits} G={group} S={splits}")
+
+
+def test_decode_step_folded_equals_append_then_attend():
+    wl = W.Workload(99, "adhoc", batch=8, num_q_heads=16, num_kv_heads=4, context_len=30001,
+                    k_bits=12)
+    c = random_cache(wl)
+    cur = 30000
+    k, v = new_rows(wl, 8, 4, np.float16)
+    d1, d2 = upload(c), upload(c)
+    out1 = vq.decode_step(d1["q"], dev(k), dev(v), d1["lam"], d1["cb_k"], d1["cb_v"],
+                          d1["codes_k"], d1["codes_v"], cur, num_splits=2)   # folded
+    vq.encode_append(dev(k[:, :, None]), dev(v[:, :, None]), d2["lam"], d2["cb_k"], d2["cb_v"],
+                     d2["codes_k"], d2["codes_v"], cur)
+    out2 = vq.decode_attention(d2["q"], d2["lam"], d2["cb_k"], d2["cb_v"], d2["codes_k"],
+                               d2["codes_v"], cur + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(d1["codes_k"], d2["codes_k"]) and torch.equal(d1["codes_v"], d2["codes_v"])
+    np.testing.assert_allclose(out1.cpu().numpy(), out2.cpu().numpy(), rtol=1e-5, atol=1e-6)
+
+
 def test_decode_step_tiny_recipe_case(tiny):
     # the chain's last token appended by the step: the oracle's own codes and
     # attention over the whole chain (fp32 rows)

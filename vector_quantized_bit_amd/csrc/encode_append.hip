@@ -34,13 +34,6 @@ __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
     return static_cast<double>(half_bits_to_float(reinterpret_cast<const uint16_t*>(p)[i]));
 }
 
-// ||c||^2 of an fp16 centroid: the squares are exact in fp32, the sums rounded
-__device__ __forceinline__ float norm2(const uint2 c) {
-    const float c0 = half_bits_to_float(c.x & 0xffffu), c1 = half_bits_to_float(c.x >> 16);
-    const float c2 = half_bits_to_float(c.y & 0xffffu), c3 = half_bits_to_float(c.y >> 16);
-    return (c0 * c0 + c1 * c1) + (c2 * c2 + c3 * c3);
-}
-
 // The nearest centroid of sub-vector rb*16 + lane % 16 of `xs` ([8 tokens]
 // [128] fp64 = [256 sub-vectors][4]) among NENT fp16 centroids staged as -2c
 // by channel (m2) and bound-scaled squared norms (cu, cd).

@@ -37,6 +37,9 @@ struct AppendArgs {
     uint16_t* win_v = nullptr;
     int win_len = 0;
     int win_cap = 0;
+    // No extra workgroup: the last split of every stream encodes the new token
+    // (and leaves its one-token partial) before attending over its tokens.
+    bool fold = false;
 };
 
 // Split-K decode attention over the VQ cache on the matrix cores: one

@@ -44,6 +44,14 @@ constexpr int kSearchStride = NENT + 16;
 constexpr float kBoundUp = 1.0f + 0x1p-16f;
 constexpr float kBoundDown = 1.0f - 0x1p-16f;
 
+// ||c||^2 of a 4-dim fp16 centroid: the squares are exact in fp32, the sums
+// rounded
+__device__ __forceinline__ float norm2(const uint2 c) {
+    const float c0 = half_bits_to_float(c.x & 0xffffu), c1 = half_bits_to_float(c.x >> 16);
+    const float c2 = half_bits_to_float(c.y & 0xffffu), c3 = half_bits_to_float(c.y >> 16);
+    return (c0 * c0 + c1 * c1) + (c2 * c2 + c3 * c3);
+}
+
 // ex[i] of a row from its fp32 squared norm
 __device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * xx) + 1e-30f; }
 
@@ -71,6 +79,15 @@ __device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * 
 // ||c||^2 (1 + 2^-16) / (1 - 2^-16).
 constexpr int kSearchUnroll = 8;
 
+// the minimum of one group's scores in this lane
+__device__ __forceinline__ float group_min(const f32x4_t (&d)[kSearchUnroll]) {
+    float m = INFINITY;
+#pragma unroll
+    for (int u = 0; u < kSearchUnroll; ++u)
+        m = fminf(m, fminf(fminf(d[u][0], d[u][1]), fminf(d[u][2], d[u][3])));
+    return m;
+}
+
 // pass 1: this lane's minimum of s(c) + E(c) (without the ||x||^2 part)
 template <typename Block, typename Cop>
 __device__ __forceinline__ float search_pass1(Block block, Cop cup, int b0, int b1) {
@@ -80,9 +97,7 @@ __device__ __forceinline__ float search_pass1(Block block, Cop cup, int b0, int 
         f32x4_t d[kSearchUnroll];
 #pragma unroll
         for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cup(blk + u));
-#pragma unroll
-        for (int u = 0; u < kSearchUnroll; ++u)
-            smin = fminf(smin, fminf(fminf(d[u][0], d[u][1]), fminf(d[u][2], d[u][3])));
+        smin = fminf(smin, group_min(d));
     }
     return smin;
 }
@@ -99,6 +114,8 @@ __device__ __forceinline__ void search_pass2(Block block, Cop cdown, int b0, int
         f32x4_t d[kSearchUnroll];
 #pragma unroll
         for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cdown(blk + u));
+        // hits are rare: a group with none in the whole wave is skipped
+        if (__builtin_amdgcn_ballot_w64(group_min(d) <= thr) == 0) continue;
         // the group's last hit as u * 4 + r (an inline constant, 0 .. 31),
         // turned into a centroid row once per group
         const int before = cnt;
@@ -126,14 +143,9 @@ __device__ __forceinline__ void search_pass3(Block block, Cop cdown, int b0, int
 #pragma nounroll
     for (int blk = b0; blk < b1; blk += kSearchUnroll) {
         f32x4_t d[kSearchUnroll];
-        bool any = false;
 #pragma unroll
-        for (int u = 0; u < kSearchUnroll; ++u) {
-            d[u] = block(blk + u, cdown(blk + u));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) any |= d[u][r] <= thr;
-        }
-        if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
+        for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cdown(blk + u));
+        if (__builtin_amdgcn_ballot_w64(group_min(d) <= thr) == 0) continue;
 #pragma unroll
         for (int u = 0; u < kSearchUnroll; ++u) {
 #pragma unroll

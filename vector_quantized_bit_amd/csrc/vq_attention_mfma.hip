@@ -235,6 +235,151 @@ __device__ __forceinline__ void new_token_inputs(const void* q, int q_f32, const
     }
 }
 
+// LDS of the new-token workgroup with 12-bit keys (offsets into `tab`):
+// C_k as -2c by channel [4][kSearchStride<4096>] fp32, its bound-scaled
+// squared norms ||c||^2 (1 + 2^-16) and (1 - 2^-16), C_v (fp16), and 4 KiB
+// for the exchanges of the key search.
+constexpr int kNtStride = kSearchStride<4096>;
+constexpr int kNtCu = 4 * kNtStride * 4;
+constexpr int kNtCd = kNtCu + 4096 * 4;
+constexpr int kNtV = kNtCd + 4096 * 4;
+constexpr int kNtX = kNtV + 256 * 8;
+static_assert(kNtX + 4096 <= 2 * kTable, "the 12-bit new-token tables fit the LDS tables");
+
+// Stage C_k of 4096 entries for new_token_keys12: -2c by channel and the
+// bound-scaled norms (the loads issued before any is used).
+__device__ __forceinline__ void stage_keys12(const uint2* __restrict__ ksrc, uint8_t* tab,
+                                             int tid) {
+    float* m2 = reinterpret_cast<float*>(tab);
+    float* cu = reinterpret_cast<float*>(tab + kNtCu);
+    float* cd = reinterpret_cast<float*>(tab + kNtCd);
+    constexpr int kPer = 4096 / kThreads;
+    uint2 c[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) c[j] = ksrc[tid + j * kThreads];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * kThreads;
+        m2[0 * kNtStride + i] = -2.f * half_bits_to_float(c[j].x & 0xffffu);
+        m2[1 * kNtStride + i] = -2.f * half_bits_to_float(c[j].x >> 16);
+        m2[2 * kNtStride + i] = -2.f * half_bits_to_float(c[j].y & 0xffffu);
+        m2[3 * kNtStride + i] = -2.f * half_bits_to_float(c[j].y >> 16);
+        const float nn = norm2(c[j]);
+        cu[i] = nn * kBoundUp;
+        cd[i] = nn * kBoundDown;
+    }
+}
+
+// The key codes of the appended token for 4096-entry C_k (d = 4), found by
+// the certified matrix-core search of nearest_search.hpp spread over the 16
+// waves: wave w takes sub-vectors 16 (w / 8) .. + 15 (one MFMA column block)
+// and centroids 512 (w % 8) .. + 511.  The 8 waves of a column block meet in
+// LDS three times: pass-1 minima (the threshold), candidate counts (a
+// sub-vector with exactly one candidate takes it), and, only when some
+// sub-vector has several, the fp64 minima over their candidates.  The
+// decisions are those of the fp64 scan: ties to the lowest index.
+//   tab   the tables of stage_keys12 (and 4 KiB of exchanges at kNtX)
+//   xk    the transformed key (fp64); codes[32] receives the codes
+// Ends with a barrier; codes is then visible to the whole workgroup.
+__device__ __forceinline__ void new_token_keys12(uint8_t* tab, const double* xk, uint32_t* codes,
+                                                 int tid, int lane, int wave) {
+    constexpr int kEnt = 4096, kCb = 8;   // waves per column block
+    static_assert(kThreads == 1024 && kEnt == (kWaves / 2) * 512, "8 waves of 512 centroids");
+    const float* m2 = reinterpret_cast<const float*>(tab);
+    uint8_t* xbuf = tab + kNtX;
+    float* wmin = reinterpret_cast<float*>(xbuf);      // [16 waves][16] pass-1 minima
+    int* wcnt = reinterpret_cast<int*>(xbuf + 1024);   // [16][16] candidate counts
+    int* wcand = reinterpret_cast<int*>(xbuf + 2048);  // [16][16] a candidate (or -1)
+    int* flag = reinterpret_cast<int*>(xbuf + 3072);   // [32] several candidates
+    double* wbd = reinterpret_cast<double*>(xbuf);     // [16][16] (reuses the above)
+    uint32_t* wbi = reinterpret_cast<uint32_t*>(xbuf + 2048);
+    const int cb = wave / kCb, sv = 16 * cb + (lane & 15), q4 = 4 * (lane >> 4);
+    double xd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xd[j] = xk[4 * sv + j];
+    float xx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float v = static_cast<float>(xd[j]);
+        xx += v * v;
+    }
+    const float bx = static_cast<float>(xk[4 * sv + (lane >> 4)]);   // B: channel lane / 16
+    const float* acol = m2 + (lane >> 4) * kNtStride + (lane & 15);
+    const auto block = [&](int blk, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(acol[blk * 16], bx, c, 0, 0, 0);
+    };
+    const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(tab + kNtCu) + lane / 16;
+    const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(tab + kNtCd) + lane / 16;
+    const auto cup = [&](int blk) { return ucol[blk * 4]; };
+    const auto cdown = [&](int blk) { return dcol[blk * 4]; };
+    // the fp16 centroid, recovered exactly from -2c
+    const auto exact = [&](uint32_t nc) {
+        double dd = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double c = -0.5 * static_cast<double>(m2[j * kNtStride + nc]);
+            const double e = __dadd_rn(xd[j], -c);
+            dd = j == 0 ? __dmul_rn(e, e) : __dadd_rn(dd, __dmul_rn(e, e));
+        }
+        return dd;
+    };
+    const int b0 = 32 * (wave % kCb), b1 = b0 + 32;   // this wave's centroid blocks
+    float smin = search_pass1(block, cup, b0, b1);
+    smin = fminf(smin, lane_partner<16>(smin, lane));
+    smin = fminf(smin, lane_partner<32>(smin, lane));
+    if (lane < 16) wmin[wave * 16 + lane] = smin;
+    __syncthreads();
+    float gmin = wmin[cb * kCb * 16 + (lane & 15)];
+    for (int w = 1; w < kCb; ++w) gmin = fminf(gmin, wmin[(cb * kCb + w) * 16 + (lane & 15)]);
+    const float thr = gmin + row_bound(xx);
+    int cnt, cand;
+    search_pass2(block, cdown, b0, b1, thr, cnt, cand);
+    cnt = sum_lanes16_32(cnt, lane);
+    cand = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
+    if (lane < 16) {
+        wcnt[wave * 16 + lane] = cnt;
+        wcand[wave * 16 + lane] = cand;
+    }
+    __syncthreads();
+    if (tid < kNumSub) {   // sub-vector tid: column block tid / 16, column tid % 16
+        const int w0 = (tid / 16) * kCb, c = tid & 15;
+        int total = 0, one = -1;
+        for (int w = w0; w < w0 + kCb; ++w) {
+            total += wcnt[w * 16 + c];
+            one = max(one, wcnt[w * 16 + c] > 0 ? wcand[w * 16 + c] : -1);
+        }
+        codes[tid] = static_cast<uint32_t>(one) & (kEnt - 1);
+        flag[tid] = total != 1;
+    }
+    __syncthreads();
+    bool several = false;
+    for (int k = 0; k < kNumSub; ++k) several |= flag[k] != 0;
+    if (several) {   // uniform: fp64 resolution of every sub-vector's candidates
+        double bd;
+        uint32_t bi;
+        search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi);
+        take_lanes16_32(bd, bi, lane);
+        if (lane < 16) {
+            wbd[wave * 16 + lane] = bd;
+            wbi[wave * 16 + lane] = bi;
+        }
+        __syncthreads();
+        if (tid < kNumSub) {
+            const int w0 = (tid / 16) * kCb, c = tid & 15;
+            double d0 = wbd[w0 * 16 + c];
+            uint32_t i0 = wbi[w0 * 16 + c];
+            for (int w = w0 + 1; w < w0 + kCb; ++w) {
+                if (nearer(wbd[w * 16 + c], wbi[w * 16 + c], d0, i0)) {
+                    d0 = wbd[w * 16 + c];
+                    i0 = wbi[w * 16 + c];
+                }
+            }
+            codes[tid] = i0 & (kEnt - 1);   // (a code always exists for finite inputs)
+        }
+    }
+    __syncthreads();
+}
+
 // The appended token of one (sequence, KV head), handled by one extra
 // workgroup of the split kernel while the others attend over the cached
 // tokens (VecInfer page, Method details, "VQ KV cache in attention": each
@@ -243,14 +388,17 @@ __device__ __forceinline__ void new_token_inputs(const void* q, int q_f32, const
 // concatenated to the cache before the query attends).
 //  1. Codes: the nearest centroid of each 4-dim sub-vector (Background, VQ
 //     principle), distances in fp64 with every operation rounded separately,
-//     ties to the lowest index: the decisions of vq_encode_append.  Thread
-//     (slice, pos) scans centroids slice, slice + 32, ... of sub-vector pos;
-//     the 32 slices are combined by the lexicographic (distance, index)
-//     minimum.  The codes are written to the cache slot append_pos.
+//     ties to the lowest index: the decisions of vq_encode_append.  For a
+//     256-entry codebook thread (slice, pos) scans centroids slice,
+//     slice + 32, ... of sub-vector pos, and the 32 slices are combined by
+//     the lexicographic (distance, index) minimum; 12-bit keys take the
+//     matrix-core search of new_token_keys12.  The codes are written to the
+//     cache slot append_pos.
 //  2. Its attention partial, as one more split of one token: m = x (its
 //     base-2 score), l = 1, o = its dequantised value, at split index `slot`.
-// LDS: the codebooks unreplicated in `tab` (keys at 0, values at 32 KiB),
-// the scratch of the combination in `scratch` (the p buffers).
+// LDS: the codebooks unreplicated in `tab` (keys at 0, values at 32 KiB; for
+// 12-bit keys the tables of stage_keys12), the scratch of the combination in
+// `scratch` (the p buffers).
 template <int G, int KBITS>
 __device__ __forceinline__ void new_token_workgroup(
     const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
@@ -259,11 +407,14 @@ __device__ __forceinline__ void new_token_workgroup(
     Partials part, int part_stride, int slot, uint8_t* tab, uint8_t* scratch,
     double (*xnew)[kHeadDim], uint32_t (*newc)[kNumSub]) {
     constexpr int KENT = 1 << KBITS;
-    constexpr int kVtab = 32768;
+    constexpr int kVtab = KBITS == 12 ? kNtV : 32768;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
     const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
-    for (int i = tid; i < KENT; i += kThreads) reinterpret_cast<uint2*>(tab)[i] = ksrc[i];
+    if constexpr (KBITS == 12)
+        stage_keys12(ksrc, tab, tid);
+    else
+        for (int i = tid; i < KENT; i += kThreads) reinterpret_cast<uint2*>(tab)[i] = ksrc[i];
     if (tid < 256) reinterpret_cast<uint2*>(tab + kVtab)[tid] = vsrc[tid];
 
     float x0, x1;
@@ -281,11 +432,13 @@ __device__ __forceinline__ void new_token_workgroup(
     }
     double dk = INFINITY, dv = INFINITY;
     uint32_t ik = 0, iv = 0;
-    for (int c = slice; c < KENT; c += 32) {
-        const double d = sqdist4_f64(xk, reinterpret_cast<const uint2*>(tab)[c]);
-        if (d < dk) {
-            dk = d;
-            ik = static_cast<uint32_t>(c);
+    if constexpr (KBITS == 8) {   // 12-bit keys: the matrix-core search below
+        for (int c = slice; c < KENT; c += 32) {
+            const double d = sqdist4_f64(xk, reinterpret_cast<const uint2*>(tab)[c]);
+            if (d < dk) {
+                dk = d;
+                ik = static_cast<uint32_t>(c);
+            }
         }
     }
 #pragma unroll 2
@@ -327,7 +480,7 @@ __device__ __forceinline__ void new_token_workgroup(
                 i0 = i;
             }
         }
-        newc[tsel][pos] = i0;
+        if (tsel || KBITS == 8) newc[tsel][pos] = i0;
         if (tsel) {
             new_codes_v[row * kNumSub + pos] = static_cast<uint8_t>(i0);
         } else if constexpr (KBITS == 8) {
@@ -336,6 +489,7 @@ __device__ __forceinline__ void new_token_workgroup(
     }
     __syncthreads();
     if constexpr (KBITS == 12) {
+        new_token_keys12(tab, xnew[0], newc[0], tid, lane, wave);
         // byte j of the row holds bits [8j, 8j + 8) of the 12-bit stream
         if (tid < 48) {
             const int bit = 8 * tid, i0 = bit / 12, sh = bit % 12;
@@ -349,11 +503,20 @@ __device__ __forceinline__ void new_token_workgroup(
     //    components 2 (l % 2), + 1 of sub-vector l / 2
     if (wave < G) {
         const int j = lane >> 1, comp = 2 * (lane & 1);
-        const uint2 kc = reinterpret_cast<const uint2*>(tab)[newc[0][j]];
+        float k0, k1;
+        if constexpr (KBITS == 12) {   // exact: -2c holds the fp16 value times -2
+            const float* m2 = reinterpret_cast<const float*>(tab);
+            k0 = -0.5f * m2[comp * kNtStride + newc[0][j]];
+            k1 = -0.5f * m2[(comp + 1) * kNtStride + newc[0][j]];
+        } else {
+            const uint2 kc = reinterpret_cast<const uint2*>(tab)[newc[0][j]];
+            const uint32_t kw = comp ? kc.y : kc.x;
+            k0 = half_bits_to_float(kw & 0xffffu);
+            k1 = half_bits_to_float(kw >> 16);
+        }
         const uint2 vc = reinterpret_cast<const uint2*>(tab + kVtab)[newc[1][j]];
-        const uint32_t kw = comp ? kc.y : kc.x, vw = comp ? vc.y : vc.x;
-        const float x = wave_sum(x0 * half_bits_to_float(kw & 0xffffu) +
-                                 x1 * half_bits_to_float(kw >> 16));
+        const uint32_t vw = comp ? vc.y : vc.x;
+        const float x = wave_sum(x0 * k0 + x1 * k1);
         const size_t pi = (static_cast<size_t>(b) * num_q_heads + g * G + wave) * part_stride + slot;
         part.o[pi * kHeadDim + 2 * lane] = half_bits_to_float(vw & 0xffffu);
         part.o[pi * kHeadDim + 2 * lane + 1] = half_bits_to_float(vw >> 16);
@@ -648,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     Partials part, const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
     int append_pos, uint8_t* __restrict__ new_codes_k, uint8_t* __restrict__ new_codes_v,
     int part_stride, uint16_t* __restrict__ win_k, uint16_t* __restrict__ win_v, int win_len,
-    int win_cap) {
+    int win_cap, int fold) {
     static_assert(G >= 1 && G <= 8, "2G MFMA rows");
     // G <= 4: the rows of every head are in lanes 0-31 of an MFMA result, so
     // the softmax packs a tile's two 16-token blocks into one set of lanes
@@ -674,8 +837,11 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // A 1-D grid, split-major: the workgroups of split s of every stream
     // (sequence, KV head) follow those of split s - 1, and the extra
     // workgroups (split == num_splits: the new token or the window) come
-    // last, so every split workgroup is dispatched before any of them.
-    const int streams = static_cast<int>(gridDim.x) / (num_splits + (append_pos >= 0 ? 1 : 0));
+    // last, so every split workgroup is dispatched before any of them.  With
+    // `fold` there are no extra workgroups: the last split of a stream
+    // encodes the new token first, then attends over its own tokens.
+    const int extra = (append_pos >= 0 && !fold) ? 1 : 0;
+    const int streams = static_cast<int>(gridDim.x) / (num_splits + extra);
     const int split = static_cast<int>(blockIdx.x) / streams;
     const int stream_id = static_cast<int>(blockIdx.x) - split * streams;
     const int g = stream_id % num_kv_heads, b = stream_id / num_kv_heads;
@@ -687,7 +853,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
                             reinterpret_cast<float*>(tab));
         return;
     }
-    if (append_pos >= 0 && split == num_splits) {   // the extra, new-token workgroup
+    if (append_pos >= 0 && split == num_splits - 1 + extra) {   // the new token
         if constexpr (kD8)
             new_token_workgroup8<G>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
                                     num_q_heads, num_kv_heads, g, b, capacity, append_pos, new_codes_k,
@@ -700,7 +866,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
                                           new_codes_k, new_codes_v, part, part_stride,
                                           num_splits, tab,
                                           reinterpret_cast<uint8_t*>(&pbuf[0][0]), xnew, newc);
-        return;
+        if (extra) return;
+        __syncthreads();   // the LDS is free for the split
     }
     const int grp = lane >> 4, n = lane & 15;
     const int kq = n >> 2, aq4 = n & 3;   // fetch-lane split of n for the transposed reads
@@ -1166,11 +1333,14 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
                          const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
                          const AppendArgs& ap, hipStream_t stream) {
     // with an append, one more workgroup per (sequence, KV head) encodes the
-    // new token (split index num_splits) and leaves its one-token partial
+    // new token (or, folded, the last split does) and leaves its one-token
+    // partial at split index num_splits
     const bool app = ap.k_new != nullptr;
+    const bool fold = app && ap.fold && ap.win_k == nullptr;
     const int pos = app ? ap.append_pos : -1;
     const int stride = s.num_splits + (app ? 1 : 0);
-    const dim3 full((grid.x + (app ? 1 : 0)) * grid.y * grid.z);   // split-major, see the kernel
+    const dim3 full((grid.x + (app && !fold ? 1 : 0)) * grid.y * grid.z);   // split-major
+    if (fold && s.num_splits < 1) return hipErrorInvalidValue;
 #define VQKV_LAUNCH(GG)                                                                       \
     case GG:                                                                                  \
         hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS, SUB>), full, dim3(kThreads), 0, \
@@ -1178,7 +1348,7 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
                            s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
                            s.num_splits, s.tokens_per_split, part, ap.k_new, ap.v_new,        \
                            ap.kv_f32 ? 1 : 0, pos, ap.codes_k, ap.codes_v, stride,           \
-                           ap.win_k, ap.win_v, ap.win_len, ap.win_cap);                      \
+                           ap.win_k, ap.win_v, ap.win_len, ap.win_cap, fold ? 1 : 0);        \
         break;
     switch (group) {
         VQKV_LAUNCH(1)

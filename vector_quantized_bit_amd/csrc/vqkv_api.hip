@@ -78,6 +78,7 @@ int check_heads(int batch, int num_q_heads, int num_kv_heads) {
 struct SplitPlan {
     int num_splits;
     int tokens_per_split;
+    bool fold = false;   // decode step: the last split encodes the new token
 };
 
 // Splits hold at least `min_len` tokens (one sweep of the workgroup) and a
@@ -323,24 +324,55 @@ int check_step_args(const vq_layout* layout, const void* q, int q_dtype, const v
                                 num_q_heads, cur_len + 1, num_splits);
 }
 
-// A decode step splits the cur_len cached tokens over the workgroups that one
-// per (sequence, KV head) new-token workgroup leaves free.
-// The split kernel of a decode step launches the splits of every stream and
-// then one extra workgroup per stream (the new token, or the window), all
-// split workgroups first.  With few streams the extra workgroups get CUs of
-// their own next to the splits (256 - streams split workgroups); from 128
-// streams on that would give half the chip or more to short workgroups, so
-// the splits fill all 256 CUs and the extra workgroups run after them.
-SplitPlan plan_step(int streams, int cur_len, int requested) {
+// The new token's encode in cached tokens that one split workgroup attends
+// over in the same time, rounded up: the encode takes about 7 us with
+// 256-entry C_k and 18-27 us with 4096 entries while the other splits load
+// the chip, and a split takes 3.7-4.1 ns per token (MI355X, timestamps).
+// Too large a value only lengthens the other splits a little; too small a
+// one makes the last split the slowest.  0 where the encode is not folded
+// (d = 8).
+int fold_tokens(const vq_layout* layout) {
+    if (layout->sub_dim != 4) return 0;
+    return layout->k_code_bits == 8 ? 2048 : 8192;
+}
+
+// From this many streams on, a decode step may fold the new token into the
+// last split of each stream.  With fewer, the extra workgroups beside the
+// splits take at most 1/8 of the CUs, and folding measured slower (8 streams
+// of 196608 tokens: split pass 23.2 us folded, 22.3 us with 8 extra
+// workgroups), the balance of a folded last split being the harder part.
+constexpr int kFoldStreams = 32;
+
+// The split kernel of a decode step.
+//  - Many streams with long splits: every stream's splits take all 256 CUs,
+//    and the last split of each stream encodes the new token before its
+//    tokens; it is shorter than the others by the encode's worth of tokens
+//    (splits of (cur_len + fold) / S tokens, the last one taking the rest).
+//  - Otherwise one extra workgroup per stream (the new token, or the window)
+//    follows the splits, all split workgroups first.  With few streams the
+//    extra workgroups get CUs of their own next to the splits (256 - streams
+//    split workgroups); from 128 streams on that would give half the chip or
+//    more to short workgroups, so the splits fill all 256 CUs and the extra
+//    workgroups run after them.
+// A window step never folds (fold = 0).
+SplitPlan plan_step(int streams, int cur_len, int requested, int fold = 0) {
+    const int n = cur_len > 0 ? cur_len : 1;
+    if (fold > 0 && streams >= kFoldStreams) {
+        const SplitPlan f = plan_splits(streams, n + fold, requested, vqkv::kVqTile,
+                                        kTargetWorkgroups, vqkv::kVqTileGrain);
+        // every split keeps tokens, and the encode is a small part of one
+        if ((f.num_splits - 1) * f.tokens_per_split < n && f.tokens_per_split >= 2 * fold)
+            return SplitPlan{f.num_splits, f.tokens_per_split, true};
+    }
     const int target = kTargetWorkgroups > 2 * streams ? kTargetWorkgroups - streams
                                                        : kTargetWorkgroups;
-    return plan_splits(streams, cur_len > 0 ? cur_len : 1, requested, vqkv::kVqTile, target,
-                       vqkv::kVqTileGrain);
+    return plan_splits(streams, n, requested, vqkv::kVqTile, target, vqkv::kVqTileGrain);
 }
 
 vqkv::AppendArgs append_args(const void* k_new, const void* v_new, int kv_dtype, int cur_len,
-                             uint8_t* codes_k, uint8_t* codes_v) {
+                             uint8_t* codes_k, uint8_t* codes_v, bool fold) {
     vqkv::AppendArgs app;
+    app.fold = fold;
     app.k_new = k_new;
     app.v_new = v_new;
     app.kv_f32 = kv_dtype == VQ_F32;
@@ -410,7 +442,8 @@ int32_t vq_decode_step_num_partials(const vq_layout* layout, int32_t batch, int3
     if (layout == nullptr || batch < 1 || cur_len < 0 || layout->num_kv_heads < 1 ||
         requested < 0)
         return 0;
-    return plan_step(batch * layout->num_kv_heads, cur_len, requested).num_splits + 1;
+    return plan_step(batch * layout->num_kv_heads, cur_len, requested, fold_tokens(layout))
+               .num_splits + 1;
 }
 
 size_t vq_decode_step_workspace_bytes(const vq_layout* layout, int32_t batch,
@@ -431,7 +464,7 @@ int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
     if (st) return st;
     if ((st = check_partials_ptrs(part_m, part_l, part_o))) return st;
     const SplitPlan p = plan_step(batch * layout->num_kv_heads, cur_len,
-                                  num_partials > 1 ? num_partials - 1 : 1);
+                                  num_partials > 1 ? num_partials - 1 : 1, fold_tokens(layout));
     if (num_partials != p.num_splits + 1)
         return fail(VQ_ERR_INVALID_ARG,
                     "num_partials %d is not a planned count for this shape "
@@ -443,7 +476,7 @@ int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
     return hip_status(vqkv::launch_vq_attention(
                           shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
                           codes_k, codes_v, part,
-                          append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v),
+                          append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v, p.fold),
                           static_cast<hipStream_t>(stream)),
                       "decode_step_partials launch");
 }
@@ -457,7 +490,8 @@ int vq_decode_step(const vq_layout* layout, const void* q, int q_dtype, const vo
                              codes_k, codes_v, batch, num_q_heads, cur_len, num_splits);
     if (st) return st;
     VQ_REQUIRE_PTR(out);
-    const SplitPlan p = plan_step(batch * layout->num_kv_heads, cur_len, num_splits);
+    const SplitPlan p = plan_step(batch * layout->num_kv_heads, cur_len, num_splits,
+                                  fold_tokens(layout));
     const int nparts = p.num_splits + 1;
     const size_t need = partials_bytes(batch, num_q_heads, nparts);
     if (workspace == nullptr || workspace_bytes < need)
@@ -471,7 +505,7 @@ int vq_decode_step(const vq_layout* layout, const void* q, int q_dtype, const vo
     st = hip_status(vqkv::launch_vq_attention(
                         shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
                         codes_k, codes_v, part,
-                        append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v), s),
+                        append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v, p.fold), s),
                     "decode_step launch");
     if (st) return st;
     return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, nparts, part, out, s),
