@@ -116,6 +116,44 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
+def measured_counters(workload: str) -> dict | None:
+    """Per-dispatch shader counters of the split kernel (waves, instructions,
+    LDS activity) from the committed counter record of this workload, or None
+    when there is no record or the kernel sources have changed since."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return dict(rec["per_dispatch"], source=os.path.relpath(path, ROOT))
+
+
+def sampled_parity(oracle, wl: W.Workload, q, lam, cb_k, cb_v, codes_k, codes_v, out,
+                   heads) -> dict:
+    """The GPU output of sequence 0 against the fp64 oracle for the given KV
+    heads, over the codes as they are on the device (the timed steps have
+    appended tokens to them): rel-L2 and max-abs over those query heads."""
+    g = wl.group
+    got, ref = [], []
+    for h in heads:
+        ref.append(oracle.decode_attention_head(
+            q[0, h * g:(h + 1) * g], lam[h], cb_k[h], cb_v[h], codes_k[h], codes_v[h],
+            wl.k_bits, wl.v_bits))
+        got.append(out[0, h * g:(h + 1) * g].astype(np.float64))
+    got, ref = np.concatenate(got), np.concatenate(ref)
+    return {"kv_heads": list(heads), "sequence": 0, "context_len": wl.context_len,
+            "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+            "max_abs": float(np.abs(got - ref).max()),
+            "bound": {"rel_l2": 1e-3, "max_abs": 2e-3}}
+
+
+def percentiles(us: np.ndarray) -> dict:
+    return {"median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90)), "calls": int(us.size)}
+
+
 def measured_traffic(workload: str) -> dict | None:
     """HBM bytes per attention launch from the committed counter record of
     this workload (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what
@@ -393,6 +431,22 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     call_us = ev0.elapsed_time(ev1) * 1e3 / steps
 
+    # 3b. the same calls and the steps one by one, each between its own event
+    #     pair (an event costs the stream a few microseconds, so these read
+    #     higher than the back-to-back averages): the spread of a call
+    def per_call(calls):
+        ea = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        eb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        head_start()
+        for i in range(steps):
+            ea[i].record()
+            calls[i % copies](stream)
+            eb[i].record()
+        torch.cuda.synchronize()
+        return percentiles(np.array([ea[i].elapsed_time(eb[i]) * 1e3 for i in range(steps)]))
+    call_pct = per_call(attends)
+    step_pct = per_call(steps_fused)
+
     # 4. decode steps with a full-precision residual window of 128 tokens at
     #    the same total length: n - 128 coded tokens, window slots 0..127
     #    (slot 127 takes the new token), and the flush that encodes a full
@@ -469,8 +523,13 @@ def main(argv=None) -> int:
                                "flush_us": flush_us, "flush_tokens_per_stream": win},
         "decode_attention": {"avg_us": call_us,
                              "gbps": ab_attn["total"] / (call_us * 1e-6) / 1e9,
-                             "kernels": "vq_attention_mfma_kernel + merge_partials_kernel"},
+                             "kernels": "vq_attention_mfma_kernel + merge_partials_kernel",
+                             "per_call_us": call_pct},
+        "decode_step_per_call_us": step_pct,
     }
+    counters = measured_counters(wl.name)
+    if counters is not None:
+        result["roofline"]["counters"] = counters
     copy_gbps = copy_bandwidth(torch, dev, head_start)
     result["roofline"]["copy_gbps"] = copy_gbps
     result["roofline"]["frac_of_copy"] = achieved / copy_gbps
@@ -513,6 +572,16 @@ def main(argv=None) -> int:
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        # the same leg checks the output of one more call against the oracle
+        import oracle
+        ck, cv = caches[0]
+        attends[0](stream)
+        torch.cuda.synchronize()
+        heads = sorted({0, hkv - 1})
+        result["cpu_baseline"]["parity"] = sampled_parity(
+            oracle, wl, q.cpu().numpy(), lam.cpu().numpy(), cb_k.cpu().numpy(),
+            cb_v.cpu().numpy(), {h: ck[0, h].cpu().numpy() for h in heads},
+            {h: cv[0, h].cpu().numpy() for h in heads}, out.cpu().numpy(), heads)
 
     print(json.dumps(result), flush=True)
     return 0
