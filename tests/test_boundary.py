@@ -176,6 +176,19 @@ def test_plan_splits_is_a_fixed_point(lib):
     assert plan(ctypes.byref(layout), 1, 32, 100, -1) == 0
 
 
+def test_split_plan_keeps_each_split_under_2gib_of_codes(lib):
+    # a split's code rows are addressed through a 32-bit byte range: an
+    # explicit request of one split over 100 M tokens of 48-byte rows is
+    # raised to the smallest count that keeps every split under 2^31 bytes
+    layout = lay(k_bits=12, hkv=1, cap=100_000_000)
+    s = lib.vq_decode_attention_plan_splits(ctypes.byref(layout), 1, 4, 100_000_000, 1)
+    assert s == 3
+    assert lib.vq_decode_attention_plan_splits(ctypes.byref(layout), 1, 4, 100_000_000, s) == s
+    # the default plan is far below the bound
+    d = lib.vq_decode_attention_plan_splits(ctypes.byref(layout), 1, 4, 100_000_000, 0)
+    assert (100_000_000 + d - 1) // d * 48 < 2 ** 31
+
+
 def partials(lib, layout, splits=1, n=100, pm=A, pl=A, po=A, **kw):
     args = dict(q=A, q_dtype=0, lam=A, cbk=A, cbv=A, ck=A, cv=A, batch=1, hq=4)
     args.update(kw)

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void fp16_attention_split_kernel(
     }
 
     const int t_begin = split * tokens_per_split;
-    const int t_end = min(context_len, t_begin + tokens_per_split);
+    const int t_end = t_begin + min(tokens_per_split, context_len - t_begin);   // no int overflow
     const size_t row0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity;
     const uint4* k4 = reinterpret_cast<const uint4*>(k);
     const uint4* v4 = reinterpret_cast<const uint4*>(v);

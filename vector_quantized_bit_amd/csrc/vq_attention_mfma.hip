@@ -873,7 +873,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const int kq = n >> 2, aq4 = n & 3;   // fetch-lane split of n for the transposed reads
 
     const int t_begin = split * tokens_per_split;
-    const int t_len = min(context_len, t_begin + tokens_per_split) - t_begin;
+    const int t_len = min(tokens_per_split, context_len - t_begin);   // no int overflow
     const size_t row0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + t_begin;
     const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(codes_k + row0 * KROW), 0, t_len * KROW, kBufferWord3);

@@ -81,14 +81,23 @@ struct SplitPlan {
     bool fold = false;   // decode step: the last split encodes the new token
 };
 
-// Splits hold at least `min_len` tokens (one sweep of the workgroup) and a
-// multiple of `gran` tokens (one wave tile); the last split takes the rest.
+// The VQ split kernel addresses one split's code rows through a buffer
+// resource whose byte range is a 32-bit count: a split holds fewer than 2^31
+// bytes of its widest rows (48 B), rounded down to whole wave tiles.
+constexpr int kVqMaxSplitTokens = (0x7fffffff / 48) / 32 * 32;
+
+// Splits hold at least `min_len` tokens (one sweep of the workgroup), at most
+// `max_len`, and a multiple of `gran` tokens (one wave tile); the last split
+// takes the rest.  A requested count is clamped into that range.
 SplitPlan plan_splits(int streams, int context_len, int requested, int min_len,
-                      int target = kTargetWorkgroups, int gran = 0) {
+                      int target = kTargetWorkgroups, int gran = 0,
+                      int max_len = kVqMaxSplitTokens) {
     if (gran <= 0) gran = min_len;
     int max_splits = (context_len + min_len - 1) / min_len;
     if (max_splits > vqkv::kMaxSplits) max_splits = vqkv::kMaxSplits;
     int s = requested > 0 ? requested : (target + streams - 1) / streams;
+    const int min_splits = static_cast<int>((static_cast<int64_t>(context_len) + max_len - 1) / max_len);
+    if (s < min_splits) s = min_splits;
     if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;
     const int per = (context_len + s - 1) / s;
