@@ -26,19 +26,6 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
-    return v;
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
 
 // The value held by the lane at distance M (lane ^ M) of the wave, for one
 // 32-bit word: DPP for M = 1, 2, 4, 8, a gfx950 permlane swap for 16 and 32,
@@ -84,6 +71,32 @@ __device__ __forceinline__ double lane_partner(double x, int lane) {
     u.x = lane_partner<M>(u.x, lane);
     u.y = lane_partner<M>(u.y, lane);
     return __builtin_bit_cast(double, u);
+}
+
+// Maximum and sum over the 64 lanes of a wave, in every lane: butterfly
+// stages at distance 32, 16, ..., 1 through lane_partner (no LDS round
+// trip).  Each stage combines a lane with its partner symmetrically, so every
+// lane ends with the same value.  Every lane must be active.
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    v = max(v, lane_partner<32>(v, lane));
+    v = max(v, lane_partner<16>(v, lane));
+    v = max(v, lane_partner<8>(v, lane));
+    v = max(v, lane_partner<4>(v, lane));
+    v = max(v, lane_partner<2>(v, lane));
+    return max(v, lane_partner<1>(v, lane));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    v += lane_partner<32>(v, lane);
+    v += lane_partner<16>(v, lane);
+    v += lane_partner<8>(v, lane);
+    v += lane_partner<4>(v, lane);
+    v += lane_partner<2>(v, lane);
+    return v + lane_partner<1>(v, lane);
 }
 
 // One butterfly stage at lane distance M: the lane with bit M clear keeps

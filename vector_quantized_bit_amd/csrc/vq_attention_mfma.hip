@@ -686,6 +686,18 @@ __device__ __forceinline__ void new_token_workgroup8(
     }
 }
 
+// Sum over the L lanes of an aligned group (L = 16 or 32), in every lane of
+// the group.
+template <int L>
+__device__ __forceinline__ float group_sum(float v, int lane) {
+    static_assert(L == 16 || L == 32, "lane group");
+    if constexpr (L == 32) v += lane_partner<16>(v, lane);
+    v += lane_partner<8>(v, lane);
+    v += lane_partner<4>(v, lane);
+    v += lane_partner<2>(v, lane);
+    return v + lane_partner<1>(v, lane);
+}
+
 // The residual-window workgroup of one (sequence, KV head), for a decode
 // step that keeps the most recent tokens in full precision (VecInfer page,
 // Experiments: a residual of 128 full-precision tokens beside the VQ cache;
@@ -694,8 +706,10 @@ __device__ __forceinline__ void new_token_workgroup8(
 //  1. The new token's k and v, rounded to fp16, go to window slot win_len.
 //  2. The G query heads attend over window tokens 0 .. win_len with raw
 //     keys: q . k / sqrt(D), which equals q~ . k~ (H_D orthonormal), so the
-//     window needs no transform.  Wave w takes tokens w, w + 16, ...; lane l
-//     holds dims 2l, 2l + 1; every wave keeps an online softmax per head.
+//     window needs no transform.  Wave w takes tokens 2w, 2w + 1, then
+//     2w + 32, 2w + 33, ...: each half of the wave (32 lanes, 4 channels per
+//     lane) keeps an online softmax per head over its tokens, and the two
+//     halves combine before the fold.
 //  3. The 16 wave states fold in LDS into one partial (m, l, o) at split
 //     index `slot`, in the base-2 units of the code splits.
 template <int G>
@@ -711,21 +725,8 @@ __device__ __forceinline__ void window_workgroup(
     uint32_t* wk = reinterpret_cast<uint32_t*>(win_k) + stream * win_cap * kWords;
     uint32_t* wv = reinterpret_cast<uint32_t*>(win_v) + stream * win_cap * kWords;
 
-    float qx[G], qy[G];   // the raw query of every head, scaled to base-2 scores
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + h;
-        if (q_f32) {
-            const float2 f = reinterpret_cast<const float2*>(q)[vec * kWords + lane];
-            qx[h] = f.x * kScale;
-            qy[h] = f.y * kScale;
-        } else {
-            const uint32_t w = reinterpret_cast<const uint32_t*>(q)[vec * kWords + lane];
-            qx[h] = half_bits_to_float(w & 0xffffu) * kScale;
-            qy[h] = half_bits_to_float(w >> 16) * kScale;
-        }
-    }
-    // the new token as the window stores it (fp16, round to nearest even)
+    // the new token as the window stores it (fp16, round to nearest even),
+    // written to slot win_len by wave 0, two channels per lane
     uint32_t kn, vn;
     if (kv_f32) {
         const float2 a = reinterpret_cast<const float2*>(k_new)[stream * kWords + lane];
@@ -741,47 +742,129 @@ __device__ __forceinline__ void window_workgroup(
         wv[static_cast<size_t>(win_len) * kWords + lane] = vn;
     }
 
-    float m[G], l[G], ox[G], oy[G];
+    // A wave takes kGrp tokens at a time, one per group of kGl lanes; lane
+    // `sub` of a group holds channels kDl sub .. kDl sub + kDl - 1, so a score
+    // is kDl products and a reduction over the group's lanes.  Heads go in
+    // passes of at most 4 (the registers of one pass stay below those of the
+    // split path).
+    constexpr int kGrp = 2;
+    constexpr int kGl = kWave / kGrp;
+    constexpr int kDl = kHeadDim / kGl;   // channels per lane
+    constexpr int kDw = kDl / 2;          // fp16 pairs per lane
+    constexpr int kGh = G < 4 ? G : 4;    // heads per pass
+    const int grp = lane / kGl, sub = lane % kGl;
+    uint32_t knd[kDw], vnd[kDw];   // the new token in this lane's channels
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = ox[h] = oy[h] = 0.f;
-    }
-    for (int t = wave; t <= win_len; t += kWaves) {
-        uint32_t kw = kn, vw = vn;   // slot win_len: the new token, from registers
-        if (t < win_len) {
-            kw = wk[static_cast<size_t>(t) * kWords + lane];
-            vw = wv[static_cast<size_t>(t) * kWords + lane];
-        }
-        const float kx = half_bits_to_float(kw & 0xffffu), ky = half_bits_to_float(kw >> 16);
-        const float vx = half_bits_to_float(vw & 0xffffu), vy = half_bits_to_float(vw >> 16);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float sc = wave_sum(qx[h] * kx + qy[h] * ky);
-            const float mn = fmaxf(m[h], sc);
-            const float f = (m[h] == -INFINITY) ? 0.f : fast_exp2(m[h] - mn);
-            const float p = fast_exp2(sc - mn);
-            l[h] = l[h] * f + p;
-            ox[h] = ox[h] * f + p * vx;
-            oy[h] = oy[h] * f + p * vy;
-            m[h] = mn;
+    for (int j = 0; j < kDw; ++j) {
+        const size_t w = stream * kWords + sub * kDw + j;
+        if (kv_f32) {
+            const float2 a = reinterpret_cast<const float2*>(k_new)[w];
+            const float2 c = reinterpret_cast<const float2*>(v_new)[w];
+            knd[j] = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(a.x), static_cast<_Float16>(a.y)});
+            vnd[j] = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(c.x), static_cast<_Float16>(c.y)});
+        } else {
+            knd[j] = reinterpret_cast<const uint32_t*>(k_new)[w];
+            vnd[j] = reinterpret_cast<const uint32_t*>(v_new)[w];
         }
     }
-
-    // fold: LDS m, l [kWaves][G] and o [kWaves][G][128]
-    float* fm = lds;
+    float* fm = lds;   // fold: LDS m, l [kWaves][G] and o [kWaves][G][128]
     float* fl = fm + kWaves * G;
     float* fo = fl + kWaves * G;
-    if (lane == 0) {
+    constexpr int kStep = kWaves * kGrp;
+    const int last_row = win_len > 0 ? win_len - 1 : 0;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            fm[wave * G + h] = m[h];
-            fl[wave * G + h] = l[h];
+    for (int h0 = 0; h0 < G; h0 += kGh) {
+        constexpr int kN = kGh;
+        float qd[kN][kDl];   // the raw query of each head of the pass, scaled to base-2 scores
+        float m[kN], l[kN], o[kN][kDl];
+#pragma unroll
+        for (int hh = 0; hh < kN; ++hh) {
+            m[hh] = -INFINITY;
+            l[hh] = 0.f;
+#pragma unroll
+            for (int j = 0; j < kDl; ++j) o[hh][j] = qd[hh][j] = 0.f;
+            if (h0 + hh >= G) continue;
+            const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + h0 + hh;
+#pragma unroll
+            for (int j = 0; j < kDw; ++j) {
+                const size_t w = vec * kWords + sub * kDw + j;
+                if (q_f32) {
+                    const float2 f = reinterpret_cast<const float2*>(q)[w];
+                    qd[hh][2 * j] = f.x * kScale;
+                    qd[hh][2 * j + 1] = f.y * kScale;
+                } else {
+                    const uint32_t x = reinterpret_cast<const uint32_t*>(q)[w];
+                    qd[hh][2 * j] = half_bits_to_float(x & 0xffffu) * kScale;
+                    qd[hh][2 * j + 1] = half_bits_to_float(x >> 16) * kScale;
+                }
+            }
+        }
+        // kGrp tokens per step (the clamped slot keeps every load in the
+        // window and unconditional)
+        for (int t0 = wave * kGrp; t0 <= win_len; t0 += kStep) {
+            const int t = t0 + grp;
+            const bool valid = t <= win_len;
+            const size_t r = static_cast<size_t>(min(t, last_row)) * kWords + sub * kDw;
+            uint32_t kw[kDw], vw[kDw];
+#pragma unroll
+            for (int j = 0; j < kDw; ++j) {
+                kw[j] = wk[r + j];
+                vw[j] = wv[r + j];
+            }
+            if (t == win_len) {   // slot win_len: the new token, from registers
+#pragma unroll
+                for (int j = 0; j < kDw; ++j) {
+                    kw[j] = knd[j];
+                    vw[j] = vnd[j];
+                }
+            }
+            float sc[kN];
+#pragma unroll
+            for (int hh = 0; hh < kN; ++hh) {
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < kDw; ++j) {
+                    acc += qd[hh][2 * j] * half_bits_to_float(kw[j] & 0xffffu);
+                    acc += qd[hh][2 * j + 1] * half_bits_to_float(kw[j] >> 16);
+                }
+                sc[hh] = group_sum<kGl>(acc, lane);
+            }
+#pragma unroll
+            for (int hh = 0; hh < kN; ++hh) {
+                const float mn = valid ? fmaxf(m[hh], sc[hh]) : m[hh];
+                const float f = (m[hh] == -INFINITY) ? 0.f : fast_exp2(m[hh] - mn);
+                const float p = valid ? fast_exp2(sc[hh] - mn) : 0.f;
+                l[hh] = l[hh] * f + p;
+#pragma unroll
+                for (int j = 0; j < kDw; ++j) {
+                    o[hh][2 * j] = o[hh][2 * j] * f + p * half_bits_to_float(vw[j] & 0xffffu);
+                    o[hh][2 * j + 1] = o[hh][2 * j + 1] * f + p * half_bits_to_float(vw[j] >> 16);
+                }
+                m[hh] = mn;
+            }
+        }
+        // the two groups of the wave combined (log-sum-exp), the same in
+        // every lane; then the wave's m, l and o go to the LDS fold
+#pragma unroll
+        for (int hh = 0; hh < kN; ++hh) {
+            if (h0 + hh >= G) continue;
+            const int h = h0 + hh;
+            const float mx = fmaxf(m[hh], lane_partner<32>(m[hh], lane));
+            const float f = (m[hh] == -INFINITY) ? 0.f : fast_exp2(m[hh] - mx);
+            const float lh = l[hh] * f;
+            const float ls = lh + lane_partner<32>(lh, lane);
+            if (lane == 0) {
+                fm[wave * G + h] = mx;
+                fl[wave * G + h] = ls;
+            }
+#pragma unroll
+            for (int j = 0; j < kDl; ++j) {
+                const float oh = o[hh][j] * f;
+                const float os = oh + lane_partner<32>(oh, lane);
+                if (grp == 0) fo[(wave * G + h) * kHeadDim + sub * kDl + j] = os;
+            }
         }
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-        reinterpret_cast<float2*>(fo + (wave * G + h) * kHeadDim)[lane] = make_float2(ox[h], oy[h]);
     __syncthreads();
     for (int i = tid; i < G * kHeadDim; i += kThreads) {
         const int h = i / kHeadDim, d = i % kHeadDim;
