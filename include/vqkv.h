@@ -205,11 +205,13 @@ int vq_merge_partials(int32_t batch, int32_t num_q_heads, int32_t num_partials,
  * arrived key takes the online dual transform and is quantised with C_k,
  * the value with C_v, both are concatenated to the cache, and the query
  * attends over the updated cache.
- * Inside the launch, one extra workgroup per (sequence, KV head) encodes the
- * new token (fp64 decisions, ties to the lowest index, as vq_encode_append)
- * and leaves that token's own partial; the other workgroups attend over the
- * cur_len cached tokens in num_splits splits (0 = library default, which
- * leaves room on the GPU for the extra workgroups).
+ * Inside the launch, the new token of every (sequence, KV head) is encoded
+ * (fp64 decisions, ties to the lowest index, as vq_encode_append) and leaves
+ * that token's own partial, either in one extra workgroup per (sequence, KV
+ * head) or, with many streams and long splits, at the start of each stream's
+ * last split; the splits attend over the cur_len cached tokens in num_splits
+ * splits (0 = library default).  The library chooses between the two; the
+ * results are the same.
  *   k_new, v_new [B][Hkv][128] in kv_dtype (fp16 or fp32)
  *   codes_k / codes_v: read over [0, cur_len), written at slot cur_len only.
  *   workspace: at least vq_decode_step_workspace_bytes(...) bytes, any
