@@ -325,10 +325,13 @@ def test_decode_step_window_plan(lib):
     # coded tokens split as in a decode step, plus the window's partial
     assert np_(ctypes.byref(layout), 1, 32, 196608, 0) == \
         lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 196608, 0) == 32
-    # many streams: a decode step folds its new token, a window step keeps its
-    # extra workgroups beside 256 - 64 split workgroups (3 splits per stream)
+    # 64 streams: a decode step folds its new token (four splits per stream
+    # over all 256 CUs), a window step keeps 192 split workgroups (3 per
+    # stream) beside its 64 window workgroups
     assert np_(ctypes.byref(layout), 8, 32, 65535, 0) == 4
     assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 8, 32, 65535, 0) == 5
+    # 128 streams: two splits per stream either way (folded window)
+    assert np_(ctypes.byref(layout), 16, 32, 32767, 0) == 3
     # no coded tokens: the window workgroup alone, one partial
     assert np_(ctypes.byref(layout), 1, 32, 0, 0) == 1
     assert np_(ctypes.byref(layout), 1, 32, -1, 0) == 0

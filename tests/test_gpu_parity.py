@@ -584,6 +584,16 @@ def test_decode_step_window_groups_widths_dtypes(group, k_bits, dtype, num_codes
                       what=f"window G={group} kbits={k_bits} {dtype}")
 
 
+@pytest.mark.parametrize("win_len,splits", [(0, 2), (77, 2), (127, 1)])
+def test_decode_step_window_folded(win_len, splits):
+    # 128 streams with long splits: the last split of each stream attends over
+    # the window before its own coded tokens
+    wl = W.Workload(93, "adhoc", batch=32, num_q_heads=16, num_kv_heads=4, context_len=20000)
+    check_window_step(random_cache(wl), 20000, win_len, splits=splits,
+                      heads=[(0, 0), (9, 3), (22, 1), (31, 2)],
+                      what=f"folded window win={win_len} S={splits}")
+
+
 def test_decode_step_window_full_size():
     # the long-context layer: 196608 coded tokens and a nearly full window
     wl = W.WORKLOADS[4]

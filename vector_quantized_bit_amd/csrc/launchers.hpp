@@ -38,7 +38,8 @@ struct AppendArgs {
     int win_len = 0;
     int win_cap = 0;
     // No extra workgroup: the last split of every stream encodes the new token
-    // (and leaves its one-token partial) before attending over its tokens.
+    // (or attends over the window) and leaves that partial before attending
+    // over its own tokens.
     bool fold = false;
 };
 

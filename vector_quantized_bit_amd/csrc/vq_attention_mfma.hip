@@ -799,24 +799,34 @@ __device__ __forceinline__ void window_workgroup(
                 }
             }
         }
-        // kGrp tokens per step (the clamped slot keeps every load in the
-        // window and unconditional)
-        for (int t0 = wave * kGrp; t0 <= win_len; t0 += kStep) {
-            const int t = t0 + grp;
-            const bool valid = t <= win_len;
-            const size_t r = static_cast<size_t>(min(t, last_row)) * kWords + sub * kDw;
-            uint32_t kw[kDw], vw[kDw];
+        // kGrp tokens per step, the rows of kPre steps loaded before any is
+        // used: one memory latency per kPre steps, which matters when the
+        // window runs beside splits that load the chip (the clamped slot keeps
+        // every load in the window and unconditional)
+        constexpr int kPre = 4;
+        for (int t00 = wave * kGrp; t00 <= win_len; t00 += kPre * kStep) {
+          uint32_t kr[kPre][kDw], vr[kPre][kDw];
+#pragma unroll
+          for (int u = 0; u < kPre; ++u) {
+            const size_t r =
+                static_cast<size_t>(min(t00 + u * kStep + grp, last_row)) * kWords + sub * kDw;
 #pragma unroll
             for (int j = 0; j < kDw; ++j) {
-                kw[j] = wk[r + j];
-                vw[j] = wv[r + j];
+                kr[u][j] = wk[r + j];
+                vr[u][j] = wv[r + j];
             }
-            if (t == win_len) {   // slot win_len: the new token, from registers
+          }
 #pragma unroll
-                for (int j = 0; j < kDw; ++j) {
-                    kw[j] = knd[j];
-                    vw[j] = vnd[j];
-                }
+          for (int u = 0; u < kPre; ++u) {
+            const int t0 = t00 + u * kStep;
+            if (t0 > win_len) break;   // uniform in the wave
+            const int t = t0 + grp;
+            const bool valid = t <= win_len;
+            uint32_t kw[kDw], vw[kDw];
+#pragma unroll
+            for (int j = 0; j < kDw; ++j) {   // slot win_len: the new token, from registers
+                kw[j] = t == win_len ? knd[j] : kr[u][j];
+                vw[j] = t == win_len ? vnd[j] : vr[u][j];
             }
             float sc[kN];
 #pragma unroll
@@ -842,6 +852,7 @@ __device__ __forceinline__ void window_workgroup(
                 }
                 m[hh] = mn;
             }
+          }
         }
         // the two groups of the wave combined (log-sum-exp), the same in
         // every lane; then the wave's m, l and o go to the LDS fold
@@ -922,7 +933,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // workgroups (split == num_splits: the new token or the window) come
     // last, so every split workgroup is dispatched before any of them.  With
     // `fold` there are no extra workgroups: the last split of a stream
-    // encodes the new token first, then attends over its own tokens.
+    // encodes the new token (or attends over the window) first, then attends
+    // over its own tokens.
     const int extra = (append_pos >= 0 && !fold) ? 1 : 0;
     const int streams = static_cast<int>(gridDim.x) / (num_splits + extra);
     const int split = static_cast<int>(blockIdx.x) / streams;
@@ -930,13 +942,13 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const int g = stream_id % num_kv_heads, b = stream_id / num_kv_heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: tile indices stay in SGPRs
-    if (append_pos >= 0 && split == num_splits && win_k != nullptr) {   // the residual window
+    if (append_pos >= 0 && split == num_splits - 1 + extra && win_k != nullptr) {   // the window
         window_workgroup<G>(q, q_f32, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, g, b, win_k,
                             win_v, win_len, win_cap, part, part_stride, num_splits,
                             reinterpret_cast<float*>(tab));
-        return;
-    }
-    if (append_pos >= 0 && split == num_splits - 1 + extra) {   // the new token
+        if (extra) return;
+        __syncthreads();   // the LDS is free for the split
+    } else if (append_pos >= 0 && split == num_splits - 1 + extra) {   // the new token
         if constexpr (kD8)
             new_token_workgroup8<G>(q, q_f32, lambda, cb_k, cb_v, k_new, v_new, kv_f32,
                                     num_q_heads, num_kv_heads, g, b, capacity, append_pos, new_codes_k,
@@ -1419,7 +1431,7 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
     // new token (or, folded, the last split does) and leaves its one-token
     // partial at split index num_splits
     const bool app = ap.k_new != nullptr;
-    const bool fold = app && ap.fold && ap.win_k == nullptr;
+    const bool fold = app && ap.fold;
     const int pos = app ? ap.append_pos : -1;
     const int stride = s.num_splits + (app ? 1 : 0);
     const dim3 full((grid.x + (app && !fold ? 1 : 0)) * grid.y * grid.z);   // split-major

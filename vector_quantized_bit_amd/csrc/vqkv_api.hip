@@ -363,7 +363,8 @@ constexpr int kFoldStreams = 32;
 //    split workgroups); from 128 streams on that would give half the chip or
 //    more to short workgroups, so the splits fill all 256 CUs and the extra
 //    workgroups run after them.
-// A window step never folds (fold = 0).
+// A window step folds its window the same way from 128 streams on
+// (kWindowFoldTokens).
 SplitPlan plan_step(int streams, int cur_len, int requested, int fold = 0) {
     const int n = cur_len > 0 ? cur_len : 1;
     if (fold > 0 && streams >= kFoldStreams) {
@@ -393,9 +394,20 @@ vqkv::AppendArgs append_args(const void* k_new, const void* v_new, int kv_dtype,
 
 // A window step splits the num_codes coded tokens like a decode step; with
 // no coded tokens there is no code split, only the window workgroup.
+// The window's attention in cached tokens, rounded up like fold_tokens (a
+// 128-token window takes about 5 us alone, more in a loaded chip).  A window
+// step folds only from 128 streams on, where its window workgroups would
+// otherwise run after the splits: beside the splits (fewer streams) they
+// measured cheaper than folded (64 streams of 65536 tokens: window step
+// 76-86 us beside, 82-88 us folded; 128 streams of 32768: 68-70 us after,
+// 62-68 us folded).
+constexpr int kWindowFoldTokens = 3072;
+constexpr int kWindowFoldStreams = 128;
+
 SplitPlan plan_window_step(int streams, int num_codes, int requested) {
     if (num_codes == 0) return SplitPlan{0, 0};
-    return plan_step(streams, num_codes, requested);
+    return plan_step(streams, num_codes, requested,
+                     streams >= kWindowFoldStreams ? kWindowFoldTokens : 0);
 }
 
 int check_window_step_args(const vq_layout* layout, const void* q, int q_dtype,
@@ -429,8 +441,10 @@ int check_window_step_args(const vq_layout* layout, const void* q, int q_dtype,
 }
 
 vqkv::AppendArgs window_args(const void* k_new, const void* v_new, int kv_dtype, int num_codes,
-                             uint16_t* win_k, uint16_t* win_v, int win_len, int win_cap) {
+                             uint16_t* win_k, uint16_t* win_v, int win_len, int win_cap,
+                             bool fold) {
     vqkv::AppendArgs app;
+    app.fold = fold;
     app.k_new = k_new;
     app.v_new = v_new;
     app.kv_f32 = kv_dtype == VQ_F32;
@@ -567,7 +581,7 @@ int vq_decode_step_window(const vq_layout* layout, const void* q, int q_dtype, c
                         shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
                         codes_k, codes_v, part,
                         window_args(k_new, v_new, kv_dtype, num_codes, win_k, win_v, win_len,
-                                    win_cap),
+                                    win_cap, p.fold),
                         s),
                     "decode_step_window launch");
     if (st) return st;
