@@ -69,7 +69,7 @@ def cpu_baseline(wl: W.Workload, seconds: float) -> dict:
     have passed, scaled to KV tokens/s per layer.  Inputs are drawn before
     the clock starts."""
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     n, g = wl.context_len, wl.group
     q = W.queries(wl.config_id, 0, wl.num_q_heads).astype(np.float16)
@@ -82,20 +82,28 @@ def cpu_baseline(wl: W.Workload, seconds: float) -> dict:
                                         sub_dim=wl.sub_dim),
                       W.random_code_rows(wl.config_id, 0, h, "k", n, wl.k_row_bytes),
                       W.random_code_rows(wl.config_id, 0, h, "v", n, wl.v_row_bytes)))
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.decode_attention_head(*heads[done % len(heads)], wl.k_bits, wl.v_bits)
-        done += 1
-        dt = time.perf_counter() - t0
-        if dt >= seconds:
-            break
+    def run(limit_s: float) -> tuple[int, float]:
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.decode_attention_head(*heads[done % len(heads)], wl.k_bits, wl.v_bits)
+            done += 1
+            dt = time.perf_counter() - t0
+            if dt >= limit_s:
+                return done, dt
+
+    done, dt = run(seconds)
     per_layer = dt / done * wl.num_kv_heads
     threads = max([1] + [p.get("num_threads", 1) for p in threadpool_info()])
+    # the same oracle with its thread pools held to one thread, a shorter sample
+    with threadpool_limits(limits=1):
+        done1, dt1 = run(seconds / 4)
     return {"value": n / per_layer, "unit": "KV tokens/s per layer",
             "cores": int(threads), "kind": "oracle",
             "sample": f"{done} KV-head passes (of {wl.num_kv_heads} per layer) of sequence 0 at "
-                      f"N={n} in {dt:.1f} s, scaled to one layer of one sequence"}
+                      f"N={n} in {dt:.1f} s, scaled to one layer of one sequence",
+            "single_thread": {"value": n / (dt1 / done1 * wl.num_kv_heads), "cores": 1,
+                              "sample": f"{done1} KV-head passes in {dt1:.1f} s"}}
 
 
 # Sources that determine the attention kernel's code: a counter record taken
