@@ -103,8 +103,11 @@ __device__ __forceinline__ float search_pass1(Block block, Cop cup, int b0, int 
 }
 
 // pass 2: how many of this lane's centroids have s(c) - E(c) <= thr, and the
-// row (16 blk + r, without the lane's 4 (lane / 16)) of the last of them
-template <typename Block, typename Cop>
+// row (16 blk + r, without the lane's 4 (lane / 16)) of the last of them.
+// kSkip: a group of 8 blocks without a hit in the whole wave is skipped after
+// one ballot, which pays where hits are sparse (a wave over 1024 or more
+// centroids) and costs a little where nearly every group has one.
+template <bool kSkip, typename Block, typename Cop>
 __device__ __forceinline__ void search_pass2(Block block, Cop cdown, int b0, int b1, float thr,
                                              int& cnt, int& cand) {
     cnt = 0;
@@ -114,8 +117,8 @@ __device__ __forceinline__ void search_pass2(Block block, Cop cdown, int b0, int
         f32x4_t d[kSearchUnroll];
 #pragma unroll
         for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cdown(blk + u));
-        // hits are rare: a group with none in the whole wave is skipped
-        if (__builtin_amdgcn_ballot_w64(group_min(d) <= thr) == 0) continue;
+        if constexpr (kSkip)
+            if (__builtin_amdgcn_ballot_w64(group_min(d) <= thr) == 0) continue;
         // the group's last hit as u * 4 + r (an inline constant, 0 .. 31),
         // turned into a centroid row once per group
         const int before = cnt;
@@ -201,7 +204,7 @@ __device__ __forceinline__ uint32_t nearest16_search(Block block, Cop cup, Cop c
 
     // pass 2: each lane counts its candidates and keeps one
     int cnt, cand;
-    search_pass2(block, cdown, 0, NENT / 16, thr, cnt, cand);
+    search_pass2<(NENT >= 1024)>(block, cdown, 0, NENT / 16, thr, cnt, cand);
     cnt = sum_lanes16_32(cnt, lane);
     const int best = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
 

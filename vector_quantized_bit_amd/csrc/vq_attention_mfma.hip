@@ -333,7 +333,7 @@ __device__ __forceinline__ void new_token_keys12(uint8_t* tab, const double* xk,
     for (int w = 1; w < kCb; ++w) gmin = fminf(gmin, wmin[(cb * kCb + w) * 16 + (lane & 15)]);
     const float thr = gmin + row_bound(xx);
     int cnt, cand;
-    search_pass2(block, cdown, b0, b1, thr, cnt, cand);
+    search_pass2<true>(block, cdown, b0, b1, thr, cnt, cand);   // sparse hits: 1 in 4096
     cnt = sum_lanes16_32(cnt, lane);
     cand = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
     if (lane < 16) {
@@ -614,7 +614,7 @@ __device__ __forceinline__ void new_token_workgroup8(
         for (int w = 1; w < kWaves; ++w) gmin = fminf(gmin, wmin[w * kPos + pos]);
         const float thr = gmin + row_bound(xx);
         int cnt, cand;
-        search_pass2(block, cdown, b0, b1, thr, cnt, cand);
+        search_pass2<true>(block, cdown, b0, b1, thr, cnt, cand);   // sparse hits: 1 in 4096
         cnt = sum_lanes16_32(cnt, lane);
         cand = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
         if (lane < kPos) {
