@@ -255,8 +255,10 @@ int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
  * runs over the coded tokens [0, num_codes) and the window slots
  * [0, win_len] in one softmax.  Window keys are raw (untransformed): a raw
  * key k scores q . k / sqrt(D), which is q~ . k~ / sqrt(D).  One launch of
- * the split kernel (the extra workgroup per (sequence, KV head) attends over
- * the window) plus the merge.
+ * the split kernel plus the merge; the window is attended over by one extra
+ * workgroup per (sequence, KV head) or, from 128 streams with long splits,
+ * at the start of each stream's last split (the library chooses; the
+ * results are the same).
  *   win_k, win_v [B][Hkv][win_cap][128] fp16, caller-owned; slots
  *   [0, win_len) are read, slot win_len is written.
  *   codes_k / codes_v: read over [0, num_codes) only (num_codes may be 0).
