@@ -594,6 +594,16 @@ def test_decode_step_window_folded(win_len, splits):
                       what=f"folded window win={win_len} S={splits}")
 
 
+@pytest.mark.parametrize("group,k_bits", [(5, 12), (8, 8)])
+def test_decode_step_window_folded_groups_widths(group, k_bits):
+    # the folded window in the 12-bit-key kernel and at the largest group
+    wl = W.Workload(94, "adhoc", batch=32, num_q_heads=4 * group, num_kv_heads=4,
+                    context_len=20000, k_bits=k_bits)
+    check_window_step(random_cache(wl), 20000, 100, splits=2,
+                      heads=[(1, 0), (17, 3), (30, 2)],
+                      what=f"folded window G={group} kbits={k_bits}")
+
+
 def test_decode_step_window_full_size():
     # the long-context layer: 196608 coded tokens and a nearly full window
     wl = W.WORKLOADS[4]
@@ -771,3 +781,11 @@ def test_d8_decode_step_window(num_codes, win_len, group):
     wl = d8_workload(160 + group, 2, group, 2, 1024)
     check_window_step(random_cache(wl), num_codes, win_len,
                       what=f"1.5bit window codes={num_codes} win={win_len} G={group}")
+
+
+def test_d8_decode_step_window_folded():
+    # 128 streams with long splits: the 1.5-bit kernel's last split of each
+    # stream attends over the window first
+    wl = d8_workload(170, 32, 4, 4, 20000)
+    check_window_step(random_cache(wl), 20000, 127, splits=2, heads=[(0, 1), (19, 2), (31, 3)],
+                      what="1.5bit folded window")
