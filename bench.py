@@ -268,6 +268,25 @@ def prefill_encode(torch, vq, wl, dev, lam, cb_k, cb_v, head_start) -> dict:
                          "flops_per_launch": flops}}
 
 
+APPEND_TOKENS = 64
+
+
+def append_encode(torch, vq, wl, dev, lam, cb_k, cb_v, codes_k, codes_v, head_start) -> dict:
+    """A chunk of APPEND_TOKENS new tokens per sequence encoded into the
+    cache's last slots by one vq_encode_append call (every KV head)."""
+    bsz, hkv, n = wl.batch, wl.num_kv_heads, wl.context_len
+    t = min(APPEND_TOKENS, n)
+    kp = synthetic_rows(torch, wl, dev, (bsz, hkv, t, 128), "k", 5000 + wl.config_id)
+    vp = synthetic_rows(torch, wl, dev, (bsz, hkv, t, 128), "v", 6000 + wl.config_id)
+    enc = vq.prepare_encode_append(kp, vp, lam, cb_k, cb_v, codes_k, codes_v, n - t)
+    us = time_calls(torch, enc, 10, head_start)
+    pairs = bsz * hkv * t * wl.num_sub * ((1 << wl.k_bits) + (1 << wl.v_bits))
+    tflops = distance_flops(pairs, wl.sub_dim) / (us * 1e-6) / 1e12
+    return {"tokens_per_sequence": t, "cur_len": n - t, "avg_launch_us": us,
+            "token_heads_per_s": bsz * hkv * t / (us * 1e-6),
+            "dense_pass_tflops": tflops, "frac_of_mfma_f32_peak": tflops / MFMA_F32_PEAK_TFLOPS}
+
+
 def calibration(torch, vq, wl, dev, head_start, iters: int) -> dict:
     """The offline calibration path at the page's calibration-set size (256
     sequences x 512 tokens per KV head): lambda, K~, and Lloyd K-Means for
@@ -575,6 +594,8 @@ def main(argv=None) -> int:
 
     if not args.no_prefill:
         result["prefill_encode"] = prefill_encode(torch, vq, wl, dev, lam, cb_k, cb_v, head_start)
+        result["append_encode"] = append_encode(torch, vq, wl, dev, lam, cb_k, cb_v, ck0, cv0,
+                                                head_start)
     if not args.no_calibration:
         result["calibration"] = calibration(torch, vq, wl, dev, head_start, args.kmeans_iters)
 
