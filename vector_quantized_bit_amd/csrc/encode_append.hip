@@ -27,6 +27,12 @@ constexpr int kEncThreads = 512;
 constexpr int kEncWaves = kEncThreads / kWave;     // 8
 constexpr int kEncTok = 8;                          // tokens per workgroup
 constexpr int kEncBlocks = kEncTok * kNumSub / 16;  // row blocks per tensor
+// Threads of the d = 4 encoder: with 4096-entry C_k its tables (about
+// 120 KiB of LDS) allow one workgroup per CU, so it takes 16 waves, one key
+// row block each, to keep 4 waves on every SIMD; with 256 entries several
+// 8-wave workgroups share a CU.
+template <int KBITS>
+constexpr int kEncThreadsOf = KBITS == 12 ? 1024 : 512;
 
 
 __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
@@ -67,13 +73,14 @@ __device__ __forceinline__ uint32_t search_rows(const float* m2, const float* cu
 }  // namespace
 
 template <int KBITS>
-__global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
+__global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
     const float* __restrict__ lambda, const uint16_t* __restrict__ cb_k,
     const uint16_t* __restrict__ cb_v, uint8_t* __restrict__ codes_k,
     uint8_t* __restrict__ codes_v, int num_kv_heads, int capacity, int cur_len, int num_new) {
     constexpr int KENT = 1 << KBITS;
     constexpr int KROW = kNumSub * KBITS / 8;
+    constexpr int kThr = kEncThreadsOf<KBITS>, kWv = kThr / kWave;
     // -2c by channel ([4][E], exact in fp32) and ||c||^2, per tensor
     __shared__ float km2[4 * kSearchStride<KENT>];
     __shared__ float vm2[4 * kSearchStride<256>];
@@ -94,14 +101,14 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
     const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
     // every load is issued before any is used (one latency, not one per entry)
-    constexpr int KPER = (KENT + kEncThreads - 1) / kEncThreads;
+    constexpr int KPER = (KENT + kThr - 1) / kThr;
     uint2 kc[KPER];
 #pragma unroll
-    for (int j = 0; j < KPER; ++j) kc[j] = ksrc[min(tid + j * kEncThreads, KENT - 1)];
+    for (int j = 0; j < KPER; ++j) kc[j] = ksrc[min(tid + j * kThr, KENT - 1)];
     const uint2 vc = vsrc[tid & 255];
 #pragma unroll
     for (int j = 0; j < KPER; ++j) {
-        const int i = tid + j * kEncThreads;
+        const int i = tid + j * kThr;
         if (i < KENT) {
             km2[0 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x & 0xffffu);
             km2[1 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x >> 16);
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     // k / lambda in fp64, the +-1 Walsh–Hadamard transform, then 1/sqrt(128);
     // values as they are.  Rows of tokens past num_new are zero.
     const float* lam = lambda + g * kHeadDim;
-    for (int t = wave; t < kEncTok; t += kEncWaves) {
+    for (int t = wave; t < kEncTok; t += kWv) {
         const bool live = t < ntok;
         const size_t in_row = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + t0 +
                               (live ? t : 0);
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     __syncthreads();
 
     // row block jobs: keys then values; sub-vector r = 32 token + position
-    for (int job = wave; job < 2 * kEncBlocks; job += kEncWaves) {
+    for (int job = wave; job < 2 * kEncBlocks; job += kWv) {
         const int tt = job / kEncBlocks, rb = job % kEncBlocks;
         if (rb * 16 >= ntok * kNumSub) continue;   // whole block past the last token
         const uint32_t cd = tt == 0 ? search_rows<KENT>(km2, kcu, kcd, xs[0], rb, lane)
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_append_kernel(
     }
     if constexpr (KBITS == 12) {
         // byte j of a row holds bits [8j, 8j + 8) of the little-endian 12-bit stream
-        for (int e = tid; e < ntok * KROW; e += kEncThreads) {
+        for (int e = tid; e < ntok * KROW; e += kThr) {
             const int t = e / KROW, j = e % KROW;
             const int bit = 8 * j, i0 = bit / 12, sh = bit % 12;
             uint32_t v = static_cast<uint32_t>(code[0][t][i0]) >> sh;
@@ -288,11 +295,11 @@ hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, cons
                            kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v, num_kv_heads,
                            capacity, cur_len, num_new);
     else if (k_bits == 8)
-        hipLaunchKernelGGL(encode_append_kernel<8>, grid, dim3(kEncThreads), 0, stream, k_new,
+        hipLaunchKernelGGL(encode_append_kernel<8>, grid, dim3(kEncThreadsOf<8>), 0, stream, k_new,
                            v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
                            num_kv_heads, capacity, cur_len, num_new);
     else
-        hipLaunchKernelGGL(encode_append_kernel<12>, grid, dim3(kEncThreads), 0, stream, k_new,
+        hipLaunchKernelGGL(encode_append_kernel<12>, grid, dim3(kEncThreadsOf<12>), 0, stream, k_new,
                            v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
                            num_kv_heads, capacity, cur_len, num_new);
     return hipGetLastError();
