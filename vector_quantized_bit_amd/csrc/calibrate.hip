@@ -140,6 +140,10 @@ __global__ __launch_bounds__(256) void transform_keys_kernel(const void* __restr
 
 constexpr int kKmThreads = 512;
 constexpr int kKmWaves = kKmThreads / kWave;   // 8
+// Threads of an assignment workgroup: 4096-entry tables fill most of a CU's
+// LDS (one workgroup per CU), so those take 16 waves to keep 4 on every SIMD.
+template <int NENT>
+constexpr int kAssignThreads = NENT >= 4096 ? 1024 : 512;
 constexpr int kKmChunk = 8192;                 // samples per assignment workgroup = sort chunk
 constexpr int kSortWaves = 4;                  // chunks per scatter workgroup (one per wave)
 
@@ -171,7 +175,7 @@ __device__ __forceinline__ double sqdist4_c64(const float4 x, const double c[4])
 // and centroids must be finite with magnitudes below about 2^60 so that no
 // fp32 score overflows.
 template <int NENT>
-__global__ __launch_bounds__(kKmThreads) void kmeans_assign_kernel(
+__global__ __launch_bounds__(kAssignThreads<NENT>) void kmeans_assign_kernel(
     const float* __restrict__ samples, int num_samples, const double* __restrict__ centroids,
     int32_t* __restrict__ assign, int32_t* __restrict__ hist) {
     __shared__ float m2[4 * kSearchStride<NENT>];   // -2 fl32(c) by channel
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_assign_kernel(
     const double* cset = centroids + static_cast<size_t>(set) * NENT * 4;
     const float4* xset = reinterpret_cast<const float4*>(samples) +
                          static_cast<size_t>(set) * num_samples;
-    for (int i = tid; i < NENT; i += kKmThreads) {
+    for (int i = tid; i < NENT; i += kAssignThreads<NENT>) {
         const double2 lo = reinterpret_cast<const double2*>(cset)[2 * i];
         const double2 hi = reinterpret_cast<const double2*>(cset)[2 * i + 1];
         const double c[4] = {lo.x, lo.y, hi.x, hi.y};
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_assign_kernel(
 
     const int s0 = chunk * kKmChunk, s1 = min(num_samples, s0 + kKmChunk);
     int32_t* aset = assign + static_cast<size_t>(set) * num_samples;
-    for (int base = s0 + wave * 16; base < s1; base += kKmWaves * 16) {
+    for (int base = s0 + wave * 16; base < s1; base += (kAssignThreads<NENT> / kWave) * 16) {
         // this lane's sample base + lane % 16 (zero past the chunk)
         const int r = base + (lane & 15);
         const float4 x = r < s1 ? xset[r] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_assign_kernel(
     if (hist != nullptr) {
         __syncthreads();
         int32_t* h = hist + (static_cast<size_t>(set) * gridDim.x + chunk) * NENT;
-        for (int i = tid; i < NENT; i += kKmThreads) h[i] = cnt[i];
+        for (int i = tid; i < NENT; i += kAssignThreads<NENT>) h[i] = cnt[i];
     }
 }
 
@@ -257,7 +261,7 @@ template <int NENT>
 constexpr int kAssign8Lds = NENT * 40 + (kKmLdsC64<NENT> ? NENT * 64 : 0);
 
 template <int NENT>
-__global__ __launch_bounds__(kKmThreads) void kmeans_assign8_kernel(
+__global__ __launch_bounds__(kAssignThreads<NENT>) void kmeans_assign8_kernel(
     const float* __restrict__ samples, int num_samples, const double* __restrict__ centroids,
     int32_t* __restrict__ assign, int32_t* __restrict__ hist) {
     __shared__ __align__(16) uint8_t lds[kAssign8Lds<NENT>];
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_assign8_kernel(
     const double* cset = centroids + static_cast<size_t>(set) * NENT * 8;
     const float4* xset = reinterpret_cast<const float4*>(samples) +
                          static_cast<size_t>(set) * num_samples * 2;
-    for (int i = tid; i < NENT; i += kKmThreads) {
+    for (int i = tid; i < NENT; i += kAssignThreads<NENT>) {
         double c[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_assign8_kernel(
     const int q4 = 4 * (lane >> 4), gq = lane >> 4;
     const ScaledNorms cup{reinterpret_cast<const f32x4_t*>(nrm + q4), kBoundUp};
     const ScaledNorms cdown{reinterpret_cast<const f32x4_t*>(nrm + q4), kBoundDown};
-    for (int base = s0 + wave * 16; base < s1; base += kKmWaves * 16) {
+    for (int base = s0 + wave * 16; base < s1; base += (kAssignThreads<NENT> / kWave) * 16) {
         // this lane's sample base + lane % 16 (zero past the chunk)
         const int r = base + (lane & 15);
         const float4 lo = r < s1 ? xset[2 * r] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_assign8_kernel(
     if (hist != nullptr) {
         __syncthreads();
         int32_t* h = hist + (static_cast<size_t>(set) * gridDim.x + chunk) * NENT;
-        for (int i = tid; i < NENT; i += kKmThreads) h[i] = cnt[i];
+        for (int i = tid; i < NENT; i += kAssignThreads<NENT>) h[i] = cnt[i];
     }
 }
 
@@ -611,10 +615,10 @@ hipError_t kmeans_assign(const float* samples, int num_sets, int num_samples,
                          hipStream_t stream) {
     const dim3 grid(kmeans_chunks(num_samples), num_sets);
     if constexpr (SUB == 8)
-        hipLaunchKernelGGL(kmeans_assign8_kernel<1 << BITS>, grid, dim3(kKmThreads), 0, stream,
+        hipLaunchKernelGGL(kmeans_assign8_kernel<1 << BITS>, grid, dim3(kAssignThreads<1 << BITS>), 0, stream,
                            samples, num_samples, centroids, assign, hist);
     else
-        hipLaunchKernelGGL(kmeans_assign_kernel<1 << BITS>, grid, dim3(kKmThreads), 0, stream,
+        hipLaunchKernelGGL(kmeans_assign_kernel<1 << BITS>, grid, dim3(kAssignThreads<1 << BITS>), 0, stream,
                            samples, num_samples, centroids, assign, hist);
     return hipGetLastError();
 }
