@@ -182,15 +182,20 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
 }
 
 // The d = 8 layout (16 sub-vectors of 8 channels, C_k and C_v of 4096
-// entries, 24-byte rows of 12-bit codes): 8 tokens per workgroup, as above,
+// entries, 24-byte rows of 12-bit codes): 16 tokens per workgroup, one per wave,
 // searched with nearest16_d8 against the fp16 codebook in LDS.  A 4096 x 8
 // table with its two norm tables takes 96 KiB, so keys and values are
 // searched one after the other with the same LDS.
 constexpr int kEnc8Ent = 4096;
 constexpr int kEnc8Pos = kHeadDim / 8;           // 16 sub-vectors per vector
 constexpr int kEnc8Row = kEnc8Pos * 12 / 8;      // 24 bytes per code row
+// One token per wave, 16 per workgroup: the tables leave room for one
+// workgroup per CU, and 16 waves keep 4 on every SIMD.
+constexpr int kEnc8Tok = 16;
+constexpr int kEnc8Waves = kEnc8Tok;
+constexpr int kEnc8Threads = kEnc8Waves * kWave;
 
-__global__ __launch_bounds__(kEncThreads) void encode_append8_kernel(
+__global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
     const float* __restrict__ lambda, const uint16_t* __restrict__ cb_k,
     const uint16_t* __restrict__ cb_v, uint8_t* __restrict__ codes_k,
@@ -198,18 +203,18 @@ __global__ __launch_bounds__(kEncThreads) void encode_append8_kernel(
     __shared__ __align__(16) uint16_t ctab[kEnc8Ent * 8];   // one codebook, fp16 as stored
     __shared__ __align__(16) float cu[kEnc8Ent];            // ||c||^2 (1 + 2^-16)
     __shared__ __align__(16) float cd[kEnc8Ent];            // ||c||^2 (1 - 2^-16)
-    __shared__ double xs[2][kEncTok][kHeadDim];             // transformed keys, values (fp64)
-    __shared__ uint16_t code[2][kEncTok][kEnc8Pos];
+    __shared__ double xs[2][kEnc8Tok][kHeadDim];             // transformed keys, values (fp64)
+    __shared__ uint16_t code[2][kEnc8Tok][kEnc8Pos];
 
-    const int t0 = blockIdx.x * kEncTok, g = blockIdx.y, b = blockIdx.z;
-    const int ntok = min(kEncTok, num_new - t0);
+    const int t0 = blockIdx.x * kEnc8Tok, g = blockIdx.y, b = blockIdx.z;
+    const int ntok = min(kEnc8Tok, num_new - t0);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const bool f32 = kv_f32 != 0;
 
     // k / lambda in fp64, the +-1 Walsh–Hadamard transform, then 1/sqrt(128);
     // values as they are.  Rows of tokens past num_new are zero.
     const float* lam = lambda + g * kHeadDim;
-    for (int t = wave; t < kEncTok; t += kEncWaves) {
+    for (int t = wave; t < kEnc8Tok; t += kEnc8Waves) {
         const bool live = t < ntok;
         const size_t in_row = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + t0 +
                               (live ? t : 0);
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_append8_kernel(
         if (tt == 1) __syncthreads();   // every search of the key table is done
         const uint4* src = reinterpret_cast<const uint4*>(tt == 0 ? cb_k : cb_v) +
                            static_cast<size_t>(g) * kEnc8Ent;
-        for (int i = tid; i < kEnc8Ent; i += kEncThreads) {
+        for (int i = tid; i < kEnc8Ent; i += kEnc8Threads) {
             const uint4 c = src[i];
             reinterpret_cast<uint4*>(ctab)[i] = c;
             const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_append8_kernel(
         __syncthreads();
         // wave w: the 16 sub-vectors of token w (position lane % 16)
         const int tok = wave, pos = lane & 15;
-        static_assert(kEncWaves == kEncTok && kEnc8Pos == 16, "one token per wave");
+        static_assert(kEnc8Waves == kEnc8Tok && kEnc8Pos == 16, "one token per wave");
         if (tok < ntok) {   // uniform
             const double* x = &xs[tt][tok][8 * pos];
             const int gq = lane >> 4;
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_append8_kernel(
 
     // the live tokens' rows: byte j holds bits [8j, 8j + 8) of the 12-bit stream
     const size_t out0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + cur_len + t0;
-    for (int e = tid; e < 2 * ntok * kEnc8Row; e += kEncThreads) {
+    for (int e = tid; e < 2 * ntok * kEnc8Row; e += kEnc8Threads) {
         const int tt = e / (ntok * kEnc8Row), rem = e % (ntok * kEnc8Row);
         const int t = rem / kEnc8Row, j = rem % kEnc8Row;
         const int bit = 8 * j, i0 = bit / 12, sh = bit % 12;
@@ -290,8 +295,9 @@ hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, cons
                                 int batch, int num_kv_heads, int capacity, int cur_len,
                                 int num_new, hipStream_t stream) {
     const dim3 grid((num_new + kEncTok - 1) / kEncTok, num_kv_heads, batch);
+    const dim3 grid8((num_new + kEnc8Tok - 1) / kEnc8Tok, num_kv_heads, batch);
     if (sub_dim == 8)
-        hipLaunchKernelGGL(encode_append8_kernel, grid, dim3(kEncThreads), 0, stream, k_new, v_new,
+        hipLaunchKernelGGL(encode_append8_kernel, grid8, dim3(kEnc8Threads), 0, stream, k_new, v_new,
                            kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v, num_kv_heads,
                            capacity, cur_len, num_new);
     else if (k_bits == 8)
