@@ -189,6 +189,22 @@ def test_split_plan_keeps_each_split_under_2gib_of_codes(lib):
     assert (100_000_000 + d - 1) // d * 48 < 2 ** 31
 
 
+def test_split_plans_near_the_int32_limit(lib):
+    # contexts up to 2^31 - 1 tokens plan without overflow: every split count
+    # is positive, within the 512 the merge takes, and keeps splits under
+    # 2^31 bytes of 48-byte rows
+    n = 2 ** 31 - 10
+    for k_bits in (8, 12):
+        layout = lay(k_bits=k_bits, hkv=8, cap=2 ** 31 - 1)
+        for bsz, req in ((1, 0), (8, 0), (8, 1), (32, 0)):
+            for f in (lib.vq_decode_step_num_partials, lib.vq_decode_step_window_num_partials):
+                m = f(ctypes.byref(layout), bsz, 32, n, req)
+                assert 2 <= m <= 513, (f, bsz, req, m)
+                assert -(-n // (m - 1)) * 48 < 2 ** 31
+            s = lib.vq_decode_attention_plan_splits(ctypes.byref(layout), bsz, 32, n, req)
+            assert 1 <= s <= 512 and -(-n // s) * 48 < 2 ** 31
+
+
 def partials(lib, layout, splits=1, n=100, pm=A, pl=A, po=A, **kw):
     args = dict(q=A, q_dtype=0, lam=A, cbk=A, cbv=A, ck=A, cv=A, batch=1, hq=4)
     args.update(kw)

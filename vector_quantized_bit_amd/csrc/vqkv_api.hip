@@ -93,16 +93,17 @@ SplitPlan plan_splits(int streams, int context_len, int requested, int min_len,
                       int target = kTargetWorkgroups, int gran = 0,
                       int max_len = kVqMaxSplitTokens) {
     if (gran <= 0) gran = min_len;
-    int max_splits = (context_len + min_len - 1) / min_len;
+    const int64_t n = context_len;   // (64-bit: contexts reach 2^31 - 1 tokens)
+    int64_t max_splits = (n + min_len - 1) / min_len;
     if (max_splits > vqkv::kMaxSplits) max_splits = vqkv::kMaxSplits;
-    int s = requested > 0 ? requested : (target + streams - 1) / streams;
-    const int min_splits = static_cast<int>((static_cast<int64_t>(context_len) + max_len - 1) / max_len);
+    int64_t s = requested > 0 ? requested : (target + streams - 1) / streams;
+    const int64_t min_splits = (n + max_len - 1) / max_len;
     if (s < min_splits) s = min_splits;
     if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;
-    const int per = (context_len + s - 1) / s;
-    const int tps = ((per + gran - 1) / gran) * gran;
-    return {(context_len + tps - 1) / tps, tps};
+    const int64_t per = (n + s - 1) / s;
+    const int64_t tps = ((per + gran - 1) / gran) * gran;
+    return {static_cast<int>((n + tps - 1) / tps), static_cast<int>(tps)};
 }
 
 // The VQ kernel's plan for `streams` (sequence, KV head) streams.
@@ -367,11 +368,12 @@ constexpr int kFoldStreams = 32;
 // (kWindowFoldTokens).
 SplitPlan plan_step(int streams, int cur_len, int requested, int fold = 0) {
     const int n = cur_len > 0 ? cur_len : 1;
-    if (fold > 0 && streams >= kFoldStreams) {
+    if (fold > 0 && streams >= kFoldStreams && n <= 0x7fffffff - fold) {
         const SplitPlan f = plan_splits(streams, n + fold, requested, vqkv::kVqTile,
                                         kTargetWorkgroups, vqkv::kVqTileGrain);
         // every split keeps tokens, and the encode is a small part of one
-        if ((f.num_splits - 1) * f.tokens_per_split < n && f.tokens_per_split >= 2 * fold)
+        if (static_cast<int64_t>(f.num_splits - 1) * f.tokens_per_split < n &&
+            f.tokens_per_split >= 2 * fold)
             return SplitPlan{f.num_splits, f.tokens_per_split, true};
     }
     const int target = kTargetWorkgroups > 2 * streams ? kTargetWorkgroups - streams
