@@ -205,6 +205,15 @@ def test_split_plans_near_the_int32_limit(lib):
             assert 1 <= s <= 512 and -(-n // s) * 48 < 2 ** 31
 
 
+def test_plan_queries_with_huge_stream_counts(lib):
+    # batch x KV heads beyond the int32 range: the plan queries stay defined
+    # (one split), and a launch with such a shape is refused before any work
+    layout = lay(hkv=8, cap=1000)
+    assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 2 ** 30, 32, 999, 0) == 2
+    assert lib.vq_decode_attention_plan_splits(ctypes.byref(layout), 2 ** 30, 32, 999, 0) == 1
+    assert attn(lib, layout, batch=2 ** 30, hq=32, n=999) == INVALID
+
+
 def partials(lib, layout, splits=1, n=100, pm=A, pl=A, po=A, **kw):
     args = dict(q=A, q_dtype=0, lam=A, cbk=A, cbv=A, ck=A, cv=A, batch=1, hq=4)
     args.update(kw)

@@ -106,6 +106,13 @@ SplitPlan plan_splits(int streams, int context_len, int requested, int min_len,
     return {static_cast<int>((n + tps - 1) / tps), static_cast<int>(tps)};
 }
 
+// (sequence, KV head) streams of a call, saturated at the int32 limit (the
+// launching entry points reject such shapes; the plan queries stay defined).
+int streams_of(int32_t batch, int32_t num_kv_heads) {
+    const int64_t n = static_cast<int64_t>(batch) * num_kv_heads;
+    return n > 0x7fffffff ? 0x7fffffff : static_cast<int>(n);
+}
+
 // The VQ kernel's plan for `streams` (sequence, KV head) streams.
 SplitPlan plan_vq(int streams, int context_len, int requested) {
     return plan_splits(streams, context_len, requested, vqkv::kVqTile, kTargetWorkgroups,
@@ -203,7 +210,7 @@ int32_t vq_decode_attention_default_splits(const vq_layout* layout, int32_t batc
                                            int32_t num_q_heads, int32_t context_len) {
     (void)num_q_heads;
     if (layout == nullptr || batch < 1 || context_len < 1 || layout->num_kv_heads < 1) return 0;
-    return plan_vq(batch * layout->num_kv_heads, context_len, 0).num_splits;
+    return plan_vq(streams_of(batch, layout->num_kv_heads), context_len, 0).num_splits;
 }
 
 size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batch,
@@ -213,7 +220,7 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
         layout->num_kv_heads < 1)
         return 0;
     const SplitPlan p =
-        plan_vq(batch * layout->num_kv_heads, context_len, num_splits);
+        plan_vq(streams_of(batch, layout->num_kv_heads), context_len, num_splits);
     return partials_bytes(batch, num_q_heads, p.num_splits);
 }
 
@@ -224,7 +231,7 @@ int32_t vq_decode_attention_plan_splits(const vq_layout* layout, int32_t batch,
     if (layout == nullptr || batch < 1 || context_len < 1 || layout->num_kv_heads < 1 ||
         requested < 0)
         return 0;
-    return plan_vq(batch * layout->num_kv_heads, context_len, requested)
+    return plan_vq(streams_of(batch, layout->num_kv_heads), context_len, requested)
         .num_splits;
 }
 
@@ -274,7 +281,7 @@ int vq_decode_attention_partials(const vq_layout* layout, const void* q, int q_d
     if (st) return st;
     if ((st = check_partials_ptrs(part_m, part_l, part_o))) return st;
     const SplitPlan p =
-        plan_vq(batch * layout->num_kv_heads, context_len, num_splits);
+        plan_vq(streams_of(batch, layout->num_kv_heads), context_len, num_splits);
     if (num_splits != p.num_splits)
         return fail(VQ_ERR_INVALID_ARG,
                     "num_splits %d is not a planned split count for this shape "
@@ -467,7 +474,7 @@ int32_t vq_decode_step_num_partials(const vq_layout* layout, int32_t batch, int3
     if (layout == nullptr || batch < 1 || cur_len < 0 || layout->num_kv_heads < 1 ||
         requested < 0)
         return 0;
-    return plan_step(batch * layout->num_kv_heads, cur_len, requested, fold_tokens(layout))
+    return plan_step(streams_of(batch, layout->num_kv_heads), cur_len, requested, fold_tokens(layout))
                .num_splits + 1;
 }
 
@@ -488,7 +495,7 @@ int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
                              codes_k, codes_v, batch, num_q_heads, cur_len, 0);
     if (st) return st;
     if ((st = check_partials_ptrs(part_m, part_l, part_o))) return st;
-    const SplitPlan p = plan_step(batch * layout->num_kv_heads, cur_len,
+    const SplitPlan p = plan_step(streams_of(batch, layout->num_kv_heads), cur_len,
                                   num_partials > 1 ? num_partials - 1 : 1, fold_tokens(layout));
     if (num_partials != p.num_splits + 1)
         return fail(VQ_ERR_INVALID_ARG,
@@ -515,7 +522,7 @@ int vq_decode_step(const vq_layout* layout, const void* q, int q_dtype, const vo
                              codes_k, codes_v, batch, num_q_heads, cur_len, num_splits);
     if (st) return st;
     VQ_REQUIRE_PTR(out);
-    const SplitPlan p = plan_step(batch * layout->num_kv_heads, cur_len, num_splits,
+    const SplitPlan p = plan_step(streams_of(batch, layout->num_kv_heads), cur_len, num_splits,
                                   fold_tokens(layout));
     const int nparts = p.num_splits + 1;
     const size_t need = partials_bytes(batch, num_q_heads, nparts);
@@ -544,7 +551,7 @@ int32_t vq_decode_step_window_num_partials(const vq_layout* layout, int32_t batc
     if (layout == nullptr || batch < 1 || num_codes < 0 || layout->num_kv_heads < 1 ||
         requested < 0)
         return 0;
-    return plan_window_step(batch * layout->num_kv_heads, num_codes, requested).num_splits + 1;
+    return plan_window_step(streams_of(batch, layout->num_kv_heads), num_codes, requested).num_splits + 1;
 }
 
 size_t vq_decode_step_window_workspace_bytes(const vq_layout* layout, int32_t batch,
@@ -568,7 +575,7 @@ int vq_decode_step_window(const vq_layout* layout, const void* q, int q_dtype, c
                                     num_codes, win_len, num_splits);
     if (st) return st;
     VQ_REQUIRE_PTR(out);
-    const SplitPlan p = plan_window_step(batch * layout->num_kv_heads, num_codes, num_splits);
+    const SplitPlan p = plan_window_step(streams_of(batch, layout->num_kv_heads), num_codes, num_splits);
     const int nparts = p.num_splits + 1;
     const size_t need = partials_bytes(batch, num_q_heads, nparts);
     if (workspace == nullptr || workspace_bytes < need)
@@ -610,7 +617,7 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
     if (st) return st;
     VQ_REQUIRE_PTR(out);
     const SplitPlan p =
-        plan_vq(batch * layout->num_kv_heads, context_len, num_splits);
+        plan_vq(streams_of(batch, layout->num_kv_heads), context_len, num_splits);
     const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -632,7 +639,7 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype, con
 size_t vq_fp16_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t context_len, int32_t num_splits) {
     if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || context_len < 1) return 0;
-    const SplitPlan p = plan_splits(batch * num_kv_heads, context_len, num_splits, vqkv::kFp16Tile,
+    const SplitPlan p = plan_splits(streams_of(batch, num_kv_heads), context_len, num_splits, vqkv::kFp16Tile,
                                       kTargetWorkgroupsFp16);
     return partials_bytes(batch, num_q_heads, p.num_splits);
 }
@@ -655,7 +662,7 @@ int vq_fp16_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_
     VQ_REQUIRE_PTR(k);
     VQ_REQUIRE_PTR(v);
     VQ_REQUIRE_PTR(out);
-    const SplitPlan p = plan_splits(batch * num_kv_heads, context_len, num_splits, vqkv::kFp16Tile,
+    const SplitPlan p = plan_splits(streams_of(batch, num_kv_heads), context_len, num_splits, vqkv::kFp16Tile,
                                       kTargetWorkgroupsFp16);
     const size_t need = partials_bytes(batch, num_q_heads, p.num_splits);
     if (workspace == nullptr || workspace_bytes < need)
