@@ -604,6 +604,21 @@ def test_decode_step_window_folded_groups_widths(group, k_bits):
                       what=f"folded window G={group} kbits={k_bits}")
 
 
+@pytest.mark.parametrize("win_cap,win_len,num_codes,streams", [
+    (16, 15, 700, 4), (16, 0, 0, 4), (256, 200, 3000, 4), (256, 255, 20000, 128),
+    (1, 0, 513, 4)])
+def test_decode_step_window_capacities(win_cap, win_len, num_codes, streams):
+    # windows other than 128 slots: the smallest, one slot, and a larger one,
+    # beside the splits and folded into them (128 streams)
+    bsz = streams // 2
+    wl = W.Workload(92, "adhoc", batch=bsz, num_q_heads=8, num_kv_heads=2,
+                    context_len=max(num_codes, 1))
+    heads = None if bsz <= 2 else [(0, 0), (bsz // 2, 1), (bsz - 1, 0)]
+    check_window_step(random_cache(wl), num_codes, win_len, win_cap=win_cap,
+                      splits=2 if streams >= 128 else 0, heads=heads,
+                      what=f"window cap={win_cap} len={win_len} codes={num_codes}")
+
+
 def test_decode_step_window_full_size():
     # the long-context layer: 196608 coded tokens and a nearly full window
     wl = W.WORKLOADS[4]
