@@ -212,6 +212,43 @@ def test_encoder_append_mixed_bits_full_size():
             check_codes(cvh[b, g, cur:cur + t_new], pv, gv, 8, v[b, g], cb_v[g], f"enc V c5 b{b} g{g}")
 
 
+@pytest.mark.parametrize("k_bits,t_new,cur,dtype", [(8, 1, 0, "f16"), (8, 9, 7, "f32"),
+                                                     (12, 1, 3, "f16"), (12, 7, 0, "f16"),
+                                                     (12, 33, 100, "f32")])
+def test_encode_append_ragged(k_bits, t_new, cur, dtype):
+    # token counts that leave a workgroup partly empty (8 tokens per
+    # workgroup), into the middle of a cache whose other slots stay untouched
+    bsz, hkv = 2, 2
+    lam = np.stack([W.random_lambda(150 + k_bits, g) for g in range(hkv)])
+    cb_k = np.stack([W.random_codebook(150 + k_bits, g, "k", 1 << k_bits, 0.6)
+                     for g in range(hkv)])
+    cb_v = np.stack([W.random_codebook(150 + k_bits, g, "v", 256, 1.0, 1 / 32)
+                     for g in range(hkv)])
+    st = np.float16 if dtype == "f16" else np.float32
+    k = np.stack([np.stack([W.kv_rows(150 + k_bits, b, g, "k", t_new, append=True)
+                            for g in range(hkv)]) for b in range(bsz)]).astype(st)
+    v = np.stack([np.stack([W.kv_rows(150 + k_bits, b, g, "v", t_new, append=True)
+                            for g in range(hkv)]) for b in range(bsz)]).astype(st)
+    cap, krow = cur + t_new + 3, 32 * k_bits // 8
+    ck = torch.full((bsz, hkv, cap, krow), 0xA5, dtype=torch.uint8, device=DEV)
+    cv = torch.full((bsz, hkv, cap, 32), 0x5A, dtype=torch.uint8, device=DEV)
+    vq.encode_append(dev(k), dev(v), dev(lam), dev(cb_k), dev(cb_v), ck, cv, cur)
+    torch.cuda.synchronize()
+    ckh, cvh = ck.cpu().numpy(), cv.cpu().numpy()
+    outside = np.ones(cap, bool)
+    outside[cur:cur + t_new] = False
+    assert np.all(ckh[:, :, outside] == 0xA5) and np.all(cvh[:, :, outside] == 0x5A)
+    for b in range(bsz):
+        for g in range(hkv):
+            pk, pv, gk, gv = oracle.encode_append(k[b, g], v[b, g], lam[g], cb_k[g], cb_v[g],
+                                                  k_bits, 8)
+            kt = oracle.transform_keys(k[b, g], lam[g])
+            check_codes(ckh[b, g, cur:cur + t_new], pk, gk, k_bits, kt, cb_k[g],
+                        f"ragged enc K b{b} g{g}")
+            check_codes(cvh[b, g, cur:cur + t_new], pv, gv, 8, v[b, g], cb_v[g],
+                        f"ragged enc V b{b} g{g}")
+
+
 def test_encoder_exact_ties_go_to_lowest_index():
     rng = np.random.default_rng(200)
     base = rng.standard_normal((128, 4)).astype(np.float16)
@@ -742,8 +779,8 @@ def test_d8_decode_step_full_size():
                what="1.5bit step config6")
 
 
-@pytest.mark.parametrize("t_new,cur,dtype", [(1, 0, "f16"), (13, 5, "f16"), (64, 100, "f32"),
-                                             (200, 0, "f16")])
+@pytest.mark.parametrize("t_new,cur,dtype", [(1, 0, "f16"), (13, 5, "f16"), (16, 3, "f16"),
+                                             (17, 0, "f16"), (64, 100, "f32"), (200, 0, "f16")])
 def test_d8_encode_append(t_new, cur, dtype):
     bsz, hkv = 2, 2
     lam = np.stack([W.random_lambda(140, g) for g in range(hkv)])
