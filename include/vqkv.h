@@ -52,6 +52,18 @@
  *    head, shared by every sub-vector position and every sequence.
  *  - Base pointers of codes, codebooks, q, lambda and out must be 16-byte
  *    aligned (VQ_ERR_INVALID_ARG otherwise).
+ *  - Numerics of the attention entry points: q~ is formed in fp32 (so q,
+ *    lambda and q~ must be finite in fp32; nothing else bounds their
+ *    range), then scaled per head by a power of two and split into two
+ *    fp16 parts for the matrix cores; dequantised keys and values are the
+ *    fp16 codebook entries themselves; scores, the online softmax and every
+ *    accumulation are fp32, and the weights 2^(s - m) enter the value
+ *    product as two fp16 parts within 2^-20 p + 2^-40 of p (m the running
+ *    maximum).  A base-2 score log2(e) s then carries an absolute error of
+ *    about 2^-22 times the sum of |q~_i k^_i| / sqrt(128), so weights stay
+ *    accurate to ~1e-4 while that sum is below a few hundred units and the
+ *    argmax stays exact far beyond (the tests cover scores near +-656 units
+ *    and a one-hot softmax at ~1e12 units).
  */
 #ifndef VQKV_H
 #define VQKV_H

@@ -11,11 +11,21 @@
 // tiles in turn.
 //  * Both products are dense contractions once a centroid is looked up, so
 //    both run on v_mfma_f32_16x16x32_f16.  The 16 MFMA rows are (head, part):
-//    q~ and p, the operands that are not exact in fp16, are split into
-//    hi = fp16(x) and lo = fp16(x - hi) on separate rows that are summed
-//    after the product; codebook entries are fp16 already.  Row 4j + i holds
+//    q~ and p, the operands that are not exact in fp16, are split into a
+//    high and a low fp16 part on separate rows that are summed after the
+//    product; codebook entries are fp16 already.  Row 4j + i holds
 //    (head 2j, hi), (head 2j+1, hi), (head 2j, lo), (head 2j+1, lo) for
 //    i = 0..3, so G <= 8 heads fit; rows of heads >= G are zero.
+//      - q~ of each head is first scaled by a power of two 2^e that puts its
+//        largest element in [2^14, 2^15): hi = fp16(x 2^e), lo =
+//        fp16(x 2^e - hi), and the head's scores are multiplied by 2^-e.
+//        Any finite q~ fits fp16 this way, and both parts stay normal
+//        numbers for every element within 2^-17 of the largest.
+//      - p = 2^(s - m) <= 2^8 is split as hi = fp16_rtz(p) and lo =
+//        fp16_rtz((p - hi) 2^16); the low rows are scaled by 2^-16 when the
+//        waves fold.  So hi + lo 2^-16 is within 2^-20 p + 2^-40 of p: a
+//        weight far below the running maximum keeps its own relative
+//        precision instead of being truncated at the fp16 subnormal step.
 //  * Scores: the B operand is two key centroids (8 fp16) per lane, each one
 //    8-byte LDS gather.
 //  * Values: the MFMA wants 8 tokens x 1 channel per lane, a gather gives
@@ -64,6 +74,8 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTok = 32;                  // tokens per wave tile
 constexpr int kStride = kWaves * kTok;    // tokens per workgroup sweep
 constexpr float kTau = 8.0f;              // lazy-rescale slack (log2 units)
+constexpr float kLoScale = 65536.0f;      // low part of p, scaled: (p - hi) 2^16
+constexpr float kLoUnscale = 1.0f / 65536.0f;
 constexpr int kTable = 65536;             // bytes of one codebook table
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9
 
@@ -922,6 +934,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t tab[2 * kTable];       // keys | values
     __shared__ __attribute__((aligned(16))) uint2 pbuf[kWaves][kTok * 4];  // [token][16 rows] fp16
     __shared__ half8_t qa[4][64];
+    __shared__ float qsc[8];   // per head: 2^-e, the inverse of q~'s scale in qa
     __shared__ float wmT[G][kWaves], wlT[G][kWaves];   // per head and wave: m, rescaled l
     __shared__ uint32_t tile_ctr;   // next 32-token tile of the split to hand out
     // appended token (new-token workgroup): transformed key and value (fp64)
@@ -1098,7 +1111,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // score A operand, shared by every wave: lane (16 qg + r) of K-step kk
     // holds row r for dims 32 qg + 8 kk + e, e = 0 .. 7, where row r is head
     // 2 (r / 4) + r % 2, its fp16 high part for r % 4 < 2, else the low part
-    // (x - hi rounded to fp16).  This lane's dims 2 lane, 2 lane + 1 are
+    // (x - hi rounded to fp16), both of x 2^e (the head's largest element in
+    // [2^14, 2^15); 2^-e goes to qsc).  This lane's dims 2 lane, 2 lane + 1 are
     // elements e = 2 (lane % 4), + 1 of entry qg = lane / 16, kk = lane % 16 / 4.
     x0 *= lam2.x;
     x1 *= lam2.y;
@@ -1107,6 +1121,11 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         const bool real = wave < G;
         x0 = real ? x0 * kScoreScaleLog2 : 0.f;
         x1 = real ? x1 * kScoreScaleLog2 : 0.f;
+        const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+        const int ex = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);
+        x0 = __builtin_amdgcn_ldexpf(x0, ex);
+        x1 = __builtin_amdgcn_ldexpf(x1, ex);
+        if (lane == 0) qsc[wave] = __builtin_amdgcn_ldexpf(1.f, -ex);
         const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
         const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
         const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
@@ -1128,7 +1147,11 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     float mA = sh < G ? -INFINITY : INFINITY;
     float mB = sh + 1 < G ? -INFINITY : INFINITY;
     float lA = 0.f, lB = 0.f;
-    float thA = mA + kTau, thB = mB + kTau;   // rescale thresholds
+    // MFMA scores are s 2^e: rsA, rsB = 2^-e of the lane's heads; m and l are
+    // in base-2 units, the rescale thresholds (m + tau) 2^e in MFMA units
+    const float rsA = qsc[sh], rsB = qsc[sh + 1];
+    const float scA = 1.f / rsA, scB = 1.f / rsB;   // exact: powers of two
+    float thA = (mA + kTau) * scA, thB = (mB + kTau) * scB;
     float4_t oacc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -1243,12 +1266,12 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
                 cA = fmaxf(cA, lane_partner<32>(cA, lane));
                 cB = fmaxf(cB, lane_partner<32>(cB, lane));
             }
-            const float nA = fmaxf(mA, cA), nB = fmaxf(mB, cB);
+            const float nA = fmaxf(mA, cA * rsA), nB = fmaxf(mB, cB * rsB);
             const float fA = rescale_factor(mA, nA), fB = rescale_factor(mB, nB);
             mA = nA;
             mB = nB;
-            thA = nA + kTau;
-            thB = nB + kTau;
+            thA = (nA + kTau) * scA;
+            thB = (nB + kTau) * scB;
             lA *= fA;
             lB *= fB;
 #pragma unroll
@@ -1261,13 +1284,15 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         }
 #pragma unroll
         for (int sb = 0; sb < kSb; ++sb) {
-            const float pA = fast_exp2(sA[sb] - mA);
-            const float pB = fast_exp2(sB[sb] - mB);
+            const float pA = fast_exp2(fmaf(sA[sb], rsA, -mA));
+            const float pB = fast_exp2(fmaf(sB[sb], rsB, -mB));
             lA += pA;
             lB += pB;
-            // hi parts round toward zero; the remainders are exact in fp32
+            // hi parts round toward zero; the remainders are exact in fp32,
+            // and so are they times 2^16 (below 2^14: no fp16 overflow)
             const uint32_t hi = pack_rtz(pA, pB);
-            const uint32_t lo = pack_rtz(pA - lo_half_to_float(hi), pB - hi_half_to_float(hi));
+            const uint32_t lo = pack_rtz((pA - lo_half_to_float(hi)) * kLoScale,
+                                         (pB - hi_half_to_float(hi)) * kLoScale);
             pw[pslot_w + 64 * sb] = make_uint2(hi, lo);   // this lane's token, rows of its heads
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1385,7 +1410,8 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             obuf[(wave * 8 + c) * kLanes + lane] =
-                make_float2(fA * (oacc[c][0] + oacc[c][2]), fB * (oacc[c][1] + oacc[c][3]));
+                make_float2(fA * fmaf(oacc[c][2], kLoUnscale, oacc[c][0]),
+                            fB * fmaf(oacc[c][3], kLoUnscale, oacc[c][1]));
     }
     if (n == 0) {
         if (hA < G) wlT[hA][wave] = fA * lA;
