@@ -147,7 +147,9 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
  * the blockwise online softmax.  The context is split into `num_splits`
  * contiguous ranges processed in parallel, and their partial results are
  * merged by log-sum-exp (0 = library default; larger requests are clamped
- * so that no split is empty).
+ * so that no split is empty, smaller ones raised so that no split holds more
+ * than 24576 tokens while 512 splits allow it: fp32 accumulation over longer
+ * splits loses accuracy behind a dominant token).
  *   q [B][Hq][128] in q_dtype (raw query: the transform happens inside)
  *   out [B][Hq][128] fp32
  *   workspace: device memory of at least
@@ -172,8 +174,8 @@ int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype,
  * different devices.
  *
  * vq_decode_attention_plan_splits: the split count the library uses for
- * `requested` splits (0 = its default; larger requests are clamped so that
- * no split is empty).  Returns 0 for invalid arguments.
+ * `requested` splits (0 = its default; clamped as vq_decode_attention
+ * clamps it).  Returns 0 for invalid arguments.
  *
  * vq_decode_attention_partials: the split pass alone.  Split s of
  * (sequence b, query head h) covers tokens [s T, min((s + 1) T, context_len))

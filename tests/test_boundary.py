@@ -179,14 +179,38 @@ def test_plan_splits_is_a_fixed_point(lib):
 def test_split_plan_keeps_each_split_under_2gib_of_codes(lib):
     # a split's code rows are addressed through a 32-bit byte range: an
     # explicit request of one split over 100 M tokens of 48-byte rows is
-    # raised to the smallest count that keeps every split under 2^31 bytes
+    # raised (here to the merge's 512 partials, by the split-length cap)
     layout = lay(k_bits=12, hkv=1, cap=100_000_000)
     s = lib.vq_decode_attention_plan_splits(ctypes.byref(layout), 1, 4, 100_000_000, 1)
-    assert s == 3
+    assert s == 512
+    assert (100_000_000 + s - 1) // s * 48 < 2 ** 31
     assert lib.vq_decode_attention_plan_splits(ctypes.byref(layout), 1, 4, 100_000_000, s) == s
     # the default plan is far below the bound
     d = lib.vq_decode_attention_plan_splits(ctypes.byref(layout), 1, 4, 100_000_000, 0)
     assert (100_000_000 + d - 1) // d * 48 < 2 ** 31
+
+
+@pytest.mark.parametrize("n,req,expect", [
+    (24576, 1, 1),            # one split of 24576 tokens is the longest allowed
+    (24577, 1, 2),
+    (65536, 1, 3),            # requests of fewer splits are raised to splits of <= 24576
+    (196608, 1, 8),
+    (196608, 0, 256),         # the default (256 workgroups) is unaffected
+    (512 * 24576, 1, 512),
+    (512 * 24576 + 32, 1, 512),   # beyond 512 x 24576 tokens the splits grow instead
+])
+def test_split_plan_caps_the_split_length(lib, n, req, expect):
+    """Waves accumulate their tiles' value products in fp32; behind a dominant
+    token the rounding of many small contributions grows with the tiles per
+    wave, so the planner keeps splits at 24576 tokens or fewer while the 512
+    splits the merge takes allow it."""
+    layout = lay(hkv=1, cap=n)
+    s = lib.vq_decode_attention_plan_splits(ctypes.byref(layout), 1, 4, n, req)
+    assert s == expect
+    per = -(-n // s)
+    assert per <= 24576 or s == 512
+    m = lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 4, n - 1, req)
+    assert -(-(n - 1) // (m - 1)) <= 24576 or m - 1 == 512
 
 
 def test_split_plans_near_the_int32_limit(lib):

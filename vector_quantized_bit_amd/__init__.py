@@ -157,21 +157,69 @@ def make_layout(codes_k: torch.Tensor, codes_v: torch.Tensor, cb_k: torch.Tensor
 
 
 def _check_cache(codes_k, codes_v, cb_k, cb_v, lam):
+    """Every shape the kernels index by: the C ABI receives raw pointers, so a
+    tensor smaller than the layout says would be read (or written) past its
+    end on the device."""
     for name, t, dt in (("codes_k", codes_k, torch.uint8), ("codes_v", codes_v, torch.uint8),
                         ("cb_k", cb_k, torch.float16), ("cb_v", cb_v, torch.float16),
                         ("lambda", lam, torch.float32)):
         _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
         _need(t.dtype == dt, f"{name} must be {dt}, got {t.dtype}")
+        _need(t.device == codes_k.device, f"{name} is on {t.device}, the cache on {codes_k.device}")
+    _need(codes_k.dim() == 4 and codes_v.dim() == 4, "codes must be [B][Hkv][cap][row]")
     _need(codes_k.shape[:3] == codes_v.shape[:3], "codes_k and codes_v disagree in [B][Hkv][cap]")
+    hkv = codes_k.shape[1]
+    _need(lam.dim() == 2 and tuple(lam.shape) == (hkv, 128),
+          f"lambda must be [Hkv={hkv}][128], got {tuple(lam.shape)}")
+    _need(cb_k.dim() == 3 and cb_v.dim() == 3, "codebooks must be [Hkv][entries][d]")
+    sub = int(cb_k.shape[2])
+    for name, cb in (("cb_k", cb_k), ("cb_v", cb_v)):
+        ent = int(cb.shape[1])
+        _need(cb.shape[0] == hkv and ent >= 1 and ent & (ent - 1) == 0 and cb.shape[2] == sub,
+              f"{name} must be [Hkv={hkv}][2^bits][d={sub}], got {tuple(cb.shape)}")
+    _need(sub in (4, 8), f"sub-vector size {sub} unsupported (4 or 8)")
+    for name, codes, cb in (("codes_k", codes_k, cb_k), ("codes_v", codes_v, cb_v)):
+        row = (128 // sub) * (int(cb.shape[1]).bit_length() - 1) // 8
+        _need(codes.shape[3] == row,
+              f"{name} rows must be {row} bytes for {cb.shape[1]}-entry codebooks of "
+              f"{sub}-dim sub-vectors, got {codes.shape[3]}")
+
+
+def _check_query(q, codes_k):
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 128,
+          "q must be contiguous [B][Hq][128]")
+    _need(q.device == codes_k.device, f"q is on {q.device}, the cache on {codes_k.device}")
+    _need(q.shape[0] == codes_k.shape[0],
+          f"q has {q.shape[0]} sequences, the cache {codes_k.shape[0]}")
+    _need(q.shape[1] % codes_k.shape[1] == 0,
+          f"query heads {q.shape[1]} are not a multiple of KV heads {codes_k.shape[1]}")
+    _dtype_code(q)
+
+
+def _check_out(out, batch, hq, device):
+    _need(out.is_cuda and out.is_contiguous() and out.dtype == torch.float32
+          and tuple(out.shape) == (batch, hq, 128) and out.device == device,
+          f"out must be contiguous float32 [{batch}][{hq}][128] on {device}")
+    return out
+
+
+def _check_workspace(ws, device):
+    _need(ws.is_cuda and ws.is_contiguous() and ws.dtype == torch.uint8 and ws.device == device,
+          f"workspace must be a contiguous uint8 tensor on {device}")
+    return ws
 
 
 def transform_query(q: torch.Tensor, lam: torch.Tensor, out: torch.Tensor | None = None):
     """q~ = q diag(lambda) H_128 -> float32 [B][Hq][128]."""
-    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
-    _need(lam.is_cuda and lam.is_contiguous() and lam.dtype == torch.float32 and lam.dim() == 2,
-          "lambda must be contiguous float32 [Hkv][128]")
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 128,
+          "q must be contiguous [B][Hq][128]")
+    _need(lam.is_cuda and lam.is_contiguous() and lam.dtype == torch.float32 and lam.dim() == 2
+          and lam.shape[1] == 128 and lam.device == q.device,
+          "lambda must be contiguous float32 [Hkv][128] on q's device")
+    _need(q.shape[1] % lam.shape[0] == 0, "query heads must be a multiple of KV heads")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check_out(out, q.shape[0], q.shape[1], q.device)
     lay = Layout(128, 4, 8, 8, int(lam.shape[0]), 1)
     _check(library().vq_transform_query(ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam),
                                         q.shape[0], q.shape[1], _ptr(out), _stream(q)),
@@ -201,8 +249,11 @@ def _encode_append_args(k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len
     _need(k_new.shape == v_new.shape and k_new.dim() == 4, "k_new/v_new must be [B][Hkv][T][128]")
     _need(k_new.dtype == v_new.dtype, "k_new and v_new must share a dtype")
     _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new/v_new must be contiguous")
-    _need(k_new.shape[0] == codes_k.shape[0] and k_new.shape[1] == codes_k.shape[1],
-          "k_new [B][Hkv] disagrees with the cache")
+    _need(k_new.shape[0] == codes_k.shape[0] and k_new.shape[1] == codes_k.shape[1]
+          and k_new.shape[3] == 128, "k_new [B][Hkv][T][128] disagrees with the cache")
+    _need(k_new.device == codes_k.device and v_new.device == codes_k.device,
+          "k_new/v_new must be on the cache's device")
+    _dtype_code(k_new)
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
     return (ctypes.byref(lay), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(lam),
             _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v), k_new.shape[0], cur_len,
@@ -241,14 +292,16 @@ def decode_attention_workspace_bytes(codes_k, codes_v, cb_k, cb_v, batch, num_q_
 def _decode_attention_args(q, lam, cb_k, cb_v, codes_k, codes_v, context_len, num_splits, out,
                            workspace):
     _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
-    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
+    _check_query(q, codes_k)
     batch, hq = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    _check_out(out, batch, hq, q.device)
     if workspace is None:
         nbytes = decode_attention_workspace_bytes(codes_k, codes_v, cb_k, cb_v, batch, hq,
                                                   context_len, num_splits)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
     args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam), _ptr(cb_k), _ptr(cb_v),
             _ptr(codes_k), _ptr(codes_v), batch, hq, context_len, num_splits, _ptr(out),
@@ -291,7 +344,7 @@ def decode_attention_plan_splits(codes_k, codes_v, cb_k, cb_v, batch, num_q_head
 
 def _partials_args(q, lam, cb_k, cb_v, codes_k, codes_v, context_len, num_splits, partials):
     _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
-    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
+    _check_query(q, codes_k)
     batch, hq = q.shape[0], q.shape[1]
     splits = decode_attention_plan_splits(codes_k, codes_v, cb_k, cb_v, batch, hq, context_len,
                                           num_splits)
@@ -303,7 +356,8 @@ def _partials_args(q, lam, cb_k, cb_v, codes_k, codes_v, context_len, num_splits
     for name, t, shape in (("m", m, (batch, hq, splits)), ("l", l, (batch, hq, splits)),
                            ("o", o, (batch, hq, splits, 128))):
         _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float32
-              and tuple(t.shape) == shape, f"partials {name} must be contiguous float32 {shape}")
+              and tuple(t.shape) == shape and t.device == q.device,
+              f"partials {name} must be contiguous float32 {shape} on q's device")
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
     args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(lam), _ptr(cb_k), _ptr(cb_v),
             _ptr(codes_k), _ptr(codes_v), batch, hq, context_len, splits, _ptr(m), _ptr(l),
@@ -369,13 +423,15 @@ def prepare_merge_partials(partials, out=None) -> PreparedCall:
 
 def _step_common(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v):
     _check_cache(codes_k, codes_v, cb_k, cb_v, lam)
-    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be contiguous [B][Hq][128]")
+    _check_query(q, codes_k)
     batch, hkv = codes_k.shape[0], codes_k.shape[1]
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         _need(t.is_cuda and t.is_contiguous() and t.numel() == batch * hkv * 128
-              and t.shape[0] == batch and t.shape[1] == hkv,
-              f"{name} must be contiguous [B][Hkv][128] (or [B][Hkv][1][128])")
+              and t.shape[0] == batch and t.shape[1] == hkv and t.shape[-1] == 128
+              and t.device == q.device,
+              f"{name} must be contiguous [B][Hkv][128] (or [B][Hkv][1][128]) on q's device")
     _need(k_new.dtype == v_new.dtype, "k_new and v_new must share a dtype")
+    _dtype_code(k_new)
     return batch, q.shape[1]
 
 
@@ -384,11 +440,13 @@ def _step_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len, num_
     batch, hq = _step_common(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v)
     if out is None:
         out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    _check_out(out, batch, hq, q.device)
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
     if workspace is None:
         nbytes = library().vq_decode_step_workspace_bytes(ctypes.byref(lay), batch, hq, cur_len,
                                                          num_splits)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(k_new), _ptr(v_new),
             _dtype_code(k_new), _ptr(lam), _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
             batch, hq, cur_len, num_splits, _ptr(out), _ptr(workspace), workspace.numel())
@@ -421,8 +479,9 @@ def _check_window(win_k, win_v, codes_k):
     batch, hkv = codes_k.shape[0], codes_k.shape[1]
     for name, t in (("win_k", win_k), ("win_v", win_v)):
         _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float16 and t.dim() == 4
-              and t.shape[0] == batch and t.shape[1] == hkv and t.shape[3] == 128,
-              f"{name} must be contiguous float16 [B][Hkv][win_cap][128]")
+              and t.shape[0] == batch and t.shape[1] == hkv and t.shape[3] == 128
+              and t.device == codes_k.device,
+              f"{name} must be contiguous float16 [B][Hkv][win_cap][128] on the cache's device")
     _need(win_k.shape == win_v.shape, "win_k and win_v must have the same shape")
     return int(win_k.shape[2])
 
@@ -447,11 +506,13 @@ def _window_step_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, win_k,
     win_cap = _check_window(win_k, win_v, codes_k)
     if out is None:
         out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    _check_out(out, batch, hq, q.device)
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
     if workspace is None:
         nbytes = library().vq_decode_step_window_workspace_bytes(ctypes.byref(lay), batch, hq,
                                                                  num_codes, num_splits)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(k_new), _ptr(v_new),
             _dtype_code(k_new), _ptr(lam), _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
             _ptr(win_k), _ptr(win_v), win_cap, batch, hq, num_codes, win_len, num_splits,
@@ -527,7 +588,8 @@ def _step_partials_args(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_
     for name, t, shape in (("m", m, (batch, hq, splits)), ("l", l, (batch, hq, splits)),
                            ("o", o, (batch, hq, splits, 128))):
         _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float32
-              and tuple(t.shape) == shape, f"partials {name} must be contiguous float32 {shape}")
+              and tuple(t.shape) == shape and t.device == q.device,
+              f"partials {name} must be contiguous float32 {shape} on q's device")
     lay = make_layout(codes_k, codes_v, cb_k, cb_v)
     args = (ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(k_new), _ptr(v_new),
             _dtype_code(k_new), _ptr(lam), _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v),
@@ -572,14 +634,20 @@ def fp16_decode_attention(q, k, v, context_len: int, num_splits: int = 0, out=No
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t.is_cuda and t.is_contiguous() and t.dtype == torch.float16,
               f"{name} must be a contiguous float16 device tensor")
-    _need(k.shape == v.shape and k.dim() == 4, "k/v must be [B][Hkv][cap][128]")
+    _need(k.shape == v.shape and k.dim() == 4 and k.shape[3] == 128,
+          "k/v must be [B][Hkv][cap][128]")
+    _need(q.dim() == 3 and q.shape[2] == 128 and q.shape[0] == k.shape[0],
+          "q must be [B][Hq][128] with the cache's B")
+    _need(k.device == q.device and v.device == q.device, "q, k and v must share a device")
     batch, hq = q.shape[0], q.shape[1]
     hkv, cap = k.shape[1], k.shape[2]
     if out is None:
         out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    _check_out(out, batch, hq, q.device)
     if workspace is None:
         nbytes = fp16_attention_workspace_bytes(batch, hq, hkv, context_len, num_splits)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     _check(library().vq_fp16_decode_attention(_ptr(q), _ptr(k), _ptr(v), batch, hq, hkv, cap,
                                               context_len, num_splits, _ptr(out),
                                               _ptr(workspace), workspace.numel(), _stream(q)),

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+
 #include "../../include/vqkv.h"
 #include "launchers.hpp"
 
@@ -86,6 +87,20 @@ struct SplitPlan {
 // bytes of its widest rows (48 B), rounded down to whole wave tiles.
 constexpr int kVqMaxSplitTokens = (0x7fffffff / 48) / 32 * 32;
 
+// Longest split the planner gives while the split count allows (up to
+// kMaxSplits): every wave of a split adds its tiles' value products into one
+// fp32 accumulator, and once a dominant token sits in it each later tile's
+// small contribution is rounded against that large value.  The error grows
+// with the tiles a wave takes.  Behind a token 20.5 base-2 units above the
+// rest, with value entries of 30: measured 7e-4 to 1.1e-3 on the GPU for one
+// 65536-token split; a CPU model of the accumulation gives 1e-4 to 5e-4 there,
+// ~2e-3 for one 196608-token split and ~2e-4 at 24576 tokens (48 tiles per
+// wave).  24576 also leaves the default plans of the workload shapes as they
+// are (up to 21856 tokens per split: a 64-stream window step).  Contexts
+// longer than kMaxSplits x 24576 tokens get splits of context / kMaxSplits
+// tokens.
+constexpr int kVqLongestSplit = 24576;
+
 // Splits hold at least `min_len` tokens (one sweep of the workgroup), at most
 // `max_len`, and a multiple of `gran` tokens (one wave tile); the last split
 // takes the rest.  A requested count is clamped into that range.
@@ -116,7 +131,7 @@ int streams_of(int32_t batch, int32_t num_kv_heads) {
 // The VQ kernel's plan for `streams` (sequence, KV head) streams.
 SplitPlan plan_vq(int streams, int context_len, int requested) {
     return plan_splits(streams, context_len, requested, vqkv::kVqTile, kTargetWorkgroups,
-                       vqkv::kVqTileGrain);
+                       vqkv::kVqTileGrain, kVqLongestSplit);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -377,7 +392,7 @@ SplitPlan plan_step(int streams, int cur_len, int requested, int fold = 0) {
     const int n = cur_len > 0 ? cur_len : 1;
     if (fold > 0 && streams >= kFoldStreams && n <= 0x7fffffff - fold) {
         const SplitPlan f = plan_splits(streams, n + fold, requested, vqkv::kVqTile,
-                                        kTargetWorkgroups, vqkv::kVqTileGrain);
+                                        kTargetWorkgroups, vqkv::kVqTileGrain, kVqLongestSplit);
         // every split keeps tokens, and the encode is a small part of one
         if (static_cast<int64_t>(f.num_splits - 1) * f.tokens_per_split < n &&
             f.tokens_per_split >= 2 * fold)
@@ -385,7 +400,8 @@ SplitPlan plan_step(int streams, int cur_len, int requested, int fold = 0) {
     }
     const int target = kTargetWorkgroups > 2 * streams ? kTargetWorkgroups - streams
                                                        : kTargetWorkgroups;
-    return plan_splits(streams, n, requested, vqkv::kVqTile, target, vqkv::kVqTileGrain);
+    return plan_splits(streams, n, requested, vqkv::kVqTile, target, vqkv::kVqTileGrain,
+                       kVqLongestSplit);
 }
 
 vqkv::AppendArgs append_args(const void* k_new, const void* v_new, int kv_dtype, int cur_len,
