@@ -21,7 +21,9 @@
  * ---------------------------------------
  *  - All array pointers are DEVICE pointers allocated and owned by the
  *    caller.  The library allocates no device memory; split partials live in
- *    a caller-provided workspace or caller-provided arrays.
+ *    a caller-provided workspace or caller-provided arrays, except those of
+ *    vq_decode_step_noalloc, which go to one static 4 MiB device array per
+ *    GPU inside the library.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call only enqueues work on that stream and returns without
  *    synchronising.  Faults inside kernels surface at the caller's next
@@ -256,6 +258,37 @@ int vq_decode_step_partials(const vq_layout* layout, const void* q, int q_dtype,
                             uint8_t* codes_k, uint8_t* codes_v, int32_t batch,
                             int32_t num_q_heads, int32_t cur_len, int32_t num_partials,
                             float* part_m, float* part_l, float* part_o, void* stream);
+
+/*
+ * vq_decode_step_noalloc: vq_decode_step for callers that cannot allocate
+ * device memory or pass a workspace — code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, codes
+ * and results as vq_decode_step minus the workspace: the split partials go
+ * to a static device buffer of VQ_NOALLOC_SCRATCH_BYTES (4 MiB) inside the
+ * library, one per GPU, held until the process ends.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *  - Limit: the step's partials, vq_decode_step_workspace_bytes(...) for the
+ *    same shape and num_splits, must fit the buffer (VQ_ERR_WORKSPACE
+ *    otherwise, before anything is enqueued): e.g. B * Hq * partials up to
+ *    about 8000 at the default plans (a 32-query-head layer at B = 16:
+ *    0.8 MB).
+ *  - The buffer is the current device's: `stream` must belong to it.  The
+ *    first call on a device resolves the buffer's address
+ *    (hipGetSymbolAddress); make one call before capturing a graph.
+ *  - Every call on a GPU shares that GPU's buffer: calls that may overlap on
+ *    one GPU (other streams, other threads) race and must be serialised by
+ *    the caller.  Each call writes every partial it reads, so the buffer's
+ *    contents from an earlier call never matter.
+ * Errors as vq_decode_step, plus VQ_ERR_HIP if the buffer's address cannot
+ * be resolved.
+ */
+#define VQ_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int vq_decode_step_noalloc(const vq_layout* layout, const void* q, int q_dtype,
+                           const void* k_new, const void* v_new, int kv_dtype,
+                           const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                           uint8_t* codes_k, uint8_t* codes_v, int32_t batch,
+                           int32_t num_q_heads, int32_t cur_len, int32_t num_splits, float* out,
+                           void* stream);
 
 /*
  * Decode step with a full-precision residual window: the most recent tokens

@@ -298,6 +298,44 @@ def test_decode_step_validation(lib, kw, status, needle):
     assert needle in vq._last_error()
 
 
+def step_noalloc(lib, layout, cur=10, splits=0, kv_dtype=0, kn=A, vn=A, out=A, hq=4, batch=1):
+    return lib.vq_decode_step_noalloc(ctypes.byref(layout), A, 0, kn, vn, kv_dtype, A, A, A, A, A,
+                                      batch, hq, cur, splits, out, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cur=1000), CAPACITY, "capacity"),
+    (dict(cur=-1), INVALID, "cur_len"),
+    (dict(kv_dtype=5), INVALID, "kv_dtype"),
+    (dict(kn=None), INVALID, "k_new"),
+    (dict(vn=MIS), INVALID, "v_new"),
+    (dict(out=None), INVALID, "out"),
+    (dict(hq=3), INVALID, "multiple"),
+])
+def test_decode_step_noalloc_validation(lib, kw, status, needle):
+    assert step_noalloc(lib, lay(hkv=2), **kw) == status, vq._last_error()
+    assert needle in vq._last_error()
+
+
+def test_decode_step_noalloc_rejects_partials_beyond_its_buffer(lib):
+    """256 sequences x 32 query heads need 8.5 MB of partials, more than the
+    4 MiB static buffer: rejected on the host, before any device call."""
+    layout = lay(hkv=8, cap=1001)
+    need = lib.vq_decode_step_workspace_bytes(ctypes.byref(layout), 256, 32, 1000, 0)
+    assert need > vq.NOALLOC_SCRATCH_BYTES
+    assert step_noalloc(lib, layout, cur=1000, hq=32, batch=256) == WORKSPACE
+    assert "static buffer" in vq._last_error()
+    # the largest batch that fits is accepted by the same size rule
+    per_seq = lib.vq_decode_step_workspace_bytes(ctypes.byref(layout), 1, 32, 1000, 0)
+    assert per_seq <= vq.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_buffer_size_matches_the_header(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define VQ_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == vq.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_step_partials_validation(lib):
     f = lib.vq_decode_step_partials
     layout = lay(hkv=2)

@@ -76,7 +76,8 @@ def test_decode_attention_refuses(cache, name, make, needle):
     assert needle in str(e.value), str(e.value)
 
 
-@pytest.mark.parametrize("fn", [vq.decode_step], ids=["decode_step"])
+@pytest.mark.parametrize("fn", [vq.decode_step, vq.decode_step_noalloc],
+                         ids=["decode_step", "decode_step_noalloc"])
 @pytest.mark.parametrize("name,make,needle", BAD, ids=[b[0] for b in BAD])
 def test_decode_step_refuses(cache, fn, name, make, needle):
     with pytest.raises(ValueError) as e:

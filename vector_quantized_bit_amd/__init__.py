@@ -80,6 +80,8 @@ def library() -> ctypes.CDLL:
         "vq_decode_step_workspace_bytes": (_size, [lp, _i32, _i32, _i32, _i32]),
         "vq_decode_step": (_c_int, [lp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
                                     _i32, _i32, _i32, _i32, _vp, _vp, _size, _vp]),
+        "vq_decode_step_noalloc": (_c_int, [lp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp,
+                                            _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
         "vq_decode_step_partials": (_c_int, [lp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp,
                                              _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                              _vp]),
@@ -473,6 +475,27 @@ def prepare_decode_step(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_
                          workspace), q.device)
     call.out = out
     return call
+
+
+def decode_step_noalloc(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v, cur_len: int,
+                        num_splits: int = 0, out=None):
+    """``decode_step`` through vq_decode_step_noalloc: the library keeps the
+    split partials in its static device buffer (VQ_NOALLOC_SCRATCH_BYTES, 4
+    MiB per GPU), so the call needs no workspace.  Calls on one GPU must not
+    overlap.  ``out`` (float32 [B][Hq][128]) is allocated here if not given."""
+    batch, hq = _step_common(q, k_new, v_new, lam, cb_k, cb_v, codes_k, codes_v)
+    if out is None:
+        out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+    _check_out(out, batch, hq, q.device)
+    lay = make_layout(codes_k, codes_v, cb_k, cb_v)
+    _check(library().vq_decode_step_noalloc(
+        ctypes.byref(lay), _ptr(q), _dtype_code(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+        _ptr(lam), _ptr(cb_k), _ptr(cb_v), _ptr(codes_k), _ptr(codes_v), batch, hq, cur_len,
+        num_splits, _ptr(out), _stream(q)), "vq_decode_step_noalloc")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 def _check_window(win_k, win_v, codes_k):

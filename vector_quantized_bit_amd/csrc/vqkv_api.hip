@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
 
 #include "../../include/vqkv.h"
 #include "launchers.hpp"
@@ -558,6 +560,82 @@ int vq_decode_step(const vq_layout* layout, const void* q, int q_dtype, const vo
     if (st) return st;
     return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, nparts, part, out, s),
                       "decode_step merge launch");
+}
+
+// ---- decode step with no allocation ------------------------------------------
+// The split partials of vq_decode_step_noalloc live in this file-scope device
+// array (one copy per GPU, held until the process ends).  Host code never
+// passes its name to a kernel: the array's device address is resolved once
+// per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = VQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device (resolved on the
+// first call there), or VQ_ERR_HIP.
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(VQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(VQ_ERR_HIP, "device %d beyond the %d devices this entry point serves", dev,
+                    kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr)
+                return fail(VQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                            hipGetErrorString(e));
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return VQ_OK;
+}
+
+}  // namespace
+
+int vq_decode_step_noalloc(const vq_layout* layout, const void* q, int q_dtype,
+                           const void* k_new, const void* v_new, int kv_dtype,
+                           const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
+                           uint8_t* codes_k, uint8_t* codes_v, int32_t batch,
+                           int32_t num_q_heads, int32_t cur_len, int32_t num_splits, float* out,
+                           void* stream) {
+    int st = check_step_args(layout, q, q_dtype, k_new, v_new, kv_dtype, lambda, cb_k, cb_v,
+                             codes_k, codes_v, batch, num_q_heads, cur_len, num_splits);
+    if (st) return st;
+    VQ_REQUIRE_PTR(out);
+    const SplitPlan p = plan_step(streams_of(batch, layout->num_kv_heads), cur_len, num_splits,
+                                  fold_tokens(layout));
+    const int nparts = p.num_splits + 1;
+    const size_t need = partials_bytes(batch, num_q_heads, nparts);
+    if (need > kScratchBytes)
+        return fail(VQ_ERR_WORKSPACE,
+                    "the step's partials take %zu bytes, above the %zu-byte static buffer of "
+                    "vq_decode_step_noalloc (use vq_decode_step with a workspace)",
+                    need, kScratchBytes);
+    void* ws = nullptr;
+    if ((st = scratch_for_current_device(&ws))) return st;
+    const vqkv::Partials part = carve_partials(ws, batch, num_q_heads, nparts);
+    const vqkv::AttnShape shape{batch, num_q_heads, layout->num_kv_heads, layout->capacity, cur_len,
+                                p.num_splits, p.tokens_per_split};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(vqkv::launch_vq_attention(
+                        shape, layout->k_code_bits, layout->sub_dim, q, q_dtype == VQ_F32, lambda, cb_k, cb_v,
+                        codes_k, codes_v, part,
+                        append_args(k_new, v_new, kv_dtype, cur_len, codes_k, codes_v, p.fold), s),
+                    "decode_step_noalloc launch");
+    if (st) return st;
+    return hip_status(vqkv::launch_merge_partials(batch, num_q_heads, nparts, part, out, s),
+                      "decode_step_noalloc merge launch");
 }
 
 int32_t vq_decode_step_window_num_partials(const vq_layout* layout, int32_t batch,
