@@ -88,6 +88,18 @@ typedef enum {
 
 typedef enum { VQ_F16 = 0, VQ_F32 = 1 } vq_dtype;
 
+/*
+ * Deterministic mode, for the whole library (all devices and threads):
+ * with on != 0 the split kernel hands its 32-token tiles to its 16 waves in
+ * a fixed order (wave w takes tiles w, w + 16, ...) instead of as waves
+ * become free, so repeated calls with the same inputs and split plan give
+ * bit-identical outputs and partials; the encoders, the merge and the
+ * calibration kernels are deterministic in either mode.  About 2-3% slower
+ * at the 196608-token Llama-3.1-8B layer (measured on MI355X).  Applies to
+ * calls made after it returns.  Returns the previous setting (0 or 1).
+ */
+int vq_set_deterministic(int on);
+
 /* Cache geometry, plain data, passed by pointer. */
 typedef struct {
     int32_t head_dim;      /* D: must be 128                          */
@@ -162,7 +174,8 @@ size_t vq_decode_attention_workspace_bytes(const vq_layout* layout, int32_t batc
  * context_len < 1 (softmax over an empty set) or Hq % Hkv != 0;
  * VQ_ERR_UNSUPPORTED if G > 8; VQ_ERR_WORKSPACE if the workspace is too small.
  * Tiles are scheduled dynamically inside a split, so repeated calls agree to
- * fp32 rounding (not bit for bit).
+ * fp32 rounding, not bit for bit, unless deterministic mode is on
+ * (vq_set_deterministic).
  */
 int vq_decode_attention(const vq_layout* layout, const void* q, int q_dtype,
                         const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,

@@ -850,3 +850,46 @@ def test_d8_decode_step_window_folded():
     wl = d8_workload(170, 32, 4, 4, 20000)
     check_window_step(random_cache(wl), 20000, 127, splits=2, heads=[(0, 1), (19, 2), (31, 3)],
                       what="1.5bit folded window")
+
+
+# --- deterministic mode: a bitwise run-to-run check (race canary) -----------------
+
+@pytest.mark.parametrize("layout", [(4, 8, 4, 5000), (5, 12, 4, 3000), (4, 12, 8, 4000),
+                                    (8, 8, 4, 2049)],
+                         ids=lambda l: f"G{l[0]}-k{l[1]}-d{l[2]}-n{l[3]}")
+def test_deterministic_mode_is_bitwise_reproducible(layout):
+    """With a fixed tile order nothing in a call depends on timing, so any
+    difference between repeated calls would come from a race (an LDS write
+    not ordered before its read, a missing barrier, an uninitialised read).
+    Every output and partial must repeat bit for bit: the split pass alone,
+    decode attention and a decode step (each on its own copy of the cache),
+    over ragged lengths and several split counts."""
+    g, kb, sd, n = layout
+    wl = W.Workload(120 + g + kb, "adhoc", batch=2, num_q_heads=2 * g, num_kv_heads=2,
+                    context_len=n, k_bits=kb, v_bits=12 if sd == 8 else 8, sub_dim=sd,
+                    qkv_dtype="f16", append_tokens=1)
+    c = random_cache(wl)
+    d = upload(c)
+    rng = np.random.default_rng(9)
+    kn = dev(rng.standard_normal((2, 2, 128)).astype(np.float16))
+    prev = vq.set_deterministic(True)
+    try:
+        for splits in (1, 3, 0):
+            runs = []
+            for _ in range(3):
+                ck, cv = d["codes_k"].clone(), d["codes_v"].clone()
+                parts = vq.decode_attention_partials(d["q"], d["lam"], d["cb_k"], d["cb_v"], ck,
+                                                     cv, n, num_splits=splits)
+                att = vq.decode_attention(d["q"], d["lam"], d["cb_k"], d["cb_v"], ck, cv, n,
+                                          num_splits=splits)
+                stp = vq.decode_step(d["q"], kn, kn, d["lam"], d["cb_k"], d["cb_v"], ck, cv,
+                                     n, num_splits=splits)
+                torch.cuda.synchronize()
+                runs.append([t.cpu().numpy() for t in (*parts, att, stp, ck, cv)])
+            for other in runs[1:]:
+                for a, b in zip(runs[0], other):
+                    assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), splits
+        ref = expected_all(c)
+        assert_close(runs[0][3].astype(np.float64), ref, f"deterministic G={g} kb={kb} d={sd}")
+    finally:
+        vq.set_deterministic(prev)

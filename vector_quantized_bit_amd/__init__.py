@@ -100,6 +100,7 @@ def library() -> ctypes.CDLL:
         "vq_fp16_attention_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32]),
         "vq_fp16_decode_attention": (_c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _vp, _vp, _size, _vp]),
+        "vq_set_deterministic": (_c_int, [_c_int]),
         "vq_status_string": (ctypes.c_char_p, [_c_int]),
         "vq_last_error": (ctypes.c_char_p, []),
     }
@@ -109,6 +110,13 @@ def library() -> ctypes.CDLL:
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def set_deterministic(on: bool) -> bool:
+    """Library-wide deterministic mode (vq_set_deterministic): a fixed tile
+    order in the split kernel, so repeated calls give bit-identical results.
+    Returns the previous setting."""
+    return bool(library().vq_set_deterministic(1 if on else 0))
 
 
 def status_string(status: int) -> str:

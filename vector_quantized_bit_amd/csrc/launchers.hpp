@@ -82,6 +82,11 @@ hipError_t launch_kmeans(const float* samples, int num_sets, int num_samples, in
                          uint16_t* codebook, int32_t* assign, void* workspace,
                          hipStream_t stream);
 
+// Library-wide deterministic mode (vq_set_deterministic): the split kernel
+// hands tiles to waves in a fixed order, so results do not depend on timing.
+bool deterministic();
+bool set_deterministic(bool on);   // returns the previous setting
+
 // Tokens one workgroup of the VQ split kernel processes per tile; split
 // lengths are multiples of it.
 constexpr int kVqWaves = 16;       // waves per workgroup of the VQ kernel; each leaves a partial

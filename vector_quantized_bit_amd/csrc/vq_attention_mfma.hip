@@ -47,7 +47,10 @@
 //    the rest of the tile is computed.
 //  * Tiles are handed to waves dynamically (LDS counter), so the tokens a
 //    wave folds into its online softmax depend on timing: results agree run
-//    to run to fp32 rounding, not bit for bit.
+//    to run to fp32 rounding, not bit for bit.  In deterministic mode
+//    (vq_set_deterministic) wave w takes tiles w, w + 16, ... instead, and
+//    every launch with the same inputs gives the same bits (2-3% slower at
+//    the 196608-token layer).
 //  * The workgroup folds its 16 wave states in LDS and leaves one base-2
 //    partial (m, l, o); a second, small kernel merges the splits by
 //    log-sum-exp.  Merging the splits inside this kernel would need a
@@ -917,7 +920,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     Partials part, const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
     int append_pos, uint8_t* __restrict__ new_codes_k, uint8_t* __restrict__ new_codes_v,
     int part_stride, uint16_t* __restrict__ win_k, uint16_t* __restrict__ win_v, int win_len,
-    int win_cap, int fold) {
+    int win_cap, int fold, int static_tiles) {
     static_assert(G >= 1 && G <= 8, "2G MFMA rows");
     // G <= 4: the rows of every head are in lanes 0-31 of an MFMA result, so
     // the softmax packs a tile's two 16-token blocks into one set of lanes
@@ -1103,24 +1106,28 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         reinterpret_cast<uint4*>(&pbuf[0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);
         static_assert(sizeof(pbuf) == kThreads * sizeof(uint4), "one 16-byte store per thread");
     }
-    float x0 = q_f32 ? __builtin_bit_cast(float, qw0) : lo_half_to_float(qw0);
-    float x1 = q_f32 ? __builtin_bit_cast(float, qw1) : hi_half_to_float(qw0);
-    // Every wave transforms (waves >= G a copy of head G - 1, discarded), so
-    // the q loads are not sunk behind the tile loads into a branch.  Waves
-    // 0 .. 7 then write head `wave` (zeros for wave >= G) straight into the
-    // score A operand, shared by every wave: lane (16 qg + r) of K-step kk
-    // holds row r for dims 32 qg + 8 kk + e, e = 0 .. 7, where row r is head
-    // 2 (r / 4) + r % 2, its fp16 high part for r % 4 < 2, else the low part
-    // (x - hi rounded to fp16), both of x 2^e (the head's largest element in
-    // [2^14, 2^15); 2^-e goes to qsc).  This lane's dims 2 lane, 2 lane + 1 are
-    // elements e = 2 (lane % 4), + 1 of entry qg = lane / 16, kk = lane % 16 / 4.
-    x0 *= lam2.x;
-    x1 *= lam2.y;
-    fwht128(x0, x1);
+    // Waves 0 .. G - 1 transform head `wave`; waves G .. 7 leave zeros.  Waves
+    // 0 .. 7 then write their rows straight into the score A operand, shared
+    // by every wave: lane (16 qg + r) of K-step kk holds row r for dims
+    // 32 qg + 8 kk + e, e = 0 .. 7, where row r is head 2 (r / 4) + r % 2, its
+    // fp16 high part for r % 4 < 2, else the low part (x - hi rounded to
+    // fp16), both of x 2^e (the head's largest element in [2^14, 2^15); 2^-e
+    // goes to qsc).  This lane's dims 2 lane, 2 lane + 1 are elements
+    // e = 2 (lane % 4), + 1 of entry qg = lane / 16, kk = lane % 16 / 4.
+    // Only G waves (one per SIMD at G = 4) run the butterflies: with every
+    // wave transforming, the 16 copies took most of the prologue.  The empty
+    // asm keeps the q loads (issued first, every wave) ahead of the branch,
+    // so they are not sunk behind the tile loads.
+    asm volatile("" ::"v"(qw0), "v"(qw1), "v"(lam2.x), "v"(lam2.y));
     if (wave < 8) {
-        const bool real = wave < G;
-        x0 = real ? x0 * kScoreScaleLog2 : 0.f;
-        x1 = real ? x1 * kScoreScaleLog2 : 0.f;
+        float x0 = 0.f, x1 = 0.f;
+        if (wave < G) {
+            x0 = (q_f32 ? __builtin_bit_cast(float, qw0) : lo_half_to_float(qw0)) * lam2.x;
+            x1 = (q_f32 ? __builtin_bit_cast(float, qw1) : hi_half_to_float(qw0)) * lam2.y;
+            fwht128(x0, x1);
+            x0 *= kScoreScaleLog2;
+            x1 *= kScoreScaleLog2;
+        }
         const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
         const int ex = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);
         x0 = __builtin_amdgcn_ldexpf(x0, ex);
@@ -1251,10 +1258,12 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         // A row's maximum exceeds m + tau exactly when one of its scores
         // does, so the rescale test needs no row reduction; the row maxima
         // are formed only on the (rare) rescale.
-        bool over = false;
+        // (one wave ballot per comparison: the masks combine in SGPRs)
+        uint64_t over = 0;
 #pragma unroll
-        for (int sb = 0; sb < kSb; ++sb) over = over || sA[sb] > thA || sB[sb] > thB;
-        if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        for (int sb = 0; sb < kSb; ++sb)
+            over |= __builtin_amdgcn_ballot_w64(sA[sb] > thA) | __builtin_amdgcn_ballot_w64(sB[sb] > thB);
+        if (over != 0) {
             float cA = sA[0], cB = sB[0];
             if constexpr (!kPack) {
                 cA = fmaxf(sA[0], sA[1]);
@@ -1353,7 +1362,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 
     // Tiles are handed out from an LDS counter as waves become free: the SIMD
     // issue arbiter favours older waves, so a fixed interleave leaves the
-    // youngest waves with a long tail.  A single register set holds a tile's
+    // youngest waves with a long tail (it is used only in deterministic mode).  A single register set holds a tile's
     // codes and is refilled during the tile (a second set, alternated by
     // unrolling, made the compiler copy the 32 output accumulators on every
     // other tile).
@@ -1364,7 +1373,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     };
     int cur = wave;
     while (cur * kTok < t_len) {
-        const int nxt = grab();
+        const int nxt = static_tiles ? cur + kWaves : grab();
         compute_tile(cur * kTok, kA, vA, nxt * kTok);
         cur = nxt;
     }
@@ -1469,7 +1478,8 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
                            s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
                            s.num_splits, s.tokens_per_split, part, ap.k_new, ap.v_new,        \
                            ap.kv_f32 ? 1 : 0, pos, ap.codes_k, ap.codes_v, stride,           \
-                           ap.win_k, ap.win_v, ap.win_len, ap.win_cap, fold ? 1 : 0);        \
+                           ap.win_k, ap.win_v, ap.win_len, ap.win_cap, fold ? 1 : 0,         \
+                           deterministic() ? 1 : 0);                                         \
         break;
     switch (group) {
         VQKV_LAUNCH(1)

@@ -10,6 +10,17 @@
 #include "../../include/vqkv.h"
 #include "launchers.hpp"
 
+namespace vqkv {
+
+namespace {
+std::atomic<bool> g_deterministic{false};
+}
+
+bool deterministic() { return g_deterministic.load(std::memory_order_relaxed); }
+bool set_deterministic(bool on) { return g_deterministic.exchange(on); }
+
+}  // namespace vqkv
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -175,6 +186,9 @@ const char* vq_status_string(int status) {
 }
 
 const char* vq_last_error(void) { return g_last_error; }
+
+int vq_set_deterministic(int on) { return vqkv::set_deterministic(on != 0) ? 1 : 0; }
+
 
 int vq_transform_query(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
                        int32_t batch, int32_t num_q_heads, float* q_tilde, void* stream) {
