@@ -98,12 +98,36 @@ def cpu_baseline(wl: W.Workload, seconds: float) -> dict:
     # the same oracle with its thread pools held to one thread, a shorter sample
     with threadpool_limits(limits=1):
         done1, dt1 = run(seconds / 4)
-    return {"value": n / per_layer, "unit": "KV tokens/s per layer",
+    value = n / per_layer
+    value1 = n / (dt1 / done1 * wl.num_kv_heads)
+    return {"value": value, "unit": "KV tokens/s per layer",
             "cores": int(threads), "kind": "oracle",
             "sample": f"{done} KV-head passes (of {wl.num_kv_heads} per layer) of sequence 0 at "
                       f"N={n} in {dt:.1f} s, scaled to one layer of one sequence",
-            "single_thread": {"value": n / (dt1 / done1 * wl.num_kv_heads), "cores": 1,
+            "host": host_info(),
+            "thread_scaling": value / value1,
+            "note": "cores is the BLAS thread pool the oracle ran with; only its two matrix "
+                    "products use it, and its table-lookup dequantisation (most of the time) "
+                    "runs on one core, so the rate barely scales with threads "
+                    "(thread_scaling = rate / single-thread rate)",
+            "single_thread": {"value": value1, "cores": 1,
                               "sample": f"{done1} KV-head passes in {dt1:.1f} s"}}
+
+
+def host_info() -> dict:
+    """The host CPU the oracle ran on: model name, logical CPUs, the CPUs this
+    process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0))}
 
 
 # Sources that determine the attention kernel's code: a counter record taken
@@ -528,7 +552,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 MFMA operands (q~ and p split into hi/lo fp16 parts), f32 accumulate",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": bsz, "context_len": n, "q_heads": hq,
                    "kv_heads": hkv, "head_dim": 128, "k_code_bits": wl.k_bits,

@@ -509,3 +509,27 @@ def test_kmeans_workspace_layout(lib):
     for bad in ((0, 10, 4, 8), (1, 0, 4, 8), (1, 10, 4, 9), (1, (1 << 28) + 1, 4, 8),
                 (1, 10, 5, 8)):
         assert lib.vq_kmeans_workspace_bytes(*bad) == 0
+
+
+def _visible_gpus(lib):
+    n = ctypes.c_int(0)
+    rc = lib.hipGetDeviceCount(ctypes.byref(n))
+    return n.value if rc == 0 else 0
+
+
+def test_runtime_errors_come_back_as_vq_err_hip(lib):
+    """A call that passes validation but cannot launch reports VQ_ERR_HIP with
+    the runtime's message.  Forced here by the missing device: this test runs
+    only where the HIP runtime sees no GPU (it would otherwise launch kernels
+    on the fake addresses)."""
+    if _visible_gpus(lib) > 0:
+        pytest.skip("a GPU is visible: the calls below would launch")
+    assert lib.vq_merge_partials(1, 4, 2, A, A, A, A, None) == HIP
+    assert "merge_partials launch" in vq._last_error()
+    layout = lay(hkv=1, cap=100)
+    assert lib.vq_transform_query(ctypes.byref(layout), A, 0, A, 1, 4, A, None) == HIP
+    assert "device" in vq._last_error()
+    assert attn(lib, layout, n=100) == HIP
+    assert vq.status_string(HIP) == "HIP runtime error"
+    # a later call that fails validation reports its own error, not the old one
+    assert attn(lib, layout, n=0) == INVALID and "context_len" in vq._last_error()

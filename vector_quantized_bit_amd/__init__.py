@@ -29,7 +29,10 @@ __all__ = [
     "kmeans_workspace_bytes", "kmeans",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvqkv.so")
+# VQKV_LIBRARY names another build of the library to load instead (the
+# tests' host-sanitized build, for one)
+LIB_PATH = os.environ.get("VQKV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libvqkv.so")
 
 VQ_F16, VQ_F32 = 0, 1
 _c_int = ctypes.c_int

@@ -40,5 +40,23 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """libvqkv_hostsan.so: the library with its host code (argument
+    validation, split planning, workspace layout, dispatch) built with
+    AddressSanitizer and UndefinedBehaviorSanitizer; device code as usual.
+    Test infrastructure for the C ABI's host side."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = out + ".tmp"
+    cmd = [hipcc, *FLAGS, "-g",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-I", os.path.join(os.path.dirname(HERE), "include"), *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose="-q" not in sys.argv)

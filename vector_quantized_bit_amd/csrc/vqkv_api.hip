@@ -124,7 +124,7 @@ SplitPlan plan_splits(int streams, int context_len, int requested, int min_len,
     const int64_t n = context_len;   // (64-bit: contexts reach 2^31 - 1 tokens)
     int64_t max_splits = (n + min_len - 1) / min_len;
     if (max_splits > vqkv::kMaxSplits) max_splits = vqkv::kMaxSplits;
-    int64_t s = requested > 0 ? requested : (target + streams - 1) / streams;
+    int64_t s = requested > 0 ? requested : (static_cast<int64_t>(target) + streams - 1) / streams;
     const int64_t min_splits = (n + max_len - 1) / max_len;
     if (s < min_splits) s = min_splits;
     if (s < 1) s = 1;
@@ -414,8 +414,9 @@ SplitPlan plan_step(int streams, int cur_len, int requested, int fold = 0) {
             f.tokens_per_split >= 2 * fold)
             return SplitPlan{f.num_splits, f.tokens_per_split, true};
     }
-    const int target = kTargetWorkgroups > 2 * streams ? kTargetWorkgroups - streams
-                                                       : kTargetWorkgroups;
+    const int target = kTargetWorkgroups > 2 * static_cast<int64_t>(streams)
+                           ? kTargetWorkgroups - streams
+                           : kTargetWorkgroups;
     return plan_splits(streams, n, requested, vqkv::kVqTile, target, vqkv::kVqTileGrain,
                        kVqLongestSplit);
 }
