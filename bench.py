@@ -148,16 +148,20 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_counters(workload: str) -> dict | None:
+def measured_counters(workload: str, score_method: str) -> dict | None:
     """Per-dispatch shader counters of the split kernel (waves, instructions,
     LDS activity) from the committed counter record of this workload, or None
-    when there is no record or the kernel sources have changed since."""
-    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    when there is no record, it was taken with another score method, or the
+    kernel sources have changed since."""
+    suffix = "" if score_method == "mfma" else f".{score_method}"
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}{suffix}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    if rec.get("score_method", "mfma") != score_method:
         return None
     return dict(rec["per_dispatch"], source=os.path.relpath(path, ROOT))
 
@@ -186,17 +190,20 @@ def percentiles(us: np.ndarray) -> dict:
             "p90": float(np.percentile(us, 90)), "calls": int(us.size)}
 
 
-def measured_traffic(workload: str) -> dict | None:
+def measured_traffic(workload: str, score_method: str) -> dict | None:
     """HBM bytes per attention launch from the committed counter record of
     this workload (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what
     the same counter read for a plain copy of known size), or None when there
-    is no record or the kernel sources have changed since it was taken."""
+    is no record, it was taken with another score method, or the kernel
+    sources have changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    if rec.get("score_method", "mfma") != score_method:
         return None
     fetch = rec["fetch_kib_per_dispatch"] * 1024 * rec["fetch_scale"]
     write = rec["write_kib_per_dispatch"] * 1024 * rec["write_scale"]
@@ -372,6 +379,11 @@ def main(argv=None) -> int:
                     help="skip the calibration timings (lambda, K~, K-Means)")
     ap.add_argument("--kmeans-iters", type=int, default=3,
                     help="Lloyd iterations per timed K-Means call")
+    ap.add_argument("--score-method", choices=["mfma", "lut"], default="mfma",
+                    help="split-kernel scores: matrix cores (default) or the q~ . C_k lookup "
+                         "table (8-bit keys, G <= 4)")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="fixed tile order in the split kernel (bit-reproducible results)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -386,6 +398,8 @@ def main(argv=None) -> int:
 
     wl = W.WORKLOADS[args.config]
     dev = torch.device("cuda:0")
+    vq.set_score_method(vq.SCORES_LUT if args.score_method == "lut" else vq.SCORES_MFMA)
+    vq.set_deterministic(args.deterministic)
     torch.cuda.set_device(dev)
     n, cap, bsz, hkv, hq = wl.context_len, wl.context_len, wl.batch, wl.num_kv_heads, wl.num_q_heads
     st = np.float16 if wl.qkv_dtype == "f16" else np.float32
@@ -539,7 +553,7 @@ def main(argv=None) -> int:
     ab = algorithmic_bytes(wl, n, append=True)
     ab_attn = algorithmic_bytes(wl, n)
     achieved = ab["total"] / (attn_us * 1e-6) / 1e9
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name, args.score_method)
     tokens = bsz * n
     result = {
         "metric": METRIC,
@@ -558,7 +572,8 @@ def main(argv=None) -> int:
                    "kv_heads": hkv, "head_dim": 128, "k_code_bits": wl.k_bits,
                    "v_code_bits": wl.v_bits, "sub_dim": wl.sub_dim, "append_tokens_per_step": 1,
                    "step_partials": step_parts, "attention_splits": splits,
-                   "cold_cache_copies": copies},
+                   "cold_cache_copies": copies, "score_method": args.score_method,
+                   "deterministic": args.deterministic},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic["bytes"],
@@ -578,7 +593,7 @@ def main(argv=None) -> int:
                              "per_call_us": call_pct},
         "decode_step_per_call_us": step_pct,
     }
-    counters = measured_counters(wl.name)
+    counters = measured_counters(wl.name, args.score_method)
     if counters is not None:
         result["roofline"]["counters"] = counters
     copy_gbps = copy_bandwidth(torch, dev, head_start)

@@ -100,6 +100,26 @@ typedef enum { VQ_F16 = 0, VQ_F32 = 1 } vq_dtype;
  */
 int vq_set_deterministic(int on);
 
+/*
+ * Score method of the attention entry points, for the whole library:
+ *   VQ_SCORES_MFMA (default): the query's two fp16 parts times the
+ *     dequantised keys on the matrix cores (the key table read as MFMA
+ *     operands);
+ *   VQ_SCORES_LUT: the VecInfer page's lookup table (Appendix, Algorithm 1:
+ *     the table of q~ against C_k, then every score a sum of its entries):
+ *     each workgroup first fills LUT[pos][code] = q~[4 pos .. 4 pos + 3] .
+ *     C_k[code] for its query heads in fp32, then each score is the sum of
+ *     32 entries, one per sub-vector position.  Only 8-bit keys with 4-dim
+ *     sub-vectors and G <= 4; other layouts keep the matrix-core scores.
+ *     The LUT takes 128 KiB of LDS, so the value table has 4 copies instead
+ *     of 32 (bank conflicts in its reads).  Slower on MI355X; it exists to
+ *     measure the pages' design against the default.
+ * Applies to calls made after it returns.  Returns the previous method, or
+ * -1 (VQ_ERR_INVALID_ARG in vq_last_error) for an unknown one.
+ */
+typedef enum { VQ_SCORES_MFMA = 0, VQ_SCORES_LUT = 1 } vq_score_method;
+int vq_set_score_method(int method);
+
 /* Cache geometry, plain data, passed by pointer. */
 typedef struct {
     int32_t head_dim;      /* D: must be 128                          */

@@ -104,6 +104,7 @@ def library() -> ctypes.CDLL:
         "vq_fp16_decode_attention": (_c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _vp, _vp, _size, _vp]),
         "vq_set_deterministic": (_c_int, [_c_int]),
+        "vq_set_score_method": (_c_int, [_c_int]),
         "vq_status_string": (ctypes.c_char_p, [_c_int]),
         "vq_last_error": (ctypes.c_char_p, []),
     }
@@ -120,6 +121,20 @@ def set_deterministic(on: bool) -> bool:
     order in the split kernel, so repeated calls give bit-identical results.
     Returns the previous setting."""
     return bool(library().vq_set_deterministic(1 if on else 0))
+
+
+SCORES_MFMA = 0
+SCORES_LUT = 1
+
+
+def set_score_method(method: int) -> int:
+    """Library-wide score method (vq_set_score_method): SCORES_MFMA (default)
+    or SCORES_LUT (the lookup-table scores; 8-bit keys, d = 4, G <= 4).
+    Returns the previous method."""
+    prev = int(library().vq_set_score_method(int(method)))
+    if prev < 0:
+        raise ValueError(_last_error())
+    return prev
 
 
 def status_string(status: int) -> str:

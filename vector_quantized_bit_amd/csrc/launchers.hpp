@@ -87,6 +87,12 @@ hipError_t launch_kmeans(const float* samples, int num_sets, int num_samples, in
 bool deterministic();
 bool set_deterministic(bool on);   // returns the previous setting
 
+// Library-wide score method of the split kernel (vq_set_score_method).
+constexpr int kScoresMfma = 0;     // matrix-core products with dequantised keys
+constexpr int kScoresLut = 1;      // sums of q~ . C_k lookup-table entries
+int score_method();
+int set_score_method(int method);   // returns the previous method
+
 // Tokens one workgroup of the VQ split kernel processes per tile; split
 // lengths are multiples of it.
 constexpr int kVqWaves = 16;       // waves per workgroup of the VQ kernel; each leaves a partial

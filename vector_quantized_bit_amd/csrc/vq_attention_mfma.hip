@@ -196,6 +196,20 @@ struct Chunk8 {
     }
 };
 
+// The 32 key codes (bytes) of one token, for the lookup-table score path.
+struct LutCodes {
+    uint32_t w[8];
+    __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[i] = a[i];
+            w[4 + i] = b[i];
+        }
+    }
+};
+
 }  // namespace
 
 // Inputs of the new-token workgroups: q~ of head `wave` (fp32, base-2 score
@@ -911,7 +925,7 @@ __device__ __forceinline__ void window_workgroup(
     }
 }
 
-template <int G, int KBITS, int SUB>
+template <int G, int KBITS, int SUB, bool LUT>
 __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const void* __restrict__ q, int q_f32, const float* __restrict__ lambda,
     const uint16_t* __restrict__ cb_k, const uint16_t* __restrict__ cb_v,
@@ -931,6 +945,11 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // 12-bit codes for K and V
     constexpr bool kD8 = SUB == 8;
     static_assert(SUB == 4 || (SUB == 8 && KBITS == 12), "d = 4, or d = 8 with 12-bit codes");
+    // LUT: the lookup-table score path (8-bit keys, d = 4, G <= 4): scores
+    // are sums over the 32 positions of LUT[pos][code][head] = q~ . C_k[code]
+    // entries instead of matrix-core products; values as below, from a
+    // 4-copy table (the LUT takes the 128 KiB of the replicated tables)
+    static_assert(!LUT || (KBITS == 8 && SUB == 4 && G <= 4), "LUT scores: 8-bit keys, d = 4, G <= 4");
     constexpr int KROW = kD8 ? 24 : kNumSub * KBITS / 8;
     constexpr int VROW = kD8 ? 24 : kNumSub;
 
@@ -943,6 +962,9 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // appended token (new-token workgroup): transformed key and value (fp64)
     __shared__ double xnew[2][kHeadDim];
     __shared__ uint32_t newc[2][kNumSub];   // its key and value codes
+    // LUT: the value table (4 copies of 256 x 8 B) and q~ in fp32 (base-2 scale)
+    __shared__ __attribute__((aligned(16))) uint8_t vtab4[LUT ? 4 * 256 * 8 : 16];
+    __shared__ __attribute__((aligned(16))) float qf[LUT ? G : 1][LUT ? kHeadDim : 1];
 
     // A 1-D grid, split-major: the workgroups of split s of every stream
     // (sequence, KV head) follow those of split s - 1, and the extra
@@ -999,6 +1021,9 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         (8 * grp + kq) * VROW + (kD8 ? 12 * (aq4 >> 1) + 4 * (aq4 & 1) : 8 * aq4));
     const uint32_t voff1 = voff0 + 4 * VROW;
     const uint32_t ksh = 16u * static_cast<uint32_t>(grp & 1);   // d = 8 only
+    // LUT: lane 16 grp + n scores token 16 (grp / 2) + n (the packed softmax's
+    // token) for heads 2 (grp % 2), + 1 over all 32 positions
+    const uint32_t koffL = static_cast<uint32_t>((16 * (grp >> 1) + n) * KROW);
     const uint32_t vsh = 16u * static_cast<uint32_t>(aq4 & 1);
 
     // ---- prologue ----------------------------------------------------------
@@ -1021,6 +1046,10 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             cent8[i] = k8[tid + i * kThreads];
             cent8[4 + i] = v8[tid + i * kThreads];
         }
+    } else if constexpr (LUT) {
+        // thread: C_k entry tid % 256 (its LUT entries), C_v entry tid % 256
+        kcent[0] = ksrc[tid & 255];
+        centroid = vsrc[tid & 255];
     } else if constexpr (KBITS == 8) {
         // thread: code = tid / 4, table = (tid / 2) % 2, slots 16 (tid % 2) .. + 15
         centroid = ((tid >> 1) & 1) ? vsrc[tid >> 2] : ksrc[tid >> 2];
@@ -1037,7 +1066,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint32_t qw0 = qw[0];
     const uint32_t qw1 = qw[q_f32 ? 1 : 0];
     const float2 lam2 = reinterpret_cast<const float2*>(lambda + g * kHeadDim)[lane];
-    using KC = std::conditional_t<kD8, Chunk8, KChunk<KBITS>>;
+    using KC = std::conditional_t<kD8, Chunk8, std::conditional_t<LUT, LutCodes, KChunk<KBITS>>>;
     using VC = std::conditional_t<kD8, Chunk8, uint2>;
     KC kA[2];
     VC vA[2];
@@ -1045,7 +1074,9 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     // covers the VGPR offset, not the scalar one)
     auto load_k = [&](int rel, KC* kk_) {
         const uint32_t ks = static_cast<uint32_t>(rel * KROW);
-        if constexpr (kD8) {
+        if constexpr (LUT) {
+            kk_[0].load(krsrc, koffL + ks);
+        } else if constexpr (kD8) {
             kk_[0].load(krsrc, koff0 + ks);
             kk_[1].load(krsrc, koff1 + ks);
         } else {
@@ -1080,7 +1111,12 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         // half row hits the same four banks, and the table build took longer
         // than the rest of the prologue.
         const int rot = tid >> 1;
-        if constexpr (kD8) {   // C_k then C_v, 16-byte entries, stored once
+        if constexpr (LUT) {   // the 4-copy value table; the LUT follows q~
+            if (tid < 256) {
+                reinterpret_cast<uint4*>(vtab4)[2 * tid] = cc;
+                reinterpret_cast<uint4*>(vtab4)[2 * tid + 1] = cc;
+            }
+        } else if constexpr (kD8) {   // C_k then C_v, 16-byte entries, stored once
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 reinterpret_cast<uint4*>(tab)[tid + i * kThreads] = cent8[i];
@@ -1128,21 +1164,55 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             x0 *= kScoreScaleLog2;
             x1 *= kScoreScaleLog2;
         }
-        const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-        const int ex = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);
-        x0 = __builtin_amdgcn_ldexpf(x0, ex);
-        x1 = __builtin_amdgcn_ldexpf(x1, ex);
-        if (lane == 0) qsc[wave] = __builtin_amdgcn_ldexpf(1.f, -ex);
-        const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
-        const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
-        const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
-        const int r = 4 * (wave >> 1) + (wave & 1);
-        const int kk = (lane & 15) >> 2, qg = lane >> 4;
-        uint32_t* row = reinterpret_cast<uint32_t*>(&qa[kk][16 * qg + r]) + (lane & 3);
-        row[0] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
-        row[8] = __builtin_bit_cast(uint32_t, half2_t{l0, l1});   // row r + 2
+        if constexpr (LUT) {   // q~ in fp32 for the LUT build; scores come unscaled
+            if (wave < G) {
+                qf[wave][2 * lane] = x0;
+                qf[wave][2 * lane + 1] = x1;
+            }
+            if (lane == 0) qsc[wave] = 1.f;
+        } else {
+            const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+            const int ex = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);
+            x0 = __builtin_amdgcn_ldexpf(x0, ex);
+            x1 = __builtin_amdgcn_ldexpf(x1, ex);
+            if (lane == 0) qsc[wave] = __builtin_amdgcn_ldexpf(1.f, -ex);
+            const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+            const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
+            const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
+            const int r = 4 * (wave >> 1) + (wave & 1);
+            const int kk = (lane & 15) >> 2, qg = lane >> 4;
+            uint32_t* row = reinterpret_cast<uint32_t*>(&qa[kk][16 * qg + r]) + (lane & 3);
+            row[0] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
+            row[8] = __builtin_bit_cast(uint32_t, half2_t{l0, l1});   // row r + 2
+        }
     }
     __syncthreads();
+    if constexpr (LUT) {
+        // The lookup table (VecInfer page, Appendix, Algorithm 1: the table of
+        // the query against C_k, then scores as sums of its entries):
+        // LUT[pos][code] holds q~_h[4 pos .. 4 pos + 3] . C_k[code] for heads
+        // h = 0 .. 3 (zero for h >= G), base-2 score units, 16 bytes per entry.
+        // Thread: code tid % 256, positions tid / 256 + 4 k.
+        const uint2 c = kcent[0];
+        const float c0 = lo_half_to_float(c.x), c1 = hi_half_to_float(c.x);
+        const float c2 = lo_half_to_float(c.y), c3 = hi_half_to_float(c.y);
+        const int code = tid & 255;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int pos = (tid >> 8) + 4 * k;
+            float e[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                e[h] = 0.f;
+                if (h < G) {
+                    const float4_t qv = *reinterpret_cast<const float4_t*>(&qf[h][4 * pos]);
+                    e[h] = fmaf(qv[3], c3, fmaf(qv[2], c2, fmaf(qv[1], c1, qv[0] * c0)));
+                }
+            }
+            reinterpret_cast<float4_t*>(tab)[pos * 256 + code] = float4_t{e[0], e[1], e[2], e[3]};
+        }
+        __syncthreads();
+    }
 
     // MFMA rows of lane 16 grp + n: 4 grp .. 4 grp + 3 = (hA hi, hB hi, hA lo, hB lo)
     const int hA = 2 * grp, hB = 2 * grp + 1;
@@ -1181,11 +1251,29 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
     const uint32_t pread1 = 8u * (4 * (8 * grp + 4 * (orr ^ 1) + kq) + (aq4 ^ (2 * orr)));  // tokens 8 grp + 4 + kq
     const uint32_t kslot = static_cast<uint32_t>(lane & 31) * 8;               // key table
     const uint32_t vslot = 0x10000u | (static_cast<uint32_t>(lane & 31) * 8);  // value table
+    const uint32_t vcopy = static_cast<uint32_t>(lane & 3) * 8;                // LUT: value copy
 
     auto compute_tile = [&](int rel_, KC* kc, VC* vc, int nrel) {
         // ---- scores: 2 blocks of 16 tokens, 4 K-steps of 32 dims ------------
         float4_t sacc[2];
-        if constexpr (kD8) {
+        float lutA = 0.f, lutB = 0.f;   // LUT: the lane's scores of heads sh, sh + 1
+        if constexpr (LUT) {
+            // one 8-byte read per position: the lane's head pair of entry
+            // (pos, code), summed in position order
+            const uint8_t* lrow = tab + 8 * (grp & 1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t w = kc[0].w[i];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t code = (w >> (8 * k)) & 0xffu;
+                    const float2 e = *reinterpret_cast<const float2*>(lrow + (4 * i + k) * 4096 +
+                                                                      code * 16);
+                    lutA += e.x;
+                    lutB += e.y;
+                }
+            }
+        } else if constexpr (kD8) {
             // K-step kk of lane (16 grp + n): dims 32 grp + 8 kk .. + 7 of its
             // token = the centroid of code kk of its chunk, one 16-byte gather
 #pragma unroll
@@ -1237,7 +1325,10 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
         // softmax runs once per tile: lane 16 grp + n then holds token
         // 16 (grp / 2) + n of heads 2 (grp % 2) and 2 (grp % 2) + 1.
         float sA[kSb], sB[kSb];
-        if constexpr (kPack) {
+        if constexpr (LUT) {
+            sA[0] = lutA;
+            sB[0] = lutB;
+        } else if constexpr (kPack) {
             sA[0] = lo_halves(sacc[0][0] + sacc[0][2], sacc[1][0] + sacc[1][2]);
             sB[0] = lo_halves(sacc[0][1] + sacc[0][3], sacc[1][1] + sacc[1][3]);
         } else {
@@ -1340,7 +1431,13 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             const uint32_t w0 = (q4 < 2) ? vc[0].x : vc[0].y;
             const uint32_t w1 = (q4 < 2) ? vc[1].x : vc[1].y;
             half4_t x[2][2];
-            if ((q4 & 1) == 0) {
+            if constexpr (LUT) {   // the 4-copy table: 32-byte rows, copy lane % 4
+                const int b0 = (q4 & 1) ? 2 : 0;
+                x[0][0] = read_tr16(vtab4 + ((((w0 >> (8 * b0)) & 0xffu) << 5) | vcopy));
+                x[0][1] = read_tr16(vtab4 + ((((w1 >> (8 * b0)) & 0xffu) << 5) | vcopy));
+                x[1][0] = read_tr16(vtab4 + ((((w0 >> (8 * b0 + 8)) & 0xffu) << 5) | vcopy));
+                x[1][1] = read_tr16(vtab4 + ((((w1 >> (8 * b0 + 8)) & 0xffu) << 5) | vcopy));
+            } else if ((q4 & 1) == 0) {
                 x[0][0] = read_tr16(tab + row_addr<0>(w0, vslot));
                 x[0][1] = read_tr16(tab + row_addr<0>(w1, vslot));
                 x[1][0] = read_tr16(tab + row_addr<1>(w0, vslot));
@@ -1457,7 +1554,7 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
 
 namespace {
 
-template <int KBITS, int SUB>
+template <int KBITS, int SUB, bool LUT>
 hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q, bool q_f32,
                          const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
                          const uint8_t* codes_k, const uint8_t* codes_v, Partials part,
@@ -1473,13 +1570,14 @@ hipError_t launch_mfma_g(int group, dim3 grid, const AttnShape& s, const void* q
     if (fold && s.num_splits < 1) return hipErrorInvalidValue;
 #define VQKV_LAUNCH(GG)                                                                       \
     case GG:                                                                                  \
-        hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS, SUB>), full, dim3(kThreads), 0, \
-                           stream, q, q_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,   \
-                           s.num_q_heads, s.num_kv_heads, s.capacity, s.context_len,          \
-                           s.num_splits, s.tokens_per_split, part, ap.k_new, ap.v_new,        \
-                           ap.kv_f32 ? 1 : 0, pos, ap.codes_k, ap.codes_v, stride,           \
-                           ap.win_k, ap.win_v, ap.win_len, ap.win_cap, fold ? 1 : 0,         \
-                           deterministic() ? 1 : 0);                                         \
+        if constexpr (!LUT || GG <= 4)                                                        \
+            hipLaunchKernelGGL((vq_attention_mfma_kernel<GG, KBITS, SUB, LUT && GG <= 4>),    \
+                               full, dim3(kThreads), 0, stream, q, q_f32 ? 1 : 0, lambda,     \
+                               cb_k, cb_v, codes_k, codes_v, s.num_q_heads, s.num_kv_heads,   \
+                               s.capacity, s.context_len, s.num_splits, s.tokens_per_split,   \
+                               part, ap.k_new, ap.v_new, ap.kv_f32 ? 1 : 0, pos, ap.codes_k,  \
+                               ap.codes_v, stride, ap.win_k, ap.win_v, ap.win_len, ap.win_cap, \
+                               fold ? 1 : 0, deterministic() ? 1 : 0);                        \
         break;
     switch (group) {
         VQKV_LAUNCH(1)
@@ -1507,12 +1605,17 @@ hipError_t launch_vq_attention(const AttnShape& s, int k_bits, int sub_dim, cons
     const dim3 grid(s.num_splits, s.num_kv_heads, s.batch);
     const int group = s.num_q_heads / s.num_kv_heads;
     if (sub_dim == 8)
-        return launch_mfma_g<12, 8>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
-                                    codes_v, part, append, stream);
-    return (k_bits == 8) ? launch_mfma_g<8, 4>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
-                                               codes_k, codes_v, part, append, stream)
-                         : launch_mfma_g<12, 4>(group, grid, s, q, q_f32, lambda, cb_k, cb_v,
-                                                codes_k, codes_v, part, append, stream);
+        return launch_mfma_g<12, 8, false>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
+                                           codes_v, part, append, stream);
+    if (k_bits == 12)
+        return launch_mfma_g<12, 4, false>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
+                                           codes_v, part, append, stream);
+    // the lookup-table score path where selected (8-bit keys, G <= 4)
+    if (score_method() == kScoresLut && group <= 4)
+        return launch_mfma_g<8, 4, true>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
+                                         codes_v, part, append, stream);
+    return launch_mfma_g<8, 4, false>(group, grid, s, q, q_f32, lambda, cb_k, cb_v, codes_k,
+                                      codes_v, part, append, stream);
 }
 
 }  // namespace vqkv

@@ -19,6 +19,13 @@ std::atomic<bool> g_deterministic{false};
 bool deterministic() { return g_deterministic.load(std::memory_order_relaxed); }
 bool set_deterministic(bool on) { return g_deterministic.exchange(on); }
 
+namespace {
+std::atomic<int> g_score_method{kScoresMfma};
+}
+
+int score_method() { return g_score_method.load(std::memory_order_relaxed); }
+int set_score_method(int method) { return g_score_method.exchange(method); }
+
 }  // namespace vqkv
 
 namespace {
@@ -188,6 +195,14 @@ const char* vq_status_string(int status) {
 const char* vq_last_error(void) { return g_last_error; }
 
 int vq_set_deterministic(int on) { return vqkv::set_deterministic(on != 0) ? 1 : 0; }
+
+int vq_set_score_method(int method) {
+    if (method != VQ_SCORES_MFMA && method != VQ_SCORES_LUT) {
+        fail(VQ_ERR_INVALID_ARG, "score method %d is not VQ_SCORES_MFMA or VQ_SCORES_LUT", method);
+        return -1;
+    }
+    return vqkv::set_score_method(method);
+}
 
 
 int vq_transform_query(const vq_layout* layout, const void* q, int q_dtype, const float* lambda,
