@@ -1117,10 +1117,17 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
                 reinterpret_cast<uint4*>(vtab4)[2 * tid + 1] = cc;
             }
         } else if constexpr (kD8) {   // C_k then C_v, 16-byte entries, stored once
+            // The value table is read 8 bytes (half an entry) at a time: an
+            // entry whose code has bit 4 set keeps its halves swapped, so the
+            // reads of one half over random codes spread over all 32 bank
+            // pairs instead of 16 (entry tid + 1024 i has bit 4 of tid).
+            const bool swap_halves = (tid & 16) != 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 reinterpret_cast<uint4*>(tab)[tid + i * kThreads] = cent8[i];
-                reinterpret_cast<uint4*>(tab + kTable)[tid + i * kThreads] = cent8[4 + i];
+                const uint4 v = cent8[4 + i];
+                reinterpret_cast<uint4*>(tab + kTable)[tid + i * kThreads] =
+                    swap_halves ? make_uint4(v.z, v.w, v.x, v.y) : v;
             }
         } else if constexpr (KBITS == 8) {
             uint4* dst = reinterpret_cast<uint4*>(tab + ((tid >> 1) & 1) * kTable +
@@ -1408,17 +1415,20 @@ __global__ __launch_bounds__(kThreads, 1) void vq_attention_mfma_kernel(
             // channel 32 a + 4 c + e is element 4 (c % 2) + e of the centroid
             // of code c / 2 of the chunk (positions 4 a ..): the fetching lane
             // points the transposing read at that half of the 16-byte entry
+            // (halves swapped where bit 4 of the code is set: bit 3 of the
+            // address flips)
             uint32_t c0[4], c1[4];
             vc[0].codes(vsh, c0);
             vc[1].codes(vsh, c1);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const uint32_t a0 = kTable + (c0[q4] << 4), a1 = kTable + (c1[q4] << 4);
+                const uint32_t f0 = (c0[q4] >> 1) & 8u, f1 = (c1[q4] >> 1) & 8u;
                 half4_t x[2][2];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    x[i][0] = read_tr16(tab + a0 + 8 * i);
-                    x[i][1] = read_tr16(tab + a1 + 8 * i);
+                    x[i][0] = read_tr16(tab + ((a0 + 8 * i) ^ f0));
+                    x[i][1] = read_tr16(tab + ((a1 + 8 * i) ^ f1));
                 }
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
