@@ -8,14 +8,14 @@
 //
 // The decision is the one the fp64 reference takes (squared distances in
 // fp64 with every difference, product and sum rounded separately, exact ties
-// to the lowest index), found by the certified matrix-core search of
-// nearest_search.hpp with the transformed keys and the values rounded to fp32
-// for the scores and kept in fp64 for the few exact distances.
+// to the lowest index), found by the certified fp16 hi/lo matrix-core search
+// of nearest_search.hpp, with the transformed keys and the values kept in
+// fp64 for the few exact distances.
 //
 // One 512-thread workgroup encodes up to 8 tokens of one (sequence, KV
 // head): 256 key and 256 value sub-vectors, 16 row blocks each, spread over
-// the 8 waves.  Codebooks (-2c by channel, fp32) and their bound-scaled
-// squared norms are staged in LDS.
+// the 8 waves.  The codebooks (fp16, as stored) and their squared norms are
+// staged in LDS.
 #include "launchers.hpp"
 #include "nearest_search.hpp"
 
@@ -41,33 +41,43 @@ __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
 }
 
 // The nearest centroid of sub-vector rb*16 + lane % 16 of `xs` ([8 tokens]
-// [128] fp64 = [256 sub-vectors][4]) among NENT fp16 centroids staged as -2c
-// by channel (m2) and bound-scaled squared norms (cu, cd).
+// [128] fp64 = [256 sub-vectors][4]) among NENT fp16 centroids c16 (the
+// codebook as stored), with the norm terms of hilo_norm_terms at scale sc in
+// nt (float2 [NENT]: upper, lower): fp16 hi/lo matrix-core scores,
+// certified (nearest_search.hpp), fp64 distances for the few candidates.
 template <int NENT>
-__device__ __forceinline__ uint32_t search_rows(const float* m2, const float* cu,
-                                                const float* cd, const double (*xs)[kHeadDim],
-                                                int rb, int lane) {
+__device__ __forceinline__ uint32_t search_rows(const uint2* c16, const float* cu, const float* cd,
+                                                float sc, const double (*xs)[kHeadDim], int rb,
+                                                int lane) {
     const double* x = &xs[0][0] + (rb * 16 + (lane & 15)) * 4;
-    const float b = static_cast<float>(x[lane >> 4]);   // B operand: channel lane / 16
+    double xd[4];
     float xx = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+        xd[j] = x[j];
         const float v = static_cast<float>(x[j]);
         xx += v * v;
     }
-    // the fp16 centroid, recovered exactly from -2c; the distance rounded as
-    // the fp64 reference rounds it
-    const auto exact = [&](uint32_t nc) {
-        double dd = 0.0;
+    const BlockD4H block(reinterpret_cast<const uint16_t*>(c16), hilo_rows<4, h4_t>(xd, lane, sc),
+                         lane);
+    // the distance rounded as the fp64 reference rounds it
+    const auto exact = [&](uint32_t nc) { return sqdist4_f64(xd, c16[nc]); };
+    return nearest16_core<NENT, 4>(cu, cd, block, row_bound_h(xx) * sc, lane, exact);
+}
+
+// The largest |2x| over the n values of xs, reduced over the workgroup
+// (red: kThr / 64 floats of LDS); every thread gets it.
+template <int kThr>
+__device__ __forceinline__ float block_absmax2(const double* xs, int n, float* red, int tid) {
+    float m = 0.f;
+    for (int i = tid; i < n; i += kThr) m = fmaxf(m, fabsf(-2.f * static_cast<float>(xs[i])));
+    m = wave_max(m);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
+    __syncthreads();
+    float r = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const double c = -0.5 * static_cast<double>(m2[j * kSearchStride<NENT> + nc]);
-            const double e = __dadd_rn(x[j], -c);
-            dd = j == 0 ? __dmul_rn(e, e) : __dadd_rn(dd, __dmul_rn(e, e));
-        }
-        return dd;
-    };
-    return nearest16<NENT>(m2, cu, cd, b, row_bound(xx), lane, exact);
+    for (int w = 0; w < kThr / kWave; ++w) r = fmaxf(r, red[w]);
+    return r;
 }
 
 }  // namespace
@@ -81,14 +91,15 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     constexpr int KENT = 1 << KBITS;
     constexpr int KROW = kNumSub * KBITS / 8;
     constexpr int kThr = kEncThreadsOf<KBITS>, kWv = kThr / kWave;
-    // -2c by channel ([4][E], exact in fp32) and ||c||^2, per tensor
-    __shared__ float km2[4 * kSearchStride<KENT>];
-    __shared__ float vm2[4 * kSearchStride<256>];
-    // ||c||^2 (1 + 2^-16), ||c||^2 (1 - 2^-16), read as float4
+    // the codebooks as stored (fp16) and their norm terms at this
+    // workgroup's scale (hilo_norm_terms), per tensor
+    __shared__ __align__(16) uint2 kc16[KENT];
+    __shared__ __align__(16) uint2 vc16[256];
     __shared__ __align__(16) float kcu[KENT];
     __shared__ __align__(16) float kcd[KENT];
     __shared__ __align__(16) float vcu[256];
     __shared__ __align__(16) float vcd[256];
+    __shared__ float red[2][kThr / kWave];
     __shared__ double xs[2][kEncTok][kHeadDim];       // transformed keys, values (fp64)
     __shared__ uint16_t code[2][kEncTok][kNumSub];
 
@@ -97,7 +108,6 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const bool f32 = kv_f32 != 0;
 
-    // codebooks (-2c by channel) and squared norms
     const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
     const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
     // every load is issued before any is used (one latency, not one per entry)
@@ -106,29 +116,6 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
 #pragma unroll
     for (int j = 0; j < KPER; ++j) kc[j] = ksrc[min(tid + j * kThr, KENT - 1)];
     const uint2 vc = vsrc[tid & 255];
-#pragma unroll
-    for (int j = 0; j < KPER; ++j) {
-        const int i = tid + j * kThr;
-        if (i < KENT) {
-            km2[0 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x & 0xffffu);
-            km2[1 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].x >> 16);
-            km2[2 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].y & 0xffffu);
-            km2[3 * kSearchStride<KENT> + i] = -2.f * half_bits_to_float(kc[j].y >> 16);
-            const float nn = norm2(kc[j]);
-            kcu[i] = nn * kBoundUp;
-            kcd[i] = nn * kBoundDown;
-        }
-    }
-    if (tid < 256) {
-        vm2[0 * kSearchStride<256> + tid] = -2.f * half_bits_to_float(vc.x & 0xffffu);
-        vm2[1 * kSearchStride<256> + tid] = -2.f * half_bits_to_float(vc.x >> 16);
-        vm2[2 * kSearchStride<256> + tid] = -2.f * half_bits_to_float(vc.y & 0xffffu);
-        vm2[3 * kSearchStride<256> + tid] = -2.f * half_bits_to_float(vc.y >> 16);
-        const float nn = norm2(vc);
-        vcu[tid] = nn * kBoundUp;
-        vcd[tid] = nn * kBoundDown;
-    }
-
     // k / lambda in fp64, the +-1 Walsh–Hadamard transform, then 1/sqrt(128);
     // values as they are.  Rows of tokens past num_new are zero.
     const float* lam = lambda + g * kHeadDim;
@@ -148,13 +135,33 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
             live ? load_elem(v_new, f32, in_row * kHeadDim + 2 * lane + 1) : 0.0;
     }
     __syncthreads();
+    // one scale per tensor for the workgroup's hi/lo rows, and the tables
+    const float ksc = hilo_scale(block_absmax2<kThr>(&xs[0][0][0], kEncTok * kHeadDim, red[0], tid));
+    const float vsc = hilo_scale(block_absmax2<kThr>(&xs[1][0][0], kEncTok * kHeadDim, red[1], tid));
+#pragma unroll
+    for (int j = 0; j < KPER; ++j) {
+        const int i = tid + j * kThr;
+        if (i < KENT) {
+            kc16[i] = kc[j];
+            const float2 t = hilo_norm_terms(norm2(kc[j]), l1_4(kc[j]), ksc);
+            kcu[i] = t.x;
+            kcd[i] = t.y;
+        }
+    }
+    if (tid < 256) {
+        vc16[tid] = vc;
+        const float2 t = hilo_norm_terms(norm2(vc), l1_4(vc), vsc);
+        vcu[tid] = t.x;
+        vcd[tid] = t.y;
+    }
+    __syncthreads();
 
     // row block jobs: keys then values; sub-vector r = 32 token + position
     for (int job = wave; job < 2 * kEncBlocks; job += kWv) {
         const int tt = job / kEncBlocks, rb = job % kEncBlocks;
         if (rb * 16 >= ntok * kNumSub) continue;   // whole block past the last token
-        const uint32_t cd = tt == 0 ? search_rows<KENT>(km2, kcu, kcd, xs[0], rb, lane)
-                                    : search_rows<256>(vm2, vcu, vcd, xs[1], rb, lane);
+        const uint32_t cd = tt == 0 ? search_rows<KENT>(kc16, kcu, kcd, ksc, xs[0], rb, lane)
+                                    : search_rows<256>(vc16, vcu, vcd, vsc, xs[1], rb, lane);
         const int r = rb * 16 + lane;
         if (lane < 16) code[tt][r >> 5][r & 31] = static_cast<uint16_t>(cd);
     }
@@ -183,9 +190,9 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
 
 // The d = 8 layout (16 sub-vectors of 8 channels, C_k and C_v of 4096
 // entries, 24-byte rows of 12-bit codes): 16 tokens per workgroup, one per wave,
-// searched with nearest16_d8 against the fp16 codebook in LDS.  A 4096 x 8
-// table with its two norm tables takes 96 KiB, so keys and values are
-// searched one after the other with the same LDS.
+// searched with fp16 hi/lo scores against the fp16 codebook in LDS.  A 4096 x 8
+// table with its norm table takes 80 KiB, so keys and values are searched
+// one after the other with the same LDS.
 constexpr int kEnc8Ent = 4096;
 constexpr int kEnc8Pos = kHeadDim / 8;           // 16 sub-vectors per vector
 constexpr int kEnc8Row = kEnc8Pos * 12 / 8;      // 24 bytes per code row
@@ -201,8 +208,10 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
     const uint16_t* __restrict__ cb_v, uint8_t* __restrict__ codes_k,
     uint8_t* __restrict__ codes_v, int num_kv_heads, int capacity, int cur_len, int num_new) {
     __shared__ __align__(16) uint16_t ctab[kEnc8Ent * 8];   // one codebook, fp16 as stored
-    __shared__ __align__(16) float cu[kEnc8Ent];            // ||c||^2 (1 + 2^-16)
-    __shared__ __align__(16) float cd[kEnc8Ent];            // ||c||^2 (1 - 2^-16)
+    // its norm terms at the workgroup's scale for the tensor (hilo_norm_terms)
+    __shared__ __align__(16) float cu[kEnc8Ent];
+    __shared__ __align__(16) float cd[kEnc8Ent];
+    __shared__ float red[2][kEnc8Waves];
     __shared__ double xs[2][kEnc8Tok][kHeadDim];             // transformed keys, values (fp64)
     __shared__ uint16_t code[2][kEnc8Tok][kEnc8Pos];
 
@@ -230,6 +239,12 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
             live ? load_elem(v_new, f32, in_row * kHeadDim + 2 * lane + 1) : 0.0;
     }
 
+    __syncthreads();
+    // one scale per tensor for the workgroup's hi/lo rows
+    float scale[2];
+    for (int tt = 0; tt < 2; ++tt)
+        scale[tt] = hilo_scale(block_absmax2<kEnc8Threads>(&xs[tt][0][0], kEnc8Tok * kHeadDim,
+                                                           red[tt], tid));
     for (int tt = 0; tt < 2; ++tt) {
         if (tt == 1) __syncthreads();   // every search of the key table is done
         const uint4* src = reinterpret_cast<const uint4*>(tt == 0 ? cb_k : cb_v) +
@@ -238,16 +253,18 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
             const uint4 c = src[i];
             reinterpret_cast<uint4*>(ctab)[i] = c;
             const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-            float nn = 0.f;   // the squares of fp16 values are exact in fp32
+            float nn = 0.f, l1 = 0.f;   // the squares of fp16 values are exact in fp32
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float lo = half_bits_to_float(static_cast<uint16_t>(w[j] & 0xffffu));
                 const float hi = half_bits_to_float(static_cast<uint16_t>(w[j] >> 16));
                 nn += lo * lo;
                 nn += hi * hi;
+                l1 += fabsf(lo) + fabsf(hi);
             }
-            cu[i] = nn * kBoundUp;
-            cd[i] = nn * kBoundDown;
+            const float2 t = hilo_norm_terms(nn, l1, scale[tt]);
+            cu[i] = t.x;
+            cd[i] = t.y;
         }
         __syncthreads();
         // wave w: the 16 sub-vectors of token w (position lane % 16)
@@ -255,9 +272,6 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
         static_assert(kEnc8Waves == kEnc8Tok && kEnc8Pos == 16, "one token per wave");
         if (tok < ntok) {   // uniform
             const double* x = &xs[tt][tok][8 * pos];
-            const int gq = lane >> 4;
-            const float b0 = -2.f * static_cast<float>(x[2 * gq]);
-            const float b1 = -2.f * static_cast<float>(x[2 * gq + 1]);
             float xx = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -270,8 +284,11 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
             const auto exact = [&](uint32_t nc) {
                 return sqdist8_f64(xd, reinterpret_cast<const uint4*>(ctab)[nc]);
             };
-            const uint32_t c = nearest16_d8<kEnc8Ent>(ctab, cu, cd, b0, b1, row_bound(xx), lane,
-                                                      exact);
+            // fp16 hi/lo matrix-core scores in units of the workgroup's 2^s
+            const float sc = scale[tt];
+            const uint32_t c = nearest16_core<kEnc8Ent, 8>(
+                cu, cd, BlockD8H(ctab, hilo_rows<8, h8_t>(xd, lane, sc), lane),
+                row_bound_h(xx) * sc, lane, exact);
             if (lane < 16) code[tt][tok][pos] = static_cast<uint16_t>(c);
         }
     }

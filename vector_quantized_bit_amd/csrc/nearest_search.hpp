@@ -1,5 +1,6 @@
-// Certified nearest-centroid search for 16 sub-vectors of dimension 4 on the
-// matrix cores, shared by the encoder and by K-Means.
+// Certified nearest-centroid search for 16 sub-vectors of dimension 4 or 8
+// on the matrix cores, shared by the encoders, the decode step's new token
+// and K-Means.
 //
 // VecInfer page, Background (VQ principle): each sub-vector x gets
 // j* = argmin_j ||x - C_j||^2.  The decision taken is the fp64 one: squared
@@ -66,13 +67,11 @@ __device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * 
 // inputs never produce).  Every lane of the wave must be active; all
 // branches below are uniform.
 //
-// SUB = 8 (nearest16_d8 below): the centroids stay fp16 in LDS as the
-// codebook stores them, c [NENT][8], and are widened to fp32 for the A
-// operand; the sub-vector enters as -2x (exact scaling).  Two K = 4 steps
-// per 16 centroids, channels 2 g and 2 g + 1 of lane group g = lane / 16 (one
-// 32-bit LDS read per lane gives both), accumulate ||c||^2 (1 +- 2^-16) -
-// 2 x.c.  With 8 products the score error is within about 16 u (||x||^2 +
-// ||c||^2), so the same bound keeps a 16x margin.
+// The encoders and the one-token searches of the decode step use the fp16
+// hi/lo form below (BlockD4H, BlockD8H): the centroids enter the matrix
+// cores as the codebook stores them (fp16) and the sub-vector as a scaled
+// hi/lo fp16 pair, with their own certified bound (2^-15).  The fp32 form
+// above remains in K-Means (BlockF32D8 for 8-dim samples).
 // The passes over centroid blocks [b0, b1) (16 centroids each; b1 - b0 a
 // multiple of 8).  block(blk, c) is the MFMA score of block blk with
 // accumulator input c; cup(blk) / cdown(blk) give the lane's 4 norm terms
@@ -262,21 +261,117 @@ struct BlockF32D8 {
     }
 };
 
-// The MFMA score of one block of 16 centroids for the d = 8 layout: ctab
-// [.][8] fp16 centroids, b0, b1 = -2x of channels 2 (lane / 16) and
-// 2 (lane / 16) + 1 of sub-vector lane % 16.
-struct BlockD8 {
-    const uint32_t* acol;
-    float b0, b1;
-    __device__ BlockD8(const uint16_t* ctab, float b0_, float b1_, int lane)
-        : acol(reinterpret_cast<const uint32_t*>(ctab) + (lane & 15) * 4 + (lane >> 4)),
-          b0(b0_), b1(b1_) {}
+// fp16 hi/lo scores (d = 8 first): one v_mfma_f32_16x16x32_f16 per block of 16
+// centroids.  The A operand is the fp16 centroid as the codebook stores it
+// (lanes 0-15 and 16-31 read the same 16-byte entry, K = 0-7 and 8-15;
+// K = 16-31 meet zeros in B).  The B operand of sub-vector l % 16 holds
+// X = fl32(-2x) 2^s split into hi = fl16(X) (lane group 0) and
+// lo = fl16(X - hi) (group 1), with 2^s putting max |X| in [2^14, 2^15):
+// the products are exact in fp32 and X - (hi + lo) is within
+// 2^-22 |X| + 2^-25.  The accumulator input is ||c||^2 (1 +- 2^-15) 2^s.
+//   Error, in units of 2^s and u = 2^-24, of the score against the exact
+//   ||c||^2 - 2 x.c: the matrix cores' sum of 16 products and the input
+//   (measured on gfx950: at most 4.2 u of the sum of magnitudes over 65536
+//   adversarial cases; modelled here as 2 u per addition, 66 u), plus the
+//   split of X (5 u of |x.c| terms) and the fp32 norm (8 u ||c||^2): at
+//   most about 140 u ||c||^2 + 70 u ||x||^2 (2 |x||c| <= ||x||^2 + ||c||^2).
+//   The bound E = 2^-15 (||x||^2 + ||c||^2) is 512 u of each: 3.6x the
+//   modelled error, ~60x the measured one.  (The fp32 search above keeps
+//   2^-16.)
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+constexpr float kBoundUpH = 1.0f + 0x1p-15f;
+constexpr float kBoundDownH = 1.0f - 0x1p-15f;
+
+// ex of a row (unscaled), for the hi/lo search
+__device__ __forceinline__ float row_bound_h(float xx) { return 2.f * (0x1p-15f * xx) + 1e-30f; }
+
+// A scale 2^s shared by a workgroup's sub-vectors (mx = the largest |2x|
+// among them): their norm terms can then be scaled once, as the tables are
+// built, instead of once per block in every lane.  A sub-vector far below mx
+// gets a subnormal lo; its split is then within 2^-25 per channel in units
+// of 2^s, so the tables add 2^-24 ||c||_1 to the upper and subtract it from
+// the lower norm term (hilo_norm_terms).
+__device__ __forceinline__ float hilo_scale(float mx) {
+    const int s = mx > 0.f ? min(max(15 - __builtin_amdgcn_frexp_expf(mx), -60), 60) : 0;
+    return __builtin_amdgcn_ldexpf(1.f, s);
+}
+// ||c||^2 (1 +- 2^-15) 2^s +- 2^-24 ||c||_1 (fp32; n = ||c||^2, l1 = ||c||_1)
+__device__ __forceinline__ float2 hilo_norm_terms(float n, float l1, float sc) {
+    return make_float2(fmaf(n, kBoundUpH * sc, 0x1p-24f * l1),
+                       fmaf(n, kBoundDownH * sc, -0x1p-24f * l1));
+}
+// hi / lo rows of X = fl32(-2x) sc for lane group lane / 16 (0: hi, 1: lo,
+// 2 and 3: zeros)
+template <int D, typename H>
+__device__ __forceinline__ H hilo_rows(const double* x, int lane, float sc) {
+    const int g = lane >> 4;
+    H b;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const float X = -2.f * static_cast<float>(x[j]) * sc;
+        const _Float16 hi = static_cast<_Float16>(X);
+        const _Float16 lo = static_cast<_Float16>(X - static_cast<float>(hi));
+        b[j] = g == 0 ? hi : (g == 1 ? lo : static_cast<_Float16>(0.f));
+    }
+    return b;
+}
+// ||c||_1 of a 4- or 8-dim fp16 centroid (the sum rounded; only a bound term)
+__device__ __forceinline__ float l1_4(const uint2 c) {
+    return (fabsf(half_bits_to_float(c.x & 0xffffu)) + fabsf(half_bits_to_float(c.x >> 16))) +
+           (fabsf(half_bits_to_float(c.y & 0xffffu)) + fabsf(half_bits_to_float(c.y >> 16)));
+}
+
+// Per-lane form (one sub-vector's own scale, for the one-token searches): the
+// B operand and the scale 2^s of sub-vector lane % 16, x its D values.
+struct HiLoD8 {
+    h8_t b;
+    float scale;
+};
+__device__ __forceinline__ HiLoD8 hilo_d8(const double* x, int lane) {
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(-2.f * static_cast<float>(x[j])));
+    const float sc = hilo_scale(mx);
+    return {hilo_rows<8, h8_t>(x, lane, sc), sc};
+}
+
+// The same for 4-dim sub-vectors (v_mfma_f32_16x16x16_f16: lane groups 0
+// and 1 carry hi and lo of the 4 channels, groups 2 and 3 zeros).
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+struct HiLoD4 {
+    h4_t b;
+    float scale;
+};
+__device__ __forceinline__ HiLoD4 hilo_d4(const double* x, int lane) {
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(-2.f * static_cast<float>(x[j])));
+    const float sc = hilo_scale(mx);
+    return {hilo_rows<4, h4_t>(x, lane, sc), sc};
+}
+
+// Block scores for 4-dim sub-vectors: ctab [.][4] fp16 centroids (8 bytes
+// each, the codebook's own layout).
+struct BlockD4H {
+    const uint2* arow;
+    h4_t b;
+    __device__ BlockD4H(const uint16_t* ctab, h4_t b_, int lane)
+        : arow(reinterpret_cast<const uint2*>(ctab) + (lane & 15)), b(b_) {}
     __device__ f32x4_t operator()(int blk, f32x4_t c) const {
-        const uint32_t w = acol[blk * 64];   // channels 2 g, 2 g + 1 of centroid 16 blk + lane % 16
-        const float a0 = half_bits_to_float(static_cast<uint16_t>(w & 0xffffu));
-        const float a1 = half_bits_to_float(static_cast<uint16_t>(w >> 16));
-        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c, 0, 0, 0);
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, d, 0, 0, 0);
+        const h4_t a = __builtin_bit_cast(h4_t, arow[blk * 16]);
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// The block score: ctab [.][8] fp16 centroids (16-byte aligned entries).
+struct BlockD8H {
+    const uint4* arow;
+    h8_t b;
+    __device__ BlockD8H(const uint16_t* ctab, h8_t b_, int lane)
+        : arow(reinterpret_cast<const uint4*>(ctab) + (lane & 15)), b(b_) {}
+    __device__ f32x4_t operator()(int blk, f32x4_t c) const {
+        const h8_t a = __builtin_bit_cast(h8_t, arow[blk * 16]);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
 };
 
@@ -292,17 +387,6 @@ __device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
         return __builtin_amdgcn_mfma_f32_16x16x4f32(acol[blk * 16], b, c, 0, 0, 0);
     };
     return nearest16_core<NENT, 4>(ccu, ccd, block, ex, lane, exact);
-}
-
-// d = 8: ctab [NENT][8] fp16 centroids (16 B each, 4-byte aligned); b0, b1
-// are -2x of channels 2 (lane / 16) and 2 (lane / 16) + 1 of sub-vector
-// lane % 16.
-template <int NENT, typename Exact>
-__device__ __forceinline__ uint32_t nearest16_d8(const uint16_t* __restrict__ ctab,
-                                                 const float* __restrict__ ccu,
-                                                 const float* __restrict__ ccd, float b0, float b1,
-                                                 float ex, int lane, Exact exact) {
-    return nearest16_core<NENT, 8>(ccu, ccd, BlockD8(ctab, b0, b1, lane), ex, lane, exact);
 }
 
 }  // namespace vqkv

@@ -265,23 +265,19 @@ __device__ __forceinline__ void new_token_inputs(const void* q, int q_f32, const
 }
 
 // LDS of the new-token workgroup with 12-bit keys (offsets into `tab`):
-// C_k as -2c by channel [4][kSearchStride<4096>] fp32, its bound-scaled
-// squared norms ||c||^2 (1 + 2^-16) and (1 - 2^-16), C_v (fp16), and 4 KiB
-// for the exchanges of the key search.
-constexpr int kNtStride = kSearchStride<4096>;
-constexpr int kNtCu = 4 * kNtStride * 4;
-constexpr int kNtCd = kNtCu + 4096 * 4;
-constexpr int kNtV = kNtCd + 4096 * 4;
+// C_k as stored (fp16, 8 bytes an entry), its squared norms ||c||^2 (fp32),
+// C_v (fp16), and 4 KiB for the exchanges of the key search.
+constexpr int kNtN = 4096 * 8;
+constexpr int kNtV = kNtN + 4096 * 4;
 constexpr int kNtX = kNtV + 256 * 8;
 static_assert(kNtX + 4096 <= 2 * kTable, "the 12-bit new-token tables fit the LDS tables");
 
-// Stage C_k of 4096 entries for new_token_keys12: -2c by channel and the
-// bound-scaled norms (the loads issued before any is used).
+// Stage C_k of 4096 entries for new_token_keys12, with its norms (the loads
+// issued before any is used).
 __device__ __forceinline__ void stage_keys12(const uint2* __restrict__ ksrc, uint8_t* tab,
                                              int tid) {
-    float* m2 = reinterpret_cast<float*>(tab);
-    float* cu = reinterpret_cast<float*>(tab + kNtCu);
-    float* cd = reinterpret_cast<float*>(tab + kNtCd);
+    uint2* k16 = reinterpret_cast<uint2*>(tab);
+    float* nrm = reinterpret_cast<float*>(tab + kNtN);
     constexpr int kPer = 4096 / kThreads;
     uint2 c[kPer];
 #pragma unroll
@@ -289,13 +285,8 @@ __device__ __forceinline__ void stage_keys12(const uint2* __restrict__ ksrc, uin
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int i = tid + j * kThreads;
-        m2[0 * kNtStride + i] = -2.f * half_bits_to_float(c[j].x & 0xffffu);
-        m2[1 * kNtStride + i] = -2.f * half_bits_to_float(c[j].x >> 16);
-        m2[2 * kNtStride + i] = -2.f * half_bits_to_float(c[j].y & 0xffffu);
-        m2[3 * kNtStride + i] = -2.f * half_bits_to_float(c[j].y >> 16);
-        const float nn = norm2(c[j]);
-        cu[i] = nn * kBoundUp;
-        cd[i] = nn * kBoundDown;
+        k16[i] = c[j];
+        nrm[i] = norm2(c[j]);
     }
 }
 
@@ -314,7 +305,7 @@ __device__ __forceinline__ void new_token_keys12(uint8_t* tab, const double* xk,
                                                  int tid, int lane, int wave) {
     constexpr int kEnt = 4096, kCb = 8;   // waves per column block
     static_assert(kThreads == 1024 && kEnt == (kWaves / 2) * 512, "8 waves of 512 centroids");
-    const float* m2 = reinterpret_cast<const float*>(tab);
+    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(tab);
     uint8_t* xbuf = tab + kNtX;
     float* wmin = reinterpret_cast<float*>(xbuf);      // [16 waves][16] pass-1 minima
     int* wcnt = reinterpret_cast<int*>(xbuf + 1024);   // [16][16] candidate counts
@@ -332,25 +323,15 @@ __device__ __forceinline__ void new_token_keys12(uint8_t* tab, const double* xk,
         const float v = static_cast<float>(xd[j]);
         xx += v * v;
     }
-    const float bx = static_cast<float>(xk[4 * sv + (lane >> 4)]);   // B: channel lane / 16
-    const float* acol = m2 + (lane >> 4) * kNtStride + (lane & 15);
-    const auto block = [&](int blk, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(acol[blk * 16], bx, c, 0, 0, 0);
-    };
-    const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(tab + kNtCu) + lane / 16;
-    const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(tab + kNtCd) + lane / 16;
-    const auto cup = [&](int blk) { return ucol[blk * 4]; };
-    const auto cdown = [&](int blk) { return dcol[blk * 4]; };
-    // the fp16 centroid, recovered exactly from -2c
+    // fp16 hi/lo matrix-core scores in units of 2^s (the lane's column)
+    const HiLoD4 hl = hilo_d4(xd, lane);
+    const BlockD4H block(k16, hl.b, lane);
+    const f32x4_t* ncol = reinterpret_cast<const f32x4_t*>(tab + kNtN) + lane / 16;
+    const float up = kBoundUpH * hl.scale, down = kBoundDownH * hl.scale;   // exact
+    const auto cup = [&](int blk) { return ncol[blk * 4] * up; };
+    const auto cdown = [&](int blk) { return ncol[blk * 4] * down; };
     const auto exact = [&](uint32_t nc) {
-        double dd = 0.0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const double c = -0.5 * static_cast<double>(m2[j * kNtStride + nc]);
-            const double e = __dadd_rn(xd[j], -c);
-            dd = j == 0 ? __dmul_rn(e, e) : __dadd_rn(dd, __dmul_rn(e, e));
-        }
-        return dd;
+        return sqdist4_f64(xd, reinterpret_cast<const uint2*>(k16)[nc]);
     };
     const int b0 = 32 * (wave % kCb), b1 = b0 + 32;   // this wave's centroid blocks
     float smin = search_pass1(block, cup, b0, b1);
@@ -360,7 +341,7 @@ __device__ __forceinline__ void new_token_keys12(uint8_t* tab, const double* xk,
     __syncthreads();
     float gmin = wmin[cb * kCb * 16 + (lane & 15)];
     for (int w = 1; w < kCb; ++w) gmin = fminf(gmin, wmin[(cb * kCb + w) * 16 + (lane & 15)]);
-    const float thr = gmin + row_bound(xx);
+    const float thr = gmin + row_bound_h(xx) * hl.scale;
     int cnt, cand;
     search_pass2<true>(block, cdown, b0, b1, thr, cnt, cand);   // sparse hits: 1 in 4096
     cnt = sum_lanes16_32(cnt, lane);
@@ -532,17 +513,11 @@ __device__ __forceinline__ void new_token_workgroup(
     //    components 2 (l % 2), + 1 of sub-vector l / 2
     if (wave < G) {
         const int j = lane >> 1, comp = 2 * (lane & 1);
-        float k0, k1;
-        if constexpr (KBITS == 12) {   // exact: -2c holds the fp16 value times -2
-            const float* m2 = reinterpret_cast<const float*>(tab);
-            k0 = -0.5f * m2[comp * kNtStride + newc[0][j]];
-            k1 = -0.5f * m2[(comp + 1) * kNtStride + newc[0][j]];
-        } else {
-            const uint2 kc = reinterpret_cast<const uint2*>(tab)[newc[0][j]];
-            const uint32_t kw = comp ? kc.y : kc.x;
-            k0 = half_bits_to_float(kw & 0xffffu);
-            k1 = half_bits_to_float(kw >> 16);
-        }
+        // (C_k sits at the start of tab as stored, for 8- and 12-bit keys)
+        const uint2 kc = reinterpret_cast<const uint2*>(tab)[newc[0][j]];
+        const uint32_t kw = comp ? kc.y : kc.x;
+        const float k0 = half_bits_to_float(kw & 0xffffu);
+        const float k1 = half_bits_to_float(kw >> 16);
         const uint2 vc = reinterpret_cast<const uint2*>(tab + kVtab)[newc[1][j]];
         const uint32_t vw = comp ? vc.y : vc.x;
         const float x = wave_sum(x0 * k0 + x1 * k1);
@@ -625,12 +600,13 @@ __device__ __forceinline__ void new_token_workgroup8(
             const float v = static_cast<float>(xd[j]);
             xx += v * v;
         }
-        const int gq = lane >> 4;
-        const BlockD8 block(table, -2.f * static_cast<float>(xd[2 * gq]),
-                            -2.f * static_cast<float>(xd[2 * gq + 1]), lane);
+        // fp16 hi/lo matrix-core scores in units of 2^s (the lane's column)
+        const HiLoD8 hl = hilo_d8(xd, lane);
+        const BlockD8H block(table, hl.b, lane);
         const f32x4_t* ncol = reinterpret_cast<const f32x4_t*>(nrm + q4);
-        const auto cup = [&](int blk) { return ncol[blk * 4] * kBoundUp; };
-        const auto cdown = [&](int blk) { return ncol[blk * 4] * kBoundDown; };
+        const float up = kBoundUpH * hl.scale, down = kBoundDownH * hl.scale;   // exact
+        const auto cup = [&](int blk) { return ncol[blk * 4] * up; };
+        const auto cdown = [&](int blk) { return ncol[blk * 4] * down; };
         const auto exact = [&](uint32_t nc) {
             return sqdist8_f64(xd, reinterpret_cast<const uint4*>(table)[nc]);
         };
@@ -641,7 +617,7 @@ __device__ __forceinline__ void new_token_workgroup8(
         __syncthreads();
         float gmin = wmin[pos];
         for (int w = 1; w < kWaves; ++w) gmin = fminf(gmin, wmin[w * kPos + pos]);
-        const float thr = gmin + row_bound(xx);
+        const float thr = gmin + row_bound_h(xx) * hl.scale;
         int cnt, cand;
         search_pass2<true>(block, cdown, b0, b1, thr, cnt, cand);   // sparse hits: 1 in 4096
         cnt = sum_lanes16_32(cnt, lane);
