@@ -75,7 +75,7 @@ def _find(directory: str, suffix: str) -> str:
 def short_name(name: str) -> str:
     """Kernel name without the argument list and the namespace of torch's
     templated elementwise kernels."""
-    base = name.split("(")[0].strip()
+    base = name.replace("(anonymous namespace)::", "").split("(")[0].strip()
     if base.startswith("void "):
         base = base[5:]
     if "at::native" in base or "at::cuda" in base:
@@ -138,6 +138,19 @@ def cmd_trace(a) -> None:
             "durations; the gap is the idle time between the previous kernel's end and "
             "the split kernel's start):", ""]
     out += loop_table(kernel_loops(trace))
+    for sub in a.breakdown or []:
+        out += ["", f"Launches of kernels matching `{sub}` by grid size (workgroups):", "",
+                "| kernel | grid | launches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+        groups: dict = collections.defaultdict(list)
+        for r in trace:
+            if sub in r["Kernel_Name"]:
+                grid = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+                        int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+                groups[(short_name(r["Kernel_Name"]), grid)].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for (name, grid), d in sorted(groups.items(), key=lambda kv: -st.mean(kv[1])):
+            out.append(f"| {name} | {grid[0]} x {grid[1]} x {grid[2]} | {len(d)} | "
+                       f"{st.mean(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
     if a.note:
         out += ["", a.note]
     with open(a.out, "w") as f:
@@ -170,12 +183,16 @@ def _split_means(directory: str, match: str = SPLIT) -> tuple[dict, int, float]:
 
 
 def _copy_reading(directory: str, counter: str) -> float:
+    """Mean reading of the calibration copies: the multiply dispatches within
+    10% of the largest reading (other, small multiplies of the run are not
+    the 256 MiB copy)."""
     vals, meta = _per_dispatch(_csv(_find(directory, "counter_collection.csv")))
     ds = [d for d in vals if COPY in meta[d][0]]
     if not ds:
         raise SystemExit(f"no copy-calibration dispatches in {directory} "
                          "(run bench.py with --copy-calibration)")
-    return st.mean(vals[d][counter] for d in ds)
+    top = max(vals[d][counter] for d in ds)
+    return st.mean(vals[d][counter] for d in ds if vals[d][counter] >= 0.9 * top)
 
 
 def _source_record() -> dict:
@@ -274,6 +291,8 @@ def main(argv=None) -> int:
     t.add_argument("--command", required=True)
     t.add_argument("--title")
     t.add_argument("--note")
+    t.add_argument("--breakdown", action="append",
+                   help="also list the launches of kernels whose name contains this, by grid size")
     t.add_argument("--out", required=True)
     for name in ("traffic", "counters"):
         p = sub.add_parser(name)

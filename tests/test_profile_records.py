@@ -59,7 +59,8 @@ def test_counters_and_traffic(tmp_path):
     _pmc(d1 / "pmc_counter_collection.csv", [
         [1, SPLIT, "FETCH_SIZE", 100.0, 0, 20000], [1, SPLIT, "FETCH_SIZE", 50.0, 0, 20000],
         [2, SPLIT, "FETCH_SIZE", 200.0, 0, 30000], [2, SPLIT, "FETCH_SIZE", 50.0, 0, 30000],
-        [3, COPY, "FETCH_SIZE", 131072.0, 0, 90000]])
+        [3, COPY, "FETCH_SIZE", 131072.0, 0, 90000],
+        [4, COPY, "FETCH_SIZE", 3.0, 0, 2000]])   # a small multiply elsewhere in the run
     _pmc(d2 / "pmc_counter_collection.csv", [
         [1, SPLIT, "WRITE_SIZE", 10.0, 0, 20000], [2, SPLIT, "WRITE_SIZE", 30.0, 0, 20000],
         [3, COPY, "WRITE_SIZE", 262144.0, 0, 90000]])
