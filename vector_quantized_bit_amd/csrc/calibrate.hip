@@ -138,8 +138,6 @@ __global__ __launch_bounds__(256) void transform_keys_kernel(const void* __restr
 // K-Means
 // ---------------------------------------------------------------------------
 
-constexpr int kKmThreads = 512;
-constexpr int kKmWaves = kKmThreads / kWave;   // 8
 // Threads of an assignment workgroup: 4096-entry tables fill most of a CU's
 // LDS (one workgroup per CU), so those take 16 waves to keep 4 on every SIMD.
 template <int NENT>

@@ -23,8 +23,6 @@ namespace vqkv {
 
 namespace {
 
-constexpr int kEncThreads = 512;
-constexpr int kEncWaves = kEncThreads / kWave;     // 8
 constexpr int kEncTok = 8;                          // tokens per workgroup
 constexpr int kEncBlocks = kEncTok * kNumSub / 16;  // row blocks per tensor
 // Threads of the d = 4 encoder: with 4096-entry C_k its tables (about

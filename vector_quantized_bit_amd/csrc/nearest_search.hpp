@@ -65,7 +65,8 @@ __device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * 
 // Returns the nearest centroid of sub-vector lane % 16 (in all 4 of its
 // lanes; 0xffffffff only for a sub-vector with no candidate, which finite
 // inputs never produce).  Every lane of the wave must be active; all
-// branches below are uniform.
+// branches below are uniform except each lane's loop over its own hits in a
+// group, which holds no cross-lane operation.
 //
 // The encoders and the one-token searches of the decode step use the fp16
 // hi/lo form below (BlockD4H, BlockD8H): the centroids enter the matrix
@@ -77,6 +78,7 @@ __device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * 
 // accumulator input c; cup(blk) / cdown(blk) give the lane's 4 norm terms
 // ||c||^2 (1 + 2^-16) / (1 - 2^-16).
 constexpr int kSearchUnroll = 8;
+static_assert(kSearchUnroll * 4 <= 32, "a group's hits fit one 32-bit mask");
 
 // the minimum of one group's scores in this lane
 __device__ __forceinline__ float group_min(const f32x4_t (&d)[kSearchUnroll]) {
@@ -148,18 +150,20 @@ __device__ __forceinline__ void search_pass3(Block block, Cop cdown, int b0, int
 #pragma unroll
         for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cdown(blk + u));
         if (__builtin_amdgcn_ballot_w64(group_min(d) <= thr) == 0) continue;
+        // the group's hits as bits u * 4 + r, then one fp64 distance per hit
+        uint32_t hits = 0;
 #pragma unroll
-        for (int u = 0; u < kSearchUnroll; ++u) {
+        for (int u = 0; u < kSearchUnroll; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (d[u][r] <= thr) {
-                    const uint32_t nc = static_cast<uint32_t>((blk + u) * 16 + q4 + r);
-                    const double dd = exact(nc);
-                    if (nearer(dd, nc, bd, bi)) {
-                        bd = dd;
-                        bi = nc;
-                    }
-                }
+            for (int r = 0; r < 4; ++r) hits |= (d[u][r] <= thr ? 1u : 0u) << (u * 4 + r);
+        while (hits != 0) {
+            const int k = __builtin_ctz(hits);
+            hits &= hits - 1;
+            const uint32_t nc = static_cast<uint32_t>((blk + (k >> 2)) * 16 + q4 + (k & 3));
+            const double dd = exact(nc);
+            if (nearer(dd, nc, bd, bi)) {
+                bd = dd;
+                bi = nc;
             }
         }
     }
@@ -362,6 +366,111 @@ struct BlockD4H {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
     }
 };
+
+// NC column blocks (16 sub-vectors each) against the same 4-dim centroids:
+// one A operand and one set of norm terms per centroid block feed all NC
+// products.
+template <int NC>
+struct BlockD4HN {
+    const uint2* arow;
+    h4_t b[NC];
+    __device__ h4_t a(int blk) const { return __builtin_bit_cast(h4_t, arow[blk * 16]); }
+    __device__ f32x4_t operator()(h4_t a, int j, f32x4_t c) const {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b[j], c, 0, 0, 0);
+    }
+};
+
+// The minimum of a group of U blocks' scores in this lane.
+template <int U>
+__device__ __forceinline__ float group_min_u(const f32x4_t (&d)[U]) {
+    float m = INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        m = fminf(m, fminf(fminf(d[u][0], d[u][1]), fminf(d[u][2], d[u][3])));
+    return m;
+}
+
+// Passes 1 and 3 for NC column blocks sharing the centroid blocks [b0, b1)
+// (b1 - b0 a multiple of U): block.a(blk) is the A operand of a block and
+// block(a, j, c) the score of column block j.  Per column block they give
+// what search_pass1 and search_pass3 give for one; exact(j, c) is the fp64
+// distance of the lane's sub-vector in column block j to centroid c.
+template <int NC, int U, typename Block, typename Cop>
+__device__ __forceinline__ void search_pass1_cols(const Block& block, Cop cup, int b0, int b1,
+                                                  float (&smin)[NC]) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) smin[j] = INFINITY;
+#pragma nounroll
+    for (int blk = b0; blk < b1; blk += U) {
+        f32x4_t d[NC][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const auto a = block.a(blk + u);
+            const f32x4_t c = cup(blk + u);
+#pragma unroll
+            for (int j = 0; j < NC; ++j) d[j][u] = block(a, j, c);
+        }
+#pragma unroll
+        for (int j = 0; j < NC; ++j) smin[j] = fminf(smin[j], group_min_u<U>(d[j]));
+    }
+}
+
+template <int NC, int U, typename Block, typename Cop, typename Exact>
+__device__ __forceinline__ void search_pass3_cols(const Block& block, Cop cdown, int b0, int b1,
+                                                  const float (&thr)[NC], int q4, Exact exact,
+                                                  double (&bd)[NC], uint32_t (&bi)[NC]) {
+    static_assert(U * 4 <= 32, "a group's hits fit one 32-bit mask");
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        bd[j] = INFINITY;
+        bi[j] = 0xffffffffu;
+    }
+#pragma nounroll
+    for (int blk = b0; blk < b1; blk += U) {
+        f32x4_t d[NC][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const auto a = block.a(blk + u);
+            const f32x4_t c = cdown(blk + u);
+#pragma unroll
+            for (int j = 0; j < NC; ++j) d[j][u] = block(a, j, c);
+        }
+        // block minima first: the hit bits of a block are formed only where
+        // some lane of the wave has one there (hits are rare)
+        float m[NC][U];
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                m[j][u] = fminf(fminf(d[j][u][0], d[j][u][1]), fminf(d[j][u][2], d[j][u][3]));
+                any |= m[j][u] <= thr[j];
+            }
+        if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            uint32_t hits = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (__builtin_amdgcn_ballot_w64(m[j][u] <= thr[j]) != 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        hits |= (d[j][u][r] <= thr[j] ? 1u : 0u) << (u * 4 + r);
+                }
+            }
+            while (hits != 0) {
+                const int k = __builtin_ctz(hits);
+                hits &= hits - 1;
+                const uint32_t nc = static_cast<uint32_t>((blk + (k >> 2)) * 16 + q4 + (k & 3));
+                const double dd = exact(j, nc);
+                if (nearer(dd, nc, bd[j], bi[j])) {
+                    bd[j] = dd;
+                    bi[j] = nc;
+                }
+            }
+        }
+    }
+}
 
 // The block score: ctab [.][8] fp16 centroids (16-byte aligned entries).
 struct BlockD8H {

@@ -265,127 +265,177 @@ __device__ __forceinline__ void new_token_inputs(const void* q, int q_f32, const
 }
 
 // LDS of the new-token workgroup with 12-bit keys (offsets into `tab`):
-// C_k as stored (fp16, 8 bytes an entry), its squared norms ||c||^2 (fp32),
-// C_v (fp16), and 4 KiB for the exchanges of the key search.
-constexpr int kNtN = 4096 * 8;
-constexpr int kNtV = kNtN + 4096 * 4;
-constexpr int kNtX = kNtV + 256 * 8;
-static_assert(kNtX + 4096 <= 2 * kTable, "the 12-bit new-token tables fit the LDS tables");
+// C_k as stored (fp16, 8 bytes an entry) with its norm terms (upper, lower),
+// C_v likewise, and the exchanges of the search.
+constexpr int kNtKu = 4096 * 8;
+constexpr int kNtKd = kNtKu + 4096 * 4;
+constexpr int kNtV = kNtKd + 4096 * 4;
+constexpr int kNtVu = kNtV + 256 * 8;
+constexpr int kNtVd = kNtVu + 256 * 4;
+constexpr int kNtX = kNtVd + 256 * 4;
+constexpr int kNtXBytes = 64 * 4 + 2 * kWaves * 16 * 8 + 2 * kWaves * 16 * 4;
+static_assert(kNtX + kNtXBytes <= 2 * kTable, "the 12-bit new-token tables fit the LDS tables");
 
-// Stage C_k of 4096 entries for new_token_keys12, with its norms (the loads
-// issued before any is used).
-__device__ __forceinline__ void stage_keys12(const uint2* __restrict__ ksrc, uint8_t* tab,
-                                             int tid) {
-    uint2* k16 = reinterpret_cast<uint2*>(tab);
-    float* nrm = reinterpret_cast<float*>(tab + kNtN);
-    constexpr int kPer = 4096 / kThreads;
-    uint2 c[kPer];
+// C_k (4096 entries) and C_v (256) of the new-token workgroup with 12-bit
+// keys, loaded before the token's inputs are known and written to LDS by
+// new_token_codes12 with their norm terms.
+struct Codes12Tables {
+    uint2 k[4096 / kThreads];
+    uint2 v;
+};
+__device__ __forceinline__ Codes12Tables load_codes12(const uint2* __restrict__ ksrc,
+                                                      const uint2* __restrict__ vsrc, int tid) {
+    Codes12Tables t;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) c[j] = ksrc[tid + j * kThreads];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int i = tid + j * kThreads;
-        k16[i] = c[j];
-        nrm[i] = norm2(c[j]);
-    }
+    for (int j = 0; j < 4096 / kThreads; ++j) t.k[j] = ksrc[tid + j * kThreads];
+    t.v = vsrc[tid & 255];
+    return t;
 }
 
-// The key codes of the appended token for 4096-entry C_k (d = 4), found by
-// the certified matrix-core search of nearest_search.hpp spread over the 16
-// waves: wave w takes sub-vectors 16 (w / 8) .. + 15 (one MFMA column block)
-// and centroids 512 (w % 8) .. + 511.  The 8 waves of a column block meet in
-// LDS three times: pass-1 minima (the threshold), candidate counts (a
-// sub-vector with exactly one candidate takes it), and, only when some
-// sub-vector has several, the fp64 minima over their candidates.  The
-// decisions are those of the fp64 scan: ties to the lowest index.
-//   tab   the tables of stage_keys12 (and 4 KiB of exchanges at kNtX)
-//   xk    the transformed key (fp64); codes[32] receives the codes
+// Float keys whose unsigned order is the float order (finite values).
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    return (u >> 31) != 0 ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_key(uint32_t k) {
+    return __builtin_bit_cast(float, (k >> 31) != 0 ? (k & 0x7fffffffu) : ~k);
+}
+
+// The codes of the appended token for 4096-entry C_k and 256-entry C_v
+// (d = 4), found by the certified fp16 hi/lo search of nearest_search.hpp
+// with one scale per tensor (the token's largest |2x|, which every wave
+// finds for itself), so that the norm terms are scaled once as the tables
+// are written.  Wave w takes the 16 sub-vectors of column block w / 8 and,
+// with k = w % 8, key centroid blocks 32 k .. 32 k + 31 and value blocks
+// 2 k, 2 k + 1.  Pass-1 minima meet in LDS as atomic minima (the
+// thresholds); the second pass evaluates each candidate (a score within the
+// bound of the threshold, about one a sub-vector) in fp64 as it finds it,
+// and the waves' fp64 minima meet in LDS.  The decisions are those of the
+// fp64 scan: ties to the lowest index.
+//   tabs   the codebooks of load_codes12; tab receives the tables, exchanges at kNtX
+//   xnew   the transformed key and the value (fp64); codes[t][32] receives the codes
 // Ends with a barrier; codes is then visible to the whole workgroup.
-__device__ __forceinline__ void new_token_keys12(uint8_t* tab, const double* xk, uint32_t* codes,
-                                                 int tid, int lane, int wave) {
-    constexpr int kEnt = 4096, kCb = 8;   // waves per column block
-    static_assert(kThreads == 1024 && kEnt == (kWaves / 2) * 512, "8 waves of 512 centroids");
-    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(tab);
-    uint8_t* xbuf = tab + kNtX;
-    float* wmin = reinterpret_cast<float*>(xbuf);      // [16 waves][16] pass-1 minima
-    int* wcnt = reinterpret_cast<int*>(xbuf + 1024);   // [16][16] candidate counts
-    int* wcand = reinterpret_cast<int*>(xbuf + 2048);  // [16][16] a candidate (or -1)
-    int* flag = reinterpret_cast<int*>(xbuf + 3072);   // [32] several candidates
-    double* wbd = reinterpret_cast<double*>(xbuf);     // [16][16] (reuses the above)
-    uint32_t* wbi = reinterpret_cast<uint32_t*>(xbuf + 2048);
-    const int cb = wave / kCb, sv = 16 * cb + (lane & 15), q4 = 4 * (lane >> 4);
-    double xd[4];
+__device__ __forceinline__ void new_token_codes12(const Codes12Tables& tabs, uint8_t* tab,
+                                                  const double (*xnew)[kHeadDim],
+                                                  uint32_t (*codes)[kNumSub], int tid, int lane,
+                                                  int wave) {
+    constexpr int kCb = 8;   // waves per column block
+    static_assert(kThreads == 1024 && 4096 == kCb * 32 * 16 && 256 == kCb * 2 * 16,
+                  "32 key blocks and 2 value blocks a wave");
+    uint32_t* wthr = reinterpret_cast<uint32_t*>(tab + kNtX);               // [2][32] keys
+    double* wbd = reinterpret_cast<double*>(tab + kNtX + 256);              // [2][16 waves][16]
+    uint32_t* wbi = reinterpret_cast<uint32_t*>(tab + kNtX + 256 + 2 * kWaves * 16 * 8);
+    // one scale per tensor: the largest |2x| of the token's 128 channels
+    float sc[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xd[j] = xk[4 * sv + j];
-    float xx = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float v = static_cast<float>(xd[j]);
-        xx += v * v;
+    for (int t = 0; t < 2; ++t) {
+        const float m = fmaxf(fabsf(-2.f * static_cast<float>(xnew[t][lane])),
+                              fabsf(-2.f * static_cast<float>(xnew[t][lane + 64])));
+        sc[t] = hilo_scale(wave_max(m));
     }
-    // fp16 hi/lo matrix-core scores in units of 2^s (the lane's column)
-    const HiLoD4 hl = hilo_d4(xd, lane);
-    const BlockD4H block(k16, hl.b, lane);
-    const f32x4_t* ncol = reinterpret_cast<const f32x4_t*>(tab + kNtN) + lane / 16;
-    const float up = kBoundUpH * hl.scale, down = kBoundDownH * hl.scale;   // exact
-    const auto cup = [&](int blk) { return ncol[blk * 4] * up; };
-    const auto cdown = [&](int blk) { return ncol[blk * 4] * down; };
-    const auto exact = [&](uint32_t nc) {
-        return sqdist4_f64(xd, reinterpret_cast<const uint2*>(k16)[nc]);
+    // the tables with their norm terms at these scales
+#pragma unroll
+    for (int j = 0; j < 4096 / kThreads; ++j) {
+        const int i = tid + j * kThreads;
+        const uint2 c = tabs.k[j];
+        const float2 nt = hilo_norm_terms(norm2(c), l1_4(c), sc[0]);
+        reinterpret_cast<uint2*>(tab)[i] = c;
+        reinterpret_cast<float*>(tab + kNtKu)[i] = nt.x;
+        reinterpret_cast<float*>(tab + kNtKd)[i] = nt.y;
+    }
+    if (tid < 256) {
+        const float2 nt = hilo_norm_terms(norm2(tabs.v), l1_4(tabs.v), sc[1]);
+        reinterpret_cast<uint2*>(tab + kNtV)[tid] = tabs.v;
+        reinterpret_cast<float*>(tab + kNtVu)[tid] = nt.x;
+        reinterpret_cast<float*>(tab + kNtVd)[tid] = nt.y;
+    }
+    if (tid < 2 * kNumSub) wthr[tid] = 0xffffffffu;
+    wave = __builtin_amdgcn_readfirstlane(wave);   // scalar: block bounds and loop counters in SGPRs
+    const int cb = wave / kCb, wk = wave % kCb, sv = 16 * cb + (lane & 15), q4 = 4 * (lane >> 4);
+    BlockD4HN<1> bk, bv;
+    bk.arow = reinterpret_cast<const uint2*>(tab) + (lane & 15);
+    bv.arow = reinterpret_cast<const uint2*>(tab + kNtV) + (lane & 15);
+    bk.b[0] = hilo_rows<4, h4_t>(&xnew[0][4 * sv], lane, sc[0]);
+    bv.b[0] = hilo_rows<4, h4_t>(&xnew[1][4 * sv], lane, sc[1]);
+    float bound[2];   // the row bound of the lane's sub-vector at the tensor's scale
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float xx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = static_cast<float>(xnew[t][4 * sv + i]);
+            xx += v * v;
+        }
+        bound[t] = row_bound_h(xx) * sc[t];
+    }
+    struct Col {
+        const f32x4_t* p;
+        __device__ f32x4_t operator()(int blk) const { return p[blk * 4]; }
     };
-    const int b0 = 32 * (wave % kCb), b1 = b0 + 32;   // this wave's centroid blocks
-    float smin = search_pass1(block, cup, b0, b1);
-    smin = fminf(smin, lane_partner<16>(smin, lane));
-    smin = fminf(smin, lane_partner<32>(smin, lane));
-    if (lane < 16) wmin[wave * 16 + lane] = smin;
-    __syncthreads();
-    float gmin = wmin[cb * kCb * 16 + (lane & 15)];
-    for (int w = 1; w < kCb; ++w) gmin = fminf(gmin, wmin[(cb * kCb + w) * 16 + (lane & 15)]);
-    const float thr = gmin + row_bound_h(xx) * hl.scale;
-    int cnt, cand;
-    search_pass2<true>(block, cdown, b0, b1, thr, cnt, cand);   // sparse hits: 1 in 4096
-    cnt = sum_lanes16_32(cnt, lane);
-    cand = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
-    if (lane < 16) {
-        wcnt[wave * 16 + lane] = cnt;
-        wcand[wave * 16 + lane] = cand;
-    }
-    __syncthreads();
-    if (tid < kNumSub) {   // sub-vector tid: column block tid / 16, column tid % 16
-        const int w0 = (tid / 16) * kCb, c = tid & 15;
-        int total = 0, one = -1;
-        for (int w = w0; w < w0 + kCb; ++w) {
-            total += wcnt[w * 16 + c];
-            one = max(one, wcnt[w * 16 + c] > 0 ? wcand[w * 16 + c] : -1);
-        }
-        codes[tid] = static_cast<uint32_t>(one) & (kEnt - 1);
-        flag[tid] = total != 1;
-    }
-    __syncthreads();
-    bool several = false;
-    for (int k = 0; k < kNumSub; ++k) several |= flag[k] != 0;
-    if (several) {   // uniform: fp64 resolution of every sub-vector's candidates
-        double bd;
-        uint32_t bi;
-        search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi);
-        take_lanes16_32(bd, bi, lane);
+    const Col kup{reinterpret_cast<const f32x4_t*>(tab + kNtKu) + lane / 16};
+    const Col kdown{reinterpret_cast<const f32x4_t*>(tab + kNtKd) + lane / 16};
+    const Col vup{reinterpret_cast<const f32x4_t*>(tab + kNtVu) + lane / 16};
+    const Col vdown{reinterpret_cast<const f32x4_t*>(tab + kNtVd) + lane / 16};
+    const auto kexact = [&](int, uint32_t nc) {
+        return sqdist4_f64(&xnew[0][4 * sv], reinterpret_cast<const uint2*>(tab)[nc]);
+    };
+    const auto vexact = [&](int, uint32_t nc) {
+        return sqdist4_f64(&xnew[1][4 * sv], reinterpret_cast<const uint2*>(tab + kNtV)[nc]);
+    };
+    const int kb0 = 32 * wk, kb1 = kb0 + 32, vb0 = 2 * wk, vb1 = vb0 + 2;
+    __syncthreads();   // tables and threshold slots written
+
+    // pass 1: the thresholds
+    {
+        float sk[1], sv1[1];
+        search_pass1_cols<1, kSearchUnroll>(bk, kup, kb0, kb1, sk);
+        search_pass1_cols<1, 2>(bv, vup, vb0, vb1, sv1);
+        sk[0] = fminf(sk[0], lane_partner<16>(sk[0], lane));
+        sk[0] = fminf(sk[0], lane_partner<32>(sk[0], lane));
+        sv1[0] = fminf(sv1[0], lane_partner<16>(sv1[0], lane));
+        sv1[0] = fminf(sv1[0], lane_partner<32>(sv1[0], lane));
         if (lane < 16) {
-            wbd[wave * 16 + lane] = bd;
-            wbi[wave * 16 + lane] = bi;
+            atomicMin(&wthr[sv], ordered_key(sk[0]));
+            atomicMin(&wthr[32 + sv], ordered_key(sv1[0]));
         }
-        __syncthreads();
-        if (tid < kNumSub) {
-            const int w0 = (tid / 16) * kCb, c = tid & 15;
-            double d0 = wbd[w0 * 16 + c];
-            uint32_t i0 = wbi[w0 * 16 + c];
-            for (int w = w0 + 1; w < w0 + kCb; ++w) {
-                if (nearer(wbd[w * 16 + c], wbi[w * 16 + c], d0, i0)) {
-                    d0 = wbd[w * 16 + c];
-                    i0 = wbi[w * 16 + c];
-                }
+    }
+    __syncthreads();
+    const float thk[1] = {from_ordered_key(wthr[sv]) + bound[0]};
+    const float thv[1] = {from_ordered_key(wthr[32 + sv]) + bound[1]};
+
+    // pass 2: fp64 distances of every candidate; the lexicographic minimum
+    // over the 4 lanes of a sub-vector, then over the waves of its block
+    {
+        double bd[1];
+        uint32_t bi[1];
+        search_pass3_cols<1, 4>(bk, kdown, kb0, kb1, thk, q4, kexact, bd, bi);
+        take_lanes16_32(bd[0], bi[0], lane);
+        if (lane < 16) {
+            wbd[wave * 16 + lane] = bd[0];
+            wbi[wave * 16 + lane] = bi[0];
+        }
+        search_pass3_cols<1, 2>(bv, vdown, vb0, vb1, thv, q4, vexact, bd, bi);
+        take_lanes16_32(bd[0], bi[0], lane);
+        if (lane < 16) {
+            wbd[(kWaves + wave) * 16 + lane] = bd[0];
+            wbi[(kWaves + wave) * 16 + lane] = bi[0];
+        }
+    }
+    __syncthreads();
+    if (tid < 2 * kNumSub) {   // tensor tid / 32, sub-vector tid % 32 (column block, column)
+        const int t = tid >> 5, sub = tid & 31, w0 = (sub / 16) * kCb, c = sub & 15;
+        const double* d = wbd + (t * kWaves + w0) * 16 + c;
+        const uint32_t* ix = wbi + (t * kWaves + w0) * 16 + c;
+        double d0 = d[0];
+        uint32_t i0 = ix[0];
+#pragma unroll
+        for (int w = 1; w < kCb; ++w) {
+            if (nearer(d[w * 16], ix[w * 16], d0, i0)) {
+                d0 = d[w * 16];
+                i0 = ix[w * 16];
             }
-            codes[tid] = i0 & (kEnt - 1);   // (a code always exists for finite inputs)
         }
+        codes[t][sub] = i0 & (t == 0 ? 4095u : 255u);   // (a code always exists for finite inputs)
     }
     __syncthreads();
 }
@@ -421,11 +471,13 @@ __device__ __forceinline__ void new_token_workgroup(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint2* ksrc = reinterpret_cast<const uint2*>(cb_k) + (static_cast<size_t>(g) << KBITS);
     const uint2* vsrc = reinterpret_cast<const uint2*>(cb_v) + static_cast<size_t>(g) * 256;
-    if constexpr (KBITS == 12)
-        stage_keys12(ksrc, tab, tid);
-    else
+    Codes12Tables tabs12;
+    if constexpr (KBITS == 12) {
+        tabs12 = load_codes12(ksrc, vsrc, tid);
+    } else {
         for (int i = tid; i < KENT; i += kThreads) reinterpret_cast<uint2*>(tab)[i] = ksrc[i];
-    if (tid < 256) reinterpret_cast<uint2*>(tab + kVtab)[tid] = vsrc[tid];
+        if (tid < 256) reinterpret_cast<uint2*>(tab + kVtab)[tid] = vsrc[tid];
+    }
 
     float x0, x1;
     new_token_inputs<G>(q, q_f32, lambda, k_new, v_new, kv_f32, num_q_heads, num_kv_heads, g, b,
@@ -433,16 +485,30 @@ __device__ __forceinline__ void new_token_workgroup(
     __syncthreads();
 
     // 1. codes
-    const int pos = tid & 31, slice = tid >> 5;
-    double xk[4], xv[4];
+    const size_t row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + append_pos;
+    if constexpr (KBITS == 12) {
+        new_token_codes12(tabs12, tab, xnew, newc, tid, lane, wave);
+        // byte j of the key row holds bits [8j, 8j + 8) of the 12-bit stream
+        if (tid < 48) {
+            const int bit = 8 * tid, i0 = bit / 12, sh = bit % 12;
+            uint32_t v = newc[0][i0] >> sh;
+            if (sh > 4) v |= newc[0][i0 + 1] << (12 - sh);
+            new_codes_k[row * 48 + tid] = static_cast<uint8_t>(v & 0xffu);
+        } else if (tid >= 64 && tid < 64 + kNumSub) {
+            new_codes_v[row * kNumSub + tid - 64] = static_cast<uint8_t>(newc[1][tid - 64]);
+        }
+    } else {
+        // fp64 scans of the 256-entry tables: thread (slice, pos) takes
+        // centroids slice, slice + 32, ... of sub-vector pos
+        const int pos = tid & 31, slice = tid >> 5;
+        double xk[4], xv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        xk[i] = xnew[0][4 * pos + i];
-        xv[i] = xnew[1][4 * pos + i];
-    }
-    double dk = INFINITY, dv = INFINITY;
-    uint32_t ik = 0, iv = 0;
-    if constexpr (KBITS == 8) {   // 12-bit keys: the matrix-core search below
+        for (int i = 0; i < 4; ++i) {
+            xk[i] = xnew[0][4 * pos + i];
+            xv[i] = xnew[1][4 * pos + i];
+        }
+        double dk = INFINITY, dv = INFINITY;
+        uint32_t ik = 0, iv = 0;
         for (int c = slice; c < KENT; c += 32) {
             const double d = sqdist4_f64(xk, reinterpret_cast<const uint2*>(tab)[c]);
             if (d < dk) {
@@ -450,63 +516,48 @@ __device__ __forceinline__ void new_token_workgroup(
                 ik = static_cast<uint32_t>(c);
             }
         }
-    }
 #pragma unroll 2
-    for (int c = slice; c < 256; c += 32) {
-        const double d = sqdist4_f64(xv, reinterpret_cast<const uint2*>(tab + kVtab)[c]);
-        if (d < dv) {
-            dv = d;
-            iv = static_cast<uint32_t>(c);
-        }
-    }
-    {
-        const double dk2 = __shfl_xor(dk, 32, kWave), dv2 = __shfl_xor(dv, 32, kWave);
-        const uint32_t ik2 = __shfl_xor(ik, 32, kWave), iv2 = __shfl_xor(iv, 32, kWave);
-        if (nearer(dk2, ik2, dk, ik)) {
-            dk = dk2;
-            ik = ik2;
-        }
-        if (nearer(dv2, iv2, dv, iv)) {
-            dv = dv2;
-            iv = iv2;
-        }
-    }
-    // [tensor][wave][pos]: lanes 0..31 report keys, 32..63 values
-    double* sd = reinterpret_cast<double*>(scratch);
-    uint32_t* si = reinterpret_cast<uint32_t*>(sd + 2 * kWaves * 32);
-    const int tsel = lane >> 5;
-    sd[(tsel * kWaves + wave) * 32 + pos] = tsel ? dv : dk;
-    si[(tsel * kWaves + wave) * 32 + pos] = tsel ? iv : ik;
-    __syncthreads();
-    const size_t row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + append_pos;
-    if (tid < 64) {
-        double d0 = sd[tsel * kWaves * 32 + pos];
-        uint32_t i0 = si[tsel * kWaves * 32 + pos];
-        for (int w = 1; w < kWaves; ++w) {
-            const double d = sd[(tsel * kWaves + w) * 32 + pos];
-            const uint32_t i = si[(tsel * kWaves + w) * 32 + pos];
-            if (nearer(d, i, d0, i0)) {
-                d0 = d;
-                i0 = i;
+        for (int c = slice; c < 256; c += 32) {
+            const double d = sqdist4_f64(xv, reinterpret_cast<const uint2*>(tab + kVtab)[c]);
+            if (d < dv) {
+                dv = d;
+                iv = static_cast<uint32_t>(c);
             }
         }
-        if (tsel || KBITS == 8) newc[tsel][pos] = i0;
-        if (tsel) {
-            new_codes_v[row * kNumSub + pos] = static_cast<uint8_t>(i0);
-        } else if constexpr (KBITS == 8) {
-            new_codes_k[row * kNumSub + pos] = static_cast<uint8_t>(i0);
+        {
+            const double dk2 = __shfl_xor(dk, 32, kWave), dv2 = __shfl_xor(dv, 32, kWave);
+            const uint32_t ik2 = __shfl_xor(ik, 32, kWave), iv2 = __shfl_xor(iv, 32, kWave);
+            if (nearer(dk2, ik2, dk, ik)) {
+                dk = dk2;
+                ik = ik2;
+            }
+            if (nearer(dv2, iv2, dv, iv)) {
+                dv = dv2;
+                iv = iv2;
+            }
         }
-    }
-    __syncthreads();
-    if constexpr (KBITS == 12) {
-        new_token_keys12(tab, xnew[0], newc[0], tid, lane, wave);
-        // byte j of the row holds bits [8j, 8j + 8) of the 12-bit stream
-        if (tid < 48) {
-            const int bit = 8 * tid, i0 = bit / 12, sh = bit % 12;
-            uint32_t v = newc[0][i0] >> sh;
-            if (sh > 4) v |= newc[0][i0 + 1] << (12 - sh);
-            new_codes_k[row * 48 + tid] = static_cast<uint8_t>(v & 0xffu);
+        // [tensor][wave][pos]: lanes 0..31 report keys, 32..63 values
+        double* sd = reinterpret_cast<double*>(scratch);
+        uint32_t* si = reinterpret_cast<uint32_t*>(sd + 2 * kWaves * 32);
+        const int tsel = lane >> 5;
+        sd[(tsel * kWaves + wave) * 32 + pos] = tsel ? dv : dk;
+        si[(tsel * kWaves + wave) * 32 + pos] = tsel ? iv : ik;
+        __syncthreads();
+        if (tid < 64) {
+            double d0 = sd[tsel * kWaves * 32 + pos];
+            uint32_t i0 = si[tsel * kWaves * 32 + pos];
+            for (int w = 1; w < kWaves; ++w) {
+                const double d = sd[(tsel * kWaves + w) * 32 + pos];
+                const uint32_t i = si[(tsel * kWaves + w) * 32 + pos];
+                if (nearer(d, i, d0, i0)) {
+                    d0 = d;
+                    i0 = i;
+                }
+            }
+            newc[tsel][pos] = i0;
+            (tsel ? new_codes_v : new_codes_k)[row * kNumSub + pos] = static_cast<uint8_t>(i0);
         }
+        __syncthreads();
     }
 
     // 2. the one-token partial of each query head: lane l holds dims 2l, 2l + 1,
@@ -537,9 +588,7 @@ __device__ __forceinline__ void new_token_workgroup(
 // nearest_search.hpp spread over the workgroup: the 16 sub-vectors of a
 // tensor are one MFMA column block, and wave w scans centroids 256 w ..
 // 256 w + 255.  Per tensor: the waves' pass-1 minima meet in LDS (the
-// threshold), their candidate counts meet in LDS, and a sub-vector with
-// exactly one candidate takes it; only when some sub-vector has several do
-// the waves evaluate their candidates in fp64 and meet a third time.
+// threshold), then the fp64 minima over their candidates.
 // LDS: C_k in `tab`, C_v 64 KiB above; ||c||^2 of the current tensor in
 // `scratch` (16 KiB); the exchanges in `xbuf` (4 KiB).
 template <int G>
@@ -568,11 +617,8 @@ __device__ __forceinline__ void new_token_workgroup8(
     static_assert(kThreads == 1024 && kEnt == kWaves * 256, "16 waves of 256 centroids");
     float* nrm = reinterpret_cast<float*>(scratch);             // [4096] ||c||^2
     float* wmin = reinterpret_cast<float*>(xbuf);               // [16 waves][16] pass-1 minima
-    int* wcnt = reinterpret_cast<int*>(xbuf + 1024);            // [16][16] candidate counts
-    int* wcand = reinterpret_cast<int*>(xbuf + 2048);           // [16][16] a candidate (or -1)
-    int* flag = reinterpret_cast<int*>(xbuf + 3072);            // [16] several candidates
-    double* wbd = reinterpret_cast<double*>(xbuf);              // [16][16] (reuses the above)
-    uint32_t* wbi = reinterpret_cast<uint32_t*>(xbuf + 2048);
+    double* wbd = reinterpret_cast<double*>(xbuf + 1024);       // [16][16] fp64 minima
+    uint32_t* wbi = reinterpret_cast<uint32_t*>(xbuf + 3072);   // [16][16] their indices
     const int pos = lane & (kPos - 1), q4 = 4 * (lane >> 4);
     const int b0 = 16 * wave, b1 = b0 + 16;   // this wave's centroid blocks
     for (int t = 0; t < 2; ++t) {
@@ -618,48 +664,27 @@ __device__ __forceinline__ void new_token_workgroup8(
         float gmin = wmin[pos];
         for (int w = 1; w < kWaves; ++w) gmin = fminf(gmin, wmin[w * kPos + pos]);
         const float thr = gmin + row_bound_h(xx) * hl.scale;
-        int cnt, cand;
-        search_pass2<true>(block, cdown, b0, b1, thr, cnt, cand);   // sparse hits: 1 in 4096
-        cnt = sum_lanes16_32(cnt, lane);
-        cand = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
+        // fp64 distances of every candidate (about one a sub-vector, so they
+        // are evaluated as they are found rather than counted first)
+        double bd;
+        uint32_t bi;
+        search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi);
+        take_lanes16_32(bd, bi, lane);
         if (lane < kPos) {
-            wcnt[wave * kPos + lane] = cnt;
-            wcand[wave * kPos + lane] = cand;
+            wbd[wave * kPos + lane] = bd;
+            wbi[wave * kPos + lane] = bi;
         }
         __syncthreads();
         if (tid < kPos) {
-            int total = 0, one = -1;
-            for (int w = 0; w < kWaves; ++w) {
-                total += wcnt[w * kPos + tid];
-                one = max(one, wcnt[w * kPos + tid] > 0 ? wcand[w * kPos + tid] : -1);
-            }
-            newc[t][tid] = static_cast<uint32_t>(one) & (kEnt - 1);
-            flag[tid] = total != 1;
-        }
-        __syncthreads();
-        bool several = false;
-        for (int k = 0; k < kPos; ++k) several |= flag[k] != 0;
-        if (several) {   // uniform: fp64 resolution of every sub-vector's candidates
-            double bd;
-            uint32_t bi;
-            search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi);
-            take_lanes16_32(bd, bi, lane);
-            if (lane < kPos) {
-                wbd[wave * kPos + lane] = bd;
-                wbi[wave * kPos + lane] = bi;
-            }
-            __syncthreads();
-            if (tid < kPos) {
-                double d0 = wbd[tid];
-                uint32_t i0 = wbi[tid];
-                for (int w = 1; w < kWaves; ++w) {
-                    if (nearer(wbd[w * kPos + tid], wbi[w * kPos + tid], d0, i0)) {
-                        d0 = wbd[w * kPos + tid];
-                        i0 = wbi[w * kPos + tid];
-                    }
+            double d0 = wbd[tid];
+            uint32_t i0 = wbi[tid];
+            for (int w = 1; w < kWaves; ++w) {
+                if (nearer(wbd[w * kPos + tid], wbi[w * kPos + tid], d0, i0)) {
+                    d0 = wbd[w * kPos + tid];
+                    i0 = wbi[w * kPos + tid];
                 }
-                newc[t][tid] = i0 & (kEnt - 1);   // (a code always exists for finite inputs)
             }
+            newc[t][tid] = i0 & (kEnt - 1);   // (a code always exists for finite inputs)
         }
         __syncthreads();   // the exchange buffers and norms are free for the next tensor
     }
