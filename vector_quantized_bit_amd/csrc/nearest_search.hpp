@@ -390,6 +390,26 @@ __device__ __forceinline__ float group_min_u(const f32x4_t (&d)[U]) {
     return m;
 }
 
+// The scores of U blocks from blk on: every A operand and norm term of the
+// group is requested before the first product, so the group waits on LDS
+// once rather than once per block.
+template <int NC, int U, typename Block, typename Cop>
+__device__ __forceinline__ void group_scores(const Block& block, Cop cop, int blk,
+                                             f32x4_t (&d)[NC][U]) {
+    decltype(block.a(0)) a[U];
+    f32x4_t c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        a[u] = block.a(blk + u);
+        c[u] = cop(blk + u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) d[j][u] = block(a[u], j, c[u]);
+}
+
 // Passes 1 and 3 for NC column blocks sharing the centroid blocks [b0, b1)
 // (b1 - b0 a multiple of U): block.a(blk) is the A operand of a block and
 // block(a, j, c) the score of column block j.  Per column block they give
@@ -403,13 +423,7 @@ __device__ __forceinline__ void search_pass1_cols(const Block& block, Cop cup, i
 #pragma nounroll
     for (int blk = b0; blk < b1; blk += U) {
         f32x4_t d[NC][U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const auto a = block.a(blk + u);
-            const f32x4_t c = cup(blk + u);
-#pragma unroll
-            for (int j = 0; j < NC; ++j) d[j][u] = block(a, j, c);
-        }
+        group_scores<NC, U>(block, cup, blk, d);
 #pragma unroll
         for (int j = 0; j < NC; ++j) smin[j] = fminf(smin[j], group_min_u<U>(d[j]));
     }
@@ -428,13 +442,7 @@ __device__ __forceinline__ void search_pass3_cols(const Block& block, Cop cdown,
 #pragma nounroll
     for (int blk = b0; blk < b1; blk += U) {
         f32x4_t d[NC][U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const auto a = block.a(blk + u);
-            const f32x4_t c = cdown(blk + u);
-#pragma unroll
-            for (int j = 0; j < NC; ++j) d[j][u] = block(a, j, c);
-        }
+        group_scores<NC, U>(block, cdown, blk, d);
         // block minima first: the hit bits of a block are formed only where
         // some lane of the wave has one there (hits are rare)
         float m[NC][U];
