@@ -388,18 +388,18 @@ int check_step_args(const vq_layout* layout, const void* q, int q_dtype, const v
 }
 
 // The new token's encode in cached tokens that one split workgroup attends
-// over in the same time, rounded up: the encode takes about 7 us with
-// 256-entry C_k while the other splits load the chip, and a split takes
-// 3.7-4.1 ns per token; with 4096 entries the folded split starts on its
-// cached tokens at most about 19 us in (codes 12.4 us median, 13.3 us max,
-// then the one-token partial and the table staging of the token loop) and
-// takes about 3.1 ns per token with 5 query heads a KV head (MI355X,
-// timestamps).  Too large a value only lengthens the other splits a little;
-// too small a one makes the last split the slowest.  0 where the encode is
-// not folded (d = 8).
+// over in the same time, rounded up.  The folded split starts on its cached
+// tokens about 7-8 us in with 256-entry C_k (encode about 6 us, then the
+// one-token partial and the table staging of the token loop) and at most
+// about 19 us in with 4096 entries (codes 12.4 us median, 13.3 us max); a
+// split takes about 2.35 ns per token with 4 query heads a KV head and
+// 3.1 ns with 5 (MI355X, timestamps, the chip loaded by the other splits).
+// Too large a value only lengthens the other splits a little; too small a
+// one makes the last split the slowest.  0 where the encode is not folded
+// (d = 8).
 int fold_tokens(const vq_layout* layout) {
     if (layout->sub_dim != 4) return 0;
-    return layout->k_code_bits == 8 ? 2048 : 6144;
+    return layout->k_code_bits == 8 ? 3072 : 6144;
 }
 
 // From this many streams on, a decode step may fold the new token into the
