@@ -14,6 +14,7 @@ Three reductions, each reading the CSV files that rocprofv3 wrote with
             copy of the same run; JSON (read by bench.py) plus a Markdown copy.
   counters  one or more ``--pmc`` runs of shader counters -> per-dispatch means
             for the split kernel, as JSON (read by bench.py).
+  compare   two counter records side by side -> a Markdown table.
 
 Each record stores the commands given here and a sha256 of the kernel's
 sources; bench.py ignores a record whose hash no longer matches.
@@ -281,6 +282,48 @@ def cmd_counters(a) -> None:
     print(path)
 
 
+# Rows of a counter comparison, in this order (where both records hold them).
+COMPARE_ROWS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+                "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES"]
+
+
+def cmd_compare(a) -> None:
+    """Two counter records of the same loops side by side (the first is the
+    reference of the ratio column) as a Markdown table."""
+    recs = [json.load(open(path)) for path in a.records]
+    md = [f"# {a.title}", "",
+          "Counter runs, one per variant (from the repository root, after "
+          "`cd /tmp && export TMPDIR=/tmp`):", ""]
+    for r in recs:
+        md += [f"    {c}" for c in r["commands"]]
+    md += ["", "Reduced by `python profile_records.py counters` into "
+           + " and ".join(f"`{os.path.relpath(p, ROOT)}`" for p in a.records)
+           + ", compared by `python profile_records.py compare`. Per dispatch of the split "
+           "kernel (means over the run's dispatches; counters serialise dispatches):", "",
+           f"| counter | {a.labels[0]} | {a.labels[1]} | ratio |", "|---|---|---|---|"]
+    p0, p1 = recs[0]["per_dispatch"], recs[1]["per_dispatch"]
+    for k in COMPARE_ROWS:
+        if k in p0 and k in p1:
+            md.append(f"| {k} | {p0[k]:,.0f} | {p1[k]:,.0f} | {p1[k] / p0[k]:.2f} |")
+    d0, d1 = recs[0]["derived"], recs[1]["derived"]
+    if "lds_bank_conflict_per_lds_active" in d0 and "lds_bank_conflict_per_lds_active" in d1:
+        md.append("| LDS bank conflicts / LDS-active cycles | "
+                  f"{d0['lds_bank_conflict_per_lds_active']:.3f} | "
+                  f"{d1['lds_bank_conflict_per_lds_active']:.3f} | |")
+    t0, t1 = recs[0]["serialized_duration_us"], recs[1]["serialized_duration_us"]
+    md.append(f"| serialized dispatch duration (us) | {t0:.2f} | {t1:.2f} | {t1 / t0:.2f} |")
+    if "sq_busy_ghz" in d0 and "sq_busy_ghz" in d1:
+        md.append(f"| SQ_BUSY_CYCLES / 32 engines / duration (GHz) | {d0['sq_busy_ghz']:.2f} "
+                  f"| {d1['sq_busy_ghz']:.2f} | |")
+    if a.note:
+        md += ["", a.note]
+    md += ["", "Kernel sources hashed (sha256 "
+           f"{recs[0]['kernel_source_sha256'][:16]}...): " + ", ".join(recs[0]["kernel_sources"])]
+    with open(a.out, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(a.out)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="what", required=True)
@@ -308,8 +351,15 @@ def main(argv=None) -> int:
     sub.choices["counters"].add_argument(
         "--match", default=SPLIT,
         help="substring of the kernel name selecting the dispatches (default: the split kernel)")
+    c = sub.add_parser("compare")
+    c.add_argument("--records", nargs=2, required=True, help="two counter records (JSON)")
+    c.add_argument("--labels", nargs=2, required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--note")
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters,
+     "compare": cmd_compare}[a.what](a)
     return 0
 
 

@@ -94,3 +94,28 @@ def test_records_follow_kernel_sources():
     import bench
     assert os.path.basename(bench.KERNEL_SOURCES[0]) == "vq_attention_mfma.hip"
     assert len(bench.kernel_source_digest()) == 64
+
+
+def test_compare_two_counter_records(tmp_path):
+    def rec(path, valu, conflicts, dur, cmd):
+        r = {"kernel": "k", "workload": "w", "score_method": "mfma",
+             "kernel_source_sha256": "ab" * 32, "kernel_sources": ["a.hip"],
+             "dispatches": 3, "serialized_duration_us": dur,
+             "per_dispatch": {"SQ_INSTS_VALU": valu, "SQ_LDS_BANK_CONFLICT": conflicts,
+                              "SQ_LDS_IDX_ACTIVE": 4 * conflicts},
+             "derived": {"lds_bank_conflict_per_lds_active": 0.25}, "commands": [cmd]}
+        path.write_text(json.dumps(r))
+        return str(path)
+
+    a = rec(tmp_path / "a.json", 1000.0, 10.0, 20.0, "run-a")
+    b = rec(tmp_path / "b.json", 3000.0, 50.0, 30.0, "run-b")
+    out = tmp_path / "cmp.md"
+    P.main(["compare", "--records", a, b, "--labels", "A", "B", "--title", "T",
+            "--out", str(out)])
+    text = out.read_text()
+    assert "    run-a" in text and "    run-b" in text
+    assert "| SQ_INSTS_VALU | 1,000 | 3,000 | 3.00 |" in text
+    assert "| SQ_LDS_BANK_CONFLICT | 10 | 50 | 5.00 |" in text
+    assert "| serialized dispatch duration (us) | 20.00 | 30.00 | 1.50 |" in text
+    # counters absent from either record are left out
+    assert "SQ_WAVES" not in text
