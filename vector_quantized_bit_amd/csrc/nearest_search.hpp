@@ -106,8 +106,9 @@ __device__ __forceinline__ float search_pass1(Block block, Cop cup, int b0, int 
 // pass 2: how many of this lane's centroids have s(c) - E(c) <= thr, and the
 // row (16 blk + r, without the lane's 4 (lane / 16)) of the last of them.
 // kSkip: a group of 8 blocks without a hit in the whole wave is skipped after
-// one ballot, which pays where hits are sparse (a wave over 1024 or more
-// centroids) and costs a little where nearly every group has one.
+// one ballot, and within a group only the blocks with a hit in some lane are
+// counted, which pays where hits are sparse (a wave over 1024 or more
+// centroids) and costs a little where nearly every block has one.
 template <bool kSkip, typename Block, typename Cop>
 __device__ __forceinline__ void search_pass2(Block block, Cop cdown, int b0, int b1, float thr,
                                              int& cnt, int& cand) {
@@ -118,19 +119,40 @@ __device__ __forceinline__ void search_pass2(Block block, Cop cdown, int b0, int
         f32x4_t d[kSearchUnroll];
 #pragma unroll
         for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cdown(blk + u));
-        if constexpr (kSkip)
-            if (__builtin_amdgcn_ballot_w64(group_min(d) <= thr) == 0) continue;
         // the group's last hit as u * 4 + r (an inline constant, 0 .. 31),
         // turned into a centroid row once per group
         const int before = cnt;
         int loc = 0;
+        if constexpr (kSkip) {
+            // block minima first; a block is counted only where some lane of
+            // the wave has a hit in it, which changes no lane's count or last hit
+            float m[kSearchUnroll];
+            bool any = false;
 #pragma unroll
-        for (int u = 0; u < kSearchUnroll; ++u) {
+            for (int u = 0; u < kSearchUnroll; ++u) {
+                m[u] = fminf(fminf(d[u][0], d[u][1]), fminf(d[u][2], d[u][3]));
+                any |= m[u] <= thr;
+            }
+            if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool hit = d[u][r] <= thr;
-                loc = hit ? u * 4 + r : loc;
-                cnt += hit ? 1 : 0;
+            for (int u = 0; u < kSearchUnroll; ++u) {
+                if (__builtin_amdgcn_ballot_w64(m[u] <= thr) == 0) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool hit = d[u][r] <= thr;
+                    loc = hit ? u * 4 + r : loc;
+                    cnt += hit ? 1 : 0;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSearchUnroll; ++u) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool hit = d[u][r] <= thr;
+                    loc = hit ? u * 4 + r : loc;
+                    cnt += hit ? 1 : 0;
+                }
             }
         }
         cand = cnt != before ? blk * 16 + (loc >> 2) * 16 + (loc & 3) : cand;
