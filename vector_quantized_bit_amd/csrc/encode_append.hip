@@ -38,29 +38,37 @@ __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
     return static_cast<double>(half_bits_to_float(reinterpret_cast<const uint16_t*>(p)[i]));
 }
 
-// The nearest centroid of sub-vector rb*16 + lane % 16 of `xs` ([8 tokens]
-// [128] fp64 = [256 sub-vectors][4]) among NENT fp16 centroids c16 (the
-// codebook as stored), with the norm terms of hilo_norm_terms at scale sc in
-// nt (float2 [NENT]: upper, lower): fp16 hi/lo matrix-core scores,
+// The nearest centroids of the 16 sub-vectors of each of the NC row blocks
+// rb0 .. rb0 + NC - 1 of `xs` ([8 tokens][128] fp64 = [256 sub-vectors][4])
+// among NENT fp16 centroids c16 (the codebook as stored), with the norm terms
+// of hilo_norm_terms at scale sc in cu / cd: fp16 hi/lo matrix-core scores,
 // certified (nearest_search.hpp), fp64 distances for the few candidates.
-template <int NENT>
-__device__ __forceinline__ uint32_t search_rows(const uint2* c16, const float* cu, const float* cd,
-                                                float sc, const double (*xs)[kHeadDim], int rb,
-                                                int lane) {
-    const double* x = &xs[0][0] + (rb * 16 + (lane & 15)) * 4;
-    double xd[4];
-    float xx = 0.f;
+// Every centroid block's A operand and norm terms are read from LDS once for
+// all NC products; lane l % 16 of row block j gets out[j].
+template <int NENT, int NC>
+__device__ __forceinline__ void search_rows_cols(const uint2* c16, const float* cu,
+                                                 const float* cd, float sc,
+                                                 const double (*xs)[kHeadDim], int rb0, int lane,
+                                                 uint32_t (&out)[NC]) {
+    const double* x0 = &xs[0][0] + (rb0 * 16 + (lane & 15)) * 4;   // row block j at + 64 j
+    BlockD4HN<NC> block;
+    block.arow = c16 + (lane & 15);
+    float ex[NC];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        xd[j] = x[j];
-        const float v = static_cast<float>(x[j]);
-        xx += v * v;
+    for (int j = 0; j < NC; ++j) {
+        const double* x = x0 + 64 * j;
+        block.b[j] = hilo_rows<4, h4_t>(x, lane, sc);
+        float xx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = static_cast<float>(x[i]);
+            xx += v * v;
+        }
+        ex[j] = row_bound_h(xx) * sc;
     }
-    const BlockD4H block(reinterpret_cast<const uint16_t*>(c16), hilo_rows<4, h4_t>(xd, lane, sc),
-                         lane);
     // the distance rounded as the fp64 reference rounds it
-    const auto exact = [&](uint32_t nc) { return sqdist4_f64(xd, c16[nc]); };
-    return nearest16_core<NENT, 4>(cu, cd, block, row_bound_h(xx) * sc, lane, exact);
+    const auto exact = [&](int j, uint32_t nc) { return sqdist4_f64(x0 + 64 * j, c16[nc]); };
+    nearest16_cols<NENT, NC, NC == 1 ? kSearchUnroll : 4>(cu, cd, block, ex, lane, exact, out);
 }
 
 // The largest |2x| over the n values of xs, reduced over the workgroup
@@ -154,14 +162,32 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     }
     __syncthreads();
 
-    // row block jobs: keys then values; sub-vector r = 32 token + position
-    for (int job = wave; job < 2 * kEncBlocks; job += kWv) {
-        const int tt = job / kEncBlocks, rb = job % kEncBlocks;
-        if (rb * 16 >= ntok * kNumSub) continue;   // whole block past the last token
-        const uint32_t cd = tt == 0 ? search_rows<KENT>(kc16, kcu, kcd, ksc, xs[0], rb, lane)
-                                    : search_rows<256>(vc16, vcu, vcd, vsc, xs[1], rb, lane);
+    // jobs of row blocks, keys then values; sub-vector r = 32 token +
+    // position.  A wave searches the blocks of a job together, so the LDS
+    // reads of the tables serve every block of the job.  4096-entry keys keep
+    // one block a job: pairs would leave half of the 16 waves without a key
+    // job (measured 18% slower).
+    constexpr int kPairK = KBITS == 12 ? 1 : 2, kPairV = 2;
+    constexpr int kJobsK = kEncBlocks / kPairK, kJobsV = kEncBlocks / kPairV;
+    const auto put = [&](int tt, int rb, uint32_t cd) {
         const int r = rb * 16 + lane;
         if (lane < 16) code[tt][r >> 5][r & 31] = static_cast<uint16_t>(cd);
+    };
+    for (int job = wave; job < kJobsK + kJobsV; job += kWv) {
+        const bool key = job < kJobsK;
+        const int rb0 = key ? job * kPairK : (job - kJobsK) * kPairV;
+        if (rb0 * 16 >= ntok * kNumSub) continue;   // every block past the last token
+        if (key) {
+            uint32_t cd[kPairK];
+            search_rows_cols<KENT, kPairK>(kc16, kcu, kcd, ksc, xs[0], rb0, lane, cd);
+#pragma unroll
+            for (int j = 0; j < kPairK; ++j) put(0, rb0 + j, cd[j]);
+        } else {
+            uint32_t cd[kPairV];
+            search_rows_cols<256, kPairV>(vc16, vcu, vcd, vsc, xs[1], rb0, lane, cd);
+#pragma unroll
+            for (int j = 0; j < kPairV; ++j) put(1, rb0 + j, cd[j]);
+        }
     }
     __syncthreads();
 
@@ -279,15 +305,19 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
             double xd[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) xd[j] = x[j];
-            const auto exact = [&](uint32_t nc) {
+            const auto exact = [&](int, uint32_t nc) {
                 return sqdist8_f64(xd, reinterpret_cast<const uint4*>(ctab)[nc]);
             };
-            // fp16 hi/lo matrix-core scores in units of the workgroup's 2^s
+            // fp16 hi/lo matrix-core scores in units of the workgroup's 2^s;
+            // groups of 4 blocks, their operands requested before the products
             const float sc = scale[tt];
-            const uint32_t c = nearest16_core<kEnc8Ent, 8>(
-                cu, cd, BlockD8H(ctab, hilo_rows<8, h8_t>(xd, lane, sc), lane),
-                row_bound_h(xx) * sc, lane, exact);
-            if (lane < 16) code[tt][tok][pos] = static_cast<uint16_t>(c);
+            BlockD8HN<1> block;
+            block.arow = reinterpret_cast<const uint4*>(ctab) + (lane & 15);
+            block.b[0] = hilo_rows<8, h8_t>(xd, lane, sc);
+            const float ex[1] = {row_bound_h(xx) * sc};
+            uint32_t c[1];
+            nearest16_cols<kEnc8Ent, 1, 4>(cu, cd, block, ex, lane, exact, c);
+            if (lane < 16) code[tt][tok][pos] = static_cast<uint16_t>(c[0]);
         }
     }
     __syncthreads();

@@ -402,6 +402,17 @@ struct BlockD4HN {
     }
 };
 
+// The same for 8-dim centroids (16-byte entries, v_mfma_f32_16x16x32_f16).
+template <int NC>
+struct BlockD8HN {
+    const uint4* arow;
+    h8_t b[NC];
+    __device__ h8_t a(int blk) const { return __builtin_bit_cast(h8_t, arow[blk * 16]); }
+    __device__ f32x4_t operator()(h8_t a, int j, f32x4_t c) const {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], c, 0, 0, 0);
+    }
+};
+
 // The minimum of a group of U blocks' scores in this lane.
 template <int U>
 __device__ __forceinline__ float group_min_u(const f32x4_t (&d)[U]) {
@@ -499,6 +510,98 @@ __device__ __forceinline__ void search_pass3_cols(const Block& block, Cop cdown,
                 }
             }
         }
+    }
+}
+
+// Pass 2 for NC column blocks (what search_pass2 gives for one, with the
+// same skip rule and kSkip meaning).
+template <bool kSkip, int NC, int U, typename Block, typename Cop>
+__device__ __forceinline__ void search_pass2_cols(const Block& block, Cop cdown, int b0, int b1,
+                                                  const float (&thr)[NC], int (&cnt)[NC],
+                                                  int (&cand)[NC]) {
+    static_assert(U * 4 <= 32, "a group's last hit fits an inline constant");
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        cnt[j] = 0;
+        cand[j] = -1;
+    }
+#pragma nounroll
+    for (int blk = b0; blk < b1; blk += U) {
+        f32x4_t d[NC][U];
+        group_scores<NC, U>(block, cdown, blk, d);
+        float m[NC][U];
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                m[j][u] = fminf(fminf(d[j][u][0], d[j][u][1]), fminf(d[j][u][2], d[j][u][3]));
+                any |= m[j][u] <= thr[j];
+            }
+        if constexpr (kSkip)
+            if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int before = cnt[j];
+            int loc = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if constexpr (kSkip)
+                    if (__builtin_amdgcn_ballot_w64(m[j][u] <= thr[j]) == 0) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool hit = d[j][u][r] <= thr[j];
+                    loc = hit ? u * 4 + r : loc;
+                    cnt[j] += hit ? 1 : 0;
+                }
+            }
+            cand[j] = cnt[j] != before ? blk * 16 + (loc >> 2) * 16 + (loc & 3) : cand[j];
+        }
+    }
+}
+
+// nearest16_core for NC column blocks at once: the block's A operands and
+// norm terms are read once for all NC products.  ex[j] is the bound term and
+// exact(j, c) the fp64 distance of the lane's sub-vector in column block j;
+// out[j] receives its nearest centroid.  U blocks a group (U * NC
+// accumulators of 4 registers stay live).
+template <int NENT, int NC, int U, typename Block, typename Exact>
+__device__ __forceinline__ void nearest16_cols(const float* __restrict__ ccu,
+                                               const float* __restrict__ ccd, const Block& block,
+                                               const float (&ex)[NC], int lane, Exact exact,
+                                               uint32_t (&out)[NC]) {
+    static_assert(NENT % (16 * U) == 0, "whole groups");
+    const int q4 = 4 * (lane >> 4);
+    struct Col {
+        const f32x4_t* p;
+        __device__ f32x4_t operator()(int blk) const { return p[blk * 4]; }
+    };
+    const Col up{reinterpret_cast<const f32x4_t*>(ccu + q4)};
+    const Col down{reinterpret_cast<const f32x4_t*>(ccd + q4)};
+    float thr[NC];
+    search_pass1_cols<NC, U>(block, up, 0, NENT / 16, thr);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        thr[j] = fminf(thr[j], lane_partner<16>(thr[j], lane));
+        thr[j] = fminf(thr[j], lane_partner<32>(thr[j], lane)) + ex[j];
+    }
+    int cnt[NC], cand[NC];
+    search_pass2_cols<(NENT >= 1024), NC, U>(block, down, 0, NENT / 16, thr, cnt, cand);
+    bool several = false;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        cnt[j] = sum_lanes16_32(cnt[j], lane);
+        out[j] = static_cast<uint32_t>(max_lanes16_32(cand[j] < 0 ? -1 : cand[j] + q4, lane));
+        several |= cnt[j] != 1;
+    }
+    if (__builtin_amdgcn_ballot_w64(several) == 0) return;
+    double bd[NC];
+    uint32_t bi[NC];
+    search_pass3_cols<NC, U>(block, down, 0, NENT / 16, thr, q4, exact, bd, bi);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        take_lanes16_32(bd[j], bi[j], lane);
+        out[j] = bi[j];
     }
 }
 
