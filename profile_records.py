@@ -15,6 +15,10 @@ Three reductions, each reading the CSV files that rocprofv3 wrote with
   counters  one or more ``--pmc`` runs of shader counters -> per-dispatch means
             for the split kernel, as JSON (read by bench.py).
   compare   two counter records side by side -> a Markdown table.
+  encoder, calibration
+            the prefill encoder's or the K-Means assignment's launches of a
+            ``--kernel-trace`` run, by grid, with the same run's bench.py
+            figures -> a Markdown summary.
 
 Each record stores the commands given here and a sha256 of the kernel's
 sources; bench.py ignores a record whose hash no longer matches.
@@ -119,6 +123,104 @@ def loop_table(loops) -> list[str]:
     return lines
 
 
+def grid_groups(trace: list[dict], sub: str) -> list:
+    """Launch durations (us) of the kernels whose name contains `sub`, by
+    (short name, grid in workgroups), longest average first."""
+    groups: dict = collections.defaultdict(list)
+    for r in trace:
+        if sub in r["Kernel_Name"]:
+            grid = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+                    int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+            groups[(short_name(r["Kernel_Name"]), grid)].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return sorted(groups.items(), key=lambda kv: -st.mean(kv[1]))
+
+
+def bench_line(path: str) -> dict:
+    """The JSON line bench.py printed into a log."""
+    with open(path) as f:
+        lines = [ln for ln in f if ln.startswith('{"metric"')]
+    if not lines:
+        raise SystemExit(f"no bench.py line in {path}")
+    return json.loads(lines[-1])
+
+
+def _header(title: str, command: str, reduced: str) -> list[str]:
+    return [f"# Kernel trace summary: {title}", "",
+            "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`; the",
+            "library built in-tree):", "", f"    {command}", "",
+            "Reduced by:", "", f"    {reduced}", ""]
+
+
+def cmd_encoder(a) -> None:
+    """The prefill encoder's launches in a bench.py run (by grid), with the
+    same run's bench.py figures, and the other layouts' prefill launches."""
+    trace = _csv(os.path.join(a.dir, f"{a.prefix}_kernel_trace.csv"))
+    line = bench_line(a.log)
+    pe, ae = line["prefill_encode"], line["append_encode"]
+    out = _header(a.title, a.command,
+                  f"python profile_records.py encoder --dir {a.dir} --log {a.log} "
+                  f"--others ... --out {a.out} --command '...'")
+    out += ["bench.py's `prefill_encode` section times one `vq_encode_append` call over a",
+            f"{pe['tokens']}-token prompt for every KV head of the layer (fp16 K and V, "
+            f"`{pe['roofline']['kernel']}`): warm-up and timed launches back to back. The",
+            "64-token append and the residual-window flushes launch the same kernel.", "",
+            "| kernel | grid (workgroups) | launches | avg us | min us | max us |",
+            "|---|---|---|---|---|---|"]
+    for (name, grid), d in grid_groups(trace, "encode_append"):
+        out.append(f"| {name} | {grid[0]} x {grid[1]} x {grid[2]} | {len(d)} | "
+                   f"{st.mean(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+    r = pe["roofline"]
+    out += ["", "The same run's bench.py line (HIP events around the back-to-back launches):",
+            f"{pe['avg_launch_us']:.1f} us per prefill launch, {pe['tokens_per_s']:.3g} prompt "
+            f"tokens/s, {r['achieved']:.1f} TFLOP/s of one dense distance pass (8 flops per",
+            f"sub-vector/centroid pair at d = 4) = {100 * r['frac']:.1f}% of the "
+            f"{r['peak']} TFLOP/s fp32 matrix peak; 64-token append {ae['avg_launch_us']:.1f} us."]
+    if a.others:
+        out += ["", "The other layouts' prefill launches, from their own runs under the same "
+                "profiler:", "", "| run | kernel | grid (workgroups) | launches | avg us |",
+                "|---|---|---|---|---|"]
+        for d in a.others:
+            t = _csv(os.path.join(d, f"{a.prefix}_kernel_trace.csv"))
+            groups = grid_groups(t, "encode_append")
+            if groups:
+                (name, grid), dur = groups[0]   # the longest: the prefill
+                out.append(f"| {d} | {name} | {grid[0]} x {grid[1]} x {grid[2]} | {len(dur)} | "
+                           f"{st.mean(dur):.1f} |")
+    with open(a.out, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(a.out)
+
+
+def cmd_calibration(a) -> None:
+    """The K-Means assignment launches of a bench.py run (by grid) with the
+    same run's calibration figures."""
+    trace = _csv(os.path.join(a.dir, f"{a.prefix}_kernel_trace.csv"))
+    cal = bench_line(a.log)["calibration"]
+    out = _header(a.title, a.command,
+                  f"python profile_records.py calibration --dir {a.dir} --log {a.log} "
+                  f"--out {a.out} --command '...'")
+    out += ["bench.py's `calibration` section: lambda and K~ over the calibration tokens, then "
+            "Lloyd K-Means iterations on every codebook's sub-vectors (every KV head a set).", "",
+            "| kernel | grid (workgroups) | launches | avg us | min us | max us |",
+            "|---|---|---|---|---|---|"]
+    for (name, grid), d in grid_groups(trace, "kmeans_assign"):
+        out.append(f"| {name} | {grid[0]} x {grid[1]} x {grid[2]} | {len(d)} | "
+                   f"{st.mean(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+    out += ["", "The same run's bench.py line (HIP events around whole calls):", "",
+            f"- lambda: {cal['lambda_us']:.1f} us ({cal['lambda_gbps']:.0f} GB/s); K~: "
+            f"{cal['transform_keys_us']:.1f} us ({cal['transform_keys_gbps']:.0f} GB/s)."]
+    for name, k in cal["kmeans"].items():
+        out.append(f"- K-Means {name}: {k['us_per_iter']:.0f} us per Lloyd iteration over "
+                   f"{k['sets']} x {k['samples_per_set']} samples (d = {k['sub_dim']}), "
+                   f"{k['entries']} centroids; one dense distance pass per iteration = "
+                   f"{k['dense_pass_tflops']:.1f} TFLOP/s "
+                   f"({100 * k['frac_of_mfma_f32_peak']:.1f}% of the fp32 matrix peak).")
+    with open(a.out, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(a.out)
+
+
 def cmd_trace(a) -> None:
     stats = _csv(os.path.join(a.dir, f"{a.prefix}_kernel_stats.csv"))
     trace = _csv(os.path.join(a.dir, f"{a.prefix}_kernel_trace.csv"))
@@ -142,14 +244,7 @@ def cmd_trace(a) -> None:
     for sub in a.breakdown or []:
         out += ["", f"Launches of kernels matching `{sub}` by grid size (workgroups):", "",
                 "| kernel | grid | launches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
-        groups: dict = collections.defaultdict(list)
-        for r in trace:
-            if sub in r["Kernel_Name"]:
-                grid = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
-                        int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
-                groups[(short_name(r["Kernel_Name"]), grid)].append(
-                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        for (name, grid), d in sorted(groups.items(), key=lambda kv: -st.mean(kv[1])):
+        for (name, grid), d in grid_groups(trace, sub):
             out.append(f"| {name} | {grid[0]} x {grid[1]} x {grid[2]} | {len(d)} | "
                        f"{st.mean(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
     if a.note:
@@ -351,6 +446,16 @@ def main(argv=None) -> int:
     sub.choices["counters"].add_argument(
         "--match", default=SPLIT,
         help="substring of the kernel name selecting the dispatches (default: the split kernel)")
+    for name in ("encoder", "calibration"):
+        e = sub.add_parser(name)
+        e.add_argument("--dir", required=True, help="rocprofv3 --kernel-trace output")
+        e.add_argument("--prefix", default="trace")
+        e.add_argument("--log", required=True, help="the same run's bench.py output")
+        e.add_argument("--command", required=True)
+        e.add_argument("--title", required=True)
+        e.add_argument("--out", required=True)
+    sub.choices["encoder"].add_argument("--others", nargs="*",
+                                        help="trace directories of the other layouts' runs")
     c = sub.add_parser("compare")
     c.add_argument("--records", nargs=2, required=True, help="two counter records (JSON)")
     c.add_argument("--labels", nargs=2, required=True)
@@ -359,7 +464,7 @@ def main(argv=None) -> int:
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters,
-     "compare": cmd_compare}[a.what](a)
+     "compare": cmd_compare, "encoder": cmd_encoder, "calibration": cmd_calibration}[a.what](a)
     return 0
 
 

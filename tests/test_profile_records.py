@@ -119,3 +119,42 @@ def test_compare_two_counter_records(tmp_path):
     assert "| serialized dispatch duration (us) | 20.00 | 30.00 | 1.50 |" in text
     # counters absent from either record are left out
     assert "SQ_WAVES" not in text
+
+
+def test_encoder_and_calibration_records(tmp_path):
+    enc = "void vqkv::encode_append_kernel<8>(int) [clone .kd]"
+    asg = "void vqkv::kmeans_assign_kernel<256>(int) [clone .kd]"
+    hdr = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
+           "Grid_Size_Z", "Workgroup_Size_X"]
+    # prefill launches (4096 workgroups of 512 threads) and short appends (8)
+    rows = [[enc, 0, 1000000, 4096 * 512, 8, 1, 512], [enc, 2000000, 3100000, 4096 * 512, 8, 1, 512],
+            [enc, 4000000, 4015000, 8 * 512, 8, 1, 512],
+            [asg, 5000000, 7000000, 512 * 256, 8, 1, 256]]
+    _write(tmp_path / "t_kernel_trace.csv", hdr, rows)
+    line = {"metric": "m",
+            "prefill_encode": {"tokens": 32768, "avg_launch_us": 1050.0, "tokens_per_s": 3.1e7,
+                               "roofline": {"kernel": "encode_append_kernel", "achieved": 32.7,
+                                            "peak": 157.3, "frac": 0.208}},
+            "append_encode": {"avg_launch_us": 15.0},
+            "calibration": {"lambda_us": 50.0, "lambda_gbps": 5000.0, "transform_keys_us": 360.0,
+                            "transform_keys_gbps": 2200.0,
+                            "kmeans": {"k8": {"us_per_iter": 3200.0, "sets": 8,
+                                              "samples_per_set": 4194304, "sub_dim": 4,
+                                              "entries": 256, "dense_pass_tflops": 21.5,
+                                              "frac_of_mfma_f32_peak": 0.137}}}}
+    log = tmp_path / "bench.log"
+    log.write_text("noise\n" + json.dumps(line) + "\n")
+    out = tmp_path / "enc.md"
+    P.main(["encoder", "--dir", str(tmp_path), "--prefix", "t", "--log", str(log),
+            "--command", "cmd", "--title", "T", "--out", str(out)])
+    text = out.read_text()
+    # the two prefill launches (1000 and 1100 us) group by grid; the append separately
+    assert "| vqkv::encode_append_kernel<8> | 4096 x 8 x 1 | 2 | 1050.0 | 1000.0 | 1100.0 |" in text
+    assert "| vqkv::encode_append_kernel<8> | 8 x 8 x 1 | 1 | 15.0 |" in text
+    assert "1050.0 us per prefill launch" in text and "20.8% of the 157.3" in text
+    out = tmp_path / "cal.md"
+    P.main(["calibration", "--dir", str(tmp_path), "--prefix", "t", "--log", str(log),
+            "--command", "cmd", "--title", "T", "--out", str(out)])
+    text = out.read_text()
+    assert "| vqkv::kmeans_assign_kernel<256> | 512 x 8 x 1 | 1 | 2000.0 |" in text
+    assert "- K-Means k8: 3200 us per Lloyd iteration" in text
