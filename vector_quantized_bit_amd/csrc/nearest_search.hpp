@@ -69,7 +69,7 @@ __device__ __forceinline__ float row_bound(float xx) { return 2.f * (0x1p-16f * 
 // group, which holds no cross-lane operation.
 //
 // The encoders and the one-token searches of the decode step use the fp16
-// hi/lo form below (BlockD4H, BlockD8H): the centroids enter the matrix
+// hi/lo form below (BlockD4HN, BlockD8HN, BlockD8H): the centroids enter the matrix
 // cores as the codebook stores them (fp16) and the sub-vector as a scaled
 // hi/lo fp16 pair, with their own certified bound (2^-15).  The fp32 form
 // above remains in K-Means (BlockF32D8 for 8-dim samples).
@@ -361,37 +361,14 @@ __device__ __forceinline__ HiLoD8 hilo_d8(const double* x, int lane) {
     return {hilo_rows<8, h8_t>(x, lane, sc), sc};
 }
 
-// The same for 4-dim sub-vectors (v_mfma_f32_16x16x16_f16: lane groups 0
-// and 1 carry hi and lo of the 4 channels, groups 2 and 3 zeros).
+// 4-dim sub-vectors use v_mfma_f32_16x16x16_f16: lane groups 0 and 1 carry
+// hi and lo of the 4 channels, groups 2 and 3 zeros.
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-struct HiLoD4 {
-    h4_t b;
-    float scale;
-};
-__device__ __forceinline__ HiLoD4 hilo_d4(const double* x, int lane) {
-    float mx = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(-2.f * static_cast<float>(x[j])));
-    const float sc = hilo_scale(mx);
-    return {hilo_rows<4, h4_t>(x, lane, sc), sc};
-}
 
-// Block scores for 4-dim sub-vectors: ctab [.][4] fp16 centroids (8 bytes
-// each, the codebook's own layout).
-struct BlockD4H {
-    const uint2* arow;
-    h4_t b;
-    __device__ BlockD4H(const uint16_t* ctab, h4_t b_, int lane)
-        : arow(reinterpret_cast<const uint2*>(ctab) + (lane & 15)), b(b_) {}
-    __device__ f32x4_t operator()(int blk, f32x4_t c) const {
-        const h4_t a = __builtin_bit_cast(h4_t, arow[blk * 16]);
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-    }
-};
-
-// NC column blocks (16 sub-vectors each) against the same 4-dim centroids:
-// one A operand and one set of norm terms per centroid block feed all NC
-// products.
+// Block scores of NC column blocks (16 sub-vectors each) against 4-dim fp16
+// centroids as the codebook stores them (8 bytes an entry; arow = the table
+// + lane % 16): one A operand and one set of norm terms per centroid block
+// feed all NC products.
 template <int NC>
 struct BlockD4HN {
     const uint2* arow;

@@ -451,14 +451,14 @@ __device__ __forceinline__ void new_token_codes12(const Codes12Tables& tabs, uin
 //     ties to the lowest index: the decisions of vq_encode_append.  For a
 //     256-entry codebook thread (slice, pos) scans centroids slice,
 //     slice + 32, ... of sub-vector pos, and the 32 slices are combined by
-//     the lexicographic (distance, index) minimum; 12-bit keys take the
-//     matrix-core search of new_token_keys12.  The codes are written to the
-//     cache slot append_pos.
+//     the lexicographic (distance, index) minimum.  With 12-bit keys both
+//     tensors take the matrix-core search of new_token_codes12.  The codes
+//     are written to the cache slot append_pos.
 //  2. Its attention partial, as one more split of one token: m = x (its
 //     base-2 score), l = 1, o = its dequantised value, at split index `slot`.
-// LDS: the codebooks unreplicated in `tab` (keys at 0, values at 32 KiB; for
-// 12-bit keys the tables of stage_keys12), the scratch of the combination in
-// `scratch` (the p buffers).
+// LDS: the codebooks unreplicated in `tab` (keys at 0, values at 32 KiB; with
+// 12-bit keys the tables and exchanges of new_token_codes12), the scratch of
+// the 256-entry scans' combination in `scratch` (the p buffers).
 template <int G, int KBITS>
 __device__ __forceinline__ void new_token_workgroup(
     const void* q, int q_f32, const float* lambda, const uint16_t* cb_k, const uint16_t* cb_v,
