@@ -412,11 +412,12 @@ def test_decode_step_window_plan(lib):
     # coded tokens split as in a decode step, plus the window's partial
     assert np_(ctypes.byref(layout), 1, 32, 196608, 0) == \
         lib.vq_decode_step_num_partials(ctypes.byref(layout), 1, 32, 196608, 0) == 32
-    # 64 streams: a decode step folds its new token (four splits per stream
-    # over all 256 CUs), a window step keeps 192 split workgroups (3 per
-    # stream) beside its 64 window workgroups
-    assert np_(ctypes.byref(layout), 8, 32, 65535, 0) == 4
+    # 64 streams: a decode step folds its new token and a window step its
+    # window (four splits per stream over all 256 CUs, plus that partial)
+    assert np_(ctypes.byref(layout), 8, 32, 65535, 0) == 5
     assert lib.vq_decode_step_num_partials(ctypes.byref(layout), 8, 32, 65535, 0) == 5
+    # 32 streams: the window workgroups run beside 224 split workgroups
+    assert np_(ctypes.byref(layout), 4, 32, 65535, 0) == 8
     # 128 streams: two splits per stream either way (folded window)
     assert np_(ctypes.byref(layout), 16, 32, 32767, 0) == 3
     # no coded tokens: the window workgroup alone, one partial

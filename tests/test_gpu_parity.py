@@ -652,10 +652,11 @@ def test_decode_step_window_folded_groups_widths(group, k_bits):
 
 @pytest.mark.parametrize("win_cap,win_len,num_codes,streams", [
     (16, 15, 700, 4), (16, 0, 0, 4), (256, 200, 3000, 4), (256, 255, 20000, 128),
-    (1, 0, 513, 4)])
+    (1, 0, 513, 4), (512, 300, 2000, 4), (512, 511, 20000, 128)])
 def test_decode_step_window_capacities(win_cap, win_len, num_codes, streams):
-    # windows other than 128 slots: the smallest, one slot, and a larger one,
-    # beside the splits and folded into them (128 streams)
+    # windows other than 128 slots: the smallest, one slot, and larger ones,
+    # beside the splits and folded into them (128 streams); past 256 tokens
+    # waves take a second block and the new token is in a later block
     bsz = streams // 2
     wl = W.Workload(92, "adhoc", batch=bsz, num_q_heads=8, num_kv_heads=2,
                     context_len=max(num_codes, 1))

@@ -736,186 +736,283 @@ __device__ __forceinline__ float group_sum(float v, int lane) {
 //  1. The new token's k and v, rounded to fp16, go to window slot win_len.
 //  2. The G query heads attend over window tokens 0 .. win_len with raw
 //     keys: q . k / sqrt(D), which equals q~ . k~ (H_D orthonormal), so the
-//     window needs no transform.  Wave w takes tokens 2w, 2w + 1, then
-//     2w + 32, 2w + 33, ...: each half of the wave (32 lanes, 4 channels per
-//     lane) keeps an online softmax per head over its tokens, and the two
-//     halves combine before the fold.
-//  3. The 16 wave states fold in LDS into one partial (m, l, o) at split
-//     index `slot`, in the base-2 units of the code splits.
+//     window needs no transform.  Wave w takes 16-token blocks w, w + 16, ...
+//     on the matrix cores: scores from the heads' q (fp16 as given; fp32 as
+//     fp16 hi and lo rows with one power-of-two scale per head, undone after
+//     the product) against the window's key rows, an online softmax per
+//     head, and the weights as fp16 hi and lo (times 2^16) rows against the
+//     block's value rows staged in LDS.  Slot win_len holds the new token,
+//     taken from k_new / v_new (the lanes that load it store it); slots past
+//     win_len are masked.  Waves past the last block
+//     (all but 8 for a 128-token window) do no work.
+//  3. The states of the waves with tokens fold in LDS into one partial
+//     (m, l, o) at split index `slot`, in the base-2 units of the code
+//     splits.
+// LDS (`lds`, the 128 KiB of the codebook tables): per wave 16 value rows at
+// a stride of 136 halves (which afterwards hold the wave's G x 128 outputs),
+// the waves' m and l, per wave a 16 x 16 fp16 weight tile and 8 head scales.
 template <int G>
 __device__ __forceinline__ void window_workgroup(
     const void* q, int q_f32, const void* k_new, const void* v_new, int kv_f32, int num_q_heads,
     int num_kv_heads, int g, int b, uint16_t* win_k, uint16_t* win_v, int win_len, int win_cap,
     Partials part, int part_stride, int slot, float* lds) {
+    static_assert(G >= 1 && G <= 8, "2 G rows of one 16-row product");
     constexpr float kScale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
     constexpr int kWords = kHeadDim / 2;                                  // fp16 pairs per row
+    constexpr int kVs = kHeadDim + 8;                                     // staged value row stride
+    constexpr int kWaveBytes = 16 * kVs * 2;                              // 4352
+    static_assert(G * kHeadDim * 4 <= kWaveBytes, "a wave's outputs fit its staging rows");
+    constexpr int kFm = kWaves * kWaveBytes, kPt = kFm + 2 * kWaves * 8 * 4,
+                  kSc = kPt + kWaves * 16 * 16 * 2, kEnd = kSc + kWaves * 8 * 4;
+    static_assert(kEnd <= 2 * kTable, "the window's LDS fits the tables");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, n = lane & 15;
     const size_t stream = static_cast<size_t>(b) * num_kv_heads + g;
-    uint32_t* wk = reinterpret_cast<uint32_t*>(win_k) + stream * win_cap * kWords;
-    uint32_t* wv = reinterpret_cast<uint32_t*>(win_v) + stream * win_cap * kWords;
+    const uint16_t* wk = win_k + stream * win_cap * kHeadDim;
+    const uint16_t* wv = win_v + stream * win_cap * kHeadDim;
+    uint8_t* base = reinterpret_cast<uint8_t*>(lds);
+    uint16_t* vst = reinterpret_cast<uint16_t*>(base + wave * kWaveBytes);
+    float* fm = reinterpret_cast<float*>(base + kFm);   // [kWaves][8] m, then [kWaves][8] l
+    float* fl = fm + kWaves * 8;
+    uint16_t* pt = reinterpret_cast<uint16_t*>(base + kPt) + wave * 256;   // [16 rows][16 tokens]
+    float* sinv = reinterpret_cast<float*>(base + kSc) + wave * 8;         // 2^-e per head
 
     // the new token as the window stores it (fp16, round to nearest even),
-    // written to slot win_len by wave 0, two channels per lane
-    uint32_t kn, vn;
-    if (kv_f32) {
-        const float2 a = reinterpret_cast<const float2*>(k_new)[stream * kWords + lane];
-        const float2 c = reinterpret_cast<const float2*>(v_new)[stream * kWords + lane];
-        kn = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(a.x), static_cast<_Float16>(a.y)});
-        vn = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(c.x), static_cast<_Float16>(c.y)});
-    } else {
-        kn = reinterpret_cast<const uint32_t*>(k_new)[stream * kWords + lane];
-        vn = reinterpret_cast<const uint32_t*>(v_new)[stream * kWords + lane];
-    }
-    if (wave == 0) {
-        wk[static_cast<size_t>(win_len) * kWords + lane] = kn;
-        wv[static_cast<size_t>(win_len) * kWords + lane] = vn;
-    }
-
-    // A wave takes kGrp tokens at a time, one per group of kGl lanes; lane
-    // `sub` of a group holds channels kDl sub .. kDl sub + kDl - 1, so a score
-    // is kDl products and a reduction over the group's lanes.  Heads go in
-    // passes of at most 4 (the registers of one pass stay below those of the
-    // split path).
-    constexpr int kGrp = 2;
-    constexpr int kGl = kWave / kGrp;
-    constexpr int kDl = kHeadDim / kGl;   // channels per lane
-    constexpr int kDw = kDl / 2;          // fp16 pairs per lane
-    constexpr int kGh = G < 4 ? G : 4;    // heads per pass
-    const int grp = lane / kGl, sub = lane % kGl;
-    uint32_t knd[kDw], vnd[kDw];   // the new token in this lane's channels
-#pragma unroll
-    for (int j = 0; j < kDw; ++j) {
-        const size_t w = stream * kWords + sub * kDw + j;
+    // two channels
+    const auto new_pair = [&](const void* src, int c2) {   // channels 2 c2, 2 c2 + 1
         if (kv_f32) {
-            const float2 a = reinterpret_cast<const float2*>(k_new)[w];
-            const float2 c = reinterpret_cast<const float2*>(v_new)[w];
-            knd[j] = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(a.x), static_cast<_Float16>(a.y)});
-            vnd[j] = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(c.x), static_cast<_Float16>(c.y)});
+            const float2 a = reinterpret_cast<const float2*>(src)[stream * kWords + c2];
+            return __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(a.x),
+                                                        static_cast<_Float16>(a.y)});
+        }
+        return reinterpret_cast<const uint32_t*>(src)[stream * kWords + c2];
+    };
+    // 16 bytes of window row `row` (slot win_len and beyond: the new token)
+    const auto row16 = [&](const uint16_t* win, const void* src, int row, int c0) {
+        if (row < win_len)
+            return *reinterpret_cast<const uint4*>(win + static_cast<size_t>(row) * kHeadDim + c0);
+        return make_uint4(new_pair(src, c0 / 2), new_pair(src, c0 / 2 + 1), new_pair(src, c0 / 2 + 2),
+                          new_pair(src, c0 / 2 + 3));
+    };
+    // waves past the window's last block hold no tokens: they skip to the
+    // fold, which reads the first nw states only
+    const int nw = min(kWaves, win_len / 16 + 1);
+    if (wave < nw) {
+        // a block's rows in registers: the key B operands of lane (16 grp + n)
+        // (token 16 blk + n, channels 32 kk + 8 grp .. + 7) and the value rows
+        // lane l copies to LDS (token l / 4, channels 32 (l % 4) + 8 j .. + 7);
+        // the wave's first block is requested before the query, so the two
+        // memory latencies overlap
+        uint4 kb[4], vb[4];
+        const int tk = 16 * wave + n, tv = 16 * wave + (lane >> 2);
+        if (!kv_f32) {   // fp16 new token: one load per operand, no branch
+            const uint16_t* rk = tk < win_len ? wk + static_cast<size_t>(tk) * kHeadDim
+                                              : static_cast<const uint16_t*>(k_new) + stream * kHeadDim;
+            const uint16_t* rv = tv < win_len ? wv + static_cast<size_t>(tv) * kHeadDim
+                                              : static_cast<const uint16_t*>(v_new) + stream * kHeadDim;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kb[kk] = *reinterpret_cast<const uint4*>(rk + 32 * kk + 8 * grp);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                vb[j] = *reinterpret_cast<const uint4*>(rv + 32 * (lane & 3) + 8 * j);
         } else {
-            knd[j] = reinterpret_cast<const uint32_t*>(k_new)[w];
-            vnd[j] = reinterpret_cast<const uint32_t*>(v_new)[w];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) kb[kk] = row16(wk, k_new, tk, 32 * kk + 8 * grp);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vb[j] = row16(wv, v_new, tv, 32 * (lane & 3) + 8 * j);
         }
-    }
-    float* fm = lds;   // fold: LDS m, l [kWaves][G] and o [kWaves][G][128]
-    float* fl = fm + kWaves * G;
-    float* fo = fl + kWaves * G;
-    constexpr int kStep = kWaves * kGrp;
-    const int last_row = win_len > 0 ? win_len - 1 : 0;
+
+        // score A operands: lane (16 grp + r) holds row r (head r % 8, hi for
+        // r < 8, lo after) at channels 32 kk + 8 grp .. + 7.  An fp16 query is
+        // its own hi row (lo rows zero, products exact in fp32); an fp32 one
+        // is scaled by 2^e per head (its largest |q| to [2^14, 2^15)) and
+        // split into fp16 hi and lo, the scale undone after the product.
+        // inv[r]: the factor from a score row to log2 units
+        const int hr = n & 7;
+        const bool hi_row = n < 8, live_row = hr < G;
+        const size_t qrow =
+            (static_cast<size_t>(b) * num_q_heads + g * G + min(hr, G - 1)) * kHeadDim + 8 * grp;
+        // output rows of lane (16 grp + n): 4 grp + r, head hq + r (hi rows in
+        // groups 0 and 1, lo rows in 2 and 3)
+        const int hq = 4 * (grp & 1);
+        half8_t aq[4];
+        float inv[4];
+        if (!q_f32) {
+            const uint16_t* qh = static_cast<const uint16_t*>(q) + qrow;
 #pragma unroll
-    for (int h0 = 0; h0 < G; h0 += kGh) {
-        constexpr int kN = kGh;
-        float qd[kN][kDl];   // the raw query of each head of the pass, scaled to base-2 scores
-        float m[kN], l[kN], o[kN][kDl];
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint4 u = *reinterpret_cast<const uint4*>(qh + 32 * kk);
+                aq[kk] = __builtin_bit_cast(half8_t, (hi_row && live_row) ? u : make_uint4(0, 0, 0, 0));
+            }
 #pragma unroll
-        for (int hh = 0; hh < kN; ++hh) {
-            m[hh] = -INFINITY;
-            l[hh] = 0.f;
+            for (int r = 0; r < 4; ++r) inv[r] = kScale;
+        } else {
+            // all of the lane's query words are requested before any is used
+            const float* qf = static_cast<const float*>(q) + qrow;
+            float qv[4][8];
 #pragma unroll
-            for (int j = 0; j < kDl; ++j) o[hh][j] = qd[hh][j] = 0.f;
-            if (h0 + hh >= G) continue;
-            const size_t vec = static_cast<size_t>(b) * num_q_heads + g * G + h0 + hh;
+            for (int kk = 0; kk < 4; ++kk) {
+                const float4 u = *reinterpret_cast<const float4*>(qf + 32 * kk);
+                const float4 v = *reinterpret_cast<const float4*>(qf + 32 * kk + 4);
+                const float t[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int j = 0; j < kDw; ++j) {
-                const size_t w = vec * kWords + sub * kDw + j;
-                if (q_f32) {
-                    const float2 f = reinterpret_cast<const float2*>(q)[w];
-                    qd[hh][2 * j] = f.x * kScale;
-                    qd[hh][2 * j + 1] = f.y * kScale;
-                } else {
-                    const uint32_t x = reinterpret_cast<const uint32_t*>(q)[w];
-                    qd[hh][2 * j] = half_bits_to_float(x & 0xffffu) * kScale;
-                    qd[hh][2 * j + 1] = half_bits_to_float(x >> 16) * kScale;
+                for (int j = 0; j < 8; ++j) qv[kk][j] = t[j];
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(qv[kk][j]));
+            // the 8 lanes of a head: n and n ^ 8, in every lane group
+            amax = fmaxf(amax, lane_partner<8>(amax, lane));
+            amax = fmaxf(amax, lane_partner<16>(amax, lane));
+            amax = fmaxf(amax, lane_partner<32>(amax, lane));
+            const int ex = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);
+            if (lane < 8) sinv[lane] = __builtin_amdgcn_ldexpf(kScale, -ex);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float x = __builtin_amdgcn_ldexpf(qv[kk][j], ex);
+                    const _Float16 h = static_cast<_Float16>(x);
+                    const _Float16 l = static_cast<_Float16>(x - static_cast<float>(h));
+                    aq[kk][j] = live_row ? (hi_row ? h : l) : static_cast<_Float16>(0.f);
                 }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int r = 0; r < 4; ++r) inv[r] = sinv[hq + r];
+        }
+
+        float m[4], l[4];
+        float4_t o[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            m[r] = -INFINITY;
+            l[r] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+        // one block; kPre: its rows are in kb / vb, else they are loaded here
+        const auto block = [&](int blk, auto pre) {
+            constexpr bool kPre = decltype(pre)::value;
+            // the block's value rows into this wave's LDS rows; in a wave's
+            // first block the lanes that hold the new token's fp16 k and v
+            // also store them to window slot win_len
+            uint16_t* slot_k = win_k + (stream * win_cap + win_len) * kHeadDim;
+            uint16_t* slot_v = win_v + (stream * win_cap + win_len) * kHeadDim;
+            const int tv = 16 * blk + (lane >> 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c0 = 32 * (lane & 3) + 8 * j;
+                const uint4 vr = kPre ? vb[j] : row16(wv, v_new, tv, c0);
+                *reinterpret_cast<uint4*>(vst + (lane >> 2) * kVs + c0) = vr;
+                if (kPre && tv == win_len) *reinterpret_cast<uint4*>(slot_v + c0) = vr;
+            }
+            // scores of token t = 16 blk + n
+            const int t = 16 * blk + n;
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int c0 = 32 * kk + 8 * grp;
+                const uint4 kr = kPre ? kb[kk] : row16(wk, k_new, t, c0);
+                if (kPre && t == win_len) *reinterpret_cast<uint4*>(slot_k + c0) = kr;
+                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[kk], __builtin_bit_cast(half8_t, kr), s,
+                                                           0, 0, 0);
+            }
+            // hi + lo rows: every lane then holds heads hq .. hq + 3 of token n
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = s[r] + lane_partner<32>(s[r], lane);
+                x[r] = t <= win_len ? v * inv[r] : -INFINITY;
+            }
+            float f[4], pv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float mn = fmaxf(m[r], row_max16(x[r]));   // finite: token 16 blk is live
+                f[r] = (m[r] == -INFINITY) ? 0.f : fast_exp2(m[r] - mn);
+                pv[r] = fast_exp2(x[r] - mn);
+                l[r] = l[r] * f[r] + pv[r];
+                m[r] = mn;
+            }
+            // weights tile: row 4 grp + r, column n; hi parts round toward zero,
+            // lo = (p - hi) 2^16 (groups 2 and 3)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const _Float16 ph =
+                    __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv[r], 0.f))[0];
+                const _Float16 pl = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(
+                                        (pv[r] - static_cast<float>(ph)) * kLoScale, 0.f))[0];
+                pt[(4 * grp + r) * 16 + n] = __builtin_bit_cast(uint16_t, grp < 2 ? ph : pl);
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[c][r] *= f[r];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // value product: A = weight rows (tokens 4 grp .. + 3), B = value
+            // rows of the same tokens at channel 16 c + n
+            const half4_t ap = *reinterpret_cast<const half4_t*>(pt + n * 16 + 4 * grp);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                half4_t bv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bv[j] = __builtin_bit_cast(_Float16, vst[(4 * grp + j) * kVs + 16 * c + n]);
+                o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap, bv, o[c], 0, 0, 0);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+        block(wave, std::true_type{});
+        for (int blk = wave + kWaves; 16 * blk <= win_len; blk += kWaves)
+            block(blk, std::false_type{});
+        // past the first blocks (windows over 256 tokens) wave 0 stores the
+        // new token, two channels per lane
+        if (win_len >= 16 * kWaves && wave == 0) {
+            reinterpret_cast<uint32_t*>(win_k)[(stream * win_cap + win_len) * kWords + lane] =
+                new_pair(k_new, lane);
+            reinterpret_cast<uint32_t*>(win_v)[(stream * win_cap + win_len) * kWords + lane] =
+                new_pair(v_new, lane);
+        }
+        // the wave's state: l summed over its lanes' tokens, o = hi + lo 2^-16
+        // rows (lanes 0-31), into its staging rows and the m / l arrays
+        float* fo = reinterpret_cast<float*>(vst);   // [G][128]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ls = row_sum16(l[r]);
+            const int h = hq + r;
+            if (lane < 32 && n == 0 && h < G) {
+                fm[wave * 8 + h] = m[r];
+                fl[wave * 8 + h] = ls;
             }
         }
-        // kGrp tokens per step, the rows of kPre steps loaded before any is
-        // used: one memory latency per kPre steps, which matters when the
-        // window runs beside splits that load the chip (the clamped slot keeps
-        // every load in the window and unconditional)
-        constexpr int kPre = 4;
-        for (int t00 = wave * kGrp; t00 <= win_len; t00 += kPre * kStep) {
-          uint32_t kr[kPre][kDw], vr[kPre][kDw];
 #pragma unroll
-          for (int u = 0; u < kPre; ++u) {
-            const size_t r =
-                static_cast<size_t>(min(t00 + u * kStep + grp, last_row)) * kWords + sub * kDw;
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int j = 0; j < kDw; ++j) {
-                kr[u][j] = wk[r + j];
-                vr[u][j] = wv[r + j];
+            for (int r = 0; r < 4; ++r) {
+                const float v = fmaf(lane_partner<32>(o[c][r], lane), kLoUnscale, o[c][r]);
+                if (lane < 32 && hq + r < G) fo[(hq + r) * kHeadDim + 16 * c + n] = v;
             }
-          }
-#pragma unroll
-          for (int u = 0; u < kPre; ++u) {
-            const int t0 = t00 + u * kStep;
-            if (t0 > win_len) break;   // uniform in the wave
-            const int t = t0 + grp;
-            const bool valid = t <= win_len;
-            uint32_t kw[kDw], vw[kDw];
-#pragma unroll
-            for (int j = 0; j < kDw; ++j) {   // slot win_len: the new token, from registers
-                kw[j] = t == win_len ? knd[j] : kr[u][j];
-                vw[j] = t == win_len ? vnd[j] : vr[u][j];
-            }
-            float sc[kN];
-#pragma unroll
-            for (int hh = 0; hh < kN; ++hh) {
-                float acc = 0.f;
-#pragma unroll
-                for (int j = 0; j < kDw; ++j) {
-                    acc += qd[hh][2 * j] * half_bits_to_float(kw[j] & 0xffffu);
-                    acc += qd[hh][2 * j + 1] * half_bits_to_float(kw[j] >> 16);
-                }
-                sc[hh] = group_sum<kGl>(acc, lane);
-            }
-#pragma unroll
-            for (int hh = 0; hh < kN; ++hh) {
-                const float mn = valid ? fmaxf(m[hh], sc[hh]) : m[hh];
-                const float f = (m[hh] == -INFINITY) ? 0.f : fast_exp2(m[hh] - mn);
-                const float p = valid ? fast_exp2(sc[hh] - mn) : 0.f;
-                l[hh] = l[hh] * f + p;
-#pragma unroll
-                for (int j = 0; j < kDw; ++j) {
-                    o[hh][2 * j] = o[hh][2 * j] * f + p * half_bits_to_float(vw[j] & 0xffffu);
-                    o[hh][2 * j + 1] = o[hh][2 * j + 1] * f + p * half_bits_to_float(vw[j] >> 16);
-                }
-                m[hh] = mn;
-            }
-          }
-        }
-        // the two groups of the wave combined (log-sum-exp), the same in
-        // every lane; then the wave's m, l and o go to the LDS fold
-#pragma unroll
-        for (int hh = 0; hh < kN; ++hh) {
-            if (h0 + hh >= G) continue;
-            const int h = h0 + hh;
-            const float mx = fmaxf(m[hh], lane_partner<32>(m[hh], lane));
-            const float f = (m[hh] == -INFINITY) ? 0.f : fast_exp2(m[hh] - mx);
-            const float lh = l[hh] * f;
-            const float ls = lh + lane_partner<32>(lh, lane);
-            if (lane == 0) {
-                fm[wave * G + h] = mx;
-                fl[wave * G + h] = ls;
-            }
-#pragma unroll
-            for (int j = 0; j < kDl; ++j) {
-                const float oh = o[hh][j] * f;
-                const float os = oh + lane_partner<32>(oh, lane);
-                if (grp == 0) fo[(wave * G + h) * kHeadDim + sub * kDl + j] = os;
-            }
-        }
     }
     __syncthreads();
     for (int i = tid; i < G * kHeadDim; i += kThreads) {
         const int h = i / kHeadDim, d = i % kHeadDim;
         float mx = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, fm[w * G + h]);
+        for (int w = 0; w < nw; ++w) mx = fmaxf(mx, fm[w * 8 + h]);
         float ls = 0.f, os = 0.f;
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = (fm[w * G + h] == -INFINITY) ? 0.f : fast_exp2(fm[w * G + h] - mx);
-            ls += f * fl[w * G + h];
-            os += f * fo[(w * G + h) * kHeadDim + d];
+        for (int w = 0; w < nw; ++w) {
+            const float fw = fast_exp2(fm[w * 8 + h] - mx);   // every state holds a token
+            ls += fw * fl[w * 8 + h];
+            os += fw * reinterpret_cast<const float*>(base + w * kWaveBytes)[h * kHeadDim + d];
         }
         const size_t pi = (static_cast<size_t>(b) * num_q_heads + g * G + h) * part_stride + slot;
         part.o[pi * kHeadDim + d] = os;

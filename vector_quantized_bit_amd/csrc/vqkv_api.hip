@@ -454,15 +454,15 @@ vqkv::AppendArgs append_args(const void* k_new, const void* v_new, int kv_dtype,
 
 // A window step splits the num_codes coded tokens like a decode step; with
 // no coded tokens there is no code split, only the window workgroup.
-// The window's attention in cached tokens, rounded up like fold_tokens (a
-// 128-token window takes about 5 us alone, more in a loaded chip).  A window
-// step folds only from 128 streams on, where its window workgroups would
-// otherwise run after the splits: beside the splits (fewer streams) they
-// measured cheaper than folded (64 streams of 65536 tokens: window step
-// 76-86 us beside, 82-88 us folded; 128 streams of 32768: 68-70 us after,
-// 62-68 us folded).
+// The window's attention in cached tokens, rounded up like fold_tokens.  A
+// window step folds from 64 streams on.  With the window on the matrix cores
+// (a 127-token window adds 1.1-1.8 us to the workgroup over an empty one)
+// folding measured faster there (64 streams of 65536 tokens: window step 69.4 us folded with
+// 3072 tokens, 71.7 us with 2048, 73.5 us beside the splits; 128 streams of
+// 32768: 3072 tokens 52.7 us, 2048 53.1 us, 1536 53.4 us).  With fewer
+// streams the window workgroups get CUs of their own beside the splits.
 constexpr int kWindowFoldTokens = 3072;
-constexpr int kWindowFoldStreams = 128;
+constexpr int kWindowFoldStreams = 64;
 
 SplitPlan plan_window_step(int streams, int num_codes, int requested) {
     if (num_codes == 0) return SplitPlan{0, 0};
