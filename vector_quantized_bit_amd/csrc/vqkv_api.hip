@@ -455,12 +455,13 @@ vqkv::AppendArgs append_args(const void* k_new, const void* v_new, int kv_dtype,
 // A window step splits the num_codes coded tokens like a decode step; with
 // no coded tokens there is no code split, only the window workgroup.
 // The window's attention in cached tokens, rounded up like fold_tokens.  A
-// window step folds from 64 streams on.  With the window on the matrix cores
-// (a 127-token window adds 1.1-1.8 us to the workgroup over an empty one)
-// folding measured faster there (64 streams of 65536 tokens: window step 69.4 us folded with
-// 3072 tokens, 71.7 us with 2048, 73.5 us beside the splits; 128 streams of
-// 32768: 3072 tokens 52.7 us, 2048 53.1 us, 1536 53.4 us).  With fewer
-// streams the window workgroups get CUs of their own beside the splits.
+// window step folds from 64 streams on: there, with the window on the matrix
+// cores (a 127-token window adds 1.1-2.1 us to the workgroup over an empty
+// one), folding measured faster (64 streams of 65536 tokens: window step
+// 62.3 us folded, 73.6 us beside the splits; of the fold sizes, 3072 tokens
+// beat 2048 by 3% there and 2048 and 1536 by 1% at 128 streams of 32768).
+// With fewer streams the window workgroups get CUs of their own beside the
+// splits.
 constexpr int kWindowFoldTokens = 3072;
 constexpr int kWindowFoldStreams = 64;
 
