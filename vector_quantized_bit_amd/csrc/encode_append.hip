@@ -41,13 +41,14 @@ __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
 // The nearest centroids of the 16 sub-vectors of each of the NC row blocks
 // rb0 .. rb0 + NC - 1 of `xs` ([8 tokens][128] fp64 = [256 sub-vectors][4])
 // among NENT fp16 centroids c16 (the codebook as stored), with the norm terms
-// of hilo_norm_terms at scale sc in cu / cd: fp16 hi/lo matrix-core scores,
-// certified (nearest_search.hpp), fp64 distances for the few candidates.
+// of hilo_norm_terms at scale sc in cu / cd (dmax: their largest
+// difference): fp16 hi/lo matrix-core scores, certified
+// (nearest_search.hpp), fp64 distances for the few candidates.
 // Every centroid block's A operand and norm terms are read from LDS once for
 // all NC products; lane l % 16 of row block j gets out[j].
 template <int NENT, int NC>
 __device__ __forceinline__ void search_rows_cols(const uint2* c16, const float* cu,
-                                                 const float* cd, float sc,
+                                                 const float* cd, float sc, float dmax,
                                                  const double (*xs)[kHeadDim], int rb0, int lane,
                                                  uint32_t (&out)[NC]) {
     const double* x0 = &xs[0][0] + (rb0 * 16 + (lane & 15)) * 4;   // row block j at + 64 j
@@ -68,7 +69,8 @@ __device__ __forceinline__ void search_rows_cols(const uint2* c16, const float* 
     }
     // the distance rounded as the fp64 reference rounds it
     const auto exact = [&](int j, uint32_t nc) { return sqdist4_f64(x0 + 64 * j, c16[nc]); };
-    nearest16_cols<NENT, NC, NC == 1 ? kSearchUnroll : 4>(cu, cd, block, ex, lane, exact, out);
+    nearest16_cols<NENT, NC, NC == 1 ? kSearchUnroll : 4>(cu, cd, block, ex, dmax, lane, exact,
+                                                          out);
 }
 
 // The largest |2x| over the n values of xs, reduced over the workgroup
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     __shared__ __align__(16) float kcd[KENT];
     __shared__ __align__(16) float vcu[256];
     __shared__ __align__(16) float vcd[256];
-    __shared__ float red[2][kThr / kWave];
+    __shared__ float red[3][kThr / kWave];
     __shared__ double xs[2][kEncTok][kHeadDim];       // transformed keys, values (fp64)
     __shared__ uint16_t code[2][kEncTok][kNumSub];
 
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     // one scale per tensor for the workgroup's hi/lo rows, and the tables
     const float ksc = hilo_scale(block_absmax2<kThr>(&xs[0][0][0], kEncTok * kHeadDim, red[0], tid));
     const float vsc = hilo_scale(block_absmax2<kThr>(&xs[1][0][0], kEncTok * kHeadDim, red[1], tid));
+    float dk = 0.f;   // the largest difference of C_k's two norm terms
 #pragma unroll
     for (int j = 0; j < KPER; ++j) {
         const int i = tid + j * kThr;
@@ -152,8 +155,11 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
             const float2 t = hilo_norm_terms(norm2(kc[j]), l1_4(kc[j]), ksc);
             kcu[i] = t.x;
             kcd[i] = t.y;
+            dk = fmaxf(dk, t.x - t.y);
         }
     }
+    dk = wave_max(dk);
+    if (lane == 0) red[2][wave] = dk;
     if (tid < 256) {
         vc16[tid] = vc;
         const float2 t = hilo_norm_terms(norm2(vc), l1_4(vc), vsc);
@@ -161,6 +167,9 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
         vcd[tid] = t.y;
     }
     __syncthreads();
+    float kdmax = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWv; ++w) kdmax = fmaxf(kdmax, red[2][w]);
 
     // jobs of row blocks, keys then values; sub-vector r = 32 token +
     // position.  A wave searches the blocks of a job together, so the LDS
@@ -179,12 +188,12 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
         if (rb0 * 16 >= ntok * kNumSub) continue;   // every block past the last token
         if (key) {
             uint32_t cd[kPairK];
-            search_rows_cols<KENT, kPairK>(kc16, kcu, kcd, ksc, xs[0], rb0, lane, cd);
+            search_rows_cols<KENT, kPairK>(kc16, kcu, kcd, ksc, kdmax, xs[0], rb0, lane, cd);
 #pragma unroll
             for (int j = 0; j < kPairK; ++j) put(0, rb0 + j, cd[j]);
         } else {
             uint32_t cd[kPairV];
-            search_rows_cols<256, kPairV>(vc16, vcu, vcd, vsc, xs[1], rb0, lane, cd);
+            search_rows_cols<256, kPairV>(vc16, vcu, vcd, vsc, 0.f, xs[1], rb0, lane, cd);
 #pragma unroll
             for (int j = 0; j < kPairV; ++j) put(1, rb0 + j, cd[j]);
         }
@@ -235,7 +244,7 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
     // its norm terms at the workgroup's scale for the tensor (hilo_norm_terms)
     __shared__ __align__(16) float cu[kEnc8Ent];
     __shared__ __align__(16) float cd[kEnc8Ent];
-    __shared__ float red[2][kEnc8Waves];
+    __shared__ float red[3][kEnc8Waves];
     __shared__ double xs[2][kEnc8Tok][kHeadDim];             // transformed keys, values (fp64)
     __shared__ uint16_t code[2][kEnc8Tok][kEnc8Pos];
 
@@ -273,6 +282,7 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
         if (tt == 1) __syncthreads();   // every search of the key table is done
         const uint4* src = reinterpret_cast<const uint4*>(tt == 0 ? cb_k : cb_v) +
                            static_cast<size_t>(g) * kEnc8Ent;
+        float dm = 0.f;
         for (int i = tid; i < kEnc8Ent; i += kEnc8Threads) {
             const uint4 c = src[i];
             reinterpret_cast<uint4*>(ctab)[i] = c;
@@ -289,8 +299,14 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
             const float2 t = hilo_norm_terms(nn, l1, scale[tt]);
             cu[i] = t.x;
             cd[i] = t.y;
+            dm = fmaxf(dm, t.x - t.y);
         }
+        dm = wave_max(dm);
+        if (lane == 0) red[2][wave] = dm;
         __syncthreads();
+        float dmax = 0.f;   // the largest difference of the two norm terms
+#pragma unroll
+        for (int w = 0; w < kEnc8Waves; ++w) dmax = fmaxf(dmax, red[2][w]);
         // wave w: the 16 sub-vectors of token w (position lane % 16)
         const int tok = wave, pos = lane & 15;
         static_assert(kEnc8Waves == kEnc8Tok && kEnc8Pos == 16, "one token per wave");
@@ -316,7 +332,7 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
             block.b[0] = hilo_rows<8, h8_t>(xd, lane, sc);
             const float ex[1] = {row_bound_h(xx) * sc};
             uint32_t c[1];
-            nearest16_cols<kEnc8Ent, 1, 4>(cu, cd, block, ex, lane, exact, c);
+            nearest16_cols<kEnc8Ent, 1, 4>(cu, cd, block, ex, dmax, lane, exact, c);
             if (lane < 16) code[tt][tok][pos] = static_cast<uint16_t>(c[0]);
         }
     }

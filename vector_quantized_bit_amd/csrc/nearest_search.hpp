@@ -420,6 +420,48 @@ __device__ __forceinline__ void group_scores(const Block& block, Cop cop, int bl
         for (int j = 0; j < NC; ++j) d[j][u] = block(a[u], j, c[u]);
 }
 
+// Pass 1 for one column block over NG groups of U blocks from b0, unrolled:
+// gmin[i] is this lane's minimum of s(c) + E(c) over the run of S blocks
+// b0 + S i .. + S - 1 (S divides U or U divides S).  With the threshold
+// known, a run whose minimum lies more than the bound's width above it holds
+// no candidate (pass3_need).
+template <int U, int S, int NG, typename Block, typename Cop>
+__device__ __forceinline__ void search_pass1_groups(const Block& block, Cop cup, int b0,
+                                                    float (&gmin)[NG * U / S]) {
+    static_assert(U % S == 0 || S % U == 0, "whole runs");
+#pragma unroll
+    for (int i = 0; i < NG * U / S; ++i) gmin[i] = INFINITY;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        f32x4_t d[1][U];
+        group_scores<1, U>(block, cup, b0 + q * U, d);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float& m = gmin[(q * U + u) / S];
+            m = fminf(m, fminf(fminf(d[0][u][0], d[0][u][1]), fminf(d[0][u][2], d[0][u][3])));
+        }
+    }
+}
+
+// The runs of search_pass1_groups that may hold a candidate, as the need
+// mask of search_pass3_cols (runs of U = S blocks there).  A score of pass 3
+// differs from the pass-1 score of the same centroid by the difference of
+// the norm terms (at most dmax, their largest difference over the table)
+// and the rounding of both products; with E's margin over the rounding
+// model, 2 dmax + ex bounds the whole, so a run whose pass-1 minimum exceeds
+// thr + 2 dmax + ex has no score of pass 3 at or below thr.
+template <int N>
+__device__ __forceinline__ uint32_t pass3_need(const float (&gmin)[N], float thr, float dmax,
+                                               float ex) {
+    static_assert(N <= 32, "one bit a run");
+    const float lim = thr + 2.f * dmax + ex;
+    uint32_t need = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        need |= __builtin_amdgcn_ballot_w64(gmin[i] <= lim) != 0 ? 1u << i : 0u;
+    return need;
+}
+
 // Passes 1 and 3 for NC column blocks sharing the centroid blocks [b0, b1)
 // (b1 - b0 a multiple of U): block.a(blk) is the A operand of a block and
 // block(a, j, c) the score of column block j.  Per column block they give
@@ -439,10 +481,15 @@ __device__ __forceinline__ void search_pass1_cols(const Block& block, Cop cup, i
     }
 }
 
-template <int NC, int U, typename Block, typename Cop, typename Exact>
+// need (wave-uniform): bit i set for the runs of S blocks from b0 (a
+// multiple of U) that may hold a candidate; the groups of the others are
+// skipped without their products.
+template <int NC, int U, int S = U, typename Block, typename Cop, typename Exact>
 __device__ __forceinline__ void search_pass3_cols(const Block& block, Cop cdown, int b0, int b1,
                                                   const float (&thr)[NC], int q4, Exact exact,
-                                                  double (&bd)[NC], uint32_t (&bi)[NC]) {
+                                                  double (&bd)[NC], uint32_t (&bi)[NC],
+                                                  uint32_t need = 0xffffffffu) {
+    static_assert(S % U == 0, "whole groups a run");
     static_assert(U * 4 <= 32, "a group's hits fit one 32-bit mask");
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -451,6 +498,7 @@ __device__ __forceinline__ void search_pass3_cols(const Block& block, Cop cdown,
     }
 #pragma nounroll
     for (int blk = b0; blk < b1; blk += U) {
+        if (((need >> ((blk - b0) / S)) & 1u) == 0) continue;
         f32x4_t d[NC][U];
         group_scores<NC, U>(block, cdown, blk, d);
         // block minima first: the hit bits of a block are formed only where
@@ -491,12 +539,13 @@ __device__ __forceinline__ void search_pass3_cols(const Block& block, Cop cdown,
 }
 
 // Pass 2 for NC column blocks (what search_pass2 gives for one, with the
-// same skip rule and kSkip meaning).
-template <bool kSkip, int NC, int U, typename Block, typename Cop>
+// same skip rule and kSkip meaning); need as in search_pass3_cols.
+template <bool kSkip, int NC, int U, int S = U, typename Block, typename Cop>
 __device__ __forceinline__ void search_pass2_cols(const Block& block, Cop cdown, int b0, int b1,
                                                   const float (&thr)[NC], int (&cnt)[NC],
-                                                  int (&cand)[NC]) {
+                                                  int (&cand)[NC], uint32_t need = 0xffffffffu) {
     static_assert(U * 4 <= 32, "a group's last hit fits an inline constant");
+    static_assert(S % U == 0, "whole groups a run");
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
         cnt[j] = 0;
@@ -504,6 +553,7 @@ __device__ __forceinline__ void search_pass2_cols(const Block& block, Cop cdown,
     }
 #pragma nounroll
     for (int blk = b0; blk < b1; blk += U) {
+        if (((need >> ((blk - b0) / S)) & 1u) == 0) continue;
         f32x4_t d[NC][U];
         group_scores<NC, U>(block, cdown, blk, d);
         float m[NC][U];
@@ -542,12 +592,18 @@ __device__ __forceinline__ void search_pass2_cols(const Block& block, Cop cdown,
 // exact(j, c) the fp64 distance of the lane's sub-vector in column block j;
 // out[j] receives its nearest centroid.  U blocks a group (U * NC
 // accumulators of 4 registers stay live).
+// dmax: the largest ccu[c] - ccd[c] of the table.  With one column block
+// and 1024 or more centroids, pass 1 keeps this lane's minimum over each of
+// 32 runs of blocks (whole groups of U), and passes 2 and 3 visit only the
+// runs where some lane of the wave may have a candidate (pass3_need).
 template <int NENT, int NC, int U, typename Block, typename Exact>
 __device__ __forceinline__ void nearest16_cols(const float* __restrict__ ccu,
                                                const float* __restrict__ ccd, const Block& block,
-                                               const float (&ex)[NC], int lane, Exact exact,
-                                               uint32_t (&out)[NC]) {
+                                               const float (&ex)[NC], float dmax, int lane,
+                                               Exact exact, uint32_t (&out)[NC]) {
     static_assert(NENT % (16 * U) == 0, "whole groups");
+    constexpr bool kRuns = NC == 1 && NENT >= 1024;
+    constexpr int kRun = kRuns ? (NENT / 16 / 32 > U ? NENT / 16 / 32 : U) : U;   // blocks a run
     const int q4 = 4 * (lane >> 4);
     struct Col {
         const f32x4_t* p;
@@ -556,14 +612,28 @@ __device__ __forceinline__ void nearest16_cols(const float* __restrict__ ccu,
     const Col up{reinterpret_cast<const f32x4_t*>(ccu + q4)};
     const Col down{reinterpret_cast<const f32x4_t*>(ccd + q4)};
     float thr[NC];
-    search_pass1_cols<NC, U>(block, up, 0, NENT / 16, thr);
+    uint32_t need = 0xffffffffu;
+    if constexpr (kRuns) {
+        constexpr int kNr = NENT / (16 * kRun);
+        float gmin[kNr];
+        search_pass1_groups<U, kRun, NENT / (16 * U)>(block, up, 0, gmin);
+        float m = gmin[0];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-        thr[j] = fminf(thr[j], lane_partner<16>(thr[j], lane));
-        thr[j] = fminf(thr[j], lane_partner<32>(thr[j], lane)) + ex[j];
+        for (int i = 1; i < kNr; ++i) m = fminf(m, gmin[i]);
+        m = fminf(m, lane_partner<16>(m, lane));
+        thr[0] = fminf(m, lane_partner<32>(m, lane)) + ex[0];
+        need = pass3_need(gmin, thr[0], dmax, ex[0]);
+    } else {
+        search_pass1_cols<NC, U>(block, up, 0, NENT / 16, thr);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            thr[j] = fminf(thr[j], lane_partner<16>(thr[j], lane));
+            thr[j] = fminf(thr[j], lane_partner<32>(thr[j], lane)) + ex[j];
+        }
     }
     int cnt[NC], cand[NC];
-    search_pass2_cols<(NENT >= 1024), NC, U>(block, down, 0, NENT / 16, thr, cnt, cand);
+    search_pass2_cols<(NENT >= 1024), NC, U, kRun>(block, down, 0, NENT / 16, thr, cnt, cand,
+                                                   need);
     bool several = false;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -574,7 +644,7 @@ __device__ __forceinline__ void nearest16_cols(const float* __restrict__ ccu,
     if (__builtin_amdgcn_ballot_w64(several) == 0) return;
     double bd[NC];
     uint32_t bi[NC];
-    search_pass3_cols<NC, U>(block, down, 0, NENT / 16, thr, q4, exact, bd, bi);
+    search_pass3_cols<NC, U, kRun>(block, down, 0, NENT / 16, thr, q4, exact, bd, bi, need);
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
         take_lanes16_32(bd[j], bi[j], lane);

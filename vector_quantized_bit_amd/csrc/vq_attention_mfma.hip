@@ -273,7 +273,7 @@ constexpr int kNtV = kNtKd + 4096 * 4;
 constexpr int kNtVu = kNtV + 256 * 8;
 constexpr int kNtVd = kNtVu + 256 * 4;
 constexpr int kNtX = kNtVd + 256 * 4;
-constexpr int kNtXBytes = 64 * 4 + 2 * kWaves * 16 * 8 + 2 * kWaves * 16 * 4;
+constexpr int kNtXBytes = 64 * 4 + 2 * kWaves * 16 * 8 + 2 * kWaves * 16 * 4 + 2 * kWaves * 4;
 static_assert(kNtX + kNtXBytes <= 2 * kTable, "the 12-bit new-token tables fit the LDS tables");
 
 // C_k (4096 entries) and C_v (256) of the new-token workgroup with 12-bit
@@ -325,6 +325,7 @@ __device__ __forceinline__ void new_token_codes12(const Codes12Tables& tabs, uin
     uint32_t* wthr = reinterpret_cast<uint32_t*>(tab + kNtX);               // [2][32] keys
     double* wbd = reinterpret_cast<double*>(tab + kNtX + 256);              // [2][16 waves][16]
     uint32_t* wbi = reinterpret_cast<uint32_t*>(tab + kNtX + 256 + 2 * kWaves * 16 * 8);
+    float* wdm = reinterpret_cast<float*>(wbi + 2 * kWaves * 16);          // [2][16 waves]
     // one scale per tensor: the largest |2x| of the token's 128 channels
     float sc[2];
 #pragma unroll
@@ -333,7 +334,9 @@ __device__ __forceinline__ void new_token_codes12(const Codes12Tables& tabs, uin
                               fabsf(-2.f * static_cast<float>(xnew[t][lane + 64])));
         sc[t] = hilo_scale(wave_max(m));
     }
-    // the tables with their norm terms at these scales
+    // the tables with their norm terms at these scales, and each wave's
+    // largest difference of the two norm terms (for the skip of pass 2)
+    float dk = 0.f;
 #pragma unroll
     for (int j = 0; j < 4096 / kThreads; ++j) {
         const int i = tid + j * kThreads;
@@ -342,12 +345,17 @@ __device__ __forceinline__ void new_token_codes12(const Codes12Tables& tabs, uin
         reinterpret_cast<uint2*>(tab)[i] = c;
         reinterpret_cast<float*>(tab + kNtKu)[i] = nt.x;
         reinterpret_cast<float*>(tab + kNtKd)[i] = nt.y;
+        dk = fmaxf(dk, nt.x - nt.y);
     }
-    if (tid < 256) {
+    dk = wave_max(dk);
+    if (lane == 0) wdm[wave] = dk;
+    if (tid < 256) {   // waves 0-3
         const float2 nt = hilo_norm_terms(norm2(tabs.v), l1_4(tabs.v), sc[1]);
         reinterpret_cast<uint2*>(tab + kNtV)[tid] = tabs.v;
         reinterpret_cast<float*>(tab + kNtVu)[tid] = nt.x;
         reinterpret_cast<float*>(tab + kNtVd)[tid] = nt.y;
+        const float dv = wave_max(nt.x - nt.y);
+        if (lane == 0) wdm[kWaves + wave] = dv;
     }
     if (tid < 2 * kNumSub) wthr[tid] = 0xffffffffu;
     wave = __builtin_amdgcn_readfirstlane(wave);   // scalar: block bounds and loop counters in SGPRs
@@ -385,36 +393,48 @@ __device__ __forceinline__ void new_token_codes12(const Codes12Tables& tabs, uin
     const int kb0 = 32 * wk, kb1 = kb0 + 32, vb0 = 2 * wk, vb1 = vb0 + 2;
     __syncthreads();   // tables and threshold slots written
 
-    // pass 1: the thresholds
+    // pass 1: the thresholds, and this lane's minimum over each run of 4 key
+    // blocks and over its 2 value blocks
+    float gk[8], gv[1];
     {
-        float sk[1], sv1[1];
-        search_pass1_cols<1, kSearchUnroll>(bk, kup, kb0, kb1, sk);
-        search_pass1_cols<1, 2>(bv, vup, vb0, vb1, sv1);
-        sk[0] = fminf(sk[0], lane_partner<16>(sk[0], lane));
-        sk[0] = fminf(sk[0], lane_partner<32>(sk[0], lane));
-        sv1[0] = fminf(sv1[0], lane_partner<16>(sv1[0], lane));
-        sv1[0] = fminf(sv1[0], lane_partner<32>(sv1[0], lane));
+        search_pass1_groups<kSearchUnroll, 4, 4>(bk, kup, kb0, gk);
+        search_pass1_groups<2, 2, 1>(bv, vup, vb0, gv);
+        float sk = fminf(fminf(fminf(gk[0], gk[1]), fminf(gk[2], gk[3])),
+                         fminf(fminf(gk[4], gk[5]), fminf(gk[6], gk[7])));
+        float sv1 = gv[0];
+        sk = fminf(sk, lane_partner<16>(sk, lane));
+        sk = fminf(sk, lane_partner<32>(sk, lane));
+        sv1 = fminf(sv1, lane_partner<16>(sv1, lane));
+        sv1 = fminf(sv1, lane_partner<32>(sv1, lane));
         if (lane < 16) {
-            atomicMin(&wthr[sv], ordered_key(sk[0]));
-            atomicMin(&wthr[32 + sv], ordered_key(sv1[0]));
+            atomicMin(&wthr[sv], ordered_key(sk));
+            atomicMin(&wthr[32 + sv], ordered_key(sv1));
         }
     }
     __syncthreads();
     const float thk[1] = {from_ordered_key(wthr[sv]) + bound[0]};
     const float thv[1] = {from_ordered_key(wthr[32 + sv]) + bound[1]};
+    float dmk = 0.f, dmv = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) dmk = fmaxf(dmk, wdm[w]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dmv = fmaxf(dmv, wdm[kWaves + w]);
+    // the runs where some lane of the wave may have a candidate
+    const uint32_t needk = pass3_need(gk, thk[0], dmk, bound[0]);
+    const uint32_t needv = pass3_need(gv, thv[0], dmv, bound[1]);
 
     // pass 2: fp64 distances of every candidate; the lexicographic minimum
     // over the 4 lanes of a sub-vector, then over the waves of its block
     {
         double bd[1];
         uint32_t bi[1];
-        search_pass3_cols<1, 4>(bk, kdown, kb0, kb1, thk, q4, kexact, bd, bi);
+        search_pass3_cols<1, 4>(bk, kdown, kb0, kb1, thk, q4, kexact, bd, bi, needk);
         take_lanes16_32(bd[0], bi[0], lane);
         if (lane < 16) {
             wbd[wave * 16 + lane] = bd[0];
             wbi[wave * 16 + lane] = bi[0];
         }
-        search_pass3_cols<1, 2>(bv, vdown, vb0, vb1, thv, q4, vexact, bd, bi);
+        search_pass3_cols<1, 2>(bv, vdown, vb0, vb1, thv, q4, vexact, bd, bi, needv);
         take_lanes16_32(bd[0], bi[0], lane);
         if (lane < 16) {
             wbd[(kWaves + wave) * 16 + lane] = bd[0];
