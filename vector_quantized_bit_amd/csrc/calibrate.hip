@@ -181,12 +181,14 @@ __global__ __launch_bounds__(kAssignThreads<NENT>) void kmeans_assign_kernel(
     __shared__ __align__(16) float ccd[NENT];       // fl32(||c||^2) (1 - 2^-16)
     __shared__ double c64s[kKmLdsC64<NENT> ? NENT * 4 : 1];
     __shared__ int32_t cnt[NENT];
+    __shared__ float wdm[kAssignThreads<NENT> / kWave];
 
     const int set = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const double* cset = centroids + static_cast<size_t>(set) * NENT * 4;
     const float4* xset = reinterpret_cast<const float4*>(samples) +
                          static_cast<size_t>(set) * num_samples;
+    float dm = 0.f;
     for (int i = tid; i < NENT; i += kAssignThreads<NENT>) {
         const double2 lo = reinterpret_cast<const double2*>(cset)[2 * i];
         const double2 hi = reinterpret_cast<const double2*>(cset)[2 * i + 1];
@@ -201,9 +203,15 @@ __global__ __launch_bounds__(kAssignThreads<NENT>) void kmeans_assign_kernel(
         const float nf = static_cast<float>(nn);
         ccu[i] = nf * kBoundUp;
         ccd[i] = nf * kBoundDown;
+        dm = fmaxf(dm, nf * kBoundUp - nf * kBoundDown);
         cnt[i] = 0;
     }
+    dm = wave_max(dm);
+    if (lane == 0) wdm[wave] = dm;
     __syncthreads();
+    float dmax = 0.f;   // the largest difference of the two norm terms
+#pragma unroll
+    for (int w = 0; w < kAssignThreads<NENT> / kWave; ++w) dmax = fmaxf(dmax, wdm[w]);
 
     const int s0 = chunk * kKmChunk, s1 = min(num_samples, s0 + kKmChunk);
     int32_t* aset = assign + static_cast<size_t>(set) * num_samples;
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(kAssignThreads<NENT>) void kmeans_assign_kernel(
             }
             return sqdist4_c64(x, c);
         };
-        const uint32_t code = nearest16<NENT>(m2, ccu, ccd, bop, ex, lane, exact);
+        const uint32_t code = nearest16<NENT>(m2, ccu, ccd, bop, ex, dmax, lane, exact);
         if (lane < 16 && r < s1) {
             aset[r] = static_cast<int32_t>(code);
             if (hist != nullptr) atomicAdd(&cnt[code & (NENT - 1)], 1);
@@ -295,6 +303,15 @@ __global__ __launch_bounds__(kAssignThreads<NENT>) void kmeans_assign8_kernel(
         cnt[i] = 0;
     }
     __syncthreads();
+    // a bound on the difference of the two norm terms ScaledNorms forms,
+    // fl(n (1 + 2^-16)) - fl(n (1 - 2^-16)) <= n (2^-15 + 2^-23 (1 + 2^-15)),
+    // from the largest norm (every wave reads the whole table: the LDS is full)
+    float nmax = 0.f;
+    for (int i = lane; i < NENT / 4; i += kWave) {
+        const f32x4_t v = reinterpret_cast<const f32x4_t*>(nrm)[i];
+        nmax = fmaxf(nmax, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    }
+    const float dmax = wave_max(nmax) * (0x1p-15f + 0x1p-22f);
 
     const int s0 = chunk * kKmChunk, s1 = min(num_samples, s0 + kKmChunk);
     int32_t* aset = assign + static_cast<size_t>(set) * num_samples;
@@ -322,7 +339,8 @@ __global__ __launch_bounds__(kAssignThreads<NENT>) void kmeans_assign8_kernel(
             return sqdist8_c64(x, c);
         };
         const BlockF32D8<NENT> block(tab, -2.f * x[2 * gq], -2.f * x[2 * gq + 1], lane);
-        const uint32_t code = nearest16_search<NENT>(block, cup, cdown, row_bound(xx), lane, exact);
+        const uint32_t code =
+            nearest16_search<NENT>(block, cup, cdown, row_bound(xx), dmax, lane, exact);
         if (lane < 16 && r < s1) {
             aset[r] = static_cast<int32_t>(code);
             if (hist != nullptr) atomicAdd(&cnt[code & (NENT - 1)], 1);

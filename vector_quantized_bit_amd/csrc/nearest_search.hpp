@@ -103,19 +103,41 @@ __device__ __forceinline__ float search_pass1(Block block, Cop cup, int b0, int 
     return smin;
 }
 
+// pass 1 over NR groups of kSearchUnroll blocks from b0, unrolled: rmin[i]
+// is this lane's minimum over group i (for the need masks of passes 2 and 3,
+// as with search_pass1_groups and pass3_need)
+template <int NR, typename Block, typename Cop>
+__device__ __forceinline__ void search_pass1_runs(Block block, Cop cup, int b0,
+                                                  float (&rmin)[NR]) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int blk = b0 + i * kSearchUnroll;
+        f32x4_t d[kSearchUnroll];
+#pragma unroll
+        for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cup(blk + u));
+        rmin[i] = group_min(d);
+        // one group's operands at a time (the unrolled loop would otherwise
+        // request every group's at once)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // pass 2: how many of this lane's centroids have s(c) - E(c) <= thr, and the
 // row (16 blk + r, without the lane's 4 (lane / 16)) of the last of them.
 // kSkip: a group of 8 blocks without a hit in the whole wave is skipped after
 // one ballot, and within a group only the blocks with a hit in some lane are
 // counted, which pays where hits are sparse (a wave over 1024 or more
 // centroids) and costs a little where nearly every block has one.
+// need (wave-uniform): bit i set for the groups i of kSearchUnroll blocks
+// from b0 that may hold a candidate; the others are skipped.
 template <bool kSkip, typename Block, typename Cop>
 __device__ __forceinline__ void search_pass2(Block block, Cop cdown, int b0, int b1, float thr,
-                                             int& cnt, int& cand) {
+                                             int& cnt, int& cand, uint32_t need = 0xffffffffu) {
     cnt = 0;
     cand = -1;
 #pragma nounroll
     for (int blk = b0; blk < b1; blk += kSearchUnroll) {
+        if (((need >> ((blk - b0) / kSearchUnroll)) & 1u) == 0) continue;
         f32x4_t d[kSearchUnroll];
 #pragma unroll
         for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cdown(blk + u));
@@ -160,14 +182,16 @@ __device__ __forceinline__ void search_pass2(Block block, Cop cdown, int b0, int
 }
 
 // pass 3: the lexicographic (fp64 distance, index) minimum over this lane's
-// candidates (bd = inf, bi = 0xffffffff when it has none)
+// candidates (bd = inf, bi = 0xffffffff when it has none); need as in pass 2
 template <typename Block, typename Cop, typename Exact>
 __device__ __forceinline__ void search_pass3(Block block, Cop cdown, int b0, int b1, float thr,
-                                             int q4, Exact exact, double& bd, uint32_t& bi) {
+                                             int q4, Exact exact, double& bd, uint32_t& bi,
+                                             uint32_t need = 0xffffffffu) {
     bd = INFINITY;
     bi = 0xffffffffu;
 #pragma nounroll
     for (int blk = b0; blk < b1; blk += kSearchUnroll) {
+        if (((need >> ((blk - b0) / kSearchUnroll)) & 1u) == 0) continue;
         f32x4_t d[kSearchUnroll];
 #pragma unroll
         for (int u = 0; u < kSearchUnroll; ++u) d[u] = block(blk + u, cdown(blk + u));
@@ -214,22 +238,59 @@ __device__ __forceinline__ int max_lanes16_32(int x, int lane) {
     return max(x, static_cast<int>(lane_partner<32>(static_cast<uint32_t>(x), lane)));
 }
 
-// The whole search over NENT centroids, the norm terms given by cup / cdown.
+// The runs of the pass-1 minima gmin (search_pass1_runs, search_pass1_groups)
+// that may hold a candidate, as the need mask of passes 2 and 3.  A score of pass 3
+// differs from the pass-1 score of the same centroid by the difference of
+// the norm terms (at most dmax, their largest difference over the table)
+// and the rounding of both products; with E's margin over the rounding
+// model, 2 dmax + ex bounds the whole, so a run whose pass-1 minimum exceeds
+// thr + 2 dmax + ex has no score of pass 3 at or below thr.
+template <int N>
+__device__ __forceinline__ uint32_t pass3_need(const float (&gmin)[N], float thr, float dmax,
+                                               float ex) {
+    static_assert(N <= 32, "one bit a run");
+    const float lim = thr + 2.f * dmax + ex;
+    uint32_t need = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        need |= __builtin_amdgcn_ballot_w64(gmin[i] <= lim) != 0 ? 1u << i : 0u;
+    return need;
+}
+
+// The whole search over NENT centroids, the norm terms given by cup / cdown
+// (dmax: the largest difference cup - cdown of a centroid, read only with
+// 1024 or more centroids, where passes 2 and 3 visit only the groups of
+// kSearchUnroll blocks that may hold a candidate; pass3_need).
 template <int NENT, typename Block, typename Cop, typename Exact>
 __device__ __forceinline__ uint32_t nearest16_search(Block block, Cop cup, Cop cdown, float ex,
-                                                     int lane, Exact exact) {
+                                                     float dmax, int lane, Exact exact) {
     static_assert(NENT % (16 * kSearchUnroll) == 0, "whole unrolled groups");
+    constexpr int kGroups = NENT / (16 * kSearchUnroll);
+    constexpr bool kRuns = NENT >= 1024 && kGroups <= 32;
     const int q4 = 4 * (lane >> 4);   // this lane's first centroid row in a block
 
     // pass 1: thr = min over c of s(c) + E(c)
-    float smin = search_pass1(block, cup, 0, NENT / 16);
-    smin = fminf(smin, lane_partner<16>(smin, lane));
-    smin = fminf(smin, lane_partner<32>(smin, lane));
-    const float thr = smin + ex;
+    float thr;
+    uint32_t need = 0xffffffffu;
+    if constexpr (kRuns) {
+        float rmin[kGroups];
+        search_pass1_runs<kGroups>(block, cup, 0, rmin);
+        float smin = rmin[0];
+#pragma unroll
+        for (int i = 1; i < kGroups; ++i) smin = fminf(smin, rmin[i]);
+        smin = fminf(smin, lane_partner<16>(smin, lane));
+        thr = fminf(smin, lane_partner<32>(smin, lane)) + ex;
+        need = pass3_need(rmin, thr, dmax, ex);
+    } else {
+        float smin = search_pass1(block, cup, 0, NENT / 16);
+        smin = fminf(smin, lane_partner<16>(smin, lane));
+        smin = fminf(smin, lane_partner<32>(smin, lane));
+        thr = smin + ex;
+    }
 
     // pass 2: each lane counts its candidates and keeps one
     int cnt, cand;
-    search_pass2<(NENT >= 1024)>(block, cdown, 0, NENT / 16, thr, cnt, cand);
+    search_pass2<(NENT >= 1024)>(block, cdown, 0, NENT / 16, thr, cnt, cand, need);
     cnt = sum_lanes16_32(cnt, lane);
     const int best = max_lanes16_32(cand < 0 ? -1 : cand + q4, lane);
 
@@ -241,7 +302,7 @@ __device__ __forceinline__ uint32_t nearest16_search(Block block, Cop cup, Cop c
     // the 4 lanes of each sub-vector
     double bd;
     uint32_t bi;
-    search_pass3(block, cdown, 0, NENT / 16, thr, q4, exact, bd, bi);
+    search_pass3(block, cdown, 0, NENT / 16, thr, q4, exact, bd, bi, need);
     take_lanes16_32(bd, bi, lane);
     return bi;
 }
@@ -250,7 +311,7 @@ __device__ __forceinline__ uint32_t nearest16_search(Block block, Cop cup, Cop c
 template <int NENT, int SUB, typename Block, typename Exact>
 __device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu,
                                                    const float* __restrict__ ccd, Block block,
-                                                   float ex, int lane, Exact exact) {
+                                                   float ex, float dmax, int lane, Exact exact) {
     const int q4 = 4 * (lane >> 4);
     const f32x4_t* ucol = reinterpret_cast<const f32x4_t*>(ccu + q4);
     const f32x4_t* dcol = reinterpret_cast<const f32x4_t*>(ccd + q4);
@@ -258,7 +319,7 @@ __device__ __forceinline__ uint32_t nearest16_core(const float* __restrict__ ccu
         const f32x4_t* p;
         __device__ f32x4_t operator()(int blk) const { return p[blk * 4]; }
     };
-    return nearest16_search<NENT>(block, Col{ucol}, Col{dcol}, ex, lane, exact);
+    return nearest16_search<NENT>(block, Col{ucol}, Col{dcol}, ex, dmax, lane, exact);
 }
 
 // One norm table [NENT] (fp32 ||c||^2, 16-byte aligned), scaled by
@@ -441,25 +502,6 @@ __device__ __forceinline__ void search_pass1_groups(const Block& block, Cop cup,
             m = fminf(m, fminf(fminf(d[0][u][0], d[0][u][1]), fminf(d[0][u][2], d[0][u][3])));
         }
     }
-}
-
-// The runs of search_pass1_groups that may hold a candidate, as the need
-// mask of search_pass3_cols (runs of U = S blocks there).  A score of pass 3
-// differs from the pass-1 score of the same centroid by the difference of
-// the norm terms (at most dmax, their largest difference over the table)
-// and the rounding of both products; with E's margin over the rounding
-// model, 2 dmax + ex bounds the whole, so a run whose pass-1 minimum exceeds
-// thr + 2 dmax + ex has no score of pass 3 at or below thr.
-template <int N>
-__device__ __forceinline__ uint32_t pass3_need(const float (&gmin)[N], float thr, float dmax,
-                                               float ex) {
-    static_assert(N <= 32, "one bit a run");
-    const float lim = thr + 2.f * dmax + ex;
-    uint32_t need = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        need |= __builtin_amdgcn_ballot_w64(gmin[i] <= lim) != 0 ? 1u << i : 0u;
-    return need;
 }
 
 // Passes 1 and 3 for NC column blocks sharing the centroid blocks [b0, b1)
@@ -665,17 +707,18 @@ struct BlockD8H {
 };
 
 // d = 4: m2 [4][kSearchStride<NENT>] fp32 -2 fl32(c) by channel; b is this
-// lane's B operand, channel lane / 16 of sub-vector lane % 16.
+// lane's B operand, channel lane / 16 of sub-vector lane % 16; dmax the
+// largest ccu[c] - ccd[c].
 template <int NENT, typename Exact>
 __device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
                                               const float* __restrict__ ccu,
                                               const float* __restrict__ ccd, float b, float ex,
-                                              int lane, Exact exact) {
+                                              float dmax, int lane, Exact exact) {
     const float* acol = m2 + (lane >> 4) * kSearchStride<NENT> + (lane & 15);
     const auto block = [&](int blk, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(acol[blk * 16], b, c, 0, 0, 0);
     };
-    return nearest16_core<NENT, 4>(ccu, ccd, block, ex, lane, exact);
+    return nearest16_core<NENT, 4>(ccu, ccd, block, ex, dmax, lane, exact);
 }
 
 }  // namespace vqkv

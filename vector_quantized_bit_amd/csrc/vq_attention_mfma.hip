@@ -676,19 +676,33 @@ __device__ __forceinline__ void new_token_workgroup8(
         const auto exact = [&](uint32_t nc) {
             return sqdist8_f64(xd, reinterpret_cast<const uint4*>(table)[nc]);
         };
-        float smin = search_pass1(block, cup, b0, b1);
+        float rmin[2];   // this lane's minimum over each of the wave's 2 groups of 8 blocks
+        static_assert(16 == 2 * kSearchUnroll, "2 groups a wave");
+        search_pass1_runs<2>(block, cup, b0, rmin);
+        float smin = fminf(rmin[0], rmin[1]);
         smin = fminf(smin, lane_partner<16>(smin, lane));
         smin = fminf(smin, lane_partner<32>(smin, lane));
         if (lane < kPos) wmin[wave * kPos + lane] = smin;
+        // the largest norm bounds the difference of the lane's two norm
+        // terms: fl(n up) - fl(n down) <= n 2^s (2^-14 + 2^-23 (1 + 2^-14))
+        float nmax = 0.f;
+        for (int i = lane; i < kEnt / 4; i += 64) {
+            const f32x4_t v = reinterpret_cast<const f32x4_t*>(nrm)[i];
+            nmax = fmaxf(nmax, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+        }
+        const float dmax = wave_max(nmax) * hl.scale * (0x1p-14f + 0x1p-22f);
         __syncthreads();
         float gmin = wmin[pos];
         for (int w = 1; w < kWaves; ++w) gmin = fminf(gmin, wmin[w * kPos + pos]);
-        const float thr = gmin + row_bound_h(xx) * hl.scale;
+        const float ex = row_bound_h(xx) * hl.scale;
+        const float thr = gmin + ex;
         // fp64 distances of every candidate (about one a sub-vector, so they
-        // are evaluated as they are found rather than counted first)
+        // are evaluated as they are found rather than counted first), in the
+        // groups where some lane may have one
         double bd;
         uint32_t bi;
-        search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi);
+        search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi,
+                     pass3_need(rmin, thr, dmax, ex));
         take_lanes16_32(bd, bi, lane);
         if (lane < kPos) {
             wbd[wave * kPos + lane] = bd;
