@@ -12,10 +12,10 @@
 // of nearest_search.hpp, with the transformed keys and the values kept in
 // fp64 for the few exact distances.
 //
-// One 512-thread workgroup encodes up to 8 tokens of one (sequence, KV
-// head): 256 key and 256 value sub-vectors, 16 row blocks each, spread over
-// the 8 waves.  The codebooks (fp16, as stored) and their squared norms are
-// staged in LDS.
+// One 512-thread workgroup (1024 with 12-bit keys) encodes up to 8 tokens
+// (4 for short appends) of one (sequence, KV head): 256 key and 256 value
+// sub-vectors, 16 row blocks each, spread over the waves.  The codebooks
+// (fp16, as stored) and their squared norms are staged in LDS.
 #include "launchers.hpp"
 #include "nearest_search.hpp"
 
@@ -23,8 +23,12 @@ namespace vqkv {
 
 namespace {
 
-constexpr int kEncTok = 8;                          // tokens per workgroup
-constexpr int kEncBlocks = kEncTok * kNumSub / 16;  // row blocks per tensor
+// Tokens per workgroup: 8, or 4 where the launch with 8 would leave CUs
+// without a workgroup (short appends), since a workgroup of 4 tokens gives
+// each wave one search job instead of two.
+constexpr int kEncTok = 8;
+constexpr int kEncTokSmall = 4;
+constexpr int kEncFill = 256;   // workgroups that fill the chip (one per CU)
 // Threads of the d = 4 encoder: with 4096-entry C_k its tables (about
 // 120 KiB of LDS) allow one workgroup per CU, so it takes 16 waves, one key
 // row block each, to keep 4 waves on every SIMD; with 256 entries several
@@ -39,7 +43,7 @@ __device__ __forceinline__ double load_elem(const void* p, bool f32, size_t i) {
 }
 
 // The nearest centroids of the 16 sub-vectors of each of the NC row blocks
-// rb0 .. rb0 + NC - 1 of `xs` ([8 tokens][128] fp64 = [256 sub-vectors][4])
+// rb0 .. rb0 + NC - 1 of `xs` ([tokens][128] fp64: 32 sub-vectors of 4 a token)
 // among NENT fp16 centroids c16 (the codebook as stored), with the norm terms
 // of hilo_norm_terms at scale sc in cu / cd (dmax: their largest
 // difference): fp16 hi/lo matrix-core scores, certified
@@ -90,7 +94,7 @@ __device__ __forceinline__ float block_absmax2(const double* xs, int n, float* r
 
 }  // namespace
 
-template <int KBITS>
+template <int KBITS, int TOK>
 __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
     const float* __restrict__ lambda, const uint16_t* __restrict__ cb_k,
@@ -108,11 +112,12 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     __shared__ __align__(16) float vcu[256];
     __shared__ __align__(16) float vcd[256];
     __shared__ float red[3][kThr / kWave];
-    __shared__ double xs[2][kEncTok][kHeadDim];       // transformed keys, values (fp64)
-    __shared__ uint16_t code[2][kEncTok][kNumSub];
+    __shared__ double xs[2][TOK][kHeadDim];       // transformed keys, values (fp64)
+    __shared__ uint16_t code[2][TOK][kNumSub];
+    constexpr int kBlocks = TOK * kNumSub / 16;   // row blocks per tensor
 
-    const int t0 = blockIdx.x * kEncTok, g = blockIdx.y, b = blockIdx.z;
-    const int ntok = min(kEncTok, num_new - t0);
+    const int t0 = blockIdx.x * TOK, g = blockIdx.y, b = blockIdx.z;
+    const int ntok = min(TOK, num_new - t0);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const bool f32 = kv_f32 != 0;
 
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     // k / lambda in fp64, the +-1 Walsh–Hadamard transform, then 1/sqrt(128);
     // values as they are.  Rows of tokens past num_new are zero.
     const float* lam = lambda + g * kHeadDim;
-    for (int t = wave; t < kEncTok; t += kWv) {
+    for (int t = wave; t < TOK; t += kWv) {
         const bool live = t < ntok;
         const size_t in_row = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + t0 +
                               (live ? t : 0);
@@ -144,8 +149,8 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     }
     __syncthreads();
     // one scale per tensor for the workgroup's hi/lo rows, and the tables
-    const float ksc = hilo_scale(block_absmax2<kThr>(&xs[0][0][0], kEncTok * kHeadDim, red[0], tid));
-    const float vsc = hilo_scale(block_absmax2<kThr>(&xs[1][0][0], kEncTok * kHeadDim, red[1], tid));
+    const float ksc = hilo_scale(block_absmax2<kThr>(&xs[0][0][0], TOK * kHeadDim, red[0], tid));
+    const float vsc = hilo_scale(block_absmax2<kThr>(&xs[1][0][0], TOK * kHeadDim, red[1], tid));
     float dk = 0.f;   // the largest difference of C_k's two norm terms
 #pragma unroll
     for (int j = 0; j < KPER; ++j) {
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     // one block a job: pairs would leave half of the 16 waves without a key
     // job (measured 18% slower).
     constexpr int kPairK = KBITS == 12 ? 1 : 2, kPairV = 2;
-    constexpr int kJobsK = kEncBlocks / kPairK, kJobsV = kEncBlocks / kPairV;
+    constexpr int kJobsK = kBlocks / kPairK, kJobsV = kBlocks / kPairV;
     const auto put = [&](int tt, int rb, uint32_t cd) {
         const int r = rb * 16 + lane;
         if (lane < 16) code[tt][r >> 5][r & 31] = static_cast<uint16_t>(cd);
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     // codes of the live tokens to their slots
     const size_t out0 = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + cur_len + t0;
     {
-        const int t = tid / kNumSub, pos = tid % kNumSub;   // 8 tokens x 32 positions (tid < 256)
+        const int t = tid / kNumSub, pos = tid % kNumSub;   // TOK tokens x 32 positions
         if (t < ntok) codes_v[(out0 + t) * kNumSub + pos] = static_cast<uint8_t>(code[1][t][pos]);
         if constexpr (KBITS == 8) {
             if (t < ntok) codes_k[(out0 + t) * KROW + pos] = static_cast<uint8_t>(code[0][t][pos]);
@@ -355,20 +360,30 @@ hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, cons
                                 const uint16_t* cb_v, uint8_t* codes_k, uint8_t* codes_v,
                                 int batch, int num_kv_heads, int capacity, int cur_len,
                                 int num_new, hipStream_t stream) {
-    const dim3 grid((num_new + kEncTok - 1) / kEncTok, num_kv_heads, batch);
     const dim3 grid8((num_new + kEnc8Tok - 1) / kEnc8Tok, num_kv_heads, batch);
-    if (sub_dim == 8)
+    if (sub_dim == 8) {
         hipLaunchKernelGGL(encode_append8_kernel, grid8, dim3(kEnc8Threads), 0, stream, k_new, v_new,
                            kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v, num_kv_heads,
                            capacity, cur_len, num_new);
-    else if (k_bits == 8)
-        hipLaunchKernelGGL(encode_append_kernel<8>, grid, dim3(kEncThreadsOf<8>), 0, stream, k_new,
-                           v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
-                           num_kv_heads, capacity, cur_len, num_new);
-    else
-        hipLaunchKernelGGL(encode_append_kernel<12>, grid, dim3(kEncThreadsOf<12>), 0, stream, k_new,
-                           v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
-                           num_kv_heads, capacity, cur_len, num_new);
+        return hipGetLastError();
+    }
+    const long long full = static_cast<long long>((num_new + kEncTok - 1) / kEncTok) *
+                           num_kv_heads * batch;
+    const bool small = full < kEncFill;
+    const int tok = small ? kEncTokSmall : kEncTok;
+    const dim3 grid((num_new + tok - 1) / tok, num_kv_heads, batch);
+    const auto launch = [&](auto kernel, int threads) {
+        hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, k_new, v_new, kv_f32 ? 1 : 0,
+                           lambda, cb_k, cb_v, codes_k, codes_v, num_kv_heads, capacity, cur_len,
+                           num_new);
+    };
+    if (k_bits == 8) {
+        if (small) launch(encode_append_kernel<8, kEncTokSmall>, kEncThreadsOf<8>);
+        else launch(encode_append_kernel<8, kEncTok>, kEncThreadsOf<8>);
+    } else {
+        if (small) launch(encode_append_kernel<12, kEncTokSmall>, kEncThreadsOf<12>);
+        else launch(encode_append_kernel<12, kEncTok>, kEncThreadsOf<12>);
+    }
     return hipGetLastError();
 }
 
