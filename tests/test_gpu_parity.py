@@ -225,7 +225,7 @@ def test_encoder_append_mixed_bits_full_size():
                                                      (12, 1, 3, "f16"), (12, 7, 0, "f16"),
                                                      (12, 33, 100, "f32")])
 def test_encode_append_ragged(k_bits, t_new, cur, dtype):
-    # token counts that leave a workgroup partly empty (8 tokens per
+    # token counts that leave a workgroup partly empty (4 or 8 tokens per
     # workgroup), into the middle of a cache whose other slots stay untouched
     bsz, hkv = 2, 2
     lam = np.stack([W.random_lambda(150 + k_bits, g) for g in range(hkv)])
@@ -273,6 +273,35 @@ def test_encoder_exact_ties_go_to_lowest_index():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(cv.cpu().numpy()[0, 0, 2:7], codes)
     assert cv.cpu().numpy()[0, 0, 2:7].max() < 128
+
+
+@pytest.mark.parametrize("t_new", [40, 1030])
+def test_encoder12_exact_ties_go_to_lowest_index(t_new):
+    # C_k's second half repeats its first (4096 entries): every key sub-vector
+    # has two nearest centroids at exactly the same distance, 2048 apart and
+    # so in different runs of the search (which skips runs that cannot hold
+    # a candidate), and must take the lower index.  40 tokens run 4-token
+    # workgroups, 1030 tokens 8-token ones.
+    bsz, hkv = 1, 2
+    lam = np.stack([W.random_lambda(170, g) for g in range(hkv)])
+    half = np.stack([W.random_codebook(170, g, "k", 2048, 0.6) for g in range(hkv)])
+    cb_k = np.ascontiguousarray(np.concatenate([half, half], axis=1))
+    cb_v = np.stack([W.random_codebook(170, g, "v", 256, 1.0, 1 / 32) for g in range(hkv)])
+    k = np.stack([W.kv_rows(170, 0, g, "k", t_new, append=True) for g in range(hkv)])[None]
+    v = np.stack([W.kv_rows(170, 0, g, "v", t_new, append=True) for g in range(hkv)])[None]
+    k, v = k.astype(np.float16), v.astype(np.float16)
+    ck = torch.zeros((bsz, hkv, t_new, 48), dtype=torch.uint8, device=DEV)
+    cv = torch.zeros((bsz, hkv, t_new, 32), dtype=torch.uint8, device=DEV)
+    vq.encode_append(dev(k), dev(v), dev(lam), dev(cb_k), dev(cb_v), ck, cv, 0)
+    torch.cuda.synchronize()
+    ckh, cvh = ck.cpu().numpy(), cv.cpu().numpy()
+    for g in range(hkv):
+        assert oracle.unpack_codes(ckh[0, g], 12, 32).max() < 2048
+        pk, pv, gk, gv = oracle.encode_append(k[0, g], v[0, g], lam[g], cb_k[g], cb_v[g], 12, 8)
+        kt = oracle.transform_keys(k[0, g], lam[g])
+        check_codes(ckh[0, g], pk, gk, 12, kt, cb_k[g], f"12-bit ties K g{g} t={t_new}")
+        check_codes(cvh[0, g], pv, gv, 8, v[0, g], cb_v[g], f"12-bit ties V g{g} t={t_new}",
+                    values=True)
 
 
 # --- fp16 comparator -----------------------------------------------------------------
