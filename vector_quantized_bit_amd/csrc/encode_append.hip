@@ -13,8 +13,9 @@
 // fp64 for the few exact distances.
 //
 // One 512-thread workgroup (1024 with 12-bit keys) encodes up to 8 tokens
-// (4 for short appends) of one (sequence, KV head): 256 key and 256 value
-// sub-vectors, 16 row blocks each, spread over the waves.  The codebooks
+// (4 for short appends, 16 for prompts) of one (sequence, KV head): 32 key
+// and 32 value sub-vectors a token, in row blocks of 16, spread over the
+// waves.  The codebooks
 // (fp16, as stored) and their squared norms are staged in LDS.
 #include "launchers.hpp"
 #include "nearest_search.hpp"
@@ -23,11 +24,14 @@ namespace vqkv {
 
 namespace {
 
-// Tokens per workgroup: 8, or 4 where the launch with 8 would leave CUs
+// Tokens per workgroup: 8; 4 where the launch with 8 would leave CUs
 // without a workgroup (short appends), since a workgroup of 4 tokens gives
-// each wave one search job instead of two.
+// each wave one search job instead of two; 16 where 8 would give more than
+// 8 workgroups a CU (prompts), which spreads each workgroup's fixed work
+// (tables, scales, barriers) over twice the tokens.
 constexpr int kEncTok = 8;
 constexpr int kEncTokSmall = 4;
+constexpr int kEncTokLarge = 16;
 constexpr int kEncFill = 256;   // workgroups that fill the chip (one per CU)
 // Threads of the d = 4 encoder: with 4096-entry C_k its tables (about
 // 120 KiB of LDS) allow one workgroup per CU, so it takes 16 waves, one key
@@ -115,6 +119,7 @@ __global__ __launch_bounds__(kEncThreadsOf<KBITS>) void encode_append_kernel(
     __shared__ double xs[2][TOK][kHeadDim];       // transformed keys, values (fp64)
     __shared__ uint16_t code[2][TOK][kNumSub];
     constexpr int kBlocks = TOK * kNumSub / 16;   // row blocks per tensor
+    static_assert(TOK * kNumSub <= kThr, "one thread per (token, position) writes the codes");
 
     const int t0 = blockIdx.x * TOK, g = blockIdx.y, b = blockIdx.z;
     const int ntok = min(TOK, num_new - t0);
@@ -370,7 +375,8 @@ hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, cons
     const long long full = static_cast<long long>((num_new + kEncTok - 1) / kEncTok) *
                            num_kv_heads * batch;
     const bool small = full < kEncFill;
-    const int tok = small ? kEncTokSmall : kEncTok;
+    const bool large = full >= 8 * kEncFill;
+    const int tok = small ? kEncTokSmall : (large ? kEncTokLarge : kEncTok);
     const dim3 grid((num_new + tok - 1) / tok, num_kv_heads, batch);
     const auto launch = [&](auto kernel, int threads) {
         hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, k_new, v_new, kv_f32 ? 1 : 0,
@@ -379,9 +385,11 @@ hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, cons
     };
     if (k_bits == 8) {
         if (small) launch(encode_append_kernel<8, kEncTokSmall>, kEncThreadsOf<8>);
+        else if (large) launch(encode_append_kernel<8, kEncTokLarge>, kEncThreadsOf<8>);
         else launch(encode_append_kernel<8, kEncTok>, kEncThreadsOf<8>);
     } else {
         if (small) launch(encode_append_kernel<12, kEncTokSmall>, kEncThreadsOf<12>);
+        else if (large) launch(encode_append_kernel<12, kEncTokLarge>, kEncThreadsOf<12>);
         else launch(encode_append_kernel<12, kEncTok>, kEncThreadsOf<12>);
     }
     return hipGetLastError();
