@@ -239,12 +239,12 @@ __device__ __forceinline__ int max_lanes16_32(int x, int lane) {
 }
 
 // The runs of the pass-1 minima gmin (search_pass1_runs, search_pass1_groups)
-// that may hold a candidate, as the need mask of passes 2 and 3.  A score of
-// those passes differs from the pass-1 score of the same centroid by the
-// difference of the norm terms (at most dmax, their largest difference over
-// the table) and the rounding of both products; with E's margin over the
-// rounding model, 2 dmax + ex bounds the whole, so a run whose pass-1
-// minimum exceeds thr + 2 dmax + ex has no score at or below thr there.
+// that may hold a candidate, as the need mask of passes 2 and 3.  A score of pass 3
+// differs from the pass-1 score of the same centroid by the difference of
+// the norm terms (at most dmax, their largest difference over the table)
+// and the rounding of both products; with E's margin over the rounding
+// model, 2 dmax + ex bounds the whole, so a run whose pass-1 minimum exceeds
+// thr + 2 dmax + ex has no score of pass 3 at or below thr.
 template <int N>
 __device__ __forceinline__ uint32_t pass3_need(const float (&gmin)[N], float thr, float dmax,
                                                float ex) {
