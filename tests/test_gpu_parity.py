@@ -851,6 +851,31 @@ def test_d8_encode_append(t_new, cur, dtype):
                         f"1.5bit enc V b{b} g{g}", 8, values=True)
 
 
+def test_d8_encode_append_prompt_workgroups():
+    # enough tokens for 16-token workgroups on every CU (8 KV heads x 33
+    # workgroups, the last one half full); shorter appends take a token a
+    # workgroup (the cases above).  Two heads are checked against the oracle.
+    hkv, t_new = 8, 520
+    lam = np.stack([W.random_lambda(141, g) for g in range(hkv)])
+    cb_k = np.stack([W.random_codebook(141, g, "k", 4096, 0.6, sub_dim=8) for g in range(hkv)])
+    cb_v = np.stack([W.random_codebook(141, g, "v", 4096, 1.0, 1 / 32, sub_dim=8)
+                     for g in range(hkv)])
+    k = np.stack([W.kv_rows(141, 0, g, "k", t_new, append=True) for g in range(hkv)])[None]
+    v = np.stack([W.kv_rows(141, 0, g, "v", t_new, append=True) for g in range(hkv)])[None]
+    k, v = k.astype(np.float16), v.astype(np.float16)
+    ck = torch.full((1, hkv, t_new, 24), 0xA5, dtype=torch.uint8, device=DEV)
+    cv = torch.full((1, hkv, t_new, 24), 0x5A, dtype=torch.uint8, device=DEV)
+    vq.encode_append(dev(k), dev(v), dev(lam), dev(cb_k), dev(cb_v), ck, cv, 0)
+    torch.cuda.synchronize()
+    ckh, cvh = ck.cpu().numpy(), cv.cpu().numpy()
+    for g in (0, hkv - 1):
+        pk, pv, gk, gv = oracle.encode_append(k[0, g], v[0, g], lam[g], cb_k[g], cb_v[g], 12, 12)
+        kt = oracle.transform_keys(k[0, g], lam[g])
+        check_codes(ckh[0, g], pk, gk, 12, kt, cb_k[g], f"1.5bit prompt K g{g}", 8)
+        check_codes(cvh[0, g], pv, gv, 12, v[0, g], cb_v[g], f"1.5bit prompt V g{g}", 8,
+                    values=True)
+
+
 def test_d8_encoder_exact_ties_go_to_lowest_index():
     rng = np.random.default_rng(150)
     base = rng.standard_normal((2048, 8)).astype(np.float16)

@@ -360,6 +360,63 @@ __global__ __launch_bounds__(kEnc8Threads) void encode_append8_kernel(
     }
 }
 
+// Short appends in the d = 8 layout: one token per workgroup, its 4096
+// centroids of each tensor spread over the 16 waves (codes8_one_token, the
+// search of the decode step's new token), so that a few tokens still occupy
+// many CUs.  The decisions are those of encode_append8_kernel.
+// LDS: C_k and C_v as stored (64 KiB each), the norms, the exchanges.
+__global__ __launch_bounds__(1024) void encode_token8_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new, int kv_f32,
+    const float* __restrict__ lambda, const uint16_t* __restrict__ cb_k,
+    const uint16_t* __restrict__ cb_v, uint8_t* __restrict__ codes_k,
+    uint8_t* __restrict__ codes_v, int num_kv_heads, int capacity, int cur_len, int num_new) {
+    constexpr int kTab = kEnc8Ent * 16;   // bytes of one codebook
+    __shared__ __align__(16) uint8_t tab[2 * kTab];
+    __shared__ __align__(16) float nrm[kEnc8Ent];
+    __shared__ __align__(16) uint8_t xbuf[4096];
+    __shared__ double xnew[2][kHeadDim];   // transformed key, value (fp64)
+    __shared__ uint32_t newc[2][kNumSub];
+
+    const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const bool f32 = kv_f32 != 0;
+    const uint4* ksrc = reinterpret_cast<const uint4*>(cb_k) + static_cast<size_t>(g) * kEnc8Ent;
+    const uint4* vsrc = reinterpret_cast<const uint4*>(cb_v) + static_cast<size_t>(g) * kEnc8Ent;
+    for (int i = tid; i < kEnc8Ent; i += 1024) {
+        reinterpret_cast<uint4*>(tab)[i] = ksrc[i];
+        reinterpret_cast<uint4*>(tab + kTab)[i] = vsrc[i];
+    }
+    // k / lambda in fp64, the +-1 Walsh–Hadamard transform, then 1/sqrt(128)
+    // (wave 0); the value as it is (wave 1)
+    if (wave < 2) {
+        const size_t in_row = (static_cast<size_t>(b) * num_kv_heads + g) * num_new + t;
+        const void* src = wave == 0 ? k_new : v_new;
+        double x0 = load_elem(src, f32, in_row * kHeadDim + 2 * lane);
+        double x1 = load_elem(src, f32, in_row * kHeadDim + 2 * lane + 1);
+        if (wave == 0) {
+            const float* lam = lambda + g * kHeadDim;
+            x0 = x0 / static_cast<double>(lam[2 * lane]);
+            x1 = x1 / static_cast<double>(lam[2 * lane + 1]);
+            fwht128(x0, x1);
+            x0 *= kInvSqrtD64;
+            x1 *= kInvSqrtD64;
+        }
+        xnew[wave][2 * lane] = x0;
+        xnew[wave][2 * lane + 1] = x1;
+    }
+    __syncthreads();
+    codes8_one_token(tab, kTab, nrm, xbuf, xnew, newc, tid, lane, wave);
+    // the two 24-byte rows: byte j holds bits [8j, 8j + 8) of the 12-bit stream
+    const size_t row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + cur_len + t;
+    if (tid < 2 * kEnc8Row) {
+        const int tsel = tid / kEnc8Row, j = tid % kEnc8Row;
+        const int bit = 8 * j, i0 = bit / 12, sh = bit % 12;
+        uint32_t v = newc[tsel][i0] >> sh;
+        if (sh > 4) v |= newc[tsel][i0 + 1] << (12 - sh);
+        (tsel ? codes_v : codes_k)[row * kEnc8Row + j] = static_cast<uint8_t>(v & 0xffu);
+    }
+}
+
 hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, const void* v_new,
                                 bool kv_f32, const float* lambda, const uint16_t* cb_k,
                                 const uint16_t* cb_v, uint8_t* codes_k, uint8_t* codes_v,
@@ -367,9 +424,15 @@ hipError_t launch_encode_append(int k_bits, int sub_dim, const void* k_new, cons
                                 int num_new, hipStream_t stream) {
     const dim3 grid8((num_new + kEnc8Tok - 1) / kEnc8Tok, num_kv_heads, batch);
     if (sub_dim == 8) {
-        hipLaunchKernelGGL(encode_append8_kernel, grid8, dim3(kEnc8Threads), 0, stream, k_new, v_new,
-                           kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v, num_kv_heads,
-                           capacity, cur_len, num_new);
+        // a token a workgroup where 16-token workgroups would leave CUs idle
+        if (static_cast<long long>(grid8.x) * num_kv_heads * batch < kEncFill)
+            hipLaunchKernelGGL(encode_token8_kernel, dim3(num_new, num_kv_heads, batch), dim3(1024),
+                               0, stream, k_new, v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k,
+                               codes_v, num_kv_heads, capacity, cur_len, num_new);
+        else
+            hipLaunchKernelGGL(encode_append8_kernel, grid8, dim3(kEnc8Threads), 0, stream, k_new,
+                               v_new, kv_f32 ? 1 : 0, lambda, cb_k, cb_v, codes_k, codes_v,
+                               num_kv_heads, capacity, cur_len, num_new);
         return hipGetLastError();
     }
     const long long full = static_cast<long long>((num_new + kEncTok - 1) / kEncTok) *

@@ -721,4 +721,113 @@ __device__ __forceinline__ uint32_t nearest16(const float* __restrict__ m2,
     return nearest16_core<NENT, 4>(ccu, ccd, block, ex, dmax, lane, exact);
 }
 
+
+// The codes of one token in the d = 8 layout (16 sub-vectors of 8 channels,
+// C_k and C_v of 4096 fp16 entries), found by one 1024-thread workgroup: the
+// 16 sub-vectors of a tensor are one MFMA column block (per-lane hi/lo
+// scale, hilo_d8), and wave w scans centroids 256 w .. 256 w + 255.  Per
+// tensor: the waves' pass-1 minima meet in LDS (the threshold), each wave
+// keeps its pass-1 minimum per group of 8 blocks for the skip of pass 3, and
+// the fp64 minima over the candidates meet in LDS; ties to the lowest index,
+// the decisions of the fp64 scan.
+//   tab     C_k as stored (16-byte entries), C_v at tab + table_bytes
+//   nrm     [4096] fp32 scratch (the current tensor's ||c||^2)
+//   xbuf    4 KiB of exchanges
+//   xnew    the transformed key and the value (fp64)
+//   newc    [2][16] receives the codes
+// Every thread of the workgroup calls it; it ends with a barrier.
+__device__ __forceinline__ void codes8_one_token(const uint8_t* tab, int table_bytes, float* nrm,
+                                                 uint8_t* xbuf, const double (*xnew)[kHeadDim],
+                                                 uint32_t (*newc)[kNumSub], int tid, int lane,
+                                                 int wave) {
+    constexpr int kEnt = 4096, kPos = 16, kThr = 1024, kWv = kThr / 64;
+    static_assert(kEnt == kWv * 256, "16 waves of 256 centroids");
+    float* wmin = reinterpret_cast<float*>(xbuf);               // [16 waves][16] pass-1 minima
+    double* wbd = reinterpret_cast<double*>(xbuf + 1024);       // [16][16] fp64 minima
+    uint32_t* wbi = reinterpret_cast<uint32_t*>(xbuf + 3072);   // [16][16] their indices
+    const int pos = lane & (kPos - 1), q4 = 4 * (lane >> 4);
+    const int b0 = 16 * wave, b1 = b0 + 16;   // this wave's centroid blocks
+    for (int t = 0; t < 2; ++t) {
+        const uint16_t* table = reinterpret_cast<const uint16_t*>(tab + t * table_bytes);
+        for (int i = tid; i < kEnt; i += kThr) {
+            const uint4 c = reinterpret_cast<const uint4*>(table)[i];
+            const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+            float nn = 0.f;   // the squares of fp16 values are exact in fp32
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = half_bits_to_float(static_cast<uint16_t>(w[j] & 0xffffu));
+                const float hi = half_bits_to_float(static_cast<uint16_t>(w[j] >> 16));
+                nn += lo * lo;
+                nn += hi * hi;
+            }
+            nrm[i] = nn;
+        }
+        __syncthreads();
+        double xd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xd[j] = xnew[t][8 * pos + j];
+        float xx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float v = static_cast<float>(xd[j]);
+            xx += v * v;
+        }
+        // fp16 hi/lo matrix-core scores in units of 2^s (the lane's column)
+        const HiLoD8 hl = hilo_d8(xd, lane);
+        const BlockD8H block(table, hl.b, lane);
+        const f32x4_t* ncol = reinterpret_cast<const f32x4_t*>(nrm + q4);
+        const float up = kBoundUpH * hl.scale, down = kBoundDownH * hl.scale;   // exact
+        const auto cup = [&](int blk) { return ncol[blk * 4] * up; };
+        const auto cdown = [&](int blk) { return ncol[blk * 4] * down; };
+        const auto exact = [&](uint32_t nc) {
+            return sqdist8_f64(xd, reinterpret_cast<const uint4*>(table)[nc]);
+        };
+        float rmin[2];   // this lane's minimum over each of the wave's 2 groups of 8 blocks
+        static_assert(16 == 2 * kSearchUnroll, "2 groups a wave");
+        search_pass1_runs<2>(block, cup, b0, rmin);
+        float smin = fminf(rmin[0], rmin[1]);
+        smin = fminf(smin, lane_partner<16>(smin, lane));
+        smin = fminf(smin, lane_partner<32>(smin, lane));
+        if (lane < kPos) wmin[wave * kPos + lane] = smin;
+        // the largest norm bounds the difference of the lane's two norm
+        // terms: fl(n up) - fl(n down) <= n 2^s (2^-14 + 2^-23 (1 + 2^-14))
+        float nmax = 0.f;
+        for (int i = lane; i < kEnt / 4; i += 64) {
+            const f32x4_t v = reinterpret_cast<const f32x4_t*>(nrm)[i];
+            nmax = fmaxf(nmax, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+        }
+        const float dmax = wave_max(nmax) * hl.scale * (0x1p-14f + 0x1p-22f);
+        __syncthreads();
+        float gmin = wmin[pos];
+        for (int w = 1; w < kWv; ++w) gmin = fminf(gmin, wmin[w * kPos + pos]);
+        const float ex = row_bound_h(xx) * hl.scale;
+        const float thr = gmin + ex;
+        // fp64 distances of every candidate (about one a sub-vector, so they
+        // are evaluated as they are found rather than counted first), in the
+        // groups where some lane may have one
+        double bd;
+        uint32_t bi;
+        search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi,
+                     pass3_need(rmin, thr, dmax, ex));
+        take_lanes16_32(bd, bi, lane);
+        if (lane < kPos) {
+            wbd[wave * kPos + lane] = bd;
+            wbi[wave * kPos + lane] = bi;
+        }
+        __syncthreads();
+        if (tid < kPos) {
+            double d0 = wbd[tid];
+            uint32_t i0 = wbi[tid];
+            for (int w = 1; w < kWv; ++w) {
+                if (nearer(wbd[w * kPos + tid], wbi[w * kPos + tid], d0, i0)) {
+                    d0 = wbd[w * kPos + tid];
+                    i0 = wbi[w * kPos + tid];
+                }
+            }
+            newc[t][tid] = i0 & (kEnt - 1);   // (a code always exists for finite inputs)
+        }
+        __syncthreads();   // the exchange buffers and norms are free for the next tensor
+    }
+}
+
 }  // namespace vqkv

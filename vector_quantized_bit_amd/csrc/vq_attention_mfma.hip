@@ -634,94 +634,9 @@ __device__ __forceinline__ void new_token_workgroup8(
     __syncthreads();
 
     // 1. codes, one tensor after the other
-    static_assert(kThreads == 1024 && kEnt == kWaves * 256, "16 waves of 256 centroids");
-    float* nrm = reinterpret_cast<float*>(scratch);             // [4096] ||c||^2
-    float* wmin = reinterpret_cast<float*>(xbuf);               // [16 waves][16] pass-1 minima
-    double* wbd = reinterpret_cast<double*>(xbuf + 1024);       // [16][16] fp64 minima
-    uint32_t* wbi = reinterpret_cast<uint32_t*>(xbuf + 3072);   // [16][16] their indices
-    const int pos = lane & (kPos - 1), q4 = 4 * (lane >> 4);
-    const int b0 = 16 * wave, b1 = b0 + 16;   // this wave's centroid blocks
-    for (int t = 0; t < 2; ++t) {
-        const uint16_t* table = reinterpret_cast<const uint16_t*>(tab + t * kTable);
-        for (int i = tid; i < kEnt; i += kThreads) {
-            const uint4 c = reinterpret_cast<const uint4*>(table)[i];
-            const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-            float nn = 0.f;   // the squares of fp16 values are exact in fp32
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float lo = half_bits_to_float(static_cast<uint16_t>(w[j] & 0xffffu));
-                const float hi = half_bits_to_float(static_cast<uint16_t>(w[j] >> 16));
-                nn += lo * lo;
-                nn += hi * hi;
-            }
-            nrm[i] = nn;
-        }
-        __syncthreads();
-        double xd[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xd[j] = xnew[t][8 * pos + j];
-        float xx = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float v = static_cast<float>(xd[j]);
-            xx += v * v;
-        }
-        // fp16 hi/lo matrix-core scores in units of 2^s (the lane's column)
-        const HiLoD8 hl = hilo_d8(xd, lane);
-        const BlockD8H block(table, hl.b, lane);
-        const f32x4_t* ncol = reinterpret_cast<const f32x4_t*>(nrm + q4);
-        const float up = kBoundUpH * hl.scale, down = kBoundDownH * hl.scale;   // exact
-        const auto cup = [&](int blk) { return ncol[blk * 4] * up; };
-        const auto cdown = [&](int blk) { return ncol[blk * 4] * down; };
-        const auto exact = [&](uint32_t nc) {
-            return sqdist8_f64(xd, reinterpret_cast<const uint4*>(table)[nc]);
-        };
-        float rmin[2];   // this lane's minimum over each of the wave's 2 groups of 8 blocks
-        static_assert(16 == 2 * kSearchUnroll, "2 groups a wave");
-        search_pass1_runs<2>(block, cup, b0, rmin);
-        float smin = fminf(rmin[0], rmin[1]);
-        smin = fminf(smin, lane_partner<16>(smin, lane));
-        smin = fminf(smin, lane_partner<32>(smin, lane));
-        if (lane < kPos) wmin[wave * kPos + lane] = smin;
-        // the largest norm bounds the difference of the lane's two norm
-        // terms: fl(n up) - fl(n down) <= n 2^s (2^-14 + 2^-23 (1 + 2^-14))
-        float nmax = 0.f;
-        for (int i = lane; i < kEnt / 4; i += 64) {
-            const f32x4_t v = reinterpret_cast<const f32x4_t*>(nrm)[i];
-            nmax = fmaxf(nmax, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-        }
-        const float dmax = wave_max(nmax) * hl.scale * (0x1p-14f + 0x1p-22f);
-        __syncthreads();
-        float gmin = wmin[pos];
-        for (int w = 1; w < kWaves; ++w) gmin = fminf(gmin, wmin[w * kPos + pos]);
-        const float ex = row_bound_h(xx) * hl.scale;
-        const float thr = gmin + ex;
-        // fp64 distances of every candidate (about one a sub-vector, so they
-        // are evaluated as they are found rather than counted first), in the
-        // groups where some lane may have one
-        double bd;
-        uint32_t bi;
-        search_pass3(block, cdown, b0, b1, thr, q4, exact, bd, bi,
-                     pass3_need(rmin, thr, dmax, ex));
-        take_lanes16_32(bd, bi, lane);
-        if (lane < kPos) {
-            wbd[wave * kPos + lane] = bd;
-            wbi[wave * kPos + lane] = bi;
-        }
-        __syncthreads();
-        if (tid < kPos) {
-            double d0 = wbd[tid];
-            uint32_t i0 = wbi[tid];
-            for (int w = 1; w < kWaves; ++w) {
-                if (nearer(wbd[w * kPos + tid], wbi[w * kPos + tid], d0, i0)) {
-                    d0 = wbd[w * kPos + tid];
-                    i0 = wbi[w * kPos + tid];
-                }
-            }
-            newc[t][tid] = i0 & (kEnt - 1);   // (a code always exists for finite inputs)
-        }
-        __syncthreads();   // the exchange buffers and norms are free for the next tensor
-    }
+    static_assert(kThreads == 1024, "16 waves of 256 centroids");
+    codes8_one_token(tab, kTable, reinterpret_cast<float*>(scratch), xbuf, xnew, newc, tid, lane,
+                     wave);
     const size_t row = (static_cast<size_t>(b) * num_kv_heads + g) * capacity + append_pos;
     if (tid < 2 * kRow) {   // byte j of a row holds bits [8j, 8j + 8) of the 12-bit stream
         const int tsel = tid / kRow, j = tid % kRow;
