@@ -448,35 +448,55 @@ __global__ __launch_bounds__(kSortWaves * kWave) void kmeans_scatter_kernel(
                        static_cast<size_t>(set) * num_samples * kV;
     float4* out = reinterpret_cast<float4*>(sorted) + static_cast<size_t>(set) * num_samples * kV;
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int i0 = s0; i0 < s1; i0 += kWave) {
-        const int i = i0 + lane;
-        const bool valid = i < s1;
-        const uint32_t c = valid ? static_cast<uint32_t>(aset[i]) & (NENT - 1) : 0u;
-        float4 x[kV];
+    // a ring of kAhead steps of 64 samples in flight: each step takes its
+    // codes and samples from the ring and requests those kAhead steps later
+    // (past the chunk: its last sample, loaded and never placed), so one
+    // memory latency is spread over kAhead steps
+    constexpr int kAhead = 8;
+    static_assert(kV == 1 || kV == 2, "4- or 8-dim samples");
+    uint32_t cpre[kAhead];
+    float4 xpre0[kAhead], xpre1[kAhead];   // the sample's first and (8-dim) second float4
 #pragma unroll
-        for (int v = 0; v < kV; ++v) x[v] = valid ? xs[i * kV + v] : make_float4(0.f, 0.f, 0.f, 0.f);
-        uint64_t same = __builtin_amdgcn_ballot_w64(valid);
+    for (int k = 0; k < kAhead; ++k) {
+        const size_t i = static_cast<size_t>(min(s0 + k * kWave + lane, s1 - 1));
+        cpre[k] = static_cast<uint32_t>(aset[i]);
+        xpre0[k] = xs[i * kV];
+        if constexpr (kV == 2) xpre1[k] = xs[i * kV + 1];
+    }
+    for (int j0 = s0; j0 < s1; j0 += kAhead * kWave) {
 #pragma unroll
-        for (int b = 0; b < BITS; ++b) {
-            const bool bit = (c >> b) & 1u;
-            const uint64_t set_bits = __builtin_amdgcn_ballot_w64(bit);
-            same &= bit ? set_bits : ~set_bits;
-        }
-        const int rank = __popcll(same & below);
-        const int total = __popcll(same);
-        int32_t start = 0;
-        if (valid) start = my[c];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (valid) my[c] = start + total;   // every lane of the group writes the same value
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int32_t pos = start + rank;
-        if (valid && static_cast<uint32_t>(pos) < static_cast<uint32_t>(num_samples)) {
+        for (int k = 0; k < kAhead; ++k) {
+            const int i = j0 + k * kWave + lane;
+            const bool valid = i < s1;
+            const uint32_t c = valid ? cpre[k] & (NENT - 1) : 0u;
+            const float4 x0 = xpre0[k], x1 = xpre1[k];
+            const size_t inext = static_cast<size_t>(min(i + kAhead * kWave, s1 - 1));
+            cpre[k] = static_cast<uint32_t>(aset[inext]);
+            xpre0[k] = xs[inext * kV];
+            if constexpr (kV == 2) xpre1[k] = xs[inext * kV + 1];
+            uint64_t same = __builtin_amdgcn_ballot_w64(valid);
 #pragma unroll
-            for (int v = 0; v < kV; ++v) out[static_cast<size_t>(pos) * kV + v] = x[v];
+            for (int b = 0; b < BITS; ++b) {
+                const bool bit = (c >> b) & 1u;
+                const uint64_t set_bits = __builtin_amdgcn_ballot_w64(bit);
+                same &= bit ? set_bits : ~set_bits;
+            }
+            const int rank = __popcll(same & below);
+            const int total = __popcll(same);
+            int32_t start = 0;
+            if (valid) start = my[c];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (valid) my[c] = start + total;   // every lane of the group writes the same value
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int32_t pos = start + rank;
+            if (valid && static_cast<uint32_t>(pos) < static_cast<uint32_t>(num_samples)) {
+                out[static_cast<size_t>(pos) * kV] = x0;
+                if constexpr (kV == 2) out[static_cast<size_t>(pos) * kV + 1] = x1;
+            }
         }
     }
 }
