@@ -25,7 +25,7 @@ sources; bench.py ignores a record whose hash no longer matches.
 
 Usage, from the repository root, for example:
 
-  python profile_records.py trace --dir gpurun_out/prof --prefix trace \\
+  python profile_records.py trace --dir <rocprofv3 output dir> --prefix trace \\
       --command "rocprofv3 ... -- python -u bench.py ..." \\
       --out profiles/vq_attention_mfma_kernel.<workload>.kernel_trace.md
 """
